@@ -1,0 +1,374 @@
+"""Pins for the CPU oracle: each test checks the oracle against something
+other than itself (numpy's own rounding, brute force, closed forms, planted
+structure, a hand-worked example), so that a dropped term, a wrong sign, a
+wrong bit order or a wrong reading of the scale fails at least one test.
+
+Method: RaBiT summary (paperlayer.ai) sections 4.1, 4.2, B and G; QBB
+summary (atlas.scime.ai) "Approach"; XNOR-Net binarization (QBB "Builds on").
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = [pytest.mark.cpu,
+              pytest.mark.filterwarnings("ignore:overflow encountered in cast")]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers written independently of the oracle (numpy / fractions only)
+# ---------------------------------------------------------------------------
+
+def unpack_signs(planes):
+    """uint32 [K][out][in/32] -> int8 +-1 [K][out][in], LSB = lowest column."""
+    K, out, words = planes.shape
+    bits = np.unpackbits(planes.view(np.uint8).reshape(K, out, words * 4), axis=-1,
+                         bitorder="little")
+    return bits.astype(np.int8) * 2 - 1
+
+
+def pack_signs(signs):
+    """+-1 [..., in] -> uint32 words, LSB = lowest column (numpy packbits)."""
+    bits = (np.asarray(signs) > 0).astype(np.uint8)
+    packed = np.packbits(bits, axis=-1, bitorder="little")
+    return packed.view(np.uint32)
+
+
+def fp16_values(scales):
+    return np.asarray(scales, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def rne16_exact(q: Fraction) -> int:
+    """Round an exact non-negative rational to binary16 (ties to even), by
+    exact comparison: the candidates are consecutive fp16 values."""
+    assert q >= 0
+    finite = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    # binary search on exact values
+    lo, hi = 0, len(finite) - 1
+    if q >= Fraction(65520):
+        return 0x7C00
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if Fraction(finite[mid]) <= q:
+            lo = mid
+        else:
+            hi = mid
+    a, b = Fraction(finite[lo]), Fraction(finite[hi])
+    if q == a:
+        return lo
+    if q >= b:
+        return hi
+    da, db = q - a, b - q
+    if da < db:
+        return lo
+    if db < da:
+        return hi
+    return lo if lo % 2 == 0 else hi
+
+
+# ---------------------------------------------------------------------------
+# fp64 -> fp16 rounding: pinned to numpy's direct float64 -> float16 cast
+# ---------------------------------------------------------------------------
+
+def test_f16_roundtrip_all_finite():
+    h = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = h.view(np.float16)
+    fin = np.isfinite(vals)
+    back = oracle.f64_to_f16_array(vals[fin].astype(np.float64))
+    assert np.array_equal(back, h[fin])
+    for b in (0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xFBFF):
+        assert oracle.f16_to_f64(b) == float(np.uint16(b).view(np.float16))
+
+
+def test_f16_midpoints_against_numpy():
+    pos = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2          # exact: fp16 values have <= 11 bits
+    cases = [mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)]
+    top = np.array([65504.0, 65519.0, 65519.99999999999, 65520.0, 65536.0, 1e10, np.inf,
+                    2.0 ** -25, np.nextafter(2.0 ** -25, 1), np.nextafter(2.0 ** -25, 0),
+                    2.0 ** -26, 0.0])
+    allv = np.concatenate(cases + [top])
+    allv = np.concatenate([allv, -allv])
+    ref = allv.astype(np.float16).view(np.uint16)
+    got = oracle.f64_to_f16_array(allv)
+    assert np.array_equal(got, ref)
+
+
+def test_f16_random_doubles_against_numpy():
+    rng = np.random.default_rng(123)
+    v = np.exp2(rng.uniform(-30, 17, size=400_000)) * rng.choice([-1.0, 1.0], size=400_000)
+    v[::7] = rng.standard_normal(v[::7].size)
+    assert np.array_equal(oracle.f64_to_f16_array(v), v.astype(np.float16).view(np.uint16))
+
+
+def test_f16_rounds_once_not_via_fp32():
+    # 1 + 2^-11 is the midpoint between 1 and 1.0009765625; one fp64 ulp above
+    # it must round up.  Going through fp32 first would land on the midpoint
+    # and round to even (1.0).
+    v = np.nextafter(1.0 + 2.0 ** -11, 2.0)
+    assert oracle.f64_to_f16(v) == 0x3C01
+    assert np.float16(np.float32(v)).view(np.uint16) == 0x3C00
+
+
+def test_f16_nan_and_overflow():
+    assert oracle.f64_to_f16(float("nan")) & 0x7C00 == 0x7C00
+    assert oracle.f64_to_f16(float("nan")) & 0x03FF != 0
+    assert oracle.f64_to_f16(65520.0) == 0x7C00
+    assert oracle.f64_to_f16(-70000.0) == 0xFC00
+
+
+# ---------------------------------------------------------------------------
+# encoder
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_k3.json")))
+    W = np.array([[float(v) for v in row] for row in g["W"]], dtype=np.float32)
+    assert np.signbit(W[2, 16:]).all() and (W[2] == 0).all()
+    K = g["num_planes"]
+    planes, scales, flags = oracle.encode(W, K, g["group_size"])
+    assert flags == 0
+    exp_planes = pack_signs(np.array(g["signs"], dtype=np.int8)).reshape(K, g["out"], 1)
+    assert np.array_equal(planes, exp_planes)
+    exp_scales = np.array([[Fraction(s) for s in row] for row in g["scales"]])
+    for k in range(K):
+        for r in range(g["out"]):
+            a = Fraction(float(np.uint16(scales[k, r, 0]).view(np.float16)))
+            assert a == exp_scales[k][r], (k, r)
+
+
+def _patterns(n):
+    return np.array(list(itertools.product([-1.0, 1.0], repeat=n)))
+
+
+@pytest.mark.parametrize("group", [8, 4])
+def test_brute_force_small_groups(group):
+    """Each step of the encoder, on each (row, group) of 4x32 matrices, must
+    pick a sign pattern that maximises <R, b> over all 2^n patterns (that is
+    the least-squares optimum for the best scale a >= 0), and its scale must
+    be the fp16 value nearest the exact least-squares scale."""
+    P = _patterns(group)
+    rng = np.random.default_rng(7 + group)
+    n_mats, K = 250, 3
+    checked = 0
+    for i in range(n_mats):
+        W = (rng.standard_normal((4, 32)) * rng.uniform(0.01, 3)).astype(np.float32)
+        if i % 10 == 0:
+            W[rng.random(W.shape) < 0.2] = 0.0
+        if i % 10 == 1:
+            W[:, :] = np.float32(rng.uniform(0.1, 1)) * rng.choice([-1, 1], size=W.shape)
+        if i % 10 == 2:
+            W[rng.random(W.shape) < 0.3] = np.float32(-0.0)
+        planes, scales, flags = oracle.encode(W, K, group)
+        assert flags == 0
+        S = unpack_signs(planes)                 # [K][4][32]
+        A = fp16_values(scales)                  # [K][4][32/group]
+        R = W.copy()
+        for k in range(K):
+            Rg = R.reshape(-1, group).astype(np.float64)
+            b = S[k].reshape(-1, group).astype(np.float64)
+            a = A[k].reshape(-1)
+            best = (Rg @ P.T).max(axis=1)
+            got = (Rg * b).sum(axis=1)
+            assert np.array_equal(got, best), (i, k)
+            for gi in range(Rg.shape[0]):
+                exact = sum(Fraction(float(abs(v))) for v in Rg[gi]) / group
+                assert rne16_exact(exact) == scales[k].reshape(-1)[gi], (i, k, gi)
+                checked += 1
+            # zeros (either sign) must be coded +1
+            zero = (R.reshape(-1, group) == 0)
+            assert (b[zero] == 1).all()
+            # residual against the stored scale, fp32, one rounding
+            R = (R - (A[k].repeat(group, axis=1).astype(np.float32) * S[k].astype(np.float32))
+                 ).astype(np.float32)
+    assert checked == n_mats * K * 4 * (32 // group)
+
+
+def test_scale_is_best_fp16_for_its_signs():
+    """For each plane the stored scale is the fp16 value minimising
+    ||R - a B||^2 over fp16 values of a (checked against both neighbours),
+    on per-row (n = 512) and grouped (n = 128) encodings."""
+    W = workloads.gaussian_weight(64, 512, seed=11, outliers=True)
+    for group in (0, 128):
+        K = 4
+        planes, scales, _ = oracle.encode(W, K, group)
+        S = unpack_signs(planes).astype(np.float64)
+        n = group or 512
+        R = W.astype(np.float64)
+        for k in range(K):
+            a = fp16_values(scales[k])
+            a_cols = np.repeat(a, n, axis=1)
+            for delta in (0, -1, 1):
+                h = (scales[k].astype(np.int32) + delta).astype(np.uint16)
+                ad = np.repeat(fp16_values(h), n, axis=1)
+                err = ((R - ad * S[k]) ** 2).reshape(64, -1, n).sum(axis=2)
+                if delta == 0:
+                    base = err
+                else:
+                    assert (base <= err * (1 + 1e-12)).all()
+            # fp32 residual chain as the encoder defines it
+            R = (R.astype(np.float32) - (a_cols.astype(np.float32) * S[k].astype(np.float32))
+                 ).astype(np.float64)
+
+
+def test_residual_norm_non_increasing():
+    W = workloads.gaussian_weight(128, 1024, seed=5, outliers=True)
+    for group in (0, 128):
+        K = 6
+        planes, scales, _ = oracle.encode(W, K, group)
+        S = unpack_signs(planes).astype(np.float64)
+        n = group or 1024
+        approx = np.zeros_like(W, dtype=np.float64)
+        prev = np.linalg.norm(W.astype(np.float64), axis=1)
+        for k in range(K):
+            approx += np.repeat(fp16_values(scales[k]), n, axis=1) * S[k]
+            cur = np.linalg.norm(W.astype(np.float64) - approx, axis=1)
+            assert (cur <= prev * (1 + 1e-6)).all(), k
+            assert (cur < prev).mean() > 0.99, k   # strictly smaller almost everywhere
+            prev = cur
+
+
+def test_k1_is_xnor_binarization():
+    """K = 1 is XNOR-Net / BWN binarization: B = sign(W), alpha = ||W_r||_1 / n."""
+    W = workloads.gaussian_weight(300, 4096, seed=3, outliers=True)
+    planes, scales, _ = oracle.encode(W, 1, 0)
+    alpha = np.abs(W.astype(np.float64)).mean(axis=1)       # numpy pairwise sum
+    assert np.array_equal(scales[0, :, 0], alpha.astype(np.float16).view(np.uint16))
+    assert np.array_equal(unpack_signs(planes)[0], np.where(W >= 0, 1, -1))
+
+
+def test_planted_planes_recovered():
+    rng = np.random.default_rng(99)
+    out, n = 40, 256
+    B1 = rng.choice([-1, 1], size=(out, n))
+    B2 = B1.copy()
+    for r in range(out):                   # exactly n/2 disagreements per row
+        flip = rng.choice(n, n // 2, replace=False)
+        B2[r, flip] *= -1
+    c1 = np.float16(rng.uniform(0.1, 1.0, size=(out, 1))).astype(np.float64)
+    c2 = (c1 * rng.uniform(0.1, 0.9, size=(out, 1))).astype(np.float16).astype(np.float64)
+    W = (c1 * B1 + c2 * B2).astype(np.float32)
+    assert np.array_equal(W.astype(np.float64), c1 * B1 + c2 * B2)   # exact
+    K = 3
+    planes, scales, _ = oracle.encode(W, K, 0)
+    S = unpack_signs(planes)
+    assert np.array_equal(S[0], B1) and np.array_equal(S[1], B2)
+    assert np.array_equal(fp16_values(scales[0]), c1)
+    assert np.array_equal(fp16_values(scales[1]), c2)
+    assert (S[2] == 1).all() and (scales[2] == 0).all()
+    # constant rows: W = +-c gives B_2 = all +1 (sign(0) = +1) and a_2 = 0
+    Wc = np.where(rng.random((8, 64)) < 0.5, 0.25, -0.25).astype(np.float32)
+    p, s, _ = oracle.encode(Wc, 2, 0)
+    assert (unpack_signs(p)[1] == 1).all() and (s[1] == 0).all()
+    assert (fp16_values(s[0]) == 0.25).all()
+
+
+def test_ragged_and_degenerate_shapes():
+    W = workloads.gaussian_weight(3, 96, seed=1)
+    p, s, f = oracle.encode(W, 2, 0)
+    assert p.shape == (2, 3, 3) and s.shape == (2, 3, 1) and f == 0
+    p, s, f = oracle.encode(np.zeros((0, 64), np.float32), 2, 0)
+    assert p.shape == (2, 0, 2)
+    with pytest.raises(ValueError):
+        oracle.encode(np.zeros((2, 48), np.float32), 2, 0)        # in % 32 != 0
+    with pytest.raises(ValueError):
+        oracle.encode(np.zeros((2, 64), np.float32), 9, 0)        # K > 8
+    Wn = W.copy()
+    Wn[1, 5] = np.nan
+    assert oracle.encode(Wn, 2, 0)[2] & 1
+    Wbig = np.full((1, 32), 70000.0, np.float32)
+    assert oracle.encode(Wbig, 1, 0)[2] & 2
+
+
+def test_encode_threads_do_not_change_results():
+    W = workloads.gaussian_weight(200, 1024, seed=8, outliers=True)
+    n0 = oracle.num_threads()
+    ref = oracle.encode(W, 3, 128)
+    oracle.set_num_threads(1)
+    try:
+        one = oracle.encode(W, 3, 128)
+    finally:
+        oracle.set_num_threads(n0)
+    assert np.array_equal(ref[0], one[0]) and np.array_equal(ref[1], one[1])
+
+
+# ---------------------------------------------------------------------------
+# dequantize / multiply
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,group", [(1, 0), (2, 0), (4, 128), (8, 128), (3, 64)])
+def test_dequant_against_numpy_unpack(K, group):
+    out, inf = 48, 512
+    planes = workloads.random_planes(K, out, inf, seed=K)
+    G = inf // group if group else 1
+    scales = workloads.random_scales(K, out, G, seed=10 + K)
+    What = oracle.dequant(planes, scales, group)
+    n = group or inf
+    ref = (np.repeat(fp16_values(scales), n, axis=2) * unpack_signs(planes)).sum(axis=0)
+    assert np.array_equal(What, ref)
+
+
+@pytest.mark.parametrize("K,group,M", [(2, 0, 1), (2, 0, 5), (4, 128, 3), (1, 0, 2)])
+def test_gemm_against_numpy_matmul(K, group, M):
+    out, inf = 96, 1024
+    planes = workloads.random_planes(K, out, inf, seed=20 + K)
+    G = inf // group if group else 1
+    scales = workloads.random_scales(K, out, G, seed=30 + K)
+    X = workloads.gaussian_activations(M, inf, seed=40 + M)
+    Y = oracle.gemm(planes, scales, X, group)
+    n = group or inf
+    What = (np.repeat(fp16_values(scales), n, axis=2) * unpack_signs(planes)).sum(axis=0)
+    ref = X.view(np.float16).astype(np.float64) @ What.T
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_closed_forms():
+    K, out, inf, group = 3, 64, 768, 128
+    planes = workloads.random_planes(K, out, inf, seed=1)
+    scales = workloads.random_scales(K, out, inf // group, seed=2)
+    A = fp16_values(scales)
+    # x = 1: y_r = sum_k sum_t a_kt (2 popcount_kt - n)
+    ones = np.full((1, inf), 0x3C00, np.uint16)
+    y = oracle.gemm(planes, scales, ones, group)[0]
+    pc = np.unpackbits(planes.view(np.uint8), bitorder="little").reshape(K, out, inf // group, group).sum(-1).astype(np.int64)
+    ref = (A * (2 * pc - group)).sum(axis=(0, 2))
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+    # x = e_j: column j of What
+    S = unpack_signs(planes)
+    for j in (0, 1, 31, 32, 127, 128, 500, inf - 1):
+        e = np.zeros((1, inf), np.uint16)
+        e[0, j] = 0x3C00
+        col = oracle.gemm(planes, scales, e, group)[0]
+        assert np.array_equal(col, (A[:, :, j // group] * S[:, :, j]).sum(axis=0))
+
+
+def test_gemm_empty_and_ragged():
+    planes = workloads.random_planes(2, 5, 96, seed=3)
+    scales = workloads.random_scales(2, 5, 1, seed=4)
+    assert oracle.gemm(planes, scales, np.zeros((0, 96), np.uint16)).shape == (0, 5)
+    X = workloads.gaussian_activations(2, 96, seed=5)
+    Y = oracle.gemm(planes, scales, X)
+    What = oracle.dequant(planes, scales)
+    np.testing.assert_allclose(Y, X.view(np.float16).astype(np.float64) @ What.T, rtol=1e-13)
+
+
+def test_scale_rounds_once_in_encoder():
+    """A row whose exact mean is 1 + 2^-11 + 2^-30: one fp64 -> fp16 rounding
+    gives 1 + 2^-10 (0x3C01); rounding through fp32 first would land on the
+    fp16 midpoint 1 + 2^-11 and go to even (0x3C00)."""
+    row = np.full(32, 1 + 2.0 ** -11, dtype=np.float64)
+    row[30] = 2 + 2.0 ** -10
+    row[31] = 2.0 ** -25
+    W = row.astype(np.float32)[None, :]
+    assert np.array_equal(W[0].astype(np.float64), row)
+    assert sum(Fraction(v) for v in row) / 32 == 1 + Fraction(1, 2 ** 11) + Fraction(1, 2 ** 30)
+    _, scales, _ = oracle.encode(W, 1, 0)
+    assert scales[0, 0, 0] == 0x3C01
