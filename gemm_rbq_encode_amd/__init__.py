@@ -1,0 +1,17 @@
+"""rbq: residual-binarized linear layers on AMD MI355X (gfx950).
+
+y = sum_k a_k (.) (B_k x) with K packed +-1 sign planes and fp16 scales per
+row or per row per group of 128 columns, encoded by sequential residual
+binarization (RaBiT summary, paperlayer.ai, sections 4.1 and 4.2; QBB
+summary, atlas.scime.ai, "Approach").  The work runs in HIP kernels of
+librbq.so behind the C ABI in include/rbq.h; this package only marshals
+torch tensors into those calls.
+"""
+from ._binding import (  # noqa: F401
+    PATH_AUTO, PATH_DECODE, PATH_PREFILL, PATH_VALU,
+    RBQ_ENCODE_FORCE_SERIAL, RBQ_ERR_ALIGNMENT, RBQ_ERR_HIP, RBQ_ERR_INVALID_ARG,
+    RBQ_ERR_NO_DEVICE, RBQ_ERR_UNSUPPORTED, RBQ_OK, RBQ_STATUS_NONFINITE_W,
+    RBQ_STATUS_SCALE_OVERFLOW, LIB_PATH, RbqError, RbqLibraryMissing, Shape, check, encode,
+    gemm, gemv, groups_per_row, last_hip_error, lib, planes_bytes, scales_bytes,
+    select_path, set_path, shape, status_string, version,
+)

@@ -1,0 +1,180 @@
+// api.hip -- the C ABI of librbq (include/rbq.h): argument checks, kernel
+// selection and launches on the caller's stream.  No allocation happens
+// here; every buffer belongs to the caller.
+#include <atomic>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "rbq.h"
+#include "rbq_kernels.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+std::atomic<int> g_forced_path{RBQ_PATH_AUTO};
+
+rbq_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return RBQ_ERR_HIP;
+}
+
+rbq_status device_present() {
+    static std::once_flag once;
+    static int count = 0;
+    std::call_once(once, [] {
+        if (hipGetDeviceCount(&count) != hipSuccess)
+            count = 0;
+        (void)hipGetLastError();
+    });
+    return count > 0 ? RBQ_OK : RBQ_ERR_NO_DEVICE;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int groups_of(const rbq_shape &s) {
+    return s.group_size ? s.in_features / s.group_size : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+rbq_status rbq_check_shape(rbq_shape s) {
+    if (s.out_features < 0 || s.in_features < 0 || s.in_features % 32 != 0)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.num_planes < 1 || s.num_planes > 8)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.group_size != 0 && s.group_size != 128)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.group_size == 128 && s.in_features % 128 != 0)
+        return RBQ_ERR_INVALID_ARG;
+    return RBQ_OK;
+}
+
+size_t rbq_planes_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK)
+        return 0;
+    return (size_t)s.num_planes * (size_t)s.out_features * (size_t)(s.in_features / 32) * 4u;
+}
+
+size_t rbq_scales_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK)
+        return 0;
+    if (s.in_features == 0)
+        return 0;
+    return (size_t)s.num_planes * (size_t)s.out_features * (size_t)groups_of(s) * 2u;
+}
+
+rbq_status rbq_encode_ex(const float *W, rbq_shape s, uint32_t *planes, uint16_t *scales,
+                         int32_t *status_dev, uint32_t flags, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (flags & ~(uint32_t)RBQ_ENCODE_FORCE_SERIAL)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.out_features == 0 || s.in_features == 0)
+        return RBQ_OK;
+    if (W == nullptr || planes == nullptr || scales == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(W, 4) || !aligned(planes, 4) || !aligned(scales, 2) ||
+        (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if (s.in_features > RBQ_ENCODE_MAX_IN)
+        return RBQ_ERR_UNSUPPORTED;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_encode(W, s.out_features, s.in_features, s.num_planes,
+                                      s.group_size, planes, scales, status_dev,
+                                      (flags & RBQ_ENCODE_FORCE_SERIAL) ? 1 : 0,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+rbq_status rbq_encode(const float *W, rbq_shape s, uint32_t *planes, uint16_t *scales,
+                      int32_t *status_dev, void *stream) {
+    return rbq_encode_ex(W, s, planes, scales, status_dev, 0u, stream);
+}
+
+size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M) {
+    (void)s;
+    (void)M;
+    return 0;
+}
+
+rbq_path rbq_set_path(rbq_path p) {
+    return (rbq_path)g_forced_path.exchange((int)p);
+}
+
+rbq_path rbq_select_path(rbq_shape s, int32_t M) {
+    (void)s;
+    (void)M;
+    return RBQ_PATH_VALU;
+}
+
+rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                    const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
+                    size_t ws_bytes, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (M < 0)
+        return RBQ_ERR_INVALID_ARG;
+    if (ws_bytes < rbq_gemm_workspace_bytes(s, M) || (ws_bytes > 0 && workspace == nullptr))
+        return RBQ_ERR_INVALID_ARG;
+    if (M == 0 || s.out_features == 0)
+        return RBQ_OK;
+    if (Y == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(Y, 2))
+        return RBQ_ERR_ALIGNMENT;
+    hipStream_t hs = (hipStream_t)stream;
+    if (s.in_features == 0) {  // empty sums: Y = 0
+        if ((st = device_present()) != RBQ_OK)
+            return st;
+        hipError_t e = rbq::launch_fill_zero_u16(Y, (int64_t)M * s.out_features, hs);
+        return e == hipSuccess ? RBQ_OK : hip_fail(e);
+    }
+    if (planes == nullptr || scales == nullptr || X == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(planes, 16) || !aligned(scales, 2) || !aligned(X, 16))
+        return RBQ_ERR_ALIGNMENT;
+    rbq_path path = (rbq_path)g_forced_path.load();
+    if (path == RBQ_PATH_AUTO)
+        path = rbq_select_path(s, M);
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e;
+    switch (path) {
+    case RBQ_PATH_VALU:
+        e = rbq::launch_gemm_valu(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                  s.group_size, X, M, Y, hs);
+        break;
+    default:
+        return RBQ_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                    const uint16_t *x, uint16_t *y, void *stream) {
+    return rbq_gemm(planes, scales, s, x, 1, y, nullptr, 0, stream);
+}
+
+int32_t rbq_last_hip_error(void) { return g_last_hip_error; }
+
+const char *rbq_status_string(rbq_status st) {
+    switch (st) {
+    case RBQ_OK: return "RBQ_OK";
+    case RBQ_ERR_INVALID_ARG: return "RBQ_ERR_INVALID_ARG: invalid argument";
+    case RBQ_ERR_ALIGNMENT: return "RBQ_ERR_ALIGNMENT: misaligned pointer";
+    case RBQ_ERR_UNSUPPORTED: return "RBQ_ERR_UNSUPPORTED: not supported by this build";
+    case RBQ_ERR_NO_DEVICE: return "RBQ_ERR_NO_DEVICE: no HIP device";
+    case RBQ_ERR_HIP: return "RBQ_ERR_HIP: HIP runtime error";
+    }
+    return "unknown rbq_status";
+}
+
+const char *rbq_version(void) { return "rbq 0.1.0 (gfx950)"; }
+
+}  // extern "C"

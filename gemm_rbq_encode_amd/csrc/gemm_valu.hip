@@ -1,0 +1,91 @@
+// gemm_valu.hip -- y = sum_k a_k (.) (B_k x) with a plain fp32 VALU bit loop.
+//
+// The correctness baseline and the fallback for shapes the MFMA kernels do
+// not take.  Each +-1 dot product is formed as 2 * (sum of x where the bit
+// is set) - (sum of x over the word), so only additions touch x ("RaBiT"
+// summary, paperlayer.ai, section 4.1: binary cores with per-channel
+// scales, computed by additions and subtractions).
+//
+// One wave per output row and token; lane l takes words l, l+64, ... of the
+// row, reads the 32 matching fp16 activations, and accumulates
+// a_k[r][t] * (2 S_k - sum x) over the K planes; a wave reduction gives y.
+#include "rbq_device.h"
+#include "rbq_kernels.h"
+
+namespace rbq {
+
+namespace {
+
+__global__ __launch_bounds__(256) void gemm_valu_kernel(
+    const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
+    int K, int group_size, const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
+    const int wave = threadIdx.x / RBQ_WAVE;
+    const int lane = threadIdx.x & (RBQ_WAVE - 1);
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= out)
+        return;
+    const int words = in >> 5;
+    const int G = group_size ? in / group_size : 1;
+    for (int m = blockIdx.y; m < M; m += gridDim.y) {
+        const uint16_t *x = X + (size_t)m * in;
+        float acc = 0.0f;
+        for (int w = lane; w < words; w += RBQ_WAVE) {
+            float xv[32];
+            const uint4 *xp = reinterpret_cast<const uint4 *>(x + 32 * w);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = xp[q];
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xv[8 * q + 2 * e] = h2f((uint16_t)(u[e] & 0xFFFFu));
+                    xv[8 * q + 2 * e + 1] = h2f((uint16_t)(u[e] >> 16));
+                }
+            }
+            float sx = 0.0f;
+#pragma unroll
+            for (int b = 0; b < 32; ++b)
+                sx += xv[b];
+            const int t = group_size ? (32 * w) / group_size : 0;
+            for (int k = 0; k < K; ++k) {
+                const uint32_t bits = planes[((size_t)k * out + r) * words + w];
+                float s = 0.0f;
+#pragma unroll
+                for (int b = 0; b < 32; ++b)
+                    s += ((bits >> b) & 1u) ? xv[b] : 0.0f;
+                const float a = h2f(scales[((size_t)k * out + r) * G + t]);
+                acc += a * (2.0f * s - sx);
+            }
+        }
+        acc = wave_sum_f32(acc);
+        if (lane == 0)
+            Y[(size_t)m * out + r] = f2h(acc);
+    }
+}
+
+__global__ void fill_zero_u16_kernel(uint16_t *Y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        Y[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            hipStream_t st) {
+    const int gy = M < 65535 ? M : 65535;
+    hipLaunchKernelGGL(gemm_valu_kernel, dim3((out + 3) / 4, gy), dim3(256), 0, st, planes,
+                       scales, out, in, K, group_size, X, M, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, Y, n);
+    return hipGetLastError();
+}
+
+}  // namespace rbq

@@ -1,0 +1,88 @@
+// rbq_device.h -- device helpers shared by the librbq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define RBQ_WAVE 64
+
+namespace rbq {
+
+// binary16 bits -> float (exact).
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// float -> binary16 bits, rounded to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f2h(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// double -> binary16 bits with ONE rounding to nearest, ties to even,
+// computed on the integer bit pattern (never through fp32).  Subnormal
+// results are kept; values at or beyond 65520 become infinity.
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
+    uint64_t b = (uint64_t)__double_as_longlong(v);
+    uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+    int e = (int)(mag >> 52);
+    uint64_t frac = mag & 0x000FFFFFFFFFFFFFull;
+    if (e == 0x7FF)
+        return (uint16_t)(sign | (frac ? 0x7E00u : 0x7C00u));
+    int E = e - 1023;                      // unbiased exponent (normal doubles)
+    if (E >= 16)
+        return (uint16_t)(sign | 0x7C00u);
+    if (E < -25)                           // below 2^-25: rounds to zero
+        return (uint16_t)sign;
+    uint64_t sig = frac | (1ull << 52);    // value = sig * 2^(E-52)
+    int qexp = (E < -14) ? -24 : E - 10;   // fp16 quantum in this binade
+    int shift = 52 + qexp - E;             // 42 .. 53 bits dropped
+    uint64_t n = sig >> shift;
+    uint64_t rem = sig & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (n & 1)))
+        ++n;
+    uint32_t bits = (E < -14) ? (uint32_t)n
+                              : ((uint32_t)(E + 15) << 10) + (uint32_t)n - 1024u;
+    if (bits >= 0x7C00u)
+        bits = 0x7C00u;
+    return (uint16_t)(sign | bits);
+}
+
+// Correctly rounded S / n in fp64 (n a positive integer), whatever the
+// accuracy of the compiler's division sequence: the quotient is corrected by
+// the exact remainder S - q n (an FMA) to the nearer neighbour, ties to even.
+__device__ __forceinline__ double div_rn(double S, double n) {
+    double q = S / n;
+    double r0 = __fma_rn(-q, n, S);
+    if (r0 == 0.0)
+        return q;
+    // q >= 0 here (S >= 0, n > 0); its neighbours are the adjacent bit patterns
+    uint64_t bq0 = (uint64_t)__double_as_longlong(q);
+    double q1 = __longlong_as_double((long long)((r0 > 0.0) ? bq0 + 1 : bq0 - 1));
+    double r1 = __fma_rn(-q1, n, S);
+    double a0 = __builtin_fabs(r0), a1 = __builtin_fabs(r1);
+    if (a1 < a0)
+        return q1;
+    if (a1 == a0) {
+        uint64_t bq = (uint64_t)__double_as_longlong(q);
+        return (bq & 1) ? q1 : q;
+    }
+    return q;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, RBQ_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, RBQ_WAVE);
+    return v;
+}
+
+}  // namespace rbq

@@ -1,0 +1,22 @@
+// rbq_kernels.h -- host-side launchers of the librbq kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rbq {
+
+// Encoder: one workgroup of 256 threads per output row.
+hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
+                         uint32_t *planes, uint16_t *scales, int32_t *status,
+                         int force_serial, hipStream_t st);
+
+// fp32 VALU bit loop, any M (correctness baseline and fallback).
+hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            hipStream_t st);
+
+// Y = 0 for in_features == 0 (an empty sum).
+hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);
+
+}  // namespace rbq

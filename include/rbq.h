@@ -1,0 +1,186 @@
+/*
+ * rbq.h -- C ABI of librbq, residual-binarized linear layers on AMD MI355X
+ * (gfx950).
+ *
+ * The layer is y = sum_{k=1..K} a_k (.) (B_k x): K binary (+-1) cores with
+ * scale vectors, computed with additions and subtractions only ("RaBiT:
+ * Residual-Aware Binarization Training for Accurate and Efficient LLMs",
+ * paperlayer.ai summary, section 4.1; "QBB: Quantization with Binary Bases
+ * for LLMs", atlas.scime.ai summary, "Approach").  The cores come from
+ * sequential residual binarization of one full-precision weight:
+ * B_1 = sign(W), R_1 = W - a_1 B_1, B_2 = sign(R_1), ... (RaBiT sections 4.2,
+ * A and B).
+ *
+ * Storage format (the only format every entry point reads and writes):
+ *   planes  uint32 [K][out][in/32], row-major.  Word w of row r of plane k
+ *           holds columns 32w .. 32w+31, bit b (least significant first) is
+ *           column 32w + b, and a set bit means +1, a clear bit -1 (RaBiT D
+ *           "GPU implementation": 32 columns per uint32).
+ *   scales  IEEE binary16 bit patterns, uint16 [K][out][G], where G = 1 for
+ *           one scale per output row (group_size 0, RaBiT) or in/128 for one
+ *           scale per row per group of 128 consecutive input columns
+ *           (group_size 128, QBB "W(4x1)A16g128").
+ *   x, y    IEEE binary16 bit patterns, row-major [M][in] and [M][out].
+ *   W       fp32, row-major [out][in].
+ *
+ * Memory and streams.  Every pointer argument is a DEVICE pointer owned by
+ * the caller (allocated with hipMalloc, or by PyTorch); the library never
+ * allocates, frees or keeps a pointer after a call returns.  `stream` is a
+ * hipStream_t (NULL = the null stream); each call only enqueues work on it
+ * and returns, so results are ready when the stream reaches that point.
+ * Calls are stateless and may be made from several host threads.
+ *
+ * Errors.  Argument errors are found on the host before anything is
+ * enqueued, and then nothing is written.  RBQ_ERR_HIP means a HIP call
+ * failed; rbq_last_hip_error() returns its hipError_t on the calling thread.
+ * Errors found in the data on the device are reported through `status_dev`.
+ */
+#ifndef RBQ_H
+#define RBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rbq_status {
+    RBQ_OK = 0,
+    RBQ_ERR_INVALID_ARG = 1,   /* null pointer, bad size, K or group size */
+    RBQ_ERR_ALIGNMENT = 2,     /* a pointer is not aligned as required */
+    RBQ_ERR_UNSUPPORTED = 3,   /* valid, but beyond what this build handles */
+    RBQ_ERR_NO_DEVICE = 4,     /* no HIP device is visible */
+    RBQ_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} rbq_status;
+
+/* Shape of one encoded linear layer.
+ *   out_features  rows of W (outputs), >= 0
+ *   in_features   columns of W (inputs), >= 0 and a multiple of 32
+ *   num_planes    K, 1..8
+ *   group_size    0 (one scale per row) or 128 (in_features % 128 == 0) */
+typedef struct rbq_shape {
+    int32_t out_features;
+    int32_t in_features;
+    int32_t num_planes;
+    int32_t group_size;
+} rbq_shape;
+
+/* Bits of the device status word written by rbq_encode. */
+#define RBQ_STATUS_NONFINITE_W     1u   /* some entry of W was NaN or +-Inf */
+#define RBQ_STATUS_SCALE_OVERFLOW  2u   /* some scale rounded to +-Inf in fp16 */
+
+/* Flags for rbq_encode_ex. */
+#define RBQ_ENCODE_FORCE_SERIAL    1u   /* take the serial summation for every
+                                           (row, group): slow, same results */
+
+/* Largest in_features the encoder handles in this build. */
+#define RBQ_ENCODE_MAX_IN          32768
+
+/* Returns RBQ_OK if `s` is a valid shape, else RBQ_ERR_INVALID_ARG. */
+rbq_status rbq_check_shape(rbq_shape s);
+
+/* Bytes of the planes array: K * out * (in/32) * 4.  0 for an invalid shape. */
+size_t rbq_planes_bytes(rbq_shape s);
+
+/* Bytes of the scales array: K * out * G * 2.  0 for an invalid shape. */
+size_t rbq_scales_bytes(rbq_shape s);
+
+/*
+ * rbq_encode -- sequential residual binarization (RaBiT sections 4.2, B and
+ * G "RaBiT training"; QBB "Approach": cascaded analytical residual
+ * binarization; scale = mean absolute residual, the closed form of XNOR-Net,
+ * which QBB lists under "Builds on").
+ *
+ * For each row r and each group t of n columns (n = in, or 128), with
+ * R = W[r, group t] in fp32, for k = 1..K:
+ *   bit_j   = (R_j >= 0)             sign(0) = +1, also for -0.0
+ *   a_k     = mean_j |R_j|, where the sum is the serial fp64 sum in
+ *             ascending column order, divided by n in fp64 (correctly
+ *             rounded), then rounded ONCE to binary16 (nearest, ties even)
+ *   R_j     = R_j - (bit_j ? a_k : -a_k)   in fp32, against the stored a_k
+ * and writes bit_j to planes[k][r] and a_k to scales[k][r][t].
+ * Results are bit-identical to that definition (the kernel sums in parallel
+ * with a proven error bound and falls back to the serial sum whenever the
+ * bound cannot decide the fp16 rounding).
+ *
+ *   W           device, fp32 [out][in], 4-byte aligned, read only
+ *   planes      device, uint32 [K][out][in/32], 4-byte aligned, written
+ *   scales      device, uint16 [K][out][G], 2-byte aligned, written
+ *   status_dev  device int32 or NULL.  If given, the kernel ORs
+ *               RBQ_STATUS_* bits into it (the caller clears it first).
+ *               Non-finite W is outside the method; its planes and scales
+ *               are then unspecified.
+ * Errors: RBQ_ERR_INVALID_ARG (shape, null pointer), RBQ_ERR_ALIGNMENT,
+ * RBQ_ERR_UNSUPPORTED (in > RBQ_ENCODE_MAX_IN), RBQ_ERR_NO_DEVICE,
+ * RBQ_ERR_HIP.  An empty shape (out == 0 or in == 0) enqueues nothing.
+ */
+rbq_status rbq_encode(const float *W, rbq_shape s, uint32_t *planes, uint16_t *scales,
+                      int32_t *status_dev, void *stream);
+
+/* rbq_encode with flags (RBQ_ENCODE_*); flags = 0 is rbq_encode. */
+rbq_status rbq_encode_ex(const float *W, rbq_shape s, uint32_t *planes, uint16_t *scales,
+                         int32_t *status_dev, uint32_t flags, void *stream);
+
+/*
+ * rbq_gemm -- Y[m] = sum_k a_k (.) (B_k X[m]) for M tokens (RaBiT section
+ * 4.1: binary cores with per-channel scales, additions and subtractions
+ * only; section 4.2: the K paths run in parallel at inference; QBB "Key
+ * results": per-group scales).  Equivalently Y = X What^T with
+ * What[r][j] = sum_k a_k[r][t(j)] (bit ? +1 : -1).  Accumulation is fp32 or
+ * wider; each output is rounded once to binary16.
+ *
+ *   planes, scales  device, encoded layer (format above); planes 16-byte
+ *                   aligned, scales 2-byte aligned; any finite fp16 scales
+ *   X               device, fp16 [M][in], 16-byte aligned
+ *   M               tokens, >= 0 (0 enqueues nothing)
+ *   Y               device, fp16 [M][out], 4-byte aligned, written
+ *   workspace       device scratch of ws_bytes >= rbq_gemm_workspace_bytes
+ *                   (may be NULL when that is 0); contents on return are
+ *                   unspecified
+ * Errors: RBQ_ERR_INVALID_ARG, RBQ_ERR_ALIGNMENT, RBQ_ERR_NO_DEVICE,
+ * RBQ_ERR_HIP.
+ */
+rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                    const uint16_t *X, int32_t M, uint16_t *Y,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes rbq_gemm needs for this shape and M (0 for all current
+ * kernels; kept so a split-K variant can be added without an ABI change). */
+size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M);
+
+/* rbq_gemv -- rbq_gemm with M = 1 (one decode token):
+ * y = sum_k a_k (.) (B_k x), x fp16 [in], y fp16 [out]. */
+rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                    const uint16_t *x, uint16_t *y, void *stream);
+
+/* Kernel families rbq_gemm can use; RBQ_PATH_AUTO picks by shape and M. */
+typedef enum rbq_path {
+    RBQ_PATH_AUTO = 0,
+    RBQ_PATH_VALU = 1,      /* plain fp32 VALU bit loop, any M */
+    RBQ_PATH_DECODE = 2,    /* int8 MFMA on unpacked bits, M <= 16 */
+    RBQ_PATH_PREFILL = 3    /* fp16 MFMA on LDS-unpacked weights, large M */
+} rbq_path;
+
+/* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for
+ * tests and A/B measurement).  A forced path that cannot take a call makes
+ * that call return RBQ_ERR_UNSUPPORTED.  Returns the previous setting. */
+rbq_path rbq_set_path(rbq_path p);
+
+/* The kernel family rbq_gemm would take for this shape and M. */
+rbq_path rbq_select_path(rbq_shape s, int32_t M);
+
+/* hipError_t of the last RBQ_ERR_HIP on the calling thread (0 if none). */
+int32_t rbq_last_hip_error(void);
+
+/* Static text for a status code. */
+const char *rbq_status_string(rbq_status st);
+
+/* Library version string. */
+const char *rbq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBQ_H */

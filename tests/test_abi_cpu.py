@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (include/rbq.h): the library loads, exports
+every declared symbol, and validates arguments before touching a device.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gemm_rbq_encode_amd as rbq
+
+pytestmark = pytest.mark.cpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rbq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rbq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13, names
+    L = ctypes.CDLL(rbq.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_header():
+    from gemm_rbq_encode_amd import _binding
+    assert set(declared_functions()) == set(_binding._SIGNATURES)
+
+
+def test_sizes_and_shape_checks():
+    s = rbq.shape(4096, 11008, 2, 0)
+    assert rbq.planes_bytes(s) == 2 * 4096 * (11008 // 32) * 4
+    assert rbq.scales_bytes(s) == 2 * 4096 * 2
+    g = rbq.shape(13824, 5120, 4, 128)
+    assert rbq.planes_bytes(g) == 4 * 13824 * 160 * 4
+    assert rbq.scales_bytes(g) == 4 * 13824 * 40 * 2
+    L = rbq.lib()
+    assert L.rbq_check_shape(s) == rbq.RBQ_OK
+    bad = [rbq.shape(-1, 64, 2), rbq.shape(8, 48, 2), rbq.shape(8, 64, 0), rbq.shape(8, 64, 9),
+           rbq.shape(8, 64, 2, 64), rbq.shape(8, 96, 2, 128), rbq.shape(8, -32, 2)]
+    for b in bad:
+        assert L.rbq_check_shape(b) == rbq.RBQ_ERR_INVALID_ARG, b
+        assert rbq.planes_bytes(b) == 0 and rbq.scales_bytes(b) == 0
+    assert rbq.planes_bytes(rbq.shape(0, 64, 2)) == 0
+    assert rbq.lib().rbq_gemm_workspace_bytes(s, 16) == 0
+
+
+def test_status_strings_and_version():
+    for st in range(6):
+        assert rbq.status_string(st).startswith("RBQ_")
+    assert "unknown" in rbq.status_string(99)
+    assert "gfx950" in rbq.version()
+    assert rbq.last_hip_error() == 0
+
+
+def test_argument_errors_before_any_launch():
+    L = rbq.lib()
+    s = rbq.shape(64, 128, 2, 0)
+    ok = 0x10000  # aligned stand-in addresses: argument checks never dereference
+    # null pointers
+    assert L.rbq_encode(None, s, ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode(ok, s, None, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm(ok, ok, s, None, 1, ok, None, 0, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm(ok, ok, s, ok, 1, None, None, 0, None) == rbq.RBQ_ERR_INVALID_ARG
+    # bad shape / M / flags
+    assert L.rbq_encode(ok, rbq.shape(64, 100, 2), ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm(ok, ok, s, ok, -1, ok, None, 0, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode_ex(ok, s, ok, ok, None, 8, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm(ok, ok, s, ok, 1, ok, None, 16, None) == rbq.RBQ_ERR_INVALID_ARG
+    # misalignment
+    assert L.rbq_encode(ok + 2, s, ok, ok, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_encode(ok, s, ok, ok + 1, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemm(ok + 4, ok, s, ok, 1, ok, None, 0, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemm(ok, ok, s, ok + 8, 1, ok, None, 0, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemm(ok, ok, s, ok, 1, ok + 1, None, 0, None) == rbq.RBQ_ERR_ALIGNMENT
+    # too long a row for the encoder
+    big = rbq.shape(4, 32768 + 32, 2, 0)
+    assert L.rbq_encode(ok, big, ok, ok, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    # empty work is fine and enqueues nothing
+    assert L.rbq_encode(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
+    assert L.rbq_gemm(None, None, s, None, 0, None, None, 0, None) == rbq.RBQ_OK
+    assert L.rbq_gemm(None, None, rbq.shape(0, 64, 2), None, 3, None, None, 0, None) == rbq.RBQ_OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_call_without_device_reports_no_device():
+    L = rbq.lib()
+    s = rbq.shape(64, 128, 2, 0)
+    ok = 0x10000
+    assert L.rbq_encode(ok, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
+    assert L.rbq_gemv(ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_NO_DEVICE
+    assert L.rbq_gemm(ok, ok, s, ok, 2, ok, None, 0, None) == rbq.RBQ_ERR_NO_DEVICE
+
+
+def test_path_override_roundtrip():
+    old = rbq.set_path(rbq.PATH_VALU)
+    try:
+        assert rbq.set_path(rbq.PATH_AUTO) == rbq.PATH_VALU
+    finally:
+        rbq.set_path(old)
+
+
+def test_binding_refuses_host_tensors():
+    with pytest.raises(TypeError):
+        rbq.encode(torch.zeros(4, 64), 2)

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Encoder: planes and scales bit-exact.  Layer output: relative L2 error
+<= 1e-3 and max abs error <= 1e-2 * rms(y_ref) against the fp64 oracle
+(fp32 accumulation, fp16 output), on every workload shape, on edge cases,
+and on every kernel family.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_rbq_encode_amd as rbq
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+REL_L2 = 1e-3
+MAX_ABS_RMS = 1e-2
+
+# kernel families rbq_gemm can be forced to, with the largest M each takes
+PATHS = {"valu": (rbq.PATH_VALU, 1 << 30)}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def gpu_encode(W, K, group, force_serial=False):
+    Wt = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev())
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    planes, scales = rbq.encode(Wt, K, group, status=status, force_serial=force_serial)
+    torch.cuda.synchronize()
+    return (planes.cpu().numpy().view(np.uint32), scales.cpu().numpy().view(np.uint16),
+            int(status.item()))
+
+
+def gpu_gemm(planes, scales, X, group, path=rbq.PATH_AUTO):
+    p = torch.from_numpy(np.ascontiguousarray(planes).view(np.int32)).to(dev())
+    s = torch.from_numpy(np.ascontiguousarray(scales).view(np.float16)).to(dev())
+    x = torch.from_numpy(np.ascontiguousarray(X).view(np.float16)).to(dev())
+    old = rbq.set_path(path)
+    try:
+        Y = rbq.gemm(p, s, x, group)
+        torch.cuda.synchronize()
+    finally:
+        rbq.set_path(old)
+    return Y.cpu().numpy().astype(np.float64)
+
+
+def assert_close(Y, Yref, what=""):
+    assert Y.shape == Yref.shape
+    assert np.isfinite(Y).all(), what
+    rms = np.sqrt(np.mean(Yref ** 2))
+    rel = np.linalg.norm(Y - Yref) / max(np.linalg.norm(Yref), 1e-300)
+    mx = np.abs(Y - Yref).max() if Y.size else 0.0
+    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
+    assert mx <= MAX_ABS_RMS * rms, f"{what}: max-abs {mx:.3e} vs rms {rms:.3e}"
+    return rel
+
+
+def assert_encode_matches(W, K, group, force_serial=False, what=""):
+    p, s, f = oracle.encode(W, K, group)
+    gp, gs, gf = gpu_encode(W, K, group, force_serial)
+    assert gf == f, f"{what}: status {gf} vs {f}"
+    assert np.array_equal(gs, s), f"{what}: scales differ at {np.argwhere(gs != s)[:5]}"
+    assert np.array_equal(gp, p), f"{what}: planes differ at {np.argwhere(gp != p)[:5]}"
+    return p, s
+
+
+# ---------------------------------------------------------------------------
+# encoder
+# ---------------------------------------------------------------------------
+
+def test_encode_small_workload():
+    wl = workloads.WORKLOADS["small"]
+    assert_encode_matches(workloads.workload_weight(wl, 0), wl.num_planes, wl.group_size, what="small")
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_encode_llama2_7b(i):
+    wl = workloads.WORKLOADS["llama2_7b"]
+    W = workloads.workload_weight(wl, i)
+    assert_encode_matches(W, wl.num_planes, wl.group_size, what=wl.linears[i].name)
+
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_encode_llama2_13b_g128(i):
+    wl = workloads.WORKLOADS["llama2_13b_g128"]
+    W = workloads.workload_weight(wl, i)
+    assert_encode_matches(W, wl.num_planes, wl.group_size, what=wl.linears[i].name)
+
+
+@pytest.mark.parametrize("i", [0, 1])
+def test_encode_llama3_8b_prefill_shapes(i):
+    wl = workloads.WORKLOADS["llama3_8b_prefill"]
+    assert_encode_matches(workloads.workload_weight(wl, i), wl.num_planes, wl.group_size)
+
+
+def test_encode_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_k3.json")))
+    W = np.array([[float(v) for v in row] for row in g["W"]], dtype=np.float32)
+    assert_encode_matches(W, g["num_planes"], g["group_size"], what="golden")
+
+
+@pytest.mark.parametrize("out,inf,K,group", [
+    (1, 32, 1, 0), (3, 96, 2, 0), (5, 160, 3, 0), (7, 4128, 2, 0), (2, 4160, 8, 0),
+    (9, 16384, 2, 0), (4, 32768, 2, 0), (3, 128, 4, 128), (6, 384, 4, 128),
+    (5, 8320, 4, 128), (2, 32768, 3, 128), (17, 1024, 8, 0), (33, 640, 5, 128)])
+def test_encode_ragged_shapes(out, inf, K, group):
+    W = workloads.gaussian_weight(out, inf, seed=out * 1000 + inf + K, outliers=True)
+    assert_encode_matches(W, K, group, what=f"{out}x{inf} K={K} g={group}")
+
+
+def test_encode_special_values():
+    rng = np.random.default_rng(5)
+    rows = []
+    rows.append(np.zeros(256, np.float32))                               # all +0
+    rows.append(np.full(256, -0.0, np.float32))                          # all -0
+    z = rng.standard_normal(256).astype(np.float32)
+    z[rng.random(256) < 0.3] = -0.0
+    rows.append(z)
+    rows.append((rng.standard_normal(256) * 1e-40).astype(np.float32))   # fp32 denormals
+    rows.append(np.full(256, 1e-7, np.float32))                          # fp16-subnormal scale
+    rows.append(np.where(rng.random(256) < 0.5, 0.25, -0.25).astype(np.float32))
+    rows.append((rng.standard_normal(256) * 3e3).astype(np.float32))     # large scales
+    W = np.stack(rows)
+    for K, group in ((4, 0), (4, 128), (8, 0)):
+        assert_encode_matches(W, K, group, what=f"special K={K} g={group}")
+
+
+def test_encode_ties_take_the_serial_path():
+    """Rows whose mean is exactly an fp16 midpoint cannot be decided by the
+    parallel sum's error bound, so the serial path decides them."""
+    rows = []
+    for base in (1.0, 0.5, 2.0 ** -14, 3.0):
+        v = np.float32(base * (1 + 2.0 ** -11))           # midpoint between two fp16 values
+        rows.append(np.full(512, v, np.float32) * np.where(np.arange(512) % 3 == 0, -1, 1))
+    row = np.full(512, 1 + 2.0 ** -11, np.float64)        # one ulp-of-fp64 above the midpoint
+    row[510] = 2 + 2.0 ** -10
+    row[511] = 2.0 ** -25
+    row[509] = 1 + 2.0 ** -11 + 2.0 ** -23
+    rows.append(row.astype(np.float32))
+    W = np.stack(rows).astype(np.float32)
+    for group in (0, 128):
+        assert_encode_matches(W, 3, group, what=f"ties g={group}")
+
+
+@pytest.mark.parametrize("out,inf,K,group", [(64, 512, 3, 0), (32, 4096, 2, 0), (16, 1024, 4, 128),
+                                             (8, 11008, 2, 0)])
+def test_encode_forced_serial_path(out, inf, K, group):
+    W = workloads.gaussian_weight(out, inf, seed=77 + inf, outliers=True)
+    assert_encode_matches(W, K, group, force_serial=True, what="serial")
+
+
+def test_encode_status_flags():
+    W = workloads.gaussian_weight(4, 256, seed=1)
+    W[2, 17] = np.inf
+    _, _, f = gpu_encode(W, 2, 0)
+    assert f & rbq.RBQ_STATUS_NONFINITE_W
+    Wb = np.full((2, 256), 7.0e4, np.float32)
+    _, _, f = gpu_encode(Wb, 1, 128)
+    assert f & rbq.RBQ_STATUS_SCALE_OVERFLOW and not f & rbq.RBQ_STATUS_NONFINITE_W
+
+
+def test_encode_deterministic_and_stream_ordered():
+    W = workloads.gaussian_weight(512, 4096, seed=9, outliers=True)
+    Wt = torch.from_numpy(W).to(dev())
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        p1, s1 = rbq.encode(Wt, 3, 0)
+        p2, s2 = rbq.encode(Wt, 3, 0)
+    side.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# layer output
+# ---------------------------------------------------------------------------
+
+def _encoded(wl_name, i):
+    wl = workloads.WORKLOADS[wl_name]
+    W = workloads.workload_weight(wl, i)
+    p, s, _ = oracle.encode(W, wl.num_planes, wl.group_size)
+    return wl, p, s
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_gemv_small_workload(path):
+    wl, p, s = _encoded("small", 0)
+    X = workloads.workload_activations(wl, 512, 1)
+    Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
+    assert_close(Y, oracle.gemm(p, s, X, wl.group_size), "small")
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("i", [0, 4, 6])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemm_llama2_7b(path, i, M):
+    if M > PATHS[path][1]:
+        pytest.skip("path does not take this M")
+    wl, p, s = _encoded("llama2_7b", i)
+    X = workloads.workload_activations(workloads.WORKLOADS["llama2_7b_skinny"] if M > 1 else wl,
+                                       wl.linears[i].in_features, M)
+    Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
+    assert_close(Y, oracle.gemm(p, s, X, wl.group_size), f"{wl.linears[i].name} M={M}")
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_gemv_llama2_13b_g128(path, i):
+    wl, p, s = _encoded("llama2_13b_g128", i)
+    X = workloads.workload_activations(wl, wl.linears[i].in_features, 1)
+    Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
+    assert_close(Y, oracle.gemm(p, s, X, wl.group_size), wl.linears[i].name)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("i", [0, 1])
+def test_gemm_prefill_sampled_tokens(path, i):
+    """M = 2048 at full size; the oracle checks a sample of token rows."""
+    if PATHS[path][1] < 2048:
+        pytest.skip("path does not take M = 2048")
+    wl, p, s = _encoded("llama3_8b_prefill", i)
+    X = workloads.workload_activations(wl, wl.linears[i].in_features, 2048)
+    Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
+    rows = np.array([0, 1, 2, 63, 64, 127, 1000, 1999, 2046, 2047])
+    assert_close(Y[rows], oracle.gemm(p, s, X[rows], wl.group_size), f"prefill {i}")
+    assert np.isfinite(Y).all()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("out,inf,K,group,M", [
+    (1, 32, 1, 0, 1), (3, 96, 2, 0, 2), (17, 4128, 3, 0, 5), (40, 384, 4, 128, 3),
+    (65, 1024, 8, 0, 16), (129, 11008, 2, 0, 7), (31, 5120, 4, 128, 17), (70, 2048, 2, 0, 33)])
+def test_gemm_ragged_random_signed_scales(path, out, inf, K, group, M):
+    if M > PATHS[path][1]:
+        pytest.skip("path does not take this M")
+    p = workloads.random_planes(K, out, inf, seed=out + inf)
+    G = inf // group if group else 1
+    s = workloads.random_scales(K, out, G, seed=M + K, signed=True)
+    X = workloads.gaussian_activations(M, inf, seed=inf + M)
+    Y = gpu_gemm(p, s, X, group, PATHS[path][0])
+    assert_close(Y, oracle.gemm(p, s, X, group), f"{out}x{inf} K={K} g={group} M={M}")
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_gemm_closed_forms(path):
+    K, out, inf, group = 2, 96, 4096, 0
+    p = workloads.random_planes(K, out, inf, seed=3)
+    s = workloads.random_scales(K, out, 1, seed=4)
+    ones = np.full((1, inf), 0x3C00, np.uint16)
+    A = s.view(np.float16).astype(np.float64)[:, :, 0]
+    pc = np.unpackbits(p.view(np.uint8), bitorder="little").reshape(K, out, inf).sum(-1).astype(np.int64)
+    ref = (A * (2 * pc - inf)).sum(axis=0)
+    assert_close(gpu_gemm(p, s, ones, group, PATHS[path][0])[0], ref, "x=1")
+    E = np.zeros((3, inf), np.uint16)
+    for m, j in enumerate((0, 33, inf - 1)):
+        E[m, j] = 0x3C00
+    Y = gpu_gemm(p, s, E, group, PATHS[path][0])
+    What = oracle.dequant(p, s, group)
+    for m, j in enumerate((0, 33, inf - 1)):
+        assert np.array_equal(Y[m], What[:, j].astype(np.float16).astype(np.float64))
+
+
+def test_gemm_empty_inputs():
+    p = torch.zeros((2, 8, 0), dtype=torch.int32, device=dev())
+    s = torch.zeros((2, 8, 0), dtype=torch.float16, device=dev())
+    X = torch.zeros((3, 0), dtype=torch.float16, device=dev())
+    Y = torch.full((3, 8), 7.0, dtype=torch.float16, device=dev())
+    rbq.gemm(p, s, X, 0, Y=Y)
+    torch.cuda.synchronize()
+    assert (Y == 0).all()
+    p2 = torch.zeros((2, 8, 4), dtype=torch.int32, device=dev())
+    s2 = torch.zeros((2, 8, 1), dtype=torch.float16, device=dev())
+    X0 = torch.zeros((0, 128), dtype=torch.float16, device=dev())
+    assert rbq.gemm(p2, s2, X0, 0).shape == (0, 8)
+
+
+def test_gemm_deterministic_on_side_stream():
+    wl, p, s = _encoded("llama2_7b", 4)
+    X = workloads.workload_activations(wl, 4096, 1)
+    pt = torch.from_numpy(p.view(np.int32)).to(dev())
+    st = torch.from_numpy(s.view(np.float16)).to(dev())
+    xt = torch.from_numpy(X.view(np.float16)).to(dev())
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y1 = rbq.gemm(pt, st, xt)
+        y2 = rbq.gemm(pt, st, xt)
+    side.synchronize()
+    assert torch.equal(y1, y2)
