@@ -26,7 +26,7 @@ RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_ENCODE_FORCE_SERIAL = 1
 
-PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL = 0, 1, 2, 3
+PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM = 0, 1, 2, 3, 4
 
 
 class RbqLibraryMissing(RuntimeError):
@@ -68,6 +68,7 @@ _SIGNATURES = {
                                 ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
+    "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
     "rbq_last_hip_error": (ctypes.c_int32, []),
     "rbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rbq_version": (ctypes.c_char_p, []),
@@ -129,6 +130,14 @@ def check(st: int, what: str) -> None:
 def set_path(path: int) -> int:
     """Force a kernel family for rbq_gemm (PATH_*); returns the old setting."""
     return int(lib().rbq_set_path(int(path)))
+
+
+def set_stream_split(waves_per_tile: int) -> int:
+    """Waves per 16-row tile in the streaming kernel (0 = automatic)."""
+    old = int(lib().rbq_set_stream_split(int(waves_per_tile)))
+    if old < 0:
+        raise ValueError("waves_per_tile must be 0, 1, 2 or 4")
+    return old
 
 
 def select_path(s: Shape, M: int) -> int:

@@ -13,6 +13,7 @@ namespace {
 
 thread_local int32_t g_last_hip_error = 0;
 std::atomic<int> g_forced_path{RBQ_PATH_AUTO};
+std::atomic<int> g_stream_split{0};
 
 rbq_status hip_fail(hipError_t e) {
     g_last_hip_error = (int32_t)e;
@@ -106,9 +107,17 @@ rbq_path rbq_set_path(rbq_path p) {
     return (rbq_path)g_forced_path.exchange((int)p);
 }
 
+int32_t rbq_set_stream_split(int32_t waves_per_tile) {
+    if (waves_per_tile != 0 && waves_per_tile != 1 && waves_per_tile != 2 && waves_per_tile != 4)
+        return -1;
+    return g_stream_split.exchange(waves_per_tile);
+}
+
 rbq_path rbq_select_path(rbq_shape s, int32_t M) {
-    (void)s;
-    (void)M;
+    if (rbq::stream_supports(s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_STREAM;
+    if (M <= 16 && rbq::decode_supports(s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_DECODE;
     return RBQ_PATH_VALU;
 }
 
@@ -149,6 +158,18 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
     case RBQ_PATH_VALU:
         e = rbq::launch_gemm_valu(planes, scales, s.out_features, s.in_features, s.num_planes,
                                   s.group_size, X, M, Y, hs);
+        break;
+    case RBQ_PATH_DECODE:
+        if (!rbq::decode_supports(s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        e = rbq::launch_gemm_decode(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                    s.group_size, X, M, Y, hs);
+        break;
+    case RBQ_PATH_STREAM:
+        if (!rbq::stream_supports(s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        e = rbq::launch_gemm_stream(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                    s.group_size, X, M, Y, hs, g_stream_split.load());
         break;
     default:
         return RBQ_ERR_UNSUPPORTED;

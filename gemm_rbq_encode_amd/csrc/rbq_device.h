@@ -86,3 +86,61 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 }  // namespace rbq
+
+namespace rbq {
+
+// DPP controls (GFX9): row_shr:n, row_shl:n, row_bcast:15, row_bcast:31.
+#define RBQ_DPP_ROW_SHR(n) (0x110 + (n))
+#define RBQ_DPP_ROW_SHL(n) (0x100 + (n))
+#define RBQ_DPP_ROW_BCAST15 0x142
+#define RBQ_DPP_ROW_BCAST31 0x143
+
+// Value of lane (lane + n) inside the same row of 16 lanes (n = 1 or 2);
+// lanes whose source falls outside the row get 0.
+template <int N>
+__device__ __forceinline__ int row_shl_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHL(N), 0xF, 0xF, false);
+}
+
+// Whole-wave sum of an int, returned to every lane (DPP row shifts, row
+// broadcasts, then lane 63).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHR(1), 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHR(2), 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHR(4), 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHR(8), 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_BCAST15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_BCAST31, 0xC, 0xF, false);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_add_f32(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, x), CTRL, RMASK, 0xF, false));
+}
+
+// Whole-wave sum of a float, returned to every lane.
+__device__ __forceinline__ float wave_sum_f32_dpp(float v) {
+    v = dpp_add_f32<RBQ_DPP_ROW_SHR(1), 0xF>(v);
+    v = dpp_add_f32<RBQ_DPP_ROW_SHR(2), 0xF>(v);
+    v = dpp_add_f32<RBQ_DPP_ROW_SHR(4), 0xF>(v);
+    v = dpp_add_f32<RBQ_DPP_ROW_SHR(8), 0xF>(v);
+    v = dpp_add_f32<RBQ_DPP_ROW_BCAST15, 0xA>(v);
+    v = dpp_add_f32<RBQ_DPP_ROW_BCAST31, 0xC>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Whole-wave maximum of an unsigned int, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    int x = (int)v;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_SHR(1), 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_SHR(2), 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_SHR(4), 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_SHR(8), 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_BCAST15, 0xA, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, RBQ_DPP_ROW_BCAST31, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
+}  // namespace rbq

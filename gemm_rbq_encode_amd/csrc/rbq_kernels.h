@@ -16,6 +16,21 @@ hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int 
                             int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                             hipStream_t st);
 
+// int8-MFMA decode kernel (per-row scales, K <= 4, in % 128 == 0); M is
+// processed in passes of 5 tokens.
+bool decode_supports(int in, int K, int group_size, int M);
+hipError_t launch_gemm_decode(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                              int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                              hipStream_t st);
+
+// Whole-row streaming int8-MFMA kernel for 1-2 tokens (per-row scales,
+// K <= 4, in % 128 == 0, activation image of in*3*M bytes in LDS).  split =
+// waves per 16-row tile (1, 2 or 4), 0 = chosen from the tile count.
+bool stream_supports(int in, int K, int group_size, int M);
+hipError_t launch_gemm_stream(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                              int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                              hipStream_t st, int split);
+
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);
 

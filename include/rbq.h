@@ -134,7 +134,7 @@ rbq_status rbq_encode_ex(const float *W, rbq_shape s, uint32_t *planes, uint16_t
  *                   aligned, scales 2-byte aligned; any finite fp16 scales
  *   X               device, fp16 [M][in], 16-byte aligned
  *   M               tokens, >= 0 (0 enqueues nothing)
- *   Y               device, fp16 [M][out], 4-byte aligned, written
+ *   Y               device, fp16 [M][out], 2-byte aligned, written
  *   workspace       device scratch of ws_bytes >= rbq_gemm_workspace_bytes
  *                   (may be NULL when that is 0); contents on return are
  *                   unspecified
@@ -158,14 +158,23 @@ rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
 typedef enum rbq_path {
     RBQ_PATH_AUTO = 0,
     RBQ_PATH_VALU = 1,      /* plain fp32 VALU bit loop, any M */
-    RBQ_PATH_DECODE = 2,    /* int8 MFMA on unpacked bits, M <= 16 */
-    RBQ_PATH_PREFILL = 3    /* fp16 MFMA on LDS-unpacked weights, large M */
+    RBQ_PATH_DECODE = 2,    /* int8 MFMA on masked bits, 512-column chunks split over
+                               8 waves, 5 tokens per pass */
+    RBQ_PATH_PREFILL = 3,   /* fp16 MFMA on LDS-unpacked weights, large M */
+    RBQ_PATH_STREAM = 4     /* int8 MFMA, whole rows streamed per wave: M <= 2, K <= 2,
+                               in <= 16384 */
 } rbq_path;
 
 /* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for
  * tests and A/B measurement).  A forced path that cannot take a call makes
  * that call return RBQ_ERR_UNSUPPORTED.  Returns the previous setting. */
 rbq_path rbq_set_path(rbq_path p);
+
+/* Waves that share one 16-row tile in RBQ_PATH_STREAM (1, 2 or 4; 0 = chosen
+ * from the number of tiles, the default).  For tuning and A/B measurement;
+ * results do not depend on it beyond fp32 rounding.  Returns the previous
+ * setting, or -1 (and changes nothing) for any other value. */
+int32_t rbq_set_stream_split(int32_t waves_per_tile);
 
 /* The kernel family rbq_gemm would take for this shape and M. */
 rbq_path rbq_select_path(rbq_shape s, int32_t M);

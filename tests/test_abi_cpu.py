@@ -104,6 +104,14 @@ def test_path_override_roundtrip():
         assert rbq.set_path(rbq.PATH_AUTO) == rbq.PATH_VALU
     finally:
         rbq.set_path(old)
+    assert rbq.set_stream_split(2) == 0
+    assert rbq.set_stream_split(0) == 2
+    with pytest.raises(ValueError):
+        rbq.set_stream_split(3)
+    L = rbq.lib()
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 1) == rbq.PATH_STREAM
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 4) == rbq.PATH_DECODE
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 8), 1) == rbq.PATH_VALU
 
 
 def test_binding_refuses_host_tensors():
