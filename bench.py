@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--split", type=int, default=0,
                     help="waves per 16-row tile in the streaming kernel (0 = automatic)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--workload", default="llama2_7b",
+                    choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
+                    help="the default is the headline decode GEMV; the others print their own line")
+    ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
     return ap.parse_args()
 
 
@@ -65,7 +69,147 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU path is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "llama2_7b":
+        bench_decode(args)
+    else:
+        bench_layer_set(args)
 
+
+def graph_launch_us(torch, dev, fns, reps):
+    """Mean device time per launch (us) of the launches `fns`: they are
+    captured once in a HIP graph on a side stream and the graph is replayed
+    `reps` times between two HIP events recorded on that same stream, so the
+    host never sits between two launches."""
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        graph.replay()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(side)
+        for _ in range(reps):
+            graph.replay()
+        b.record(side)
+    b.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(fns))
+
+
+def bench_layer_set(args):
+    """Skinny, grouped-scale and prefill workloads: each linear of the set is
+    run back to back (one launch each) over a rotation of encoded copies;
+    reports algorithmic GB/s (decode-like sets) or dense-equivalent TFLOP/s
+    (prefill), and the per-launch device time from HIP events."""
+    import torch
+
+    import gemm_rbq_encode_amd as rbq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS[args.workload]
+    K, group = wl.num_planes, wl.group_size
+    M = args.tokens or max(wl.tokens)
+    stream = torch.cuda.current_stream(dev)
+    # distinct shapes only (q/k/v/o and gate/up share shapes)
+    uniq = []
+    for i, lin in enumerate(wl.linears):
+        if all((lin.out_features, lin.in_features) != (l.out_features, l.in_features) for _, l in uniq):
+            uniq.append((i, lin))
+    prefill = args.workload == "llama3_8b_prefill"
+    rot = 2 if prefill else max(2, int(2.0e9 // sum(
+        K * l.out_features * l.in_features // 8 for _, l in uniq)))
+    sets = []
+    for i, lin in uniq:
+        W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
+        p, sc = rbq.encode(W, K, group)
+        del W
+        X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
+        Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
+        copies = [(p.clone(), sc.clone()) for _ in range(rot)]
+        sets.append((lin, copies, X, Y))
+    torch.cuda.synchronize()
+    path = rbq.select_path(rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
+    names = {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
+             rbq.PATH_STREAM: "stream"}
+    launches = []
+    for r in range(max(args.kernel_reps, 1) * (2 if prefill else 8)):
+        for lin, copies, X, Y in sets:
+            p, sc = copies[r % rot]
+            launches.append((f"{lin.out_features}x{lin.in_features}",
+                             (lambda p=p, sc=sc, X=X, Y=Y: rbq.gemm(p, sc, X, group, Y=Y))))
+    for _, fn in launches[:len(sets) * 2]:
+        fn()
+    torch.cuda.synchronize()
+    # whole-set wall time: one pass over every shape and rotation copy,
+    # captured in a HIP graph and replayed (launch cost off the host)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _, fn in launches[:len(sets) * rot]:
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / (args.steps * rot)   # one pass over the shapes
+    mean_us = {}
+    for lin, copies, X, Y in sets:
+        key = f"{lin.out_features}x{lin.in_features}"
+        fns = [(lambda p=p, sc=sc, X=X, Y=Y: rbq.gemm(p, sc, X, group, Y=Y)) for p, sc in copies]
+        mean_us[key] = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1))
+    per_shape = {}
+    tot_bytes = tot_flop = tot_us = 0.0
+    for lin, _, _, _ in sets:
+        key = f"{lin.out_features}x{lin.in_features}"
+        G = lin.in_features // group if group else 1
+        nbytes = gemv_bytes(lin.out_features, lin.in_features, K, G, M)
+        flop = 2.0 * M * lin.out_features * lin.in_features
+        us = mean_us[key]
+        per_shape[key] = {"bytes": nbytes, "mean_us": round(us, 3),
+                          "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "TFLOPs_dense_eq": round(flop / (us * 1e-6) / 1e12, 2)}
+        tot_bytes += nbytes
+        tot_flop += flop
+        tot_us += us
+    if prefill:
+        metric = "prefill dense-equivalent TFLOP/s (2*M*out*in / t), fp16 MFMA"
+        value = tot_flop / wall / 1e12
+        unit = "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(tot_flop / (tot_us * 1e-6) / 1e12, 2),
+                "peak": 2500.0, "unit": "TFLOP/s"}
+    else:
+        metric = f"K={K} batch-{M} GEMM effective GB/s on {wl.name} layers"
+        value = tot_bytes / wall / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": round(tot_bytes / (tot_us * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = f"rbq gemm ({names[path]})"
+    roof["per_shape"] = per_shape
+    line = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16" if names[path] == "prefill" else ("i8" if names[path] != "valu" else "f32"),
+            "data": "synthetic",
+            "config": {"workload": wl.name, "linears": [f"{l.out_features}x{l.in_features}" for _, l in uniq],
+                       "num_planes": K, "group_size": group, "tokens": M, "rotation": rot,
+                       "path": names[path]},
+            "roofline": roof, "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(args):
     import torch
 
     import gemm_rbq_encode_amd as rbq
@@ -161,34 +305,42 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # ---- per-launch kernel timing with HIP events on the launch stream
+    # ---- per-launch device time of each shape: its launches over all layers
+    # in one graph, replayed between two HIP events on the launch stream
     nlin = len(wl.linears)
-    evs = []
-    for rep in range(args.kernel_reps):
-        for pp, sp, sh, xp, yp, i in calls:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            rc = L.rbq_gemv(pp, sp, sh, xp, yp, stream.cuda_stream)
-            b.record(stream)
-            if rc != 0:
-                raise rbq.RbqError(rc, "rbq_gemv")
-            evs.append((i, a, b))
-    torch.cuda.synchronize()
-    dur = [[] for _ in range(nlin)]
-    for i, a, b in evs:
-        dur[i].append(a.elapsed_time(b) * 1e3)          # microseconds
-    mean_us = [float(np.mean(d)) for d in dur]
-    # the GEMV kernel over all its launches (one kernel family serves every shape)
-    tot_bytes = sum(per_call)
+    mean_us = [0.0] * nlin
+    seen = {}
+    for i, lin in enumerate(wl.linears):
+        key = (lin.out_features, lin.in_features)
+        if key in seen:
+            mean_us[i] = mean_us[seen[key]]
+            continue
+        seen[key] = i
+        fns = []
+        for layer in layers:
+            p, s = layer[i]
+            fns.append(lambda pp=p.data_ptr(), sp=s.data_ptr(), sh=shapes[i],
+                       xp=xs[lin.in_features].data_ptr(), yp=ys[i].data_ptr():
+                       L.rbq_gemv(pp, sp, sh, xp, yp, torch.cuda.current_stream(dev).cuda_stream))
+        mean_us[i] = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1) * 4)
+    # the dominant kernel: the shape with the largest share of a step
+    share = {}
+    for i, lin in enumerate(wl.linears):
+        key = f"{lin.out_features}x{lin.in_features}"
+        share[key] = share.get(key, 0.0) + mean_us[i]
+    dom = max(share, key=share.get)
+    dom_i = [i for i, l in enumerate(wl.linears) if f"{l.out_features}x{l.in_features}" == dom][0]
+    achieved = per_call[dom_i] / (mean_us[dom_i] * 1e-6) / 1e9
     tot_us = sum(mean_us)
-    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     per_shape = {}
     for i, lin in enumerate(wl.linears):
         key = f"{lin.out_features}x{lin.in_features}"
         if key not in per_shape:
             per_shape[key] = {"bytes": per_call[i], "mean_us": round(mean_us[i], 3),
-                              "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1)}
+                              "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1),
+                              "launches_per_layer": sum(
+                                  1 for l in wl.linears
+                                  if (l.out_features, l.in_features) == (lin.out_features, lin.in_features))}
 
     # ---- CPU oracle baseline on a bounded sample (layer 0, one token)
     cpu = None
@@ -232,8 +384,10 @@ def main():
                    "path": path_name, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": f"rbq gemv ({path_name})",
-                     "mean_launch_us": round(tot_us / nlin, 3), "per_shape": per_shape},
+                     "traffic": None, "kernel": f"rbq gemv ({path_name}) {dom}",
+                     "bytes_per_launch": per_call[dom_i], "mean_launch_us": round(mean_us[dom_i], 3),
+                     "layer_GBps_from_launch_times": round(sum(per_call) / (tot_us * 1e-6) / 1e9, 1),
+                     "per_shape": per_shape},
         "cpu_baseline": cpu,
         "encode": {"linears": nlin, "ms": round(enc_ms, 4),
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},

@@ -118,6 +118,8 @@ rbq_path rbq_select_path(rbq_shape s, int32_t M) {
         return RBQ_PATH_STREAM;
     if (M <= 16 && rbq::decode_supports(s.in_features, s.num_planes, s.group_size, M))
         return RBQ_PATH_DECODE;
+    if (M > 16 && rbq::prefill_supports(s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_PREFILL;
     return RBQ_PATH_VALU;
 }
 
@@ -164,6 +166,12 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
             return RBQ_ERR_UNSUPPORTED;
         e = rbq::launch_gemm_decode(planes, scales, s.out_features, s.in_features, s.num_planes,
                                     s.group_size, X, M, Y, hs);
+        break;
+    case RBQ_PATH_PREFILL:
+        if (!rbq::prefill_supports(s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        e = rbq::launch_gemm_prefill(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                     s.group_size, X, M, Y, hs);
         break;
     case RBQ_PATH_STREAM:
         if (!rbq::stream_supports(s.in_features, s.num_planes, s.group_size, M))

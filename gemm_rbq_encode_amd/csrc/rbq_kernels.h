@@ -31,6 +31,12 @@ hipError_t launch_gemm_stream(const uint32_t *planes, const uint16_t *scales, in
                               int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                               hipStream_t st, int split);
 
+// fp16-MFMA prefill GEMM over LDS-unpacked What (in % 64 == 0, K <= 4).
+bool prefill_supports(int in, int K, int group_size, int M);
+hipError_t launch_gemm_prefill(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                               int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                               hipStream_t st);
+
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);
 
