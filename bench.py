@@ -1,8 +1,12 @@
 """Benchmark: K=2 batch-1 GEMV on the Llama-2-7B decoder linears.
 
 One step is one decode token through the seven linears (q, k, v, o 4096x4096;
-gate, up 11008x4096; down 4096x11008) of each of 32 layers: 224 rbq_gemv
-calls, captured once in a HIP graph and replayed.  Each layer has its own
+gate, up 11008x4096; down 4096x11008) of each of 32 layers, captured once in
+a HIP graph and replayed.  By default q, k, v are stacked row-wise into one
+12288x4096 matrix and gate, up into one 22016x4096 matrix, as decode engines
+lay them out (4 rbq_gemv launches per layer, 128 per step; every row is
+encoded on its own, so the stacked encoding is exactly the separate ones);
+--layout separate runs the 7 linears as 224 launches.  Each layer has its own
 copy of the encoded planes and scales (1.63 GB in total, far more than the
 L2 and Infinity Cache), so every step streams the weights from HBM.  The
 weights are seeded synthetic N(0, 0.02^2) matrices with 0.1 % outliers x20,
@@ -56,6 +60,9 @@ def parse():
     ap.add_argument("--split", type=int, default=0,
                     help="waves per 16-row tile in the streaming kernel (0 = automatic)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--layout", choices=["fused", "separate"], default="fused",
+                    help="fused: q/k/v stacked into one 12288x4096 matrix and gate/up into one "
+                         "22016x4096 matrix (4 launches per layer); separate: 7 launches per layer")
     ap.add_argument("--workload", default="llama2_7b",
                     choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
@@ -244,26 +251,44 @@ def bench_decode(args):
     torch.cuda.synchronize()
     enc_ms = sum(a.elapsed_time(b) for a, b in enc_ev)
 
+    # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
+    # into one matrix: rows are encoded independently, so the stacked planes
+    # and scales are exactly the separate ones placed one after another.
+    if args.layout == "fused":
+        groups = [("qkv_proj", [0, 1, 2]), ("o_proj", [3]), ("gate_up_proj", [4, 5]),
+                  ("down_proj", [6])]
+    else:
+        groups = [(lin.name, [i]) for i, lin in enumerate(wl.linears)]
+    g_planes, g_scales, g_shapes, g_in = [], [], [], []
+    for name, idx in groups:
+        p = torch.cat([enc_planes[i] for i in idx], dim=1).contiguous()
+        s = torch.cat([enc_scales[i] for i in idx], dim=1).contiguous()
+        g_planes.append(p)
+        g_scales.append(s)
+        g_shapes.append(rbq.shape(p.shape[1], p.shape[2] * 32, K, group))
+        g_in.append(p.shape[2] * 32)
+    del enc_planes, enc_scales
+
     # ---- rotation set: one copy of planes and scales per layer
     layers = []
     for layer in range(args.layers):
-        layers.append([(p.clone(), s.clone()) for p, s in zip(enc_planes, enc_scales)])
+        layers.append([(p.clone(), s.clone()) for p, s in zip(g_planes, g_scales)])
     torch.cuda.synchronize()
     xs = {}
-    for lin in wl.linears:
-        if lin.in_features not in xs:
-            xa = workloads.workload_activations(wl, lin.in_features, 1)
-            xs[lin.in_features] = torch.from_numpy(xa.view(np.float16)[0].copy()).to(dev)
-    ys = [torch.empty(lin.out_features, dtype=torch.float16, device=dev) for lin in wl.linears]
+    for n_in in g_in:
+        if n_in not in xs:
+            xa = workloads.workload_activations(wl, n_in, 1)
+            xs[n_in] = torch.from_numpy(xa.view(np.float16)[0].copy()).to(dev)
+    ys = [torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in g_shapes]
 
-    shapes = [rbq.shape(lin.out_features, lin.in_features, K, group) for lin in wl.linears]
-    per_call = [gemv_bytes(lin.out_features, lin.in_features, K, 1) for lin in wl.linears]
+    shapes = g_shapes
+    per_call = [gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in g_shapes]
     bytes_per_step = sum(per_call) * args.layers
     calls = []
     for layer in layers:
         for i, (p, s) in enumerate(layer):
-            calls.append((p.data_ptr(), s.data_ptr(), shapes[i],
-                           xs[wl.linears[i].in_features].data_ptr(), ys[i].data_ptr(), i))
+            calls.append((p.data_ptr(), s.data_ptr(), shapes[i], xs[g_in[i]].data_ptr(),
+                          ys[i].data_ptr(), i))
 
     def step(st_handle):
         for pp, sp, sh, xp, yp, _ in calls:
@@ -305,55 +330,41 @@ def bench_decode(args):
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # ---- per-launch device time of each shape: its launches over all layers
-    # in one graph, replayed between two HIP events on the launch stream
-    nlin = len(wl.linears)
+    # ---- per-launch device time of each launch group: its launches over all
+    # layers in one graph, replayed between two HIP events on the launch stream
+    nlin = len(groups)
     mean_us = [0.0] * nlin
-    seen = {}
-    for i, lin in enumerate(wl.linears):
-        key = (lin.out_features, lin.in_features)
-        if key in seen:
-            mean_us[i] = mean_us[seen[key]]
-            continue
-        seen[key] = i
+    for i in range(nlin):
         fns = []
         for layer in layers:
             p, s = layer[i]
             fns.append(lambda pp=p.data_ptr(), sp=s.data_ptr(), sh=shapes[i],
-                       xp=xs[lin.in_features].data_ptr(), yp=ys[i].data_ptr():
+                       xp=xs[g_in[i]].data_ptr(), yp=ys[i].data_ptr():
                        L.rbq_gemv(pp, sp, sh, xp, yp, torch.cuda.current_stream(dev).cuda_stream))
         mean_us[i] = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1) * 4)
-    # the dominant kernel: the shape with the largest share of a step
-    share = {}
-    for i, lin in enumerate(wl.linears):
-        key = f"{lin.out_features}x{lin.in_features}"
-        share[key] = share.get(key, 0.0) + mean_us[i]
-    dom = max(share, key=share.get)
-    dom_i = [i for i, l in enumerate(wl.linears) if f"{l.out_features}x{l.in_features}" == dom][0]
+    # the dominant kernel: the launch group with the largest share of a step
+    dom_i = max(range(nlin), key=lambda i: mean_us[i])
+    dom = f"{groups[dom_i][0]} {shapes[dom_i].out_features}x{shapes[dom_i].in_features}"
     achieved = per_call[dom_i] / (mean_us[dom_i] * 1e-6) / 1e9
     tot_us = sum(mean_us)
     per_shape = {}
-    for i, lin in enumerate(wl.linears):
-        key = f"{lin.out_features}x{lin.in_features}"
-        if key not in per_shape:
-            per_shape[key] = {"bytes": per_call[i], "mean_us": round(mean_us[i], 3),
-                              "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1),
-                              "launches_per_layer": sum(
-                                  1 for l in wl.linears
-                                  if (l.out_features, l.in_features) == (lin.out_features, lin.in_features))}
+    for i, (name, _) in enumerate(groups):
+        per_shape[name] = {"shape": f"{shapes[i].out_features}x{shapes[i].in_features}",
+                           "bytes": per_call[i], "mean_us": round(mean_us[i], 3),
+                           "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1)}
 
     # ---- CPU oracle baseline on a bounded sample (layer 0, one token)
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        planes_np = [p.cpu().numpy().view(np.uint32) for p in enc_planes]
-        scales_np = [s.cpu().numpy().view(np.uint16) for s in enc_scales]
+        planes_np = [p.cpu().numpy().view(np.uint32) for p in g_planes]
+        scales_np = [s.cpu().numpy().view(np.uint16) for s in g_scales]
         xs_np = {k: v.cpu().numpy().view(np.uint16)[None, :] for k, v in xs.items()}
         t_start = time.perf_counter()
         done_bytes, reps = 0, 0
         while True:
-            for i, lin in enumerate(wl.linears):
-                oracle.gemm(planes_np[i], scales_np[i], xs_np[lin.in_features], group)
+            for i in range(nlin):
+                oracle.gemm(planes_np[i], scales_np[i], xs_np[g_in[i]], group)
                 done_bytes += per_call[i]
             reps += 1
             if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 50:
@@ -361,7 +372,7 @@ def bench_decode(args):
         el = time.perf_counter() - t_start
         cpu = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{reps} pass(es) over the 7 layer-0 linears at M=1 "
+               "sample": f"{reps} pass(es) over the layer-0 linears at M=1 "
                          f"(fp64 dequantize-and-multiply), {el:.1f} s"}
 
     line = {
@@ -379,6 +390,9 @@ def bench_decode(args):
         "data": "synthetic",
         "config": {"workload": "llama2_7b_decode_gemv", "layers": args.layers,
                    "linears": [f"{l.name} {l.out_features}x{l.in_features}" for l in wl.linears],
+                   "layout": args.layout,
+                   "launches_per_layer": {name: f"{sh.out_features}x{sh.in_features}"
+                                          for (name, _), sh in zip(groups, shapes)},
                    "num_planes": K, "group_size": group, "tokens": 1,
                    "bytes_per_step": bytes_per_step, "graph": graph is not None,
                    "path": path_name, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
@@ -389,7 +403,7 @@ def bench_decode(args):
                      "layer_GBps_from_launch_times": round(sum(per_call) / (tot_us * 1e-6) / 1e9, 1),
                      "per_shape": per_shape},
         "cpu_baseline": cpu,
-        "encode": {"linears": nlin, "ms": round(enc_ms, 4),
+        "encode": {"linears": len(wl.linears), "ms": round(enc_ms, 4),
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
     }
     print(json.dumps(line), flush=True)

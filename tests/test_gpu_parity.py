@@ -312,3 +312,15 @@ def test_stream_splits_agree(split, i, M):
     finally:
         rbq.set_stream_split(old)
     assert_close(Y, oracle.gemm(p, s, X, wl.group_size), f"split {split}")
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("idx", [(0, 1, 2), (4, 5)])
+def test_gemv_fused_llama2_7b(path, idx):
+    """The stacked q/k/v (12288x4096) and gate/up (22016x4096) matrices."""
+    wl = workloads.WORKLOADS["llama2_7b"]
+    W = np.concatenate([workloads.workload_weight(wl, i) for i in idx])
+    p, s = assert_encode_matches(W, wl.num_planes, wl.group_size, what=f"fused {idx}")
+    X = workloads.workload_activations(wl, 4096, 1)
+    Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
+    assert_close(Y, oracle.gemm(p, s, X, wl.group_size), f"fused {idx}")

@@ -372,3 +372,16 @@ def test_scale_rounds_once_in_encoder():
     assert sum(Fraction(v) for v in row) / 32 == 1 + Fraction(1, 2 ** 11) + Fraction(1, 2 ** 30)
     _, scales, _ = oracle.encode(W, 1, 0)
     assert scales[0, 0, 0] == 0x3C01
+
+
+def test_row_stacking_commutes_with_encoding():
+    """Per-row scales make rows independent: encoding [W1; W2] gives the
+    planes and scales of W1 and W2 stacked (the fused q/k/v and gate/up
+    layouts rely on this)."""
+    W1 = workloads.gaussian_weight(40, 512, seed=1, outliers=True)
+    W2 = workloads.gaussian_weight(24, 512, seed=2, outliers=True)
+    p, s, _ = oracle.encode(np.concatenate([W1, W2]), 2, 0)
+    p1, s1, _ = oracle.encode(W1, 2, 0)
+    p2, s2, _ = oracle.encode(W2, 2, 0)
+    assert np.array_equal(p, np.concatenate([p1, p2], axis=1))
+    assert np.array_equal(s, np.concatenate([s1, s2], axis=1))
