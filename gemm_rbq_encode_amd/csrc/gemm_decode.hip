@@ -74,7 +74,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
     __shared__ float red[DEC_WAVES][MT][TILE_ROWS];
 
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
-    const int wave = threadIdx.x / RBQ_WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE);
     const int row0 = blockIdx.x * TILE_ROWS;
     const int m0 = blockIdx.y * MT;
     const int mt = min(M - m0, MT);                 // tokens in this pass
@@ -87,8 +87,10 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
 
     const int li = lane & 15;        // A row / B column inside the MFMA
     const int lg = lane >> 4;        // lane group: k-slice of the MFMA
-    const int row = row0 + li;
-    const bool row_ok = row < out;
+    // rows past the end read the last row (their outputs are never stored):
+    // loads carry no per-lane guard, which would make the compiler wait for
+    // every outstanding load where the guarded and unguarded paths meet
+    const int row = min(row0 + li, out - 1);
     const int my_m = li / 3;         // token whose high limb this lane's column holds
     const bool owner = (li % 3 == 0) && li < NC;
     // B-register source of this lane: its column's image, or the zero pad
@@ -101,8 +103,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
     for (int k = 0; k < K; ++k)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int r = row0 + 4 * lg + v;
-            a[k][v] = (r < out) ? h2f(scales[(size_t)k * out + r]) : 0.0f;
+            const int r = min(row0 + 4 * lg + v, out - 1);
+            a[k][v] = h2f(scales[(size_t)k * out + r]);
         }
     float yacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -118,23 +120,22 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
         uint4 xv[CPW][MT];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
-            const int c = base + DEC_WAVES * cc;
-            const int wi = c * CHUNK_WORDS + 4 * lg;
+            // chunks past the row are never multiplied; words past the row
+            // meet zero activations in the image
+            const int c = min(base + DEC_WAVES * cc, nchunks - 1);
+            const int wi = min(c * CHUNK_WORDS + 4 * lg, words - 4);
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (c < nchunks && row_ok && wi < words)
-                    wv[cc][k] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(
-                        planes + ((size_t)k * out + row) * words + wi));
-                else
-                    wv[cc][k] = (v4u){0u, 0u, 0u, 0u};
-            }
+            for (int k = 0; k < K; ++k)
+                wv[cc][k] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(
+                    planes + ((size_t)k * out + row) * words + wi));
             const int col = c * CHUNK_COLS + 8 * lane;
+            const int colc = min(col, in - 8);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if (c < nchunks && m < mt && col < in)
-                    xv[cc][m] = *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + m) * in + col);
-                else
-                    xv[cc][m] = make_uint4(0, 0, 0, 0);
+                const uint4 u = *reinterpret_cast<const uint4 *>(
+                    X + (size_t)(m0 + min(m, mt - 1)) * in + colc);
+                const bool ok = col < in;   // a select on the value, not a guarded load
+                xv[cc][m] = make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
             }
         }
 
