@@ -56,7 +56,7 @@ def parse():
                     help="passes over all layers for the per-launch kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream"], default="auto")
+    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream", "flat"], default="auto")
     ap.add_argument("--split", type=int, default=0,
                     help="waves per 16-row tile in the streaming kernel (0 = automatic)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
@@ -68,6 +68,11 @@ def parse():
                     help="the default is the headline decode GEMV; the others print their own line")
     ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
     return ap.parse_args()
+
+
+def path_names(rbq):
+    return {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
+            rbq.PATH_STREAM: "stream", rbq.PATH_FLAT: "flat"}
 
 
 def main():
@@ -141,8 +146,7 @@ def bench_layer_set(args):
         sets.append((lin, copies, X, Y))
     torch.cuda.synchronize()
     path = rbq.select_path(rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
-    names = {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
-             rbq.PATH_STREAM: "stream"}
+    names = path_names(rbq)
     launches = []
     for r in range(max(args.kernel_reps, 1) * (2 if prefill else 8)):
         for lin, copies, X, Y in sets:
@@ -228,7 +232,7 @@ def bench_decode(args):
     K, group = wl.num_planes, wl.group_size
     L = rbq.lib()
     path = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
-            "stream": rbq.PATH_STREAM}[args.path]
+            "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT}[args.path]
     rbq.set_path(path)
     rbq.set_stream_split(args.split)
 
@@ -296,9 +300,11 @@ def bench_decode(args):
             if rc != 0:
                 raise rbq.RbqError(rc, "rbq_gemv")
 
-    chosen = rbq.select_path(shapes[0], 1) if path == rbq.PATH_AUTO else path
-    path_name = {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
-                 rbq.PATH_STREAM: "stream"}[chosen]
+    names = path_names(rbq)
+    shape_paths = {f"{sh.out_features}x{sh.in_features}":
+                   names[rbq.select_path(sh, 1) if path == rbq.PATH_AUTO else path]
+                   for sh in shapes}
+    path_name = "+".join(sorted(set(shape_paths.values())))
 
     # ---- whole-job timing: graph replays (or eager steps)
     side = torch.cuda.Stream(dev)
@@ -395,10 +401,11 @@ def bench_decode(args):
                                           for (name, _), sh in zip(groups, shapes)},
                    "num_planes": K, "group_size": group, "tokens": 1,
                    "bytes_per_step": bytes_per_step, "graph": graph is not None,
-                   "path": path_name, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
+                   "path": path_name, "path_per_shape": shape_paths,
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": f"rbq gemv ({path_name}) {dom}",
+                     "traffic": None, "kernel": f"rbq gemv ({shape_paths[f'{shapes[dom_i].out_features}x{shapes[dom_i].in_features}']}) {dom}",
                      "bytes_per_launch": per_call[dom_i], "mean_launch_us": round(mean_us[dom_i], 3),
                      "layer_GBps_from_launch_times": round(sum(per_call) / (tot_us * 1e-6) / 1e9, 1),
                      "per_shape": per_shape},

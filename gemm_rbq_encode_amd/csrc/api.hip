@@ -114,6 +114,8 @@ int32_t rbq_set_stream_split(int32_t waves_per_tile) {
 }
 
 rbq_path rbq_select_path(rbq_shape s, int32_t M) {
+    if (rbq::flat_preferred(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_FLAT;
     if (rbq::stream_supports(s.in_features, s.num_planes, s.group_size, M))
         return RBQ_PATH_STREAM;
     if (M <= 16 && rbq::decode_supports(s.in_features, s.num_planes, s.group_size, M))
@@ -178,6 +180,12 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
             return RBQ_ERR_UNSUPPORTED;
         e = rbq::launch_gemm_stream(planes, scales, s.out_features, s.in_features, s.num_planes,
                                     s.group_size, X, M, Y, hs, g_stream_split.load());
+        break;
+    case RBQ_PATH_FLAT:
+        if (!rbq::flat_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        e = rbq::launch_gemm_flat(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                  s.group_size, X, M, Y, hs);
         break;
     default:
         return RBQ_ERR_UNSUPPORTED;

@@ -1,0 +1,518 @@
+// gemm_flat.hip -- residual-binary GEMV for a few tokens: one 16-wave
+// workgroup per compute unit, with the activation image built by 4 waves
+// while the other 12 already stream weights.
+//
+// y[m][r] = sum_k a_k[r] * (2 S_k - sum x), S_k = sum of x over the set bits
+// of row r of plane k ("RaBiT" summary, paperlayer.ai, sections 4.1 and 4.2:
+// binary cores with per-channel scales, the K paths side by side; D "GPU
+// implementation": 32 columns per word).  S_k is an exact integer product on
+// v_mfma_i32_16x16x64_i8:
+//   * each token is quantised once, q = round(x * 2^sh) with one power of two
+//     per token (|q| < 2^19), and split into three signed 7-bit limbs,
+//     q = l_0 + 2^7 l_1 + 2^14 l_2, l_j in [-64, 63];
+//   * the A operand is a masked weight word, w & (0x01010101 << s): byte kk
+//     holds bit 8kk + s of the word times 2^s (bit 7 reads as -128);
+//   * the B operand for bit position s holds the limbs of the matching
+//     columns times c_s = 2 (s even), 1 (s odd), -1 (s = 7), so that the
+//     products of bit positions 2j and 2j+1 both carry the weight 2^(2j+1)
+//     (and 2^7 for j = 3).  Four accumulators per plane, one per pair, give
+//     T = 64 acc_0 + 16 acc_1 + 4 acc_2 + acc_3 = 2^7 sum(bit * limb).
+//
+// Organisation.  A GEMV reads each weight byte once, so its time is the HBM
+// latency plus the bytes over the bandwidth -- if the memory is busy from
+// the start and the arithmetic keeps pace with the arrivals:
+//   * one workgroup per compute unit; workgroup b owns the 16-row tiles
+//     [b T / G, (b+1) T / G), whose (tile, 512-column chunk) units are split
+//     evenly, in order, over waves 4..15;
+//   * those stream waves request their first RING units at entry and then
+//     wait for the image; a wave whose loads exceed the memory queue stalls
+//     at the issue of the next load, which is why the image is left to
+//     waves 0..3, which request no weights: they load the activations, find
+//     the per-token maximum (meeting through an LDS counter), write the
+//     image and count themselves done in LDS;
+//   * a stream wave consumes a unit and requests the next one; the partial
+//     sums of a tile from several waves meet in LDS as int32 additions
+//     (exact, so the result does not depend on their order), and one
+//     thread per output row applies the scales.
+// The LDS waits are bounded; the waves they wait for belong to the same
+// workgroup, run concurrently and wait for nothing themselves.
+#include "rbq_device.h"
+#include "rbq_kernels.h"
+
+namespace rbq {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int FL_WAVES = 16;
+constexpr int FL_THREADS = FL_WAVES * RBQ_WAVE;
+constexpr int FL_PREP = 4;                            // waves that build the image
+constexpr int FL_PREP_THREADS = FL_PREP * RBQ_WAVE;
+constexpr int FL_STREAM = FL_WAVES - FL_PREP;         // waves that stream weights
+constexpr int TILE_ROWS = 16;
+constexpr int CHUNK_WORDS = 16;                       // 512 columns
+constexpr int IMG_PER_NC = 8 * 4 * 16;                // image bytes per chunk and MFMA column
+constexpr int NLIMB = 3;
+constexpr int FL_MAX_TOKENS = 5;                      // 3 limbs x 5 tokens <= 16 MFMA columns
+constexpr int FL_MAX_TILES = FL_THREADS / TILE_ROWS;  // one finishing thread per row
+constexpr int FL_MAX_XQ = 8;                          // 8-column loads per prep thread and token
+constexpr int FL_MAX_IN = FL_MAX_XQ * FL_PREP_THREADS * 8;
+constexpr int FL_SPIN_LIMIT = 1 << 22;                // bound of each LDS wait (never reached)
+
+// LDS bytes: activation image, 16 zero bytes, int32 partial sums, raw x
+// (two bytes per column of the padded row).
+size_t flat_lds_bytes(int in, int K, int mt, int tiles_per_wg) {
+    const size_t nchunks = (size_t)((in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS);
+    const size_t nc = (size_t)NLIMB * mt;
+    return nchunks * IMG_PER_NC * nc + 16 + (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4 +
+           (size_t)2 * mt * nchunks * CHUNK_WORDS * 32;
+}
+
+// Waits until the LDS counter reaches `target` (relaxed reads: the writers
+// release their LDS stores before counting, and LDS is coherent within the
+// compute unit).
+__device__ __forceinline__ void lds_wait_count(int *counter, int target) {
+    for (int i = 0; i < FL_SPIN_LIMIT; ++i) {
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+template <int K, int MT, int XQ, int RING>
+__global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
+    const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
+    const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ uint32_t wmax[MT][FL_PREP];
+    __shared__ float wsum[MT][FL_PREP];
+    __shared__ int shs[MT];
+    __shared__ int counters[2];       // prep waves past the maximum, past the image
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (RBQ_WAVE - 1);
+    // wave-uniform values in scalar registers: branches on them are scalar
+    // and loads under them carry no per-lane predicate
+    const int wave = __builtin_amdgcn_readfirstlane(tid / RBQ_WAVE);
+    const int li = lane & 15, lg = lane >> 4;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(M - m0, MT);
+    const int NC = NLIMB * mt;
+    const int words = in >> 5;
+    const int nchunks = (words + CHUNK_WORDS - 1) / CHUNK_WORDS;
+    const int img_chunk = IMG_PER_NC * NC;
+    const int pad = nchunks * img_chunk;            // 16 zero bytes for unused MFMA columns
+
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    const int G = gridDim.x;
+    const int t0 = (int)(((long)blockIdx.x * T) / G);
+    const int t1 = (int)(((long)(blockIdx.x + 1) * T) / G);
+    const int ntl = t1 - t0;
+    int *red = reinterpret_cast<int *>(lds + pad + 16);                         // [ntl][K][NC][16]
+    uint16_t *xs = reinterpret_cast<uint16_t *>(red + ntl * K * NC * TILE_ROWS);  // [mt][8][wpad][4]
+
+    // scales of the output row this thread finishes (requested after the
+    // activations or the first weights, whose waits must not include them)
+    const int frow = min(t0 * TILE_ROWS + tid, out - 1);
+    uint16_t a_bits[K];
+    auto load_scales = [&]() {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            a_bits[k] = scales[(size_t)k * out + frow];
+    };
+
+    // (no load is outstanding here, so the barrier waits for nothing else)
+    if (tid == 0)
+        counters[0] = counters[1] = 0;
+    for (int i = tid; i < ntl * K * NC * TILE_ROWS; i += FL_THREADS)
+        red[i] = 0;
+    if (tid < 4)
+        reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
+    __syncthreads();
+
+    if (wave < FL_PREP) {
+        // ================= image waves =================
+        // activations: thread q holds columns 8q .. 8q+7 of each token
+        const int xq_total = in >> 3;
+        uint4 xr[MT][XQ];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mc = min(m, mt - 1);
+#pragma unroll
+            for (int j = 0; j < XQ; ++j) {
+                const int q = min(tid + j * FL_PREP_THREADS, xq_total - 1);
+                xr[m][j] = *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + mc) * in + 8 * q);
+            }
+        }
+        load_scales();
+        const int wpad = nchunks * CHUNK_WORDS;
+        // per-token maximum of |x| (fp16 bit patterns without the sign
+        // compare like magnitudes); the raw rows into LDS
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            v2u16 mx2 = (v2u16){0, 0};
+#pragma unroll
+            for (int j = 0; j < XQ; ++j) {
+                // clamped repeats only repeat real values: harmless for a maximum
+                const uint4 u = xr[m][j];
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.x & 0x7FFF7FFFu));
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.y & 0x7FFF7FFFu));
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.z & 0x7FFF7FFFu));
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.w & 0x7FFF7FFFu));
+                // raw halves to xs[m][s][w][kk] (column 32w + 8kk + s), so that
+                // an image entry reads its four columns as one 8-byte word
+                const int q = tid + j * FL_PREP_THREADS;
+                if (m < mt && q < xq_total) {
+                    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+                    uint16_t *xd = xs + ((size_t)m * 8 * wpad + (q >> 2)) * 4 + (q & 3);
+#pragma unroll
+                    for (int h = 0; h < 8; ++h)
+                        xd[(size_t)h * wpad * 4] = (uint16_t)(uu[h >> 1] >> (16 * (h & 1)));
+                }
+            }
+            const uint32_t mx = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+            if (lane == 0)
+                wmax[m][wave] = mx;
+        }
+        if (lane == 0)
+            __hip_atomic_fetch_add(&counters[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_wait_count(&counters[0], FL_PREP);
+
+        // |x| < 2^E per token; q = round(x * 2^sh), sh = 19 - E (|q| < 2^19:
+        // the limbs reach -64 * 16513 .. 63 * 16513)
+        int sh[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int v = 0; v < FL_PREP; ++v)
+                mx = max(mx, wmax[m][v]);
+            const int e = (int)(mx >> 10);
+            sh[m] = 19 - ((e == 0 ? 1 : e) - 14);
+        }
+        // Image entry (word w, bit s): the four columns 32w + 8kk + s, kk =
+        // 0..3, one byte each, at [chunk w/16][s][lane group (w/4)%4][column
+        // n][4 (w%4) + kk].  Entries are taken s-major over the words rounded
+        // up to 64, so s is the same for a whole wave.  fma(x, 2^sh, 1.5*2^23)
+        // leaves q in the low mantissa bits; v = q + 64 (1 + 2^7 + 2^14) lies
+        // in [0, 2^21), and its 7-bit fields minus 64 are the
+        // limbs.  Words past the row end get zero limbs.
+        int psum[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            psum[m] = 0;
+        const int wp64 = (wpad + 63) & ~63;
+        for (int e = tid; e < 8 * wp64; e += FL_PREP_THREADS) {
+            // s is the same for the 64 entries of a wave (scalar division)
+            const int s = (__builtin_amdgcn_readfirstlane(e) >> 6) / (wp64 >> 6);
+            const int w = e - s * wp64;
+            if (w < wpad) {
+                const bool live = w < words;
+                const int wc = live ? w : 0;
+                unsigned char *dst = lds + (w / CHUNK_WORDS) * img_chunk + s * (4 * NC * 16) +
+                                     ((w >> 2) & 3) * (NC * 16) + (w & 3) * 4;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m < mt) {
+                        const float scale = __builtin_ldexpf(1.0f, sh[m]);
+                        uint32_t nb[NLIMB] = {0u, 0u, 0u};   // 7-bit fields, column kk in byte kk
+                        const uint2 hx = *reinterpret_cast<const uint2 *>(
+                            xs + (((size_t)m * 8 + s) * wpad + wc) * 4);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const uint16_t h = (uint16_t)((kk < 2 ? hx.x : hx.y) >> (16 * (kk & 1)));
+                            const float f = __builtin_fmaf(h2f(h), scale, 12582912.0f);
+                            // v = q + 0x102040 (fields of 64 past the row end: zero limbs)
+                            const uint32_t v = live ? __builtin_bit_cast(uint32_t, f) - 0x4B2FDFC0u : 0x102040u;
+                            psum[m] += (int)v - 0x102040;
+#pragma unroll
+                            for (int l = 0; l < NLIMB; ++l)
+                                nb[l] |= ((v >> (7 * l)) & 0x7Fu) << (8 * kk);
+                        }
+#pragma unroll
+                        for (int l = 0; l < NLIMB; ++l) {
+                            // bytes c_s * (n - 64), every n below 0x80
+                            uint32_t b;
+                            if (s == 7) {
+                                b = (0xC0C0C0C0u - nb[l]) ^ 0x80808080u;
+                            } else if ((s & 1) == 0) {
+                                b = (nb[l] << 1) ^ 0x80808080u;
+                            } else {
+                                const uint32_t t = nb[l] ^ 0x40404040u;
+                                b = t | ((t & 0x40404040u) << 1);
+                            }
+                            *reinterpret_cast<uint32_t *>(dst + (NLIMB * m + l) * 16) = b;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float ws = wave_sum_f32_dpp((float)psum[m]);   // sum of q over the wave's entries
+            if (lane == 0)
+                wsum[m][wave] = ws;
+            if (wave == 0 && lane == 0)
+                shs[m] = sh[m];
+        }
+        if (lane == 0)
+            __hip_atomic_fetch_add(&counters[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+        // ================= stream waves =================
+        const int sw = wave - FL_PREP;
+        const int U = ntl * nchunks;
+        const int u0 = (sw * U) / FL_STREAM;
+        const int u1 = ((sw + 1) * U) / FL_STREAM;
+        const int n = u1 - u0;
+        // loads past the wave's last unit repeat it (a wave without units
+        // repeats a neighbour's): every load is unconditional, since a load
+        // skipped on some path makes the compiler wait for all outstanding
+        // loads where the paths meet
+        const int ulast = max(min(u0, U - 1), u1 - 1);
+        const size_t plane_stride = (size_t)out * words;
+        // unit u -> (tile u / nchunks, chunk u % nchunks) with u * magic >> 21:
+        // exact for u < 2^11 and nchunks <= 32 (the error u * e / 2^21, e <
+        // nchunks, stays below 1 / nchunks)
+        const uint32_t magic = ((1u << 21) + nchunks - 1) / nchunks;
+        // Lane (li, lg) reads words 4lg .. 4lg+3 of the chunk in row li of
+        // the tile; rows past the end read the last row (never stored), words
+        // past the end of a row read the last four words and meet zeros in
+        // the image.  The address of load j comes from the clamped unit
+        // min(u0 + j, ulast) alone, so no load depends on a branch.
+        int lnext = u0;
+        v4u ring[RING][K];
+        auto load_unit = [&](v4u (&slot)[K]) {
+            const int u = min(lnext, ulast);
+            const int tq = (int)(((uint32_t)u * magic) >> 21);
+            const int row = min((t0 + tq) * TILE_ROWS + li, out - 1);
+            const int wi = min((u - tq * nchunks) * CHUNK_WORDS + 4 * lg, words - 4);
+            const uint32_t *p = planes + (size_t)row * words + wi;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                slot[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + k * plane_stride));
+            ++lnext;
+        };
+#pragma unroll
+        for (int d = 0; d < RING; ++d)
+            load_unit(ring[d]);
+        load_scales();
+        lds_wait_count(&counters[1], FL_PREP);
+
+        // acc[k][j] collects bit positions 2j and 2j+1 of plane k
+        v4i acc[K][4];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[k][j] = (v4i){0, 0, 0, 0};
+        const int b_off = (li < NC) ? (lg * NC + li) * 16 : pad;
+        const int b_stride = (li < NC) ? 4 * NC * 16 : 0;
+        const int b_chunk = (li < NC) ? img_chunk : 0;
+
+        int ptile = t0 + (int)(((uint32_t)u0 * magic) >> 21);
+        int pchunk = u0 - (ptile - t0) * nchunks;
+        auto chunk = [&](const v4u (&wv)[K]) {
+            const unsigned char *bp = lds + b_off + pchunk * b_chunk;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const v4i b = *reinterpret_cast<const v4i *>(bp + s * b_stride);
+                const uint32_t mask = 0x01010101u << s;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const v4i av = (v4i){(int)(wv[k].x & mask), (int)(wv[k].y & mask),
+                                         (int)(wv[k].z & mask), (int)(wv[k].w & mask)};
+                    acc[k][s >> 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, acc[k][s >> 1], 0, 0, 0);
+                }
+            }
+        };
+        // after unit i: move to the next chunk; at a tile's end or at the
+        // wave's last unit, add T into LDS.  Lane (li, lg) holds rows 4lg + v
+        // of MFMA column li.
+        auto step = [&](int i) {
+            const bool tile_end = ++pchunk == nchunks;
+            if (tile_end || i == n - 1) {
+                if (li < NC) {
+                    int *rp = red + (ptile - t0) * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int t = ((acc[k][0][v] * 4 + acc[k][1][v]) * 4 + acc[k][2][v]) * 4 +
+                                          acc[k][3][v];
+                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, t, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[k][j] = (v4i){0, 0, 0, 0};
+            }
+            if (tile_end) {
+                pchunk = 0;
+                ++ptile;
+            }
+        };
+        const int nbk = (n + RING - 1) / RING;
+        for (int bi = 0; bi + 1 < nbk; ++bi) {
+#pragma unroll
+            for (int d = 0; d < RING; ++d) {
+                // consume the slot, then refill it: the refill may reuse the
+                // slot's registers, so no copy of a pending load is kept
+                chunk(ring[d]);
+                load_unit(ring[d]);
+                step(bi * RING + d);
+            }
+        }
+        if (nbk > 0) {
+#pragma unroll
+            for (int d = 0; d < RING; ++d) {
+                const int i = (nbk - 1) * RING + d;
+                if (i < n) {
+                    chunk(ring[d]);
+                    step(i);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- one thread per output row.  Column 3m + l holds 2^7 sum(bit l_j);
+    // 2^7 sum(bit q) = T_0 + 2^7 T_1 + 2^14 T_2 (exact in fp64), and
+    // y = sum_k a_k (2 sum(bit q) - sum q) 2^-sh.
+    if (tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out) {
+        const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < mt) {
+                float sx = 0.0f;
+#pragma unroll
+                for (int v = 0; v < FL_PREP; ++v)
+                    sx += wsum[m][v];
+                float y = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
+                    const double t = (double)rp[0] + 128.0 * (double)rp[TILE_ROWS] +
+                                     16384.0 * (double)rp[2 * TILE_ROWS];
+                    y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx);
+                }
+                Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = f2h(__builtin_ldexpf(y, -shs[m]));
+            }
+        }
+    }
+}
+
+int flat_num_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+size_t flat_lds_limit() {
+    static size_t lim = 0;
+    if (lim == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 64 * 1024;
+        // the kernel's static LDS (maxima, sums, counters) comes on top
+        lim = (size_t)v - 512;
+    }
+    return lim;
+}
+
+int flat_grid(int out) {
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    return T < flat_num_cus() ? T : flat_num_cus();
+}
+
+template <int K, int MT, int XQ, int RING>
+hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                       const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+    const int G = flat_grid(out);
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    const int tpw = (T + G - 1) / G;
+    const int mt = M < MT ? M : MT;
+    const size_t lds = flat_lds_bytes(in, K, mt, tpw);
+    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XQ, RING>), dim3(G, (M + MT - 1) / MT),
+                       dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
+    return hipGetLastError();
+}
+
+#ifndef RBQ_FLAT_RING_MAX
+#define RBQ_FLAT_RING_MAX 4
+#endif
+
+// The ring covers a stream wave's whole share of units when it can.
+template <int K, int MT, int XQ>
+hipError_t launch_kmx(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+    const int G = flat_grid(out);
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+    const int per_wave = ((T + G - 1) / G * nchunks + FL_STREAM - 1) / FL_STREAM;
+    if (per_wave <= 2 || RBQ_FLAT_RING_MAX == 2)
+        return launch_kmxr<K, MT, XQ, 2>(planes, scales, out, in, X, M, Y, st);
+    if (per_wave <= 3 || RBQ_FLAT_RING_MAX == 3)
+        return launch_kmxr<K, MT, XQ, 3>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmxr<K, MT, XQ, 4>(planes, scales, out, in, X, M, Y, st);
+}
+
+template <int K, int MT>
+hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                     const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+    const int xq = (in / 8 + FL_PREP_THREADS - 1) / FL_PREP_THREADS;
+    if (xq <= 2)
+        return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, st);
+    if (xq <= 4)
+        return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmx<K, MT, 8>(planes, scales, out, in, X, M, Y, st);
+}
+
+}  // namespace
+
+bool flat_supports(int out, int in, int K, int group_size, int M) {
+    if (group_size != 0 || K < 1 || K > 2 || in % 128 != 0 || in <= 0 || in > FL_MAX_IN ||
+        M < 1 || M > 2 || out < 1)
+        return false;
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    const int G = flat_grid(out);
+    const int tpw = (T + G - 1) / G;
+    return tpw <= FL_MAX_TILES && flat_lds_bytes(in, K, M, tpw) <= flat_lds_limit();
+}
+
+// Measured on MI355X (fp16 in/out, K = 2, one token): ahead of the
+// whole-row streaming kernel when every compute unit gets at least two
+// 16-row tiles and the image build (4 waves, about 10 VALU operations per
+// column) stays short.
+bool flat_preferred(int out, int in, int K, int group_size, int M) {
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    return flat_supports(out, in, K, group_size, M) && T >= 2 * flat_num_cus() && in <= 8192;
+}
+
+hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            hipStream_t st) {
+    if (!flat_supports(out, in, K, group_size, M))
+        return hipErrorInvalidValue;
+    if (K == 1)
+        return M == 1 ? launch_km<1, 1>(planes, scales, out, in, X, M, Y, st)
+                      : launch_km<1, 2>(planes, scales, out, in, X, M, Y, st);
+    return M == 1 ? launch_km<2, 1>(planes, scales, out, in, X, M, Y, st)
+                  : launch_km<2, 2>(planes, scales, out, in, X, M, Y, st);
+}
+
+}  // namespace rbq

@@ -31,6 +31,16 @@ hipError_t launch_gemm_stream(const uint32_t *planes, const uint16_t *scales, in
                               int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                               hipStream_t st, int split);
 
+// One-workgroup-per-CU int8-MFMA GEMV for 1-2 tokens (per-row scales,
+// K <= 2, in % 128 == 0): 12 waves stream weight units while 4 build the
+// activation image; tile partial sums combined as int32 in LDS.
+bool flat_supports(int out, int in, int K, int group_size, int M);
+// Whether the flat kernel is the faster choice (many 16-row tiles per CU).
+bool flat_preferred(int out, int in, int K, int group_size, int M);
+hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            hipStream_t st);
+
 // fp16-MFMA prefill GEMM over LDS-unpacked What (in % 64 == 0, K <= 4).
 bool prefill_supports(int in, int K, int group_size, int M);
 hipError_t launch_gemm_prefill(const uint32_t *planes, const uint16_t *scales, int out, int in,

@@ -161,8 +161,12 @@ typedef enum rbq_path {
     RBQ_PATH_DECODE = 2,    /* int8 MFMA on masked bits, 512-column chunks split over
                                8 waves, 5 tokens per pass */
     RBQ_PATH_PREFILL = 3,   /* fp16 MFMA on LDS-unpacked weights, large M */
-    RBQ_PATH_STREAM = 4     /* int8 MFMA, whole rows streamed per wave: M <= 2, K <= 2,
+    RBQ_PATH_STREAM = 4,    /* int8 MFMA, whole rows streamed per wave: M <= 2, K <= 2,
                                in <= 16384 */
+    RBQ_PATH_FLAT = 5       /* int8 MFMA, one 16-wave workgroup per compute unit whose
+                               (tile, chunk) units are split evenly over 12 waves while
+                               4 build the activation image: M <= 2, K <= 2,
+                               in <= 16384; taken for layers of many rows */
 } rbq_path;
 
 /* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for
