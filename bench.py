@@ -67,6 +67,9 @@ def parse():
                     choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
     ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="for hardware-counter runs: a few eager launches of each decode shape "
+                         "(no graph, no timing), then a plain copy of known size")
     return ap.parse_args()
 
 
@@ -81,10 +84,75 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU path is not built.", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "llama2_7b":
+    if args.counter_pass:
+        counter_pass(args)
+    elif args.workload == "llama2_7b":
         bench_decode(args)
     else:
         bench_layer_set(args)
+
+
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "gemv_llama2_7b_decode_hbm_traffic.json")
+
+
+def measured_traffic(shape_key, path_name):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a copy
+    of known size) recorded for this shape, or None when there is no record or
+    the kernel's source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in doc.get("entries", []):
+        if e["shape"] != shape_key or not e["kernel"].startswith(f"gemm_{path_name}_kernel"):
+            continue
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gemm_rbq_encode_amd", "csrc",
+                           e["source"])
+        try:
+            with open(src, "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+        except OSError:
+            return None
+        return e["traffic_bytes"] if digest == e["source_sha256"] else None
+    return None
+
+
+def counter_pass(args):
+    """Launches for `rocprofv3 --pmc`: each fused decode shape of the
+    Llama-2-7B layer 8 times through rbq_gemv (rotating 8 encoded copies, so
+    no launch finds its planes in a cache), then torch copies of a 256 MiB
+    buffer, whose read bytes calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    import gemm_rbq_encode_amd as rbq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS["llama2_7b"]
+    K = wl.num_planes
+    for out_f, in_f in ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008)):
+        g = torch.Generator(device="cpu").manual_seed(out_f * 31 + in_f)
+        W = (torch.randn((out_f, in_f), generator=g) * 0.02).to(dev)
+        p, sc = rbq.encode(W, K, 0)
+        del W
+        copies = [(p.clone(), sc.clone()) for _ in range(8)]
+        x = torch.from_numpy(workloads.workload_activations(wl, in_f, 1).view(np.float16)).to(dev)[0]
+        for pp, ss in copies:
+            rbq.gemv(pp, ss, x)
+        torch.cuda.synchronize()
+        print(f"counter pass: {out_f}x{in_f} x8 "
+              f"({gemv_bytes(out_f, in_f, K, 1)} algorithmic bytes per launch)", flush=True)
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"counter pass: copy of {COPY_PROBE_BYTES} bytes x4", flush=True)
 
 
 def graph_launch_us(torch, dev, fns, reps):
@@ -352,6 +420,7 @@ def bench_decode(args):
     dom_i = max(range(nlin), key=lambda i: mean_us[i])
     dom = f"{groups[dom_i][0]} {shapes[dom_i].out_features}x{shapes[dom_i].in_features}"
     achieved = per_call[dom_i] / (mean_us[dom_i] * 1e-6) / 1e9
+    dom_key = f"{shapes[dom_i].out_features}x{shapes[dom_i].in_features}"
     tot_us = sum(mean_us)
     per_shape = {}
     for i, (name, _) in enumerate(groups):
@@ -405,7 +474,8 @@ def bench_decode(args):
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": f"rbq gemv ({shape_paths[f'{shapes[dom_i].out_features}x{shapes[dom_i].in_features}']}) {dom}",
+                     "traffic": measured_traffic(dom_key, shape_paths[dom_key]),
+                     "kernel": f"rbq gemv ({shape_paths[dom_key]}) {dom}",
                      "bytes_per_launch": per_call[dom_i], "mean_launch_us": round(mean_us[dom_i], 3),
                      "layer_GBps_from_launch_times": round(sum(per_call) / (tot_us * 1e-6) / 1e9, 1),
                      "per_shape": per_shape},
