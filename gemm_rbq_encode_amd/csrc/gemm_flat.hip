@@ -58,17 +58,21 @@ constexpr int IMG_PER_NC = 8 * 4 * 16;                // image bytes per chunk a
 constexpr int NLIMB = 3;
 constexpr int FL_MAX_TOKENS = 5;                      // 3 limbs x 5 tokens <= 16 MFMA columns
 constexpr int FL_MAX_TILES = FL_THREADS / TILE_ROWS;  // one finishing thread per row
-constexpr int FL_MAX_XQ = 8;                          // 8-column loads per prep thread and token
-constexpr int FL_MAX_IN = FL_MAX_XQ * FL_PREP_THREADS * 8;
+constexpr int FL_MAX_XP = 8;                          // column pairs per image thread and token
+constexpr int FL_MAX_IN = FL_MAX_XP * FL_PREP_THREADS * 8;   // 4 pairs per 32-column word
 constexpr int FL_SPIN_LIMIT = 1 << 22;                // bound of each LDS wait (never reached)
 
-// LDS bytes: activation image, 16 zero bytes, int32 partial sums, raw x
-// (two bytes per column of the padded row).
+// LDS bytes: activation image, 16 zero bytes, int32 partial sums.
 size_t flat_lds_bytes(int in, int K, int mt, int tiles_per_wg) {
     const size_t nchunks = (size_t)((in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS);
     const size_t nc = (size_t)NLIMB * mt;
-    return nchunks * IMG_PER_NC * nc + 16 + (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4 +
-           (size_t)2 * mt * nchunks * CHUNK_WORDS * 32;
+    return nchunks * IMG_PER_NC * nc + 16 + (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4;
+}
+
+// Column pairs (4 per 32-column word, padded words included) per image thread.
+int flat_pairs_per_thread(int in) {
+    const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+    return (nchunks * CHUNK_WORDS * 4 + FL_PREP_THREADS - 1) / FL_PREP_THREADS;
 }
 
 // Waits until the LDS counter reaches `target` (relaxed reads: the writers
@@ -83,7 +87,7 @@ __device__ __forceinline__ void lds_wait_count(int *counter, int target) {
     asm volatile("" ::: "memory");
 }
 
-template <int K, int MT, int XQ, int RING>
+template <int K, int MT, int XP, int RING>
 __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
     const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
@@ -113,7 +117,6 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const int t1 = (int)(((long)(blockIdx.x + 1) * T) / G);
     const int ntl = t1 - t0;
     int *red = reinterpret_cast<int *>(lds + pad + 16);                         // [ntl][K][NC][16]
-    uint16_t *xs = reinterpret_cast<uint16_t *>(red + ntl * K * NC * TILE_ROWS);  // [mt][8][wpad][4]
 
     // scales of the output row this thread finishes (requested after the
     // activations or the first weights, whose waits must not include them)
@@ -136,44 +139,41 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
 
     if (wave < FL_PREP) {
         // ================= image waves =================
-        // activations: thread q holds columns 8q .. 8q+7 of each token
-        const int xq_total = in >> 3;
-        uint4 xr[MT][XQ];
+        // Thread t owns the column pairs P = t + j * FL_PREP_THREADS (j < XP),
+        // pair P = (word w = P / 4, p = P % 4): columns 32w + 8kk + 2p and
+        // 32w + 8kk + 2p + 1, kk = 0..3, read as four 4-byte words.  They are
+        // exactly the columns of the image entries (w, 2p) and (w, 2p + 1), so
+        // each thread quantises and writes whole entries from its registers.
+        // Pairs past the row end read its last pair (clamped) and are written
+        // as zeros.
+        const int npairs = words * 4;                     // pairs of the row
+        const int ppad = nchunks * CHUNK_WORDS * 4;       // with the padded words
+        uint32_t xw[MT][XP][4];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int mc = min(m, mt - 1);
+            const uint16_t *xrow = X + (size_t)(m0 + mc) * in;
 #pragma unroll
-            for (int j = 0; j < XQ; ++j) {
-                const int q = min(tid + j * FL_PREP_THREADS, xq_total - 1);
-                xr[m][j] = *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + mc) * in + 8 * q);
+            for (int j = 0; j < XP; ++j) {
+                const int P = min(tid + j * FL_PREP_THREADS, npairs - 1);
+                const uint16_t *xp = xrow + 32 * (P >> 2) + 2 * (P & 3);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    xw[m][j][kk] = *reinterpret_cast<const uint32_t *>(xp + 8 * kk);
             }
         }
         load_scales();
-        const int wpad = nchunks * CHUNK_WORDS;
         // per-token maximum of |x| (fp16 bit patterns without the sign
-        // compare like magnitudes); the raw rows into LDS
+        // compare like magnitudes; clamped repeats only repeat real values)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             v2u16 mx2 = (v2u16){0, 0};
 #pragma unroll
-            for (int j = 0; j < XQ; ++j) {
-                // clamped repeats only repeat real values: harmless for a maximum
-                const uint4 u = xr[m][j];
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.x & 0x7FFF7FFFu));
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.y & 0x7FFF7FFFu));
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.z & 0x7FFF7FFFu));
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, u.w & 0x7FFF7FFFu));
-                // raw halves to xs[m][s][w][kk] (column 32w + 8kk + s), so that
-                // an image entry reads its four columns as one 8-byte word
-                const int q = tid + j * FL_PREP_THREADS;
-                if (m < mt && q < xq_total) {
-                    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-                    uint16_t *xd = xs + ((size_t)m * 8 * wpad + (q >> 2)) * 4 + (q & 3);
+            for (int j = 0; j < XP; ++j)
 #pragma unroll
-                    for (int h = 0; h < 8; ++h)
-                        xd[(size_t)h * wpad * 4] = (uint16_t)(uu[h >> 1] >> (16 * (h & 1)));
-                }
-            }
+                for (int kk = 0; kk < 4; ++kk)
+                    mx2 = __builtin_elementwise_max(
+                        mx2, __builtin_bit_cast(v2u16, xw[m][j][kk] & 0x7FFF7FFFu));
             const uint32_t mx = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
             if (lane == 0)
                 wmax[m][wave] = mx;
@@ -196,56 +196,50 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         }
         // Image entry (word w, bit s): the four columns 32w + 8kk + s, kk =
         // 0..3, one byte each, at [chunk w/16][s][lane group (w/4)%4][column
-        // n][4 (w%4) + kk].  Entries are taken s-major over the words rounded
-        // up to 64, so s is the same for a whole wave.  fma(x, 2^sh, 1.5*2^23)
-        // leaves q in the low mantissa bits; v = q + 64 (1 + 2^7 + 2^14) lies
-        // in [0, 2^21), and its 7-bit fields minus 64 are the
-        // limbs.  Words past the row end get zero limbs.
+        // n][4 (w%4) + kk].  fma(x, 2^sh, 1.5*2^23) leaves q in the low
+        // mantissa bits; v = q + 64 (1 + 2^7 + 2^14) lies in [0, 2^21), and its
+        // 7-bit fields minus 64 are the limbs (fields of 64 past the row end).
         int psum[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             psum[m] = 0;
-        const int wp64 = (wpad + 63) & ~63;
-        for (int e = tid; e < 8 * wp64; e += FL_PREP_THREADS) {
-            // s is the same for the 64 entries of a wave (scalar division)
-            const int s = (__builtin_amdgcn_readfirstlane(e) >> 6) / (wp64 >> 6);
-            const int w = e - s * wp64;
-            if (w < wpad) {
-                const bool live = w < words;
-                const int wc = live ? w : 0;
-                unsigned char *dst = lds + (w / CHUNK_WORDS) * img_chunk + s * (4 * NC * 16) +
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const int P = tid + j * FL_PREP_THREADS;
+            if (P < ppad) {
+                const bool live = P < npairs;
+                const int w = P >> 2, p = P & 3;
+                unsigned char *dst = lds + (w / CHUNK_WORDS) * img_chunk + (2 * p) * (4 * NC * 16) +
                                      ((w >> 2) & 3) * (NC * 16) + (w & 3) * 4;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m < mt) {
                         const float scale = __builtin_ldexpf(1.0f, sh[m]);
-                        uint32_t nb[NLIMB] = {0u, 0u, 0u};   // 7-bit fields, column kk in byte kk
-                        const uint2 hx = *reinterpret_cast<const uint2 *>(
-                            xs + (((size_t)m * 8 + s) * wpad + wc) * 4);
+                        uint32_t ne[NLIMB] = {0u, 0u, 0u}, no[NLIMB] = {0u, 0u, 0u};
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk) {
-                            const uint16_t h = (uint16_t)((kk < 2 ? hx.x : hx.y) >> (16 * (kk & 1)));
-                            const float f = __builtin_fmaf(h2f(h), scale, 12582912.0f);
-                            // v = q + 0x102040 (fields of 64 past the row end: zero limbs)
-                            const uint32_t v = live ? __builtin_bit_cast(uint32_t, f) - 0x4B2FDFC0u : 0x102040u;
-                            psum[m] += (int)v - 0x102040;
+                            const uint32_t u = xw[m][j][kk];
+                            const float fe = __builtin_fmaf(h2f((uint16_t)u), scale, 12582912.0f);
+                            const float fo = __builtin_fmaf(h2f((uint16_t)(u >> 16)), scale, 12582912.0f);
+                            const uint32_t ve = live ? __builtin_bit_cast(uint32_t, fe) - 0x4B2FDFC0u : 0x102040u;
+                            const uint32_t vo = live ? __builtin_bit_cast(uint32_t, fo) - 0x4B2FDFC0u : 0x102040u;
+                            psum[m] += (int)(ve + vo) - 2 * 0x102040;
 #pragma unroll
-                            for (int l = 0; l < NLIMB; ++l)
-                                nb[l] |= ((v >> (7 * l)) & 0x7Fu) << (8 * kk);
+                            for (int lb = 0; lb < NLIMB; ++lb) {
+                                ne[lb] |= ((ve >> (7 * lb)) & 0x7Fu) << (8 * kk);
+                                no[lb] |= ((vo >> (7 * lb)) & 0x7Fu) << (8 * kk);
+                            }
                         }
 #pragma unroll
-                        for (int l = 0; l < NLIMB; ++l) {
-                            // bytes c_s * (n - 64), every n below 0x80
-                            uint32_t b;
-                            if (s == 7) {
-                                b = (0xC0C0C0C0u - nb[l]) ^ 0x80808080u;
-                            } else if ((s & 1) == 0) {
-                                b = (nb[l] << 1) ^ 0x80808080u;
-                            } else {
-                                const uint32_t t = nb[l] ^ 0x40404040u;
-                                b = t | ((t & 0x40404040u) << 1);
-                            }
-                            *reinterpret_cast<uint32_t *>(dst + (NLIMB * m + l) * 16) = b;
+                        for (int lb = 0; lb < NLIMB; ++lb) {
+                            // bytes c_s (n - 64), every n below 0x80: c = 2 for the even
+                            // bit 2p, c = 1 for the odd bit 2p + 1, c = -1 for bit 7
+                            const uint32_t be = (ne[lb] << 1) ^ 0x80808080u;
+                            const uint32_t t = no[lb] ^ 0x40404040u;
+                            const uint32_t bo = (p == 3) ? ((0xC0C0C0C0u - no[lb]) ^ 0x80808080u)
+                                                         : (t | ((t & 0x40404040u) << 1));
+                            *reinterpret_cast<uint32_t *>(dst + (NLIMB * m + lb) * 16) = be;
+                            *reinterpret_cast<uint32_t *>(dst + 4 * NC * 16 + (NLIMB * m + lb) * 16) = bo;
                         }
                     }
                 }
@@ -439,7 +433,7 @@ int flat_grid(int out) {
     return T < flat_num_cus() ? T : flat_num_cus();
 }
 
-template <int K, int MT, int XQ, int RING>
+template <int K, int MT, int XP, int RING>
 hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, int in,
                        const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
     const int G = flat_grid(out);
@@ -447,17 +441,17 @@ hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, 
     const int tpw = (T + G - 1) / G;
     const int mt = M < MT ? M : MT;
     const size_t lds = flat_lds_bytes(in, K, mt, tpw);
-    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XQ, RING>), dim3(G, (M + MT - 1) / MT),
+    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XP, RING>), dim3(G, (M + MT - 1) / MT),
                        dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
     return hipGetLastError();
 }
 
 #ifndef RBQ_FLAT_RING_MAX
-#define RBQ_FLAT_RING_MAX 4
+#define RBQ_FLAT_RING_MAX 2
 #endif
 
 // The ring covers a stream wave's whole share of units when it can.
-template <int K, int MT, int XQ>
+template <int K, int MT, int XP>
 hipError_t launch_kmx(const uint32_t *planes, const uint16_t *scales, int out, int in,
                       const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
     const int G = flat_grid(out);
@@ -465,28 +459,28 @@ hipError_t launch_kmx(const uint32_t *planes, const uint16_t *scales, int out, i
     const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
     const int per_wave = ((T + G - 1) / G * nchunks + FL_STREAM - 1) / FL_STREAM;
     if (per_wave <= 2 || RBQ_FLAT_RING_MAX == 2)
-        return launch_kmxr<K, MT, XQ, 2>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmxr<K, MT, XP, 2>(planes, scales, out, in, X, M, Y, st);
     if (per_wave <= 3 || RBQ_FLAT_RING_MAX == 3)
-        return launch_kmxr<K, MT, XQ, 3>(planes, scales, out, in, X, M, Y, st);
-    return launch_kmxr<K, MT, XQ, 4>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmxr<K, MT, XP, 3>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmxr<K, MT, XP, 4>(planes, scales, out, in, X, M, Y, st);
 }
 
 template <int K, int MT>
 hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, int in,
                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
-    const int xq = (in / 8 + FL_PREP_THREADS - 1) / FL_PREP_THREADS;
-    if (xq <= 2)
+    const int xp = flat_pairs_per_thread(in);
+    if (xp <= 2)
         return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, st);
-    if (xq <= 4)
+    if (xp <= 4 || MT > 1)   // two tokens: at most 4 pairs (32 loads) per thread
         return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
-    return launch_kmx<K, MT, 8>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmx<K, (MT > 1 ? 1 : MT), 8>(planes, scales, out, in, X, M, Y, st);
 }
 
 }  // namespace
 
 bool flat_supports(int out, int in, int K, int group_size, int M) {
     if (group_size != 0 || K < 1 || K > 2 || in % 128 != 0 || in <= 0 || in > FL_MAX_IN ||
-        M < 1 || M > 2 || out < 1)
+        M < 1 || M > 2 || out < 1 || (M > 1 && flat_pairs_per_thread(in) > 4))
         return false;
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
     const int G = flat_grid(out);
