@@ -8,15 +8,13 @@
 // implementation": 32 columns per word).  S_k is an exact integer product on
 // v_mfma_i32_16x16x64_i8:
 //   * each token is quantised once, q = round(x * 2^sh) with one power of two
-//     per token (|q| < 2^19), and split into three signed 7-bit limbs,
-//     q = l_0 + 2^7 l_1 + 2^14 l_2, l_j in [-64, 63];
+//     per token (|q| <= 2^22), and split into three signed bytes,
+//     q = l_0 + 2^8 l_1 + 2^16 l_2, l_j in [-128, 127];
 //   * the A operand is a masked weight word, w & (0x01010101 << s): byte kk
 //     holds bit 8kk + s of the word times 2^s (bit 7 reads as -128);
 //   * the B operand for bit position s holds the limbs of the matching
-//     columns times c_s = 2 (s even), 1 (s odd), -1 (s = 7), so that the
-//     products of bit positions 2j and 2j+1 both carry the weight 2^(2j+1)
-//     (and 2^7 for j = 3).  Four accumulators per plane, one per pair, give
-//     T = 64 acc_0 + 16 acc_1 + 4 acc_2 + acc_3 = 2^7 sum(bit * limb).
+//     columns.  One accumulator per plane and bit position; the flush
+//     T = sum_{s<7} 2^(7-s) acc_s - acc_7 = 2^7 sum(bit * limb).
 //
 // Organisation.  A GEMV reads each weight byte once, so its time is the HBM
 // latency plus the bytes over the bandwidth -- if the memory is busy from
@@ -27,9 +25,9 @@
 //   * those stream waves request their first RING units at entry and then
 //     wait for the image; a wave whose loads exceed the memory queue stalls
 //     at the issue of the next load, which is why the image is left to
-//     waves 0..3, which request no weights: they load the activations, find
-//     the per-token maximum (meeting through an LDS counter), write the
-//     image and count themselves done in LDS;
+//     waves 0..3, which request no weights: they load the activations with
+//     16-byte loads, find the per-token maximum (meeting through an LDS
+//     counter), write the image and count themselves done in LDS;
 //   * a stream wave consumes a unit and requests the next one; the partial
 //     sums of a tile from several waves meet in LDS as int32 additions
 //     (exact, so the result does not depend on their order), and one
@@ -55,24 +53,26 @@ constexpr int FL_STREAM = FL_WAVES - FL_PREP;         // waves that stream weigh
 constexpr int TILE_ROWS = 16;
 constexpr int CHUNK_WORDS = 16;                       // 512 columns
 constexpr int IMG_PER_NC = 8 * 4 * 16;                // image bytes per chunk and MFMA column
+constexpr int IMG_CHUNK_PAD = 64;                     // moves consecutive chunks to other LDS banks
 constexpr int NLIMB = 3;
 constexpr int FL_MAX_TOKENS = 5;                      // 3 limbs x 5 tokens <= 16 MFMA columns
 constexpr int FL_MAX_TILES = FL_THREADS / TILE_ROWS;  // one finishing thread per row
-constexpr int FL_MAX_XP = 8;                          // column pairs per image thread and token
-constexpr int FL_MAX_IN = FL_MAX_XP * FL_PREP_THREADS * 8;   // 4 pairs per 32-column word
+constexpr int FL_MAX_XU = 4;                          // half-words per image thread and token
+constexpr int FL_MAX_IN = FL_MAX_XU * FL_PREP_THREADS * 16;  // 16 columns per half-word
 constexpr int FL_SPIN_LIMIT = 1 << 22;                // bound of each LDS wait (never reached)
 
 // LDS bytes: activation image, 16 zero bytes, int32 partial sums.
 size_t flat_lds_bytes(int in, int K, int mt, int tiles_per_wg) {
     const size_t nchunks = (size_t)((in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS);
     const size_t nc = (size_t)NLIMB * mt;
-    return nchunks * IMG_PER_NC * nc + 16 + (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4;
+    return nchunks * (IMG_PER_NC * nc + IMG_CHUNK_PAD) + 16 +
+           (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4;
 }
 
-// Column pairs (4 per 32-column word, padded words included) per image thread.
-int flat_pairs_per_thread(int in) {
+// Half-words (16 columns; padded words included) per image thread.
+int flat_units_per_thread(int in) {
     const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
-    return (nchunks * CHUNK_WORDS * 4 + FL_PREP_THREADS - 1) / FL_PREP_THREADS;
+    return (nchunks * CHUNK_WORDS * 2 + FL_PREP_THREADS - 1) / FL_PREP_THREADS;
 }
 
 // Waits until the LDS counter reaches `target` (relaxed reads: the writers
@@ -87,7 +87,7 @@ __device__ __forceinline__ void lds_wait_count(int *counter, int target) {
     asm volatile("" ::: "memory");
 }
 
-template <int K, int MT, int XP, int RING>
+template <int K, int MT, int XU, int RING>
 __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
     const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const int NC = NLIMB * mt;
     const int words = in >> 5;
     const int nchunks = (words + CHUNK_WORDS - 1) / CHUNK_WORDS;
-    const int img_chunk = IMG_PER_NC * NC;
+    const int img_chunk = IMG_PER_NC * NC + IMG_CHUNK_PAD;
     const int pad = nchunks * img_chunk;            // 16 zero bytes for unused MFMA columns
 
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
@@ -139,27 +139,25 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
 
     if (wave < FL_PREP) {
         // ================= image waves =================
-        // Thread t owns the column pairs P = t + j * FL_PREP_THREADS (j < XP),
-        // pair P = (word w = P / 4, p = P % 4): columns 32w + 8kk + 2p and
-        // 32w + 8kk + 2p + 1, kk = 0..3, read as four 4-byte words.  They are
-        // exactly the columns of the image entries (w, 2p) and (w, 2p + 1), so
-        // each thread quantises and writes whole entries from its registers.
-        // Pairs past the row end read its last pair (clamped) and are written
-        // as zeros.
-        const int npairs = words * 4;                     // pairs of the row
-        const int ppad = nchunks * CHUNK_WORDS * 4;       // with the padded words
-        uint32_t xw[MT][XP][4];
+        // Thread t owns the half-words H = t + j * FL_PREP_THREADS (j < XU):
+        // word w = H / 2, half e = H % 2, the 16 columns 32w + 16e + i, read
+        // with two 16-byte loads.  Column 32w + 8kk + s is byte kk of image
+        // entry (w, s), so a half-word holds bytes 2e and 2e + 1 of all eight
+        // entries of its word.  Half-words past the row end load its last
+        // one and are quantised with the scale 0 (limbs 0).
+        const int nh = words * 2;                         // half-words of the row
+        const int hpad = nchunks * CHUNK_WORDS * 2;       // with the padded words
+        v4u xw[MT][XU][2];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int mc = min(m, mt - 1);
             const uint16_t *xrow = X + (size_t)(m0 + mc) * in;
 #pragma unroll
-            for (int j = 0; j < XP; ++j) {
-                const int P = min(tid + j * FL_PREP_THREADS, npairs - 1);
-                const uint16_t *xp = xrow + 32 * (P >> 2) + 2 * (P & 3);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    xw[m][j][kk] = *reinterpret_cast<const uint32_t *>(xp + 8 * kk);
+            for (int j = 0; j < XU; ++j) {
+                const int H = min(tid + j * FL_PREP_THREADS, nh - 1);
+                const v4u *xp = reinterpret_cast<const v4u *>(xrow + 16 * H);
+                xw[m][j][0] = xp[0];
+                xw[m][j][1] = xp[1];
             }
         }
         load_scales();
@@ -169,11 +167,13 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         for (int m = 0; m < MT; ++m) {
             v2u16 mx2 = (v2u16){0, 0};
 #pragma unroll
-            for (int j = 0; j < XP; ++j)
+            for (int j = 0; j < XU; ++j)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    mx2 = __builtin_elementwise_max(
-                        mx2, __builtin_bit_cast(v2u16, xw[m][j][kk] & 0x7FFF7FFFu));
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        mx2 = __builtin_elementwise_max(
+                            mx2, __builtin_bit_cast(v2u16, xw[m][j][h][c] & 0x7FFF7FFFu));
             const uint32_t mx = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
             if (lane == 0)
                 wmax[m][wave] = mx;
@@ -182,8 +182,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             __hip_atomic_fetch_add(&counters[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         lds_wait_count(&counters[0], FL_PREP);
 
-        // |x| < 2^E per token; q = round(x * 2^sh), sh = 19 - E (|q| < 2^19:
-        // the limbs reach -64 * 16513 .. 63 * 16513)
+        // |x| < 2^E per token; q = round(x * 2^sh), sh = 22 - E, |q| <= 2^22
         int sh[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -192,54 +191,49 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             for (int v = 0; v < FL_PREP; ++v)
                 mx = max(mx, wmax[m][v]);
             const int e = (int)(mx >> 10);
-            sh[m] = 19 - ((e == 0 ? 1 : e) - 14);
+            sh[m] = 22 - ((e == 0 ? 1 : e) - 14);
         }
         // Image entry (word w, bit s): the four columns 32w + 8kk + s, kk =
         // 0..3, one byte each, at [chunk w/16][s][lane group (w/4)%4][column
-        // n][4 (w%4) + kk].  fma(x, 2^sh, 1.5*2^23) leaves q in the low
-        // mantissa bits; v = q + 64 (1 + 2^7 + 2^14) lies in [0, 2^21), and its
-        // 7-bit fields minus 64 are the limbs (fields of 64 past the row end).
+        // n][4 (w%4) + kk].  fma(x, 2^sh, 1.5*2^23) leaves 2^22 + q in the
+        // mantissa; v = q + 0x808080 lies in [0, 2^24), and its bytes xor 0x80
+        // are the limbs.  Each thread writes the two bytes of its half.
         int psum[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             psum[m] = 0;
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            const int P = tid + j * FL_PREP_THREADS;
-            if (P < ppad) {
-                const bool live = P < npairs;
-                const int w = P >> 2, p = P & 3;
-                unsigned char *dst = lds + (w / CHUNK_WORDS) * img_chunk + (2 * p) * (4 * NC * 16) +
-                                     ((w >> 2) & 3) * (NC * 16) + (w & 3) * 4;
+        for (int j = 0; j < XU; ++j) {
+            const int H = tid + j * FL_PREP_THREADS;
+            if (H < hpad) {
+                const bool live = H < nh;
+                const int w = H >> 1, e = H & 1;
+                unsigned char *dst = lds + (w / CHUNK_WORDS) * img_chunk + ((w >> 2) & 3) * (NC * 16) +
+                                     (w & 3) * 4 + 2 * e;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m < mt) {
-                        const float scale = __builtin_ldexpf(1.0f, sh[m]);
-                        uint32_t ne[NLIMB] = {0u, 0u, 0u}, no[NLIMB] = {0u, 0u, 0u};
+                        const float scale = live ? __builtin_ldexpf(1.0f, sh[m]) : 0.0f;
 #pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) {
-                            const uint32_t u = xw[m][j][kk];
-                            const float fe = __builtin_fmaf(h2f((uint16_t)u), scale, 12582912.0f);
-                            const float fo = __builtin_fmaf(h2f((uint16_t)(u >> 16)), scale, 12582912.0f);
-                            const uint32_t ve = live ? __builtin_bit_cast(uint32_t, fe) - 0x4B2FDFC0u : 0x102040u;
-                            const uint32_t vo = live ? __builtin_bit_cast(uint32_t, fo) - 0x4B2FDFC0u : 0x102040u;
-                            psum[m] += (int)(ve + vo) - 2 * 0x102040;
-#pragma unroll
-                            for (int lb = 0; lb < NLIMB; ++lb) {
-                                ne[lb] |= ((ve >> (7 * lb)) & 0x7Fu) << (8 * kk);
-                                no[lb] |= ((vo >> (7 * lb)) & 0x7Fu) << (8 * kk);
-                            }
-                        }
-#pragma unroll
-                        for (int lb = 0; lb < NLIMB; ++lb) {
-                            // bytes c_s (n - 64), every n below 0x80: c = 2 for the even
-                            // bit 2p, c = 1 for the odd bit 2p + 1, c = -1 for bit 7
-                            const uint32_t be = (ne[lb] << 1) ^ 0x80808080u;
-                            const uint32_t t = no[lb] ^ 0x40404040u;
-                            const uint32_t bo = (p == 3) ? ((0xC0C0C0C0u - no[lb]) ^ 0x80808080u)
-                                                         : (t | ((t & 0x40404040u) << 1));
-                            *reinterpret_cast<uint32_t *>(dst + (NLIMB * m + lb) * 16) = be;
-                            *reinterpret_cast<uint32_t *>(dst + 4 * NC * 16 + (NLIMB * m + lb) * 16) = bo;
+                        for (int s = 0; s < 8; ++s) {
+                            // columns 32w + 16e + s (byte 2e) and + 8 (byte 2e + 1)
+                            const uint32_t u0 = xw[m][j][0][s >> 1], u1 = xw[m][j][1][s >> 1];
+                            const uint16_t h0 = (s & 1) ? (uint16_t)(u0 >> 16) : (uint16_t)u0;
+                            const uint16_t h1 = (s & 1) ? (uint16_t)(u1 >> 16) : (uint16_t)u1;
+                            const uint32_t v0 =
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) -
+                                0x4ABF7F80u;
+                            const uint32_t v1 =
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) -
+                                0x4ABF7F80u;
+                            psum[m] += (int)(v0 + v1) - 2 * 0x808080;
+                            // [v0.b0 v1.b0 v0.b1 v1.b1], [v0.b2 v1.b2 0 0]
+                            const uint32_t l01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u) ^ 0x80808080u;
+                            const uint32_t l2 = __builtin_amdgcn_perm(v1, v0, 0x0C0C0602u) ^ 0x8080u;
+                            unsigned char *d = dst + s * (4 * NC * 16) + (NLIMB * m) * 16;
+                            *reinterpret_cast<uint16_t *>(d) = (uint16_t)l01;
+                            *reinterpret_cast<uint16_t *>(d + 16) = (uint16_t)(l01 >> 16);
+                            *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
                         }
                     }
                 }
@@ -296,12 +290,12 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         load_scales();
         lds_wait_count(&counters[1], FL_PREP);
 
-        // acc[k][j] collects bit positions 2j and 2j+1 of plane k
-        v4i acc[K][4];
+        // acc[k][s] collects bit position s of plane k
+        v4i acc[K][8];
 #pragma unroll
         for (int k = 0; k < K; ++k)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j)
                 acc[k][j] = (v4i){0, 0, 0, 0};
         const int b_off = (li < NC) ? (lg * NC + li) * 16 : pad;
         const int b_stride = (li < NC) ? 4 * NC * 16 : 0;
@@ -319,7 +313,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                 for (int k = 0; k < K; ++k) {
                     const v4i av = (v4i){(int)(wv[k].x & mask), (int)(wv[k].y & mask),
                                          (int)(wv[k].z & mask), (int)(wv[k].w & mask)};
-                    acc[k][s >> 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, acc[k][s >> 1], 0, 0, 0);
+                    acc[k][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, acc[k][s], 0, 0, 0);
                 }
             }
         };
@@ -335,16 +329,19 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                     for (int k = 0; k < K; ++k)
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const int t = ((acc[k][0][v] * 4 + acc[k][1][v]) * 4 + acc[k][2][v]) * 4 +
-                                          acc[k][3][v];
-                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, t, __ATOMIC_RELAXED,
+                            // modulo 2^32; the sum itself stays below 2^29
+                            uint32_t t = 0u - (uint32_t)acc[k][7][v];
+#pragma unroll
+                            for (int q = 0; q < 7; ++q)
+                                t += (uint32_t)acc[k][q][v] << (7 - q);
+                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)t, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
                         }
                 }
 #pragma unroll
                 for (int k = 0; k < K; ++k)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 8; ++j)
                         acc[k][j] = (v4i){0, 0, 0, 0};
             }
             if (tile_end) {
@@ -377,7 +374,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     __syncthreads();
 
     // ---- one thread per output row.  Column 3m + l holds 2^7 sum(bit l_j);
-    // 2^7 sum(bit q) = T_0 + 2^7 T_1 + 2^14 T_2 (exact in fp64), and
+    // 2^7 sum(bit q) = T_0 + 2^8 T_1 + 2^16 T_2 (exact in fp64), and
     // y = sum_k a_k (2 sum(bit q) - sum q) 2^-sh.
     if (tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out) {
         const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
@@ -392,8 +389,8 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
-                    const double t = (double)rp[0] + 128.0 * (double)rp[TILE_ROWS] +
-                                     16384.0 * (double)rp[2 * TILE_ROWS];
+                    const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
+                                     65536.0 * (double)rp[2 * TILE_ROWS];
                     y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx);
                 }
                 Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = f2h(__builtin_ldexpf(y, -shs[m]));
@@ -433,7 +430,7 @@ int flat_grid(int out) {
     return T < flat_num_cus() ? T : flat_num_cus();
 }
 
-template <int K, int MT, int XP, int RING>
+template <int K, int MT, int XU, int RING>
 hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, int in,
                        const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
     const int G = flat_grid(out);
@@ -441,46 +438,39 @@ hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, 
     const int tpw = (T + G - 1) / G;
     const int mt = M < MT ? M : MT;
     const size_t lds = flat_lds_bytes(in, K, mt, tpw);
-    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XP, RING>), dim3(G, (M + MT - 1) / MT),
+    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XU, RING>), dim3(G, (M + MT - 1) / MT),
                        dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
     return hipGetLastError();
 }
 
-#ifndef RBQ_FLAT_RING_MAX
-#define RBQ_FLAT_RING_MAX 2
+// Two units in flight per stream wave: deeper rings measured slower (their
+// refills stall the issue of the wave's next loads for longer).
+#ifndef RBQ_FLAT_RING
+#define RBQ_FLAT_RING 2
 #endif
 
-// The ring covers a stream wave's whole share of units when it can.
-template <int K, int MT, int XP>
+template <int K, int MT, int XU>
 hipError_t launch_kmx(const uint32_t *planes, const uint16_t *scales, int out, int in,
                       const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
-    const int G = flat_grid(out);
-    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
-    const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
-    const int per_wave = ((T + G - 1) / G * nchunks + FL_STREAM - 1) / FL_STREAM;
-    if (per_wave <= 2 || RBQ_FLAT_RING_MAX == 2)
-        return launch_kmxr<K, MT, XP, 2>(planes, scales, out, in, X, M, Y, st);
-    if (per_wave <= 3 || RBQ_FLAT_RING_MAX == 3)
-        return launch_kmxr<K, MT, XP, 3>(planes, scales, out, in, X, M, Y, st);
-    return launch_kmxr<K, MT, XP, 4>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmxr<K, MT, XU, RBQ_FLAT_RING>(planes, scales, out, in, X, M, Y, st);
 }
 
 template <int K, int MT>
 hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, int in,
                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
-    const int xp = flat_pairs_per_thread(in);
-    if (xp <= 2)
+    const int xu = flat_units_per_thread(in);
+    if (xu <= 1)
+        return launch_kmx<K, MT, 1>(planes, scales, out, in, X, M, Y, st);
+    if (xu <= 2)
         return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, st);
-    if (xp <= 4 || MT > 1)   // two tokens: at most 4 pairs (32 loads) per thread
-        return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
-    return launch_kmx<K, (MT > 1 ? 1 : MT), 8>(planes, scales, out, in, X, M, Y, st);
+    return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
 }
 
 }  // namespace
 
 bool flat_supports(int out, int in, int K, int group_size, int M) {
     if (group_size != 0 || K < 1 || K > 2 || in % 128 != 0 || in <= 0 || in > FL_MAX_IN ||
-        M < 1 || M > 2 || out < 1 || (M > 1 && flat_pairs_per_thread(in) > 4))
+        M < 1 || M > 2 || out < 1)
         return false;
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
     const int G = flat_grid(out);
@@ -488,13 +478,17 @@ bool flat_supports(int out, int in, int K, int group_size, int M) {
     return tpw <= FL_MAX_TILES && flat_lds_bytes(in, K, M, tpw) <= flat_lds_limit();
 }
 
-// Measured on MI355X (fp16 in/out, K = 2, one token): ahead of the
-// whole-row streaming kernel when every compute unit gets at least two
-// 16-row tiles and the image build (4 waves, about 10 VALU operations per
-// column) stays short.
+// Measured on MI355X (fp16 in/out, K = 2, one and two tokens): ahead of
+// the whole-row streaming kernel once every stream wave gets at least one
+// (tile, chunk) unit; with fewer units per workgroup (4096 x 4096: 8) the
+// streaming kernel, which spreads a tile over more workgroups, is faster.
 bool flat_preferred(int out, int in, int K, int group_size, int M) {
+    if (!flat_supports(out, in, K, group_size, M))
+        return false;
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
-    return flat_supports(out, in, K, group_size, M) && T >= 2 * flat_num_cus() && in <= 8192;
+    const int G = flat_grid(out);
+    const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+    return ((T + G - 1) / G) * nchunks >= FL_STREAM;
 }
 
 hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int out, int in,

@@ -111,7 +111,9 @@ def test_path_override_roundtrip():
     L = rbq.lib()
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 1) == rbq.PATH_STREAM
     assert L.rbq_select_path(rbq.shape(22016, 4096, 2), 1) == rbq.PATH_FLAT
-    assert L.rbq_select_path(rbq.shape(22016, 11008, 2), 1) == rbq.PATH_STREAM
+    assert L.rbq_select_path(rbq.shape(4096, 11008, 2), 1) == rbq.PATH_FLAT
+    assert L.rbq_select_path(rbq.shape(22016, 4096, 2), 2) == rbq.PATH_FLAT
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 2) == rbq.PATH_STREAM
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 4) == rbq.PATH_DECODE
     assert L.rbq_select_path(rbq.shape(4096, 4096, 8), 1) == rbq.PATH_VALU
 
