@@ -56,7 +56,8 @@ def parse():
                     help="passes over all layers for the per-launch kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream", "flat"], default="auto")
+    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream", "flat", "group"],
+                    default="auto")
     ap.add_argument("--split", type=int, default=0,
                     help="waves per 16-row tile in the streaming kernel (0 = automatic)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
@@ -75,7 +76,7 @@ def parse():
 
 def path_names(rbq):
     return {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
-            rbq.PATH_STREAM: "stream", rbq.PATH_FLAT: "flat"}
+            rbq.PATH_STREAM: "stream", rbq.PATH_FLAT: "flat", rbq.PATH_GROUP: "group"}
 
 
 def main():
@@ -213,7 +214,11 @@ def bench_layer_set(args):
         copies = [(p.clone(), sc.clone()) for _ in range(rot)]
         sets.append((lin, copies, X, Y))
     torch.cuda.synchronize()
-    path = rbq.select_path(rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
+    forced = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
+              "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT, "group": rbq.PATH_GROUP}[args.path]
+    rbq.set_path(forced)
+    path = forced if forced != rbq.PATH_AUTO else rbq.select_path(
+        rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
     names = path_names(rbq)
     launches = []
     for r in range(max(args.kernel_reps, 1) * (2 if prefill else 8)):
@@ -300,7 +305,8 @@ def bench_decode(args):
     K, group = wl.num_planes, wl.group_size
     L = rbq.lib()
     path = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
-            "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT}[args.path]
+            "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT,
+            "group": rbq.PATH_GROUP}[args.path]
     rbq.set_path(path)
     rbq.set_stream_split(args.split)
 

@@ -26,7 +26,8 @@ RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_ENCODE_FORCE_SERIAL = 1
 
-PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT = 0, 1, 2, 3, 4, 5
+PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP = (
+    0, 1, 2, 3, 4, 5, 6)
 
 
 class RbqLibraryMissing(RuntimeError):

@@ -114,6 +114,8 @@ int32_t rbq_set_stream_split(int32_t waves_per_tile) {
 }
 
 rbq_path rbq_select_path(rbq_shape s, int32_t M) {
+    if (rbq::group_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_GROUP;
     if (rbq::flat_preferred(s.out_features, s.in_features, s.num_planes, s.group_size, M))
         return RBQ_PATH_FLAT;
     if (rbq::stream_supports(s.in_features, s.num_planes, s.group_size, M))
@@ -153,8 +155,11 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
     if (!aligned(planes, 16) || !aligned(scales, 2) || !aligned(X, 16))
         return RBQ_ERR_ALIGNMENT;
     rbq_path path = (rbq_path)g_forced_path.load();
-    if (path == RBQ_PATH_AUTO)
+    if (path == RBQ_PATH_AUTO) {
         path = rbq_select_path(s, M);
+        if (path == RBQ_PATH_GROUP && !aligned(scales, 8))   // the group kernel reads 4 scales at once
+            path = RBQ_PATH_VALU;
+    }
     if ((st = device_present()) != RBQ_OK)
         return st;
     hipError_t e;
@@ -186,6 +191,14 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
             return RBQ_ERR_UNSUPPORTED;
         e = rbq::launch_gemm_flat(planes, scales, s.out_features, s.in_features, s.num_planes,
                                   s.group_size, X, M, Y, hs);
+        break;
+    case RBQ_PATH_GROUP:
+        if (!rbq::group_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        if (!aligned(scales, 8))
+            return RBQ_ERR_ALIGNMENT;
+        e = rbq::launch_gemm_group(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                   s.group_size, X, M, Y, hs);
         break;
     default:
         return RBQ_ERR_UNSUPPORTED;

@@ -41,6 +41,13 @@ hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int 
                             int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                             hipStream_t st);
 
+// One-workgroup-per-compute-unit int8-MFMA GEMV for one token with a scale
+// per (row, 128-column group), K <= 4, in % 512 == 0; scales 8-byte aligned.
+bool group_supports(int out, int in, int K, int group_size, int M);
+hipError_t launch_gemm_group(const uint32_t *planes, const uint16_t *scales, int out, int in,
+                             int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                             hipStream_t st);
+
 // fp16-MFMA prefill GEMM over LDS-unpacked What (in % 64 == 0, K <= 4).
 bool prefill_supports(int in, int K, int group_size, int M);
 hipError_t launch_gemm_prefill(const uint32_t *planes, const uint16_t *scales, int out, int in,

@@ -163,10 +163,14 @@ typedef enum rbq_path {
     RBQ_PATH_PREFILL = 3,   /* fp16 MFMA on LDS-unpacked weights, large M */
     RBQ_PATH_STREAM = 4,    /* int8 MFMA, whole rows streamed per wave: M <= 2, K <= 2,
                                in <= 16384 */
-    RBQ_PATH_FLAT = 5       /* int8 MFMA, one 16-wave workgroup per compute unit whose
+    RBQ_PATH_FLAT = 5,      /* int8 MFMA, one 16-wave workgroup per compute unit whose
                                (tile, chunk) units are split evenly over 12 waves while
                                4 build the activation image: M <= 2, K <= 2,
                                in <= 16384; taken for layers of many rows */
+    RBQ_PATH_GROUP = 6      /* int8 MFMA for one token with 128-column group scales
+                               (group_size 128, K <= 4, in % 512 == 0, in <= 16384,
+                               scales 8-byte aligned); the lanes that hold a group's
+                               MFMA sums apply its scales.  Layout as RBQ_PATH_FLAT */
 } rbq_path;
 
 /* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for

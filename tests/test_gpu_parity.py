@@ -24,7 +24,7 @@ MAX_ABS_RMS = 1e-2
 # kernel families rbq_gemm can be forced to, with the largest M each takes
 PATHS = {"valu": (rbq.PATH_VALU, 1 << 30), "decode": (rbq.PATH_DECODE, 64),
          "stream": (rbq.PATH_STREAM, 2), "flat": (rbq.PATH_FLAT, 2),
-         "prefill": (rbq.PATH_PREFILL, 1 << 30)}
+         "group": (rbq.PATH_GROUP, 1), "prefill": (rbq.PATH_PREFILL, 1 << 30)}
 
 
 def dev():
@@ -241,7 +241,9 @@ def test_gemm_prefill_sampled_tokens(path, i):
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("out,inf,K,group,M", [
     (1, 32, 1, 0, 1), (3, 96, 2, 0, 2), (17, 4128, 3, 0, 5), (40, 384, 4, 128, 3),
-    (65, 1024, 8, 0, 16), (129, 11008, 2, 0, 7), (31, 5120, 4, 128, 17), (70, 2048, 2, 0, 33)])
+    (65, 1024, 8, 0, 16), (129, 11008, 2, 0, 7), (31, 5120, 4, 128, 17), (70, 2048, 2, 0, 33),
+    (1, 512, 1, 128, 1), (40, 1536, 4, 128, 1), (33, 5120, 3, 128, 1), (4100, 2048, 2, 128, 1),
+    (17, 16384, 4, 128, 1)])
 def test_gemm_ragged_random_signed_scales(path, out, inf, K, group, M):
     if M > PATHS[path][1]:
         pytest.skip("path does not take this M")
@@ -270,6 +272,50 @@ def test_gemm_closed_forms(path):
     What = oracle.dequant(p, s, group)
     for m, j in enumerate((0, 33, inf - 1)):
         assert np.array_equal(Y[m], What[:, j].astype(np.float16).astype(np.float64))
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_gemv_g128_closed_forms(path):
+    """x = 1 gives sum_k sum_t a_k,t (2 popcount - 128); a unit vector e_j
+    gives column j of the dequantised matrix, rounded once to fp16."""
+    K, out, inf, group = 4, 48, 2048, 128
+    p = workloads.random_planes(K, out, inf, seed=13)
+    s = workloads.random_scales(K, out, inf // group, seed=14, signed=True)
+    ones = np.full((1, inf), 0x3C00, np.uint16)
+    A = s.view(np.float16).astype(np.float64)
+    bits = np.unpackbits(p.view(np.uint8), bitorder="little").reshape(K, out, inf // group, group)
+    ref = (A * (2 * bits.sum(-1).astype(np.int64) - group)).sum(axis=(0, 2))
+    assert_close(gpu_gemm(p, s, ones, group, PATHS[path][0])[0], ref, "x=1")
+    What = oracle.dequant(p, s, group)
+    for j in (0, 127, 128, 1000, inf - 1):
+        e = np.zeros((1, inf), np.uint16)
+        e[0, j] = 0x3C00
+        Y = gpu_gemm(p, s, e, group, PATHS[path][0])
+        assert np.array_equal(Y[0], What[:, j].astype(np.float16).astype(np.float64)), j
+
+
+def test_group_path_needs_aligned_scales():
+    """Scales 2 bytes off an 8-byte boundary: the automatic choice falls back
+    to another kernel with the same result; the forced group kernel refuses."""
+    K, out, inf, group = 2, 64, 1024, 128
+    p = workloads.random_planes(K, out, inf, seed=21)
+    s = workloads.random_scales(K, out, inf // group, seed=22)
+    X = workloads.gaussian_activations(1, inf, seed=23)
+    pt = torch.from_numpy(p.view(np.int32)).to(dev())
+    buf = torch.zeros(s.size + 1, dtype=torch.float16, device=dev())
+    buf[1:] = torch.from_numpy(s.reshape(-1).view(np.float16)).to(dev())
+    st = buf[1:].view(s.shape)
+    assert st.data_ptr() % 8 != 0
+    x = torch.from_numpy(X.view(np.float16)).to(dev())
+    Y = rbq.gemm(pt, st, x, group).cpu().numpy().astype(np.float64)
+    assert_close(Y, oracle.gemm(p, s, X, group), "misaligned scales")
+    old = rbq.set_path(rbq.PATH_GROUP)
+    try:
+        with pytest.raises(rbq.RbqError) as ei:
+            rbq.gemm(pt, st, x, group)
+        assert ei.value.status == rbq.RBQ_ERR_ALIGNMENT
+    finally:
+        rbq.set_path(old)
 
 
 def test_gemm_empty_inputs():
