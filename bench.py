@@ -221,7 +221,7 @@ def bench_layer_set(args):
         rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
     names = path_names(rbq)
     launches = []
-    for r in range(max(args.kernel_reps, 1) * (2 if prefill else 8)):
+    for r in range(rot):   # one pass over every shape and rotation copy
         for lin, copies, X, Y in sets:
             p, sc = copies[r % rot]
             launches.append((f"{lin.out_features}x{lin.in_features}",
@@ -235,7 +235,7 @@ def bench_layer_set(args):
     side.wait_stream(stream)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
-        for _, fn in launches[:len(sets) * rot]:
+        for _, fn in launches:
             fn()
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -312,22 +312,35 @@ def bench_decode(args):
 
     # ---- weights: layer 0 from the seeded generator, encoded on the GPU
     stream = torch.cuda.current_stream(dev)
-    enc_ev = []
-    enc_planes, enc_scales, enc_bytes = [], [], 0
+    enc_planes, enc_scales, enc_bytes, Ws = [], [], 0, []
     for i, lin in enumerate(wl.linears):
         W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         p, s = rbq.encode(W, K, group)
-        e1.record(stream)
-        enc_ev.append((e0, e1))
+        Ws.append(W)
         enc_planes.append(p)
         enc_scales.append(s)
         enc_bytes += 4 * W.numel() + p.numel() * 4 + s.numel() * 2
-        del W
     torch.cuda.synchronize()
-    enc_ms = sum(a.elapsed_time(b) for a, b in enc_ev)
+    # encoder time: the seven encodes (outputs rewritten in place) captured in
+    # one HIP graph, replayed back to back
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    enc_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(enc_graph, stream=side):
+        for W, p, s in zip(Ws, enc_planes, enc_scales):
+            rbq.encode(W, K, group, planes=p, scales=s)
+    torch.cuda.synchronize()
+    enc_graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    enc_reps = 5
+    e0.record(stream)
+    for _ in range(enc_reps):
+        enc_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1) / enc_reps
+    del enc_graph, Ws
 
     # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
     # into one matrix: rows are encoded independently, so the stacked planes

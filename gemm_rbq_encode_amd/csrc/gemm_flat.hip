@@ -55,7 +55,7 @@ constexpr int CHUNK_WORDS = 16;                       // 512 columns
 constexpr int IMG_PER_NC = 8 * 4 * 16;                // image bytes per chunk and MFMA column
 constexpr int IMG_CHUNK_PAD = 64;                     // moves consecutive chunks to other LDS banks
 constexpr int NLIMB = 3;
-constexpr int FL_MAX_TOKENS = 5;                      // 3 limbs x 5 tokens <= 16 MFMA columns
+constexpr int FL_MAX_M = 16;                          // tokens per call (passes of up to 4)
 constexpr int FL_MAX_TILES = FL_THREADS / TILE_ROWS;  // one finishing thread per row
 constexpr int FL_MAX_XU = 4;                          // half-words per image thread and token
 constexpr int FL_MAX_IN = FL_MAX_XU * FL_PREP_THREADS * 16;  // 16 columns per half-word
@@ -68,6 +68,10 @@ size_t flat_lds_bytes(int in, int K, int mt, int tiles_per_wg) {
     return nchunks * (IMG_PER_NC * nc + IMG_CHUNK_PAD) + 16 +
            (size_t)tiles_per_wg * K * nc * TILE_ROWS * 4;
 }
+
+// Tokens per pass over the weights: 1, 2 or 4 (3 limbs x 4 tokens = 12 of
+// the 16 MFMA columns).
+int flat_tokens_per_pass(int M) { return M <= 2 ? M : 4; }
 
 // Half-words (16 columns; padded words included) per image thread.
 int flat_units_per_thread(int in) {
@@ -463,19 +467,23 @@ hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, in
         return launch_kmx<K, MT, 1>(planes, scales, out, in, X, M, Y, st);
     if (xu <= 2)
         return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, st);
-    return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
+    if (xu <= 3)
+        return launch_kmx<K, MT, 3>(planes, scales, out, in, X, M, Y, st);
+    if constexpr (MT <= 2)   // four tokens hold at most 3 half-words each in registers
+        return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool flat_supports(int out, int in, int K, int group_size, int M) {
     if (group_size != 0 || K < 1 || K > 2 || in % 128 != 0 || in <= 0 || in > FL_MAX_IN ||
-        M < 1 || M > 2 || out < 1)
+        M < 1 || M > FL_MAX_M || out < 1 || (M > 2 && flat_units_per_thread(in) > 3))
         return false;
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
     const int G = flat_grid(out);
     const int tpw = (T + G - 1) / G;
-    return tpw <= FL_MAX_TILES && flat_lds_bytes(in, K, M, tpw) <= flat_lds_limit();
+    return tpw <= FL_MAX_TILES && flat_lds_bytes(in, K, flat_tokens_per_pass(M), tpw) <= flat_lds_limit();
 }
 
 // Measured on MI355X (fp16 in/out, K = 2, one and two tokens): ahead of
@@ -496,11 +504,14 @@ hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int 
                             hipStream_t st) {
     if (!flat_supports(out, in, K, group_size, M))
         return hipErrorInvalidValue;
+    const int mt = flat_tokens_per_pass(M);
     if (K == 1)
-        return M == 1 ? launch_km<1, 1>(planes, scales, out, in, X, M, Y, st)
-                      : launch_km<1, 2>(planes, scales, out, in, X, M, Y, st);
-    return M == 1 ? launch_km<2, 1>(planes, scales, out, in, X, M, Y, st)
-                  : launch_km<2, 2>(planes, scales, out, in, X, M, Y, st);
+        return mt == 1 ? launch_km<1, 1>(planes, scales, out, in, X, M, Y, st)
+             : mt == 2 ? launch_km<1, 2>(planes, scales, out, in, X, M, Y, st)
+                       : launch_km<1, 4>(planes, scales, out, in, X, M, Y, st);
+    return mt == 1 ? launch_km<2, 1>(planes, scales, out, in, X, M, Y, st)
+         : mt == 2 ? launch_km<2, 2>(planes, scales, out, in, X, M, Y, st)
+                   : launch_km<2, 4>(planes, scales, out, in, X, M, Y, st);
 }
 
 }  // namespace rbq

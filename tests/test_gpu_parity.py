@@ -23,7 +23,7 @@ MAX_ABS_RMS = 1e-2
 
 # kernel families rbq_gemm can be forced to, with the largest M each takes
 PATHS = {"valu": (rbq.PATH_VALU, 1 << 30), "decode": (rbq.PATH_DECODE, 64),
-         "stream": (rbq.PATH_STREAM, 2), "flat": (rbq.PATH_FLAT, 2),
+         "stream": (rbq.PATH_STREAM, 2), "flat": (rbq.PATH_FLAT, 16),
          "group": (rbq.PATH_GROUP, 1), "prefill": (rbq.PATH_PREFILL, 1 << 30)}
 
 
