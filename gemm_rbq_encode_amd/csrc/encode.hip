@@ -20,11 +20,12 @@
 // and divides with a correctly rounded division.  Residuals are updated in
 // fp32 with one rounding, exactly as the definition states.
 //
-// Deciding.  The candidate h is the fp16 rounding of (float)m; it is the
-// answer for every value in [m - d, m + d] exactly when that interval lies
-// strictly between the midpoints of h and its two fp16 neighbours (which fp64
-// holds exactly).  A wrong candidate (fp32 double rounding near a midpoint)
-// fails that test and goes to the serial path.
+// Deciding.  The candidate h is the fp16 rounding of m itself (one rounding
+// from fp64: going through fp32 rounds twice and lands on the wrong side of
+// an fp16 midpoint about once in 10^4 means, which sent a few rows of most
+// matrices to the serial path); it is the answer for every value in
+// [m - d, m + d] exactly when that interval lies strictly between the
+// midpoints of h and its two fp16 neighbours (which fp64 holds exactly).
 //
 // Layout.  One workgroup (4 or 16 waves) per row; the row is cut into 64-column
 // chunks and wave w keeps chunks [w*CPW, (w+1)*CPW) in registers, lane l
@@ -81,7 +82,7 @@ __device__ __forceinline__ uint32_t decide_scale(double S, int n) {
     const double nd = (double)n;
     const double m = S / nd;
     const double d = m * ((2.0 * nd + 64.0) * 0x1p-53);
-    const uint32_t h = f2h((float)m);
+    const uint32_t h = f64_to_f16_rne(m);
     if (!(h < 0x7BFFu))          // the largest finite value, infinity, NaN
         return UNDECIDED;
     const double v = (double)h2f((uint16_t)h);
