@@ -15,10 +15,13 @@
 // than a relative (2n + 64)u (the 64u also covers both divisions).  If
 // every value in that interval rounds to the same fp16 number, that number
 // is the serial result (rounding is monotonic).  Otherwise -- an exact tie
-// or a mean within ~1e-11 of an fp16 rounding boundary -- one lane redoes
-// the serial sum, rebuilding each R_j from W and the scales already chosen,
-// and divides with a correctly rounded division.  Residuals are updated in
-// fp32 with one rounding, exactly as the definition states.
+// or a mean within ~1e-11 of an fp16 rounding boundary -- the serial sum is
+// redone and divided with a correctly rounded division: for a 128-column
+// group from the residuals the wave holds (read lane by lane in column
+// order), for a whole row by one lane that rebuilds each R_j from W and the
+// scales already chosen.  Exact ties do occur at the later steps of 4-plane
+// group encodings (a few groups per 13824 x 5120 matrix).  Residuals are
+// updated in fp32 with one rounding, exactly as the definition states.
 //
 // Deciding.  The candidate h is the fp16 rounding of m itself (one rounding
 // from fp64: going through fp32 rounds twice and lands on the wrong side of
@@ -111,12 +114,12 @@ __device__ __forceinline__ uint16_t serial_scale(const float *__restrict__ Wr, i
 }
 
 // Shared state of one workgroup while it encodes its rows.
-template <int WAVES, int GPW>
+template <int WAVES, int CPW>
 struct EncodeLds {
     double part[2][WAVES];          // per-wave row sums, alternating by step
     float hist_row[8];              // scales chosen so far (serial path)
     uint32_t decided_row;
-    float hist_grp[WAVES][8][GPW];  // per-group scales chosen so far (serial path)
+    uint64_t bits[WAVES][CPW];      // each wave's chunk ballots of the current step
 };
 
 template <int WAVES, int CPW>
@@ -137,7 +140,7 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
                                            uint32_t *__restrict__ planes,
                                            uint16_t *__restrict__ scales,
                                            int32_t *__restrict__ status, int force_serial,
-                                           EncodeLds<WAVES, CPW / 2> &sh, int &phase) {
+                                           EncodeLds<WAVES, CPW> &sh, int &phase) {
     constexpr int GPW = CPW / 2;  // 128-column groups per wave
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE);
@@ -169,11 +172,8 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
         if (!GROUPED) {
             double s = 0.0;
 #pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                const int col = (chunk0 + i) * RBQ_WAVE + lane;
-                if (col < in)
-                    s += (double)__builtin_fabsf(R[i]);
-            }
+            for (int i = 0; i < CPW; ++i)   // columns past the row end hold 0
+                s += (double)__builtin_fabsf(R[i]);
             s = wave_sum_f64_dpp(s);
             const int b = phase & 1;
             ++phase;
@@ -217,14 +217,19 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
                 const bool gvalid = col0 < in;
                 uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hl, g);
                 if (h == UNDECIDED && gvalid) {  // uniform in the wave
-                    uint32_t hs = 0;
-                    if (lane == 0)
-                        hs = serial_scale(Wr, col0, 128, &sh.hist_grp[wave][0][g], GPW, k);
-                    h = (uint32_t)__builtin_amdgcn_readlane((int)hs, 0);
+                    // the defining serial sum, in column order, over the
+                    // group's residuals: columns 128g' + l and 128g' + 64 + l
+                    // sit in lane l of R[2g] and R[2g + 1]
+                    double S = 0.0;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        for (int l = 0; l < RBQ_WAVE; ++l)
+                            S += (double)__builtin_fabsf(__builtin_bit_cast(
+                                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R[2 * g + c]), l)));
+                    h = f64_to_f16_rne(div_rn(S, 128.0));
                 }
                 a_grp[g] = gvalid ? h2f((uint16_t)h) : 0.0f;
                 if (lane == 0 && gvalid) {
-                    sh.hist_grp[wave][k][g] = a_grp[g];
                     scales[((size_t)k * out + r) * G + (col0 >> 7)] = (uint16_t)h;
                     if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
                         atomicOr(status, (int32_t)2);
@@ -232,33 +237,30 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
             }
         }
 
-        // signs, packed words and the residual update
-        uint32_t wv[(2 * CPW + RBQ_WAVE - 1) / RBQ_WAVE];
-#pragma unroll
-        for (int q = 0; q < (2 * CPW + RBQ_WAVE - 1) / RBQ_WAVE; ++q)
-            wv[q] = 0;
+        // signs, packed words and the residual update.  Chunk i's ballot is
+        // its two packed words; the ballots go through LDS so that lane 2i + h
+        // picks up word h of chunk i with one read.
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            const int col = (chunk0 + i) * RBQ_WAVE + lane;
-            const bool valid = col < in;
-            const bool plus = valid && (R[i] >= 0.0f);
+            // chunk c = chunk0 + i is whole (c < in / 64), half (in % 64 = 32:
+            // lanes < 32) or past the row end; columns past the end keep 0
+            // and their bits are never stored
+            const int c = chunk0 + i;
+            const bool valid = c < (in >> 6) || (c == (in >> 6) && lane < (in & 63));
+            const bool plus = R[i] >= 0.0f;
             const uint64_t m = __ballot(plus);
             const float a = GROUPED ? a_grp[i / 2] : a_row;
             if (valid)
                 R[i] = R[i] - (plus ? a : -a);
-            const int w0 = (2 * i) % RBQ_WAVE, q = (2 * i) / RBQ_WAVE;
-            if (lane == w0)
-                wv[q] = (uint32_t)m;
-            if (lane == w0 + 1)
-                wv[q] = (uint32_t)(m >> 32);
+            if (lane == 0)
+                sh.bits[wave][i] = m;
         }
+        static_assert(2 * CPW <= RBQ_WAVE, "one packed word per lane");
+        const uint32_t wv = reinterpret_cast<const uint32_t *>(sh.bits[wave])[lane < 2 * CPW ? lane : 0];
         uint32_t *prow = planes + ((size_t)k * out + r) * words;
-#pragma unroll
-        for (int q = 0; q < (2 * CPW + RBQ_WAVE - 1) / RBQ_WAVE; ++q) {
-            const int idx = chunk0 * 2 + q * RBQ_WAVE + lane;
-            if (q * RBQ_WAVE + lane < 2 * CPW && idx < words)
-                prow[idx] = wv[q];
-        }
+        const int idx = chunk0 * 2 + lane;
+        if (lane < 2 * CPW && idx < words)
+            prow[idx] = wv;
     }
 }
 
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     const float *__restrict__ W, int out, int in, int K, uint32_t *__restrict__ planes,
     uint16_t *__restrict__ scales, int32_t *__restrict__ status, int force_serial) {
     static_assert(CPW % 2 == 0, "a 128-column group must be a chunk pair of one wave");
-    __shared__ EncodeLds<WAVES, CPW / 2> sh;
+    __shared__ EncodeLds<WAVES, CPW> sh;
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
     const int G = gridDim.x;
