@@ -371,3 +371,43 @@ def test_gemv_fused_llama2_7b(path, idx):
     X = workloads.workload_activations(wl, 4096, 1)
     Y = gpu_gemm(p, s, X, wl.group_size, PATHS[path][0])
     assert_close(Y, oracle.gemm(p, s, X, wl.group_size), f"fused {idx}")
+
+
+def test_graph_replays_match_eager():
+    """The calls bench.py captures -- encodes and GEMMs on every kernel family
+    the automatic choice takes -- captured in one HIP graph: each of several
+    replays, with eager work and synchronisations between them, reproduces the
+    eager results bit for bit (the kernels are deterministic, and no call
+    records a memset)."""
+    cases = [(12288, 4096, 2, 0, 1), (4096, 4096, 2, 0, 1), (4096, 11008, 2, 0, 4),
+             (1024, 5120, 4, 128, 1), (512, 1024, 2, 0, 40)]
+    W = [torch.from_numpy(workloads.gaussian_weight(o, i, seed=o + i, outliers=True)).to(dev())
+         for o, i, _, _, _ in cases]
+    X = [torch.from_numpy(workloads.gaussian_activations(m, i, seed=m + i).view(np.float16)).to(dev())
+         for _, i, _, _, m in cases]
+    enc = [rbq.encode(w, K, g) for w, (_, _, K, g, _) in zip(W, cases)]
+    Y = [rbq.gemm(p, s, x, g) for (p, s), x, (_, _, _, g, _) in zip(enc, X, cases)]
+    torch.cuda.synchronize()
+    ref_p = [p.clone() for p, _ in enc]
+    ref_s = [s.clone() for _, s in enc]
+    ref_y = [y.clone() for y in Y]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for w, (p, s), x, y, (_, _, K, g, _) in zip(W, enc, X, Y, cases):
+            rbq.encode(w, K, g, planes=p, scales=s)
+            rbq.gemm(p, s, x, g, Y=y)
+    for rep in range(3):
+        for p, s, y in zip(*zip(*enc), Y):
+            p.zero_()
+            s.zero_()
+            y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j in range(len(cases)):
+            assert torch.equal(enc[j][0], ref_p[j]), (rep, j, "planes")
+            assert torch.equal(enc[j][1], ref_s[j]), (rep, j, "scales")
+            assert torch.equal(Y[j], ref_y[j]), (rep, j, "y")
+        _ = rbq.gemm(enc[0][0], enc[0][1], X[0], 0)   # eager work between replays
