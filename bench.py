@@ -56,7 +56,7 @@ def parse():
                     help="passes over all layers for the per-launch kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream", "flat", "group"],
+    ap.add_argument("--path", choices=["auto", "valu", "decode", "stream", "flat", "group", "split"],
                     default="auto")
     ap.add_argument("--split", type=int, default=0,
                     help="waves per 16-row tile in the streaming kernel (0 = automatic)")
@@ -76,7 +76,8 @@ def parse():
 
 def path_names(rbq):
     return {rbq.PATH_VALU: "valu", rbq.PATH_DECODE: "decode", rbq.PATH_PREFILL: "prefill",
-            rbq.PATH_STREAM: "stream", rbq.PATH_FLAT: "flat", rbq.PATH_GROUP: "group"}
+            rbq.PATH_STREAM: "stream", rbq.PATH_FLAT: "flat", rbq.PATH_GROUP: "group",
+            rbq.PATH_SPLIT: "split"}
 
 
 def main():
@@ -215,7 +216,8 @@ def bench_layer_set(args):
         sets.append((lin, copies, X, Y))
     torch.cuda.synchronize()
     forced = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
-              "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT, "group": rbq.PATH_GROUP}[args.path]
+              "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT, "group": rbq.PATH_GROUP,
+              "split": rbq.PATH_SPLIT}[args.path]
     rbq.set_path(forced)
     path = forced if forced != rbq.PATH_AUTO else rbq.select_path(
         rbq.shape(uniq[0][1].out_features, uniq[0][1].in_features, K, group), M)
@@ -288,7 +290,11 @@ def bench_layer_set(args):
             "data": "synthetic",
             "config": {"workload": wl.name, "linears": [f"{l.out_features}x{l.in_features}" for _, l in uniq],
                        "num_planes": K, "group_size": group, "tokens": M, "rotation": rot,
-                       "path": names[path]},
+                       "path": names[path],
+                       "path_per_shape": {f"{l.out_features}x{l.in_features}": names[
+                           forced if forced != rbq.PATH_AUTO else
+                           rbq.select_path(rbq.shape(l.out_features, l.in_features, K, group), M)]
+                           for _, l in uniq}},
             "roofline": roof, "cpu_baseline": None}
     print(json.dumps(line), flush=True)
 
@@ -306,7 +312,7 @@ def bench_decode(args):
     L = rbq.lib()
     path = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
             "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT,
-            "group": rbq.PATH_GROUP}[args.path]
+            "group": rbq.PATH_GROUP, "split": rbq.PATH_SPLIT}[args.path]
     rbq.set_path(path)
     rbq.set_stream_split(args.split)
 

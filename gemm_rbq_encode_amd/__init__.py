@@ -8,7 +8,7 @@ librbq.so behind the C ABI in include/rbq.h; this package only marshals
 torch tensors into those calls.
 """
 from ._binding import (  # noqa: F401
-    PATH_AUTO, PATH_DECODE, PATH_FLAT, PATH_GROUP, PATH_PREFILL, PATH_STREAM, PATH_VALU,
+    PATH_AUTO, PATH_DECODE, PATH_FLAT, PATH_GROUP, PATH_PREFILL, PATH_SPLIT, PATH_STREAM, PATH_VALU,
     RBQ_ENCODE_FORCE_SERIAL, RBQ_ERR_ALIGNMENT, RBQ_ERR_HIP, RBQ_ERR_INVALID_ARG,
     RBQ_ERR_NO_DEVICE, RBQ_ERR_UNSUPPORTED, RBQ_OK, RBQ_STATUS_NONFINITE_W,
     RBQ_STATUS_SCALE_OVERFLOW, LIB_PATH, RbqError, RbqLibraryMissing, Shape, check, encode,

@@ -26,8 +26,8 @@ RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_ENCODE_FORCE_SERIAL = 1
 
-PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP = (
-    0, 1, 2, 3, 4, 5, 6)
+PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP, PATH_SPLIT = (
+    0, 1, 2, 3, 4, 5, 6, 7)
 
 
 class RbqLibraryMissing(RuntimeError):

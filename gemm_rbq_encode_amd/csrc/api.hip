@@ -98,9 +98,9 @@ rbq_status rbq_encode(const float *W, rbq_shape s, uint32_t *planes, uint16_t *s
 }
 
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M) {
-    (void)s;
-    (void)M;
-    return 0;
+    if (rbq_check_shape(s) != RBQ_OK || M < 2)
+        return 0;
+    return rbq::split_workspace_bytes(s.out_features, s.in_features, s.num_planes, s.group_size, M);
 }
 
 rbq_path rbq_set_path(rbq_path p) {
@@ -113,7 +113,8 @@ int32_t rbq_set_stream_split(int32_t waves_per_tile) {
     return g_stream_split.exchange(waves_per_tile);
 }
 
-rbq_path rbq_select_path(rbq_shape s, int32_t M) {
+// The choice among the families that need no workspace.
+static rbq_path select_path_no_workspace(rbq_shape s, int32_t M) {
     if (rbq::group_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
         return RBQ_PATH_GROUP;
     if (rbq::flat_preferred(s.out_features, s.in_features, s.num_planes, s.group_size, M))
@@ -127,6 +128,12 @@ rbq_path rbq_select_path(rbq_shape s, int32_t M) {
     return RBQ_PATH_VALU;
 }
 
+rbq_path rbq_select_path(rbq_shape s, int32_t M) {
+    if (rbq::split_preferred(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+        return RBQ_PATH_SPLIT;
+    return select_path_no_workspace(s, M);
+}
+
 rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
                     size_t ws_bytes, void *stream) {
@@ -135,7 +142,7 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
         return st;
     if (M < 0)
         return RBQ_ERR_INVALID_ARG;
-    if (ws_bytes < rbq_gemm_workspace_bytes(s, M) || (ws_bytes > 0 && workspace == nullptr))
+    if (ws_bytes > 0 && workspace == nullptr)
         return RBQ_ERR_INVALID_ARG;
     if (M == 0 || s.out_features == 0)
         return RBQ_OK;
@@ -155,8 +162,11 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
     if (!aligned(planes, 16) || !aligned(scales, 2) || !aligned(X, 16))
         return RBQ_ERR_ALIGNMENT;
     rbq_path path = (rbq_path)g_forced_path.load();
+    const size_t ws_need = rbq_gemm_workspace_bytes(s, M);
     if (path == RBQ_PATH_AUTO) {
         path = rbq_select_path(s, M);
+        if (path == RBQ_PATH_SPLIT && (ws_bytes < ws_need || !aligned(workspace, 4)))
+            path = select_path_no_workspace(s, M);
         if (path == RBQ_PATH_GROUP && !aligned(scales, 8))   // the group kernel reads 4 scales at once
             path = RBQ_PATH_VALU;
     }
@@ -191,6 +201,16 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
             return RBQ_ERR_UNSUPPORTED;
         e = rbq::launch_gemm_flat(planes, scales, s.out_features, s.in_features, s.num_planes,
                                   s.group_size, X, M, Y, hs);
+        break;
+    case RBQ_PATH_SPLIT:
+        if (!rbq::split_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
+            return RBQ_ERR_UNSUPPORTED;
+        if (ws_bytes < ws_need)
+            return RBQ_ERR_INVALID_ARG;
+        if (!aligned(workspace, 4))
+            return RBQ_ERR_ALIGNMENT;
+        e = rbq::launch_gemm_split(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                   s.group_size, X, M, Y, workspace, ws_bytes, hs);
         break;
     case RBQ_PATH_GROUP:
         if (!rbq::group_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))

@@ -145,8 +145,12 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     const uint16_t *X, int32_t M, uint16_t *Y,
                     void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes rbq_gemm needs for this shape and M (0 for all current
- * kernels; kept so a split-K variant can be added without an ABI change). */
+/* Workspace bytes the split-column kernel family (RBQ_PATH_SPLIT) needs for
+ * this shape and M: S * M * out fp32 partial outputs, S column slices; 0 when
+ * that family cannot take the call (M < 2 or > 16, group scales, K > 2).
+ * With less workspace than this (or none) rbq_gemm chooses another family;
+ * a forced RBQ_PATH_SPLIT then returns RBQ_ERR_INVALID_ARG.  The workspace
+ * must be 4-byte aligned; its contents need no initialisation. */
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M);
 
 /* rbq_gemv -- rbq_gemm with M = 1 (one decode token):
@@ -167,10 +171,14 @@ typedef enum rbq_path {
                                (tile, chunk) units are split evenly over 12 waves while
                                4 build the activation image: M <= 2, K <= 2,
                                in <= 16384; taken for layers of many rows */
-    RBQ_PATH_GROUP = 6      /* int8 MFMA for one token with 128-column group scales
+    RBQ_PATH_GROUP = 6,     /* int8 MFMA for one token with 128-column group scales
                                (group_size 128, K <= 4, in % 512 == 0, in <= 16384,
                                scales 8-byte aligned); the lanes that hold a group's
                                MFMA sums apply its scales.  Layout as RBQ_PATH_FLAT */
+    RBQ_PATH_SPLIT = 7      /* int8 MFMA for 2..16 tokens (per-row scales, K <= 2) with
+                               the input columns split over workgroups, each quantising
+                               only its slice; fp32 partial outputs in the workspace,
+                               added in slice order by a second kernel */
 } rbq_path;
 
 /* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for

@@ -115,6 +115,11 @@ def test_path_override_roundtrip():
     assert L.rbq_select_path(rbq.shape(22016, 4096, 2), 2) == rbq.PATH_FLAT
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 2) == rbq.PATH_STREAM
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 4) == rbq.PATH_DECODE
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 16) == rbq.PATH_DECODE
+    # the split family needs a workspace only where it can run
+    assert L.rbq_gemm_workspace_bytes(rbq.shape(4096, 11008, 2), 1) == 0
+    assert L.rbq_gemm_workspace_bytes(rbq.shape(5120, 5120, 4, 128), 16) == 0
+    assert L.rbq_select_path(rbq.shape(11008, 4096, 2), 4) == rbq.PATH_FLAT
     assert L.rbq_select_path(rbq.shape(4096, 4096, 8), 1) == rbq.PATH_VALU
 
 

@@ -24,7 +24,8 @@ MAX_ABS_RMS = 1e-2
 # kernel families rbq_gemm can be forced to, with the largest M each takes
 PATHS = {"valu": (rbq.PATH_VALU, 1 << 30), "decode": (rbq.PATH_DECODE, 64),
          "stream": (rbq.PATH_STREAM, 2), "flat": (rbq.PATH_FLAT, 16),
-         "group": (rbq.PATH_GROUP, 1), "prefill": (rbq.PATH_PREFILL, 1 << 30)}
+         "group": (rbq.PATH_GROUP, 1), "split": (rbq.PATH_SPLIT, 16),
+         "prefill": (rbq.PATH_PREFILL, 1 << 30)}
 
 
 def dev():
@@ -411,3 +412,31 @@ def test_graph_replays_match_eager():
             assert torch.equal(enc[j][1], ref_s[j]), (rep, j, "scales")
             assert torch.equal(Y[j], ref_y[j]), (rep, j, "y")
         _ = rbq.gemm(enc[0][0], enc[0][1], X[0], 0)   # eager work between replays
+
+
+def test_split_path_workspace_contract():
+    """Without workspace the automatic choice takes a family that needs none
+    (same result); the forced split family refuses a missing workspace."""
+    K, out, inf, M = 2, 256, 2048, 8
+    p = workloads.random_planes(K, out, inf, seed=31)
+    s = workloads.random_scales(K, out, 1, seed=32)
+    X = workloads.gaussian_activations(M, inf, seed=33)
+    L = rbq.lib()
+    shp = rbq.shape(out, inf, K, 0)
+    assert L.rbq_gemm_workspace_bytes(shp, M) > 0
+    assert L.rbq_gemm_workspace_bytes(shp, 1) == 0
+    pt = torch.from_numpy(p.view(np.int32)).to(dev())
+    st = torch.from_numpy(s.view(np.float16)).to(dev())
+    xt = torch.from_numpy(X.view(np.float16)).to(dev())
+    Y = torch.empty((M, out), dtype=torch.float16, device=dev())
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = L.rbq_gemm(pt.data_ptr(), st.data_ptr(), shp, xt.data_ptr(), M, Y.data_ptr(), None, 0, stream)
+    assert rc == rbq.RBQ_OK
+    torch.cuda.synchronize()
+    assert_close(Y.cpu().numpy().astype(np.float64), oracle.gemm(p, s, X, 0), "no workspace")
+    old = rbq.set_path(rbq.PATH_SPLIT)
+    try:
+        rc = L.rbq_gemm(pt.data_ptr(), st.data_ptr(), shp, xt.data_ptr(), M, Y.data_ptr(), None, 0, stream)
+        assert rc == rbq.RBQ_ERR_INVALID_ARG
+    finally:
+        rbq.set_path(old)
