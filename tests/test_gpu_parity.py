@@ -256,6 +256,20 @@ def test_gemm_ragged_random_signed_scales(path, out, inf, K, group, M):
     assert_close(Y, oracle.gemm(p, s, X, group), f"{out}x{inf} K={K} g={group} M={M}")
 
 
+@pytest.mark.parametrize("out,inf,K,group,M", [
+    (300, 1024, 1, 0, 200), (520, 2048, 2, 128, 300), (257, 640, 2, 0, 129),
+    (2304, 1024, 2, 0, 300), (1000, 4096, 1, 128, 257), (64, 8192, 2, 128, 2048)])
+def test_gemm_prefill_tiles_ragged(out, inf, K, group, M):
+    """Several 128-token and 256-row tiles with ragged last tiles, one and two
+    planes, per-row and per-128-column scales (signed)."""
+    p = workloads.random_planes(K, out, inf, seed=out + 7 * inf)
+    G = inf // group if group else 1
+    s = workloads.random_scales(K, out, G, seed=M + 3 * K, signed=True)
+    X = workloads.gaussian_activations(M, inf, seed=inf + 5 * M)
+    Y = gpu_gemm(p, s, X, group, rbq.PATH_PREFILL)
+    assert_close(Y, oracle.gemm(p, s, X, group), f"{out}x{inf} K={K} g={group} M={M}")
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 def test_gemm_closed_forms(path):
     K, out, inf, group = 2, 96, 4096, 0
