@@ -428,6 +428,33 @@ def test_graph_replays_match_eager():
         _ = rbq.gemm(enc[0][0], enc[0][1], X[0], 0)   # eager work between replays
 
 
+def test_split_workspace_any_contents():
+    """The workspace needs no initialisation: filled with 0x00, 0xFF or
+    0xA5, then reused by calls of other shapes (other slice and row-group
+    counts), it gives the oracle's result every time."""
+    cases = [(2, 700, 4096, 16), (1, 300, 9216, 9), (2, 2000, 1536, 4), (2, 700, 4096, 16)]
+    L = rbq.lib()
+    need = max(L.rbq_gemm_workspace_bytes(rbq.shape(o, i, K, 0), M) for K, o, i, M in cases)
+    assert need > 0
+    old = rbq.set_path(rbq.PATH_SPLIT)
+    try:
+        for fill in (0x00, 0xFF, 0xA5):
+            ws = torch.full((need,), fill, dtype=torch.uint8, device=dev())
+            for K, out, inf, M in cases:
+                p = workloads.random_planes(K, out, inf, seed=out + inf + fill)
+                s = workloads.random_scales(K, out, 1, seed=M + fill, signed=True)
+                X = workloads.gaussian_activations(M, inf, seed=inf + M + fill)
+                pt = torch.from_numpy(p.view(np.int32)).to(dev())
+                st = torch.from_numpy(s.view(np.float16)).to(dev())
+                xt = torch.from_numpy(X.view(np.float16)).to(dev())
+                Y = rbq.gemm(pt, st, xt, 0, workspace=ws)
+                torch.cuda.synchronize()
+                assert_close(Y.cpu().numpy().astype(np.float64), oracle.gemm(p, s, X, 0),
+                             f"fill {fill:#x} {out}x{inf} K={K} M={M}")
+    finally:
+        rbq.set_path(old)
+
+
 def test_split_path_workspace_contract():
     """Without workspace the automatic choice takes a family that needs none
     (same result); the forced split family refuses a missing workspace."""
