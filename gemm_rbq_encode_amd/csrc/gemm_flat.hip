@@ -132,14 +132,31 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             a_bits[k] = scales[(size_t)k * out + frow];
     };
 
-    // (no load is outstanding here, so the barrier waits for nothing else)
-    if (tid == 0)
-        counters[0] = counters[1] = 0;
-    for (int i = tid; i < ntl * K * NC * TILE_ROWS; i += FL_THREADS)
-        red[i] = 0;
-    if (tid < 4)
-        reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
-    __syncthreads();
+    // LDS set-up, then the entry barrier.  One token: before the branches
+    // below.  Several tokens: the image waves first request their
+    // activations, and the two kinds of waves reach a barrier that waits for
+    // LDS only (so those loads stay in flight) in their own branches (each
+    // wave passes one s_barrier).  (The same split for one token measured
+    // slower.)
+    auto lds_init = [&]() {
+        if (tid == 0)
+            counters[0] = counters[1] = 0;
+        for (int i = tid; i < ntl * K * NC * TILE_ROWS; i += FL_THREADS)
+            red[i] = 0;
+        if (tid < 4)
+            reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
+    };
+    auto entry = [&]() {
+        if constexpr (MT > 1) {
+            lds_init();
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    };
+    if constexpr (MT == 1) {
+        // (no load is outstanding here, so the barrier waits for nothing else)
+        lds_init();
+        __syncthreads();
+    }
 
     if (wave < FL_PREP) {
         // ================= image waves =================
@@ -164,6 +181,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                 xw[m][j][1] = xp[1];
             }
         }
+        entry();
         load_scales();
         // per-token maximum of |x| (fp16 bit patterns without the sign
         // compare like magnitudes; clamped repeats only repeat real values)
@@ -254,6 +272,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         if (lane == 0)
             __hip_atomic_fetch_add(&counters[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
+        entry();
         // ================= stream waves =================
         const int sw = wave - FL_PREP;
         const int U = ntl * nchunks;
