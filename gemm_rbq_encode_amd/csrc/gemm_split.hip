@@ -1,38 +1,45 @@
 // gemm_split.hip -- residual-binary GEMM for a few tokens (2 .. 16), the
-// input columns split over workgroups.
+// input columns split over workgroups, on the fp16 matrix cores.
 //
-// y[m][r] = sum_k a_k[r] * (2 S_k - sum x), S_k = sum of x over the set bits
-// of row r of plane k ("RaBiT" summary, paperlayer.ai, sections 4.1 and 4.2:
-// binary cores with per-channel scales, the K paths side by side).
+// Y = X What^T with What[r][j] = sum_k a_k[r] (bit ? +1 : -1) ("RaBiT"
+// summary, paperlayer.ai, section 4.1: binary cores with per-channel scales,
+// the K paths side by side), rounded once to fp16, fp32 accumulation, one
+// fp16 rounding of each output.
 //
-// Why split the columns.  With several tokens every workgroup that covers a
-// whole row has to quantise every token over the whole row, and that
-// per-workgroup VALU work (about 6 operations per column and token) grows
-// with the token count until it dominates: 16 tokens of 11008 columns take
-// ~7 us of one compute unit.  Here workgroup (r, c) covers the 16-row tiles
-// of row group r but only the 512-column chunks of slice c, so it quantises
-// only its slice, with its own power-of-two scale per token (each partial sum
-// is converted back to float before slices are added).  The slices' fp32
-// partial outputs go to a workspace and a second kernel adds them in slice
-// order and rounds once to fp16.
+// Why not the int8 route of the one-token kernels.  Those quantise x into
+// signed 8-bit limbs per workgroup, and with several tokens that work (about
+// 6 VALU operations per column and token), the per-token maxima and the
+// limb image grow with the token count until they dominate.  Here x goes to
+// LDS unchanged as fp16, and What is formed in registers from the sign words
+// by byte-table lookups: the four values sum_k +-a_k of a row held as a byte
+// table (low bytes in one register, high bytes in another), 8 weights from
+// four v_perm_b32 whose selectors come from the sign bits (about 4 VALU
+// operations per 2 weights, the same for any token count).  An int8 version
+// of this kernel measured 487 GB/s for 16 tokens on the Llama-2-7B shapes,
+// this one 753 GB/s.
 //
-// Inside a workgroup (16 waves, one per compute unit), in three phases
-// separated by barriers that wait for LDS traffic only:
-//   * every wave requests its share of the slice of x (16-column pieces of
-//     single tokens), then the weights of its first two (tile, chunk) units;
-//   * all waves quantise x into an LDS image laid out like the B operand of
-//     v_mfma_i32_16x16x64_i8 (token groups of 4 tokens x 3 limbs = 12
-//     columns), per-token maxima and sums of q meeting in LDS atomics (the
-//     sums as 64-bit integers, so exact and order-free);
-//   * all waves stream their units.  The A operand is the weight word shifted
-//     right by the bit position s and masked with 0x01010101 (bytes 0 or 1),
-//     so every bit position adds into one accumulator per plane and token
-//     group, and the masks are shared by the token groups.  Partial sums of a
-//     tile meet in LDS as int32 additions (exact), and one thread per (row,
-//     token) converts them with the row's scales.
-// An earlier version left the quantisation to 4 waves (one per SIMD), one
-// token group at a time: 16 tokens took ~8 us there, latency rather than
-// arithmetic.
+// Why split the columns.  16 tokens x 4096 columns of x are 128 KB, the most
+// one workgroup's LDS holds next to its partial sums.  Workgroup (r, c)
+// covers the 16-row tiles of row group r and the 512-column chunks of slice
+// c (up to 8 chunks per slice, fewer while LDS does not fit).  With one slice
+// the workgroup writes Y; with several, fp32 partial outputs go to the
+// workspace and a second kernel adds them in slice order (adding them in the
+// last workgroup to finish, behind device-coherent stores, measured slower).
+//
+// Inside a workgroup (16 waves, one per compute unit):
+//   * every wave requests the scales of its first two tiles, its share of
+//     the slice of x (direct global-to-LDS loads, 16 tokens padded with
+//     copies of the last one), then the weights of its first two units;
+//   * a barrier once its x loads have landed (the weight loads stay in
+//     flight); pieces past the row end are then zeroed;
+//   * each wave streams its contiguous range of (tile, chunk) units: 16
+//     v_mfma_f32_16x16x32_f16 per unit (A = x, B = What).  Lane (li, lg)
+//     loads words 4lg .. 4lg+3 of row li of the chunk, and MFMA t of the
+//     unit takes byte t % 4 of word 4lg + t / 4 (x columns 128 lg + 8 t ..
+//     + 7 of the chunk), so no data crosses lanes;
+//   * the fp32 sums of a wave's run of units in one tile go to one LDS slot
+//     per run, and one thread per (row, token) adds a tile's slots in unit
+//     order (deterministic).
 #include "rbq_device.h"
 #include "rbq_kernels.h"
 
@@ -40,47 +47,49 @@ namespace rbq {
 
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int SP_WAVES = 16;
 constexpr int SP_THREADS = SP_WAVES * RBQ_WAVE;
 constexpr int TILE_ROWS = 16;
 constexpr int CHUNK_WORDS = 16;                        // 512 columns
-constexpr int NLIMB = 3;
-constexpr int TOK = 4;                                 // tokens per group
-constexpr int NC = NLIMB * TOK;                        // MFMA columns per group
-constexpr int ENTRY_ROW = NC * 16;                     // one lane group, one bit position
-constexpr int IMG_CHUNK = 8 * 4 * ENTRY_ROW + 64;      // one chunk of one group (padded)
 constexpr int SP_MAX_CPS = 8;                          // chunks per slice
-#ifndef SP_TARGET_CPS
-#define SP_TARGET_CPS 2
-#endif
 constexpr int SP_MAX_M = 16;
 constexpr int SP_MAX_TILES = SP_THREADS / TILE_ROWS;
 
-size_t split_lds_bytes(int cps, int ng, int K, int tpw) {
-    return (size_t)cps * ng * IMG_CHUNK + 16 + (size_t)tpw * ng * K * NC * TILE_ROWS * 4;
+// Y[m][r] = fp16(sum over slices of P[s][m][r]), slices in order.
+__global__ __launch_bounds__(256) void split_combine_kernel(const float *__restrict__ P, int S,
+                                                            int n, uint16_t *__restrict__ Y) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        float y = 0.0f;
+        for (int s = 0; s < S; ++s)
+            y += P[(size_t)s * n + i];
+        Y[i] = f2h(y);
+    }
 }
 
-// Workgroup barrier that waits for this wave's LDS operations only: global
-// loads already requested stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// x slot layout: [chunk][token][64 pieces of 16 B], piece q of token m at
+// position q ^ m (m < 16), so the A-fragment reads of 16 lanes (16 tokens,
+// one piece) hit distinct banks; one load instruction writes one token's
+// 1 KB chunk row, lane i the 16 bytes at position i.
+constexpr int SF_XCHUNK = 16 * 1024;                  // 16 tokens x 512 fp16
+
+size_t splitf_lds_bytes(int cps, int tpw) {
+    return (size_t)cps * SF_XCHUNK + (size_t)tpw * cps * 1024;
 }
 
-// Grid: x = row group (tiles [x T / NR, (x+1) T / NR)), y = column slice
-// (chunks [y C / S, (y+1) C / S)).  P = fp32 partial outputs [S][M][out].
-// IPT = (half-word, token) items per thread in the quantisation phase.
-template <int K, int NG, int IPT>
-__global__ __launch_bounds__(SP_THREADS, 1) void gemm_split_kernel(
+__device__ __forceinline__ uint32_t sf_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <int K>
+__global__ __launch_bounds__(SP_THREADS, 1) void gemm_splitf_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
-    const uint16_t *__restrict__ X, int M, float *__restrict__ P) {
+    const uint16_t *__restrict__ X, int M, float *__restrict__ P, uint16_t *__restrict__ Y) {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ uint32_t tmax[NG * TOK];
-    __shared__ unsigned long long tsum[NG * TOK];   // sum of q per token, exact
-
     const int tid = threadIdx.x;
     const int lane = tid & (RBQ_WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / RBQ_WAVE);
@@ -96,39 +105,49 @@ __global__ __launch_bounds__(SP_THREADS, 1) void gemm_split_kernel(
     const int t0 = (int)(((long)blockIdx.x * T) / NR);
     const int t1 = (int)(((long)(blockIdx.x + 1) * T) / NR);
     const int ntl = t1 - t0;
-    const int img_group = cps * IMG_CHUNK;            // one token group's image
-    const int pad = NG * img_group;                   // 16 zero bytes for unused MFMA columns
-    int *red = reinterpret_cast<int *>(lds + pad + 16);   // [ntl][NG][K][NC][16]
-
-    // ---- activations first (their wait must not include the weights):
-    // item i = token i / nhs, half-word i % nhs of the slice (16 columns);
-    // half-words past the row end load its last one and get the scale 0
-    const int nhs = cps * CHUNK_WORDS * 2;                                   // half-words of the slice
-    const int nh = min(cps * CHUNK_WORDS, words - c0 * CHUNK_WORDS) * 2;    // those inside the row
-    const int nitems = M * nhs;
-    v4u xw[IPT][2];
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int it = min(tid + j * SP_THREADS, nitems - 1);
-        const int m = it / nhs, h = it - m * nhs;
-        const v4u *xp = reinterpret_cast<const v4u *>(X + (size_t)m * in + 16 * (c0 * CHUNK_WORDS * 2 + min(h, nh - 1)));
-        xw[j][0] = xp[0];
-        xw[j][1] = xp[1];
-    }
-
-    // ---- then each wave's first two (tile, chunk) units; units are split
-    // evenly, in order, over all 16 waves
     const int U = ntl * cps;
+    float *slots = reinterpret_cast<float *>(lds + cps * SF_XCHUNK);   // [U][64 lanes][4]
+    __shared__ uint32_t run_start[16];                                   // bit u: a wave's range starts at u
+    if (tid < 16)
+        run_start[tid] = 0u;
+
+    // this wave's contiguous unit range, and the scales of this lane's row in
+    // its first two tiles (a run rarely spans more; later tiles load theirs
+    // when they start), requested before the x loads so that the wait for
+    // those below counts only the weight loads after them
     const int u0 = (wave * U) / SP_WAVES;
     const int u1 = ((wave + 1) * U) / SP_WAVES;
     const int n = u1 - u0;
+    const uint32_t magic = ((1u << 21) + cps - 1) / cps;   // u / cps for u < 2^11
+    int ptile = t0 + (int)(((uint32_t)u0 * magic) >> 21);
+    // (packed: plane k in bits 16k; scalars, not an array, so that they stay
+    // in registers)
+    auto row_scales = [&](int t) __attribute__((always_inline)) {
+        const int row = min(t * TILE_ROWS + li, out - 1);
+        uint32_t v = scales[row];
+        if (K > 1)
+            v |= (uint32_t)scales[(size_t)out + row] << 16;
+        return v;
+    };
+    const uint32_t sc0 = row_scales(ptile), sc1 = row_scales(ptile + 1);
+
+    // ---- x slice into LDS: load i (of 16 cps) = token i % 16, chunk i / 16;
+    // pieces past the row end read its last piece and are zeroed below
+    const uint32_t xl = __builtin_amdgcn_readfirstlane(sf_lds_addr(lds));
+    const int npieces = in / 8;                         // 16-byte pieces of a row
+    for (int i = wave; i < 16 * cps; i += SP_WAVES) {
+        const int m = i & 15, c = i >> 4;
+        const int q = lane ^ m;
+        const int piece = min((c0 + c) * 64 + q, npieces - 1);
+        const uint32_t voff = (uint32_t)((min(m, M - 1) * in + 8 * piece) * 2);
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(X),
+                     "s"(xl + (uint32_t)(c * SF_XCHUNK + m * 1024))
+                     : "memory");
+    }
+
+    // ---- then the weights of each wave's first two units
     const int ulast = max(min(u0, U - 1), u1 - 1);
     const size_t plane_stride = (size_t)out * words;
-    // u -> (tile u / cps, chunk u % cps): exact for u < 2^11 and cps <= 32
-    const uint32_t magic = ((1u << 21) + cps - 1) / cps;
-    // lane (li, lg): words 4lg .. 4lg+3 of the chunk in row li of the tile
-    // (rows past the end read the last row, words past the row end its last
-    // four words, which meet zeros in the image)
     int lnext = u0;
     v4u ring[2][K];
     auto load_unit = [&](v4u (&slot)[K]) {
@@ -144,133 +163,93 @@ __global__ __launch_bounds__(SP_THREADS, 1) void gemm_split_kernel(
     };
     load_unit(ring[0]);
     load_unit(ring[1]);
-
-    if (tid < NG * TOK) {
-        tmax[tid] = 0u;
-        tsum[tid] = 0ull;
-    }
-    for (int i = tid; i < ntl * NG * K * NC * TILE_ROWS; i += SP_THREADS)
-        red[i] = 0;
-    if (tid < 4)
-        reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
-    lds_barrier();
-
-    // ---- quantisation by all waves: per-token maximum of |x| over the slice
-    // (fp16 bit patterns without the sign compare like magnitudes)
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int it = tid + j * SP_THREADS;
-        if (it < nitems) {
-            v2u16 mx2 = (v2u16){0, 0};
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, xw[j][hh][c] & 0x7FFF7FFFu));
-            __hip_atomic_fetch_max(&tmax[it / nhs], max((uint32_t)mx2.x, (uint32_t)mx2.y), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    // this wave's x loads have landed (only its 2K weight loads are younger)
+    // and its LDS stores are done
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * K) : "memory");
+    if (lane == 0 && n > 0)
+        __hip_atomic_fetch_or(&run_start[u0 >> 5], 1u << (u0 & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((c0 + cps) * 64 > npieces) {
+        // zero the pieces past the row end in the slice's last chunk
+        const int c = cps - 1, q0 = npieces - (c0 + c) * 64;
+        for (int i = tid; i < 16 * 64; i += SP_THREADS) {
+            const int m = i >> 6, q = i & 63;
+            if (q >= q0)
+                *reinterpret_cast<v4u *>(lds + c * SF_XCHUNK + m * 1024 + 16 * (q ^ m)) = (v4u){0, 0, 0, 0};
         }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    lds_barrier();
-    // q = round(x * 2^sh), |x| < 2^E, sh = 22 - E, |q| <= 2^22; v = q + 0x808080
-    // from fma(x, 2^sh, 1.5*2^23); its bytes xor 0x80 are the limbs.  Image
-    // entry (word w, bit s) of token group g: columns 32w + 8kk + s, one byte
-    // each, at [g][chunk w/16][s][lane group (w/4)%4][column 3 (m%4) + l][4 (w%4) + kk]
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int it = tid + j * SP_THREADS;
-        if (it < nitems) {
-            const int m = it / nhs, h = it - m * nhs;
-            const int e = (int)(tmax[m] >> 10);
-            const int sh = 22 - ((e == 0 ? 1 : e) - 14);
-            const float scale = h < nh ? __builtin_ldexpf(1.0f, sh) : 0.0f;
-            const int w = h >> 1, eh = h & 1;   // word of the slice
-            unsigned char *dst = lds + (m / TOK) * img_group + (w / CHUNK_WORDS) * IMG_CHUNK +
-                                 ((w >> 2) & 3) * ENTRY_ROW + (w & 3) * 4 + 2 * eh + (NLIMB * (m % TOK)) * 16;
-            int psum = 0;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const uint32_t uu0 = xw[j][0][s >> 1], uu1 = xw[j][1][s >> 1];
-                const uint16_t h0 = (s & 1) ? (uint16_t)(uu0 >> 16) : (uint16_t)uu0;
-                const uint16_t h1 = (s & 1) ? (uint16_t)(uu1 >> 16) : (uint16_t)uu1;
-                const uint32_t v0 =
-                    __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) - 0x4ABF7F80u;
-                const uint32_t v1 =
-                    __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) - 0x4ABF7F80u;
-                psum += (int)(v0 + v1) - 2 * 0x808080;
-                const uint32_t l01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u) ^ 0x80808080u;
-                const uint32_t l2 = __builtin_amdgcn_perm(v1, v0, 0x0C0C0602u) ^ 0x8080u;
-                unsigned char *d = dst + s * (4 * ENTRY_ROW);
-                *reinterpret_cast<uint16_t *>(d) = (uint16_t)l01;
-                *reinterpret_cast<uint16_t *>(d + 16) = (uint16_t)(l01 >> 16);
-                *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
-            }
-            __hip_atomic_fetch_add(&tsum[m], (unsigned long long)(long long)psum, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-    }
-    lds_barrier();
 
-    // ---- streaming by all waves.  A operand: the word shifted right by the
-    // bit position s, masked with 0x01010101 (bytes 0 or 1), shared by the
-    // token groups; one accumulator per plane and token group.
-    v4i acc[NG][K];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
+    // ---- streaming
+    const int tfirst = ptile;
+    int pchunk = u0 - (ptile - t0) * cps;
+    int seg = u0;                      // first unit of the current run
+    uint32_t plo = 0, phi = 0;
+    auto tables = [&]() __attribute__((always_inline)) {
+        const uint32_t sv = ptile == tfirst ? sc0 : ptile == tfirst + 1 ? sc1 : row_scales(ptile);
+        float a[K];
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            acc[g][k] = (v4i){0, 0, 0, 0};
-    const bool bl = li < NC;
-    const int b_off = bl ? (lg * NC + li) * 16 : pad;
-    const int b_stride = bl ? 4 * ENTRY_ROW : 0;
-    const int b_chunk = bl ? IMG_CHUNK : 0;
-    const int b_group = bl ? img_group : 0;
-    int ptile = t0 + (int)(((uint32_t)u0 * magic) >> 21);
-    int pchunk = u0 - (ptile - t0) * cps;
-    auto chunk = [&](const v4u (&wv)[K]) {
-        const unsigned char *bp = lds + b_off + pchunk * b_chunk;
+            a[k] = h2f((uint16_t)(sv >> (16 * k)));
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            v4i av[K];
+        for (int v = 0; v < 4; ++v) {
+            float w = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                av[k] = (v4i){(int)((wv[k].x >> s) & 0x01010101u), (int)((wv[k].y >> s) & 0x01010101u),
-                              (int)((wv[k].z >> s) & 0x01010101u), (int)((wv[k].w >> s) & 0x01010101u)};
+                w += ((v >> k) & 1) ? a[k] : -a[k];
+            const uint32_t hv = f2h(w);
+            lo |= (hv & 0xFFu) << (8 * v);
+            hi |= (hv >> 8) << (8 * v);
+        }
+        plo = lo;
+        phi = hi;
+    };
+    if (n > 0)
+        tables();
+    v4f acc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    const int a_row = li * 1024;
+    auto chunk = [&](const v4u (&wv)[K]) {
+        const unsigned char *xb = lds + pchunk * SF_XCHUNK + a_row;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const v4i b = *reinterpret_cast<const v4i *>(bp + g * b_group + s * b_stride);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w1 = wv[0][j], w2 = K > 1 ? wv[K > 1 ? 1 : 0][j] : 0u;
+            // 2-bit table index of every even (z) and odd (zo) column
+            const uint32_t z = (w1 & 0x55555555u) | ((w2 & 0x55555555u) << 1);
+            const uint32_t zo = ((w1 >> 1) & 0x55555555u) | (w2 & 0xAAAAAAAAu);
+            const uint32_t y01 = __builtin_amdgcn_perm(zo, z, 0x05040100u);   // bytes 0, 1
+            const uint32_t y23 = __builtin_amdgcn_perm(zo, z, 0x07060302u);   // bytes 2, 3
+            v4u wf[4];
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    acc[g][k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[k], b, acc[g][k], 0, 0, 0);
+            for (int p = 0; p < 4; ++p) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t ym = ((half ? y23 : y01) >> (2 * p)) & 0x03030303u;
+                    const uint32_t ym4 = ym | 0x04040404u;
+                    wf[2 * half][p] = __builtin_amdgcn_perm(phi, plo, __builtin_amdgcn_perm(ym4, ym, 0x06020400u));
+                    wf[2 * half + 1][p] = __builtin_amdgcn_perm(phi, plo, __builtin_amdgcn_perm(ym4, ym, 0x07030501u));
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int t = 4 * j + b;      // columns 128 lg + 8 t .. + 7
+                const v8h xa = *reinterpret_cast<const v8h *>(xb + 16 * ((16 * lg + t) ^ li));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(v8h, wf[b]), acc, 0, 0, 0);
             }
         }
     };
-    // at a tile's end or at the wave's last unit, add the sums into LDS
-    // (lane (li, lg) holds rows 4lg + v of MFMA column li)
+    // at a tile's end or the wave's last unit: the run's sums to its slot
     auto step = [&](int i) {
         const bool tile_end = ++pchunk == cps;
         if (tile_end || i == n - 1) {
-            if (li < NC) {
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-#pragma unroll
-                    for (int k = 0; k < K; ++k) {
-                        int *rp = red + ((((ptile - t0) * NG + g) * K + k) * NC + li) * TILE_ROWS + 4 * lg;
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            __hip_atomic_fetch_add(rp + v, acc[g][k][v], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-                    }
-            }
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-#pragma unroll
-                for (int k = 0; k < K; ++k)
-                    acc[g][k] = (v4i){0, 0, 0, 0};
+            *reinterpret_cast<v4f *>(slots + ((size_t)seg * 64 + lane) * 4) = acc;
+            acc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+            seg = u0 + i + 1;
         }
         if (tile_end) {
             pchunk = 0;
             ++ptile;
+            if (i + 1 < n)
+                tables();
         }
     };
     const int nbk = (n + 1) / 2;
@@ -294,38 +273,23 @@ __global__ __launch_bounds__(SP_THREADS, 1) void gemm_split_kernel(
     }
     __syncthreads();
 
-    // ---- one thread per (row, token): column 3m + l of a group holds
-    // sum(bit l_j); sum(bit q) = T_0 + 2^8 T_1 + 2^16 T_2 (exact in fp64) and
-    // the slice's partial y = sum_k a_k (2 sum(bit q) - sum q) 2^-sh
+    // ---- one thread per (row, token): the tile's runs in unit order (a run
+    // starts where its tile or some wave's range starts).  C of a 16 x 16
+    // MFMA tile: token i, row j in lane j + 16 (i / 4), register i % 4.
     const int rows = min(ntl * TILE_ROWS, out - t0 * TILE_ROWS);
     for (int idx = tid; idx < rows * M; idx += SP_THREADS) {
         const int m = idx / rows, rr = idx - m * rows;
-        const int tl = rr / TILE_ROWS, i = rr % TILE_ROWS;
-        const int g = m / TOK, mm = m % TOK;
+        const int tl = rr >> 4, i = rr & 15;
         const int row = t0 * TILE_ROWS + rr;
-        const int e = (int)(tmax[m] >> 10);
-        const int sh = 22 - ((e == 0 ? 1 : e) - 14);
-        const double sx = (double)(long long)tsum[m];
+        const float *sp = slots + i * 4 + 16 * 4 * (m >> 2) + (m & 3);
         float y = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int *rp = red + (((tl * NG + g) * K + k) * NC + NLIMB * mm) * TILE_ROWS + i;
-            const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] + 65536.0 * (double)rp[2 * TILE_ROWS];
-            y += h2f(scales[(size_t)k * out + row]) * (float)(2.0 * t - sx);
-        }
-        P[((size_t)blockIdx.y * M + m) * out + row] = __builtin_ldexpf(y, -sh);
-    }
-}
-
-// Y[m][r] = fp16(sum over slices of P[s][m][r]), slices in order.
-__global__ __launch_bounds__(256) void split_combine_kernel(const float *__restrict__ P, int S,
-                                                            int n, uint16_t *__restrict__ Y) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) {
-        float y = 0.0f;
-        for (int s = 0; s < S; ++s)
-            y += P[(size_t)s * n + i];
-        Y[i] = f2h(y);
+        for (int u = tl * cps; u < (tl + 1) * cps; ++u)
+            if (u == tl * cps || (run_start[u >> 5] >> (u & 31)) & 1u)
+                y += sp[(size_t)u * 256];
+        if (S == 1)
+            Y[(size_t)m * out + row] = f2h(y);
+        else
+            P[((size_t)blockIdx.y * M + m) * out + row] = y;
     }
 }
 
@@ -355,33 +319,30 @@ size_t split_lds_limit() {
 }
 
 struct SplitPlan {
-    int S = 0, NR = 0, tpw = 0, cps = 0, ng = 0;
+    int S = 0, NR = 0, tpw = 0, cps = 0;
     size_t lds = 0;
 };
 
-// About one workgroup per compute unit; slices of SP_TARGET_CPS chunks when
-// the image and the partial sums of the then taller row groups fit in LDS
-// (narrow slices keep the per-workgroup quantisation short), wider ones
-// otherwise.
-SplitPlan split_plan(int out, int in, int K, int M) {
+// About one workgroup per compute unit; slices of SP_MAX_CPS chunks (one
+// slice, no second kernel, for in <= 4096), narrower while the x slice and
+// the partial-sum slots do not fit in LDS.  (Slices of 2 or 4 chunks
+// measured slower: 632 and 672 GB/s against 753 for 16 tokens.)
+SplitPlan split_plan(int out, int in) {
     SplitPlan p;
     const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
-    const int ng = (M + TOK - 1) / TOK;
-    const int s_hi = (nchunks + SP_TARGET_CPS - 1) / SP_TARGET_CPS;
-    const int s_lo = (nchunks + SP_MAX_CPS - 1) / SP_MAX_CPS;
-    for (int S = s_hi; S >= s_lo; --S) {
+    for (int want = SP_MAX_CPS; want >= 1; --want) {
+        const int S = (nchunks + want - 1) / want;
         const int cps = (nchunks + S - 1) / S;
         int NR = split_num_cus() / S;
         NR = NR < 1 ? 1 : (NR > T ? T : NR);
         const int tpw = (T + NR - 1) / NR;
-        const size_t lds = split_lds_bytes(cps, ng, K, tpw);
+        const size_t lds = splitf_lds_bytes(cps, tpw);
         if (tpw <= SP_MAX_TILES && lds <= split_lds_limit()) {
             p.S = S;
             p.NR = NR;
             p.tpw = tpw;
             p.cps = cps;
-            p.ng = ng;
             p.lds = lds;
             return p;
         }
@@ -389,75 +350,55 @@ SplitPlan split_plan(int out, int in, int K, int M) {
     return p;
 }
 
-template <int K, int NG>
-hipError_t launch_kg(const uint32_t *planes, const uint16_t *scales, int out, int in, const uint16_t *X,
-                     int M, uint16_t *Y, float *P, const SplitPlan &pl, hipStream_t st) {
-    const int ipt = (M * pl.cps * CHUNK_WORDS * 2 + SP_THREADS - 1) / SP_THREADS;
-    if (ipt <= 1)
-        hipLaunchKernelGGL((gemm_split_kernel<K, NG, 1>), dim3(pl.NR, pl.S), dim3(SP_THREADS), pl.lds, st,
-                           planes, scales, out, in, X, M, P);
-    else if (ipt <= 2)
-        hipLaunchKernelGGL((gemm_split_kernel<K, NG, 2>), dim3(pl.NR, pl.S), dim3(SP_THREADS), pl.lds, st,
-                           planes, scales, out, in, X, M, P);
-    else if (ipt <= 4)
-        hipLaunchKernelGGL((gemm_split_kernel<K, NG, 4>), dim3(pl.NR, pl.S), dim3(SP_THREADS), pl.lds, st,
-                           planes, scales, out, in, X, M, P);
-    else
-        hipLaunchKernelGGL((gemm_split_kernel<K, NG, 8>), dim3(pl.NR, pl.S), dim3(SP_THREADS), pl.lds, st,
-                           planes, scales, out, in, X, M, P);
+template <int K>
+hipError_t launch_f(const uint32_t *planes, const uint16_t *scales, int out, int in, const uint16_t *X,
+                    int M, uint16_t *Y, float *P, const SplitPlan &pl, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_splitf_kernel<K>), dim3(pl.NR, pl.S), dim3(SP_THREADS), pl.lds, st, planes, scales,
+                       out, in, X, M, P, Y);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || pl.S == 1)
         return e;
     const int n = M * out;
     hipLaunchKernelGGL(split_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, st, P, pl.S, n, Y);
     return hipGetLastError();
 }
 
-template <int K>
-hipError_t launch_k(const uint32_t *planes, const uint16_t *scales, int out, int in, const uint16_t *X,
-                    int M, uint16_t *Y, float *P, const SplitPlan &pl, hipStream_t st) {
-    switch (pl.ng) {
-    case 1: return launch_kg<K, 1>(planes, scales, out, in, X, M, Y, P, pl, st);
-    case 2: return launch_kg<K, 2>(planes, scales, out, in, X, M, Y, P, pl, st);
-    case 3: return launch_kg<K, 3>(planes, scales, out, in, X, M, Y, P, pl, st);
-    default: return launch_kg<K, 4>(planes, scales, out, in, X, M, Y, P, pl, st);
-    }
-}
-
 }  // namespace
 
 bool split_supports(int out, int in, int K, int group_size, int M) {
     return group_size == 0 && K >= 1 && K <= 2 && in % 128 == 0 && in > 0 && M >= 2 &&
-           M <= SP_MAX_M && out >= 1 && split_plan(out, in, K, M).S > 0;
+           M <= SP_MAX_M && out >= 1 && split_plan(out, in).S > 0;
 }
 
 // Measured on MI355X (K = 2, Llama-2-7B shapes): ahead of the flat and
-// decode kernels from 8 tokens on for tall (at least two 16-row tiles per
-// compute unit) or wide (more than 8192 columns) layers -- 16 tokens:
-// 11008 x 4096 20.9 us (flat 26.4), 4096 x 11008 23.5 us (flat 39.5) --
-// and behind them with 4 tokens or on 4096 x 4096.
+// decode kernels from 8 tokens on for layers of at least one 16-row tile
+// per compute unit or more than 8192 columns -- 16 tokens: 4096 x 4096
+// 10.0 us (decode 14.7), 11008 x 4096 13.0 us (flat 27.0), 4096 x 11008
+// 15.6 us (flat 38.2) -- and behind the flat kernel with 4 tokens.
 bool split_preferred(int out, int in, int K, int group_size, int M) {
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
-    return M >= 8 && (T >= 2 * split_num_cus() || in > 8192) && split_supports(out, in, K, group_size, M);
+    return M >= 8 && (T >= split_num_cus() || in > 8192) && split_supports(out, in, K, group_size, M);
 }
 
+// fp32 partial outputs of the slices when there are several; none with one
 size_t split_workspace_bytes(int out, int in, int K, int group_size, int M) {
     if (!split_supports(out, in, K, group_size, M))
         return 0;
-    return (size_t)split_plan(out, in, K, M).S * M * out * sizeof(float);
+    const SplitPlan pl = split_plan(out, in);
+    return pl.S > 1 ? (size_t)pl.S * M * out * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_split(const uint32_t *planes, const uint16_t *scales, int out, int in, int K,
                              int group_size, const uint16_t *X, int M, uint16_t *Y, void *workspace,
                              size_t ws_bytes, hipStream_t st) {
-    if (!split_supports(out, in, K, group_size, M) ||
-        ws_bytes < split_workspace_bytes(out, in, K, group_size, M) || workspace == nullptr ||
+    const size_t need = split_workspace_bytes(out, in, K, group_size, M);
+    if (!split_supports(out, in, K, group_size, M) || ws_bytes < need || (need > 0 && workspace == nullptr) ||
         ((uintptr_t)workspace & 3u) != 0)
         return hipErrorInvalidValue;
-    const SplitPlan pl = split_plan(out, in, K, M);
+    const SplitPlan pl = split_plan(out, in);
     float *P = static_cast<float *>(workspace);
-    return K == 1 ? launch_k<1>(planes, scales, out, in, X, M, Y, P, pl, st)
-                  : launch_k<2>(planes, scales, out, in, X, M, Y, P, pl, st);
+    return K == 1 ? launch_f<1>(planes, scales, out, in, X, M, Y, P, pl, st)
+                  : launch_f<2>(planes, scales, out, in, X, M, Y, P, pl, st);
 }
 
 }  // namespace rbq

@@ -48,9 +48,10 @@ hipError_t launch_gemm_group(const uint32_t *planes, const uint16_t *scales, int
                              int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                              hipStream_t st);
 
-// Few-token GEMM (2 <= M <= 16, per-row scales, K <= 2) with the input
-// columns split over workgroups: fp32 partial outputs in a workspace of
-// split_workspace_bytes, added in slice order by a second kernel.
+// Few-token GEMM (2 <= M <= 16, per-row scales, K <= 2) on the fp16 matrix
+// cores with the input columns split over workgroups: with several slices,
+// fp32 partial outputs in a workspace of split_workspace_bytes (0 for one
+// slice), added in slice order by a second kernel.
 bool split_supports(int out, int in, int K, int group_size, int M);
 bool split_preferred(int out, int in, int K, int group_size, int M);
 size_t split_workspace_bytes(int out, int in, int K, int group_size, int M);

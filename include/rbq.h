@@ -146,11 +146,13 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes the split-column kernel family (RBQ_PATH_SPLIT) needs for
- * this shape and M: S * M * out fp32 partial outputs, S column slices; 0 when
- * that family cannot take the call (M < 2 or > 16, group scales, K > 2).
- * With less workspace than this (or none) rbq_gemm chooses another family;
- * a forced RBQ_PATH_SPLIT then returns RBQ_ERR_INVALID_ARG.  The workspace
- * must be 4-byte aligned; its contents need no initialisation. */
+ * this shape and M: S * M * out fp32 partial outputs when the input columns
+ * are split into S > 1 slices (in > 4096); 0 when one slice takes the whole
+ * row or when that family cannot take the call (M < 2 or > 16, group
+ * scales, K > 2).  With less workspace than this (or none) rbq_gemm chooses
+ * another family; a forced RBQ_PATH_SPLIT then returns RBQ_ERR_INVALID_ARG.
+ * The workspace must be 4-byte aligned; its contents need no
+ * initialisation. */
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M);
 
 /* rbq_gemv -- rbq_gemm with M = 1 (one decode token):
@@ -164,7 +166,8 @@ typedef enum rbq_path {
     RBQ_PATH_VALU = 1,      /* plain fp32 VALU bit loop, any M */
     RBQ_PATH_DECODE = 2,    /* int8 MFMA on masked bits, 512-column chunks split over
                                8 waves, 5 tokens per pass */
-    RBQ_PATH_PREFILL = 3,   /* fp16 MFMA on LDS-unpacked weights, large M */
+    RBQ_PATH_PREFILL = 3,   /* fp16 MFMA, large M: What formed in registers by table
+                               lookup (K <= 2) or unpacked into LDS (K = 3, 4) */
     RBQ_PATH_STREAM = 4,    /* int8 MFMA, whole rows streamed per wave: M <= 2, K <= 2,
                                in <= 16384 */
     RBQ_PATH_FLAT = 5,      /* int8 MFMA, one 16-wave workgroup per compute unit whose
@@ -175,10 +178,11 @@ typedef enum rbq_path {
                                (group_size 128, K <= 4, in % 512 == 0, in <= 16384,
                                scales 8-byte aligned); the lanes that hold a group's
                                MFMA sums apply its scales.  Layout as RBQ_PATH_FLAT */
-    RBQ_PATH_SPLIT = 7      /* int8 MFMA for 2..16 tokens (per-row scales, K <= 2) with
-                               the input columns split over workgroups, each quantising
-                               only its slice; fp32 partial outputs in the workspace,
-                               added in slice order by a second kernel */
+    RBQ_PATH_SPLIT = 7      /* fp16 MFMA for 2..16 tokens (per-row scales, K <= 2), What
+                               formed in registers from the sign words, the input columns
+                               split over workgroups; with several slices fp32 partial
+                               outputs in the workspace, added in slice order by a
+                               second kernel */
 } rbq_path;
 
 /* Forces rbq_gemm/rbq_gemv to one kernel family for the whole process (for

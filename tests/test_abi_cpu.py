@@ -48,7 +48,10 @@ def test_sizes_and_shape_checks():
         assert L.rbq_check_shape(b) == rbq.RBQ_ERR_INVALID_ARG, b
         assert rbq.planes_bytes(b) == 0 and rbq.scales_bytes(b) == 0
     assert rbq.planes_bytes(rbq.shape(0, 64, 2)) == 0
-    assert rbq.lib().rbq_gemm_workspace_bytes(s, 16) == 0
+    # the split family takes 2..16 tokens; its workspace holds whole
+    # slices of fp32 partial outputs
+    assert rbq.lib().rbq_gemm_workspace_bytes(s, 17) == 0
+    assert rbq.lib().rbq_gemm_workspace_bytes(s, 16) % (16 * 4096 * 4) == 0
 
 
 def test_status_strings_and_version():
@@ -115,7 +118,9 @@ def test_path_override_roundtrip():
     assert L.rbq_select_path(rbq.shape(22016, 4096, 2), 2) == rbq.PATH_FLAT
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 2) == rbq.PATH_STREAM
     assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 4) == rbq.PATH_DECODE
-    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 16) == rbq.PATH_DECODE
+    assert L.rbq_select_path(rbq.shape(4096, 4096, 2), 16) == rbq.PATH_SPLIT
+    assert L.rbq_select_path(rbq.shape(11008, 4096, 2), 8) == rbq.PATH_SPLIT
+    assert L.rbq_select_path(rbq.shape(4096, 11008, 2), 16) == rbq.PATH_SPLIT
     # the split family needs a workspace only where it can run
     assert L.rbq_gemm_workspace_bytes(rbq.shape(4096, 11008, 2), 1) == 0
     assert L.rbq_gemm_workspace_bytes(rbq.shape(5120, 5120, 4, 128), 16) == 0

@@ -456,9 +456,18 @@ def test_split_workspace_any_contents():
 
 
 def test_split_path_workspace_contract():
-    """Without workspace the automatic choice takes a family that needs none
-    (same result); the forced split family refuses a missing workspace."""
-    K, out, inf, M = 2, 256, 2048, 8
+    """A layer split into several column slices needs a workspace: without
+    one the automatic choice takes a family that needs none (same result)
+    and the forced split family refuses.  A layer of one slice (in <= 4096)
+    needs none, and the forced split family runs without it."""
+    K, out, inf, M = 2, 256, 4096, 8
+    L = rbq.lib()
+    assert L.rbq_gemm_workspace_bytes(rbq.shape(out, inf, K, 0), M) == 0
+    p = workloads.random_planes(K, out, inf, seed=34)
+    s = workloads.random_scales(K, out, 1, seed=35)
+    X = workloads.gaussian_activations(M, inf, seed=36)
+    assert_close(gpu_gemm(p, s, X, 0, rbq.PATH_SPLIT), oracle.gemm(p, s, X, 0), "one slice")
+    K, out, inf, M = 2, 256, 11008, 8
     p = workloads.random_planes(K, out, inf, seed=31)
     s = workloads.random_scales(K, out, 1, seed=32)
     X = workloads.gaussian_activations(M, inf, seed=33)
