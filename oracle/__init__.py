@@ -9,13 +9,15 @@ The arithmetic lives in ``rbq_oracle.c`` (plain C, fp64, serial per row);
 this file only builds it with gcc, loads it, and marshals numpy arrays.
 Every function here cites the same passages as the C file: the RaBiT
 summary (paperlayer.ai) sections 4.1, 4.2, A, B, G and D, and the QBB
-summary (atlas.scime.ai) "Approach".
+summary (atlas.scime.ai) "Approach" (also for ``refit``).
 
 Parity status: every function is pinned (see tests/test_oracle_pins.py):
 ``f64_to_f16`` against numpy's own float64->float16 conversion, ``encode``
 against brute force over all sign patterns, closed forms, planted planes and
 a hand-worked example, ``dequant``/``gemm`` against numpy unpacking and
-matmul and against closed forms for x = 1 and x = e_j.
+matmul and against closed forms for x = 1 and x = e_j, ``refit`` against
+numpy's least-squares solver, planted consistent systems, the cascade's own
+scale for one plane, and optimality against the cascade's scales.
 """
 from __future__ import annotations
 
@@ -67,6 +69,8 @@ def lib():
         L.oracle_dequant.restype = i32
         L.oracle_gemm.argtypes = [vp, vp, i64, i64, i32, i64, vp, i64, vp]
         L.oracle_gemm.restype = i32
+        L.oracle_refit.argtypes = [vp, i64, i64, i32, i64, vp, vp]
+        L.oracle_refit.restype = i32
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         L.oracle_set_num_threads.argtypes = [i32]
@@ -124,6 +128,23 @@ def encode(W: np.ndarray, num_planes: int, group_size: int = 0):
     if flags < 0:
         raise ValueError("oracle_encode: bad arguments")
     return planes, scales, flags
+
+
+def refit(W: np.ndarray, planes: np.ndarray, scales: np.ndarray, group_size: int = 0):
+    """Joint least-squares refit of the K scales of every (row, group) for
+    the fixed planes (QBB summary, "Approach").  ``scales`` are kept where
+    no refit is made.  Returns (scales uint16 [K][out][G], flags) with
+    flags bit 0 = non-finite W, bit 2 = some (row, group) kept its scales."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    out_scales = np.array(scales, dtype=np.uint16, copy=True, order="C")
+    K, out, words = planes.shape
+    inf = words * 32
+    assert W.shape == (out, inf)
+    flags = lib().oracle_refit(_ptr(W), out, inf, K, group_size, _ptr(planes), _ptr(out_scales))
+    if flags < 0:
+        raise ValueError("oracle_refit: bad arguments")
+    return out_scales, flags
 
 
 def dequant(planes: np.ndarray, scales: np.ndarray, group_size: int = 0) -> np.ndarray:

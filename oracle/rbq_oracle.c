@@ -23,6 +23,10 @@
  *   y = sum_k a_k (.) (B_k x): the layer output as a plain fp64
  *   dequantize-and-multiply (RaBiT 4.1 "additions and subtractions").
  *
+ *   Optional refinement of the scales for fixed planes: the joint
+ *   least-squares fit of the K scales of each (row, group) (QBB
+ *   "Approach", the data-free part of its refinement of the bases).
+ *
  * Readings where the pages are silent (each also listed in the design doc):
  *   - sign(0) = +1, decided by comparison (R >= 0), so -0.0 gives +1.
  *   - packed layout: plane k, row r, word w, bit b (LSB first) holds column
@@ -235,6 +239,119 @@ int oracle_gemm(const uint32_t *planes, const uint16_t *scales, int64_t out, int
     }
     free(xd);
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Joint least-squares refit of the K scales for fixed planes           */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The cascade picks each scale for its own step only; the refinement the
+ * QBB summary describes ("Approach": the binary bases are refined after
+ * the analytical initialisation) starts from there.  Its part that needs no
+ * data is the joint least-squares fit of the K scales of every (row, group)
+ * to W with the planes held fixed:
+ *     minimise sum_j (W_j - sum_k a_k B_kj)^2  over a = (a_1 .. a_K).
+ * Normal equations G a = b with
+ *     G_kl = sum_j B_kj B_lj = n - 2 * (columns where planes k, l differ),
+ *     b_k  = sum_j B_kj W_j   (one serial fp64 sum, ascending columns).
+ * G is factored as L D L^T (unit lower L, no square roots) in the fixed
+ * order below, and the solve runs forward, diagonal, backward.  A pivot
+ * D_i <= n * 2^-30 (dependent planes, e.g. all-zero rows where every plane
+ * is +1), a non-finite b, or a solution that is not finite in binary16
+ * keeps the given scales of that (row, group).  Each solved scale is rounded
+ * once to binary16.  For K = 1 this is b / n = mean |W|, the cascade's own
+ * first scale.
+ *
+ * scales: in = the scales kept where no refit is made (normally the
+ * encoder's), out = the refit.  Returns flags: bit 0 = a non-finite W,
+ * bit 2 = some (row, group) kept its scales; -1 on bad arguments.
+ */
+int oracle_refit(const float *W, int64_t out, int64_t in, int K, int64_t group_size,
+                 const uint32_t *planes, uint16_t *scales)
+{
+    if (out < 0 || in < 0 || in % 32 || K < 1 || K > 8 || group_size < 0)
+        return -1;
+    if (group_size && in % group_size)
+        return -1;
+    int64_t n = group_size ? group_size : in;
+    int64_t G = (in == 0) ? 0 : (group_size ? in / group_size : 1);
+    int64_t words = in / 32;
+    int flags = 0;
+
+    #pragma omp parallel for schedule(static) reduction(|:flags)
+    for (int64_t r = 0; r < out; ++r) {
+        const float *w = W + r * in;
+        for (int64_t j = 0; j < in; ++j)
+            if (!isfinite(w[j]))
+                flags |= 1;
+        for (int64_t t = 0; t < G; ++t) {
+            int64_t c0 = t * n;
+            double g[8][8], b[8], L[8][8], D[8], z[8], a[8];
+            /* normal equations */
+            for (int k = 0; k < K; ++k) {
+                const uint32_t *pk = planes + ((int64_t)k * out + r) * words;
+                b[k] = 0.0;
+                for (int64_t j = c0; j < c0 + n; ++j) {
+                    int plus = (pk[j / 32] >> (j % 32)) & 1u;
+                    b[k] += plus ? (double)w[j] : -(double)w[j];
+                }
+                for (int l = 0; l <= k; ++l) {
+                    const uint32_t *pl = planes + ((int64_t)l * out + r) * words;
+                    int64_t differ = 0;
+                    for (int64_t j = c0; j < c0 + n; ++j)
+                        differ += ((pk[j / 32] ^ pl[j / 32]) >> (j % 32)) & 1u;
+                    g[k][l] = g[l][k] = (double)(n - 2 * differ);
+                }
+            }
+            /* G = L D L^T */
+            int ok = 1;
+            for (int i = 0; i < K && ok; ++i) {
+                for (int j = 0; j < i; ++j) {
+                    double s = g[i][j];
+                    for (int p = 0; p < j; ++p)
+                        s = s - (L[i][p] * D[p]) * L[j][p];
+                    L[i][j] = s / D[j];
+                }
+                double s = g[i][i];
+                for (int p = 0; p < i; ++p)
+                    s = s - (L[i][p] * D[p]) * L[i][p];
+                D[i] = s;
+                if (!(s > (double)n * 0x1p-30))
+                    ok = 0;
+            }
+            for (int k = 0; k < K && ok; ++k)
+                if (!isfinite(b[k]))
+                    ok = 0;
+            uint16_t h[8];
+            if (ok) {
+                for (int i = 0; i < K; ++i) {      /* L z = b */
+                    double s = b[i];
+                    for (int p = 0; p < i; ++p)
+                        s = s - L[i][p] * z[p];
+                    z[i] = s;
+                }
+                for (int i = K - 1; i >= 0; --i) { /* D L^T a = z */
+                    double s = z[i] / D[i];
+                    for (int p = i + 1; p < K; ++p)
+                        s = s - L[p][i] * a[p];
+                    a[i] = s;
+                }
+                for (int k = 0; k < K; ++k) {
+                    h[k] = oracle_f64_to_f16(a[k]);
+                    if ((h[k] & 0x7c00) == 0x7c00)  /* inf or nan */
+                        ok = 0;
+                }
+            }
+            if (ok) {
+                for (int k = 0; k < K; ++k)
+                    scales[((int64_t)k * out + r) * G + t] = h[k];
+            } else {
+                flags |= 4;
+            }
+        }
+    }
+    return flags;
 }
 
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */

@@ -385,3 +385,148 @@ def test_row_stacking_commutes_with_encoding():
     p2, s2, _ = oracle.encode(W2, 2, 0)
     assert np.array_equal(p, np.concatenate([p1, p2], axis=1))
     assert np.array_equal(s, np.concatenate([s1, s2], axis=1))
+
+
+# ---------------------------------------------------------------------------
+# refit: joint least-squares scales for fixed planes (QBB "Approach")
+# ---------------------------------------------------------------------------
+
+def _exact_ls(B, w):
+    """Exact least-squares coefficients for the +-1 rows of B (K x n ints)
+    and fp32 values w (Fractions), by Gaussian elimination on rationals."""
+    K = B.shape[0]
+    G = [[Fraction(int(np.dot(B[k], B[l]))) for l in range(K)] for k in range(K)]
+    b = [sum((wj if s > 0 else -wj) for s, wj in zip(B[k], w)) for k in range(K)]
+    A = [G[i] + [b[i]] for i in range(K)]
+    for c in range(K):
+        piv = next(i for i in range(c, K) if A[i][c] != 0)
+        A[c], A[piv] = A[piv], A[c]
+        for i in range(K):
+            if i != c and A[i][c] != 0:
+                f = A[i][c] / A[c][c]
+                A[i] = [x - f * y for x, y in zip(A[i], A[c])]
+    return [A[i][K] / A[i][i] for i in range(K)]
+
+
+def _rne16_signed(q):
+    h = rne16_exact(abs(q))
+    return h | (0x8000 if q < 0 else 0)
+
+
+def _near_midpoint(q, rel=2.0 ** -40):
+    """True if the exact q lies within rel of a binary16 rounding midpoint."""
+    lo = np.uint16(rne16_exact(abs(q)))
+    v = Fraction(float(lo.view(np.float16)))
+    nb = [v]
+    for d in (-1, 1):
+        u = int(lo) + d
+        if 0 <= u < 0x7C00:
+            nb.append(Fraction(float(np.uint16(u).view(np.float16))))
+    mids = [(x + y) / 2 for x in nb for y in nb if x < y]
+    return any(abs(abs(q) - m) <= rel * abs(q) for m in mids)
+
+
+@pytest.mark.parametrize("K,group", [(1, 0), (2, 0), (3, 128), (4, 128), (8, 0)])
+def test_refit_is_exact_least_squares(K, group):
+    """Random planes, Gaussian W: each refit scale is the exact least-squares
+    coefficient (rational arithmetic on the fp32 values) rounded once to
+    binary16, except where that exact value lies within 2^-40 of a rounding
+    midpoint (the oracle's fp64 solve may then land on either side)."""
+    rng = np.random.default_rng(50 + K)
+    out, inf = 5, 256
+    signs = rng.choice(np.array([-1, 1], dtype=np.int8), size=(K, out, inf))
+    W = workloads.gaussian_weight(out, inf, seed=60 + K)
+    G = inf // group if group else 1
+    keep = np.zeros((K, out, G), dtype=np.uint16)
+    refit, flags = oracle.refit(W, pack_signs(signs), keep, group)
+    assert flags == 0
+    n = group or inf
+    checked = 0
+    for r in range(out):
+        for t in range(G):
+            cols = slice(t * n, (t + 1) * n)
+            a = _exact_ls(signs[:, r, cols].astype(np.int64), [Fraction(float(x)) for x in W[r, cols]])
+            for k in range(K):
+                want = _rne16_signed(a[k])
+                if refit[k, r, t] != want:
+                    assert _near_midpoint(a[k]), (k, r, t, float(a[k]))
+                else:
+                    checked += 1
+    assert checked >= K * out * G - 1
+
+
+@pytest.mark.parametrize("K,group", [(2, 0), (4, 128)])
+def test_refit_matches_numpy_lstsq(K, group):
+    """Against numpy's least-squares solver on the +-1 design matrix of each
+    (row, group): equal binary16, or one unit apart at most."""
+    W = workloads.gaussian_weight(12, 512, seed=70, outliers=True)
+    planes, scales, _ = oracle.encode(W, K, group)
+    refit, flags = oracle.refit(W, planes, scales, group)
+    assert flags == 0
+    signs = unpack_signs(planes).astype(np.float64)
+    n = group or 512
+    G = 512 // n
+    for r in range(12):
+        for t in range(G):
+            cols = slice(t * n, (t + 1) * n)
+            a = np.linalg.lstsq(signs[:, r, cols].T, W[r, cols].astype(np.float64), rcond=None)[0]
+            got = refit[:, r, t].astype(np.int64)
+            want = a.astype(np.float16).view(np.uint16).astype(np.int64)
+            assert np.all(np.abs(got - want) <= 1), (r, t, got, want)
+
+
+def test_refit_one_plane_is_cascade_scale():
+    """With one plane the least-squares scale is sum_j |W_j| / n: the
+    cascade's own scale, bit for bit (same serial sum, same rounding)."""
+    for group in (0, 128):
+        W = workloads.gaussian_weight(16, 1024, seed=80 + group, outliers=True)
+        planes, scales, _ = oracle.encode(W, 1, group)
+        refit, flags = oracle.refit(W, planes, np.zeros_like(scales), group)
+        assert flags == 0 and np.array_equal(refit, scales)
+
+
+def test_refit_recovers_planted_scales():
+    """W = sum_k a_k B_k exactly (fp16 scales, +-1 planes, exact in fp32):
+    the refit returns a_k exactly for every row, whichever planes."""
+    rng = np.random.default_rng(90)
+    K, out, inf = 3, 8, 256
+    signs = rng.choice(np.array([-1, 1], dtype=np.int8), size=(K, out, inf))
+    a = rng.choice(np.array([0.5, -0.25, 0.375, 0.0625, -1.5, 2.0, 0.75], dtype=np.float16),
+                   size=(K, out))
+    W64 = np.einsum("kr,krj->rj", a.astype(np.float64), signs.astype(np.float64))
+    W = W64.astype(np.float32)
+    assert np.array_equal(W.astype(np.float64), W64)
+    refit, flags = oracle.refit(W, pack_signs(signs), np.zeros((K, out, 1), np.uint16), 0)
+    assert flags == 0
+    assert np.array_equal(refit[:, :, 0], a.view(np.uint16))
+
+
+def test_refit_never_worse_than_cascade():
+    """For the cascade's planes, the refit scales reconstruct W at least as
+    well as the cascade's own scales, row by row (both rounded to binary16),
+    and clearly better in total."""
+    for K, group in ((2, 0), (4, 128)):
+        W = workloads.gaussian_weight(32, 1024, seed=100 + K, outliers=True)
+        planes, scales, _ = oracle.encode(W, K, group)
+        refit, flags = oracle.refit(W, planes, scales, group)
+        assert flags == 0
+        W64 = W.astype(np.float64)
+        e0 = ((W64 - oracle.dequant(planes, scales, group)) ** 2).sum(axis=1)
+        e1 = ((W64 - oracle.dequant(planes, refit, group)) ** 2).sum(axis=1)
+        assert np.all(e1 <= e0 * (1 + 1e-4))
+        assert e1.sum() < 0.99 * e0.sum()
+
+
+def test_refit_keeps_scales_of_singular_or_nonfinite_groups():
+    """All-zero rows give identical planes (all +1), so G is singular: the
+    given scales stay and flag bit 2 is set.  A non-finite W sets bit 0 and
+    keeps that row's scales; other rows are refit."""
+    W = workloads.gaussian_weight(4, 256, seed=5)
+    W[1] = 0.0
+    W[2, 7] = np.inf
+    planes, scales, _ = oracle.encode(W, 2, 0)
+    marker = np.full_like(scales, 0x1234)
+    refit, flags = oracle.refit(W, planes, marker, 0)
+    assert flags == 1 | 4
+    assert np.all(refit[:, 1] == 0x1234) and np.all(refit[:, 2] == 0x1234)
+    assert np.all(refit[:, 0] != 0x1234) and np.all(refit[:, 3] != 0x1234)
