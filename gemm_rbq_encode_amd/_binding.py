@@ -24,6 +24,7 @@ RBQ_ERR_HIP = 5
 
 RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
+RBQ_STATUS_REFIT_KEPT = 4
 RBQ_ENCODE_FORCE_SERIAL = 1
 
 PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP, PATH_SPLIT = (
@@ -61,6 +62,8 @@ _SIGNATURES = {
                                   ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_encode_ex": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "rbq_refit": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_size_t, ctypes.c_void_p]),
@@ -188,6 +191,28 @@ def encode(W: torch.Tensor, num_planes: int, group_size: int = 0, *,
     check(lib().rbq_encode_ex(W.data_ptr(), s, planes.data_ptr(), scales.data_ptr(), sp,
                               flags, _stream(W, stream)), "rbq_encode")
     return planes, scales
+
+
+def refit(W: torch.Tensor, planes: torch.Tensor, scales: torch.Tensor, group_size: int = 0, *,
+          status: torch.Tensor | None = None, stream=None):
+    """rbq_refit: joint least-squares refit of the K scales of every (row,
+    group) of W for the fixed planes, in place on `scales` (which also hold
+    the scales kept where no refit is made).  Returns `scales`."""
+    _dev(W, torch.float32, "W")
+    _dev(planes, torch.int32, "planes")
+    _dev(scales, torch.float16, "scales")
+    out_f, in_f = W.shape
+    K = planes.shape[0]
+    s = shape(out_f, in_f, K, group_size)
+    if planes.numel() * 4 < planes_bytes(s) or scales.numel() * 2 < scales_bytes(s):
+        raise ValueError("planes/scales buffers are too small for the shape")
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    check(lib().rbq_refit(W.data_ptr(), s, planes.data_ptr(), scales.data_ptr(), sp, _stream(W, stream)),
+          "rbq_refit")
+    return scales
 
 
 def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size: int = 0, *,

@@ -97,6 +97,27 @@ rbq_status rbq_encode(const float *W, rbq_shape s, uint32_t *planes, uint16_t *s
     return rbq_encode_ex(W, s, planes, scales, status_dev, 0u, stream);
 }
 
+rbq_status rbq_refit(const float *W, rbq_shape s, const uint32_t *planes, uint16_t *scales,
+                     int32_t *status_dev, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (s.out_features == 0 || s.in_features == 0)
+        return RBQ_OK;
+    if (W == nullptr || planes == nullptr || scales == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(W, 16) || !aligned(planes, 4) || !aligned(scales, 2) ||
+        (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if (s.in_features > RBQ_ENCODE_MAX_IN)
+        return RBQ_ERR_UNSUPPORTED;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_refit(W, s.out_features, s.in_features, s.num_planes, s.group_size, planes,
+                                     scales, status_dev, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M) {
     if (rbq_check_shape(s) != RBQ_OK || M < 2)
         return 0;

@@ -11,6 +11,10 @@ hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
                          uint32_t *planes, uint16_t *scales, int32_t *status,
                          int force_serial, hipStream_t st);
 
+// Joint least-squares refit of the K scales for fixed planes (in place).
+hipError_t launch_refit(const float *W, int out, int in, int K, int group_size, const uint32_t *planes,
+                        uint16_t *scales, int32_t *status, hipStream_t st);
+
 // fp32 VALU bit loop, any M (correctness baseline and fallback).
 hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int out, int in,
                             int K, int group_size, const uint16_t *X, int M, uint16_t *Y,

@@ -66,9 +66,13 @@ typedef struct rbq_shape {
     int32_t group_size;
 } rbq_shape;
 
-/* Bits of the device status word written by rbq_encode. */
+/* Bits of the device status word written by rbq_encode and rbq_refit. */
 #define RBQ_STATUS_NONFINITE_W     1u   /* some entry of W was NaN or +-Inf */
 #define RBQ_STATUS_SCALE_OVERFLOW  2u   /* some scale rounded to +-Inf in fp16 */
+#define RBQ_STATUS_REFIT_KEPT      4u   /* rbq_refit kept the given scales of some
+                                           (row, group): singular normal
+                                           equations, non-finite W, or a
+                                           solution outside binary16 */
 
 /* Flags for rbq_encode_ex. */
 #define RBQ_ENCODE_FORCE_SERIAL    1u   /* take the serial summation for every
@@ -121,6 +125,36 @@ rbq_status rbq_encode(const float *W, rbq_shape s, uint32_t *planes, uint16_t *s
 /* rbq_encode with flags (RBQ_ENCODE_*); flags = 0 is rbq_encode. */
 rbq_status rbq_encode_ex(const float *W, rbq_shape s, uint32_t *planes, uint16_t *scales,
                          int32_t *status_dev, uint32_t flags, void *stream);
+
+/*
+ * rbq_refit -- joint least-squares refit of the K scales of every (row,
+ * group) for fixed planes: the data-free part of the refinement of the
+ * binary bases in the QBB summary ("Approach"; the cascade of rbq_encode
+ * fits each scale for its own step only).  For each row r and group t of n
+ * columns, with the planes B_k held fixed:
+ *   minimise sum_j (W_j - sum_k a_k B_kj)^2,
+ *   normal equations G a = b, G_kl = sum_j B_kj B_lj (exact integers),
+ *   b_k = sum_j B_kj W_j in fp64; G = L D L^T in fp64 in a fixed order;
+ *   each a_k rounded once to binary16 (nearest, ties to even).
+ * A (row, group) whose pivot D_i <= n 2^-30 (dependent planes), whose W has a
+ * non-finite entry, or whose solution is not finite in binary16 keeps its
+ * given scales.  With K = 1 the result equals rbq_encode's scale.
+ *
+ *   W            device, fp32 [out][in] row-major, 16-byte aligned
+ *   planes       device, the planes of W (format above), 4-byte aligned
+ *   scales       device, fp16 bits [K][out][G], 2-byte aligned: read (the
+ *                scales kept where no refit is made, normally rbq_encode's)
+ *                and overwritten with the refit
+ *   status_dev   device int32 or NULL; RBQ_STATUS_NONFINITE_W and
+ *                RBQ_STATUS_REFIT_KEPT are OR-ed in (never cleared)
+ * The fp64 sums b_k are added in parallel, so a refit scale can differ by
+ * one binary16 unit from one computed with another summation order.
+ * Errors: RBQ_ERR_INVALID_ARG, RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED
+ * (in_features > RBQ_ENCODE_MAX_IN), RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.  An empty
+ * shape enqueues nothing.
+ */
+rbq_status rbq_refit(const float *W, rbq_shape s, const uint32_t *planes, uint16_t *scales,
+                     int32_t *status_dev, void *stream);
 
 /*
  * rbq_gemm -- Y[m] = sum_k a_k (.) (B_k X[m]) for M tokens (RaBiT section

@@ -85,6 +85,14 @@ def test_argument_errors_before_any_launch():
     # too long a row for the encoder
     big = rbq.shape(4, 32768 + 32, 2, 0)
     assert L.rbq_encode(ok, big, ok, ok, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    # refit: null pointers, shape, W alignment (16 bytes), row length
+    assert L.rbq_refit(None, s, ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_refit(ok, s, ok, None, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_refit(ok, rbq.shape(64, 100, 2), ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_refit(ok + 4, s, ok, ok, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_refit(ok, s, ok, ok + 1, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_refit(ok, big, ok, ok, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_refit(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
     # empty work is fine and enqueues nothing
     assert L.rbq_encode(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
     assert L.rbq_gemm(None, None, s, None, 0, None, None, 0, None) == rbq.RBQ_OK
@@ -97,6 +105,7 @@ def test_valid_call_without_device_reports_no_device():
     s = rbq.shape(64, 128, 2, 0)
     ok = 0x10000
     assert L.rbq_encode(ok, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
+    assert L.rbq_refit(ok, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_gemv(ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_gemm(ok, ok, s, ok, 2, ok, None, 0, None) == rbq.RBQ_ERR_NO_DEVICE
 

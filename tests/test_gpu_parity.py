@@ -490,3 +490,77 @@ def test_split_path_workspace_contract():
         assert rc == rbq.RBQ_ERR_INVALID_ARG
     finally:
         rbq.set_path(old)
+
+
+# ---------------------------------------------------------------------------
+# refit: joint least-squares scales for fixed planes
+# ---------------------------------------------------------------------------
+
+def gpu_refit(W, planes, scales, group):
+    Wt = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev())
+    p = torch.from_numpy(np.ascontiguousarray(planes).view(np.int32)).to(dev())
+    s = torch.from_numpy(np.ascontiguousarray(scales).view(np.float16)).to(dev())
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    rbq.refit(Wt, p, s, group, status=status)
+    torch.cuda.synchronize()
+    return s.cpu().numpy().view(np.uint16), int(status.item())
+
+
+def assert_refit_close(got, want, what):
+    """Equal binary16, or one unit apart (the fp64 sums of b are added in
+    another order, which can move a value across a rounding midpoint); such
+    differences stay rare."""
+    g = got.view(np.float16).astype(np.float64)
+    w = want.view(np.float16).astype(np.float64)
+    unit = np.spacing(np.maximum(np.abs(g), np.abs(w)).astype(np.float16)).astype(np.float64)
+    bad = np.abs(g - w) > unit
+    assert not bad.any(), (what, np.argwhere(bad)[:5], g[bad][:5], w[bad][:5])
+    assert (got != want).mean() <= 1e-3, (what, (got != want).mean())
+
+
+@pytest.mark.parametrize("name,i", [("small", 0), ("llama2_7b", 0), ("llama2_7b", 4), ("llama2_7b", 6),
+                                    ("llama2_13b_g128", 0), ("llama2_13b_g128", 4)])
+def test_refit_matches_oracle_on_workloads(name, i):
+    wl = workloads.WORKLOADS[name]
+    W = workloads.workload_weight(wl, i)
+    planes, scales, _ = oracle.encode(W, wl.num_planes, wl.group_size)
+    want, wflags = oracle.refit(W, planes, scales, wl.group_size)
+    got, gflags = gpu_refit(W, planes, scales, wl.group_size)
+    assert gflags == wflags
+    assert_refit_close(got, want, f"{name} {i}")
+
+
+@pytest.mark.parametrize("out,inf,K,group", [(3, 96, 2, 0), (17, 640, 3, 128), (33, 4128, 8, 0),
+                                             (9, 1024, 1, 128), (70, 2048, 4, 0), (5, 32768, 2, 0)])
+def test_refit_ragged_shapes(out, inf, K, group):
+    W = workloads.gaussian_weight(out, inf, seed=out * 7 + inf, outliers=True)
+    planes, scales, _ = oracle.encode(W, K, group)
+    want, wflags = oracle.refit(W, planes, scales, group)
+    got, gflags = gpu_refit(W, planes, scales, group)
+    assert gflags == wflags
+    assert_refit_close(got, want, f"{out}x{inf} K={K} g={group}")
+
+
+def test_refit_keeps_singular_and_nonfinite_groups():
+    W = workloads.gaussian_weight(6, 512, seed=11)
+    W[1] = 0.0
+    W[4, 100] = np.nan
+    for group in (0, 128):
+        planes, scales, _ = oracle.encode(W, 2, group)
+        marker = np.full_like(scales, 0x1234)
+        want, wflags = oracle.refit(W, planes, marker, group)
+        got, gflags = gpu_refit(W, planes, marker, group)
+        assert gflags == wflags == rbq.RBQ_STATUS_NONFINITE_W | rbq.RBQ_STATUS_REFIT_KEPT
+        assert np.array_equal(got == 0x1234, want == 0x1234)
+        assert_refit_close(got, want, f"kept g={group}")
+
+
+def test_refit_one_plane_is_the_encoder_scale_and_deterministic():
+    """K = 1: the least-squares scale is the encoder's mean |W| (within one
+    binary16 unit: the refit's sum is parallel).  Two runs agree bit for bit."""
+    W = workloads.gaussian_weight(300, 4096, seed=12, outliers=True)
+    gp, gs, _ = gpu_encode(W, 1, 0)
+    got1, f1 = gpu_refit(W, gp, np.zeros_like(gs), 0)
+    got2, f2 = gpu_refit(W, gp, np.zeros_like(gs), 0)
+    assert f1 == f2 == 0 and np.array_equal(got1, got2)
+    assert_refit_close(got1, gs, "K=1")
