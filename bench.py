@@ -21,6 +21,9 @@ Reported (one JSON line):
   cpu_baseline  the CPU oracle on the host cores on a bounded sample
   encode     rbq_encode of the seven linears (GB/s over W read + planes and
              scales written)
+  refit      rbq_refit of the seven linears (GB/s over W and planes read,
+             scales read and written); on the 13B g128 set both are timed
+             per distinct shape
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -181,6 +184,29 @@ def graph_launch_us(torch, dev, fns, reps):
     return a.elapsed_time(b) * 1e3 / (reps * len(fns))
 
 
+def graph_ms(torch, dev, fns, reps):
+    """Milliseconds per replay of one HIP graph holding the calls `fns`
+    (captured on a side stream, replayed back to back `reps` times)."""
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
 def bench_layer_set(args):
     """Skinny, grouped-scale and prefill workloads: each linear of the set is
     run back to back (one launch each) over a rotation of encoded copies;
@@ -205,10 +231,22 @@ def bench_layer_set(args):
     prefill = args.workload == "llama3_8b_prefill"
     rot = 2 if prefill else max(2, int(2.0e9 // sum(
         K * l.out_features * l.in_features // 8 for _, l in uniq)))
-    sets = []
+    sets, prep = [], {}
     for i, lin in uniq:
         W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
         p, sc = rbq.encode(W, K, group)
+        if group:
+            # encoder and refit time of this shape (outputs rewritten in place)
+            key = f"{lin.out_features}x{lin.in_features}"
+            pe, se, sr = torch.empty_like(p), torch.empty_like(sc), sc.clone()
+            enc_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)], 3)
+            ref_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)], 3)
+            wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * sc.numel()
+            prep[key] = {"encode_us": round(enc_ms * 1e3, 1),
+                         "encode_GBps": round((wb + pb + sb) / (enc_ms * 1e-3) / 1e9, 1),
+                         "refit_us": round(ref_ms * 1e3, 1),
+                         "refit_GBps": round((wb + pb + 2 * sb) / (ref_ms * 1e-3) / 1e9, 1)}
+            del pe, se, sr
         del W
         X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
         Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
@@ -286,7 +324,7 @@ def bench_layer_set(args):
     line = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f16" if names[path] == "prefill" else ("i8" if names[path] != "valu" else "f32"),
+            "dtype": "f16" if names[path] in ("prefill", "split") else ("i8" if names[path] != "valu" else "f32"),
             "data": "synthetic",
             "config": {"workload": wl.name, "linears": [f"{l.out_features}x{l.in_features}" for _, l in uniq],
                        "num_planes": K, "group_size": group, "tokens": M, "rotation": rot,
@@ -296,6 +334,8 @@ def bench_layer_set(args):
                            rbq.select_path(rbq.shape(l.out_features, l.in_features, K, group), M)]
                            for _, l in uniq}},
             "roofline": roof, "cpu_baseline": None}
+    if prep:
+        line["encode_refit_per_shape"] = prep
     print(json.dumps(line), flush=True)
 
 
@@ -346,7 +386,14 @@ def bench_decode(args):
     e1.record(stream)
     torch.cuda.synchronize()
     enc_ms = e0.elapsed_time(e1) / enc_reps
-    del enc_graph, Ws
+    del enc_graph
+    # refit time: the seven refits (into copies of the scales) in one graph
+    ref_scales = [s.clone() for s in enc_scales]
+    ref_bytes = sum(4 * W.numel() + p.numel() * 4 + 4 * s.numel()
+                    for W, p, s in zip(Ws, enc_planes, ref_scales))
+    ref_ms = graph_ms(torch, dev, [(lambda W=W, p=p, s=s: rbq.refit(W, p, s, group))
+                                   for W, p, s in zip(Ws, enc_planes, ref_scales)], 5)
+    del Ws, ref_scales
 
     # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
     # into one matrix: rows are encoded independently, so the stacked planes
@@ -507,6 +554,8 @@ def bench_decode(args):
         "cpu_baseline": cpu,
         "encode": {"linears": len(wl.linears), "ms": round(enc_ms, 4),
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
+        "refit": {"linears": len(wl.linears), "ms": round(ref_ms, 4),
+                  "GBps": round(ref_bytes / (ref_ms * 1e-3) / 1e9, 1)},
     }
     print(json.dumps(line), flush=True)
 

@@ -18,13 +18,17 @@
 // in binary16 keeps the given scales of that (row, group) and sets a status
 // bit.  With one plane the refit is sum_j |W_j| / n, the encoder's scale.
 //
-// Work: a segment (row, group of n columns) is handled by LPS lanes (16 for
-// 128-column groups, so four segments per wave; 64 for whole rows).  Each
-// lane reads 8 consecutive columns at a time (two 16-byte loads of W and one
-// byte of every plane's word), adds +-W_j into K fp64 sums and counts plane
+// Work: a segment (row, group of n columns) is handled by LPS lanes (4 for
+// 128-column groups, so 16 segments per wave; 64 for whole rows).  Each lane
+// reads 8 consecutive columns at a time (two 16-byte loads of W and one byte
+// of every plane's word), adds +-W_j into K fp64 sums and counts plane
 // differences with popcounts; the lanes of a segment then combine with
-// shuffles, and the segment's first lane solves and writes.  The kernel
-// reads W once (HBM-bound, like the encoder).
+// shuffles, and the segment's first lane solves and writes.  The serial
+// solve runs once per wave for all its segments, so fewer lanes per group
+// means fewer solves: 13824 x 5120, K = 4, took 169 us with 16 lanes per
+// group, 85 us with 4, 88 us with 2 and 162 us with 1 (whose loads no longer
+// fill whole cache lines).  The kernel reads W once (HBM-bound, like the
+// encoder).
 #include "rbq.h"
 #include "rbq_device.h"
 #include "rbq_kernels.h"
@@ -36,6 +40,7 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int RF_THREADS = 256;
+constexpr int RF_GROUP_LPS = 4;                 // lanes per 128-column group
 
 template <int LPS>
 __device__ __forceinline__ double seg_sum_f64(double v) {
@@ -210,9 +215,9 @@ hipError_t launch_kl(const float *W, int out, int in, int n, const uint32_t *pla
 template <int K>
 hipError_t launch_k(const float *W, int out, int in, int n, const uint32_t *planes, uint16_t *scales,
                     int32_t *status, hipStream_t st) {
-    // 16 lanes for 128-column groups (8 columns each), 64 for longer segments
+    // 4 lanes for 128-column groups (8 columns at a time), 64 for longer segments
     if (n <= 128)
-        return launch_kl<K, 16>(W, out, in, n, planes, scales, status, st);
+        return launch_kl<K, RF_GROUP_LPS>(W, out, in, n, planes, scales, status, st);
     return launch_kl<K, 64>(W, out, in, n, planes, scales, status, st);
 }
 
