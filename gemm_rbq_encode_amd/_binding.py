@@ -25,6 +25,8 @@ RBQ_ERR_HIP = 5
 RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_STATUS_REFIT_KEPT = 4
+RBQ_EPILOGUE_NONE = 0
+RBQ_EPILOGUE_SILU_MUL = 1
 RBQ_ENCODE_FORCE_SERIAL = 1
 
 PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP, PATH_SPLIT = (
@@ -67,6 +69,9 @@ _SIGNATURES = {
     "rbq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_size_t, ctypes.c_void_p]),
+    "rbq_gemm_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "rbq_gemm_workspace_bytes": (ctypes.c_size_t, [Shape, ctypes.c_int32]),
     "rbq_gemv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p]),
@@ -216,8 +221,11 @@ def refit(W: torch.Tensor, planes: torch.Tensor, scales: torch.Tensor, group_siz
 
 
 def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size: int = 0, *,
-         Y: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
-    """rbq_gemm: Y[M][out] = sum_k a_k (.) (B_k X[m]), fp16 in and out."""
+         Y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         epilogue: int = 0, stream=None):
+    """rbq_gemm_ex: Y[M][out] = sum_k a_k (.) (B_k X[m]), fp16 in and out;
+    with epilogue=RBQ_EPILOGUE_SILU_MUL the rows are (gate, up) pairs and
+    Y[M][out/2] holds silu(gate) * up."""
     _dev(planes, torch.int32, "planes")
     _dev(scales, torch.float16, "scales")
     _dev(X, torch.float16, "X")
@@ -229,10 +237,11 @@ def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size
     s = shape(out_f, in_f, K, group_size)
     if scales.numel() * 2 < scales_bytes(s):
         raise ValueError("scales buffer too small for the shape")
+    ycols = out_f // 2 if epilogue == RBQ_EPILOGUE_SILU_MUL else out_f
     if Y is None:
-        Y = torch.empty((M, out_f), dtype=torch.float16, device=X.device)
+        Y = torch.empty((M, ycols), dtype=torch.float16, device=X.device)
     _dev(Y, torch.float16, "Y")
-    if Y.numel() < M * out_f:
+    if Y.numel() < M * ycols:
         raise ValueError("Y too small")
     ws_need = int(lib().rbq_gemm_workspace_bytes(s, M))
     ws_ptr, ws_bytes = None, 0
@@ -240,8 +249,8 @@ def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size
         if workspace is None:
             workspace = torch.empty(ws_need, dtype=torch.uint8, device=X.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    check(lib().rbq_gemm(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), M,
-                         Y.data_ptr(), ws_ptr, ws_bytes, _stream(X, stream)), "rbq_gemm")
+    check(lib().rbq_gemm_ex(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), M,
+                            Y.data_ptr(), ws_ptr, ws_bytes, int(epilogue), _stream(X, stream)), "rbq_gemm")
     return Y
 
 

@@ -155,14 +155,20 @@ rbq_path rbq_select_path(rbq_shape s, int32_t M) {
     return select_path_no_workspace(s, M);
 }
 
-rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
-                    const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
-                    size_t ws_bytes, void *stream) {
+rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                       const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
+                       size_t ws_bytes, uint32_t epilogue, void *stream) {
     rbq_status st = rbq_check_shape(s);
     if (st != RBQ_OK)
         return st;
     if (M < 0)
         return RBQ_ERR_INVALID_ARG;
+    if (epilogue != RBQ_EPILOGUE_NONE && epilogue != RBQ_EPILOGUE_SILU_MUL)
+        return RBQ_ERR_INVALID_ARG;
+    const int silu = epilogue == RBQ_EPILOGUE_SILU_MUL;
+    if (silu && s.out_features % 2 != 0)
+        return RBQ_ERR_INVALID_ARG;
+    const int64_t ycols = silu ? s.out_features / 2 : s.out_features;
     if (ws_bytes > 0 && workspace == nullptr)
         return RBQ_ERR_INVALID_ARG;
     if (M == 0 || s.out_features == 0)
@@ -175,7 +181,7 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
     if (s.in_features == 0) {  // empty sums: Y = 0
         if ((st = device_present()) != RBQ_OK)
             return st;
-        hipError_t e = rbq::launch_fill_zero_u16(Y, (int64_t)M * s.out_features, hs);
+        hipError_t e = rbq::launch_fill_zero_u16(Y, (int64_t)M * ycols, hs);   // silu(0) * 0 = 0
         return e == hipSuccess ? RBQ_OK : hip_fail(e);
     }
     if (planes == nullptr || scales == nullptr || X == nullptr)
@@ -190,14 +196,19 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
             path = select_path_no_workspace(s, M);
         if (path == RBQ_PATH_GROUP && !aligned(scales, 8))   // the group kernel reads 4 scales at once
             path = RBQ_PATH_VALU;
+        if (silu)   // the epilogue is built into the flat and VALU kernels
+            path = rbq::flat_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M)
+                       ? RBQ_PATH_FLAT : RBQ_PATH_VALU;
     }
+    if (silu && path != RBQ_PATH_FLAT && path != RBQ_PATH_VALU)
+        return RBQ_ERR_UNSUPPORTED;
     if ((st = device_present()) != RBQ_OK)
         return st;
     hipError_t e;
     switch (path) {
     case RBQ_PATH_VALU:
         e = rbq::launch_gemm_valu(planes, scales, s.out_features, s.in_features, s.num_planes,
-                                  s.group_size, X, M, Y, hs);
+                                  s.group_size, X, M, Y, silu, hs);
         break;
     case RBQ_PATH_DECODE:
         if (!rbq::decode_supports(s.in_features, s.num_planes, s.group_size, M))
@@ -221,7 +232,7 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
         if (!rbq::flat_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
             return RBQ_ERR_UNSUPPORTED;
         e = rbq::launch_gemm_flat(planes, scales, s.out_features, s.in_features, s.num_planes,
-                                  s.group_size, X, M, Y, hs);
+                                  s.group_size, X, M, Y, silu, hs);
         break;
     case RBQ_PATH_SPLIT:
         if (!rbq::split_supports(s.out_features, s.in_features, s.num_planes, s.group_size, M))
@@ -245,6 +256,12 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
         return RBQ_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                    const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
+                    size_t ws_bytes, void *stream) {
+    return rbq_gemm_ex(planes, scales, s, X, M, Y, workspace, ws_bytes, RBQ_EPILOGUE_NONE, stream);
 }
 
 rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,

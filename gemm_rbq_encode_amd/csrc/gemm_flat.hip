@@ -91,7 +91,7 @@ __device__ __forceinline__ void lds_wait_count(int *counter, int target) {
     asm volatile("" ::: "memory");
 }
 
-template <int K, int MT, int XU, int RING>
+template <int K, int MT, int XU, int RING, bool SILU>
 __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
     const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
@@ -398,25 +398,42 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
 
     // ---- one thread per output row.  Column 3m + l holds 2^7 sum(bit l_j);
     // 2^7 sum(bit q) = T_0 + 2^8 T_1 + 2^16 T_2 (exact in fp64), and
-    // y = sum_k a_k (2 sum(bit q) - sum q) 2^-sh.
-    if (tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out) {
+    // y = sum_k a_k (2 sum(bit q) - sum q) 2^-sh.  With the SiLU-mul epilogue
+    // the rows come in (gate, up) pairs 2i, 2i + 1 -- neighbouring threads of
+    // one wave, as tiles start at even rows -- and the even thread writes
+    // silu(y_2i) * y_2i+1 to column i of a Y of out / 2 columns.
+    auto row_sum = [&](int m) {
         const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+        float sx = 0.0f;
+#pragma unroll
+        for (int v = 0; v < FL_PREP; ++v)
+            sx += wsum[m][v];
+        float y = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
+            const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
+                             65536.0 * (double)rp[2 * TILE_ROWS];
+            y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx);
+        }
+        return __builtin_ldexpf(y, -shs[m]);
+    };
+    const bool rowok = tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out;
+    if constexpr (!SILU) {
+        if (rowok) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < mt)
+                    Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = f2h(row_sum(m));
+        }
+    } else {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < mt) {
-                float sx = 0.0f;
-#pragma unroll
-                for (int v = 0; v < FL_PREP; ++v)
-                    sx += wsum[m][v];
-                float y = 0.0f;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
-                    const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
-                                     65536.0 * (double)rp[2 * TILE_ROWS];
-                    y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx);
-                }
-                Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = f2h(__builtin_ldexpf(y, -shs[m]));
+                const float y = rowok ? row_sum(m) : 0.0f;
+                const float up = __shfl_down(y, 1, RBQ_WAVE);
+                if (rowok && (tid & 1) == 0)
+                    Y[(size_t)(m0 + m) * (out / 2) + (t0 * TILE_ROWS + tid) / 2] = f2h(silu_f32(y) * up);
             }
         }
     }
@@ -455,14 +472,18 @@ int flat_grid(int out) {
 
 template <int K, int MT, int XU, int RING>
 hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                       const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+                       const uint16_t *X, int M, uint16_t *Y, int silu, hipStream_t st) {
     const int G = flat_grid(out);
     const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
     const int tpw = (T + G - 1) / G;
     const int mt = M < MT ? M : MT;
     const size_t lds = flat_lds_bytes(in, K, mt, tpw);
-    hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XU, RING>), dim3(G, (M + MT - 1) / MT),
-                       dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
+    if (silu)
+        hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XU, RING, true>), dim3(G, (M + MT - 1) / MT),
+                           dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
+    else
+        hipLaunchKernelGGL((gemm_flat_kernel<K, MT, XU, RING, false>), dim3(G, (M + MT - 1) / MT),
+                           dim3(FL_THREADS), lds, st, planes, scales, out, in, X, M, Y);
     return hipGetLastError();
 }
 
@@ -474,22 +495,22 @@ hipError_t launch_kmxr(const uint32_t *planes, const uint16_t *scales, int out, 
 
 template <int K, int MT, int XU>
 hipError_t launch_kmx(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
-    return launch_kmxr<K, MT, XU, RBQ_FLAT_RING>(planes, scales, out, in, X, M, Y, st);
+                      const uint16_t *X, int M, uint16_t *Y, int silu, hipStream_t st) {
+    return launch_kmxr<K, MT, XU, RBQ_FLAT_RING>(planes, scales, out, in, X, M, Y, silu, st);
 }
 
 template <int K, int MT>
 hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                     const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+                     const uint16_t *X, int M, uint16_t *Y, int silu, hipStream_t st) {
     const int xu = flat_units_per_thread(in);
     if (xu <= 1)
-        return launch_kmx<K, MT, 1>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmx<K, MT, 1>(planes, scales, out, in, X, M, Y, silu, st);
     if (xu <= 2)
-        return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmx<K, MT, 2>(planes, scales, out, in, X, M, Y, silu, st);
     if (xu <= 3)
-        return launch_kmx<K, MT, 3>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmx<K, MT, 3>(planes, scales, out, in, X, M, Y, silu, st);
     if constexpr (MT <= 2)   // four tokens hold at most 3 half-words each in registers
-        return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, st);
+        return launch_kmx<K, MT, 4>(planes, scales, out, in, X, M, Y, silu, st);
     return hipErrorInvalidValue;
 }
 
@@ -519,18 +540,18 @@ bool flat_preferred(int out, int in, int K, int group_size, int M) {
 }
 
 hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y, int silu,
                             hipStream_t st) {
-    if (!flat_supports(out, in, K, group_size, M))
+    if (!flat_supports(out, in, K, group_size, M) || (silu && out % 2 != 0))
         return hipErrorInvalidValue;
     const int mt = flat_tokens_per_pass(M);
     if (K == 1)
-        return mt == 1 ? launch_km<1, 1>(planes, scales, out, in, X, M, Y, st)
-             : mt == 2 ? launch_km<1, 2>(planes, scales, out, in, X, M, Y, st)
-                       : launch_km<1, 4>(planes, scales, out, in, X, M, Y, st);
-    return mt == 1 ? launch_km<2, 1>(planes, scales, out, in, X, M, Y, st)
-         : mt == 2 ? launch_km<2, 2>(planes, scales, out, in, X, M, Y, st)
-                   : launch_km<2, 4>(planes, scales, out, in, X, M, Y, st);
+        return mt == 1 ? launch_km<1, 1>(planes, scales, out, in, X, M, Y, silu, st)
+             : mt == 2 ? launch_km<1, 2>(planes, scales, out, in, X, M, Y, silu, st)
+                       : launch_km<1, 4>(planes, scales, out, in, X, M, Y, silu, st);
+    return mt == 1 ? launch_km<2, 1>(planes, scales, out, in, X, M, Y, silu, st)
+         : mt == 2 ? launch_km<2, 2>(planes, scales, out, in, X, M, Y, silu, st)
+                   : launch_km<2, 4>(planes, scales, out, in, X, M, Y, silu, st);
 }
 
 }  // namespace rbq

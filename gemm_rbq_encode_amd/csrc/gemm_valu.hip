@@ -18,17 +18,21 @@ namespace {
 
 __global__ __launch_bounds__(256) void gemm_valu_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
-    int K, int group_size, const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
+    int K, int group_size, const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y, int silu) {
     const int wave = threadIdx.x / RBQ_WAVE;
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
+    // one output per wave: row r, or with the SiLU-mul epilogue the (gate,
+    // up) rows 2r, 2r + 1 giving column r of a Y of out / 2 columns
     const int r = blockIdx.x * 4 + wave;
-    if (r >= out)
+    const int nout = silu ? out / 2 : out;
+    if (r >= nout)
         return;
+    const int nr = silu ? 2 : 1;
     const int words = in >> 5;
     const int G = group_size ? in / group_size : 1;
     for (int m = blockIdx.y; m < M; m += gridDim.y) {
         const uint16_t *x = X + (size_t)m * in;
-        float acc = 0.0f;
+        float acc[2] = {0.0f, 0.0f};
         for (int w = lane; w < words; w += RBQ_WAVE) {
             float xv[32];
             const uint4 *xp = reinterpret_cast<const uint4 *>(x + 32 * w);
@@ -47,19 +51,24 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(
             for (int b = 0; b < 32; ++b)
                 sx += xv[b];
             const int t = group_size ? (32 * w) / group_size : 0;
-            for (int k = 0; k < K; ++k) {
-                const uint32_t bits = planes[((size_t)k * out + r) * words + w];
-                float s = 0.0f;
+            for (int q = 0; q < nr; ++q) {
+                const int row = nr * r + q;
+                for (int k = 0; k < K; ++k) {
+                    const uint32_t bits = planes[((size_t)k * out + row) * words + w];
+                    float s = 0.0f;
 #pragma unroll
-                for (int b = 0; b < 32; ++b)
-                    s += ((bits >> b) & 1u) ? xv[b] : 0.0f;
-                const float a = h2f(scales[((size_t)k * out + r) * G + t]);
-                acc += a * (2.0f * s - sx);
+                    for (int b = 0; b < 32; ++b)
+                        s += ((bits >> b) & 1u) ? xv[b] : 0.0f;
+                    const float a = h2f(scales[((size_t)k * out + row) * G + t]);
+                    acc[q] += a * (2.0f * s - sx);
+                }
             }
         }
-        acc = wave_sum_f32(acc);
+        acc[0] = wave_sum_f32(acc[0]);
+        if (silu)
+            acc[1] = wave_sum_f32(acc[1]);
         if (lane == 0)
-            Y[(size_t)m * out + r] = f2h(acc);
+            Y[(size_t)m * nout + r] = f2h(silu ? silu_f32(acc[0]) * acc[1] : acc[0]);
     }
 }
 
@@ -72,11 +81,14 @@ __global__ void fill_zero_u16_kernel(uint16_t *Y, int64_t n) {
 }  // namespace
 
 hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y, int silu,
                             hipStream_t st) {
+    if (silu && out % 2 != 0)
+        return hipErrorInvalidValue;
     const int gy = M < 65535 ? M : 65535;
-    hipLaunchKernelGGL(gemm_valu_kernel, dim3((out + 3) / 4, gy), dim3(256), 0, st, planes,
-                       scales, out, in, K, group_size, X, M, Y);
+    const int nout = silu ? out / 2 : out;
+    hipLaunchKernelGGL(gemm_valu_kernel, dim3((nout + 3) / 4, gy), dim3(256), 0, st, planes,
+                       scales, out, in, K, group_size, X, M, Y, silu);
     return hipGetLastError();
 }
 

@@ -13,6 +13,12 @@ __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// SiLU (sigmoid-weighted linear unit) v / (1 + e^-v) in fp32, for the
+// gate of a gated MLP: the gate/up epilogue writes silu(gate) * up.
+__device__ __forceinline__ float silu_f32(float v) {
+    return v / (1.0f + expf(-v));
+}
+
 // float -> binary16 bits, rounded to nearest even (v_cvt_f16_f32).
 __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);

@@ -16,8 +16,10 @@ hipError_t launch_refit(const float *W, int out, int in, int K, int group_size, 
                         uint16_t *scales, int32_t *status, hipStream_t st);
 
 // fp32 VALU bit loop, any M (correctness baseline and fallback).
+// silu != 0: rows come in (gate, up) pairs 2i, 2i+1 and Y[m][i] =
+// silu(y_2i) * y_2i+1 (Y has out / 2 columns; out even).
 hipError_t launch_gemm_valu(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y, int silu,
                             hipStream_t st);
 
 // int8-MFMA decode kernel (per-row scales, K <= 4, in % 128 == 0); M is
@@ -42,7 +44,7 @@ bool flat_supports(int out, int in, int K, int group_size, int M);
 // Whether the flat kernel is the faster choice (many 16-row tiles per CU).
 bool flat_preferred(int out, int in, int K, int group_size, int M);
 hipError_t launch_gemm_flat(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
+                            int K, int group_size, const uint16_t *X, int M, uint16_t *Y, int silu,
                             hipStream_t st);
 
 // One-workgroup-per-compute-unit int8-MFMA GEMV for one token with a scale

@@ -179,6 +179,30 @@ rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     const uint16_t *X, int32_t M, uint16_t *Y,
                     void *workspace, size_t ws_bytes, void *stream);
 
+/* Epilogues of rbq_gemm_ex. */
+#define RBQ_EPILOGUE_NONE          0u
+#define RBQ_EPILOGUE_SILU_MUL      1u   /* gated-MLP gate/up: see rbq_gemm_ex */
+
+/*
+ * rbq_gemm_ex -- rbq_gemm with an epilogue on the outputs (RaBiT section 5
+ * and QBB "Key results" measure whole decoder layers, whose MLP multiplies
+ * SiLU of the gate projection into the up projection).
+ *   RBQ_EPILOGUE_NONE      rbq_gemm.
+ *   RBQ_EPILOGUE_SILU_MUL  the layer's rows come in (gate, up) pairs: row 2i
+ *                          is gate row i, row 2i+1 up row i (out even).  Y is
+ *                          fp16 [M][out/2] with
+ *                          Y[m][i] = silu(y[m][2i]) * y[m][2i+1],
+ *                          silu(v) = v / (1 + e^-v), from the fp32 sums,
+ *                          rounded once to binary16.  Served by the
+ *                          RBQ_PATH_FLAT and RBQ_PATH_VALU families (another
+ *                          forced family returns RBQ_ERR_UNSUPPORTED).
+ * Other arguments and errors as rbq_gemm; an unknown epilogue or an odd out
+ * with RBQ_EPILOGUE_SILU_MUL is RBQ_ERR_INVALID_ARG.
+ */
+rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                       const uint16_t *X, int32_t M, uint16_t *Y,
+                       void *workspace, size_t ws_bytes, uint32_t epilogue, void *stream);
+
 /* Workspace bytes the split-column kernel family (RBQ_PATH_SPLIT) needs for
  * this shape and M: S * M * out fp32 partial outputs when the input columns
  * are split into S > 1 slices (in > 4096); 0 when one slice takes the whole

@@ -147,6 +147,16 @@ def refit(W: np.ndarray, planes: np.ndarray, scales: np.ndarray, group_size: int
     return out_scales, flags
 
 
+def silu_mul(Y: np.ndarray) -> np.ndarray:
+    """Gated-MLP epilogue on layer outputs whose columns come in (gate, up)
+    pairs 2i, 2i+1: H[m][i] = silu(Y[m][2i]) * Y[m][2i+1] with
+    silu(v) = v / (1 + e^-v), in fp64 (the pages measure whole decoder
+    layers: RaBiT section 5, QBB "Key results")."""
+    Y = np.asarray(Y, dtype=np.float64)
+    g, u = Y[:, 0::2], Y[:, 1::2]
+    return g / (1.0 + np.exp(-g)) * u
+
+
 def dequant(planes: np.ndarray, scales: np.ndarray, group_size: int = 0) -> np.ndarray:
     """Materialise What = sum_k a_k (.) B_k in fp64, [out][in]."""
     planes = np.ascontiguousarray(planes, dtype=np.uint32)

@@ -564,3 +564,77 @@ def test_refit_one_plane_is_the_encoder_scale_and_deterministic():
     got2, f2 = gpu_refit(W, gp, np.zeros_like(gs), 0)
     assert f1 == f2 == 0 and np.array_equal(got1, got2)
     assert_refit_close(got1, gs, "K=1")
+
+
+# ---------------------------------------------------------------------------
+# gated-MLP epilogue: silu(gate) * up from interleaved (gate, up) rows
+# ---------------------------------------------------------------------------
+
+def _interleaved_gate_up():
+    wl = workloads.WORKLOADS["llama2_7b"]
+    gate, up = workloads.workload_weight(wl, 4), workloads.workload_weight(wl, 5)
+    W = np.empty((2 * gate.shape[0], gate.shape[1]), dtype=np.float32)
+    W[0::2], W[1::2] = gate, up
+    p, s, _ = oracle.encode(W, 2, 0)
+    return p, s
+
+
+_GU = {}
+
+
+def gpu_gemm_epi(planes, scales, X, path):
+    p = torch.from_numpy(np.ascontiguousarray(planes).view(np.int32)).to(dev())
+    s = torch.from_numpy(np.ascontiguousarray(scales).view(np.float16)).to(dev())
+    x = torch.from_numpy(np.ascontiguousarray(X).view(np.float16)).to(dev())
+    old = rbq.set_path(path)
+    try:
+        Y = rbq.gemm(p, s, x, 0, epilogue=rbq.RBQ_EPILOGUE_SILU_MUL)
+        torch.cuda.synchronize()
+    finally:
+        rbq.set_path(old)
+    return Y.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("path", ["auto", "flat", "valu"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemm_silu_mul_llama2_7b_gate_up(path, M):
+    if "p" not in _GU:
+        _GU["p"], _GU["s"] = _interleaved_gate_up()
+    p, s = _GU["p"], _GU["s"]
+    X = workloads.gaussian_activations(M, 4096, seed=40 + M)
+    pid = {"auto": rbq.PATH_AUTO, "flat": rbq.PATH_FLAT, "valu": rbq.PATH_VALU}[path]
+    H = gpu_gemm_epi(p, s, X, pid)
+    assert H.shape == (M, 11008)
+    assert_close(H, oracle.silu_mul(oracle.gemm(p, s, X, 0)), f"silu-mul {path} M={M}")
+
+
+@pytest.mark.parametrize("path", ["flat", "valu"])
+@pytest.mark.parametrize("out,inf,K,M", [(34, 512, 1, 3), (2, 128, 2, 1), (66, 11008, 2, 16), (4098, 2048, 2, 2)])
+def test_gemm_silu_mul_ragged(path, out, inf, K, M):
+    p = workloads.random_planes(K, out, inf, seed=out + inf)
+    s = workloads.random_scales(K, out, 1, seed=M + K, signed=True)
+    X = workloads.gaussian_activations(M, inf, seed=inf + M)
+    pid = {"flat": rbq.PATH_FLAT, "valu": rbq.PATH_VALU}[path]
+    H = gpu_gemm_epi(p, s, X, pid)
+    assert_close(H, oracle.silu_mul(oracle.gemm(p, s, X, 0)), f"silu-mul {out}x{inf} K={K} M={M}")
+
+
+def test_gemm_epilogue_errors():
+    L = rbq.lib()
+    p = torch.zeros((2, 6, 4), dtype=torch.int32, device=dev())
+    s = torch.zeros((2, 6, 1), dtype=torch.float16, device=dev())
+    x = torch.zeros((1, 128), dtype=torch.float16, device=dev())
+    y = torch.zeros((1, 6), dtype=torch.float16, device=dev())
+    st = torch.cuda.current_stream().cuda_stream
+    args = (p.data_ptr(), s.data_ptr(), rbq.shape(6, 128, 2, 0), x.data_ptr(), 1, y.data_ptr(), None, 0)
+    assert L.rbq_gemm_ex(*args, 7, st) == rbq.RBQ_ERR_INVALID_ARG
+    odd = (p.data_ptr(), s.data_ptr(), rbq.shape(5, 128, 2, 0), x.data_ptr(), 1, y.data_ptr(), None, 0)
+    assert L.rbq_gemm_ex(*odd, rbq.RBQ_EPILOGUE_SILU_MUL, st) == rbq.RBQ_ERR_INVALID_ARG
+    old = rbq.set_path(rbq.PATH_DECODE)
+    try:
+        assert L.rbq_gemm_ex(*args, rbq.RBQ_EPILOGUE_SILU_MUL, st) == rbq.RBQ_ERR_UNSUPPORTED
+    finally:
+        rbq.set_path(old)
+    assert L.rbq_gemm_ex(*args, rbq.RBQ_EPILOGUE_SILU_MUL, st) == rbq.RBQ_OK
+    torch.cuda.synchronize()
+    assert (y[0, 3:] == 0).all()   # only out/2 = 3 columns written

@@ -530,3 +530,17 @@ def test_refit_keeps_scales_of_singular_or_nonfinite_groups():
     assert flags == 1 | 4
     assert np.all(refit[:, 1] == 0x1234) and np.all(refit[:, 2] == 0x1234)
     assert np.all(refit[:, 0] != 0x1234) and np.all(refit[:, 3] != 0x1234)
+
+
+def test_silu_mul_against_scipy_expit():
+    """silu(v) * u = v * sigmoid(v) * u, with scipy's logistic function, and
+    the closed values silu(0) = 0, silu(v) -> v for large v, -> 0 for very
+    negative v; columns pair as (2i, 2i+1)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(7)
+    Y = rng.standard_normal((3, 10)) * 4
+    H = oracle.silu_mul(Y)
+    assert H.shape == (3, 5)
+    np.testing.assert_allclose(H, Y[:, 0::2] * expit(Y[:, 0::2]) * Y[:, 1::2], rtol=1e-14)
+    Z = np.array([[0.0, 5.0, 40.0, 2.0, -40.0, 3.0]])
+    np.testing.assert_allclose(oracle.silu_mul(Z), [[0.0, 80.0, -40.0 * np.exp(-40.0) * 3.0]], rtol=1e-12)
