@@ -207,6 +207,61 @@ def graph_ms(torch, dev, fns, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, xs, K, group):
+    """The same 32 layers as a chained decoder step: q/k/v on x, o on q
+    (the attention between them is outside this library), gate/up with the
+    silu(gate) * up epilogue on rows interleaved as (gate, up) pairs, down on
+    its output h.  Each launch reads what the one before it wrote, as in
+    decoding.  One HIP graph per step; reports ms and GB/s over the same
+    algorithmic bytes (h is written once at half the gate/up rows)."""
+    n_ff = shapes[2].out_features // 2
+    perm = torch.stack([torch.arange(n_ff), torch.arange(n_ff) + n_ff], dim=1).reshape(-1).to(dev)
+    gu = [(p.index_select(1, perm).contiguous(), s.index_select(1, perm).contiguous())
+          for p, s in (layer[2] for layer in layers)]
+    x = xs[shapes[0].in_features]
+    qkv = torch.empty(shapes[0].out_features, dtype=torch.float16, device=dev)
+    o = torch.empty(shapes[1].out_features, dtype=torch.float16, device=dev)
+    h = torch.empty(n_ff, dtype=torch.float16, device=dev)
+    y = torch.empty(shapes[3].out_features, dtype=torch.float16, device=dev)
+
+    def step(st):
+        for layer, (gp, gs) in zip(layers, gu):
+            rcs = (L.rbq_gemv(layer[0][0].data_ptr(), layer[0][1].data_ptr(), shapes[0], x.data_ptr(),
+                              qkv.data_ptr(), st),
+                   L.rbq_gemv(layer[1][0].data_ptr(), layer[1][1].data_ptr(), shapes[1], qkv.data_ptr(),
+                              o.data_ptr(), st),
+                   L.rbq_gemm_ex(gp.data_ptr(), gs.data_ptr(), shapes[2], x.data_ptr(), 1, h.data_ptr(),
+                                 None, 0, rbq.RBQ_EPILOGUE_SILU_MUL, st),
+                   L.rbq_gemv(layer[3][0].data_ptr(), layer[3][1].data_ptr(), shapes[3], h.data_ptr(),
+                              y.data_ptr(), st))
+            if any(rcs):
+                raise rbq.RbqError(max(rcs), "decode layer chain")
+
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(side.cuda_stream)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    per_layer = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) - 2 * n_ff
+    del graph, gu
+    return {"layers": len(layers), "ms_per_step": round(ms, 4),
+            "GBps": round(per_layer * len(layers) / (ms * 1e-3) / 1e9, 1),
+            "launches_per_layer": 4, "epilogue": "silu(gate)*up in the gate/up launch"}
+
+
 def bench_layer_set(args):
     """Skinny, grouped-scale and prefill workloads: each linear of the set is
     run back to back (one launch each) over a rotation of encoded copies;
@@ -475,6 +530,8 @@ def bench_decode(args):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    layer_chain = decode_layer_chain(args, torch, rbq, L, dev, layers, g_shapes, xs, K, group) \
+        if args.layout == "fused" and graph is not None else None
 
     # ---- per-launch device time of each launch group: its launches over all
     # layers in one graph, replayed between two HIP events on the launch stream
@@ -556,6 +613,7 @@ def bench_decode(args):
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
         "refit": {"linears": len(wl.linears), "ms": round(ref_ms, 4),
                   "GBps": round(ref_bytes / (ref_ms * 1e-3) / 1e9, 1)},
+        "decode_layer_chain": layer_chain,
     }
     print(json.dumps(line), flush=True)
 
