@@ -30,15 +30,27 @@
 // [m - d, m + d] exactly when that interval lies strictly between the
 // midpoints of h and its two fp16 neighbours (which fp64 holds exactly).
 //
-// Layout.  One workgroup (4 or 16 waves) per row; the row is cut into 64-column
-// chunks and wave w keeps chunks [w*CPW, (w+1)*CPW) in registers, lane l
-// holding column 64c + l of chunk c.  Loads are therefore coalesced 256-byte
-// wave reads, a wave ballot of (R >= 0) is exactly the two packed words of a
-// chunk, and a 128-column group is a chunk pair inside one wave.  W is read
-// from HBM once; the K steps run on registers.  Sums are reduced with DPP;
-// a row's waves meet at barriers that wait for LDS only, so the plane
-// stores of earlier steps stay in flight.  A wave decides the scales of its
-// 128-column groups together, lane g taking group g.
+// Layout, whole rows.  One workgroup (4 or 16 waves) per row; the row is
+// cut into 64-column chunks and wave w keeps chunks [w*CPW, (w+1)*CPW) in
+// registers, lane l holding column 64c + l of chunk c.  Loads are therefore
+// coalesced 256-byte wave reads and a wave ballot of (R >= 0) is exactly the
+// two packed words of a chunk.  W is read from HBM once; the K steps run on
+// registers.  Sums are reduced with DPP; a row's waves meet at barriers that
+// wait for LDS only, so the plane stores of earlier steps stay in flight.
+//
+// Layout, 128-column groups.  Groups are independent and never cross a row,
+// so the matrix is a flat sequence of groups (group q = elements [128q,
+// 128q + 128) of W) and each wave encodes GPW consecutive groups, a group
+// being a chunk pair.  The group sums are taken in fp32 first: all GPW sums
+// come out of one transposed reduction (each exchange level halves the
+// number of values a lane carries until one is left), a tree of depth 7
+// (the pair |R| + |R'| and six lane levels), so the fp32 sum is within a
+// relative 7u/(1 - 7u) (u = 2^-24) of the exact sum and the serial fp64
+// mean within a relative 8u of the fp32 mean m.  If [m - 10u m, m + 10u m]
+// (the wider margin absorbs the rounding of the test itself) lies strictly
+// between the fp16 midpoints around the fp16 rounding of m, that rounding is
+// the serial result; otherwise (a small fraction of groups, and every exact tie) the
+// group takes the serial fp64 sum of its residuals.
 #include "rbq_device.h"
 #include "rbq_kernels.h"
 
@@ -134,18 +146,16 @@ __device__ __forceinline__ void load_row(float (&R)[CPW], const float *__restric
 
 // All K steps of row r, whose columns this wave holds in R.  `phase` counts
 // the workgroup's row-sum exchanges and picks the LDS buffer.
-template <int WAVES, int CPW, bool GROUPED>
+template <int WAVES, int CPW>
 __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *__restrict__ W,
                                            int out, int in_row, int K,
                                            uint32_t *__restrict__ planes,
                                            uint16_t *__restrict__ scales,
                                            int32_t *__restrict__ status, int force_serial,
                                            EncodeLds<WAVES, CPW> &sh, int &phase) {
-    constexpr int GPW = CPW / 2;  // 128-column groups per wave
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE);
     const int words = in_row >> 5;
-    const int G = GROUPED ? in_row / 128 : 1;
     const float *Wr = W + (size_t)r * in_row;
     const int chunk0_row = wave * CPW;
 
@@ -167,74 +177,34 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
         // not kept in scalar registers across the whole loop
         int in = in_row, chunk0 = chunk0_row;
         asm volatile("" : "+s"(in), "+s"(chunk0));
-        float a_row = 0.0f;
-        float a_grp[GPW];
-        if (!GROUPED) {
-            double s = 0.0;
+        // the row sum: each wave's share, then the waves' shares in wave order
+        double s = 0.0;
 #pragma unroll
-            for (int i = 0; i < CPW; ++i)   // columns past the row end hold 0
-                s += (double)__builtin_fabsf(R[i]);
-            s = wave_sum_f64_dpp(s);
-            const int b = phase & 1;
-            ++phase;
-            if (lane == 0)
-                sh.part[b][wave] = s;
+        for (int i = 0; i < CPW; ++i)   // columns past the row end hold 0
+            s += (double)__builtin_fabsf(R[i]);
+        s = wave_sum_f64_dpp(s);
+        const int b = phase & 1;
+        ++phase;
+        if (lane == 0)
+            sh.part[b][wave] = s;
+        lds_barrier();
+        double S = sh.part[b][0];
+#pragma unroll
+        for (int v = 1; v < WAVES; ++v)
+            S += sh.part[b][v];
+        uint32_t h = force_serial ? UNDECIDED : decide_scale(S, in);
+        if (h == UNDECIDED) {  // same decision in every thread of the block
+            if (threadIdx.x == 0)
+                sh.decided_row = serial_scale(Wr, 0, in, sh.hist_row, 1, k);
             lds_barrier();
-            double S = sh.part[b][0];
-#pragma unroll
-            for (int v = 1; v < WAVES; ++v)
-                S += sh.part[b][v];
-            uint32_t h = force_serial ? UNDECIDED : decide_scale(S, in);
-            if (h == UNDECIDED) {  // same decision in every thread of the block
-                if (threadIdx.x == 0)
-                    sh.decided_row = serial_scale(Wr, 0, in, sh.hist_row, 1, k);
-                lds_barrier();
-                h = sh.decided_row;
-            }
-            a_row = h2f((uint16_t)h);
-            if (threadIdx.x == 0) {
-                sh.hist_row[k] = a_row;
-                scales[(size_t)k * out + r] = (uint16_t)h;
-                if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
-                    atomicOr(status, (int32_t)2);
-            }
-        } else {
-            // the wave's group sums, then lane g decides group g
-            double mine = 0.0;
-#pragma unroll
-            for (int g = 0; g < GPW; ++g) {
-                const bool gvalid = (chunk0 + 2 * g) * RBQ_WAVE < in;
-                double s = gvalid ? (double)__builtin_fabsf(R[2 * g]) +
-                                        (double)__builtin_fabsf(R[2 * g + 1])
-                                  : 0.0;
-                s = wave_sum_f64_dpp(s);
-                mine = (lane == g) ? s : mine;
-            }
-            const uint32_t hl = force_serial ? UNDECIDED : decide_scale(mine, 128);
-#pragma unroll
-            for (int g = 0; g < GPW; ++g) {
-                const int col0 = (chunk0 + 2 * g) * RBQ_WAVE;  // group start (in % 128 == 0)
-                const bool gvalid = col0 < in;
-                uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hl, g);
-                if (h == UNDECIDED && gvalid) {  // uniform in the wave
-                    // the defining serial sum, in column order, over the
-                    // group's residuals: columns 128g' + l and 128g' + 64 + l
-                    // sit in lane l of R[2g] and R[2g + 1]
-                    double S = 0.0;
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        for (int l = 0; l < RBQ_WAVE; ++l)
-                            S += (double)__builtin_fabsf(__builtin_bit_cast(
-                                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R[2 * g + c]), l)));
-                    h = f64_to_f16_rne(div_rn(S, 128.0));
-                }
-                a_grp[g] = gvalid ? h2f((uint16_t)h) : 0.0f;
-                if (lane == 0 && gvalid) {
-                    scales[((size_t)k * out + r) * G + (col0 >> 7)] = (uint16_t)h;
-                    if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
-                        atomicOr(status, (int32_t)2);
-                }
-            }
+            h = sh.decided_row;
+        }
+        const float a_row = h2f((uint16_t)h);
+        if (threadIdx.x == 0) {
+            sh.hist_row[k] = a_row;
+            scales[(size_t)k * out + r] = (uint16_t)h;
+            if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
+                atomicOr(status, (int32_t)2);
         }
 
         // signs, packed words and the residual update.  Chunk i's ballot is
@@ -249,7 +219,7 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
             const bool valid = c < (in >> 6) || (c == (in >> 6) && lane < (in & 63));
             const bool plus = R[i] >= 0.0f;
             const uint64_t m = __ballot(plus);
-            const float a = GROUPED ? a_grp[i / 2] : a_row;
+            const float a = a_row;
             if (valid)
                 R[i] = R[i] - (plus ? a : -a);
             if (lane == 0)
@@ -266,11 +236,10 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
 
 // A workgroup encodes rows blockIdx.x, blockIdx.x + gridDim.x, ...; the
 // loads of its next row are in flight while it encodes the current one.
-template <int WAVES, int CPW, bool GROUPED>
+template <int WAVES, int CPW>
 __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     const float *__restrict__ W, int out, int in, int K, uint32_t *__restrict__ planes,
     uint16_t *__restrict__ scales, int32_t *__restrict__ status, int force_serial) {
-    static_assert(CPW % 2 == 0, "a 128-column group must be a chunk pair of one wave");
     __shared__ EncodeLds<WAVES, CPW> sh;
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
@@ -283,7 +252,7 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
         const bool more = r + G < out;
         if (more)
             load_row<WAVES, CPW>(Rn, W + (size_t)(r + G) * in, in, chunk0, lane);
-        encode_row<WAVES, CPW, GROUPED>(R, r, W, out, in, K, planes, scales, status,
+        encode_row<WAVES, CPW>(R, r, W, out, in, K, planes, scales, status,
                                         force_serial, sh, phase);
         if (more) {
 #pragma unroll
@@ -291,6 +260,188 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
                 R[i] = Rn[i];
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// 128-column groups
+// ---------------------------------------------------------------------------
+
+constexpr int GR_WAVES = 4;                     // waves per workgroup
+
+// v_writelane_b32 (write one lane of a VGPR from a uniform value): this
+// compiler has no builtin for it, so its LLVM intrinsic is named directly.
+extern "C" __device__ int rbq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// DPP lane permutations inside a row of 16 lanes: level L pairs each lane
+// with the lane whose bit (3 - L) differs (row rotate by 8, half-row mirror,
+// quad swaps by 2 and by 1).
+template <int L>
+__device__ __forceinline__ float row_partner(float x) {
+    constexpr int ctrl = L == 0 ? 0x128 : L == 1 ? 0x141 : L == 2 ? 0x4E : 0xB1;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
+                                                                 0xF, 0xF, false));
+}
+
+// One exchange level over N live values: with N > 1 value i (i < N/2) pairs
+// with value i + N/2, the lane whose level bit is clear keeping i and its
+// partner keeping i + N/2, each adding what the other sent; with N = 1 the
+// two lanes simply add.  Every level is one rounded addition per lane.
+template <int L, int N, int GPW>
+__device__ __forceinline__ void fold_level(float (&v)[GPW], int lane) {
+    if constexpr (N > 1) {
+        const bool upper = (lane >> (3 - L)) & 1;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float send = upper ? v[i] : v[i + N / 2];
+            const float keep = upper ? v[i + N / 2] : v[i];
+            v[i] = keep + row_partner<L>(send);
+        }
+    } else {
+        v[0] = v[0] + row_partner<L>(v[0]);
+    }
+    if constexpr (L < 3)
+        fold_level<L + 1, (N > 1 ? N / 2 : 1), GPW>(v, lane);
+}
+
+// fp16 bits of the mean s / 128 when the fp32 group sum s decides it (the
+// bound of the layout notes above), else UNDECIDED.
+__device__ __forceinline__ uint32_t decide_scale_f32(float s) {
+    const float m = s * 0x1p-7f;                 // exact unless m < 2^-126 (then h = 0)
+    const uint32_t h = f2h(m);                   // one rounding, ties to even
+    if (!(h < 0x7BFFu))                          // the largest finite value, infinity, NaN
+        return UNDECIDED;
+    const float v = h2f((uint16_t)h);
+    const float below = (h == 0u) ? -0x1p-24f : h2f((uint16_t)(h - 1u));
+    const float above = h2f((uint16_t)(h + 1u));
+    const float d = m * 0x1.4p-21f;              // 10 u m
+    const bool inside = (m - d > 0.5f * (below + v)) && (m + d < 0.5f * (v + above));
+    return inside ? h : UNDECIDED;
+}
+
+// Step k of groups [q0, q0 + live) held by one wave: lane l holds element
+// 128 q0 + 64 c + l in R[c].  After the reduction every lane of block g
+// (lanes (16/GPW) g .. (16/GPW)(g + 1) - 1 of each 16-lane row) holds the
+// sum of group g.  UPDATE: compute the next residual (not after the last
+// step).
+template <int GPW, bool UPDATE>
+__device__ __forceinline__ void group_step(float (&R)[2 * GPW], int k, long ngroups, long q0, int live,
+                                           int lane, uint32_t *__restrict__ planes,
+                                           uint16_t *__restrict__ scales, int32_t *__restrict__ status,
+                                           int force_serial) {
+    constexpr int SPAN = 16 / GPW;               // lanes per group inside a row
+    const int gl = (lane & 15) / SPAN;           // the group this lane's sum belongs to
+
+    float v[GPW];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g)
+        v[g] = __builtin_fabsf(R[2 * g]) + __builtin_fabsf(R[2 * g + 1]);
+    fold_level<0, GPW, GPW>(v, lane);
+    float s = v[0];
+    s = s + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __builtin_bit_cast(int, s)));
+    s = s + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, s)));
+
+    if (k == 0 && status != nullptr && __ballot(!__builtin_isfinite(s)) != 0) {
+        // a non-finite sum: look for a non-finite element (a finite W whose
+        // sum overflows is not flagged)
+        bool bad = false;
+#pragma unroll
+        for (int c = 0; c < 2 * GPW; ++c)
+            bad |= !__builtin_isfinite(R[c]);
+        if (__ballot(bad) != 0 && lane == 0)
+            atomicOr(status, (int32_t)1);
+    }
+
+    uint32_t h = force_serial ? UNDECIDED : decide_scale_f32(s);
+    const uint64_t undecided = __ballot(h == UNDECIDED);
+    if (undecided != 0) {
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            if (((undecided >> (g * SPAN)) & 1u) && g < live) {   // uniform in the wave
+                // the defining serial sum over the group's residuals in
+                // column order: columns 64c + l sit in lane l of R[c]
+                double S = 0.0;
+#pragma unroll
+                for (int c = 2 * g; c < 2 * g + 2; ++c)
+#pragma nounroll
+                    for (int l = 0; l < RBQ_WAVE; ++l)
+                        S += (double)__builtin_fabsf(__builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R[c]), l)));
+                const uint32_t hs = f64_to_f16_rne(S * 0x1p-7);   // S / 128, exact
+                h = (gl == g) ? hs : h;
+                if (status != nullptr && (hs & 0x7FFFu) == 0x7C00u && lane == 0)
+                    atomicOr(status, (int32_t)2);
+            }
+        }
+    }
+
+    // scales: the first lane of each group's block in row 0
+    if (lane < 16 && lane % SPAN == 0 && gl < live)
+        scales[(size_t)k * ngroups + q0 + gl] = (uint16_t)h;
+
+    // signs, packed words (chunk c's ballot is words 2c and 2c + 1, put in
+    // lanes 2c and 2c + 1) and the residual update R - (bit ? a : -a),
+    // written as fma(sign, -a, R): the product is exact, so it rounds once
+    // like the subtraction
+    const float af = h2f((uint16_t)h);
+    uint32_t wv = 0;
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, af), g * SPAN));
+#pragma unroll
+        for (int c = 2 * g; c < 2 * g + 2; ++c) {
+            const bool plus = R[c] >= 0.0f;
+            const uint64_t m = __ballot(plus);
+            if constexpr (UPDATE)
+                R[c] = __builtin_fmaf(plus ? 1.0f : -1.0f, -a, R[c]);
+            wv = (uint32_t)rbq_writelane_i32((int)(uint32_t)m, 2 * c, (int)wv);
+            wv = (uint32_t)rbq_writelane_i32((int)(uint32_t)(m >> 32), 2 * c + 1, (int)wv);
+        }
+    }
+    if (lane < 4 * live)
+        planes[(size_t)k * 4 * ngroups + (size_t)q0 * 4 + lane] = wv;
+}
+
+// Each wave encodes GPW consecutive groups, all K steps on registers.
+template <int GPW>
+__global__ __launch_bounds__(GR_WAVES * RBQ_WAVE) void encode_group_kernel(
+    const float *__restrict__ W, long ngroups, int K, uint32_t *__restrict__ planes,
+    uint16_t *__restrict__ scales, int32_t *__restrict__ status, int force_serial) {
+    static_assert(GPW >= 1 && GPW <= 16 && (GPW & (GPW - 1)) == 0, "GPW: a power of two up to 16");
+    const int lane = threadIdx.x & (RBQ_WAVE - 1);
+    const long q0 = ((long)blockIdx.x * GR_WAVES + threadIdx.x / RBQ_WAVE) * GPW;
+    if (q0 >= ngroups)
+        return;
+    const int live = (int)(ngroups - q0 < GPW ? ngroups - q0 : GPW);   // groups to write
+
+    float R[2 * GPW];
+    const float *Wq = W + (size_t)q0 * 128 + lane;
+#pragma unroll
+    for (int c = 0; c < 2 * GPW; ++c)
+        R[c] = (c / 2 < live) ? Wq[c * RBQ_WAVE] : 0.0f;
+
+    for (int k = 0; k + 1 < K; ++k)
+        group_step<GPW, true>(R, k, ngroups, q0, live, lane, planes, scales, status, force_serial);
+    group_step<GPW, false>(R, K - 1, ngroups, q0, live, lane, planes, scales, status, force_serial);
+}
+
+template <int GPW>
+hipError_t launch_gpw(const float *W, long ngroups, int K, uint32_t *planes, uint16_t *scales,
+                      int32_t *status, int force_serial, hipStream_t st) {
+    const long per_block = (long)GR_WAVES * GPW;
+    const long blocks = (ngroups + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFL)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((encode_group_kernel<GPW>), dim3((unsigned)blocks), dim3(GR_WAVES * RBQ_WAVE), 0, st, W,
+                       ngroups, K, planes, scales, status, force_serial);
+    return hipGetLastError();
+}
+
+hipError_t launch_groups(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *scales,
+                         int32_t *status, int force_serial, hipStream_t st) {
+    if (in % 128 != 0)
+        return hipErrorInvalidValue;
+    const long ngroups = (long)out * (in / 128);
+    return launch_gpw<8>(W, ngroups, K, planes, scales, status, force_serial, st);
 }
 
 int encode_num_cus() {
@@ -305,14 +456,14 @@ int encode_num_cus() {
     return cus;
 }
 
-template <int WAVES, int CPW, bool GROUPED>
-hipError_t launch_cpwg(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *scales,
-                       int32_t *status, int force_serial, hipStream_t st) {
+template <int WAVES, int CPW>
+hipError_t launch_cpw(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *scales,
+                      int32_t *status, int force_serial, hipStream_t st) {
     // as many resident workgroups as the compute units hold
     static int per_cu = 0;
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, encode_kernel<WAVES, CPW, GROUPED>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, encode_kernel<WAVES, CPW>,
                                                          WAVES * RBQ_WAVE, 0) != hipSuccess ||
             n <= 0)
             n = 1;
@@ -320,18 +471,9 @@ hipError_t launch_cpwg(const float *W, int out, int in, int K, uint32_t *planes,
     }
     const long want = (long)encode_num_cus() * per_cu;
     const int grid = (int)(want < out ? want : out);
-    hipLaunchKernelGGL((encode_kernel<WAVES, CPW, GROUPED>), dim3(grid), dim3(WAVES * RBQ_WAVE), 0,
+    hipLaunchKernelGGL((encode_kernel<WAVES, CPW>), dim3(grid), dim3(WAVES * RBQ_WAVE), 0,
                        st, W, out, in, K, planes, scales, status, force_serial);
     return hipGetLastError();
-}
-
-template <int WAVES, int CPW>
-hipError_t launch_cpw(const float *W, int out, int in, int K, int group_size, uint32_t *planes,
-                      uint16_t *scales, int32_t *status, int force_serial, hipStream_t st) {
-    return group_size ? launch_cpwg<WAVES, CPW, true>(W, out, in, K, planes, scales, status,
-                                                      force_serial, st)
-                      : launch_cpwg<WAVES, CPW, false>(W, out, in, K, planes, scales, status,
-                                                       force_serial, st);
 }
 
 }  // namespace
@@ -339,6 +481,8 @@ hipError_t launch_cpw(const float *W, int out, int in, int K, int group_size, ui
 hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
                          uint32_t *planes, uint16_t *scales, int32_t *status, int force_serial,
                          hipStream_t st) {
+    if (group_size)
+        return launch_groups(W, out, in, K, planes, scales, status, force_serial, st);
     // Rows of up to 4096 columns: 4 waves; longer rows: 16 waves, so that each
     // lane keeps at most 2 x 32 values of two rows in registers.
     const int chunks = (in + RBQ_WAVE - 1) / RBQ_WAVE;
@@ -346,8 +490,7 @@ hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
     const int need = (chunks + waves - 1) / waves;
 #define RBQ_ENC_CASE(WV, C)                                                              \
     if (waves == WV && need <= C)                                                        \
-        return launch_cpw<WV, C>(W, out, in, K, group_size, planes, scales, status,       \
-                                 force_serial, st);
+        return launch_cpw<WV, C>(W, out, in, K, planes, scales, status, force_serial, st);
     RBQ_ENC_CASE(4, 2)
     RBQ_ENC_CASE(4, 4)
     RBQ_ENC_CASE(4, 8)

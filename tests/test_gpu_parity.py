@@ -156,6 +156,41 @@ def test_encode_ties_take_the_serial_path():
         assert_encode_matches(W, 3, group, what=f"ties g={group}")
 
 
+def _near_midpoint_rows():
+    """Rows of 512 columns (four 128-column groups) whose group means sit 0,
+    1, 2, 4, 16 and 64 fp32 ulps from an fp16 rounding boundary, at several
+    magnitudes (normal and subnormal fp16 scales), with mixed signs."""
+    rows = []
+    signs = np.where(np.arange(128) % 5 < 2, -1.0, 1.0).astype(np.float32)
+    for base in (1.0, 0.375, 2.0 ** -14, 3.0 * 2.0 ** -22, 700.0):
+        h = np.float16(base)
+        mid = (float(h) + float(np.nextafter(h, np.float16(np.inf)))) / 2     # exact in fp32
+        groups = []
+        for ulps in (0, 1, -1, 2, -2, 4, -4, 16, -16, 64):
+            v = np.float32(mid)
+            step = np.float32(np.inf if ulps > 0 else -np.inf)
+            for _ in range(abs(ulps)):
+                v = np.nextafter(v, step)
+            groups.append(np.full(128, v, np.float32) * signs)
+        # an exact midpoint mean from unequal values, and one a hair above it
+        lo = np.float32(mid * (1 - 2.0 ** -12))
+        hi = np.float32(2 * mid - float(lo))
+        g = np.where(np.arange(128) % 2 == 0, lo, hi).astype(np.float32)
+        groups.append(g * signs)
+        g2 = g.copy()
+        g2[7] = np.nextafter(g2[7], np.float32(np.inf))
+        groups.append(g2 * signs)
+        rows.extend(np.concatenate(groups[i:i + 4]) for i in range(0, len(groups), 4))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_encode_means_near_fp16_midpoints(group):
+    """Means within a few fp32 ulps of an fp16 midpoint cannot be decided by
+    an fp32 sum; the encoder must still return the serial fp64 result."""
+    assert_encode_matches(_near_midpoint_rows(), 3, group, what=f"near midpoints g={group}")
+
+
 @pytest.mark.parametrize("out,inf,K,group", [(64, 512, 3, 0), (32, 4096, 2, 0), (16, 1024, 4, 128),
                                              (8, 11008, 2, 0)])
 def test_encode_forced_serial_path(out, inf, K, group):
