@@ -9,48 +9,26 @@
 // Exactness.  The scale is defined as the serial fp64 sum of |R_j| in
 // ascending column order, divided by n, rounded once to fp16.  A serial
 // chain per row would leave most of the GPU idle, so each (row, group) is
-// summed in parallel in fp64 instead.  Any summation order of n
-// non-negative terms is within a relative (n-1)u/(1-(n-1)u) of the exact
-// sum (u = 2^-53), so the serial mean and the parallel mean differ by less
-// than a relative (2n + 64)u (the 64u also covers both divisions).  If
-// every value in that interval rounds to the same fp16 number, that number
-// is the serial result (rounding is monotonic).  Otherwise -- an exact tie
-// or a mean within ~1e-11 of an fp16 rounding boundary -- the serial sum is
-// redone and divided with a correctly rounded division: for a 128-column
-// group from the residuals the wave holds (read lane by lane in column
-// order), for a whole row by one lane that rebuilds each R_j from W and the
-// scales already chosen.  Exact ties do occur at the later steps of 4-plane
-// group encodings (a few groups per 13824 x 5120 matrix).  Residuals are
-// updated in fp32 with one rounding, exactly as the definition states.
+// summed in parallel, first in fp32.  A summation tree of depth d over
+// non-negative terms is within a relative d u/(1 - d u) of the exact sum
+// (u = 2^-24 in fp32, 2^-53 in fp64), and the serial fp64 mean is within a
+// relative ~n 2^-53 of the exact mean, so the serial mean lies within a known
+// relative margin of the parallel mean m.  If every value in
+// [m(1 - margin), m(1 + margin)] rounds to the same fp16 number, that number
+// is the serial result (rounding is monotonic): the candidate h is the fp16
+// rounding of m, accepted when the interval lies strictly between the
+// midpoints of h and its two fp16 neighbours (exact in fp32).  The fp32 test
+// leaves a few tenths of a percent of the means undecided.  Those take a
+// second tier (whole rows: the parallel fp64 sum, margin (2n + 64) 2^-53,
+// with the candidate rounded once from fp64 -- through fp32 it would round
+// twice), and what is still undecided -- exact ties, or a mean within ~1e-11
+// of an fp16 midpoint -- the serial sum itself: for a 128-column group from
+// the residuals the wave holds (read lane by lane in column order), for a
+// whole row by one lane that rebuilds each R_j from W and the scales already
+// chosen.  Exact ties do occur at the later steps of 4-plane group encodings.
+// Residuals are updated in fp32 with one rounding, exactly as the definition
+// states.
 //
-// Deciding.  The candidate h is the fp16 rounding of m itself (one rounding
-// from fp64: going through fp32 rounds twice and lands on the wrong side of
-// an fp16 midpoint about once in 10^4 means, which sent a few rows of most
-// matrices to the serial path); it is the answer for every value in
-// [m - d, m + d] exactly when that interval lies strictly between the
-// midpoints of h and its two fp16 neighbours (which fp64 holds exactly).
-//
-// Layout, whole rows.  One workgroup (4 or 16 waves) per row; the row is
-// cut into 64-column chunks and wave w keeps chunks [w*CPW, (w+1)*CPW) in
-// registers, lane l holding column 64c + l of chunk c.  Loads are therefore
-// coalesced 256-byte wave reads and a wave ballot of (R >= 0) is exactly the
-// two packed words of a chunk.  W is read from HBM once; the K steps run on
-// registers.  Sums are reduced with DPP; a row's waves meet at barriers that
-// wait for LDS only, so the plane stores of earlier steps stay in flight.
-//
-// Layout, 128-column groups.  Groups are independent and never cross a row,
-// so the matrix is a flat sequence of groups (group q = elements [128q,
-// 128q + 128) of W) and each wave encodes GPW consecutive groups, a group
-// being a chunk pair.  The group sums are taken in fp32 first: all GPW sums
-// come out of one transposed reduction (each exchange level halves the
-// number of values a lane carries until one is left), a tree of depth 7
-// (the pair |R| + |R'| and six lane levels), so the fp32 sum is within a
-// relative 7u/(1 - 7u) (u = 2^-24) of the exact sum and the serial fp64
-// mean within a relative 8u of the fp32 mean m.  If [m - 10u m, m + 10u m]
-// (the wider margin absorbs the rounding of the test itself) lies strictly
-// between the fp16 midpoints around the fp16 rounding of m, that rounding is
-// the serial result; otherwise (a small fraction of groups, and every exact tie) the
-// group takes the serial fp64 sum of its residuals.
 #include "rbq_device.h"
 #include "rbq_kernels.h"
 
@@ -61,6 +39,10 @@ namespace rbq {
 namespace {
 
 constexpr uint32_t UNDECIDED = 0xFFFFFFFFu;
+
+// v_writelane_b32 (write one lane of a VGPR from a uniform value): this
+// compiler has no builtin for it, so its LLVM intrinsic is named directly.
+extern "C" __device__ int rbq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 // Whole-wave fp64 sum (DPP row shifts and broadcasts, then lane 63), the
 // same value in every lane.  Lanes a DPP move does not reach add +0.
@@ -125,13 +107,44 @@ __device__ __forceinline__ uint16_t serial_scale(const float *__restrict__ Wr, i
     return f64_to_f16_rne(div_rn(S, (double)n));
 }
 
+// fp16 bits of a mean m computed in fp32 when every value within a relative
+// `margin` of m rounds to the same fp16 number (the interval lies strictly
+// between the midpoints around the fp16 rounding of m), else UNDECIDED.  The
+// margin covers the error of the fp32 sum and division plus two roundings of
+// this test itself.  A mean below 2^-126 (inexact in fp32) rounds to 0
+// either way.
+__device__ __forceinline__ uint32_t decide_scale_f32(float m, float margin) {
+    const uint32_t h = f2h(m);                   // one rounding, ties to even
+    if (!(h < 0x7BFFu))                          // the largest finite value, infinity, NaN
+        return UNDECIDED;
+    const float v = h2f((uint16_t)h);
+    const float below = (h == 0u) ? -0x1p-24f : h2f((uint16_t)(h - 1u));
+    const float above = h2f((uint16_t)(h + 1u));
+    const float d = m * margin;
+    const bool inside = (m - d > 0.5f * (below + v)) && (m + d < 0.5f * (v + above));
+    return inside ? h : UNDECIDED;
+}
+
+// Pairwise sum of N values (depth ceil(log2 N)), in a fixed order.
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&t)[N]) {
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w)
+            t[i] = t[i] + t[i + w];
+    return t[0];
+}
+
+constexpr int log2_ceil(int n) { return n <= 1 ? 0 : 1 + log2_ceil((n + 1) / 2); }
+
 // Shared state of one workgroup while it encodes its rows.
 template <int WAVES, int CPW>
 struct EncodeLds {
-    double part[2][WAVES];          // per-wave row sums, alternating by step
+    float part32[2][WAVES];         // per-wave fp32 row sums, alternating by exchange
+    double part[2][WAVES];          // per-wave fp64 row sums (undecided steps)
     float hist_row[8];              // scales chosen so far (serial path)
     uint32_t decided_row;
-    uint64_t bits[WAVES][CPW];      // each wave's chunk ballots of the current step
 };
 
 template <int WAVES, int CPW>
@@ -144,94 +157,138 @@ __device__ __forceinline__ void load_row(float (&R)[CPW], const float *__restric
         R[i] = Wr[min((chunk0 + i) * RBQ_WAVE + lane, in - 1)];
 }
 
-// All K steps of row r, whose columns this wave holds in R.  `phase` counts
-// the workgroup's row-sum exchanges and picks the LDS buffer.
-template <int WAVES, int CPW>
+// Step k of row r, whose columns this wave holds in R (columns past the row
+// end hold 0 and keep it; FULL: this wave has none).  `phase` counts the
+// workgroup's row-sum exchanges and picks the LDS buffer.  UPDATE: compute
+// the next residual (not after the last step).
+template <int WAVES, int CPW, bool FULL, bool UPDATE>
+__device__ __forceinline__ void row_step(float (&R)[CPW], int r, int k, const float *__restrict__ Wr,
+                                         int out, int in_row, uint32_t *__restrict__ planes,
+                                         uint16_t *__restrict__ scales, int32_t *__restrict__ status,
+                                         int force_serial, EncodeLds<WAVES, CPW> &sh, int &phase) {
+    // fp32 sum: depth log2 CPW (lane) + 6 (wave) + log2 WAVES (workgroup),
+    // division, test: within a relative 24 u for the shapes used here
+    static_assert(log2_ceil(CPW) + 6 + log2_ceil(WAVES) <= 19, "fp32 margin");
+    const int lane = threadIdx.x & (RBQ_WAVE - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE);
+    const int words = in_row >> 5;
+
+    // the row sum: each wave's share, then the waves' shares in a fixed order
+    float t[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)               // columns past the row end hold 0
+        t[i] = __builtin_fabsf(R[i]);
+    const float sw = wave_sum_f32_dpp(tree_sum<CPW>(t));
+    {
+        const int b = phase & 1;
+        ++phase;
+        if (lane == 0)
+            sh.part32[b][wave] = sw;
+        lds_barrier();
+        float p[WAVES];
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v)
+            p[v] = sh.part32[b][v];
+        const float S32 = tree_sum<WAVES>(p);
+        if (k == 0 && status != nullptr && !__builtin_isfinite(S32)) {
+            // a non-finite sum: look for a non-finite element (a finite row
+            // whose sum overflows is not flagged)
+            bool bad = false;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+                bad |= !__builtin_isfinite(R[i]);
+            if (__ballot(bad) != 0 && lane == 0)
+                atomicOr(status, (int32_t)1);
+        }
+        uint32_t h = force_serial ? UNDECIDED : decide_scale_f32(S32 / (float)in_row, 0x1.8p-20f);
+        if (h == UNDECIDED) {   // the same in every wave: the same sum in the same order
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+                s += (double)__builtin_fabsf(R[i]);
+            s = wave_sum_f64_dpp(s);
+            const int b2 = phase & 1;
+            ++phase;
+            if (lane == 0)
+                sh.part[b2][wave] = s;
+            lds_barrier();
+            double S = sh.part[b2][0];
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v)
+                S += sh.part[b2][v];
+            h = force_serial ? UNDECIDED : decide_scale(S, in_row);
+            if (h == UNDECIDED) {
+                if (threadIdx.x == 0)
+                    sh.decided_row = serial_scale(Wr, 0, in_row, sh.hist_row, 1, k);
+                lds_barrier();
+                h = sh.decided_row;
+            }
+        }
+        const float a = h2f((uint16_t)h);
+        if (threadIdx.x == 0) {
+            sh.hist_row[k] = a;
+            scales[(size_t)k * out + r] = (uint16_t)h;
+            if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
+                atomicOr(status, (int32_t)2);
+        }
+
+        // signs, packed words (chunk i's ballot is words 2i and 2i + 1, put
+        // in lanes 2i and 2i + 1) and the residual update R - (bit ? a : -a),
+        // written as fma(sign, -a, R): the product is exact, so it rounds
+        // once like the subtraction
+        static_assert(2 * CPW <= RBQ_WAVE, "one packed word per lane");
+        int in = in_row, chunk0 = wave * CPW;
+        if constexpr (!FULL)   // masks derived from the bounds are not kept across steps
+            asm volatile("" : "+s"(in), "+s"(chunk0));
+        uint32_t wv = 0;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const bool plus = R[i] >= 0.0f;
+            const uint64_t m = __ballot(plus);
+            if constexpr (UPDATE) {
+                const float upd = __builtin_fmaf(plus ? 1.0f : -1.0f, -a, R[i]);
+                if constexpr (FULL) {
+                    R[i] = upd;
+                } else {
+                    // chunk c = chunk0 + i is whole (c < in / 64), half (in % 64
+                    // = 32: lanes < 32) or past the row end
+                    const int c = chunk0 + i;
+                    const bool valid = c < (in >> 6) || (c == (in >> 6) && lane < (in & 63));
+                    R[i] = valid ? upd : R[i];
+                }
+            }
+            wv = (uint32_t)rbq_writelane_i32((int)(uint32_t)m, 2 * i, (int)wv);
+            wv = (uint32_t)rbq_writelane_i32((int)(uint32_t)(m >> 32), 2 * i + 1, (int)wv);
+        }
+        uint32_t *prow = planes + ((size_t)k * out + r) * words;
+        const int idx = chunk0 * 2 + lane;
+        if (lane < 2 * CPW && (FULL || idx < words))
+            prow[idx] = wv;
+    }
+}
+
+// All K steps of row r.
+template <int WAVES, int CPW, bool FULL>
 __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *__restrict__ W,
                                            int out, int in_row, int K,
                                            uint32_t *__restrict__ planes,
                                            uint16_t *__restrict__ scales,
                                            int32_t *__restrict__ status, int force_serial,
                                            EncodeLds<WAVES, CPW> &sh, int &phase) {
-    const int lane = threadIdx.x & (RBQ_WAVE - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE);
-    const int words = in_row >> 5;
     const float *Wr = W + (size_t)r * in_row;
-    const int chunk0_row = wave * CPW;
-
-    bool bad = false;
-    {
-        int in = in_row, chunk0 = chunk0_row;
+    if constexpr (!FULL) {
+        const int lane = threadIdx.x & (RBQ_WAVE - 1);
+        int in = in_row, chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
         asm volatile("" : "+s"(in), "+s"(chunk0));
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
+        for (int i = 0; i < CPW; ++i)
             R[i] = ((chunk0 + i) * RBQ_WAVE + lane < in) ? R[i] : 0.0f;
-            bad |= !__builtin_isfinite(R[i]);
-        }
     }
-    if (status != nullptr && __any(bad) && lane == 0)
-        atomicOr(status, (int32_t)1);
-
-    for (int k = 0; k < K; ++k) {
-        // the bounds are re-read each step: masks derived from them are then
-        // not kept in scalar registers across the whole loop
-        int in = in_row, chunk0 = chunk0_row;
-        asm volatile("" : "+s"(in), "+s"(chunk0));
-        // the row sum: each wave's share, then the waves' shares in wave order
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i)   // columns past the row end hold 0
-            s += (double)__builtin_fabsf(R[i]);
-        s = wave_sum_f64_dpp(s);
-        const int b = phase & 1;
-        ++phase;
-        if (lane == 0)
-            sh.part[b][wave] = s;
-        lds_barrier();
-        double S = sh.part[b][0];
-#pragma unroll
-        for (int v = 1; v < WAVES; ++v)
-            S += sh.part[b][v];
-        uint32_t h = force_serial ? UNDECIDED : decide_scale(S, in);
-        if (h == UNDECIDED) {  // same decision in every thread of the block
-            if (threadIdx.x == 0)
-                sh.decided_row = serial_scale(Wr, 0, in, sh.hist_row, 1, k);
-            lds_barrier();
-            h = sh.decided_row;
-        }
-        const float a_row = h2f((uint16_t)h);
-        if (threadIdx.x == 0) {
-            sh.hist_row[k] = a_row;
-            scales[(size_t)k * out + r] = (uint16_t)h;
-            if (status != nullptr && (h & 0x7FFFu) == 0x7C00u)
-                atomicOr(status, (int32_t)2);
-        }
-
-        // signs, packed words and the residual update.  Chunk i's ballot is
-        // its two packed words; the ballots go through LDS so that lane 2i + h
-        // picks up word h of chunk i with one read.
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            // chunk c = chunk0 + i is whole (c < in / 64), half (in % 64 = 32:
-            // lanes < 32) or past the row end; columns past the end keep 0
-            // and their bits are never stored
-            const int c = chunk0 + i;
-            const bool valid = c < (in >> 6) || (c == (in >> 6) && lane < (in & 63));
-            const bool plus = R[i] >= 0.0f;
-            const uint64_t m = __ballot(plus);
-            const float a = a_row;
-            if (valid)
-                R[i] = R[i] - (plus ? a : -a);
-            if (lane == 0)
-                sh.bits[wave][i] = m;
-        }
-        static_assert(2 * CPW <= RBQ_WAVE, "one packed word per lane");
-        const uint32_t wv = reinterpret_cast<const uint32_t *>(sh.bits[wave])[lane < 2 * CPW ? lane : 0];
-        uint32_t *prow = planes + ((size_t)k * out + r) * words;
-        const int idx = chunk0 * 2 + lane;
-        if (lane < 2 * CPW && idx < words)
-            prow[idx] = wv;
-    }
+    for (int k = 0; k + 1 < K; ++k)
+        row_step<WAVES, CPW, FULL, true>(R, r, k, Wr, out, in_row, planes, scales, status, force_serial, sh,
+                                         phase);
+    row_step<WAVES, CPW, FULL, false>(R, r, K - 1, Wr, out, in_row, planes, scales, status, force_serial, sh,
+                                      phase);
 }
 
 // A workgroup encodes rows blockIdx.x, blockIdx.x + gridDim.x, ...; the
@@ -243,6 +300,7 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     __shared__ EncodeLds<WAVES, CPW> sh;
     const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
+    const bool full = (chunk0 + CPW) * RBQ_WAVE <= in;   // no column past the row end
     const int G = gridDim.x;
     int phase = 0;
 
@@ -252,8 +310,10 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
         const bool more = r + G < out;
         if (more)
             load_row<WAVES, CPW>(Rn, W + (size_t)(r + G) * in, in, chunk0, lane);
-        encode_row<WAVES, CPW>(R, r, W, out, in, K, planes, scales, status,
-                                        force_serial, sh, phase);
+        if (full)
+            encode_row<WAVES, CPW, true>(R, r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
+        else
+            encode_row<WAVES, CPW, false>(R, r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
         if (more) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i)
@@ -262,15 +322,44 @@ __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     }
 }
 
+int encode_num_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int WAVES, int CPW>
+hipError_t launch_cpw(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *scales,
+                      int32_t *status, int force_serial, hipStream_t st) {
+    // as many resident workgroups as the compute units hold
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, encode_kernel<WAVES, CPW>,
+                                                         WAVES * RBQ_WAVE, 0) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        per_cu = n;
+    }
+    const long want = (long)encode_num_cus() * per_cu;
+    const int grid = (int)(want < out ? want : out);
+    hipLaunchKernelGGL((encode_kernel<WAVES, CPW>), dim3(grid), dim3(WAVES * RBQ_WAVE), 0,
+                       st, W, out, in, K, planes, scales, status, force_serial);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // 128-column groups
 // ---------------------------------------------------------------------------
 
 constexpr int GR_WAVES = 4;                     // waves per workgroup
 
-// v_writelane_b32 (write one lane of a VGPR from a uniform value): this
-// compiler has no builtin for it, so its LLVM intrinsic is named directly.
-extern "C" __device__ int rbq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 // DPP lane permutations inside a row of 16 lanes: level L pairs each lane
 // with the lane whose bit (3 - L) differs (row rotate by 8, half-row mirror,
@@ -301,21 +390,6 @@ __device__ __forceinline__ void fold_level(float (&v)[GPW], int lane) {
     }
     if constexpr (L < 3)
         fold_level<L + 1, (N > 1 ? N / 2 : 1), GPW>(v, lane);
-}
-
-// fp16 bits of the mean s / 128 when the fp32 group sum s decides it (the
-// bound of the layout notes above), else UNDECIDED.
-__device__ __forceinline__ uint32_t decide_scale_f32(float s) {
-    const float m = s * 0x1p-7f;                 // exact unless m < 2^-126 (then h = 0)
-    const uint32_t h = f2h(m);                   // one rounding, ties to even
-    if (!(h < 0x7BFFu))                          // the largest finite value, infinity, NaN
-        return UNDECIDED;
-    const float v = h2f((uint16_t)h);
-    const float below = (h == 0u) ? -0x1p-24f : h2f((uint16_t)(h - 1u));
-    const float above = h2f((uint16_t)(h + 1u));
-    const float d = m * 0x1.4p-21f;              // 10 u m
-    const bool inside = (m - d > 0.5f * (below + v)) && (m + d < 0.5f * (v + above));
-    return inside ? h : UNDECIDED;
 }
 
 // Step k of groups [q0, q0 + live) held by one wave: lane l holds element
@@ -351,7 +425,8 @@ __device__ __forceinline__ void group_step(float (&R)[2 * GPW], int k, long ngro
             atomicOr(status, (int32_t)1);
     }
 
-    uint32_t h = force_serial ? UNDECIDED : decide_scale_f32(s);
+    // mean s / 128 (exact unless below 2^-126); margin 10 u
+    uint32_t h = force_serial ? UNDECIDED : decide_scale_f32(s * 0x1p-7f, 0x1.4p-21f);
     const uint64_t undecided = __ballot(h == UNDECIDED);
     if (undecided != 0) {
 #pragma unroll
@@ -442,38 +517,6 @@ hipError_t launch_groups(const float *W, int out, int in, int K, uint32_t *plane
         return hipErrorInvalidValue;
     const long ngroups = (long)out * (in / 128);
     return launch_gpw<8>(W, ngroups, K, planes, scales, status, force_serial, st);
-}
-
-int encode_num_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
-    return cus;
-}
-
-template <int WAVES, int CPW>
-hipError_t launch_cpw(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *scales,
-                      int32_t *status, int force_serial, hipStream_t st) {
-    // as many resident workgroups as the compute units hold
-    static int per_cu = 0;
-    if (per_cu == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, encode_kernel<WAVES, CPW>,
-                                                         WAVES * RBQ_WAVE, 0) != hipSuccess ||
-            n <= 0)
-            n = 1;
-        per_cu = n;
-    }
-    const long want = (long)encode_num_cus() * per_cu;
-    const int grid = (int)(want < out ? want : out);
-    hipLaunchKernelGGL((encode_kernel<WAVES, CPW>), dim3(grid), dim3(WAVES * RBQ_WAVE), 0,
-                       st, W, out, in, K, planes, scales, status, force_serial);
-    return hipGetLastError();
 }
 
 }  // namespace
