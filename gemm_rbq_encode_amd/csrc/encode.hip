@@ -147,14 +147,26 @@ struct EncodeLds {
     uint32_t decided_row;
 };
 
-template <int WAVES, int CPW>
-__device__ __forceinline__ void load_row(float (&R)[CPW], const float *__restrict__ Wr, int in,
+// This wave's columns of row r: FULL, every chunk inside the row (one base
+// address, the chunks at immediate offsets); otherwise columns past the row
+// end are not read and hold 0.
+template <int CPW, bool FULL>
+__device__ __forceinline__ void load_row(float (&R)[CPW], const float *__restrict__ Wr, int in_row,
                                          int chunk0, int lane) {
-    // columns past the row end read its last column (never used: encode_row
-    // replaces them by zeros)
+    const float *p = Wr + chunk0 * RBQ_WAVE + lane;
+    if constexpr (FULL) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
-        R[i] = Wr[min((chunk0 + i) * RBQ_WAVE + lane, in - 1)];
+        for (int i = 0; i < CPW; ++i)
+            R[i] = p[i * RBQ_WAVE];
+    } else {
+        // the bounds are opaque here, so that per-chunk masks are not kept
+        // in registers across rows
+        int in = in_row, c0 = chunk0;
+        asm volatile("" : "+s"(in), "+s"(c0));
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            R[i] = ((c0 + i) * RBQ_WAVE + lane < in) ? p[i * RBQ_WAVE] : 0.0f;
+    }
 }
 
 // Step k of row r, whose columns this wave holds in R (columns past the row
@@ -269,21 +281,14 @@ __device__ __forceinline__ void row_step(float (&R)[CPW], int r, int k, const fl
 
 // All K steps of row r.
 template <int WAVES, int CPW, bool FULL>
-__device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *__restrict__ W,
-                                           int out, int in_row, int K,
-                                           uint32_t *__restrict__ planes,
-                                           uint16_t *__restrict__ scales,
+__device__ __forceinline__ void encode_row(int r, const float *__restrict__ W, int out, int in_row, int K,
+                                           uint32_t *__restrict__ planes, uint16_t *__restrict__ scales,
                                            int32_t *__restrict__ status, int force_serial,
                                            EncodeLds<WAVES, CPW> &sh, int &phase) {
     const float *Wr = W + (size_t)r * in_row;
-    if constexpr (!FULL) {
-        const int lane = threadIdx.x & (RBQ_WAVE - 1);
-        int in = in_row, chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
-        asm volatile("" : "+s"(in), "+s"(chunk0));
-#pragma unroll
-        for (int i = 0; i < CPW; ++i)
-            R[i] = ((chunk0 + i) * RBQ_WAVE + lane < in) ? R[i] : 0.0f;
-    }
+    float R[CPW];
+    load_row<CPW, FULL>(R, Wr, in_row, __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW,
+                        threadIdx.x & (RBQ_WAVE - 1));
     for (int k = 0; k + 1 < K; ++k)
         row_step<WAVES, CPW, FULL, true>(R, r, k, Wr, out, in_row, planes, scales, status, force_serial, sh,
                                          phase);
@@ -291,34 +296,23 @@ __device__ __forceinline__ void encode_row(float (&R)[CPW], int r, const float *
                                       phase);
 }
 
-// A workgroup encodes rows blockIdx.x, blockIdx.x + gridDim.x, ...; the
-// loads of its next row are in flight while it encodes the current one.
+// A workgroup encodes rows blockIdx.x, blockIdx.x + gridDim.x, ...  It does
+// not prefetch its next row: the registers that would take are worth more
+// as further resident workgroups, whose loads overlap this one's steps
+// (4096 x 4096: 17.0 us with a one-row prefetch, 14.8 us without).
 template <int WAVES, int CPW>
 __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     const float *__restrict__ W, int out, int in, int K, uint32_t *__restrict__ planes,
     uint16_t *__restrict__ scales, int32_t *__restrict__ status, int force_serial) {
     __shared__ EncodeLds<WAVES, CPW> sh;
-    const int lane = threadIdx.x & (RBQ_WAVE - 1);
     const int chunk0 = __builtin_amdgcn_readfirstlane(threadIdx.x / RBQ_WAVE) * CPW;
     const bool full = (chunk0 + CPW) * RBQ_WAVE <= in;   // no column past the row end
-    const int G = gridDim.x;
     int phase = 0;
-
-    float R[CPW], Rn[CPW];
-    load_row<WAVES, CPW>(R, W + (size_t)blockIdx.x * in, in, chunk0, lane);
-    for (int r = blockIdx.x; r < out; r += G) {
-        const bool more = r + G < out;
-        if (more)
-            load_row<WAVES, CPW>(Rn, W + (size_t)(r + G) * in, in, chunk0, lane);
+    for (int r = blockIdx.x; r < out; r += gridDim.x) {
         if (full)
-            encode_row<WAVES, CPW, true>(R, r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
+            encode_row<WAVES, CPW, true>(r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
         else
-            encode_row<WAVES, CPW, false>(R, r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < CPW; ++i)
-                R[i] = Rn[i];
-        }
+            encode_row<WAVES, CPW, false>(r, W, out, in, K, planes, scales, status, force_serial, sh, phase);
     }
 }
 
@@ -347,7 +341,20 @@ hipError_t launch_cpw(const float *W, int out, int in, int K, uint32_t *planes, 
             n = 1;
         per_cu = n;
     }
-    const long want = (long)encode_num_cus() * per_cu;
+    // Workgroups per compute unit: the most that fit whose rows divide
+    // evenly enough.  A workgroup's rows run one after another, so a compute
+    // unit finishes with its workgroup that has the most rows; p per unit
+    // costs ceil(out / (cus p)) p row times against out / cus ideally
+    // (11008 rows: 8 per unit give 6 x 8 = 48 against 43).
+    const int cus = encode_num_cus();
+    int p = per_cu;
+    while (p > 1) {
+        const long rows = ((long)out + (long)cus * p - 1) / ((long)cus * p);
+        if (rows * p * cus <= (long)out * 105 / 100 + (long)cus)
+            break;
+        --p;
+    }
+    const long want = (long)cus * p;
     const int grid = (int)(want < out ? want : out);
     hipLaunchKernelGGL((encode_kernel<WAVES, CPW>), dim3(grid), dim3(WAVES * RBQ_WAVE), 0,
                        st, W, out, in, K, planes, scales, status, force_serial);
@@ -526,10 +533,12 @@ hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
                          hipStream_t st) {
     if (group_size)
         return launch_groups(W, out, in, K, planes, scales, status, force_serial, st);
-    // Rows of up to 4096 columns: 4 waves; longer rows: 16 waves, so that each
-    // lane keeps at most 2 x 32 values of two rows in registers.
+    // Rows of up to 4096 columns: 4 waves; up to 16384: 8 waves; longer: 16
+    // waves.  Chunks per wave come in steps that keep the idle chunks of
+    // the common widths few (11008 columns: 8 x 22 of 172 chunks; 8 x 24
+    // would leave 20 idle).
     const int chunks = (in + RBQ_WAVE - 1) / RBQ_WAVE;
-    const int waves = chunks <= 64 ? 4 : 16;
+    const int waves = chunks <= 64 ? 4 : chunks <= 256 ? 8 : 16;
     const int need = (chunks + waves - 1) / waves;
 #define RBQ_ENC_CASE(WV, C)                                                              \
     if (waves == WV && need <= C)                                                        \
@@ -538,10 +547,13 @@ hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
     RBQ_ENC_CASE(4, 4)
     RBQ_ENC_CASE(4, 8)
     RBQ_ENC_CASE(4, 16)
-    RBQ_ENC_CASE(16, 6)
-    RBQ_ENC_CASE(16, 8)
-    RBQ_ENC_CASE(16, 12)
-    RBQ_ENC_CASE(16, 16)
+    RBQ_ENC_CASE(8, 12)
+    RBQ_ENC_CASE(8, 16)
+    RBQ_ENC_CASE(8, 20)
+    RBQ_ENC_CASE(8, 22)
+    RBQ_ENC_CASE(8, 24)
+    RBQ_ENC_CASE(8, 28)
+    RBQ_ENC_CASE(8, 32)
     RBQ_ENC_CASE(16, 24)
     RBQ_ENC_CASE(16, 32)
 #undef RBQ_ENC_CASE
