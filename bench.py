@@ -290,18 +290,18 @@ def bench_layer_set(args):
     for i, lin in uniq:
         W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
         p, sc = rbq.encode(W, K, group)
-        if group:
-            # encoder and refit time of this shape (outputs rewritten in place)
-            key = f"{lin.out_features}x{lin.in_features}"
-            pe, se, sr = torch.empty_like(p), torch.empty_like(sc), sc.clone()
-            enc_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)], 3)
-            ref_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)], 3)
-            wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * sc.numel()
-            prep[key] = {"encode_us": round(enc_ms * 1e3, 1),
-                         "encode_GBps": round((wb + pb + sb) / (enc_ms * 1e-3) / 1e9, 1),
-                         "refit_us": round(ref_ms * 1e3, 1),
-                         "refit_GBps": round((wb + pb + 2 * sb) / (ref_ms * 1e-3) / 1e9, 1)}
-            del pe, se, sr
+        # encoder and refit time of this shape (outputs rewritten in place)
+        key = f"{lin.out_features}x{lin.in_features}"
+        pe, se, sr = torch.empty_like(p), torch.empty_like(sc), sc.clone()
+        # ten calls per graph, three replays
+        enc_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)] * 10, 3) / 10
+        ref_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)] * 10, 3) / 10
+        wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * sc.numel()
+        prep[key] = {"encode_us": round(enc_ms * 1e3, 1),
+                     "encode_GBps": round((wb + pb + sb) / (enc_ms * 1e-3) / 1e9, 1),
+                     "refit_us": round(ref_ms * 1e3, 1),
+                     "refit_GBps": round((wb + pb + 2 * sb) / (ref_ms * 1e-3) / 1e9, 1)}
+        del pe, se, sr
         del W
         X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
         Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
@@ -448,6 +448,22 @@ def bench_decode(args):
                     for W, p, s in zip(Ws, enc_planes, ref_scales))
     ref_ms = graph_ms(torch, dev, [(lambda W=W, p=p, s=s: rbq.refit(W, p, s, group))
                                    for W, p, s in zip(Ws, enc_planes, ref_scales)], 5)
+    # per distinct shape: encoder and refit time of one matrix
+    prep = {}
+    for W, p, s in zip(Ws, enc_planes, enc_scales):
+        key = f"{W.shape[0]}x{W.shape[1]}"
+        if key in prep:
+            continue
+        pe, se, sr = torch.empty_like(p), torch.empty_like(s), s.clone()
+        # ten calls per graph, three replays
+        e_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)] * 10, 3) / 10
+        r_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)] * 10, 3) / 10
+        wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * s.numel()
+        prep[key] = {"encode_us": round(e_ms * 1e3, 1),
+                     "encode_GBps": round((wb + pb + sb) / (e_ms * 1e-3) / 1e9, 1),
+                     "refit_us": round(r_ms * 1e3, 1),
+                     "refit_GBps": round((wb + pb + 2 * sb) / (r_ms * 1e-3) / 1e9, 1)}
+        del pe, se, sr
     del Ws, ref_scales
 
     # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
@@ -613,6 +629,7 @@ def bench_decode(args):
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
         "refit": {"linears": len(wl.linears), "ms": round(ref_ms, 4),
                   "GBps": round(ref_bytes / (ref_ms * 1e-3) / 1e9, 1)},
+        "encode_refit_per_shape": prep,
         "decode_layer_chain": layer_chain,
     }
     print(json.dumps(line), flush=True)
