@@ -544,3 +544,131 @@ def test_silu_mul_against_scipy_expit():
     np.testing.assert_allclose(H, Y[:, 0::2] * expit(Y[:, 0::2]) * Y[:, 1::2], rtol=1e-14)
     Z = np.array([[0.0, 5.0, 40.0, 2.0, -40.0, 3.0]])
     np.testing.assert_allclose(oracle.silu_mul(Z), [[0.0, 80.0, -40.0 * np.exp(-40.0) * 3.0]], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# dual-scale paths (RaBiT section 4.1: per-channel scales on both sides of
+# each binary core; section 4.3 / "RaBiT initialization": residual SVID)
+# ---------------------------------------------------------------------------
+
+from oracle import dual  # noqa: E402
+
+
+def _f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def test_dual_rank1_exact_for_rank1_magnitudes():
+    """|W| = a b^T exactly: the fit reproduces it and B_1 = sign(W)."""
+    rng = np.random.default_rng(41)
+    # binary16 factors: their products are exact in fp32, so |W| is exactly rank 1
+    a = rng.uniform(0.5, 2.0, 24).astype(np.float16).astype(np.float64)
+    b = rng.uniform(0.1, 1.0, 64).astype(np.float16).astype(np.float64)
+    S = np.where(rng.random((24, 64)) < 0.5, -1.0, 1.0)
+    W = (S * np.outer(a, b)).astype(np.float32)
+    assert np.array_equal(np.abs(W).astype(np.float64), np.outer(a, b))
+    u, v = dual.svid_rank1(np.abs(W).astype(np.float64))
+    A = np.abs(W).astype(np.float64)
+    assert np.abs(np.outer(u, v) - A).max() <= 1e-12 * A.max()
+    planes, g, h = dual.encode_dual(W, 1)
+    assert np.array_equal(unpack_signs(planes)[0], S.astype(np.int8))
+
+
+def test_dual_rank1_matches_numpy_svd():
+    """On non-square |R| the fit equals the top singular triple s1 u1 v1^T
+    (a transposed operand or a dropped normalisation would not)."""
+    rng = np.random.default_rng(42)
+    A = np.abs(rng.standard_normal((48, 80)))
+    u, v = dual.svid_rank1(A)
+    U, s, Vt = np.linalg.svd(A)
+    ref = s[0] * np.outer(U[:, 0], Vt[0])
+    assert np.linalg.norm(np.outer(u, v) - ref) <= 1e-9 * np.linalg.norm(ref)
+
+
+def test_dual_row_constant_magnitudes_give_row_scales():
+    """|W_rj| = c_r: the rank-1 fit is c 1^T, the per-row scale of the
+    single-scale method (mean |W_r| = c_r)."""
+    rng = np.random.default_rng(43)
+    c = rng.uniform(0.01, 0.05, 16)
+    W = (np.where(rng.random((16, 96)) < 0.5, -1.0, 1.0) * c[:, None]).astype(np.float32)
+    u, v = dual.svid_rank1(np.abs(W).astype(np.float64))
+    assert np.allclose(np.outer(u, v), np.abs(W).astype(np.float64), rtol=1e-12, atol=0)
+    assert np.allclose(v, v[0], rtol=1e-12)
+
+
+def test_dual_fit_never_worse_than_row_means():
+    """The first least-squares step from v = 1 is the row-mean fit; later
+    steps only lower the error, so the final fit is no worse."""
+    rng = np.random.default_rng(44)
+    for _ in range(5):
+        A = np.abs(rng.standard_normal((32, 64)) * rng.uniform(0.2, 3.0, 64)[None, :])
+        u, v = dual.svid_rank1(A)
+        e_fit = np.linalg.norm(A - np.outer(u, v))
+        e_row = np.linalg.norm(A - A.mean(axis=1, keepdims=True))
+        assert e_fit <= e_row * (1 + 1e-12)
+        assert e_fit < e_row   # column scales that differ are worth something
+
+
+def test_dual_residual_norms_do_not_grow():
+    rng = np.random.default_rng(45)
+    W = workloads.gaussian_weight(32, 256, seed=46, outliers=True)
+    planes, g, h = dual.encode_dual(W, 4)
+    prev = np.linalg.norm(W.astype(np.float64))
+    for k in range(1, 5):
+        What = dual.dequant_dual(planes[:k], g[:k], h[:k])
+        err = np.linalg.norm(W.astype(np.float64) - What)
+        assert err <= prev * (1 + 1e-3)
+        prev = err
+    # and the dual scales fit at least as well as one scale per row
+    p1, s1, _ = oracle.encode(W, 4)
+    err_row = np.linalg.norm(W.astype(np.float64) - oracle.dequant(p1, s1))
+    assert prev <= err_row * 1.01
+
+
+def test_dual_first_plane_matches_c_oracle_and_layout():
+    """B_1 = sign(W) packed in the canonical layout: the same words as the C
+    oracle's first plane (independent code); -0.0 counts as +1."""
+    W = workloads.gaussian_weight(8, 160, seed=47)
+    W[1, 5] = -0.0
+    W[2, 33] = 0.0
+    planes, _, _ = dual.encode_dual(W, 1)
+    p_c, _, _ = oracle.encode(W, 1)
+    assert np.array_equal(planes, p_c)
+
+
+def test_dual_scales_are_balanced_fp16_roundings():
+    rng = np.random.default_rng(48)
+    A = np.abs(rng.standard_normal((20, 64))) * 0.02
+    u, v = dual.svid_rank1(A)
+    c = math.sqrt(math.sqrt(u @ u) / math.sqrt(v @ v))
+    g, h = dual.svid_scales(A)
+    assert np.array_equal(g, np.asarray(u / c, dtype=np.float64).astype(np.float16).view(np.uint16))
+    assert np.array_equal(h, np.asarray(v * c, dtype=np.float64).astype(np.float16).view(np.uint16))
+    assert abs(np.linalg.norm(u / c) - np.linalg.norm(v * c)) <= 1e-12 * np.linalg.norm(v * c)
+
+
+def test_dual_layer_output_against_loops():
+    """y_r = sum_k g_k[r] sum_j (bit ? +1 : -1) h_k[j] x_j by plain loops."""
+    rng = np.random.default_rng(49)
+    out, inf, K = 4, 64, 2
+    words = rng.integers(0, 2 ** 32, (K, out, inf // 32), dtype=np.uint64).astype(np.uint32)
+    g = rng.uniform(0.01, 0.1, (K, out)).astype(np.float16).view(np.uint16)
+    h = rng.uniform(0.2, 2.0, (K, inf)).astype(np.float16).view(np.uint16)
+    x = rng.standard_normal((1, inf)).astype(np.float16)
+    y = dual.gemm_dual(words, g, h, x)[0]
+    for r in range(out):
+        ref = 0.0
+        for k in range(K):
+            acc = 0.0
+            for j in range(inf):
+                bit = (int(words[k, r, j // 32]) >> (j % 32)) & 1
+                acc += (1.0 if bit else -1.0) * float(_f16(h[k, j])) * float(x[0, j])
+            ref += float(_f16(g[k, r])) * acc
+        assert abs(y[r] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_dual_zero_matrix_gives_zero_scales():
+    W = np.zeros((4, 64), np.float32)
+    planes, g, h = dual.encode_dual(W, 2)
+    assert not g.any() and not h.any()
+    assert (planes == 0xFFFFFFFF).all()
