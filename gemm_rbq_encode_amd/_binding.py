@@ -75,6 +75,14 @@ _SIGNATURES = {
     "rbq_gemm_workspace_bytes": (ctypes.c_size_t, [Shape, ctypes.c_int32]),
     "rbq_gemv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_dual_g_bytes": (ctypes.c_size_t, [Shape]),
+    "rbq_dual_h_bytes": (ctypes.c_size_t, [Shape]),
+    "rbq_encode_dual_workspace_bytes": (ctypes.c_size_t, [Shape]),
+    "rbq_encode_dual": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_gemv_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, Shape,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
     "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
@@ -270,4 +278,63 @@ def gemv(planes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, group_size
     _dev(y, torch.float16, "y")
     check(lib().rbq_gemv(planes.data_ptr(), scales.data_ptr(), s, x.data_ptr(), y.data_ptr(),
                          _stream(x, stream)), "rbq_gemv")
+    return y
+
+
+def encode_dual_workspace_bytes(s: Shape) -> int:
+    return int(lib().rbq_encode_dual_workspace_bytes(s))
+
+
+def encode_dual(W: torch.Tensor, num_planes: int, *, workspace: torch.Tensor | None = None,
+                status: torch.Tensor | None = None, planes: torch.Tensor | None = None,
+                g: torch.Tensor | None = None, h: torch.Tensor | None = None, stream=None):
+    """rbq_encode_dual: fp32 W [out][in] -> (planes int32 [K][out][in/32],
+    g float16 [K][out], h float16 [K][in]), scales from a residual SVID."""
+    _dev(W, torch.float32, "W")
+    out_f, in_f = W.shape
+    s = shape(out_f, in_f, num_planes, 0)
+    if planes is None:
+        planes = torch.empty((num_planes, out_f, in_f // 32), dtype=torch.int32, device=W.device)
+    if g is None:
+        g = torch.empty((num_planes, out_f), dtype=torch.float16, device=W.device)
+    if h is None:
+        h = torch.empty((num_planes, in_f), dtype=torch.float16, device=W.device)
+    _dev(planes, torch.int32, "planes")
+    _dev(g, torch.float16, "g")
+    _dev(h, torch.float16, "h")
+    if (planes.numel() * 4 < planes_bytes(s) or g.numel() * 2 < int(lib().rbq_dual_g_bytes(s))
+            or h.numel() * 2 < int(lib().rbq_dual_h_bytes(s))):
+        raise ValueError("planes/g/h buffers are too small for the shape")
+    need = encode_dual_workspace_bytes(s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    check(lib().rbq_encode_dual(W.data_ptr(), s, planes.data_ptr(), g.data_ptr(), h.data_ptr(),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp,
+                                _stream(W, stream)), "rbq_encode_dual")
+    return planes, g, h
+
+
+def gemv_dual(planes: torch.Tensor, g: torch.Tensor, h: torch.Tensor, x: torch.Tensor, *,
+              y: torch.Tensor | None = None, stream=None):
+    """rbq_gemv_dual: y[out] = sum_k g_k (.) (B_k (h_k (.) x)), fp16 in and out."""
+    _dev(planes, torch.int32, "planes")
+    _dev(g, torch.float16, "g")
+    _dev(h, torch.float16, "h")
+    _dev(x, torch.float16, "x")
+    K, out_f, words = planes.shape
+    in_f = words * 32
+    if x.numel() != in_f:
+        raise ValueError(f"x must have {in_f} elements")
+    s = shape(out_f, in_f, K, 0)
+    if g.numel() * 2 < int(lib().rbq_dual_g_bytes(s)) or h.numel() * 2 < int(lib().rbq_dual_h_bytes(s)):
+        raise ValueError("g/h buffers are too small for the shape")
+    if y is None:
+        y = torch.empty(out_f, dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "y")
+    check(lib().rbq_gemv_dual(planes.data_ptr(), g.data_ptr(), h.data_ptr(), s, x.data_ptr(),
+                              y.data_ptr(), _stream(x, stream)), "rbq_gemv_dual")
     return y

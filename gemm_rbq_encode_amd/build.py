@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librbq.so")
 
-SOURCES = ["api.hip", "encode.hip", "gemm_valu.hip", "gemm_decode.hip", "gemm_stream.hip",
+SOURCES = ["api.hip", "encode.hip", "encode_dual.hip", "gemm_valu.hip", "gemm_decode.hip", "gemm_stream.hip",
            "gemm_flat.hip", "gemm_group.hip", "gemm_split.hip", "gemm_prefill.hip", "refit.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

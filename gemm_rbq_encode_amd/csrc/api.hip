@@ -269,6 +269,81 @@ rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
     return rbq_gemm(planes, scales, s, x, 1, y, nullptr, 0, stream);
 }
 
+size_t rbq_dual_g_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK || s.group_size != 0)
+        return 0;
+    return (size_t)s.num_planes * (size_t)s.out_features * 2u;
+}
+
+size_t rbq_dual_h_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK || s.group_size != 0)
+        return 0;
+    return (size_t)s.num_planes * (size_t)s.in_features * 2u;
+}
+
+size_t rbq_encode_dual_workspace_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK || s.group_size != 0)
+        return 0;
+    return rbq::encode_dual_workspace_bytes(s.out_features, s.in_features);
+}
+
+rbq_status rbq_encode_dual(const float *W, rbq_shape s, uint32_t *planes, uint16_t *g, uint16_t *h,
+                           void *workspace, size_t workspace_bytes, int32_t *status_dev, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (s.group_size != 0)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.out_features == 0 || s.in_features == 0)
+        return RBQ_OK;
+    if (s.in_features % 128 != 0 || s.in_features > RBQ_DUAL_MAX_IN)
+        return RBQ_ERR_UNSUPPORTED;
+    if (W == nullptr || planes == nullptr || g == nullptr || h == nullptr || workspace == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (workspace_bytes < rbq_encode_dual_workspace_bytes(s))
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(W, 4) || !aligned(planes, 4) || !aligned(g, 2) || !aligned(h, 2) ||
+        !aligned(workspace, 256) || (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_encode_dual(W, s.out_features, s.in_features, s.num_planes, planes, g, h,
+                                           workspace, status_dev, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,
+                         const uint16_t *x, uint16_t *y, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (s.group_size != 0)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.out_features == 0)
+        return RBQ_OK;
+    if (y == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(y, 2))
+        return RBQ_ERR_ALIGNMENT;
+    hipStream_t hs = (hipStream_t)stream;
+    if (s.in_features == 0) {  // empty sums: y = 0
+        if ((st = device_present()) != RBQ_OK)
+            return st;
+        hipError_t e = rbq::launch_fill_zero_u16(y, s.out_features, hs);
+        return e == hipSuccess ? RBQ_OK : hip_fail(e);
+    }
+    if (!rbq::dual_supports(s.in_features, s.num_planes))
+        return RBQ_ERR_UNSUPPORTED;
+    if (planes == nullptr || g == nullptr || h == nullptr || x == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(planes, 16) || !aligned(g, 2) || !aligned(h, 16) || !aligned(x, 16))
+        return RBQ_ERR_ALIGNMENT;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_gemv_dual(planes, g, h, s.out_features, s.in_features, s.num_planes, x, y, hs);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 int32_t rbq_last_hip_error(void) { return g_last_hip_error; }
 
 const char *rbq_status_string(rbq_status st) {

@@ -64,10 +64,17 @@ __device__ __forceinline__ void wave_sync() {
 // used, so a workgroup pays one memory round trip per batch (one batch
 // covers rows of up to 4096*CPW columns).  Each batch has its own
 // activation scale per token and is folded into a float partial output.
-template <int K, int CPW, int MT>
+//
+// DUAL: one token and per-plane input scales h_k [K][in] (row scales g_k in
+// `scales`): y = sum_k g_k (.) (B_k (h_k (.) x)).  The K products h_k (.) x
+// take the place of the tokens -- each is formed exactly in fp32 (two
+// binary16 factors) and quantised with its own power of two -- and plane k
+// keeps only its sums against copy k, so the MFMA count is that of one token.
+template <int K, int CPW, int MT, bool DUAL>
 __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
-    const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
+    const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y, const uint16_t *__restrict__ H) {
+    static_assert(!DUAL || MT == K, "dual scales: one activation copy per plane");
     // LDS: per wave, the B image of one chunk, [s 8][g 4][n NC][16 bytes],
     // followed by 16 zero bytes read by the MFMA columns not in use
     extern __shared__ __align__(16) unsigned char lds[];
@@ -117,7 +124,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
     for (int base = wave; base < nchunks; base += DEC_WAVES * CPW) {
         // ---- every load of the batch first
         v4u wv[CPW][K];
-        uint4 xv[CPW][MT];
+        uint4 xv[CPW][MT];      // DUAL: the h_k of this lane's columns
+        uint4 x1[DUAL ? CPW : 1];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
             // chunks past the row are never multiplied; words past the row
@@ -130,12 +138,17 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
                     planes + ((size_t)k * out + row) * words + wi));
             const int col = c * CHUNK_COLS + 8 * lane;
             const int colc = min(col, in - 8);
+            const bool ok = col < in;   // a select on the value, not a guarded load
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(
-                    X + (size_t)(m0 + min(m, mt - 1)) * in + colc);
-                const bool ok = col < in;   // a select on the value, not a guarded load
+                const uint16_t *src = DUAL ? H + (size_t)m * in + colc
+                                           : X + (size_t)(m0 + min(m, mt - 1)) * in + colc;
+                const uint4 u = *reinterpret_cast<const uint4 *>(src);
                 xv[cc][m] = make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
+            }
+            if constexpr (DUAL) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(X + colc);
+                x1[cc] = make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
             }
         }
 
@@ -143,6 +156,25 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
         int sh[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+            if constexpr (DUAL) {
+                // max |x h_k| in fp32 (non-negative floats order as integers);
+                // a non-zero product is at least 2^-48
+                uint32_t mb = 0;
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc) {
+                    const uint32_t hh[4] = {xv[cc][m].x, xv[cc][m].y, xv[cc][m].z, xv[cc][m].w};
+                    const uint32_t xx[4] = {x1[cc].x, x1[cc].y, x1[cc].z, x1[cc].w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float p = h2f((uint16_t)(xx[j >> 1] >> (16 * (j & 1)))) *
+                                        h2f((uint16_t)(hh[j >> 1] >> (16 * (j & 1))));
+                        mb = max(mb, __builtin_bit_cast(uint32_t, p) & 0x7FFFFFFFu);
+                    }
+                }
+                const uint32_t mx = wave_max_u32_dpp(mb);
+                sh[m] = mx == 0 ? 0 : 148 - (int)(mx >> 23);   // max < 2^(e - 126)
+                continue;
+            }
             v2u16 mx2 = (v2u16){0, 0};
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) {
@@ -187,11 +219,16 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
                 const float scale = __builtin_ldexpf(1.0f, sh[m]);
                 const uint4 u = xv[cc][m];
                 const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+                const uint32_t xx[4] = {x1[DUAL ? cc : 0].x, x1[DUAL ? cc : 0].y, x1[DUAL ? cc : 0].z,
+                                        x1[DUAL ? cc : 0].w};
                 int part = 0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const uint32_t hb = (j & 1) ? (uu[j >> 1] >> 16) : (uu[j >> 1] & 0xFFFFu);
-                    const float f = __builtin_fmaf(h2f((uint16_t)hb), scale, 12582912.0f);
+                    float xf = h2f((uint16_t)hb);
+                    if constexpr (DUAL)   // x_j h_kj, exact in fp32
+                        xf = h2f((uint16_t)(xx[j >> 1] >> (16 * (j & 1)))) * xf;
+                    const float f = __builtin_fmaf(xf, scale, 12582912.0f);
                     const uint32_t v = __builtin_bit_cast(uint32_t, f) + (0x808080u - 0x4B400000u);
                     part += (int)v;
                     const uint32_t lb = v ^ 0x808080u;
@@ -248,7 +285,11 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
                 const float tm = (float)row_shl_i32<1>(t);
                 const float tl = (float)row_shl_i32<2>(t);
                 const float T = (float)t * 65536.0f + tm * 256.0f + tl;   // 2^7 * sum(bit * q)
-                yv += a[k][v] * (T * (2.0f / 128.0f) - sxm);
+                const float contrib = a[k][v] * (T * (2.0f / 128.0f) - sxm);
+                if constexpr (DUAL)
+                    yv += (my_m == k) ? contrib : 0.0f;   // plane k against its own copy
+                else
+                    yv += contrib;
             }
             yacc[v] += __builtin_ldexpf(yv, -shm);
         }
@@ -260,6 +301,21 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
             red[wave][my_m][4 * lg + v] = yacc[v];
     }
     __syncthreads();
+    if constexpr (DUAL) {
+        if (threadIdx.x < TILE_ROWS) {
+            const int r = row0 + threadIdx.x;
+            if (r < out) {
+                float y = 0.0f;
+#pragma unroll
+                for (int w = 0; w < DEC_WAVES; ++w)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        y += red[w][m][threadIdx.x];
+                Y[r] = f2h(y);
+            }
+        }
+        return;
+    }
     if (threadIdx.x < mt * TILE_ROWS) {
         const int mm = threadIdx.x / TILE_ROWS, i = threadIdx.x % TILE_ROWS;
         const int r = row0 + i;
@@ -273,16 +329,29 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void gemm_decode_kernel(
     }
 }
 
-template <int K, int CPW, int MT>
+template <int K, int CPW, int MT, bool DUAL = false>
 hipError_t launch_kcm(const uint32_t *planes, const uint16_t *scales, int out, int in,
-                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st) {
+                      const uint16_t *X, int M, uint16_t *Y, hipStream_t st, const uint16_t *H = nullptr) {
     const int tiles = (out + TILE_ROWS - 1) / TILE_ROWS;
     const int passes = (M + MT - 1) / MT;
     const int mt = M < MT ? M : MT;
     const size_t lds = (size_t)DEC_WAVES * (IMG_BYTES_PER_NC * 3 * mt + 16);
-    hipLaunchKernelGGL((gemm_decode_kernel<K, CPW, MT>), dim3(tiles, passes), dim3(DEC_THREADS),
-                       lds, st, planes, scales, out, in, X, M, Y);
+    hipLaunchKernelGGL((gemm_decode_kernel<K, CPW, MT, DUAL>), dim3(tiles, passes), dim3(DEC_THREADS),
+                       lds, st, planes, scales, out, in, X, M, Y, H);
     return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_dual_k(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                         const uint16_t *x, uint16_t *y, hipStream_t st) {
+    // M = K "tokens" (the K scaled copies of x) in one pass
+    const int nchunks = (in / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+    const int per_wave = (nchunks + DEC_WAVES - 1) / DEC_WAVES;
+    if (per_wave <= 1)
+        return launch_kcm<K, 1, K, true>(planes, g, out, in, x, K, y, st, h);
+    if (per_wave <= 2)
+        return launch_kcm<K, 2, K, true>(planes, g, out, in, x, K, y, st, h);
+    return launch_kcm<K, 4, K, true>(planes, g, out, in, x, K, y, st, h);
 }
 
 template <int K>
@@ -308,6 +377,23 @@ hipError_t launch_k(const uint32_t *planes, const uint16_t *scales, int out, int
 
 bool decode_supports(int in, int K, int group_size, int M) {
     return group_size == 0 && K >= 1 && K <= 4 && in % 128 == 0 && M >= 1 && M <= 65535 * 5;
+}
+
+bool dual_supports(int in, int K) {
+    return K >= 1 && K <= 4 && in % 128 == 0;
+}
+
+hipError_t launch_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                            int K, const uint16_t *x, uint16_t *y, hipStream_t st) {
+    if (!dual_supports(in, K))
+        return hipErrorInvalidValue;
+    switch (K) {
+    case 1: return launch_dual_k<1>(planes, g, h, out, in, x, y, st);
+    case 2: return launch_dual_k<2>(planes, g, h, out, in, x, y, st);
+    case 3: return launch_dual_k<3>(planes, g, h, out, in, x, y, st);
+    case 4: return launch_dual_k<4>(planes, g, h, out, in, x, y, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_decode(const uint32_t *planes, const uint16_t *scales, int out, int in,

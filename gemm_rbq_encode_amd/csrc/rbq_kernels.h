@@ -29,6 +29,17 @@ hipError_t launch_gemm_decode(const uint32_t *planes, const uint16_t *scales, in
                               int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                               hipStream_t st);
 
+// Dual-scale GEMV on the decode kernel: y = sum_k g_k (.) (B_k (h_k (.) x)),
+// g [K][out], h [K][in] binary16, one token (K <= 4, in % 128 == 0).
+bool dual_supports(int in, int K);
+hipError_t launch_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                            int K, const uint16_t *x, uint16_t *y, hipStream_t st);
+
+// Residual SVID encoder (dual scales); workspace layout in encode_dual.hip.
+size_t encode_dual_workspace_bytes(int out, int in);
+hipError_t launch_encode_dual(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *g,
+                              uint16_t *h, void *workspace, int32_t *status, hipStream_t st);
+
 // Whole-row streaming int8-MFMA kernel for 1-2 tokens (per-row scales,
 // K <= 4, in % 128 == 0, activation image of in*3*M bytes in LDS).  split =
 // waves per 16-row tile (1, 2 or 4), 0 = chosen from the tile count.

@@ -218,6 +218,72 @@ size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M);
 rbq_status rbq_gemv(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     const uint16_t *x, uint16_t *y, void *stream);
 
+/*
+ * Dual-scale paths (RaBiT section 4.1: each binary core carries per-channel
+ * scaling vectors on its output and its input side):
+ *   y = sum_k g_k (.) (B_k (h_k (.) x))
+ * with planes B_k as above (group_size must be 0), g_k binary16 [K][out] and
+ * h_k binary16 [K][in].
+ */
+
+/* Largest in_features rbq_encode_dual handles in this build. */
+#define RBQ_DUAL_MAX_IN            16384
+
+/* Bytes of g (K * out * 2) and of h (K * in * 2); 0 for an invalid shape or
+ * group_size != 0. */
+size_t rbq_dual_g_bytes(rbq_shape s);
+size_t rbq_dual_h_bytes(rbq_shape s);
+
+/* Device workspace rbq_encode_dual needs: the fp32 residual (out * in * 4)
+ * plus fp64 vectors and per-workgroup partial sums (about 2 KB per input
+ * column); 0 for an invalid shape. */
+size_t rbq_encode_dual_workspace_bytes(rbq_shape s);
+
+/*
+ * rbq_encode_dual -- residual binarization whose scales come from a residual
+ * SVID (RaBiT section 4.3 and "RaBiT initialization", Tmax = 20 SVID
+ * iterations in "Training configuration"; the calibration-data
+ * preconditioning is left out).  With R_0 = W (fp32), for k = 1..K:
+ *   B_k = (R_{k-1} >= 0)              sign(0) = +1, also for -0.0
+ *   |R_{k-1}| ~ u v^T by 20 alternating least-squares steps from v = 1:
+ *       u = |R| v / (v.v),  then  v = |R|^T u / (u.u)   (fp64)
+ *   c = sqrt(||u|| / ||v||);  g_k = fp16(u / c), h_k = fp16(v c), each
+ *       rounded once to nearest even (zero scales for an all-zero |R|)
+ *   R_k = R_{k-1} - (bit ? 1 : -1) g_k[r] h_k[j]   in fp32
+ *
+ *   W          device fp32 [out][in], finite, 4-byte aligned, read only
+ *   planes     device uint32 [K][out][in/32], 4-byte aligned, written
+ *   g, h       device binary16 [K][out] and [K][in], 2-byte aligned, written
+ *   workspace  device, rbq_encode_dual_workspace_bytes(s) bytes, 256-byte
+ *              aligned, any contents; calls that share one overlap on the
+ *              stream order only
+ *   status_dev device int32 or NULL: RBQ_STATUS_NONFINITE_W is OR-ed in
+ * The sums are fp64 in a fixed order (deterministic on a given device); a
+ * different order changes a stored scale only when its value lies within
+ * ~1e-13 of an fp16 rounding boundary.
+ * Errors: RBQ_ERR_INVALID_ARG (shape, group_size != 0, null pointer,
+ * workspace too small), RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED
+ * (in % 128 != 0 or in > RBQ_DUAL_MAX_IN), RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.
+ * An empty shape enqueues nothing.
+ */
+rbq_status rbq_encode_dual(const float *W, rbq_shape s, uint32_t *planes, uint16_t *g, uint16_t *h,
+                           void *workspace, size_t workspace_bytes, int32_t *status_dev, void *stream);
+
+/*
+ * rbq_gemv_dual -- y = sum_k g_k (.) (B_k (h_k (.) x)) for one token, on the
+ * int8 matrix cores: the K products h_k (.) x (exact in fp32) take the place
+ * of tokens, each quantised to three 8-bit limbs with its own power of two.
+ *   planes  device uint32 [K][out][in/32], 16-byte aligned
+ *   g       device binary16 [K][out], 2-byte aligned
+ *   h       device binary16 [K][in], 16-byte aligned
+ *   x       device fp16 [in], 16-byte aligned;  y device fp16 [out], written
+ * K <= 4 and in % 128 == 0 (else RBQ_ERR_UNSUPPORTED); group_size must be 0
+ * (RBQ_ERR_INVALID_ARG).  out == 0 enqueues nothing; in == 0 writes y = 0.
+ * Errors as rbq_gemm.
+ */
+rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,
+                         const uint16_t *x, uint16_t *y, void *stream);
+
 /* Kernel families rbq_gemm can use; RBQ_PATH_AUTO picks by shape and M. */
 typedef enum rbq_path {
     RBQ_PATH_AUTO = 0,

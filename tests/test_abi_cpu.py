@@ -140,3 +140,48 @@ def test_path_override_roundtrip():
 def test_binding_refuses_host_tensors():
     with pytest.raises(TypeError):
         rbq.encode(torch.zeros(4, 64), 2)
+
+
+def test_dual_sizes_and_argument_errors():
+    L = rbq.lib()
+    s = rbq.shape(64, 256, 2, 0)
+    assert L.rbq_dual_g_bytes(s) == 2 * 64 * 2 and L.rbq_dual_h_bytes(s) == 2 * 256 * 2
+    assert L.rbq_dual_g_bytes(rbq.shape(64, 256, 2, 128)) == 0
+    ws = L.rbq_encode_dual_workspace_bytes(s)
+    assert ws >= 64 * 256 * 4 + 64 * 8 + 256 * 8 and ws % 256 == 0
+    ok = 0x10000
+    g128 = rbq.shape(64, 256, 2, 128)
+    assert L.rbq_encode_dual(ok, g128, ok, ok, ok, ok, ws, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemv_dual(ok, ok, ok, g128, ok, ok, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode_dual(None, s, ok, ok, ok, ok, ws, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode_dual(ok, s, ok, ok, ok, None, ws, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode_dual(ok, s, ok, ok, ok, ok, ws - 1, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_encode_dual(ok, s, ok, ok, ok, ok + 16, ws, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_encode_dual(ok, rbq.shape(64, 96, 2), ok, ok, ok, ok, ws, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    big = rbq.shape(4, rbq_dual_max_in() + 128, 2)
+    assert L.rbq_encode_dual(ok, big, ok, ok, ok, ok, 1 << 40, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_gemv_dual(ok, ok, ok, rbq.shape(64, 256, 5), ok, ok, None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_gemv_dual(ok, ok, ok, rbq.shape(64, 96, 2), ok, ok, None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_gemv_dual(ok, ok, None, s, ok, ok, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemv_dual(ok, ok, ok + 8, s, ok, ok, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemv_dual(ok, ok, ok, s, ok + 8, ok, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemv_dual(ok + 4, ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_gemv_dual(ok, ok, ok, s, ok, ok + 1, None) == rbq.RBQ_ERR_ALIGNMENT
+    # empty shapes enqueue nothing
+    assert L.rbq_encode_dual(None, rbq.shape(0, 256, 2), None, None, None, None, 0, None, None) == rbq.RBQ_OK
+    assert L.rbq_gemv_dual(None, None, None, rbq.shape(0, 256, 2), None, None, None) == rbq.RBQ_OK
+
+
+def rbq_dual_max_in():
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "rbq.h")).read()
+    return int(re.search(r"#define RBQ_DUAL_MAX_IN\s+(\d+)", text).group(1))
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_dual_valid_call_without_device_reports_no_device():
+    L = rbq.lib()
+    s = rbq.shape(64, 256, 2, 0)
+    ok = 0x10000
+    ws = L.rbq_encode_dual_workspace_bytes(s)
+    assert L.rbq_encode_dual(ok, s, ok, ok, ok, ok, ws, None, None) == rbq.RBQ_ERR_NO_DEVICE
+    assert L.rbq_gemv_dual(ok, ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_NO_DEVICE

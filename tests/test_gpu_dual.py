@@ -1,0 +1,173 @@
+"""GPU parity of the dual-scale paths, y = sum_k g_k (.) (B_k (h_k (.) x))
+(RaBiT summary section 4.1; scales from a residual SVID, section 4.3),
+through the C ABI against the fp64 oracle in oracle/dual.py.
+
+Encoder: planes, g and h equal to the oracle's.  Both sum in fp64 but in
+different orders, so a scale whose fp64 value lies within ~1e-13 of an fp16
+rounding boundary could round to the neighbouring fp16 value; where that
+happens the test accepts neighbours only and compares the reconstruction
+from there on.  Layer output: relative L2 error <= 1e-3 and max abs error
+<= 1e-2 * rms(y_ref).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_rbq_encode_amd as rbq
+import workloads
+from oracle import dual
+
+pytestmark = pytest.mark.gpu
+REL_L2 = 1e-3
+MAX_ABS_RMS = 1e-2
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def gpu_encode_dual(W, K):
+    Wt = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).to(dev())
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    p, g, h = rbq.encode_dual(Wt, K, status=status)
+    torch.cuda.synchronize()
+    return (p.cpu().numpy().view(np.uint32), g.cpu().numpy().view(np.uint16),
+            h.cpu().numpy().view(np.uint16), int(status.item()))
+
+
+def recon_error(W, p, g, h):
+    return np.linalg.norm(W.astype(np.float64) - dual.dequant_dual(p, g, h))
+
+
+def assert_dual_encode_matches(W, K, what=""):
+    po, go, ho = dual.encode_dual(W, K)
+    p, g, h, st = gpu_encode_dual(W, K)
+    assert st == 0, f"{what}: status {st}"
+    for k in range(K):
+        dg = np.abs(g[k].astype(np.int32) - go[k].astype(np.int32))
+        dh = np.abs(h[k].astype(np.int32) - ho[k].astype(np.int32))
+        if dg.any() or dh.any():
+            assert dg.max() <= 1 and dh.max() <= 1 and int(dg.sum() + dh.sum()) <= 4, \
+                f"{what}: plane {k} scales differ beyond a boundary case"
+            e, eo = recon_error(W, p, g, h), recon_error(W, po, go, ho)
+            assert abs(e - eo) <= 1e-4 * eo, f"{what}: reconstruction {e} vs {eo}"
+            return
+        assert np.array_equal(p[k], po[k]), f"{what}: plane {k} differs at {np.argwhere(p[k] != po[k])[:5]}"
+
+
+def assert_close(y, yref, what=""):
+    assert np.isfinite(y).all(), what
+    rms = np.sqrt(np.mean(yref ** 2))
+    rel = np.linalg.norm(y - yref) / max(np.linalg.norm(yref), 1e-300)
+    mx = np.abs(y - yref).max() if y.size else 0.0
+    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
+    assert mx <= MAX_ABS_RMS * rms, f"{what}: max-abs {mx:.3e} vs rms {rms:.3e}"
+
+
+def gpu_gemv_dual(p, g, h, x):
+    pt = torch.from_numpy(np.ascontiguousarray(p).view(np.int32)).to(dev())
+    gt = torch.from_numpy(np.ascontiguousarray(g).view(np.float16)).to(dev())
+    ht = torch.from_numpy(np.ascontiguousarray(h).view(np.float16)).to(dev())
+    xt = torch.from_numpy(np.ascontiguousarray(x).reshape(-1).view(np.float16)).to(dev())
+    y = rbq.gemv_dual(pt, gt, ht, xt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# encoder
+# ---------------------------------------------------------------------------
+
+def test_encode_dual_small_workload():
+    wl = workloads.WORKLOADS["small"]
+    assert_dual_encode_matches(workloads.workload_weight(wl, 0), 2, "small")
+
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_encode_dual_llama2_7b(i):
+    wl = workloads.WORKLOADS["llama2_7b"]
+    assert_dual_encode_matches(workloads.workload_weight(wl, i), 2, wl.linears[i].name)
+
+
+@pytest.mark.parametrize("out,inf,K", [(1, 128, 1), (17, 128, 2), (33, 384, 3), (5, 1280, 4),
+                                       (300, 640, 8), (40, 16384, 2), (1031, 4224, 2)])
+def test_encode_dual_ragged_shapes(out, inf, K):
+    W = workloads.gaussian_weight(out, inf, seed=out * 7 + inf + K, outliers=True)
+    assert_dual_encode_matches(W, K, f"{out}x{inf} K={K}")
+
+
+def test_encode_dual_special_values():
+    rng = np.random.default_rng(21)
+    W = (rng.standard_normal((24, 256)) * 0.02).astype(np.float32)
+    W[3] = 0.0                       # a zero row
+    W[5, ::3] = -0.0                 # negative zeros count as +1
+    W[7] *= 1e-30                    # a tiny row
+    assert_dual_encode_matches(W, 3, "special")
+    assert_dual_encode_matches(np.zeros((16, 128), np.float32), 2, "zero matrix")
+
+
+def test_encode_dual_rank1_magnitudes():
+    rng = np.random.default_rng(22)
+    a = rng.uniform(0.5, 2.0, 48).astype(np.float16).astype(np.float32)
+    b = rng.uniform(0.01, 0.1, 512).astype(np.float16).astype(np.float32)
+    W = (np.where(rng.random((48, 512)) < 0.5, -1.0, 1.0) * np.outer(a, b)).astype(np.float32)
+    assert_dual_encode_matches(W, 2, "rank-1 magnitudes")
+
+
+def test_encode_dual_flags_nonfinite_w():
+    W = workloads.gaussian_weight(8, 256, seed=3)
+    W[2, 9] = np.nan
+    _, _, _, st = gpu_encode_dual(W, 1)
+    assert st & rbq.RBQ_STATUS_NONFINITE_W
+
+
+def test_encode_dual_deterministic():
+    W = workloads.gaussian_weight(512, 1024, seed=5, outliers=True)
+    a = gpu_encode_dual(W, 2)
+    b = gpu_encode_dual(W, 2)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+# ---------------------------------------------------------------------------
+# layer output
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+def test_gemv_dual_llama2_7b(i):
+    wl = workloads.WORKLOADS["llama2_7b"]
+    W = workloads.workload_weight(wl, i)
+    p, g, h = dual.encode_dual(W, 2)
+    x = workloads.workload_activations(wl, W.shape[1], 1)
+    assert_close(gpu_gemv_dual(p, g, h, x), dual.gemm_dual(p, g, h, x)[0], wl.linears[i].name)
+
+
+@pytest.mark.parametrize("out,inf,K", [(1, 128, 1), (15, 256, 2), (17, 640, 3), (257, 4224, 4),
+                                       (1000, 128, 2), (64, 16384, 2), (33, 32768, 1)])
+def test_gemv_dual_random_scales(out, inf, K):
+    """Random planes, signed g, h of mixed magnitude and sign."""
+    rng = np.random.default_rng(out + inf + K)
+    p = rng.integers(0, 2 ** 32, (K, out, inf // 32), dtype=np.uint64).astype(np.uint32)
+    g = (rng.standard_normal((K, out)) * 0.05).astype(np.float16).view(np.uint16)
+    h = (rng.standard_normal((K, inf)) * np.exp(rng.uniform(-3, 3, (K, inf)))).astype(np.float16).view(np.uint16)
+    x = rng.standard_normal((1, inf)).astype(np.float16)
+    assert_close(gpu_gemv_dual(p, g, h, x), dual.gemm_dual(p, g, h, x)[0], f"{out}x{inf} K={K}")
+
+
+def test_gemv_dual_with_unit_input_scales_is_the_row_scale_layer():
+    """h = 1: the dual layer is the per-row-scale layer with a_k = g_k."""
+    wl = workloads.WORKLOADS["small"]
+    W = workloads.workload_weight(wl, 0)
+    p, s, _ = __import__("oracle").encode(W, 2)
+    h = np.full((2, W.shape[1]), np.float16(1.0)).view(np.uint16)
+    x = workloads.workload_activations(wl, W.shape[1], 1)
+    y_dual = gpu_gemv_dual(p, s[:, :, 0], h, x)
+    assert_close(y_dual, __import__("oracle").gemm(p, s, x)[0], "h = 1")
+
+
+def test_gemv_dual_zero_input_columns_and_empty():
+    y = torch.full((8,), 7.0, dtype=torch.float16, device=dev())
+    L = rbq.lib()
+    st = L.rbq_gemv_dual(None, None, None, rbq.shape(8, 0, 2), None, y.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert st == rbq.RBQ_OK and not y.any()
+    assert L.rbq_gemv_dual(None, None, None, rbq.shape(0, 128, 2), None, None, None) == rbq.RBQ_OK
