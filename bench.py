@@ -459,11 +459,19 @@ def bench_decode(args):
         e_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)] * 10, 3) / 10
         r_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)] * 10, 3) / 10
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * s.numel()
+        # dual-scale encoder (residual SVID, 20 alternating steps per plane)
+        shp = rbq.shape(W.shape[0], W.shape[1], K, 0)
+        wsd = torch.empty(rbq.encode_dual_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+        pd = torch.empty_like(p)
+        gd = torch.empty((K, W.shape[0]), dtype=torch.float16, device=dev)
+        hd = torch.empty((K, W.shape[1]), dtype=torch.float16, device=dev)
+        d_ms = graph_ms(torch, dev, [lambda: rbq.encode_dual(W, K, workspace=wsd, planes=pd, g=gd, h=hd)], 3)
         prep[key] = {"encode_us": round(e_ms * 1e3, 1),
                      "encode_GBps": round((wb + pb + sb) / (e_ms * 1e-3) / 1e9, 1),
                      "refit_us": round(r_ms * 1e3, 1),
-                     "refit_GBps": round((wb + pb + 2 * sb) / (r_ms * 1e-3) / 1e9, 1)}
-        del pe, se, sr
+                     "refit_GBps": round((wb + pb + 2 * sb) / (r_ms * 1e-3) / 1e9, 1),
+                     "encode_dual_us": round(d_ms * 1e3, 1)}
+        del pe, se, sr, wsd, pd, gd, hd
     del Ws, ref_scales
 
     # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
@@ -573,6 +581,26 @@ def bench_decode(args):
                            "bytes": per_call[i], "mean_us": round(mean_us[i], 3),
                            "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1)}
 
+    # ---- dual-scale layer y = sum_k g_k (B_k (h_k x)) on the same planes (the
+    # row scales serve as g; h is one input-scale vector per plane and width)
+    dual_shape = {}
+    hvec = {}
+    for i, (name, _) in enumerate(groups):
+        n_in = g_in[i]
+        if n_in not in hvec:
+            hvec[n_in] = torch.ones((K, n_in), dtype=torch.float16, device=dev)
+        fns = []
+        for layer in layers:
+            p, s = layer[i]
+            fns.append(lambda pp=p.data_ptr(), sp=s.data_ptr(), hp=hvec[n_in].data_ptr(), sh=shapes[i],
+                       xp=xs[n_in].data_ptr(), yp=ys[i].data_ptr():
+                       rbq.check(L.rbq_gemv_dual(pp, sp, hp, sh, xp, yp,
+                                                 torch.cuda.current_stream(dev).cuda_stream), "rbq_gemv_dual"))
+        us = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1) * 4)
+        nb = per_call[i] + 2 * K * n_in
+        dual_shape[name] = {"shape": f"{shapes[i].out_features}x{n_in}", "bytes": nb,
+                            "mean_us": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+
     # ---- CPU oracle baseline on a bounded sample (layer 0, one token)
     cpu = None
     if args.cpu_seconds > 0:
@@ -630,6 +658,7 @@ def bench_decode(args):
         "refit": {"linears": len(wl.linears), "ms": round(ref_ms, 4),
                   "GBps": round(ref_bytes / (ref_ms * 1e-3) / 1e9, 1)},
         "encode_refit_per_shape": prep,
+        "gemv_dual_per_shape": dual_shape,
         "decode_layer_chain": layer_chain,
     }
     print(json.dumps(line), flush=True)
