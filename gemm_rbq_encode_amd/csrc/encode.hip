@@ -44,29 +44,6 @@ constexpr uint32_t UNDECIDED = 0xFFFFFFFFu;
 // compiler has no builtin for it, so its LLVM intrinsic is named directly.
 extern "C" __device__ int rbq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
-// Whole-wave fp64 sum (DPP row shifts and broadcasts, then lane 63), the
-// same value in every lane.  Lanes a DPP move does not reach add +0.
-template <int CTRL, int RMASK>
-__device__ __forceinline__ double dpp_f64(double x) {
-    const uint64_t b = (uint64_t)__double_as_longlong(x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, RMASK, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, RMASK, 0xF, false);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
-    v += dpp_f64<RBQ_DPP_ROW_SHR(1), 0xF>(v);
-    v += dpp_f64<RBQ_DPP_ROW_SHR(2), 0xF>(v);
-    v += dpp_f64<RBQ_DPP_ROW_SHR(4), 0xF>(v);
-    v += dpp_f64<RBQ_DPP_ROW_SHR(8), 0xF>(v);
-    v += dpp_f64<RBQ_DPP_ROW_BCAST15, 0xA>(v);
-    v += dpp_f64<RBQ_DPP_ROW_BCAST31, 0xC>(v);
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global stores.
 __device__ __forceinline__ void lds_barrier() {

@@ -13,8 +13,8 @@
 //       binary16 values is exact in fp32, so this rounds once)
 //
 // Kernels per path: `svid_pass` (u for every row and per-workgroup partial
-// sums of |R|^T u and of u.u), `svid_reduce` (v from the partials, added in
-// workgroup order, and per-block partial sums of v.v), 20 times; then
+// sums of |R|^T u and of u.u), `svid_reduce` (v from the partials, one
+// workgroup per 64 columns), 20 times; then
 // `svid_finish` (balance and round) and `svid_update` (signs into plane
 // words, next residual).  All sums are fp64 in a fixed order, so the result
 // is deterministic for a given device; it differs from other summation
@@ -22,8 +22,9 @@
 // only for a value within ~1e-13 of an fp16 rounding boundary.
 //
 // Workspace (rbq_encode_dual_workspace_bytes): R fp32 [out][in], u [out],
-// v [in], column partials [SV_G][in], u.u partials [SV_G], v.v partials
-// [ceil(in / 256)], all fp64 but R, each at a 256-byte boundary.
+// v [in], column partials [in/64][SV_G][64] (each workgroup writes 64
+// consecutive columns per wave store) and u.u partials [SV_G], all fp64 but
+// R, each at a 256-byte boundary.
 #include "rbq.h"
 #include "rbq_device.h"
 #include "rbq_kernels.h"
@@ -40,7 +41,7 @@ constexpr int SV_RB = 256;                       // reduce / finish / update blo
 
 struct Ws {
     float *R;
-    double *u, *v, *vpart, *upart, *vvpart;
+    double *u, *v, *vpart, *upart;
 };
 
 __host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -52,11 +53,12 @@ inline Ws carve(void *base, int out, int in) {
     w.u = (double *)p;         p += align256((size_t)out * 8);
     w.v = (double *)p;         p += align256((size_t)in * 8);
     w.vpart = (double *)p;     p += align256((size_t)SV_G * in * 8);
-    w.upart = (double *)p;     p += align256((size_t)SV_G * 8);
-    w.vvpart = (double *)p;
+    w.upart = (double *)p;
     return w;
 }
 
+// Sum over the wave, the same value in every lane (each butterfly step adds
+// the same two values in both lanes of a pair).
 __device__ __forceinline__ double wave_sum_f64_shfl(double v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
@@ -64,133 +66,175 @@ __device__ __forceinline__ double wave_sum_f64_shfl(double v) {
     return v;
 }
 
-// v = 1 (and v.v = in) before the first pass.
-__global__ __launch_bounds__(SV_RB) void svid_init(double *__restrict__ v, double *__restrict__ vvpart, int in,
-                                                    int nvb) {
+// Sum over a workgroup of NW waves in wave order, returned to every thread.
+template <int NW>
+__device__ __forceinline__ double block_sum_f64(double v, double *red) {
+    v = wave_sum_f64_shfl(v);
+    if ((threadIdx.x & (RBQ_WAVE - 1)) == 0)
+        red[threadIdx.x / RBQ_WAVE] = v;
+    __syncthreads();
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        s += red[w];
+    return s;
+}
+
+// v = 1 before the first pass.
+__global__ __launch_bounds__(SV_RB) void svid_init(double *__restrict__ v, int in) {
     const int j = blockIdx.x * SV_RB + threadIdx.x;
     if (j < in)
         v[j] = 1.0;
-    if (j < nvb)
-        vvpart[j] = (j == 0) ? (double)in : 0.0;
 }
 
-// u_r = sum_j |R_rj| v_j / (v.v) for rows r = b, b + SV_G, ...; workgroup b
-// also sums |R_rj| u_r over its rows per column, and u_r^2.
-template <int CPT>
+// u_r = sum_j |R_rj| v_j / (v.v) for the rows of workgroup b, RPI at a
+// time (rows b RPI .. b RPI + RPI - 1, then SV_G RPI further on): their
+// loads are in flight together and one barrier serves all of them.
+// Workgroup b also sums |R_rj| u_r over its rows per column, and u_r^2, in
+// row order.
+template <int CPT, int RPI>
 __global__ __launch_bounds__(SV_THREADS) void svid_pass(const float *__restrict__ R, int out, int in,
-                                                        const double *__restrict__ v,
-                                                        const double *__restrict__ vvpart, int nvb,
-                                                        double *__restrict__ u, double *__restrict__ vpart,
-                                                        double *__restrict__ upart) {
-    __shared__ double red[2][SV_WAVES];
+                                                        const double *__restrict__ v, double *__restrict__ u,
+                                                        double *__restrict__ vpart, double *__restrict__ upart) {
+    __shared__ double red[2][RPI][SV_WAVES];
+    __shared__ double red_vv[SV_WAVES];
+    __shared__ double vsh[CPT * SV_THREADS];    // v, read once per row from LDS
     const int t = threadIdx.x;
     const int lane = t & (RBQ_WAVE - 1), wave = t / RBQ_WAVE;
+    double acc[CPT];
     double vv = 0.0;
-    for (int i = 0; i < nvb; ++i)
-        vv += vvpart[i];
-    double vj[CPT], acc[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int j = t + SV_THREADS * i;
-        vj[i] = (j < in) ? v[j] : 0.0;
+        const double vj = (j < in) ? v[j] : 0.0;
+        vsh[j] = vj;
+        vv += vj * vj;
         acc[i] = 0.0;
     }
+    vv = block_sum_f64<SV_WAVES>(vv, red_vv);    // also makes vsh visible
     double uu = 0.0;
-    float a[CPT], an[CPT];
-    auto load = [&](float(&dst)[CPT], int r) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int j = t + SV_THREADS * i;
-            dst[i] = (j < in) ? __builtin_fabsf(R[(size_t)r * in + j]) : 0.0f;
-        }
-    };
     int phase = 0;
-    if (blockIdx.x < out)
-        load(a, blockIdx.x);
-    for (int r = blockIdx.x; r < out; r += SV_G) {
-        const bool more = r + SV_G < out;
-        if (more)
-            load(an, r + SV_G);
-        double s = 0.0;
+    for (int r0 = blockIdx.x * RPI; r0 < out; r0 += SV_G * RPI) {
+        float a[RPI][CPT];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            s += (double)a[i] * vj[i];
-        s = wave_sum_f64_shfl(s);
+        for (int q = 0; q < RPI; ++q) {
+            // a uniform row address plus 32-bit column offsets: no 64-bit
+            // address per load kept in registers
+            const float *rowp = R + (size_t)min(r0 + q, out - 1) * in;
+            const bool live = r0 + q < out;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const unsigned j = (unsigned)t + SV_THREADS * i;
+                const float x = rowp[min(j, (unsigned)in - 1u)];
+                a[q][i] = (live && j < (unsigned)in) ? __builtin_fabsf(x) : 0.0f;
+            }
+        }
         const int b = phase & 1;
         ++phase;
-        if (lane == 0)
-            red[b][wave] = s;
-        __syncthreads();
-        double S = 0.0;
 #pragma unroll
-        for (int w = 0; w < SV_WAVES; ++w)
-            S += red[b][w];
-        const double ur = (vv > 0.0) ? S / vv : 0.0;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            acc[i] += (double)a[i] * ur;
-        if (t == 0) {
-            u[r] = ur;
-            uu += ur * ur;
-        }
-        if (more) {
+        for (int q = 0; q < RPI; ++q) {
+            double s = 0.0;
 #pragma unroll
             for (int i = 0; i < CPT; ++i)
-                a[i] = an[i];
+                s += (double)a[q][i] * vsh[t + SV_THREADS * i];
+            s = wave_sum_f64_dpp(s);
+            if (lane == 0)
+                red[b][q][wave] = s;
+        }
+        __syncthreads();
+        // row q's sum over the 16 waves: lane 16q' + w reads wave w's share
+        // of row qq + q', each row of 16 lanes adds them in wave order, and
+        // lane 16q' + 15 holds the total (the same in every wave)
+        double S[RPI];
+#pragma unroll
+        for (int qq = 0; qq < RPI; qq += 4) {
+            const int q = qq + (lane >> 4);
+            const double p = (q < RPI) ? red[b][q < RPI ? q : 0][lane & 15] : 0.0;
+            const double rs = row16_sum_f64_dpp(p);
+#pragma unroll
+            for (int d = 0; d < 4 && qq + d < RPI; ++d)
+                S[qq + d] = __longlong_as_double((long long)(
+                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                         (int)(uint32_t)((uint64_t)__double_as_longlong(rs) >> 32), 16 * d + 15) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(rs), 16 * d + 15)));
+        }
+        // keep the loaded values as fp32 across the barrier (their fp64
+        // conversions are not shared between the two sums: twice the
+        // registers)
+#pragma unroll
+        for (int q = 0; q < RPI; ++q)
+#pragma unroll
+            for (int i = 0; i < CPT; ++i)
+                asm volatile("" : "+v"(a[q][i]));
+#pragma unroll
+        for (int q = 0; q < RPI; ++q) {
+            const double ur = (vv > 0.0) ? S[q] / vv : 0.0;   // rows past the end: 0
+#pragma unroll
+            for (int i = 0; i < CPT; ++i)
+                acc[i] += (double)a[q][i] * ur;
+            if (t == 0 && r0 + q < out) {
+                u[r0 + q] = ur;
+                uu += ur * ur;
+            }
         }
     }
+    // partials [in/64][SV_G][64]: a wave stores 64 consecutive columns
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int j = t + SV_THREADS * i;
         if (j < in)
-            vpart[(size_t)blockIdx.x * in + j] = acc[i];
+            vpart[((size_t)(j >> 6) * SV_G + blockIdx.x) * 64 + (j & 63)] = acc[i];
     }
     if (t == 0)
         upart[blockIdx.x] = uu;
 }
 
-// v_j = (sum over workgroups of the partials, in order) / (u.u); per block
-// of columns, the sum of v_j^2.
+// v_j = (sum over workgroups of the partials, in workgroup order) / (u.u):
+// one workgroup per 64 columns, wave w adding workgroups [64w, 64w + 64)
+// for lane j, then wave 0 adding the four waves' sums in order.
 __global__ __launch_bounds__(SV_RB) void svid_reduce(const double *__restrict__ vpart,
                                                       const double *__restrict__ upart, int groups, int in,
-                                                      double *__restrict__ v, double *__restrict__ vvpart) {
-    __shared__ double red[SV_RB / RBQ_WAVE];
-    const int j = blockIdx.x * SV_RB + threadIdx.x;
-    double uu = 0.0;
-    for (int b = 0; b < groups; ++b)
-        uu += upart[b];
-    double vj = 0.0;
-    if (j < in) {
-        double s = 0.0;
-        for (int b = 0; b < groups; ++b)
-            s += vpart[(size_t)b * in + j];
-        vj = (uu > 0.0) ? s / uu : 0.0;
-        v[j] = vj;
-    }
-    const double w = wave_sum_f64_shfl(vj * vj);
-    if ((threadIdx.x & (RBQ_WAVE - 1)) == 0)
-        red[threadIdx.x / RBQ_WAVE] = w;
+                                                      double *__restrict__ v) {
+    static_assert(SV_G == 4 * RBQ_WAVE && SV_RB == 4 * RBQ_WAVE, "four waves of 64 workgroups");
+    __shared__ double part[4][RBQ_WAVE];
+    const int lane = threadIdx.x & (RBQ_WAVE - 1), wave = threadIdx.x / RBQ_WAVE;
+    const double *p = vpart + (size_t)blockIdx.x * SV_G * 64 + lane;
+    double s = 0.0;
+    const int b0 = wave * RBQ_WAVE;
+    const int nb = min(RBQ_WAVE, groups - b0);          // may be <= 0
+#pragma unroll 16
+    for (int b = 0; b < nb; ++b)
+        s += p[(size_t)(b0 + b) * 64];
+    part[wave][lane] = s;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double s = 0.0;
+    if (wave == 0) {
+        // u.u: lane l adds workgroups l, l + 64, l + 128, l + 192, then the wave
+        double uu = 0.0;
 #pragma unroll
-        for (int i = 0; i < SV_RB / RBQ_WAVE; ++i)
-            s += red[i];
-        vvpart[blockIdx.x] = s;
+        for (int m = 0; m < 4; ++m) {
+            const int b = lane + RBQ_WAVE * m;
+            uu += (b < groups) ? upart[b] : 0.0;
+        }
+        uu = wave_sum_f64_shfl(uu);
+        const double t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        const int j = blockIdx.x * 64 + lane;
+        if (j < in)
+            v[j] = (uu > 0.0) ? t / uu : 0.0;
     }
 }
 
 // Balanced scales, one rounding each: g = fp16(u / c), h = fp16(v c),
 // c = sqrt(||u|| / ||v||); zero when either vector is zero.
 __global__ __launch_bounds__(SV_RB) void svid_finish(const double *__restrict__ u, const double *__restrict__ v,
-                                                      const double *__restrict__ upart, int groups,
-                                                      const double *__restrict__ vvpart, int nvb, int out,
+                                                      const double *__restrict__ upart, int groups, int out,
                                                       int in, uint16_t *__restrict__ g, uint16_t *__restrict__ h) {
-    double uu = 0.0, vv = 0.0;
-    for (int b = 0; b < groups; ++b)
-        uu += upart[b];
-    for (int b = 0; b < nvb; ++b)
-        vv += vvpart[b];
+    __shared__ double red_u[SV_RB / RBQ_WAVE], red_v[SV_RB / RBQ_WAVE];
+    const double uu = block_sum_f64<SV_RB / RBQ_WAVE>(
+        (int)threadIdx.x < groups ? upart[threadIdx.x] : 0.0, red_u);
+    double vs = 0.0;
+    for (int j = threadIdx.x; j < in; j += SV_RB)
+        vs += v[j] * v[j];
+    const double vv = block_sum_f64<SV_RB / RBQ_WAVE>(vs, red_v);
     const double nu = sqrt(uu), nv = sqrt(vv);
     const bool zero = !(nu > 0.0) || !(nv > 0.0);
     const double c = zero ? 1.0 : sqrt(nu / nv);
@@ -234,9 +278,8 @@ __global__ __launch_bounds__(SV_RB) void svid_update(const float *__restrict__ R
 size_t encode_dual_workspace_bytes(int out, int in) {
     if (out <= 0 || in <= 0)
         return 0;
-    const int nvb = (in + SV_RB - 1) / SV_RB;
     return align256((size_t)out * in * 4) + align256((size_t)out * 8) + align256((size_t)in * 8) +
-           align256((size_t)SV_G * in * 8) + align256((size_t)SV_G * 8) + align256((size_t)nvb * 8);
+           align256((size_t)SV_G * in * 8) + align256((size_t)SV_G * 8);
 }
 
 hipError_t launch_encode_dual(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *g, uint16_t *h,
@@ -245,27 +288,29 @@ hipError_t launch_encode_dual(const float *W, int out, int in, int K, uint32_t *
         return hipErrorInvalidValue;
     const Ws w = carve(workspace, out, in);
     const int nvb = (in + SV_RB - 1) / SV_RB;
-    const int groups = out < SV_G ? out : SV_G;
+    // columns per thread (4, 8, 12 or 16) and rows per barrier (8, 4, 3, 2)
+    const int cpt = (in + SV_THREADS - 1) / SV_THREADS;
+    const int rpi = cpt <= 4 ? 8 : cpt <= 8 ? 4 : cpt <= 12 ? 3 : 2;
+    auto pass = cpt <= 4 ? svid_pass<4, 8> : cpt <= 8 ? svid_pass<8, 4> : cpt <= 12 ? svid_pass<12, 3>
+                                                                              : svid_pass<16, 2>;
+    const int row_blocks = (out + rpi - 1) / rpi;
+    const int groups = row_blocks < SV_G ? row_blocks : SV_G;
     const size_t words = (size_t)out * (in / 32);
     const size_t total = (size_t)out * in;
     const unsigned upd_blocks = (unsigned)((total + SV_RB - 1) / SV_RB);
     const unsigned fin_blocks = (unsigned)(((out > in ? out : in) + SV_RB - 1) / SV_RB);
     for (int k = 0; k < K; ++k) {
         const float *Rk = (k == 0) ? W : w.R;
-        hipLaunchKernelGGL(svid_init, dim3(nvb), dim3(SV_RB), 0, st, w.v, w.vvpart, in, nvb);
+        hipLaunchKernelGGL(svid_init, dim3(nvb), dim3(SV_RB), 0, st, w.v, in);
         for (int it = 0; it < SVID_ITERS; ++it) {
-            // columns per thread: 4, 8, 12 or 16
-            const int cpt = (in + SV_THREADS - 1) / SV_THREADS;
-            auto pass = cpt <= 4 ? svid_pass<4> : cpt <= 8 ? svid_pass<8> : cpt <= 12 ? svid_pass<12> : svid_pass<16>;
-            hipLaunchKernelGGL(pass, dim3(groups), dim3(SV_THREADS), 0, st, Rk, out, in,
-                               (const double *)w.v, (const double *)w.vvpart, nvb, w.u, w.vpart, w.upart);
-            hipLaunchKernelGGL(svid_reduce, dim3(nvb), dim3(SV_RB), 0, st, (const double *)w.vpart,
-                               (const double *)w.upart, groups, in, w.v, w.vvpart);
+            hipLaunchKernelGGL(pass, dim3(groups), dim3(SV_THREADS), 0, st, Rk, out, in, (const double *)w.v,
+                               w.u, w.vpart, w.upart);
+            hipLaunchKernelGGL(svid_reduce, dim3(in / 64), dim3(SV_RB), 0, st, (const double *)w.vpart,
+                               (const double *)w.upart, groups, in, w.v);
         }
         uint16_t *gk = g + (size_t)k * out, *hk = h + (size_t)k * in;
         hipLaunchKernelGGL(svid_finish, dim3(fin_blocks), dim3(SV_RB), 0, st, (const double *)w.u,
-                           (const double *)w.v, (const double *)w.upart, groups, (const double *)w.vvpart, nvb,
-                           out, in, gk, hk);
+                           (const double *)w.v, (const double *)w.upart, groups, out, in, gk, hk);
         uint32_t *pk = planes + (size_t)k * words;
         if (k + 1 < K)
             hipLaunchKernelGGL(svid_update<false>, dim3(upd_blocks), dim3(SV_RB), 0, st, Rk, w.R, out, in,

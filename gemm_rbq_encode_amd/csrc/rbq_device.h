@@ -108,6 +108,39 @@ __device__ __forceinline__ int row_shl_i32(int v) {
     return __builtin_amdgcn_update_dpp(0, v, RBQ_DPP_ROW_SHL(N), 0xF, 0xF, false);
 }
 
+// Whole-wave fp64 sum (DPP row shifts and broadcasts, then lane 63), the
+// same value in every lane.  Lanes a DPP move does not reach add +0.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, RMASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, RMASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+    v += dpp_f64<RBQ_DPP_ROW_SHR(1), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(2), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(4), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(8), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_BCAST15, 0xA>(v);
+    v += dpp_f64<RBQ_DPP_ROW_BCAST31, 0xC>(v);
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum of each row of 16 lanes, in lane 15 of that row (DPP row shifts; the
+// same order in every row).
+__device__ __forceinline__ double row16_sum_f64_dpp(double v) {
+    v += dpp_f64<RBQ_DPP_ROW_SHR(1), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(2), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(4), 0xF>(v);
+    v += dpp_f64<RBQ_DPP_ROW_SHR(8), 0xF>(v);
+    return v;
+}
+
 // Whole-wave sum of an int, returned to every lane (DPP row shifts, row
 // broadcasts, then lane 63).
 __device__ __forceinline__ int wave_sum_i32(int v) {
