@@ -332,7 +332,18 @@ rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16
         hipError_t e = rbq::launch_fill_zero_u16(y, s.out_features, hs);
         return e == hipSuccess ? RBQ_OK : hip_fail(e);
     }
-    if (!rbq::dual_supports(s.in_features, s.num_planes))
+    // the flat kernel on tall layers of up to 8192 columns, else the decode
+    // kernel; rbq_set_path can force either of the two.  (Measured, K = 2:
+    // 22016 x 4096 10.7 us flat against 14.9 decode; 4096 x 11008 10.5 flat
+    // against 8.4 decode, where the flat kernel's image waves quantise two
+    // copies of three half-words per thread.)
+    rbq_path path = (rbq_path)g_forced_path.load();
+    if (path == RBQ_PATH_AUTO)
+        path = rbq::flat_dual_preferred(s.out_features, s.in_features, s.num_planes) && s.in_features <= 8192
+                   ? RBQ_PATH_FLAT
+                   : RBQ_PATH_DECODE;
+    if (path == RBQ_PATH_FLAT ? !rbq::flat_dual_supports(s.out_features, s.in_features, s.num_planes)
+                              : (path != RBQ_PATH_DECODE || !rbq::dual_supports(s.in_features, s.num_planes)))
         return RBQ_ERR_UNSUPPORTED;
     if (planes == nullptr || g == nullptr || h == nullptr || x == nullptr)
         return RBQ_ERR_INVALID_ARG;
@@ -340,7 +351,11 @@ rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16
         return RBQ_ERR_ALIGNMENT;
     if ((st = device_present()) != RBQ_OK)
         return st;
-    hipError_t e = rbq::launch_gemv_dual(planes, g, h, s.out_features, s.in_features, s.num_planes, x, y, hs);
+    hipError_t e = path == RBQ_PATH_FLAT
+                       ? rbq::launch_gemv_dual_flat(planes, g, h, s.out_features, s.in_features, s.num_planes, x,
+                                                    y, hs)
+                       : rbq::launch_gemv_dual(planes, g, h, s.out_features, s.in_features, s.num_planes, x, y,
+                                               hs);
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 

@@ -91,10 +91,15 @@ __device__ __forceinline__ void lds_wait_count(int *counter, int target) {
     asm volatile("" ::: "memory");
 }
 
-template <int K, int MT, int XU, int RING, bool SILU>
+// DUAL: one token x and per-plane input scales H [K][in] (row scales in
+// `scales`): y = sum_k a_k (.) (B_k (h_k (.) x)).  The K products h_k (.) x,
+// exact in fp32, take the place of the tokens (MT = K, M = K), each with its
+// own power of two, and plane k keeps only its sums against copy k.
+template <int K, int MT, int XU, int RING, bool SILU, bool DUAL = false>
 __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     const uint32_t *__restrict__ planes, const uint16_t *__restrict__ scales, int out, int in,
-    const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y) {
+    const uint16_t *__restrict__ X, int M, uint16_t *__restrict__ Y, const uint16_t *__restrict__ Hs = nullptr) {
+    static_assert(!DUAL || (MT == K && !SILU), "dual scales: one activation copy per plane");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ uint32_t wmax[MT][FL_PREP];
     __shared__ float wsum[MT][FL_PREP];
@@ -168,17 +173,27 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         // one and are quantised with the scale 0 (limbs 0).
         const int nh = words * 2;                         // half-words of the row
         const int hpad = nchunks * CHUNK_WORDS * 2;       // with the padded words
-        v4u xw[MT][XU][2];
+        v4u xw[MT][XU][2];            // DUAL: the h_k of this thread's columns
+        v4u x1[DUAL ? XU : 1][2];     // DUAL: x
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int mc = min(m, mt - 1);
-            const uint16_t *xrow = X + (size_t)(m0 + mc) * in;
+            const uint16_t *xrow = DUAL ? Hs + (size_t)m * in : X + (size_t)(m0 + mc) * in;
 #pragma unroll
             for (int j = 0; j < XU; ++j) {
-                const int H = min(tid + j * FL_PREP_THREADS, nh - 1);
-                const v4u *xp = reinterpret_cast<const v4u *>(xrow + 16 * H);
+                const int Hh = min(tid + j * FL_PREP_THREADS, nh - 1);
+                const v4u *xp = reinterpret_cast<const v4u *>(xrow + 16 * Hh);
                 xw[m][j][0] = xp[0];
                 xw[m][j][1] = xp[1];
+            }
+        }
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int j = 0; j < XU; ++j) {
+                const int Hh = min(tid + j * FL_PREP_THREADS, nh - 1);
+                const v4u *xp = reinterpret_cast<const v4u *>(X + 16 * Hh);
+                x1[j][0] = xp[0];
+                x1[j][1] = xp[1];
             }
         }
         entry();
@@ -187,16 +202,33 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         // compare like magnitudes; clamped repeats only repeat real values)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            v2u16 mx2 = (v2u16){0, 0};
+            uint32_t mloc;
+            if constexpr (DUAL) {
+                // max |x h_k| in fp32 (non-negative floats order as integers)
+                mloc = 0;
 #pragma unroll
-            for (int j = 0; j < XU; ++j)
+                for (int j = 0; j < XU; ++j)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        mx2 = __builtin_elementwise_max(
-                            mx2, __builtin_bit_cast(v2u16, xw[m][j][h][c] & 0x7FFF7FFFu));
-            const uint32_t mx = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+                        for (int c = 0; c < 8; ++c) {
+                            const float p = h2f((uint16_t)(x1[j][h][c >> 1] >> (16 * (c & 1)))) *
+                                            h2f((uint16_t)(xw[m][j][h][c >> 1] >> (16 * (c & 1))));
+                            mloc = max(mloc, __builtin_bit_cast(uint32_t, p) & 0x7FFFFFFFu);
+                        }
+            } else {
+                v2u16 mx2 = (v2u16){0, 0};
+#pragma unroll
+                for (int j = 0; j < XU; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            mx2 = __builtin_elementwise_max(
+                                mx2, __builtin_bit_cast(v2u16, xw[m][j][h][c] & 0x7FFF7FFFu));
+                mloc = max((uint32_t)mx2.x, (uint32_t)mx2.y);
+            }
+            const uint32_t mx = wave_max_u32_dpp(mloc);
             if (lane == 0)
                 wmax[m][wave] = mx;
         }
@@ -212,8 +244,12 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
 #pragma unroll
             for (int v = 0; v < FL_PREP; ++v)
                 mx = max(mx, wmax[m][v]);
-            const int e = (int)(mx >> 10);
-            sh[m] = 22 - ((e == 0 ? 1 : e) - 14);
+            if constexpr (DUAL) {   // fp32 maximum < 2^(e - 126); a non-zero product is >= 2^-48
+                sh[m] = mx == 0 ? 0 : 148 - (int)(mx >> 23);
+            } else {
+                const int e = (int)(mx >> 10);
+                sh[m] = 22 - ((e == 0 ? 1 : e) - 14);
+            }
         }
         // Image entry (word w, bit s): the four columns 32w + 8kk + s, kk =
         // 0..3, one byte each, at [chunk w/16][s][lane group (w/4)%4][column
@@ -236,17 +272,34 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                 for (int m = 0; m < MT; ++m) {
                     if (m < mt) {
                         const float scale = live ? __builtin_ldexpf(1.0f, sh[m]) : 0.0f;
+                        // DUAL: h_k read again (from L2) rather than kept in
+                        // registers since the maximum
+                        v4u hv[2];
+                        if constexpr (DUAL) {
+                            const v4u *hp = reinterpret_cast<const v4u *>(Hs + (size_t)m * in + 16 * min(H, nh - 1));
+                            hv[0] = hp[0];
+                            hv[1] = hp[1];
+                        } else {
+                            hv[0] = xw[m][j][0];
+                            hv[1] = xw[m][j][1];
+                        }
 #pragma unroll
                         for (int s = 0; s < 8; ++s) {
                             // columns 32w + 16e + s (byte 2e) and + 8 (byte 2e + 1)
-                            const uint32_t u0 = xw[m][j][0][s >> 1], u1 = xw[m][j][1][s >> 1];
+                            const uint32_t u0 = hv[0][s >> 1], u1 = hv[1][s >> 1];
                             const uint16_t h0 = (s & 1) ? (uint16_t)(u0 >> 16) : (uint16_t)u0;
                             const uint16_t h1 = (s & 1) ? (uint16_t)(u1 >> 16) : (uint16_t)u1;
+                            float f0 = h2f(h0), f1 = h2f(h1);
+                            if constexpr (DUAL) {   // x_j h_kj, exact in fp32
+                                const uint32_t w0 = x1[j][0][s >> 1], w1 = x1[j][1][s >> 1];
+                                f0 = h2f((s & 1) ? (uint16_t)(w0 >> 16) : (uint16_t)w0) * f0;
+                                f1 = h2f((s & 1) ? (uint16_t)(w1 >> 16) : (uint16_t)w1) * f1;
+                            }
                             const uint32_t v0 =
-                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) -
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(f0, scale, 12582912.0f)) -
                                 0x4ABF7F80u;
                             const uint32_t v1 =
-                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) -
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(f1, scale, 12582912.0f)) -
                                 0x4ABF7F80u;
                             psum[m] += (int)(v0 + v1) - 2 * 0x808080;
                             // [v0.b0 v1.b0 v0.b1 v1.b1], [v0.b2 v1.b2 0 0]
@@ -419,7 +472,25 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         return __builtin_ldexpf(y, -shs[m]);
     };
     const bool rowok = tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out;
-    if constexpr (!SILU) {
+    if constexpr (DUAL) {
+        // plane k against copy k, each copy with its own power of two
+        if (rowok) {
+            const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+            float y = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float sx = 0.0f;
+#pragma unroll
+                for (int v = 0; v < FL_PREP; ++v)
+                    sx += wsum[k][v];
+                const int *rp = red + ((tl * K + k) * NC + NLIMB * k) * TILE_ROWS + i;
+                const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
+                                 65536.0 * (double)rp[2 * TILE_ROWS];
+                y += __builtin_ldexpf(h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx), -shs[k]);
+            }
+            Y[t0 * TILE_ROWS + tid] = f2h(y);
+        }
+    } else if constexpr (!SILU) {
         if (rowok) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -514,7 +585,45 @@ hipError_t launch_km(const uint32_t *planes, const uint16_t *scales, int out, in
     return hipErrorInvalidValue;
 }
 
+template <int K, int XU>
+hipError_t launch_dual_x(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                         const uint16_t *x, uint16_t *y, hipStream_t st) {
+    const int G = flat_grid(out);
+    const int T = (out + TILE_ROWS - 1) / TILE_ROWS;
+    const int tpw = (T + G - 1) / G;
+    const size_t lds = flat_lds_bytes(in, K, K, tpw);
+    hipLaunchKernelGGL((gemm_flat_kernel<K, K, XU, RBQ_FLAT_RING, false, true>), dim3(G, 1), dim3(FL_THREADS),
+                       lds, st, planes, g, out, in, x, K, y, h);
+    return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_dual_k(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                         const uint16_t *x, uint16_t *y, hipStream_t st) {
+    const int xu = flat_units_per_thread(in);
+    if (xu <= 1)
+        return launch_dual_x<K, 1>(planes, g, h, out, in, x, y, st);
+    if (xu <= 2)
+        return launch_dual_x<K, 2>(planes, g, h, out, in, x, y, st);
+    if (xu <= 3)
+        return launch_dual_x<K, 3>(planes, g, h, out, in, x, y, st);
+    return launch_dual_x<K, 4>(planes, g, h, out, in, x, y, st);
+}
+
 }  // namespace
+
+// The dual-scale layer on this kernel: the K scaled copies of x are its
+// tokens (M = K).
+bool flat_dual_supports(int out, int in, int K) { return flat_supports(out, in, K, 0, K); }
+bool flat_dual_preferred(int out, int in, int K) { return flat_preferred(out, in, K, 0, K); }
+
+hipError_t launch_gemv_dual_flat(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                                 int K, const uint16_t *x, uint16_t *y, hipStream_t st) {
+    if (!flat_dual_supports(out, in, K))
+        return hipErrorInvalidValue;
+    return K == 1 ? launch_dual_k<1>(planes, g, h, out, in, x, y, st)
+                  : launch_dual_k<2>(planes, g, h, out, in, x, y, st);
+}
 
 bool flat_supports(int out, int in, int K, int group_size, int M) {
     if (group_size != 0 || K < 1 || K > 2 || in % 128 != 0 || in <= 0 || in > FL_MAX_IN ||

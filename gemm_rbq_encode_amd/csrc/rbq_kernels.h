@@ -35,6 +35,12 @@ bool dual_supports(int in, int K);
 hipError_t launch_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
                             int K, const uint16_t *x, uint16_t *y, hipStream_t st);
 
+// The same on the flat kernel (K <= 2; the layers it serves for two tokens).
+bool flat_dual_supports(int out, int in, int K);
+bool flat_dual_preferred(int out, int in, int K);
+hipError_t launch_gemv_dual_flat(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                                 int K, const uint16_t *x, uint16_t *y, hipStream_t st);
+
 // Residual SVID encoder (dual scales); workspace layout in encode_dual.hip.
 size_t encode_dual_workspace_bytes(int out, int in);
 hipError_t launch_encode_dual(const float *W, int out, int in, int K, uint32_t *planes, uint16_t *g,

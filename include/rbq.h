@@ -279,6 +279,9 @@ rbq_status rbq_encode_dual(const float *W, rbq_shape s, uint32_t *planes, uint16
  *   x       device fp16 [in], 16-byte aligned;  y device fp16 [out], written
  * K <= 4 and in % 128 == 0 (else RBQ_ERR_UNSUPPORTED); group_size must be 0
  * (RBQ_ERR_INVALID_ARG).  out == 0 enqueues nothing; in == 0 writes y = 0.
+ * Kernel family: RBQ_PATH_FLAT where rbq_gemm would take it for two tokens
+ * (K <= 2, tall layers) and in <= 8192, else RBQ_PATH_DECODE; rbq_set_path
+ * may force either (any other forced family gives RBQ_ERR_UNSUPPORTED).
  * Errors as rbq_gemm.
  */
 rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,

@@ -153,6 +153,41 @@ def test_gemv_dual_random_scales(out, inf, K):
     assert_close(gpu_gemv_dual(p, g, h, x), dual.gemm_dual(p, g, h, x)[0], f"{out}x{inf} K={K}")
 
 
+DUAL_PATHS = {"auto": rbq.PATH_AUTO, "decode": rbq.PATH_DECODE, "flat": rbq.PATH_FLAT}
+
+
+@pytest.mark.parametrize("path", list(DUAL_PATHS))
+@pytest.mark.parametrize("out,inf,K", [(8200, 6144, 2), (8200, 6144, 1), (22016, 4096, 2),
+                                       (4100, 11008, 2), (6000, 16384, 2)])
+def test_gemv_dual_kernel_families(path, out, inf, K):
+    """The flat kernel (tall layers, K <= 2) and the decode kernel, forced
+    and chosen, on ragged row counts and the widths each takes."""
+    rng = np.random.default_rng(out + 3 * inf + K)
+    p = rng.integers(0, 2 ** 32, (K, out, inf // 32), dtype=np.uint64).astype(np.uint32)
+    g = (rng.standard_normal((K, out)) * 0.05).astype(np.float16).view(np.uint16)
+    h = (rng.standard_normal((K, inf)) * np.exp(rng.uniform(-2, 2, (K, inf)))).astype(np.float16).view(np.uint16)
+    x = rng.standard_normal((1, inf)).astype(np.float16)
+    old = rbq.set_path(DUAL_PATHS[path])
+    try:
+        y = gpu_gemv_dual(p, g, h, x)
+    finally:
+        rbq.set_path(old)
+    assert_close(y, dual.gemm_dual(p, g, h, x)[0], f"{path} {out}x{inf} K={K}")
+
+
+def test_gemv_dual_forced_unsupported_family():
+    p = torch.zeros((2, 64, 8), dtype=torch.int32, device=dev())
+    g = torch.zeros((2, 64), dtype=torch.float16, device=dev())
+    h = torch.zeros((2, 256), dtype=torch.float16, device=dev())
+    x = torch.zeros(256, dtype=torch.float16, device=dev())
+    old = rbq.set_path(rbq.PATH_VALU)
+    try:
+        with pytest.raises(rbq.RbqError):
+            rbq.gemv_dual(p, g, h, x)
+    finally:
+        rbq.set_path(old)
+
+
 def test_gemv_dual_with_unit_input_scales_is_the_row_scale_layer():
     """h = 1: the dual layer is the per-row-scale layer with a_k = g_k."""
     wl = workloads.WORKLOADS["small"]
