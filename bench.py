@@ -71,6 +71,9 @@ def parse():
                     choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
     ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
+    ap.add_argument("--encode-counter-pass", action="store_true",
+                    help="for hardware-counter runs: encoder launches on the Llama-2-7B (K=2) and "
+                         "Llama-2-13B g128 (K=4) shapes, each after a cache-flushing copy, then exit")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for hardware-counter runs: a few eager launches of each decode shape "
                          "(no graph, no timing), then a plain copy of known size")
@@ -89,6 +92,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU path is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.encode_counter_pass:
+        encode_counter_pass(args)
+        return
     if args.counter_pass:
         counter_pass(args)
     elif args.workload == "llama2_7b":
@@ -160,6 +166,34 @@ def counter_pass(args):
     print(f"counter pass: copy of {COPY_PROBE_BYTES} bytes x4", flush=True)
 
 
+def encode_counter_pass(args):
+    """Launches for `rocprofv3 --pmc`: rbq_encode three times on each
+    Llama-2-7B shape (per-row scales, K=2) and Llama-2-13B shape (g128, K=4),
+    each launch after a copy of a 256 MiB buffer that evicts W from the
+    caches; the copies' read and write bytes calibrate the counters."""
+    import torch
+
+    import gemm_rbq_encode_amd as rbq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for out_f, in_f, K, group in ((4096, 4096, 2, 0), (11008, 4096, 2, 0), (4096, 11008, 2, 0),
+                                  (5120, 5120, 4, 128), (13824, 5120, 4, 128), (5120, 13824, 4, 128)):
+        g = torch.Generator(device="cpu").manual_seed(out_f * 31 + in_f + K)
+        W = (torch.randn((out_f, in_f), generator=g) * 0.02).to(dev)
+        p, sc = rbq.encode(W, K, group)
+        for _ in range(3):
+            dst.copy_(src)
+            rbq.encode(W, K, group, planes=p, scales=sc)
+        torch.cuda.synchronize()
+        nbytes = 4 * W.numel() + 4 * p.numel() + 2 * sc.numel()
+        print(f"encode counter pass: {out_f}x{in_f} K={K} g={group} x3 ({nbytes} algorithmic bytes)",
+              flush=True)
+        del W, p, sc
+
+
 def graph_launch_us(torch, dev, fns, reps):
     """Mean device time per launch (us) of the launches `fns`: they are
     captured once in a HIP graph on a side stream and the graph is replayed
@@ -182,6 +216,13 @@ def graph_launch_us(torch, dev, fns, reps):
         b.record(side)
     b.synchronize()
     return a.elapsed_time(b) * 1e3 / (reps * len(fns))
+
+
+def rotation_copies(W, total_bytes=640 * 2 ** 20):
+    """Copies of W whose combined size exceeds the caches (32 MB L2 + 256 MB
+    MALL) about twice, so that a launch cycling over them reads W from HBM."""
+    n = max(1, -(-total_bytes // (4 * W.numel())))
+    return [W] + [W.clone() for _ in range(n - 1)]
 
 
 def graph_ms(torch, dev, fns, reps):
@@ -293,9 +334,12 @@ def bench_layer_set(args):
         # encoder and refit time of this shape (outputs rewritten in place)
         key = f"{lin.out_features}x{lin.in_features}"
         pe, se, sr = torch.empty_like(p), torch.empty_like(sc), sc.clone()
-        # ten calls per graph, three replays
-        enc_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)] * 10, 3) / 10
-        ref_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)] * 10, 3) / 10
+        # one call per copy of W (copies exceed the caches), three replays
+        Wc = rotation_copies(W)
+        enc_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.encode(Wi, K, group, planes=pe, scales=se))
+                                       for Wi in Wc], 3) / len(Wc)
+        ref_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.refit(Wi, p, sr, group)) for Wi in Wc], 3) / len(Wc)
+        del Wc
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * sc.numel()
         prep[key] = {"encode_us": round(enc_ms * 1e3, 1),
                      "encode_GBps": round((wb + pb + sb) / (enc_ms * 1e-3) / 1e9, 1),
@@ -455,9 +499,12 @@ def bench_decode(args):
         if key in prep:
             continue
         pe, se, sr = torch.empty_like(p), torch.empty_like(s), s.clone()
-        # ten calls per graph, three replays
-        e_ms = graph_ms(torch, dev, [lambda: rbq.encode(W, K, group, planes=pe, scales=se)] * 10, 3) / 10
-        r_ms = graph_ms(torch, dev, [lambda: rbq.refit(W, p, sr, group)] * 10, 3) / 10
+        # one call per copy of W (copies exceed the caches), three replays
+        Wc = rotation_copies(W)
+        e_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.encode(Wi, K, group, planes=pe, scales=se))
+                                     for Wi in Wc], 3) / len(Wc)
+        r_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.refit(Wi, p, sr, group)) for Wi in Wc], 3) / len(Wc)
+        del Wc
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * s.numel()
         # dual-scale encoder (residual SVID, 20 alternating steps per plane)
         shp = rbq.shape(W.shape[0], W.shape[1], K, 0)
