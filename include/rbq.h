@@ -11,7 +11,7 @@
  * B_1 = sign(W), R_1 = W - a_1 B_1, B_2 = sign(R_1), ... (RaBiT sections 4.2,
  * A and B).
  *
- * Storage format (the only format every entry point reads and writes):
+ * Storage format (every entry point reads and writes this format):
  *   planes  uint32 [K][out][in/32], row-major.  Word w of row r of plane k
  *           holds columns 32w .. 32w+31, bit b (least significant first) is
  *           column 32w + b, and a set bit means +1, a clear bit -1 (RaBiT D
@@ -20,6 +20,10 @@
  *           one scale per output row (group_size 0, RaBiT) or in/128 for one
  *           scale per row per group of 128 consecutive input columns
  *           (group_size 128, QBB "W(4x1)A16g128").
+ *   g, h    (dual-scale entry points only: rbq_encode_dual, rbq_gemv_dual)
+ *           binary16 row scales g [K][out] and input-column scales h
+ *           [K][in] of y = sum_k g_k (.) (B_k (h_k (.) x)) (RaBiT section 4.1:
+ *           scaling vectors on both sides of each binary core).
  *   x, y    IEEE binary16 bit patterns, row-major [M][in] and [M][out].
  *   W       fp32, row-major [out][in].
  *
