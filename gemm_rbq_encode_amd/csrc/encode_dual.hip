@@ -227,7 +227,8 @@ __global__ __launch_bounds__(SV_RB) void svid_reduce(const double *__restrict__ 
 // c = sqrt(||u|| / ||v||); zero when either vector is zero.
 __global__ __launch_bounds__(SV_RB) void svid_finish(const double *__restrict__ u, const double *__restrict__ v,
                                                       const double *__restrict__ upart, int groups, int out,
-                                                      int in, uint16_t *__restrict__ g, uint16_t *__restrict__ h) {
+                                                      int in, uint16_t *__restrict__ g, uint16_t *__restrict__ h,
+                                                      int32_t *__restrict__ status) {
     __shared__ double red_u[SV_RB / RBQ_WAVE], red_v[SV_RB / RBQ_WAVE];
     const double uu = block_sum_f64<SV_RB / RBQ_WAVE>(
         (int)threadIdx.x < groups ? upart[threadIdx.x] : 0.0, red_u);
@@ -239,10 +240,19 @@ __global__ __launch_bounds__(SV_RB) void svid_finish(const double *__restrict__ 
     const bool zero = !(nu > 0.0) || !(nv > 0.0);
     const double c = zero ? 1.0 : sqrt(nu / nv);
     const int i = blockIdx.x * SV_RB + threadIdx.x;
-    if (i < out)
-        g[i] = zero ? (uint16_t)0 : f64_to_f16_rne(u[i] / c);
-    if (i < in)
-        h[i] = zero ? (uint16_t)0 : f64_to_f16_rne(v[i] * c);
+    bool inf = false;
+    if (i < out) {
+        const uint16_t b = zero ? (uint16_t)0 : f64_to_f16_rne(u[i] / c);
+        g[i] = b;
+        inf |= (b & 0x7FFFu) == 0x7C00u;
+    }
+    if (i < in) {
+        const uint16_t b = zero ? (uint16_t)0 : f64_to_f16_rne(v[i] * c);
+        h[i] = b;
+        inf |= (b & 0x7FFFu) == 0x7C00u;
+    }
+    if (status != nullptr && __any(inf) && (threadIdx.x & (RBQ_WAVE - 1)) == 0)
+        atomicOr(status, (int32_t)RBQ_STATUS_SCALE_OVERFLOW);
 }
 
 // Signs of R into plane words (a wave covers 64 consecutive columns of one
@@ -310,7 +320,7 @@ hipError_t launch_encode_dual(const float *W, int out, int in, int K, uint32_t *
         }
         uint16_t *gk = g + (size_t)k * out, *hk = h + (size_t)k * in;
         hipLaunchKernelGGL(svid_finish, dim3(fin_blocks), dim3(SV_RB), 0, st, (const double *)w.u,
-                           (const double *)w.v, (const double *)w.upart, groups, out, in, gk, hk);
+                           (const double *)w.v, (const double *)w.upart, groups, out, in, gk, hk, status);
         uint32_t *pk = planes + (size_t)k * words;
         if (k + 1 < K)
             hipLaunchKernelGGL(svid_update<false>, dim3(upd_blocks), dim3(SV_RB), 0, st, Rk, w.R, out, in,

@@ -261,7 +261,9 @@ size_t rbq_encode_dual_workspace_bytes(rbq_shape s);
  *   workspace  device, rbq_encode_dual_workspace_bytes(s) bytes, 256-byte
  *              aligned, any contents; calls that share one overlap on the
  *              stream order only
- *   status_dev device int32 or NULL: RBQ_STATUS_NONFINITE_W is OR-ed in
+ *   status_dev device int32 or NULL: RBQ_STATUS_NONFINITE_W and
+ *              RBQ_STATUS_SCALE_OVERFLOW (a g or h entry rounded to +-Inf)
+ *              are OR-ed in
  * The sums are fp64 in a fixed order (deterministic on a given device); a
  * different order changes a stored scale only when its value lies within
  * ~1e-13 of an fp16 rounding boundary.

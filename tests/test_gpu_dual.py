@@ -121,6 +121,16 @@ def test_encode_dual_flags_nonfinite_w():
     assert st & rbq.RBQ_STATUS_NONFINITE_W
 
 
+def test_encode_dual_flags_scale_overflow():
+    """|W| ~ 1e30: the balanced scales (~ sqrt of the fitted products) pass
+    65504 and round to infinity in binary16."""
+    W = np.where(np.arange(8 * 128).reshape(8, 128) % 3 == 0, -1e30, 1e30).astype(np.float32)
+    _, g, h, st = gpu_encode_dual(W, 1)
+    assert st & rbq.RBQ_STATUS_SCALE_OVERFLOW and not st & rbq.RBQ_STATUS_NONFINITE_W
+    po, go, ho = dual.encode_dual(W, 1)
+    assert np.array_equal(g, go) and np.array_equal(h, ho)
+
+
 def test_encode_dual_deterministic():
     W = workloads.gaussian_weight(512, 1024, seed=5, outliers=True)
     a = gpu_encode_dual(W, 2)
