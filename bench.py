@@ -601,8 +601,10 @@ def bench_decode(args):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    # (the chain's gate/up epilogue runs in the flat and VALU kernels only)
     layer_chain = decode_layer_chain(args, torch, rbq, L, dev, layers, g_shapes, xs, K, group) \
-        if args.layout == "fused" and graph is not None else None
+        if args.layout == "fused" and graph is not None and \
+        path in (rbq.PATH_AUTO, rbq.PATH_FLAT, rbq.PATH_VALU) else None
 
     # ---- per-launch device time of each launch group: its launches over all
     # layers in one graph, replayed between two HIP events on the launch stream
