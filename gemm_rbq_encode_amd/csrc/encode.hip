@@ -274,9 +274,10 @@ __device__ __forceinline__ void encode_row(int r, const float *__restrict__ W, i
 }
 
 // A workgroup encodes rows blockIdx.x, blockIdx.x + gridDim.x, ...  It does
-// not prefetch its next row: the registers that would take are worth more
-// as further resident workgroups, whose loads overlap this one's steps
-// (4096 x 4096: 17.0 us with a one-row prefetch, 14.8 us without).
+// not prefetch its next row: further resident workgroups overlap their loads
+// with this one's steps as well (4096 x 4096 with W in HBM: 18.2 us with a
+// one-row prefetch, 18.4 us without; with W held in the last-level cache
+// 17.0 and 14.8 us).
 template <int WAVES, int CPW>
 __global__ __launch_bounds__(WAVES * RBQ_WAVE) void encode_kernel(
     const float *__restrict__ W, int out, int in, int K, uint32_t *__restrict__ planes,
