@@ -672,3 +672,152 @@ def test_dual_zero_matrix_gives_zero_scales():
     planes, g, h = dual.encode_dual(W, 2)
     assert not g.any() and not h.any()
     assert (planes == 0xFFFFFFFF).all()
+
+
+# ---------------------------------------------------------------------------
+# re-binarization for fixed scales (oracle/rebin.py; QBB "Approach")
+# ---------------------------------------------------------------------------
+
+from oracle import rebin  # noqa: E402
+
+
+def rebin_brute_force(W, scales, group_size=0):
+    """Pattern per weight by exact rational arithmetic over every sign
+    pattern: smallest |W - c|, then the larger value c, then the larger p
+    (p's bit k = sign of plane k); NaN counts as -Inf.  Returns int [out][in]."""
+    K, out, G = scales.shape
+    inf = W.shape[1]
+    n = group_size if group_size else inf
+    a = scales.view(np.float16).astype(np.float64)
+    best = np.zeros((out, inf), dtype=np.int64)
+    for r in range(out):
+        for t in range(G):
+            vals = [sum(Fraction(float(a[k, r, t])) * (1 if (p >> k) & 1 else -1) for k in range(K))
+                    for p in range(1 << K)]
+            for j in range(t * n, (t + 1) * n):
+                w = float(W[r, j])
+                if math.isnan(w) or math.isinf(w):
+                    # -Inf (and NaN): the smallest value; +Inf: the largest
+                    key = (lambda p: (vals[p], -p)) if (math.isnan(w) or w < 0) else (lambda p: (-vals[p], -p))
+                else:
+                    fw = Fraction(w)
+                    key = lambda p: (abs(fw - vals[p]), -vals[p], -p)
+                best[r, j] = min(range(1 << K), key=key)
+    return best
+
+
+def patterns_of(planes):
+    """uint32 planes [K][out][in/32] -> pattern index p [out][in]."""
+    s = unpack_signs(planes)
+    return sum(((s[k] > 0).astype(np.int64) << k) for k in range(s.shape[0]))
+
+
+def special_rebin_case(K, rng, group_size=0):
+    """Scales with equal, zero and negative entries, and weights placed on
+    the midpoints, on the values, at +-0, tiny, subnormal, +-Inf and NaN."""
+    out, inf = 6, 256
+    G = inf // group_size if group_size else 1
+    a = np.abs(rng.standard_normal((K, out, G))) * 0.05 + 0.01
+    a[:, 1] = a[0, 1]                                # all scales equal in row 1
+    a[-1, 2] = 0.0                                   # a zero scale
+    a[0, 3] = -a[0, 3]                               # a negative scale
+    a[:, 5] = 0.0                                    # an all-zero row
+    scales = a.astype(np.float16).view(np.uint16)
+    af = scales.view(np.float16).astype(np.float64)
+    W = (rng.standard_normal((out, inf)) * 0.05).astype(np.float32)
+    n = group_size if group_size else inf
+    P = rebin.patterns(K)
+    for r in range(out):
+        for j in range(0, inf, 3):
+            vals = P @ af[:, r, j // n]
+            u, v = rng.choice(vals, 2)
+            W[r, j] = np.float32((u + v) / 2)        # exact: a few fp16 terms
+        for j in range(1, inf, 7):
+            W[r, j] = np.float32(rng.choice(P @ af[:, r, j // n]))
+    W[0, 2], W[0, 4], W[0, 5] = 0.0, -0.0, 1e-30
+    W[0, 7], W[0, 8] = -1e-40, 1e-40                 # fp32 subnormals
+    W[4, 10], W[4, 11], W[4, 13] = np.inf, -np.inf, np.nan
+    return W, scales
+
+
+@pytest.mark.parametrize("K,group", [(1, 0), (2, 0), (3, 0), (4, 0), (2, 128), (4, 128)])
+def test_rebin_matches_exact_brute_force(K, group):
+    rng = np.random.default_rng(100 + K + group)
+    W, scales = special_rebin_case(K, rng, group)
+    planes0 = np.zeros((K, W.shape[0], W.shape[1] // 32), np.uint32)
+    got, flags = rebin.rebinarize(W, planes0, scales, group)
+    assert np.array_equal(patterns_of(got), rebin_brute_force(W, scales, group))
+    assert flags == 1                                # the Inf/NaN weights
+
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_rebin_reaches_the_minimum_over_all_planes(K):
+    """The objective equals the minimum over every choice of K planes (all
+    2^(K*in) of them for a 1 x 32 row, checked weight by weight)."""
+    rng = np.random.default_rng(7 + K)
+    W = (rng.standard_normal((3, 32)) * 0.05).astype(np.float32)
+    scales = (np.abs(rng.standard_normal((K, 3, 1))) * 0.05).astype(np.float16).view(np.uint16)
+    got, _ = rebin.rebinarize(W, np.zeros((K, 3, 1), np.uint32), scales)
+    a = scales.view(np.float16).astype(np.float64)
+    best = 0.0
+    for r in range(3):
+        for j in range(32):
+            best += min((float(W[r, j]) - sum(s[k] * a[k, r, 0] for k in range(K))) ** 2
+                        for s in itertools.product((-1, 1), repeat=K))
+    assert rebin.objective(W, got, scales) == pytest.approx(best, rel=1e-12)
+
+
+def test_rebin_one_plane_is_sign():
+    W = workloads.gaussian_weight(16, 256, seed=31)
+    W[3, :5] = [0.0, -0.0, 1e-40, -1e-40, 0.0]
+    p, s, _ = oracle.encode(W, 1)
+    got, flags = rebin.rebinarize(W, np.zeros_like(p), s)
+    assert flags == 0 and np.array_equal(got, p)
+    assert np.array_equal(unpack_signs(got)[0], np.where(W >= 0, 1, -1))
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_rebin_two_planes_keep_the_cascade_when_a1_exceeds_a2(group):
+    """With a_1 > a_2 the cascade's two signs are the nearest of the four
+    values (midpoints -a_1, 0, a_1, ties up), so re-binarizing the C
+    oracle's encoding changes nothing."""
+    W = workloads.gaussian_weight(64, 512, seed=32, outliers=True)
+    p, s, _ = oracle.encode(W, 2, group)
+    a = s.view(np.float16).astype(np.float64)
+    assert (a[0] > a[1]).all()
+    got, _ = rebin.rebinarize(W, np.zeros_like(p), s, group)
+    assert np.array_equal(got, p)
+
+
+@pytest.mark.parametrize("K,group", [(3, 0), (4, 128), (4, 0)])
+def test_rebin_alternation_with_refit_never_raises_the_objective(K, group):
+    """Planes re-chosen for fixed scales are never worse than the cascade's
+    planes, and alternating with the C oracle's refit keeps descending
+    (each scale rounding can cost at most a binary16 unit's share)."""
+    W = workloads.gaussian_weight(48, 512, seed=33 + K, outliers=True)
+    p, s, _ = oracle.encode(W, K, group)
+    prev = rebin.objective(W, p, s, group)
+    for _ in range(3):
+        p2, _ = rebin.rebinarize(W, p, s, group)
+        e = rebin.objective(W, p2, s, group)
+        assert e <= prev * (1 + 1e-12)
+        s, _ = oracle.refit(W, p2, s, group)
+        prev, p = rebin.objective(W, p2, s, group), p2
+        assert prev <= e * (1 + 1e-3)
+    first = rebin.objective(W, *oracle.encode(W, K, group)[:2], group)
+    assert prev < first
+
+
+def test_rebin_keeps_planes_of_nonfinite_scales():
+    W = workloads.gaussian_weight(4, 256, seed=34)
+    p, s, _ = oracle.encode(W, 2, 128)
+    s = s.copy()
+    s[1, 2, 1] = np.float16(np.inf).view(np.uint16)
+    s[0, 3, 0] = np.float16(np.nan).view(np.uint16)
+    junk = np.full_like(p, 0x5A5A5A5A)
+    got, flags = rebin.rebinarize(W, junk, s, 128)
+    assert flags == 8
+    kept = np.zeros((4, 8), bool)
+    kept[2, 4:8] = kept[3, 0:4] = True
+    assert np.array_equal(got[:, kept], junk[:, kept])
+    assert np.array_equal(got[:, ~kept], p[:, ~kept])
