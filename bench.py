@@ -24,6 +24,10 @@ Reported (one JSON line):
   refit      rbq_refit of the seven linears (GB/s over W and planes read,
              scales read and written); on the 13B g128 set both are timed
              per distinct shape
+  encode_refit_per_shape  per distinct shape, one matrix at a time (W
+             rotated over copies larger than the caches): encoder, refit,
+             re-binarization (GB/s over W and scales read, planes written)
+             and, on the decode workload, the dual-scale encoder
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -339,13 +343,17 @@ def bench_layer_set(args):
         enc_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.encode(Wi, K, group, planes=pe, scales=se))
                                        for Wi in Wc], 3) / len(Wc)
         ref_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.refit(Wi, p, sr, group)) for Wi in Wc], 3) / len(Wc)
+        pr = p.clone()
+        rb_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.rebinarize(Wi, pr, sc, group)) for Wi in Wc], 3) / len(Wc)
         del Wc
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * sc.numel()
         prep[key] = {"encode_us": round(enc_ms * 1e3, 1),
                      "encode_GBps": round((wb + pb + sb) / (enc_ms * 1e-3) / 1e9, 1),
                      "refit_us": round(ref_ms * 1e3, 1),
-                     "refit_GBps": round((wb + pb + 2 * sb) / (ref_ms * 1e-3) / 1e9, 1)}
-        del pe, se, sr
+                     "refit_GBps": round((wb + pb + 2 * sb) / (ref_ms * 1e-3) / 1e9, 1),
+                     "rebinarize_us": round(rb_ms * 1e3, 1),
+                     "rebinarize_GBps": round((wb + pb + sb) / (rb_ms * 1e-3) / 1e9, 1)}
+        del pe, se, sr, pr
         del W
         X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
         Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
@@ -504,6 +512,8 @@ def bench_decode(args):
         e_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.encode(Wi, K, group, planes=pe, scales=se))
                                      for Wi in Wc], 3) / len(Wc)
         r_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.refit(Wi, p, sr, group)) for Wi in Wc], 3) / len(Wc)
+        pr = p.clone()
+        rb_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.rebinarize(Wi, pr, s, group)) for Wi in Wc], 3) / len(Wc)
         del Wc
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * s.numel()
         # dual-scale encoder (residual SVID, 20 alternating steps per plane)
@@ -517,8 +527,10 @@ def bench_decode(args):
                      "encode_GBps": round((wb + pb + sb) / (e_ms * 1e-3) / 1e9, 1),
                      "refit_us": round(r_ms * 1e3, 1),
                      "refit_GBps": round((wb + pb + 2 * sb) / (r_ms * 1e-3) / 1e9, 1),
+                     "rebinarize_us": round(rb_ms * 1e3, 1),
+                     "rebinarize_GBps": round((wb + pb + sb) / (rb_ms * 1e-3) / 1e9, 1),
                      "encode_dual_us": round(d_ms * 1e3, 1)}
-        del pe, se, sr, wsd, pd, gd, hd
+        del pe, se, sr, pr, wsd, pd, gd, hd
     del Ws, ref_scales
 
     # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)

@@ -11,7 +11,8 @@ from ._binding import (  # noqa: F401
     PATH_AUTO, PATH_DECODE, PATH_FLAT, PATH_GROUP, PATH_PREFILL, PATH_SPLIT, PATH_STREAM, PATH_VALU,
     RBQ_ENCODE_FORCE_SERIAL, RBQ_EPILOGUE_NONE, RBQ_EPILOGUE_SILU_MUL, RBQ_ERR_ALIGNMENT, RBQ_ERR_HIP, RBQ_ERR_INVALID_ARG,
     RBQ_ERR_NO_DEVICE, RBQ_ERR_UNSUPPORTED, RBQ_OK, RBQ_STATUS_NONFINITE_W,
-    RBQ_STATUS_REFIT_KEPT, RBQ_STATUS_SCALE_OVERFLOW, LIB_PATH, RbqError, RbqLibraryMissing, Shape, check,
-    encode, encode_dual, encode_dual_workspace_bytes, gemm, gemv, gemv_dual, groups_per_row, last_hip_error, lib, planes_bytes, refit, scales_bytes,
+    RBQ_STATUS_PLANES_KEPT, RBQ_STATUS_REFIT_KEPT, RBQ_STATUS_SCALE_OVERFLOW, LIB_PATH, RbqError, RbqLibraryMissing, Shape, check,
+    encode, encode_dual, encode_dual_workspace_bytes, gemm, gemv, gemv_dual, groups_per_row, last_hip_error, lib, planes_bytes, rebinarize, refit,
+    scales_bytes,
     select_path, set_path, set_stream_split, shape, status_string, version,
 )

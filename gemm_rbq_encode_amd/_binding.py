@@ -25,6 +25,7 @@ RBQ_ERR_HIP = 5
 RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_STATUS_REFIT_KEPT = 4
+RBQ_STATUS_PLANES_KEPT = 8
 RBQ_EPILOGUE_NONE = 0
 RBQ_EPILOGUE_SILU_MUL = 1
 RBQ_ENCODE_FORCE_SERIAL = 1
@@ -66,6 +67,8 @@ _SIGNATURES = {
                                      ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "rbq_refit": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_rebinarize": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_size_t, ctypes.c_void_p]),
@@ -226,6 +229,29 @@ def refit(W: torch.Tensor, planes: torch.Tensor, scales: torch.Tensor, group_siz
     check(lib().rbq_refit(W.data_ptr(), s, planes.data_ptr(), scales.data_ptr(), sp, _stream(W, stream)),
           "rbq_refit")
     return scales
+
+
+def rebinarize(W: torch.Tensor, planes: torch.Tensor, scales: torch.Tensor, group_size: int = 0, *,
+               status: torch.Tensor | None = None, stream=None):
+    """rbq_rebinarize: the planes of W for the fixed scales (each weight
+    takes the nearest of the 2^K values sum_k +-a_k), in place on `planes`
+    (which keep their words where a group's scales are not finite).
+    Returns `planes`."""
+    _dev(W, torch.float32, "W")
+    _dev(planes, torch.int32, "planes")
+    _dev(scales, torch.float16, "scales")
+    out_f, in_f = W.shape
+    K = planes.shape[0]
+    s = shape(out_f, in_f, K, group_size)
+    if planes.numel() * 4 < planes_bytes(s) or scales.numel() * 2 < scales_bytes(s):
+        raise ValueError("planes/scales buffers are too small for the shape")
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    check(lib().rbq_rebinarize(W.data_ptr(), s, planes.data_ptr(), scales.data_ptr(), sp,
+                               _stream(W, stream)), "rbq_rebinarize")
+    return planes
 
 
 def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size: int = 0, *,

@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librbq.so")
 
 SOURCES = ["api.hip", "encode.hip", "encode_dual.hip", "gemm_valu.hip", "gemm_decode.hip", "gemm_stream.hip",
-           "gemm_flat.hip", "gemm_group.hip", "gemm_split.hip", "gemm_prefill.hip", "refit.hip"]
+           "gemm_flat.hip", "gemm_group.hip", "gemm_split.hip", "gemm_prefill.hip", "refit.hip",
+           "rebin.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -118,6 +118,27 @@ rbq_status rbq_refit(const float *W, rbq_shape s, const uint32_t *planes, uint16
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+rbq_status rbq_rebinarize(const float *W, rbq_shape s, uint32_t *planes, const uint16_t *scales,
+                          int32_t *status_dev, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (s.out_features == 0 || s.in_features == 0)
+        return RBQ_OK;
+    if (W == nullptr || planes == nullptr || scales == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(W, 4) || !aligned(planes, 4) || !aligned(scales, 2) ||
+        (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if (s.num_planes > RBQ_REBIN_MAX_PLANES)
+        return RBQ_ERR_UNSUPPORTED;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_rebinarize(W, s.out_features, s.in_features, s.num_planes, s.group_size, planes,
+                                          scales, status_dev, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M) {
     if (rbq_check_shape(s) != RBQ_OK || M < 2)
         return 0;

@@ -14,6 +14,8 @@ hipError_t launch_encode(const float *W, int out, int in, int K, int group_size,
 // Joint least-squares refit of the K scales for fixed planes (in place).
 hipError_t launch_refit(const float *W, int out, int in, int K, int group_size, const uint32_t *planes,
                         uint16_t *scales, int32_t *status, hipStream_t st);
+hipError_t launch_rebinarize(const float *W, int out, int in, int K, int group_size, uint32_t *planes,
+                             const uint16_t *scales, int32_t *status, hipStream_t st);
 
 // fp32 VALU bit loop, any M (correctness baseline and fallback).
 // silu != 0: rows come in (gate, up) pairs 2i, 2i+1 and Y[m][i] =

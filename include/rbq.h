@@ -73,6 +73,9 @@ typedef struct rbq_shape {
 /* Bits of the device status word written by rbq_encode and rbq_refit. */
 #define RBQ_STATUS_NONFINITE_W     1u   /* some entry of W was NaN or +-Inf */
 #define RBQ_STATUS_SCALE_OVERFLOW  2u   /* some scale rounded to +-Inf in fp16 */
+#define RBQ_STATUS_PLANES_KEPT     8u   /* rbq_rebinarize kept the planes of some
+                                           (row, group) whose scales are not all
+                                           finite */
 #define RBQ_STATUS_REFIT_KEPT      4u   /* rbq_refit kept the given scales of some
                                            (row, group): singular normal
                                            equations, non-finite W, or a
@@ -159,6 +162,38 @@ rbq_status rbq_encode_ex(const float *W, rbq_shape s, uint32_t *planes, uint16_t
  */
 rbq_status rbq_refit(const float *W, rbq_shape s, const uint32_t *planes, uint16_t *scales,
                      int32_t *status_dev, void *stream);
+
+/* Largest K rbq_rebinarize handles (2^K candidate values per weight). */
+#define RBQ_REBIN_MAX_PLANES       4
+
+/*
+ * rbq_rebinarize -- the planes for fixed scales: the other half of the
+ * data-free refinement of the binary bases in the QBB summary ("Approach"),
+ * alternated with rbq_refit.  With the scales of every (row, group) fixed,
+ * sum_j (W_j - sum_k a_k B_kj)^2 is minimised weight by weight: W_j takes
+ * the sign pattern s (s_k = +-1) whose value sum_k s_k a_k is nearest to
+ * it, decided exactly (no rounding in the comparison).  Ties: a weight
+ * halfway between two values takes the larger value; among patterns of
+ * equal value the one with the most +1 bits in the highest planes (the
+ * largest p = sum_k [s_k = +1] 2^k) wins, which keeps sign(0) = +1: with
+ * K = 1 the planes are sign(W), and with K = 2 and a_1 > a_2 they are
+ * rbq_encode's.  A NaN weight takes the smallest value's pattern, +-Inf the
+ * largest or smallest.
+ *
+ *   W            device, fp32 [out][in] row-major, 4-byte aligned, read only
+ *   planes       device, uint32 [K][out][in/32], 4-byte aligned: overwritten,
+ *                except the words of a (row, group) whose scales are not all
+ *                finite, which are kept
+ *   scales       device, fp16 bits [K][out][G], 2-byte aligned, read only
+ *   status_dev   device int32 or NULL; RBQ_STATUS_NONFINITE_W and
+ *                RBQ_STATUS_PLANES_KEPT are OR-ed in (never cleared)
+ * The result does not depend on the launch or on the summation order.
+ * Errors: RBQ_ERR_INVALID_ARG, RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED
+ * (num_planes > RBQ_REBIN_MAX_PLANES), RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.  An
+ * empty shape enqueues nothing.
+ */
+rbq_status rbq_rebinarize(const float *W, rbq_shape s, uint32_t *planes, const uint16_t *scales,
+                          int32_t *status_dev, void *stream);
 
 /*
  * rbq_gemm -- Y[m] = sum_k a_k (.) (B_k X[m]) for M tokens (RaBiT section

@@ -93,6 +93,17 @@ def test_argument_errors_before_any_launch():
     assert L.rbq_refit(ok, s, ok, ok + 1, None, None) == rbq.RBQ_ERR_ALIGNMENT
     assert L.rbq_refit(ok, big, ok, ok, None, None) == rbq.RBQ_ERR_UNSUPPORTED
     assert L.rbq_refit(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
+    # rebinarize: null pointers, shape, alignment, K beyond 4
+    assert L.rbq_rebinarize(None, s, ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_rebinarize(ok, s, None, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_rebinarize(ok, s, ok, None, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_rebinarize(ok, rbq.shape(64, 100, 2), ok, ok, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_rebinarize(ok + 2, s, ok, ok, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_rebinarize(ok, s, ok + 2, ok, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_rebinarize(ok, s, ok, ok + 1, None, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_rebinarize(ok, s, ok, ok, ok + 2, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_rebinarize(ok, rbq.shape(64, 128, 5), ok, ok, None, None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_rebinarize(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
     # empty work is fine and enqueues nothing
     assert L.rbq_encode(None, rbq.shape(0, 64, 2), None, None, None, None) == rbq.RBQ_OK
     assert L.rbq_gemm(None, None, s, None, 0, None, None, 0, None) == rbq.RBQ_OK
@@ -106,6 +117,7 @@ def test_valid_call_without_device_reports_no_device():
     ok = 0x10000
     assert L.rbq_encode(ok, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_refit(ok, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
+    assert L.rbq_rebinarize(ok + 4, s, ok, ok, None, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_gemv(ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_gemm(ok, ok, s, ok, 2, ok, None, 0, None) == rbq.RBQ_ERR_NO_DEVICE
 
