@@ -23,13 +23,16 @@
 // to bit.  fp32 denormals are kept (the default mode on gfx950), so tiny
 // weights compare exactly as well.
 //
-// Work: a wave takes SB consecutive segments (row, group of n columns) --
-// their columns are contiguous in W and their words contiguous in each
-// plane.  Lane i computes segment i's thresholds and masks (O(4^K) fp64
-// compares); the wave then streams the segments' columns 64 at a time, one
-// fp32 per lane (256 coalesced bytes), reading segment j's thresholds with
-// readlane.  The ballot of a chunk is two plane words; v_writelane gathers
-// 64 words into one VGPR per plane, which is then stored coalesced.
+// Work: segments (row, group of n columns) are contiguous in W and their
+// words contiguous in each plane, so a wave takes a run of consecutive
+// segments.  Lane i computes segment i's thresholds and masks (O(4^K) fp64
+// compares); the wave then streams the columns 64 at a time, one fp32 per
+// lane (256 coalesced bytes), reading the current segment's thresholds with
+// readlane, the next batch of loads in flight while one is decided.  The
+// ballot of a chunk is two plane words; v_writelane gathers 64 words into
+// one VGPR per plane, which is then stored coalesced.  The whole pass is a
+// few dozen instructions per 64 weights, so it is bound by the read of W
+// (4 bytes per weight against K/8 written).
 #include "rbq.h"
 #include "rbq_device.h"
 #include "rbq_kernels.h"
@@ -44,6 +47,7 @@ namespace {
 constexpr int RB_THREADS = 256;
 constexpr int RB_WAVES = RB_THREADS / RBQ_WAVE;
 constexpr int RB_UNROLL = 8;                  // chunk loads in flight per lane
+constexpr int RB_FLAT_UNROLL = 16;            // the same for whole-chunk layouts
 
 __device__ __forceinline__ float ru_f32(double m) {
     float f = (float)m;                       // nearest
@@ -107,9 +111,11 @@ __device__ void segment_setup(const uint16_t *__restrict__ scales, int out, int 
     }
 }
 
-// TAIL: n % 64 == 32, so each segment ends in a half chunk.
-template <int K, bool TAIL>
-__global__ __launch_bounds__(RB_THREADS) void rebin_kernel(const float *__restrict__ W, int out, int in, int n,
+// Ragged layouts (n % 64 == 32: each segment ends in a half chunk, one
+// word).  A wave takes SB whole segments and gathers words with a running
+// cursor.
+template <int K>
+__global__ __launch_bounds__(RB_THREADS) void rebin_tail_kernel(const float *__restrict__ W, int out, int in, int n,
                                                            int sb, uint32_t *__restrict__ planes,
                                                            const uint16_t *__restrict__ scales,
                                                            int32_t *__restrict__ status) {
@@ -139,6 +145,7 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_kernel(const float *__restri
             mask[k] = 0u;
     }
     const int keep_lane = fin ? 0 : 1;
+    const bool any_keep = __ballot(!fin) != 0;
 
     const int cps = (n + RBQ_WAVE - 1) / RBQ_WAVE;      // chunks per segment
     const int nchunks = nsb * cps;
@@ -183,10 +190,7 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_kernel(const float *__restri
         for (int u = 0; u < RB_UNROLL; ++u) {
             const int col = lc * RBQ_WAVE + lane;
             if (q0 + u < nchunks) {           // uniform
-                if (TAIL)
-                    wv[u] = col < n ? wbase[(size_t)lj * n + col] : 0.0f;
-                else
-                    wv[u] = wbase[(size_t)lj * n + col];
+                wv[u] = col < n ? wbase[(size_t)lj * n + col] : 0.0f;
             } else {
                 wv[u] = 0.0f;
             }
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_kernel(const float *__restri
                 skip = __builtin_amdgcn_readlane(keep_lane, pj);
             }
             const float w = wcur[u];
-            const bool half = TAIL && pc == cps - 1;
+            const bool half = pc == cps - 1;
             bad = bad || ((!half || lane < 32) && !__builtin_isfinite(w));
             int rank = 0;
 #pragma unroll
@@ -247,10 +251,135 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_kernel(const float *__restri
 
     if (status != nullptr) {
         const bool any_bad = __ballot(bad) != 0;
-        const bool any_kept = __ballot(lane < nsb && !fin) != 0;
-        if (lane == 0 && (any_bad || any_kept))
+        if (lane == 0 && (any_bad || any_keep))
             atomicOr(status, (any_bad ? (int)RBQ_STATUS_NONFINITE_W : 0) |
-                                 (any_kept ? (int)RBQ_STATUS_PLANES_KEPT : 0));
+                                 (any_keep ? (int)RBQ_STATUS_PLANES_KEPT : 0));
+    }
+}
+
+// Whole-chunk layouts (n % 64 == 0): the matrix is one stream of 64-column
+// chunks (chunk q = flat columns 64q .. 64q + 63, plane words 2q and 2q + 1;
+// segment q / cps).  Wave w takes chunks [w cpw, (w + 1) cpw), cpw a
+// multiple of 32, so every 32 chunks fill the 64 gathered words exactly.
+// Its chunks touch at most 64 segments: lane i sets up segment seg0 + i.
+template <int K>
+__global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__restrict__ W, int out, int in, int n,
+                                                                int cpw, uint32_t *__restrict__ planes,
+                                                                const uint16_t *__restrict__ scales,
+                                                                int32_t *__restrict__ status) {
+    constexpr int P = 1 << K;
+    constexpr int U = RB_FLAT_UNROLL;
+    const int lane = threadIdx.x & (RBQ_WAVE - 1);
+    const int G = in / n;
+    const int cps = n / RBQ_WAVE;
+    const long total = (long)out * G * cps;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / RBQ_WAVE));
+    const long q_begin = ((long)blockIdx.x * RB_WAVES + wave) * cpw;
+    if (q_begin >= total)
+        return;                               // whole wave; no barriers below
+    const int nq = (int)(total - q_begin < cpw ? total - q_begin : cpw);
+    const long seg0 = q_begin / cps;
+    const int nsb = (int)((q_begin + nq - 1) / cps - seg0 + 1);
+
+    float t[P];
+    uint32_t mask[K];
+    bool fin = true;
+    if (lane < nsb) {
+        segment_setup<K>(scales, out, G, seg0 + lane, t, mask, fin);
+    } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            t[p] = __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            mask[k] = 0u;
+    }
+    const int keep_lane = fin ? 0 : 1;
+    const bool any_keep = __ballot(!fin) != 0;
+
+    const float *wq = W + (size_t)q_begin * RBQ_WAVE + lane;
+    const size_t plane_stride = (size_t)out * (in >> 5);
+    uint32_t *pq = planes + (size_t)q_begin * 2;
+
+    uint32_t acc[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        acc[k] = 0u;
+    uint32_t keepv = 0u;
+    bool bad = false;
+    float T[P];
+    uint32_t M[K];
+    int skip = 0;
+
+    auto load = [&](float (&wv)[U], int q0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wv[u] = q0 + u < nq ? wq[(size_t)(q0 + u) * RBQ_WAVE] : 0.0f;   // uniform test
+    };
+
+    int pj = 0;                               // segment of chunk q, relative to seg0
+    int pc = (int)(q_begin - seg0 * cps);     // chunk within it
+    float wcur[U];
+    load(wcur, 0);
+    for (int q0 = 0; q0 < nq; q0 += U) {
+        float wnext[U];
+        if (q0 + U < nq)
+            load(wnext, q0 + U);              // in flight while this batch is decided
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (q0 + u >= nq)
+                break;
+            if (pc == 0 || (q0 == 0 && u == 0)) {
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    T[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t[p]), pj));
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    M[k] = (uint32_t)__builtin_amdgcn_readlane((int)mask[k], pj);
+                skip = __builtin_amdgcn_readlane(keep_lane, pj);
+            }
+            const float w = wcur[u];
+            bad = bad || !__builtin_isfinite(w);
+            int rank = 0;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                rank += (w >= T[p]) ? 1 : 0;
+            const uint32_t onehot = 1u << rank;
+            const int slot = 2 * ((q0 + u) & 31);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint64_t m = __ballot((M[k] & onehot) != 0u);
+                acc[k] = (uint32_t)rbq_writelane_i32((int)(uint32_t)m, slot, (int)acc[k]);
+                acc[k] = (uint32_t)rbq_writelane_i32((int)(uint32_t)(m >> 32), slot + 1, (int)acc[k]);
+            }
+            if (any_keep) {
+                keepv = (uint32_t)rbq_writelane_i32(skip, slot, (int)keepv);
+                keepv = (uint32_t)rbq_writelane_i32(skip, slot + 1, (int)keepv);
+            }
+            if (++pc == cps) {
+                pc = 0;
+                ++pj;
+            }
+            if (((q0 + u + 1) & 31) == 0 || q0 + u + 1 == nq) {
+                const int first = 2 * ((q0 + u) & ~31);
+                const int cnt = 2 * (q0 + u + 1) - first;
+                if (lane < cnt && keepv == 0u) {
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        pq[(size_t)k * plane_stride + first + lane] = acc[k];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            wcur[u] = wnext[u];
+    }
+
+    if (status != nullptr) {
+        const bool any_bad = __ballot(bad) != 0;
+        if (lane == 0 && (any_bad || any_keep))
+            atomicOr(status, (any_bad ? (int)RBQ_STATUS_NONFINITE_W : 0) |
+                                 (any_keep ? (int)RBQ_STATUS_PLANES_KEPT : 0));
     }
 }
 
@@ -258,6 +387,23 @@ template <int K>
 hipError_t launch_k(const float *W, int out, int in, int n, uint32_t *planes, const uint16_t *scales,
                     int32_t *status, hipStream_t st) {
     const long nseg = (long)out * (in / n);
+    if (n % RBQ_WAVE == 0) {
+        // about 8192 waves; a multiple of 32 chunks each, spanning at most
+        // 64 segments
+        const int cps = n / RBQ_WAVE;
+        const long total = nseg * cps;
+        long cpw = ((total + 8191) / 8192 + 31) / 32 * 32;
+        const long cap = ((long)(RBQ_WAVE - 1) * cps) / 32 * 32;     // keeps nsb <= 64
+        cpw = cpw > cap ? cap : cpw;
+        cpw = cpw < 32 ? 32 : cpw;
+        const long waves = (total + cpw - 1) / cpw;
+        const long blocks = (waves + RB_WAVES - 1) / RB_WAVES;
+        if (blocks > 0x7FFFFFFFL || total > 0x7FFFFFFFL * 32L)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((rebin_flat_kernel<K>), dim3((unsigned)blocks), dim3(RB_THREADS), 0, st, W, out, in, n,
+                           (int)cpw, planes, scales, status);
+        return hipGetLastError();
+    }
     // a few thousand waves; at most 64 segments (one per lane) each
     long sb = (nseg + 4095) / 4096;
     sb = sb < 1 ? 1 : sb > RBQ_WAVE ? RBQ_WAVE : sb;
@@ -265,12 +411,8 @@ hipError_t launch_k(const float *W, int out, int in, int n, uint32_t *planes, co
     const long blocks = (waves + RB_WAVES - 1) / RB_WAVES;
     if (blocks > 0x7FFFFFFFL)
         return hipErrorInvalidValue;
-    if (n % RBQ_WAVE != 0)
-        hipLaunchKernelGGL((rebin_kernel<K, true>), dim3((unsigned)blocks), dim3(RB_THREADS), 0, st, W, out, in, n,
-                           (int)sb, planes, scales, status);
-    else
-        hipLaunchKernelGGL((rebin_kernel<K, false>), dim3((unsigned)blocks), dim3(RB_THREADS), 0, st, W, out, in, n,
-                           (int)sb, planes, scales, status);
+    hipLaunchKernelGGL((rebin_tail_kernel<K>), dim3((unsigned)blocks), dim3(RB_THREADS), 0, st, W, out, in, n,
+                       (int)sb, planes, scales, status);
     return hipGetLastError();
 }
 

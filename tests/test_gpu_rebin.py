@@ -50,7 +50,7 @@ def test_rebin_small_workload_after_encode():
 @pytest.mark.parametrize("out,inf,K,group", [
     (1, 32, 1, 0), (3, 96, 2, 0), (17, 160, 3, 0), (65, 4224, 4, 0), (40, 16384, 2, 0),
     (5, 128, 4, 128), (300, 640, 2, 128), (1031, 4224, 4, 128), (77, 1152, 3, 128),
-    (4100, 256, 2, 0), (9000, 128, 1, 128)])
+    (4100, 256, 2, 0), (9000, 128, 1, 128), (3000, 64, 3, 0), (20000, 128, 2, 0)])
 def test_rebin_ragged_shapes_random_scales(out, inf, K, group):
     """Random (not cascade) scales, so every pattern occurs; rows of 32 or
     96 columns end in half chunks; segment counts not a multiple of the
