@@ -62,7 +62,7 @@ __device__ __forceinline__ float ru_f32(double m) {
 // its scales is not.
 template <int K>
 __device__ void segment_setup(const uint16_t *__restrict__ scales, int out, int G, long seg, float (&t)[1 << K],
-                              uint32_t (&mask)[K], bool &finite) {
+                              uint32_t (&mask)[K], bool &finite, int (&trank)[1 << K]) {
     constexpr int P = 1 << K;
     const long r = seg / G;
     const long g = seg - r * G;
@@ -105,6 +105,7 @@ __device__ void segment_setup(const uint16_t *__restrict__ scales, int out, int 
             lower = below ? fmax(lower, c[q]) : lower;
         }
         t[p] = (rep[p] && rank > 0) ? ru_f32((lower + c[p]) * 0.5) : __builtin_nanf("");
+        trank[p] = (rep[p] && rank > 0) ? rank : 0;           // 0: no threshold
 #pragma unroll
         for (int k = 0; k < K; ++k)
             mask[k] |= (rep[p] && ((p >> k) & 1)) ? (1u << rank) : 0u;
@@ -134,8 +135,9 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_tail_kernel(const float *__r
     float t[P];
     uint32_t mask[K];
     bool fin = true;
+    int trank[P];
     if (lane < nsb) {
-        segment_setup<K>(scales, out, G, base + lane, t, mask, fin);
+        segment_setup<K>(scales, out, G, base + lane, t, mask, fin, trank);
     } else {
 #pragma unroll
         for (int p = 0; p < P; ++p)
@@ -284,18 +286,44 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
     float t[P];
     uint32_t mask[K];
     bool fin = true;
+    int trank[P];
     if (lane < nsb) {
-        segment_setup<K>(scales, out, G, seg0 + lane, t, mask, fin);
+        segment_setup<K>(scales, out, G, seg0 + lane, t, mask, fin, trank);
     } else {
 #pragma unroll
-        for (int p = 0; p < P; ++p)
+        for (int p = 0; p < P; ++p) {
             t[p] = __builtin_nanf("");
+            trank[p] = 0;
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k)
             mask[k] = 0u;
     }
     const int keep_lane = fin ? 0 : 1;
     const bool any_keep = __ballot(!fin) != 0;
+
+    // K = 4: the 15 thresholds of segment i, sorted by rank (rank r at
+    // index r - 1, NaN where a value repeats), at sorted[16 i ..] in this
+    // wave's part of LDS.  They are non-decreasing, so w >= sorted[i] holds
+    // for a prefix of i, and the rank -- that prefix's length -- is found
+    // from indices 3, 7, 11 (which quarter) and then three of the quarter.
+    // Only this wave reads what it wrote (in order, no barrier needed).
+    __shared__ float4 sorted_lds[K == 4 ? RB_WAVES * RBQ_WAVE * 4 : 1];
+    float *sorted = reinterpret_cast<float *>(sorted_lds) + (K == 4 ? wave * RBQ_WAVE * 16 : 0);
+    if constexpr (K == 4) {
+        const float nan = __builtin_nanf("");
+        float4 *mine = reinterpret_cast<float4 *>(sorted + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mine[i] = make_float4(nan, nan, nan, nan);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (trank[p] > 0)
+                sorted[lane * 16 + trank[p] - 1] = t[p];
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes are done
+        __builtin_amdgcn_wave_barrier();
+    }
+    float S3 = 0.0f, S7 = 0.0f, S11 = 0.0f;
 
     const float *wq = W + (size_t)q_begin * RBQ_WAVE + lane;
     const size_t plane_stride = (size_t)out * (in >> 5);
@@ -330,9 +358,15 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
             if (q0 + u >= nq)
                 break;
             if (pc == 0 || (q0 == 0 && u == 0)) {
+                if constexpr (K == 4) {
+                    S3 = sorted[pj * 16 + 3];
+                    S7 = sorted[pj * 16 + 7];
+                    S11 = sorted[pj * 16 + 11];
+                } else {
 #pragma unroll
-                for (int p = 0; p < P; ++p)
-                    T[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t[p]), pj));
+                    for (int p = 0; p < P; ++p)
+                        T[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t[p]), pj));
+                }
 #pragma unroll
                 for (int k = 0; k < K; ++k)
                     M[k] = (uint32_t)__builtin_amdgcn_readlane((int)mask[k], pj);
@@ -341,9 +375,15 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
             const float w = wcur[u];
             bad = bad || !__builtin_isfinite(w);
             int rank = 0;
+            if constexpr (K == 4) {
+                const int qt = (w >= S3 ? 1 : 0) + (w >= S7 ? 1 : 0) + (w >= S11 ? 1 : 0);
+                const float4 v = *reinterpret_cast<const float4 *>(sorted + pj * 16 + 4 * qt);
+                rank = 4 * qt + (w >= v.x ? 1 : 0) + (w >= v.y ? 1 : 0) + (w >= v.z ? 1 : 0);
+            } else {
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-                rank += (w >= T[p]) ? 1 : 0;
+                for (int p = 0; p < P; ++p)
+                    rank += (w >= T[p]) ? 1 : 0;
+            }
             const uint32_t onehot = 1u << rank;
             const int slot = 2 * ((q0 + u) & 31);
 #pragma unroll
