@@ -48,6 +48,7 @@ constexpr int RB_THREADS = 256;
 constexpr int RB_WAVES = RB_THREADS / RBQ_WAVE;
 constexpr int RB_UNROLL = 8;                  // chunk loads in flight per lane
 constexpr int RB_FLAT_UNROLL = 16;            // the same for whole-chunk layouts
+static_assert(32 % RB_FLAT_UNROLL == 0, "word flushes fall on batch ends");
 
 __device__ __forceinline__ float ru_f32(double m) {
     float f = (float)m;                       // nearest
@@ -400,14 +401,17 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
                 pc = 0;
                 ++pj;
             }
-            if (((q0 + u + 1) & 31) == 0 || q0 + u + 1 == nq) {
-                const int first = 2 * ((q0 + u) & ~31);
-                const int cnt = 2 * (q0 + u + 1) - first;
-                if (lane < cnt && keepv == 0u) {
+        }
+        // 32 % U == 0 and the range starts 32-aligned, so the 64 gathered
+        // words fill up only at the end of a batch
+        const int qe = q0 + U < nq ? q0 + U : nq;
+        if ((qe & 31) == 0 || qe == nq) {
+            const int first = 2 * ((qe - 1) & ~31);
+            const int cnt = 2 * qe - first;
+            if (lane < cnt && keepv == 0u) {
 #pragma unroll
-                    for (int k = 0; k < K; ++k)
-                        pq[(size_t)k * plane_stride + first + lane] = acc[k];
-                }
+                for (int k = 0; k < K; ++k)
+                    pq[(size_t)k * plane_stride + first + lane] = acc[k];
             }
         }
 #pragma unroll
