@@ -136,7 +136,7 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_tail_kernel(const float *__r
     float t[P];
     uint32_t mask[K];
     bool fin = true;
-    int trank[P];
+    int trank[P];                             // not needed here: thresholds stay per pattern
     if (lane < nsb) {
         segment_setup<K>(scales, out, G, base + lane, t, mask, fin, trank);
     } else {
