@@ -171,10 +171,11 @@ def counter_pass(args):
 
 
 def encode_counter_pass(args):
-    """Launches for `rocprofv3 --pmc`: rbq_encode three times on each
-    Llama-2-7B shape (per-row scales, K=2) and Llama-2-13B shape (g128, K=4),
-    each launch after a copy of a 256 MiB buffer that evicts W from the
-    caches; the copies' read and write bytes calibrate the counters."""
+    """Launches for `rocprofv3 --pmc`: rbq_encode, then rbq_rebinarize,
+    three times each on each Llama-2-7B shape (per-row scales, K=2) and
+    Llama-2-13B shape (g128, K=4), each launch after a copy of a 256 MiB
+    buffer that evicts W from the caches; the copies' read and write bytes
+    calibrate the counters."""
     import torch
 
     import gemm_rbq_encode_amd as rbq
@@ -191,10 +192,14 @@ def encode_counter_pass(args):
         for _ in range(3):
             dst.copy_(src)
             rbq.encode(W, K, group, planes=p, scales=sc)
+        # then rbq_rebinarize with those scales (W read, planes rewritten)
+        for _ in range(3):
+            dst.copy_(src)
+            rbq.rebinarize(W, p, sc, group)
         torch.cuda.synchronize()
         nbytes = 4 * W.numel() + 4 * p.numel() + 2 * sc.numel()
-        print(f"encode counter pass: {out_f}x{in_f} K={K} g={group} x3 ({nbytes} algorithmic bytes)",
-              flush=True)
+        print(f"encode counter pass: {out_f}x{in_f} K={K} g={group} x3 encode, x3 rebinarize "
+              f"({nbytes} algorithmic bytes each)", flush=True)
         del W, p, sc
 
 
