@@ -70,16 +70,17 @@ typedef struct rbq_shape {
     int32_t group_size;
 } rbq_shape;
 
-/* Bits of the device status word written by rbq_encode and rbq_refit. */
+/* Bits of the device status word written by rbq_encode, rbq_refit,
+ * rbq_rebinarize and rbq_encode_dual. */
 #define RBQ_STATUS_NONFINITE_W     1u   /* some entry of W was NaN or +-Inf */
 #define RBQ_STATUS_SCALE_OVERFLOW  2u   /* some scale rounded to +-Inf in fp16 */
-#define RBQ_STATUS_PLANES_KEPT     8u   /* rbq_rebinarize kept the planes of some
-                                           (row, group) whose scales are not all
-                                           finite */
 #define RBQ_STATUS_REFIT_KEPT      4u   /* rbq_refit kept the given scales of some
                                            (row, group): singular normal
                                            equations, non-finite W, or a
                                            solution outside binary16 */
+#define RBQ_STATUS_PLANES_KEPT     8u   /* rbq_rebinarize kept the planes of some
+                                           (row, group) whose scales are not all
+                                           finite */
 
 /* Flags for rbq_encode_ex. */
 #define RBQ_ENCODE_FORCE_SERIAL    1u   /* take the serial summation for every
