@@ -61,9 +61,11 @@ __device__ __forceinline__ float ru_f32(double m) {
 
 // Thresholds and rank masks of one segment; `finite` is false when one of
 // its scales is not.
+// With `sorted` given, threshold p goes to sorted[rank - 1] instead of t[p]
+// (rank order, as the K = 4 two-level count reads them).
 template <int K>
 __device__ void segment_setup(const uint16_t *__restrict__ scales, int out, int G, long seg, float (&t)[1 << K],
-                              uint32_t (&mask)[K], bool &finite, int (&trank)[1 << K]) {
+                              uint32_t (&mask)[K], bool &finite, float *sorted = nullptr) {
     constexpr int P = 1 << K;
     const long r = seg / G;
     const long g = seg - r * G;
@@ -105,8 +107,11 @@ __device__ void segment_setup(const uint16_t *__restrict__ scales, int out, int 
             rank += (below && rep[q]) ? 1 : 0;
             lower = below ? fmax(lower, c[q]) : lower;
         }
-        t[p] = (rep[p] && rank > 0) ? ru_f32((lower + c[p]) * 0.5) : __builtin_nanf("");
-        trank[p] = (rep[p] && rank > 0) ? rank : 0;           // 0: no threshold
+        const float th = (rep[p] && rank > 0) ? ru_f32((lower + c[p]) * 0.5) : __builtin_nanf("");
+        if (sorted == nullptr)
+            t[p] = th;
+        else if (rep[p] && rank > 0)
+            sorted[rank - 1] = th;
 #pragma unroll
         for (int k = 0; k < K; ++k)
             mask[k] |= (rep[p] && ((p >> k) & 1)) ? (1u << rank) : 0u;
@@ -136,9 +141,8 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_tail_kernel(const float *__r
     float t[P];
     uint32_t mask[K];
     bool fin = true;
-    int trank[P];                             // not needed here: thresholds stay per pattern
     if (lane < nsb) {
-        segment_setup<K>(scales, out, G, base + lane, t, mask, fin, trank);
+        segment_setup<K>(scales, out, G, base + lane, t, mask, fin);
     } else {
 #pragma unroll
         for (int p = 0; p < P; ++p)
@@ -287,22 +291,6 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
     float t[P];
     uint32_t mask[K];
     bool fin = true;
-    int trank[P];
-    if (lane < nsb) {
-        segment_setup<K>(scales, out, G, seg0 + lane, t, mask, fin, trank);
-    } else {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            t[p] = __builtin_nanf("");
-            trank[p] = 0;
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            mask[k] = 0u;
-    }
-    const int keep_lane = fin ? 0 : 1;
-    const bool any_keep = __ballot(!fin) != 0;
-
     // K = 4: the 15 thresholds of segment i, sorted by rank (rank r at
     // index r - 1, NaN where a value repeats), at sorted[16 i ..] in this
     // wave's part of LDS.  They are non-decreasing, so w >= sorted[i] holds
@@ -317,13 +305,24 @@ __global__ __launch_bounds__(RB_THREADS) void rebin_flat_kernel(const float *__r
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             mine[i] = make_float4(nan, nan, nan, nan);
+    }
+    if (lane < nsb) {
+        segment_setup<K>(scales, out, G, seg0 + lane, t, mask, fin, K == 4 ? sorted + lane * 16 : nullptr);
+    } else {
 #pragma unroll
         for (int p = 0; p < P; ++p)
-            if (trank[p] > 0)
-                sorted[lane * 16 + trank[p] - 1] = t[p];
+            t[p] = __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            mask[k] = 0u;
+    }
+    if constexpr (K == 4) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes are done
         __builtin_amdgcn_wave_barrier();
     }
+    const int keep_lane = fin ? 0 : 1;
+    const bool any_keep = __ballot(!fin) != 0;
+
     float S3 = 0.0f, S7 = 0.0f, S11 = 0.0f;
 
     const float *wq = W + (size_t)q_begin * RBQ_WAVE + lane;
