@@ -81,20 +81,30 @@ def svid_rank1(A: np.ndarray, iters: int = SVID_ITERS):
     return u, v
 
 
-def svid_scales(A: np.ndarray, iters: int = SVID_ITERS):
-    """Balanced fp16 scales (g bits [out], h bits [in]) of the rank-1 fit."""
+def svid_balanced(A: np.ndarray, iters: int = SVID_ITERS):
+    """The rank-1 fit balanced so that ||g|| = ||h||, before rounding:
+    (u / c, v c) in fp64 with c = sqrt(||u|| / ||v||); zeros for a zero fit."""
     u, v = svid_rank1(A, iters)
     nu, nv = np.sqrt(u @ u), np.sqrt(v @ v)
     if nu == 0.0 or nv == 0.0:
-        return np.zeros(A.shape[0], np.uint16), np.zeros(A.shape[1], np.uint16)
+        return np.zeros(A.shape[0]), np.zeros(A.shape[1])
     c = np.sqrt(nu / nv)
-    return f64_to_f16_array(u / c), f64_to_f16_array(v * c)
+    return u / c, v * c
 
 
-def encode_dual(W: np.ndarray, num_planes: int, iters: int = SVID_ITERS):
+def svid_scales(A: np.ndarray, iters: int = SVID_ITERS):
+    """Balanced fp16 scales (g bits [out], h bits [in]) of the rank-1 fit."""
+    gb, hb = svid_balanced(A, iters)
+    return f64_to_f16_array(gb), f64_to_f16_array(hb)
+
+
+def encode_dual(W: np.ndarray, num_planes: int, iters: int = SVID_ITERS, fits: list | None = None):
     """Residual SVID binarization of fp32 W [out][in] (finite values).
 
-    Returns (planes uint32 [K][out][in/32], g uint16 [K][out], h uint16 [K][in])."""
+    Returns (planes uint32 [K][out][in/32], g uint16 [K][out], h uint16 [K][in]).
+    If `fits` is a list, the unrounded balanced pair (fp64 g, fp64 h) of each
+    plane is appended to it (tests use it to see how close a scale lies to a
+    binary16 rounding boundary)."""
     R = np.array(W, dtype=np.float32, copy=True)
     out, inf = R.shape
     planes = np.zeros((num_planes, out, inf // 32), dtype=np.uint32)
@@ -102,7 +112,10 @@ def encode_dual(W: np.ndarray, num_planes: int, iters: int = SVID_ITERS):
     h = np.zeros((num_planes, inf), dtype=np.uint16)
     for k in range(num_planes):
         B = R >= np.float32(0.0)
-        g[k], h[k] = svid_scales(np.abs(R).astype(np.float64), iters)
+        gb, hb = svid_balanced(np.abs(R).astype(np.float64), iters)
+        if fits is not None:
+            fits.append((gb, hb))
+        g[k], h[k] = f64_to_f16_array(gb), f64_to_f16_array(hb)
         planes[k] = pack_signs(B)
         a = f16(g[k]).astype(np.float32)[:, None] * f16(h[k]).astype(np.float32)[None, :]
         R = np.where(B, R - a, R + a).astype(np.float32)

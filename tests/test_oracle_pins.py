@@ -821,3 +821,111 @@ def test_rebin_keeps_planes_of_nonfinite_scales():
     kept[2, 4:8] = kept[3, 0:4] = True
     assert np.array_equal(got[:, kept], junk[:, kept])
     assert np.array_equal(got[:, ~kept], p[:, ~kept])
+
+
+# ---------------------------------------------------------------------------
+# dual-scale residual step: hand-worked example (tests/golden/dual_rank1_k3.json)
+# ---------------------------------------------------------------------------
+
+def _rne16_pos_sqrt(x2: Fraction) -> Fraction:
+    """binary16 value nearest sqrt(x2) for a positive rational x2 whose square
+    root is irrational (no ties), decided exactly by comparing squares."""
+    assert x2 > 0
+    e = 0
+    while Fraction(2) ** (2 * (e + 1)) <= x2:
+        e += 1
+    while Fraction(2) ** (2 * e) > x2:
+        e -= 1
+    q = Fraction(2) ** (max(e, -14) - 10)          # quantum of the binade (subnormals: 2^-24)
+    k = 0
+    lo, hi = 0, 1 << 40                             # largest k with (k q)^2 <= x2
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if (mid * q) ** 2 <= x2:
+            lo = mid
+        else:
+            hi = mid - 1
+    k = lo
+    m = (k + Fraction(1, 2)) * q
+    assert m * m != x2
+    return (k + 1) * q if x2 > m * m else k * q
+
+
+def _decimal_rne16(x, margin):
+    """binary16 value nearest the positive Decimal x, with x required to lie
+    more than `margin` (relative) away from the midpoint it is compared with."""
+    from decimal import Decimal
+    e = 0
+    while Decimal(2) ** (e + 1) <= x:
+        e += 1
+    while Decimal(2) ** e > x:
+        e -= 1
+    q = Decimal(2) ** (max(e, -14) - 10)
+    k = int(x / q)
+    m = (Decimal(k) + Decimal("0.5")) * q
+    assert abs(x - m) > Decimal(margin) * x, f"{x} lies within {margin} of a binary16 midpoint"
+    return Fraction((k + 1) if x > m else k) * Fraction(q)
+
+
+def _decimal_svid(A, iters=20):
+    """The rank-1 fit of the dual-scale reading (alternating least squares
+    from v = 1) in 80-digit decimal arithmetic, balanced: (g, h) as Decimals."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 80
+        Ad = [[Decimal(x.numerator) / Decimal(x.denominator) for x in row] for row in A]
+        out, inf = len(Ad), len(Ad[0])
+        v = [Decimal(1)] * inf
+        for _ in range(iters):
+            vv = sum(x * x for x in v)
+            u = [sum(Ad[r][j] * v[j] for j in range(inf)) / vv for r in range(out)]
+            uu = sum(x * x for x in u)
+            v = [sum(Ad[r][j] * u[r] for r in range(out)) / uu for j in range(inf)]
+        c = (sum(x * x for x in u).sqrt() / sum(x * x for x in v).sqrt()).sqrt()
+        return [x / c for x in u], [x * c for x in v]
+
+
+def test_dual_residual_subtracts_the_stored_binary16_scales():
+    """RaBiT section 4.1 / 4.3: the residual after path k subtracts the path
+    as stored, g_k h_k^T in binary16.  On |W| = a b^T exactly (rank 1,
+    ||b|| = 2 ||a||) the first plane's scales are a sqrt(2) and b / sqrt(2),
+    rounded once to binary16; the residual is then S (a b - g h) exactly, so
+    B_2 = S where a b > g h and -S where a b < g h.  Plane 2's scales come
+    from an 80-digit evaluation of the same 20 least-squares steps, and B_3
+    from the exact sign of R_1 - B_2 g_2 h_2.  Subtracting the unrounded fit
+    u v^T (or rounding only one of g, h) breaks B_2."""
+    doc = json.load(open(os.path.join(GOLDEN, "dual_rank1_k3.json")))
+    a = [Fraction(s) for s in doc["a"]]
+    b = [Fraction(s) for s in doc["b"]]
+    S = doc["S"]
+    out, inf = doc["out"], doc["in"]
+    assert sum(x * x for x in b) == 4 * sum(x * x for x in a)
+    W = np.array([[float(S[r][j] * a[r] * b[j]) for j in range(inf)] for r in range(out)], dtype=np.float32)
+    assert all(Fraction(float(W[r, j])) == S[r][j] * a[r] * b[j] for r in range(out) for j in range(inf))
+    planes, g, h = dual.encode_dual(W, 3)
+    got = unpack_signs(planes)                       # [K][out][in] of +-1
+
+    # plane 1: exact roundings of a sqrt(2) and b / sqrt(2)
+    g1 = [_rne16_pos_sqrt(2 * x * x) for x in a]
+    h1 = [_rne16_pos_sqrt(x * x / 2) for x in b]
+    assert [Fraction(float(v)) for v in _f16(g[0])] == g1
+    assert [Fraction(float(v)) for v in _f16(h[0])] == h1
+    assert any(g1[r] * g1[r] > 2 * a[r] * a[r] for r in range(out))      # some round up ...
+    assert any(g1[r] * g1[r] < 2 * a[r] * a[r] for r in range(out))      # ... some down
+    assert np.array_equal(got[0], np.array(S, dtype=np.int8))
+
+    # plane 2: the signs of S (a b - g h), exact
+    R1 = [[S[r][j] * (a[r] * b[j] - g1[r] * h1[j]) for j in range(inf)] for r in range(out)]
+    B2 = [[1 if R1[r][j] >= 0 else -1 for j in range(inf)] for r in range(out)]
+    flips = sum(B2[r][j] != S[r][j] for r in range(out) for j in range(inf))
+    assert 0 < flips < out * inf
+    assert np.array_equal(got[1], np.array(B2, dtype=np.int8))
+    gd, hd = _decimal_svid([[abs(x) for x in row] for row in R1])
+    g2 = [_decimal_rne16(x, 1e-9) for x in gd]
+    h2 = [_decimal_rne16(x, 1e-9) for x in hd]
+    assert [Fraction(float(v)) for v in _f16(g[1])] == g2
+    assert [Fraction(float(v)) for v in _f16(h[1])] == h2
+
+    # plane 3: the exact signs of R_2 = R_1 - B_2 g_2 h_2
+    B3 = [[1 if R1[r][j] - B2[r][j] * g2[r] * h2[j] >= 0 else -1 for j in range(inf)] for r in range(out)]
+    assert np.array_equal(got[2], np.array(B3, dtype=np.int8))
