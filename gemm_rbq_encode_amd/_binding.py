@@ -21,6 +21,8 @@ RBQ_ERR_ALIGNMENT = 2
 RBQ_ERR_UNSUPPORTED = 3
 RBQ_ERR_NO_DEVICE = 4
 RBQ_ERR_HIP = 5
+RBQ_ERR_SCRATCH_LIMIT = 6
+RBQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
@@ -75,6 +77,8 @@ _SIGNATURES = {
     "rbq_gemm_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "rbq_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_gemm_workspace_bytes": (ctypes.c_size_t, [Shape, ctypes.c_int32]),
     "rbq_gemv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p]),
@@ -285,6 +289,30 @@ def gemm(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     check(lib().rbq_gemm_ex(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), M,
                             Y.data_ptr(), ws_ptr, ws_bytes, int(epilogue), _stream(X, stream)), "rbq_gemm")
+    return Y
+
+
+def gemm_noalloc(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, Y: torch.Tensor,
+                 group_size: int = 0, *, stream=None):
+    """rbq_gemm_noalloc: rbq_gemm into a caller-given Y [M][out], with the
+    split kernels' scratch taken from the library's static device buffer
+    (nothing is allocated; calls that overlap on one GPU race)."""
+    _dev(planes, torch.int32, "planes")
+    _dev(scales, torch.float16, "scales")
+    _dev(X, torch.float16, "X")
+    _dev(Y, torch.float16, "Y")
+    K, out_f, words = planes.shape
+    in_f = words * 32
+    if X.dim() != 2 or X.shape[1] != in_f:
+        raise ValueError(f"X must be [M][{in_f}], got {tuple(X.shape)}")
+    M = X.shape[0]
+    s = shape(out_f, in_f, K, group_size)
+    if scales.numel() * 2 < scales_bytes(s):
+        raise ValueError("scales buffer too small for the shape")
+    if Y.numel() < M * out_f:
+        raise ValueError("Y too small")
+    check(lib().rbq_gemm_noalloc(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), M, Y.data_ptr(),
+                                 _stream(X, stream)), "rbq_gemm_noalloc")
     return Y
 
 

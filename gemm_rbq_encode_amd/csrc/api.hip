@@ -176,9 +176,13 @@ rbq_path rbq_select_path(rbq_shape s, int32_t M) {
     return select_path_no_workspace(s, M);
 }
 
-rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
-                       const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
-                       size_t ws_bytes, uint32_t epilogue, void *stream) {
+}  // extern "C"
+
+// rbq_gemm_ex and rbq_gemm_noalloc: argument checks, the kernel family, the
+// launch.  `workspace` / `ws_bytes` is the caller's buffer or the static one.
+static rbq_status gemm_impl(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                            const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
+                            size_t ws_bytes, uint32_t epilogue, void *stream) {
     rbq_status st = rbq_check_shape(s);
     if (st != RBQ_OK)
         return st;
@@ -277,6 +281,77 @@ rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape
         return RBQ_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+// ---- the static scratch of rbq_gemm_noalloc ----------------------------------
+// One copy per GPU, held until the process ends.  In host code `scratch` names
+// a host-side stand-in, not the device array: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is passed to kernels.  Calls on one GPU share the array.
+static __device__ __align__(256) unsigned char scratch[RBQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of `scratch` on the current device (nullptr and the
+// HIP error on failure).
+void *scratch_on_current_device(hipError_t *err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_err[dev] = r;
+        g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                       const uint16_t *X, int32_t M, uint16_t *Y, void *workspace,
+                       size_t ws_bytes, uint32_t epilogue, void *stream) {
+    return gemm_impl(planes, scales, s, X, M, Y, workspace, ws_bytes, epilogue, stream);
+}
+
+rbq_status rbq_gemm_noalloc(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                            const uint16_t *X, int32_t M, uint16_t *Y, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (M < 0)
+        return RBQ_ERR_INVALID_ARG;
+    // the same choice as rbq_gemm given a large enough workspace; more scratch
+    // than the static array holds is refused before anything is enqueued
+    const rbq_path forced = (rbq_path)g_forced_path.load();
+    const bool may_split = forced == RBQ_PATH_SPLIT ||
+                           (forced == RBQ_PATH_AUTO && rbq_select_path(s, M) == RBQ_PATH_SPLIT);
+    const size_t need = may_split ? rbq_gemm_workspace_bytes(s, M) : 0;
+    if (need > RBQ_NOALLOC_SCRATCH_BYTES)
+        return RBQ_ERR_SCRATCH_LIMIT;
+    if (need == 0 || M == 0 || s.out_features == 0 || s.in_features == 0)
+        return gemm_impl(planes, scales, s, X, M, Y, nullptr, 0, RBQ_EPILOGUE_NONE, stream);
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = hipSuccess;
+    void *ws = scratch_on_current_device(&e);
+    if (ws == nullptr)
+        return hip_fail(e == hipSuccess ? hipErrorInvalidSymbol : e);
+    return gemm_impl(planes, scales, s, X, M, Y, ws, RBQ_NOALLOC_SCRATCH_BYTES, RBQ_EPILOGUE_NONE, stream);
 }
 
 rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
@@ -390,6 +465,9 @@ const char *rbq_status_string(rbq_status st) {
     case RBQ_ERR_UNSUPPORTED: return "RBQ_ERR_UNSUPPORTED: not supported by this build";
     case RBQ_ERR_NO_DEVICE: return "RBQ_ERR_NO_DEVICE: no HIP device";
     case RBQ_ERR_HIP: return "RBQ_ERR_HIP: HIP runtime error";
+    case RBQ_ERR_SCRATCH_LIMIT:
+        return "RBQ_ERR_SCRATCH_LIMIT: the call needs more scratch than rbq_gemm_noalloc's static buffer "
+               "(RBQ_NOALLOC_SCRATCH_BYTES) holds";
     }
     return "unknown rbq_status";
 }

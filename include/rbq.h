@@ -55,7 +55,9 @@ typedef enum rbq_status {
     RBQ_ERR_ALIGNMENT = 2,     /* a pointer is not aligned as required */
     RBQ_ERR_UNSUPPORTED = 3,   /* valid, but beyond what this build handles */
     RBQ_ERR_NO_DEVICE = 4,     /* no HIP device is visible */
-    RBQ_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+    RBQ_ERR_HIP = 5,           /* a HIP runtime call or launch failed */
+    RBQ_ERR_SCRATCH_LIMIT = 6  /* rbq_gemm_noalloc: the call needs more scratch
+                                  than RBQ_NOALLOC_SCRATCH_BYTES */
 } rbq_status;
 
 /* Shape of one encoded linear layer.
@@ -252,6 +254,29 @@ rbq_status rbq_gemm_ex(const uint32_t *planes, const uint16_t *scales, rbq_shape
  * The workspace must be 4-byte aligned; its contents need no
  * initialisation. */
 size_t rbq_gemm_workspace_bytes(rbq_shape s, int32_t M);
+
+/* Size of the static device buffer rbq_gemm_noalloc takes its scratch from
+ * (one per GPU the library runs on, held until the process ends). */
+#define RBQ_NOALLOC_SCRATCH_BYTES  (8u << 20)
+
+/*
+ * rbq_gemm_noalloc -- rbq_gemm for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * kernel choice as rbq_gemm given a workspace of rbq_gemm_workspace_bytes;
+ * the scratch the split-column kernels need (S * M * out fp32 partial
+ * outputs) comes from a static device array of RBQ_NOALLOC_SCRATCH_BYTES
+ * per GPU instead.  It never calls hipMalloc, hipFree or any allocating
+ * routine.  Every call on one GPU shares that GPU's array, so calls that
+ * may overlap on one GPU (different streams, different host threads without
+ * ordering) race and give unspecified results; calls ordered on one stream
+ * are safe.  The array needs no initialisation and keeps the last call's
+ * partial sums.
+ * Errors: as rbq_gemm, and RBQ_ERR_SCRATCH_LIMIT (before anything is
+ * enqueued) when the call would need more than RBQ_NOALLOC_SCRATCH_BYTES.
+ */
+rbq_status rbq_gemm_noalloc(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
+                            const uint16_t *X, int32_t M, uint16_t *Y, void *stream);
 
 /* rbq_gemv -- rbq_gemm with M = 1 (one decode token):
  * y = sum_k a_k (.) (B_k x), x fp16 [in], y fp16 [out]. */
