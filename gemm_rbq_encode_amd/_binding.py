@@ -28,6 +28,9 @@ RBQ_STATUS_NONFINITE_W = 1
 RBQ_STATUS_SCALE_OVERFLOW = 2
 RBQ_STATUS_REFIT_KEPT = 4
 RBQ_STATUS_PLANES_KEPT = 8
+RBQ_STATUS_PROGRAM_TIMEOUT = 16
+RBQ_STATUS_PROGRAM_MISMATCH = 32
+RBQ_PROGRAM_MAX_OPS = 512
 RBQ_EPILOGUE_NONE = 0
 RBQ_EPILOGUE_SILU_MUL = 1
 RBQ_ENCODE_FORCE_SERIAL = 1
@@ -54,6 +57,13 @@ class Shape(ctypes.Structure):
     def __repr__(self):
         return (f"Shape(out={self.out_features}, in={self.in_features}, "
                 f"K={self.num_planes}, group={self.group_size})")
+
+
+class ProgramOp(ctypes.Structure):
+    """rbq_program_op."""
+    _fields_ = [("planes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("out_features", ctypes.c_int32), ("in_features", ctypes.c_int32),
+                ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32)]
 
 
 _lib = None
@@ -90,6 +100,12 @@ _SIGNATURES = {
                                        ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_gemv_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, Shape,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_program_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
+    "rbq_program_counters_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
+    "rbq_program_build": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t]),
+    "rbq_program_run": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
     "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
@@ -392,3 +408,59 @@ def gemv_dual(planes: torch.Tensor, g: torch.Tensor, h: torch.Tensor, x: torch.T
     check(lib().rbq_gemv_dual(planes.data_ptr(), g.data_ptr(), h.data_ptr(), s, x.data_ptr(),
                               y.data_ptr(), _stream(x, stream)), "rbq_gemv_dual")
     return y
+
+
+class Program:
+    """A list of one-token GEMVs run by one persistent launch (rbq_program_*).
+
+    ops: sequence of dicts with keys planes (int32 [K][out][in/32]), scales
+    (fp16 [K][out]), x (fp16 [in]), y (fp16 [out], or [out/2] with
+    epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue and wait_for
+    (index of an earlier op whose y this op reads; -1 = none).  The tensors
+    are kept referenced; the image is built on the host, copied to the
+    device once, and run() enqueues the launch on the current stream."""
+
+    def __init__(self, ops, num_planes: int = 2):
+        if not ops:
+            raise ValueError("a program needs at least one op")
+        self._keep = []
+        arr = (ProgramOp * len(ops))()
+        dev = None
+        for i, o in enumerate(ops):
+            p, s, x, y = o["planes"], o["scales"], o["x"], o["y"]
+            _dev(p, torch.int32, "planes")
+            _dev(s, torch.float16, "scales")
+            _dev(x, torch.float16, "x")
+            _dev(y, torch.float16, "y")
+            K, out_f, words = p.shape
+            if K != num_planes:
+                raise ValueError(f"op {i}: {K} planes, the program has {num_planes}")
+            ep = int(o.get("epilogue", RBQ_EPILOGUE_NONE))
+            if x.numel() != words * 32 or s.numel() < K * out_f:
+                raise ValueError(f"op {i}: x or scales do not match the planes")
+            if y.numel() < (out_f // 2 if ep == RBQ_EPILOGUE_SILU_MUL else out_f):
+                raise ValueError(f"op {i}: y too small")
+            arr[i] = ProgramOp(p.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), out_f, words * 32, ep,
+                               int(o.get("wait_for", -1)))
+            self._keep += [p, s, x, y]
+            dev = x.device
+        n = len(ops)
+        nbytes = int(lib().rbq_program_bytes(n))
+        if nbytes == 0:
+            raise RbqError(RBQ_ERR_UNSUPPORTED, "rbq_program_bytes")
+        host = (ctypes.c_ubyte * nbytes)()
+        check(lib().rbq_program_build(ctypes.cast(arr, ctypes.c_void_p), n, int(num_planes),
+                                      ctypes.cast(host, ctypes.c_void_p), nbytes), "rbq_program_build")
+        self._host = host
+        self.n_ops = n
+        self.image_dev = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8).to(dev)
+        self.counters = torch.zeros(int(lib().rbq_program_counters_bytes(n)) // 4, dtype=torch.int32, device=dev)
+
+    def run(self, status: torch.Tensor | None = None, stream=None) -> None:
+        sp = None
+        if status is not None:
+            _dev(status, torch.int32, "status")
+            sp = status.data_ptr()
+        check(lib().rbq_program_run(ctypes.cast(self._host, ctypes.c_void_p), self.image_dev.data_ptr(),
+                                    self.counters.data_ptr(), sp, _stream(self.image_dev, stream)),
+              "rbq_program_run")

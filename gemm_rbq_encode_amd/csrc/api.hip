@@ -455,6 +455,36 @@ rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+size_t rbq_program_bytes(int32_t n_ops) { return rbq::program_bytes(n_ops); }
+
+size_t rbq_program_counters_bytes(int32_t n_ops) {
+    if (n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS)
+        return 0;
+    return (size_t)(n_ops + 1) * sizeof(int32_t);
+}
+
+// Host only: the checks and the image need no device (the image is laid out
+// for the current device's compute units, or 256 when none is visible).
+rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t num_planes, void *image,
+                             size_t image_bytes) {
+    return rbq::program_build(ops, n_ops, num_planes, image, image_bytes);
+}
+
+rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *counters_dev,
+                           int32_t *status_dev, void *stream) {
+    if (image == nullptr || image_dev == nullptr || counters_dev == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(image_dev, 16) || !aligned(counters_dev, 4) || (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    rbq_status st = device_present();
+    if (st != RBQ_OK)
+        return st;
+    if ((st = rbq::program_check(image)) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_program(image, image_dev, counters_dev, status_dev, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 int32_t rbq_last_hip_error(void) { return g_last_hip_error; }
 
 const char *rbq_status_string(rbq_status st) {

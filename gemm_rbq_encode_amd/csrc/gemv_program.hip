@@ -1,0 +1,902 @@
+// gemv_program.hip -- a list of residual-binary GEMVs (one token) run by one
+// persistent launch.
+//
+// Each op is y = sum_k a_k (.) (B_k x) with per-row scales ("RaBiT" summary,
+// paperlayer.ai, sections 4.1 and 4.2; D "GPU implementation": 32 columns per
+// word), computed as in the flat kernel: x quantised once per op to
+// q = round(x 2^sh) split into three signed bytes, the masked weight words
+// w & (0x01010101 << s) as the A operand of v_mfma_i32_16x16x64_i8, and
+// y = sum_k a_k (2 S_k - sum q) 2^-sh.
+//
+// Why one launch.  A decode step is a chain of GEMVs over weights that do
+// not depend on the activations.  Launched one by one, every GEMV pays the
+// launch latency and the ramp of its first HBM requests (about 2 us), which
+// at Llama-2-7B sizes (4-23 MB per GEMV) is a third of its time.  Here one
+// 16-wave workgroup per compute unit walks the whole list:
+//   * 12 stream waves keep a ring of 16-byte weight loads in flight that
+//     runs on from one op into the next, so HBM stays busy across op
+//     boundaries;
+//   * 4 image waves build each op's activation image (x quantised into LDS,
+//     laid out as the MFMA B operand; two buffers, so op i+1's image is
+//     built while op i streams), and finish each op: the int32 partial sums
+//     of a 16-row tile meet in LDS, one image thread per row applies the
+//     scales and writes y;
+//   * an op may wait for an earlier op (its x is that op's y, as in a
+//     decoder layer): the image waves of every workgroup, after writing their
+//     rows of the earlier op's y with device-coherent stores, add 1 to that
+//     op's counter in global memory; the waiting op's image is built once
+//     the counter reaches the number of workgroups, from device-coherent
+//     loads of x.  Weight loads never wait, so the ring keeps streaming the
+//     next op's weights meanwhile.
+// Every wait is bounded (0.2 s of the real-time clock); a wait that runs out sets
+// RBQ_STATUS_PROGRAM_TIMEOUT in the status word and the kernel still runs to
+// its end.  The waits across workgroups need all workgroups resident: one
+// per compute unit, as launched (the LDS each takes leaves room for one).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "rbq.h"
+#include "rbq_device.h"
+#include "rbq_kernels.h"
+
+namespace rbq {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int PG_WAVES = 16;
+constexpr int PG_THREADS = PG_WAVES * RBQ_WAVE;
+constexpr int PG_PREP = 4;                                 // image waves
+constexpr int PG_PREP_THREADS = PG_PREP * RBQ_WAVE;
+constexpr int PG_STREAM = PG_WAVES - PG_PREP;              // stream waves
+constexpr int TILE_ROWS = 16;
+constexpr int CHUNK_WORDS = 16;                            // 512 columns
+constexpr int NC = 3;                                      // MFMA columns: the 3 limbs of one token
+constexpr int IMG_CHUNK = 8 * 4 * 16 * NC + 64;            // image bytes per chunk (+64: other banks)
+constexpr int PG_MAX_TILES = PG_PREP_THREADS / TILE_ROWS;  // rows of one op per workgroup: one per image thread
+constexpr int PG_MAX_XU = 4;                               // half-words (16 columns) per image thread
+constexpr int PG_MAX_CHUNKS = PG_MAX_XU * PG_PREP_THREADS / (2 * CHUNK_WORDS);   // 32: in <= 16384
+constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wait: 0.2 s of the
+                                                           // 100 MHz real-time clock (never reached)
+constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
+constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
+
+// flags of an op
+constexpr uint32_t PF_SILU = 1u;       // (gate, up) row pairs -> silu(gate) * up
+constexpr uint32_t PF_X_SHARED = 2u;   // x is written by an earlier op of the program
+constexpr uint32_t PF_SIGNAL = 4u;     // a later op waits for this one
+constexpr uint32_t PF_Y_SHARED = 8u;   // y is read (or written again) by a later op
+constexpr uint32_t PF_BUF1 = 16u;      // the op's activation image sits in buffer 1 (else 0)
+constexpr uint32_t PF_REUSE = 32u;     // same x as the op before: its image is used again
+constexpr int PF_WROT_SHIFT = 8;       // bits 8..11: rotation of the stream waves over the units
+
+// One op in device memory (64 bytes).
+struct ProgOp {
+    const uint32_t *planes;
+    const uint16_t *scales;
+    const uint16_t *x;
+    uint16_t *y;
+    int32_t out, in;
+    int32_t wait_for;
+    uint32_t flags;
+    int32_t trot;      // rotation of the workgroups that take one more tile
+    int32_t free_after;   // the last earlier op whose image used this op's buffer (-1: none)
+    int32_t tiles;     // 16-row tiles
+    int32_t nchunks;   // 512-column chunks
+};
+static_assert(sizeof(ProgOp) == 64, "op layout");
+
+// Program image: header, ops, then the unit count of every (workgroup,
+// stream wave) over the whole program.
+struct ProgHeader {
+    uint32_t magic;
+    int32_t n_ops;
+    int32_t K;
+    int32_t grid;
+    uint32_t lds_bytes;
+    uint32_t checksum;
+    int32_t max_chunks;
+    int32_t reserved;
+};
+static_assert(sizeof(ProgHeader) == 32, "header layout");
+
+size_t image_bytes(int n_ops, int grid) {
+    return sizeof(ProgHeader) + (size_t)n_ops * sizeof(ProgOp) + (size_t)grid * PG_STREAM * sizeof(int32_t);
+}
+
+int program_num_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+// tiles [t0, t0 + ntl) of an op taken by workgroup b of G: T / G each, and
+// one more for the T % G workgroups starting at the op's rotation
+__host__ __device__ inline void op_tiles(int T, int trot, int b, int G, int &t0, int &ntl) {
+    const int base = T / G, extra = T % G;
+    const int bb = (b - trot + G) % G;
+    ntl = base + (bb < extra ? 1 : 0);
+    t0 = bb * base + (bb < extra ? bb : extra);
+}
+
+// units [u0, u1) of stream wave sw among the U (tile, chunk) units of a workgroup
+__host__ __device__ inline void op_units(int U, int wrot, int sw, int &u0, int &u1) {
+    const int s = (sw + wrot) % PG_STREAM;
+    u0 = (s * U) / PG_STREAM;
+    u1 = ((s + 1) * U) / PG_STREAM;
+}
+
+// LDS waits (relaxed reads: writers release their LDS stores before they
+// count, LDS is coherent within the compute unit).  False when the wait ran
+// out or an earlier one did (abort_flag).
+// A waiting wave sleeps between polls (s_sleep 4: 256 clocks); every
+// producer ends with s_wakeup, which wakes the sleeping waves of its
+// workgroup at once.  Polling without sleeping took issue slots and LDS
+// bandwidth from the waves doing the work.
+__device__ __forceinline__ void wake_workgroup() { asm volatile("s_wakeup" ::: "memory"); }
+
+__device__ __forceinline__ bool lds_wait_ge(int *counter, int target, int *abort_flag) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+        return true;
+    const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + PG_WAIT_TICKS;
+    for (int it = 1;; ++it) {
+        __builtin_amdgcn_s_sleep(4);
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            return true;
+        if ((it & 15) == 0 && (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ||
+                               __builtin_amdgcn_s_memrealtime() > deadline))
+            return false;
+    }
+}
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <class T>
+__device__ __forceinline__ T *rflp(T *p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)rfl((int)(uint32_t)u), hi = (uint32_t)rfl((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<T *>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
+// Pointers into global memory.  Read back from LDS a pointer is generic,
+// and generic (flat) loads count against the LDS wait counter as well: every
+// wait for an LDS read would then also wait for the weight loads in flight.
+#define GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ GLOBAL T *gptr(T *p) {
+    return (GLOBAL T *)p;
+}
+
+// The fields of op i, read from the workgroup's LDS copy of the op table
+// (uniform across the wave: scalar registers).
+struct OpView {
+    GLOBAL const uint32_t *planes;
+    GLOBAL const uint16_t *scales;
+    GLOBAL const uint16_t *x;
+    GLOBAL uint16_t *y;
+    int out, in, wait_for, tiles, nchunks, trot, wrot, free_after;
+    uint32_t flags;
+};
+
+__device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
+    const ProgOp &o = table[i];
+    OpView v;
+    v.planes = gptr(rflp(o.planes));
+    v.scales = gptr(rflp(o.scales));
+    v.x = gptr(rflp(o.x));
+    v.y = gptr(rflp(o.y));
+    v.out = rfl(o.out);
+    v.in = rfl(o.in);
+    v.wait_for = rfl(o.wait_for);
+    v.tiles = rfl(o.tiles);
+    v.nchunks = rfl(o.nchunks);
+    v.trot = rfl(o.trot);
+    v.free_after = rfl(o.free_after);
+    v.flags = (uint32_t)rfl((int)o.flags);
+    v.wrot = (int)((v.flags >> PF_WROT_SHIFT) & 15u);
+    return v;
+}
+
+template <int K, int RING>
+__global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
+    const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
+    int32_t *__restrict__ status) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ int img_cnt;                 // image waves' publications: 4 per op
+    __shared__ int sdone[2];                // stream waves done with an op, by op parity
+    __shared__ int isync;                   // phases of the image waves' barrier
+    __shared__ int abort_flag;              // a wait ran out: the rest runs without waiting
+    __shared__ uint32_t wmax[2][PG_PREP];
+    __shared__ float wsum[2][PG_PREP];
+    __shared__ int shs[2];
+    __shared__ uint16_t sc_lds[2][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+
+    if (hdr->magic != PG_MAGIC || hdr->n_ops != n_ops || hdr->checksum != checksum || hdr->K != K ||
+        hdr->grid != (int)gridDim.x) {
+        if (threadIdx.x == 0 && status != nullptr)
+            __hip_atomic_fetch_or(status, (int)RBQ_STATUS_PROGRAM_MISMATCH, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const ProgOp *__restrict__ ops_g = reinterpret_cast<const ProgOp *>(hdr + 1);
+    const int32_t *__restrict__ wave_units = reinterpret_cast<const int32_t *>(ops_g + n_ops);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (RBQ_WAVE - 1);
+    const int wave = rfl(tid / RBQ_WAVE);
+    const int li = lane & 15, lg = lane >> 4;
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int img_bytes = hdr->max_chunks * IMG_CHUNK;
+    const int pad = 2 * img_bytes;                           // 16 zero bytes
+    int *red0 = reinterpret_cast<int *>(lds + pad + 16);     // [2][PG_MAX_TILES][K][NC][16]
+    constexpr int RED_OP = PG_MAX_TILES * K * NC * TILE_ROWS;
+    ProgOp *table = reinterpret_cast<ProgOp *>(red0 + 2 * RED_OP);   // the op table, [n_ops]
+
+    // A wait that runs out only raises the LDS flag (the status word is
+    // written once at the end): the stream waves then issue no global memory
+    // operation besides their weight loads, so the compiler's wait counts
+    // stay exact and each slot of the ring waits for its own loads only.
+    auto report_timeout = [&]() {
+        __hip_atomic_store(&abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+
+    if (tid == 0) {
+        img_cnt = 0;
+        sdone[0] = sdone[1] = 0;
+        isync = 0;
+        abort_flag = 0;
+    }
+    for (int i = tid; i < 2 * RED_OP; i += PG_THREADS)
+        red0[i] = 0;
+    if (tid < 4)
+        reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
+    {
+        const v4u *src = reinterpret_cast<const v4u *>(ops_g);
+        v4u *dst = reinterpret_cast<v4u *>(table);
+        for (int i = tid; i < n_ops * (int)(sizeof(ProgOp) / 16); i += PG_THREADS)
+            dst[i] = src[i];
+    }
+    __syncthreads();
+
+    if (wave < PG_PREP) {
+        // ===================== image waves =====================
+        int phase = 0;
+        auto img_sync = [&]() {   // barrier of the 4 image waves (LDS writes released)
+            ++phase;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&isync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            wake_workgroup();
+            if (!lds_wait_ge(&isync, PG_PREP * phase, &abort_flag) && lane == 0)
+                report_timeout();
+            asm volatile("" ::: "memory");
+        };
+
+        // ---- finish op j: y for this workgroup's rows of it
+        auto finish = [&](int j) {
+            const OpView op = op_view(table, j);
+            const int par = j & 1;
+            int t0, ntl;
+            op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+            if (!lds_wait_ge(&sdone[par], PG_STREAM, &abort_flag) && lane == 0)
+                report_timeout();
+            asm volatile("" ::: "memory");
+            int *red = red0 + par * RED_OP;
+            const int row = t0 * TILE_ROWS + tid;
+            const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
+            float y = 0.0f;
+            if (rowok) {
+                float sx = 0.0f;
+#pragma unroll
+                for (int v = 0; v < PG_PREP; ++v)
+                    sx += wsum[par][v];
+                const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
+                    const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
+                                     65536.0 * (double)rp[2 * TILE_ROWS];
+                    y += h2f(sc_lds[par][k][tid]) * (float)(t * (2.0 / 128.0) - (double)sx);
+                }
+                y = __builtin_ldexpf(y, -shs[par]);
+            }
+            const bool shared_y = (op.flags & PF_Y_SHARED) != 0;
+            if (op.flags & PF_SILU) {
+                // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
+                const float up = __shfl_down(y, 1, RBQ_WAVE);
+                if (rowok && (tid & 1) == 0) {
+                    const uint16_t h = f2h(silu_f32(y) * up);
+                    GLOBAL uint16_t *dst = op.y + row / 2;
+                    if (shared_y)
+                        __hip_atomic_store(dst, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *dst = h;
+                }
+            } else if (rowok) {
+                const uint16_t h = f2h(y);
+                if (shared_y)
+                    __hip_atomic_store(op.y + row, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    op.y[row] = h;
+            }
+            img_sync();   // every partial sum of the op has been read
+            for (int e = tid; e < ntl * K * NC * TILE_ROWS; e += PG_PREP_THREADS)
+                red[e] = 0;
+            if (tid == 0)
+                __hip_atomic_store(&sdone[par], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (op.flags & PF_SIGNAL) {
+                // this workgroup's rows of y are stored (device-coherent) before it counts
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                img_sync();
+                if (tid == 0)
+                    __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+
+        // ---- wait until every workgroup has finished op j
+        auto wait_op = [&](int j) {
+            if (tid == 0) {
+                const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + PG_WAIT_TICKS;
+                for (;;) {
+                    if (__hip_atomic_load(counters + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= G)
+                        break;
+                    if (__hip_atomic_load(&abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ||
+                        __builtin_amdgcn_s_memrealtime() > deadline) {
+                        report_timeout();
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            img_sync();
+        };
+
+        // ---- the loads of an op's image, issued one op ahead: x (thread t
+        // owns half-words H = t + j * 256, 16 columns each; past the row end it
+        // loads the last one, quantised with scale 0) and the scales of the row
+        // the thread finishes.  x that an earlier op writes is loaded only after
+        // the wait, with device-coherent loads.
+        v4u xw[PG_MAX_XU][2];
+        uint16_t a_bits[K];
+        auto load_x = [&](const OpView &op) {
+            const int nh = (op.in >> 5) * 2;
+            const int xu = (op.nchunks * CHUNK_WORDS * 2 + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
+            const bool shared_x = (op.flags & PF_X_SHARED) != 0;
+#pragma unroll
+            for (int j = 0; j < PG_MAX_XU; ++j) {
+                xw[j][0] = xw[j][1] = (v4u){0u, 0u, 0u, 0u};
+                if (j < xu) {
+                    const int Hh = min(tid + j * PG_PREP_THREADS, nh - 1);
+                    GLOBAL const uint16_t *src = op.x + 16 * Hh;
+                    if (shared_x) {
+                        GLOBAL const uint64_t *p = reinterpret_cast<GLOBAL const uint64_t *>(src);
+                        uint64_t q[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            q[c] = __hip_atomic_load(p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        xw[j][0] = (v4u){(uint32_t)q[0], (uint32_t)(q[0] >> 32), (uint32_t)q[1],
+                                         (uint32_t)(q[1] >> 32)};
+                        xw[j][1] = (v4u){(uint32_t)q[2], (uint32_t)(q[2] >> 32), (uint32_t)q[3],
+                                         (uint32_t)(q[3] >> 32)};
+                    } else {
+                        GLOBAL const v4u *xp = reinterpret_cast<GLOBAL const v4u *>(src);
+                        xw[j][0] = xp[0];
+                        xw[j][1] = xp[1];
+                    }
+                }
+            }
+        };
+        auto load_scales = [&](const OpView &op) {
+            int t0, ntl;
+            op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+            const int row = t0 * TILE_ROWS + tid;
+            const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                a_bits[k] = rowok ? op.scales[(size_t)k * op.out + row] : (uint16_t)0;
+        };
+
+        // this wave's part of op i's image and sums is written: count it
+        auto publish = [&]() {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&img_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            wake_workgroup();
+        };
+        // op i reads the same x as op i - 1: its image (and the sums that go
+        // with it) serve again; only the scales are op i's own
+        auto reuse = [&](int i) {
+            const int par = i & 1;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                sc_lds[par][k][tid] = a_bits[k];
+            if (lane == 0)
+                wsum[par][wave] = wsum[par ^ 1][wave];
+            if (tid == 0)
+                shs[par] = shs[par ^ 1];
+            publish();
+        };
+
+        // ---- build op i's activation image from xw, a_bits into its buffer
+        auto build = [&](int i, const OpView &op) {
+            const int par = i & 1;
+            const int nh = (op.in >> 5) * 2;                  // half-words of the row
+            const int hpad = op.nchunks * CHUNK_WORDS * 2;    // with the padded words
+            const int xu = (hpad + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
+            // maximum of |x| (fp16 bits without the sign order like magnitudes)
+            v2u16 mx2 = (v2u16){0, 0};
+#pragma unroll
+            for (int j = 0; j < PG_MAX_XU; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, xw[j][h][c] & 0x7FFF7FFFu));
+            const uint32_t mw = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+            if (lane == 0)
+                wmax[par][wave] = mw;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                sc_lds[par][k][tid] = a_bits[k];
+            img_sync();
+            uint32_t mx = 0;
+#pragma unroll
+            for (int v = 0; v < PG_PREP; ++v)
+                mx = max(mx, wmax[par][v]);
+            // |x| < 2^E; q = round(x 2^sh), sh = 22 - E, |q| <= 2^22
+            const int e = (int)(mx >> 10);
+            const int sh = 22 - ((e == 0 ? 1 : e) - 14);
+            // image entry (word w, bit s): the columns 32w + 8kk + s, kk = 0..3,
+            // at [chunk w/16][s][lane group (w/4)%4][limb][4 (w%4) + kk];
+            // fma(x, 2^sh, 1.5 2^23) leaves 2^22 + q in the mantissa, v = q +
+            // 0x808080 lies in [0, 2^24) and its bytes xor 0x80 are the limbs
+            unsigned char *img = lds + ((op.flags & PF_BUF1) ? img_bytes : 0);
+            int psum = 0;
+#pragma unroll
+            for (int j = 0; j < PG_MAX_XU; ++j) {
+                const int H = tid + j * PG_PREP_THREADS;
+                if (j < xu && H < hpad) {
+                    const float scale = H < nh ? __builtin_ldexpf(1.0f, sh) : 0.0f;
+                    const int w = H >> 1, eh = H & 1;
+                    unsigned char *dst = img + (w / CHUNK_WORDS) * IMG_CHUNK + ((w >> 2) & 3) * (NC * 16) +
+                                         (w & 3) * 4 + 2 * eh;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const uint32_t u0 = xw[j][0][s >> 1], u1 = xw[j][1][s >> 1];
+                        const uint16_t h0 = (s & 1) ? (uint16_t)(u0 >> 16) : (uint16_t)u0;
+                        const uint16_t h1 = (s & 1) ? (uint16_t)(u1 >> 16) : (uint16_t)u1;
+                        const uint32_t v0 =
+                            __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) - 0x4ABF7F80u;
+                        const uint32_t v1 =
+                            __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) - 0x4ABF7F80u;
+                        psum += (int)(v0 + v1) - 2 * 0x808080;
+                        const uint32_t l01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u) ^ 0x80808080u;
+                        const uint32_t l2 = __builtin_amdgcn_perm(v1, v0, 0x0C0C0602u) ^ 0x8080u;
+                        unsigned char *d = dst + s * (4 * NC * 16);
+                        *reinterpret_cast<uint16_t *>(d) = (uint16_t)l01;
+                        *reinterpret_cast<uint16_t *>(d + 16) = (uint16_t)(l01 >> 16);
+                        *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
+                    }
+                }
+            }
+            const float ws = wave_sum_f32_dpp((float)psum);   // sum of q over the wave's columns
+            if (lane == 0)
+                wsum[par][wave] = ws;
+            if (tid == 0)
+                shs[par] = sh;
+            publish();
+        };
+
+        int next_fin = 0;
+        OpView cur = op_view(table, 0);
+        if (!(cur.flags & PF_X_SHARED))
+            load_x(cur);
+        load_scales(cur);
+        for (int i = 0; i < n_ops; ++i) {
+            // finish what the op waits for, the op whose partial sums and
+            // scales slot it takes (i - 2), and the last op that used the
+            // image buffer it is built into
+            const int upto = max(max(cur.wait_for, i - 2), cur.free_after);
+            while (next_fin <= upto)
+                finish(next_fin++);
+            if (cur.wait_for >= 0)
+                wait_op(cur.wait_for);
+            if (cur.flags & PF_REUSE) {
+                reuse(i);
+            } else {
+                if (cur.flags & PF_X_SHARED)
+                    load_x(cur);
+                build(i, cur);
+            }
+            if (i + 1 < n_ops) {
+                // the next op's loads go out now, to arrive while this op streams
+                cur = op_view(table, i + 1);
+                if (!(cur.flags & (PF_X_SHARED | PF_REUSE)))
+                    load_x(cur);
+                load_scales(cur);
+            }
+        }
+        while (next_fin < n_ops)
+            finish(next_fin++);
+    } else {
+        // ===================== stream waves =====================
+        const int sw = wave - PG_PREP;
+        const int total = wave_units[b * PG_STREAM + sw];
+
+        // ---- load cursor: the next (op, unit) whose weights are requested
+        int lop = 0, lu = 0, lu1 = 0, lt0 = 0, lnch = 1, lwords = 4, lout = 1;
+        uint32_t lmagic = 0;
+        const OpView op0 = op_view(table, 0);
+        GLOBAL const uint32_t *lplanes = op0.planes;
+        size_t lstride = 0;
+        auto lseek = [&]() {   // the first op from lop on that gives this wave units
+            while (lop < n_ops) {
+                const OpView op = op_view(table, lop);
+                int t0, ntl;
+                op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+                op_units(ntl * op.nchunks, op.wrot, sw, lu, lu1);
+                if (lu < lu1) {
+                    lt0 = t0;
+                    lnch = op.nchunks;
+                    lwords = op.in >> 5;
+                    lout = op.out;
+                    lplanes = op.planes;
+                    lstride = (size_t)op.out * lwords;
+                    lmagic = ((1u << 21) + lnch - 1) / lnch;
+                    return;
+                }
+                ++lop;
+            }
+        };
+        // lanes (li, lg) read words 4lg .. 4lg+3 of row li of a unit's tile;
+        // past the last unit the last address is loaded again (a wave with no
+        // units at all reads the first words of op 0)
+        GLOBAL const uint32_t *lastp = lplanes + min(4 * lg, (op0.in >> 5) - 4);
+        size_t laststride = (size_t)op0.out * (op0.in >> 5);
+        lseek();
+        auto load_next = [&](v4u (&slot)[K]) {
+            if (lop < n_ops) {
+                const int tq = (int)(((uint32_t)lu * lmagic) >> 21);
+                const int row = min((lt0 + tq) * TILE_ROWS + li, lout - 1);
+                const int wi = min((lu - tq * lnch) * CHUNK_WORDS + 4 * lg, lwords - 4);
+                lastp = lplanes + (size_t)row * lwords + wi;
+                laststride = lstride;
+                if (++lu == lu1) {
+                    ++lop;
+                    lseek();
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                slot[k] = __builtin_nontemporal_load(reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride));
+        };
+
+        // ---- consume cursor: the op and unit the MFMAs work on
+        int cop = 0, cu = 0, cu1 = 0, cnch = 1, ctile = 0, cchunk = 0, cimg = 0;
+        auto report = [&](int j) {   // this wave is done with op j
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&sdone[j & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            wake_workgroup();
+        };
+        auto cseek = [&]() {   // wait for op cop's image; skip (and report) ops without units here
+            while (cop < n_ops) {
+                if (!lds_wait_ge(&img_cnt, PG_PREP * (cop + 1), &abort_flag) && lane == 0)
+                    report_timeout();
+                asm volatile("" ::: "memory");
+                const OpView op = op_view(table, cop);
+                int t0, ntl;
+                op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+                op_units(ntl * op.nchunks, op.wrot, sw, cu, cu1);
+                if (cu < cu1) {
+                    cnch = op.nchunks;
+                    cimg = (op.flags & PF_BUF1) ? img_bytes : 0;
+                    const uint32_t magic = ((1u << 21) + cnch - 1) / cnch;
+                    const int tq = (int)(((uint32_t)cu * magic) >> 21);
+                    ctile = tq;
+                    cchunk = cu - tq * cnch;
+                    return;
+                }
+                report(cop);
+                ++cop;
+            }
+        };
+
+        v4i acc[K][8];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[k][j] = (v4i){0, 0, 0, 0};
+
+        v4u ring[RING][K];
+#pragma unroll
+        for (int d = 0; d < RING; ++d)
+            load_next(ring[d]);
+        cseek();
+
+        auto consume = [&](const v4u (&wv)[K]) {
+            const int par = cop & 1;
+            const unsigned char *bp = li < NC ? lds + cimg + (lg * NC + li) * 16 + cchunk * IMG_CHUNK
+                                              : lds + pad;
+            const int bstride = li < NC ? 4 * NC * 16 : 0;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const v4i bv = *reinterpret_cast<const v4i *>(bp + s * bstride);
+                const uint32_t mask = 0x01010101u << s;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const v4i av = (v4i){(int)(wv[k].x & mask), (int)(wv[k].y & mask), (int)(wv[k].z & mask),
+                                         (int)(wv[k].w & mask)};
+                    acc[k][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[k][s], 0, 0, 0);
+                }
+            }
+            // next chunk; at a tile's end or the wave's last unit of the op, add
+            // T = sum_{s<7} 2^(7-s) acc_s - acc_7 = 2^7 sum(bit * limb) into LDS
+            ++cu;
+            const bool tile_end = ++cchunk == cnch;
+            const bool op_end = cu == cu1;
+            if (tile_end || op_end) {
+                // (the empty asm keeps the recombination below inside this
+                // branch: hoisted, it cost ~80 VALU operations on every unit)
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        asm volatile("" : "+v"(acc[k][j]));
+                if (li < NC) {
+                    int *rp = red0 + par * RED_OP + ctile * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            uint32_t t = (uint32_t)acc[k][0][v];
+#pragma unroll
+                            for (int q = 1; q < 7; ++q)
+                                t = (t << 1) + (uint32_t)acc[k][q][v];
+                            t = (t << 1) - (uint32_t)acc[k][7][v];
+                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)t, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[k][j] = (v4i){0, 0, 0, 0};
+            }
+            if (tile_end) {
+                cchunk = 0;
+                ++ctile;
+            }
+            if (op_end) {
+                report(cop);
+                ++cop;
+                cseek();
+            }
+        };
+
+        const int nbk = (total + RING - 1) / RING;
+        for (int bi = 0; bi + 1 < nbk; ++bi) {
+#pragma unroll
+            for (int d = 0; d < RING; ++d) {
+                consume(ring[d]);
+                load_next(ring[d]);
+            }
+        }
+        if (nbk > 0) {
+#pragma unroll
+            for (int d = 0; d < RING; ++d)
+                if ((nbk - 1) * RING + d < total)
+                    consume(ring[d]);
+        }
+        // ops after this wave's last unit that give it none are reported by
+        // cseek (also when the wave has no units at all)
+    }
+    __syncthreads();
+
+    if (tid == 0 && status != nullptr && abort_flag)
+        __hip_atomic_fetch_or(status, (int)RBQ_STATUS_PROGRAM_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the last workgroup to finish clears the op counters for the next run
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(counters + n_ops, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == G - 1) {
+            for (int j = 0; j <= n_ops; ++j)
+                __hip_atomic_store(counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+uint32_t image_checksum(const unsigned char *img, size_t bytes) {
+    // FNV-1a over everything after the header's checksum field
+    uint32_t h = 2166136261u;
+    for (size_t i = 0; i < bytes; ++i) {
+        if (i >= offsetof(ProgHeader, checksum) && i < offsetof(ProgHeader, checksum) + 4)
+            continue;
+        h ^= img[i];
+        h *= 16777619u;
+    }
+    return h;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+size_t program_bytes(int n_ops) {
+    if (n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS)
+        return 0;
+    return image_bytes(n_ops, program_num_cus());
+}
+
+rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *image, size_t bytes) {
+    if (ops == nullptr || image == nullptr || n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS || K < 1 || K > 2)
+        return n_ops > RBQ_PROGRAM_MAX_OPS || K > 2 ? RBQ_ERR_UNSUPPORTED : RBQ_ERR_INVALID_ARG;
+    const int G = program_num_cus();
+    if (bytes < image_bytes(n_ops, G))
+        return RBQ_ERR_INVALID_ARG;
+    auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
+    const int max_out = PG_MAX_TILES * TILE_ROWS * G;
+    std::vector<size_t> xb(n_ops), yb(n_ops), pb(n_ops), sb(n_ops);
+    for (int i = 0; i < n_ops; ++i) {
+        const rbq_program_op &o = ops[i];
+        if (o.planes == nullptr || o.scales == nullptr || o.x == nullptr || o.y == nullptr)
+            return RBQ_ERR_INVALID_ARG;
+        if (o.out_features < 1 || o.in_features < 1 || o.in_features % 32 != 0)
+            return RBQ_ERR_INVALID_ARG;
+        if (o.epilogue != RBQ_EPILOGUE_NONE && o.epilogue != RBQ_EPILOGUE_SILU_MUL)
+            return RBQ_ERR_INVALID_ARG;
+        if (o.epilogue == RBQ_EPILOGUE_SILU_MUL && o.out_features % 2 != 0)
+            return RBQ_ERR_INVALID_ARG;
+        if (o.wait_for < -1 || o.wait_for >= i)
+            return RBQ_ERR_INVALID_ARG;
+        if (o.in_features % 128 != 0 || o.in_features > PG_MAX_CHUNKS * CHUNK_WORDS * 32 ||
+            o.out_features > max_out)
+            return RBQ_ERR_UNSUPPORTED;
+        if (!al(o.planes, 16) || !al(o.x, 16) || !al(o.scales, 2) || !al(o.y, 2))
+            return RBQ_ERR_ALIGNMENT;
+        xb[i] = (size_t)o.in_features * 2;
+        yb[i] = (size_t)(o.epilogue == RBQ_EPILOGUE_SILU_MUL ? o.out_features / 2 : o.out_features) * 2;
+        pb[i] = (size_t)K * o.out_features * (o.in_features / 32) * 4;
+        sb[i] = (size_t)K * o.out_features * 2;
+    }
+    // Ordering.  Workgroups run the ops in order, each on its own rows, so two
+    // accesses of ops j < i to one buffer are ordered across workgroups only
+    // when some op in (j, i] waits for an op >= j.  y must not overlap its own
+    // x or any weights.
+    std::vector<uint32_t> flags(n_ops, 0u);
+    for (int i = 0; i < n_ops; ++i) {
+        if (ops[i].epilogue == RBQ_EPILOGUE_SILU_MUL)
+            flags[i] |= PF_SILU;
+        if (ops[i].wait_for >= 0)
+            flags[ops[i].wait_for] |= PF_SIGNAL;
+        if (ranges_overlap(ops[i].y, yb[i], ops[i].x, xb[i]))
+            return RBQ_ERR_INVALID_ARG;
+        for (int j = 0; j < n_ops; ++j)
+            if (ranges_overlap(ops[i].y, yb[i], ops[j].planes, pb[j]) ||
+                ranges_overlap(ops[i].y, yb[i], ops[j].scales, sb[j]))
+                return RBQ_ERR_INVALID_ARG;
+        int m = -1;   // max wait_for over ops j+1 .. i
+        for (int j = i - 1; j >= 0; --j) {
+            m = std::max(m, ops[j + 1].wait_for);
+            const bool raw = ranges_overlap(ops[i].x, xb[i], ops[j].y, yb[j]);
+            const bool war = ranges_overlap(ops[i].y, yb[i], ops[j].x, xb[j]);
+            const bool waw = ranges_overlap(ops[i].y, yb[i], ops[j].y, yb[j]);
+            if ((raw || war || waw) && m < j)
+                return RBQ_ERR_INVALID_ARG;
+            if (raw) {
+                flags[i] |= PF_X_SHARED;
+                flags[j] |= PF_Y_SHARED;
+            }
+            if (war || waw)
+                flags[i] |= PF_Y_SHARED;
+        }
+    }
+    unsigned char *img = static_cast<unsigned char *>(image);
+    memset(img, 0, image_bytes(n_ops, G));
+    ProgHeader *h = reinterpret_cast<ProgHeader *>(img);
+    ProgOp *d = reinterpret_cast<ProgOp *>(h + 1);
+    int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
+    int max_chunks = 1;
+    int trot = 0, wrot = 0;
+    int last_user[2] = {-1, -1};   // the last op whose image sat in each buffer
+    int buf = 1;
+    for (int i = 0; i < n_ops; ++i) {
+        const rbq_program_op &o = ops[i];
+        ProgOp &p = d[i];
+        p.planes = o.planes;
+        p.scales = o.scales;
+        p.x = o.x;
+        p.y = o.y;
+        p.out = o.out_features;
+        p.in = o.in_features;
+        p.wait_for = o.wait_for;
+        p.flags = flags[i];
+        p.tiles = (o.out_features + TILE_ROWS - 1) / TILE_ROWS;
+        p.nchunks = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+        p.trot = trot;
+        // an op that reads the same x as the one before (and no op writes it)
+        // takes that op's image; otherwise its image goes to the other buffer
+        const bool same = i > 0 && o.x == ops[i - 1].x && o.in_features == ops[i - 1].in_features &&
+                          !(flags[i] & PF_X_SHARED) && !(flags[i - 1] & PF_X_SHARED);
+        if (same) {
+            p.flags |= PF_REUSE;
+            p.free_after = -1;
+        } else {
+            buf ^= 1;
+            p.free_after = last_user[buf];
+        }
+        last_user[buf] = i;
+        if (buf)
+            p.flags |= PF_BUF1;
+        p.flags |= (uint32_t)wrot << PF_WROT_SHIFT;
+        max_chunks = std::max(max_chunks, p.nchunks);
+        trot = (trot + p.tiles % G) % G;
+        wrot = (wrot + ((p.tiles + G - 1) / G) * p.nchunks) % PG_STREAM;
+        for (int bb = 0; bb < G; ++bb) {
+            int t0, ntl;
+            op_tiles(p.tiles, p.trot, bb, G, t0, ntl);
+            for (int s = 0; s < PG_STREAM; ++s) {
+                int u0, u1;
+                op_units(ntl * p.nchunks, (int)((p.flags >> PF_WROT_SHIFT) & 15u), s, u0, u1);
+                wu[bb * PG_STREAM + s] += u1 - u0;
+            }
+        }
+    }
+    const size_t lds = std::max(PG_MIN_LDS, (size_t)2 * max_chunks * IMG_CHUNK + 16 +
+                                                (size_t)2 * PG_MAX_TILES * K * NC * TILE_ROWS * 4 +
+                                                (size_t)n_ops * sizeof(ProgOp));
+    h->magic = PG_MAGIC;
+    h->n_ops = n_ops;
+    h->K = K;
+    h->grid = G;
+    h->lds_bytes = (uint32_t)lds;
+    h->max_chunks = max_chunks;
+    h->checksum = image_checksum(img, image_bytes(n_ops, G));
+    return RBQ_OK;
+}
+
+#ifndef RBQ_PROGRAM_RING
+#define RBQ_PROGRAM_RING 2
+#endif
+
+rbq_status program_check(const void *image) {
+    const ProgHeader *h = static_cast<const ProgHeader *>(image);
+    if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
+        h->grid != program_num_cus() || (h->K != 1 && h->K != 2))
+        return RBQ_ERR_INVALID_ARG;
+    if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
+        return RBQ_ERR_INVALID_ARG;
+    return RBQ_OK;
+}
+
+int program_num_ops(const void *image) { return static_cast<const ProgHeader *>(image)->n_ops; }
+
+hipError_t launch_program(const void *image, const void *image_dev, int32_t *counters, int32_t *status,
+                          hipStream_t st) {
+    const ProgHeader *h = static_cast<const ProgHeader *>(image);
+    const ProgHeader *hd = static_cast<const ProgHeader *>(image_dev);
+    if (h->K == 1)
+        hipLaunchKernelGGL((gemv_program_kernel<1, RBQ_PROGRAM_RING>), dim3(h->grid), dim3(PG_THREADS),
+                           h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
+    else
+        hipLaunchKernelGGL((gemv_program_kernel<2, RBQ_PROGRAM_RING>), dim3(h->grid), dim3(PG_THREADS),
+                           h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
+    return hipGetLastError();
+}
+
+}  // namespace rbq

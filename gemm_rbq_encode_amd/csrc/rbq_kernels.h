@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rbq.h"
+
 namespace rbq {
 
 // Encoder: one workgroup of 256 threads per output row.
@@ -89,6 +91,14 @@ bool prefill_supports(int in, int K, int group_size, int M);
 hipError_t launch_gemm_prefill(const uint32_t *planes, const uint16_t *scales, int out, int in,
                                int K, int group_size, const uint16_t *X, int M, uint16_t *Y,
                                hipStream_t st);
+
+// Programs of one-token GEMVs in one persistent launch (gemv_program.hip).
+size_t program_bytes(int n_ops);
+rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *image, size_t bytes);
+rbq_status program_check(const void *image);   // a valid image for the current device
+int program_num_ops(const void *image);
+hipError_t launch_program(const void *image, const void *image_dev, int32_t *counters, int32_t *status,
+                          hipStream_t st);
 
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);

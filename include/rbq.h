@@ -354,6 +354,90 @@ rbq_status rbq_encode_dual(const float *W, rbq_shape s, uint32_t *planes, uint16
 rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,
                          const uint16_t *x, uint16_t *y, void *stream);
 
+/*
+ * Programs: a list of one-token GEMVs run by ONE persistent launch.
+ *
+ * A decode step is a chain of GEMVs whose weights do not depend on the
+ * activations (RaBiT summary section 4.2: at inference the binary paths run
+ * side by side with additions only; section 5 and QBB "Key results" time
+ * whole decoder layers).  Launched one by one, each GEMV pays the launch and
+ * the ramp of its first memory requests; a program streams the weights of
+ * every op back to back on all compute units, and an op that reads an
+ * earlier op's output waits for it on the device (its weights are fetched
+ * meanwhile).  Each op computes exactly what rbq_gemv computes (per-row
+ * scales, one token), or rbq_gemm_ex with RBQ_EPILOGUE_SILU_MUL.
+ */
+#define RBQ_PROGRAM_MAX_OPS        512
+
+/* Status bits written by rbq_program_run. */
+#define RBQ_STATUS_PROGRAM_TIMEOUT  16u  /* a bounded wait of rbq_program_run ran
+                                            out (not every workgroup was resident:
+                                            the device was shared); the outputs
+                                            are then unspecified */
+#define RBQ_STATUS_PROGRAM_MISMATCH 32u  /* image_dev does not hold the image
+                                            passed on the host; nothing was run */
+
+/* One op of a program. */
+typedef struct rbq_program_op {
+    const uint32_t *planes;   /* device, [K][out][in/32], 16-byte aligned */
+    const uint16_t *scales;   /* device, fp16 [K][out] (one scale per row), 2-byte aligned */
+    const uint16_t *x;        /* device, fp16 [in], 16-byte aligned */
+    uint16_t *y;              /* device, fp16 [out] ([out/2] with SILU_MUL), 2-byte aligned */
+    int32_t out_features;     /* 1 .. 256 * number of compute units */
+    int32_t in_features;      /* multiple of 128, at most 16384 */
+    uint32_t epilogue;        /* RBQ_EPILOGUE_NONE or RBQ_EPILOGUE_SILU_MUL (out even) */
+    int32_t wait_for;         /* -1, or an earlier op: this op reads x only after
+                                 every op up to and including that one has
+                                 written all of its y */
+} rbq_program_op;
+
+/* Bytes of the program image for n_ops ops on the current device (0 when
+ * n_ops is outside 1 .. RBQ_PROGRAM_MAX_OPS). */
+size_t rbq_program_bytes(int32_t n_ops);
+
+/* Bytes of the counters a program run uses: (n_ops + 1) int32. */
+size_t rbq_program_counters_bytes(int32_t n_ops);
+
+/*
+ * rbq_program_build -- check a list of ops and write its program image into
+ * host memory (`image`, image_bytes >= rbq_program_bytes(n_ops)).  Host only;
+ * enqueues nothing and needs no device.  The image is for the current device
+ * (it depends on the number of compute units; 256 when no device is
+ * visible), and rbq_program_run refuses it on another.  The caller copies it to device memory
+ * (16-byte aligned) and passes both copies to rbq_program_run.
+ *
+ * Ordering rules, checked here: every workgroup runs the ops in list order on
+ * its own rows, so two ops j < i that touch one buffer (i reads what j
+ * wrote, i writes what j read, or both write it) must be ordered by a wait:
+ * some op in j+1 .. i must have wait_for >= j.  An op's y may not overlap its
+ * own x, or any op's planes or scales.
+ * Errors: RBQ_ERR_INVALID_ARG (null pointer, bad shape or epilogue, wait_for
+ * not an earlier op, an unordered overlap, image too small),
+ * RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (num_planes > 2, in_features % 128
+ * != 0 or > 16384, out_features too large, too many ops).
+ */
+rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t num_planes, void *image,
+                             size_t image_bytes);
+
+/*
+ * rbq_program_run -- run a program on `stream`: one launch of one 16-wave
+ * workgroup per compute unit.
+ *   image        the host image written by rbq_program_build
+ *   image_dev    device copy of the same bytes, 16-byte aligned (read only)
+ *   counters_dev device int32 [n_ops + 1], all zero before the first run;
+ *                every run that completes leaves them zero again.  One set
+ *                per program that may run concurrently with another.
+ *   status_dev   device int32 or NULL: RBQ_STATUS_PROGRAM_* bits are OR-ed in
+ * Needs the whole device: the waits between ops assume that every workgroup
+ * of the launch is resident (they are bounded, and report
+ * RBQ_STATUS_PROGRAM_TIMEOUT instead of hanging).
+ * Errors: RBQ_ERR_INVALID_ARG (null pointer, an image that is not a valid
+ * program for this device), RBQ_ERR_ALIGNMENT, RBQ_ERR_NO_DEVICE,
+ * RBQ_ERR_HIP.
+ */
+rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *counters_dev,
+                           int32_t *status_dev, void *stream);
+
 /* Kernel families rbq_gemm can use; RBQ_PATH_AUTO picks by shape and M. */
 typedef enum rbq_path {
     RBQ_PATH_AUTO = 0,

@@ -1,0 +1,104 @@
+"""Host checks of rbq_program_build (no GPU): shapes, alignment, waits that
+point forward, and the ordering rule for ops that share a buffer.  The
+pointers are fake device addresses; the build only compares them."""
+import ctypes
+
+import pytest
+
+import gemm_rbq_encode_amd as rbq
+
+MiB = 1 << 20
+
+
+def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1):
+    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for)
+
+
+def build(ops, K=2, nbytes=None):
+    L = rbq.lib()
+    arr = (rbq.ProgramOp * len(ops))(*ops)
+    n = int(L.rbq_program_bytes(len(ops)))
+    assert n > 0
+    buf = (ctypes.c_ubyte * (n if nbytes is None else nbytes))()
+    return L.rbq_program_build(ctypes.cast(arr, ctypes.c_void_p), len(ops), K, ctypes.cast(buf, ctypes.c_void_p),
+                               n if nbytes is None else nbytes)
+
+
+# distinct fake buffers: weights at 1 GiB + k MiB, activations at 2 GiB + k MiB
+def W(k):
+    return (1 << 30) + k * MiB
+
+
+def A(k):
+    return (2 << 30) + k * MiB
+
+
+def independent(n):
+    return [op(W(2 * i), W(2 * i + 1), A(0), A(1 + i)) for i in range(n)]
+
+
+def test_valid_programs_build():
+    assert build(independent(1)) == rbq.RBQ_OK
+    assert build(independent(128)) == rbq.RBQ_OK
+    chain = [op(W(0), W(1), A(0), A(1)),
+             op(W(2), W(3), A(1), A(2), wait_for=0),
+             op(W(4), W(5), A(2), A(3), epilogue=rbq.RBQ_EPILOGUE_SILU_MUL, wait_for=1),
+             op(W(6), W(7), A(3), A(0), out=512, inf=128, wait_for=2)]    # writes the first op's x
+    assert build(chain) == rbq.RBQ_OK
+    assert build(chain, K=1) == rbq.RBQ_OK
+
+
+def test_bad_arguments():
+    L = rbq.lib()
+    assert L.rbq_program_build(None, 1, 2, None, 0) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([op(0, W(1), A(0), A(1))]) == rbq.RBQ_ERR_INVALID_ARG               # null planes
+    assert build([op(W(0), W(1), A(0), A(1), out=0)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([op(W(0), W(1), A(0), A(1), inf=100)]) == rbq.RBQ_ERR_INVALID_ARG   # not a multiple of 32
+    assert build([op(W(0), W(1), A(0), A(1), inf=96)]) == rbq.RBQ_ERR_UNSUPPORTED    # not a multiple of 128
+    assert build([op(W(0), W(1), A(0), A(1), inf=16512)]) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([op(W(0), W(1), A(0), A(1), epilogue=7)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([op(W(0), W(1), A(0), A(1), out=255, epilogue=1)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([op(W(0), W(1), A(0), A(1), wait_for=0)]) == rbq.RBQ_ERR_INVALID_ARG    # not earlier
+    assert build(independent(2)[:1] + [op(W(2), W(3), A(0), A(5), wait_for=3)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build(independent(1), K=3) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build(independent(1), nbytes=16) == rbq.RBQ_ERR_INVALID_ARG
+    assert int(rbq.lib().rbq_program_bytes(0)) == 0
+    assert int(rbq.lib().rbq_program_bytes(rbq.RBQ_PROGRAM_MAX_OPS + 1)) == 0
+
+
+def test_alignment():
+    assert build([op(W(0) + 8, W(1), A(0), A(1))]) == rbq.RBQ_ERR_ALIGNMENT   # planes 16-byte
+    assert build([op(W(0), W(1), A(0) + 8, A(1))]) == rbq.RBQ_ERR_ALIGNMENT   # x 16-byte
+    assert build([op(W(0), W(1) + 1, A(0), A(1))]) == rbq.RBQ_ERR_ALIGNMENT
+    assert build([op(W(0), W(1), A(0), A(1) + 1)]) == rbq.RBQ_ERR_ALIGNMENT
+
+
+def test_unordered_sharing_is_refused():
+    # op 1 reads op 0's y without waiting (read after write)
+    raw = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(1), A(2))]
+    assert build(raw) == rbq.RBQ_ERR_INVALID_ARG
+    raw[1].wait_for = 0
+    assert build(raw) == rbq.RBQ_OK
+    # op 1 overwrites op 0's x (write after read)
+    war = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(2), A(0) + 256, out=64)]
+    assert build(war) == rbq.RBQ_ERR_INVALID_ARG
+    war[1].wait_for = 0
+    assert build(war) == rbq.RBQ_OK
+    # both write one buffer (write after write)
+    waw = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(1) + 64, out=64)]
+    assert build(waw) == rbq.RBQ_ERR_INVALID_ARG
+    # a wait on an op after the writer orders it too (every workgroup runs the ops in order)
+    mid = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2)), op(W(4), W(5), A(2), A(3), wait_for=1),
+           op(W(6), W(7), A(1), A(4))]
+    assert build(mid) == rbq.RBQ_OK
+    # ... but a wait on an op before the writer does not
+    early = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2)), op(W(4), W(5), A(1), A(3), wait_for=0),
+             op(W(6), W(7), A(2), A(4))]
+    assert build(early) == rbq.RBQ_ERR_INVALID_ARG
+
+
+def test_outputs_may_not_overlap_inputs_or_weights():
+    assert build([op(W(0), W(1), A(0), A(0) + 128)]) == rbq.RBQ_ERR_INVALID_ARG     # y inside its own x
+    assert build([op(W(0), W(1), A(0), W(0) + 4096)]) == rbq.RBQ_ERR_INVALID_ARG    # y inside the planes
+    two = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), W(1))]                   # y on another op's scales
+    assert build(two) == rbq.RBQ_ERR_INVALID_ARG
