@@ -64,6 +64,7 @@ constexpr int PG_MAX_CHUNKS = PG_MAX_XU * PG_PREP_THREADS / (2 * CHUNK_WORDS);  
 constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wait: 0.2 s of the
                                                            // 100 MHz real-time clock (never reached)
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
+constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
 constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
 
 // flags of an op
@@ -71,7 +72,6 @@ constexpr uint32_t PF_SILU = 1u;       // (gate, up) row pairs -> silu(gate) * u
 constexpr uint32_t PF_X_SHARED = 2u;   // x is written by an earlier op of the program
 constexpr uint32_t PF_SIGNAL = 4u;     // a later op waits for this one
 constexpr uint32_t PF_Y_SHARED = 8u;   // y is read (or written again) by a later op
-constexpr uint32_t PF_BUF1 = 16u;      // the op's activation image sits in buffer 1 (else 0)
 constexpr uint32_t PF_REUSE = 32u;     // same x as the op before: its image is used again
 constexpr int PF_WROT_SHIFT = 8;       // bits 8..11: rotation of the stream waves over the units
 
@@ -82,12 +82,13 @@ struct ProgOp {
     const uint16_t *x;
     uint16_t *y;
     int32_t out, in;
-    int32_t wait_for;
+    int16_t wait_for;     // earlier op this one waits for (-1: none)
+    int16_t free_after;   // the last earlier op whose image shared LDS bytes with this op's (-1: none)
     uint32_t flags;
-    int32_t trot;      // rotation of the workgroups that take one more tile
-    int32_t free_after;   // the last earlier op whose image used this op's buffer (-1: none)
-    int32_t tiles;     // 16-row tiles
-    int32_t nchunks;   // 512-column chunks
+    int32_t trot;         // rotation of the workgroups that take one more tile
+    uint32_t split;       // tiles / G (bits 0..7) | tiles % G (bits 8..): the tile split, precomputed
+    uint32_t nch_img;     // 512-column chunks (bits 0..7) | image offset in the arena / 16 (bits 8..)
+    uint32_t magic;       // ceil(2^21 / chunks): unit -> (tile, chunk) by a multiply and a shift
 };
 static_assert(sizeof(ProgOp) == 64, "op layout");
 
@@ -100,10 +101,45 @@ struct ProgHeader {
     int32_t grid;
     uint32_t lds_bytes;
     uint32_t checksum;
-    int32_t max_chunks;
+    int32_t arena_bytes;   // LDS bytes of the image arena
     int32_t reserved;
 };
 static_assert(sizeof(ProgHeader) == 32, "header layout");
+
+// The kernel's fixed LDS (its size is known to the host, which gives the
+// image arena what remains of the compute unit's LDS).
+template <int K>
+struct PgShared {
+    int img_cnt;                              // image waves' publications: 4 per op
+    int sdone[PG_SLOTS];                      // stream waves done with an op, by op slot (i % PG_SLOTS)
+    int isync;                                // phases of the image waves' barrier
+    int abort_flag;                           // a wait ran out: the rest runs without waiting
+    uint32_t wmax[PG_SLOTS][PG_PREP];
+    float wsum[PG_SLOTS][PG_PREP];
+    int shs[PG_SLOTS];
+    uint16_t sc_lds[PG_SLOTS][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+};
+
+// LDS of one compute unit available to a workgroup (160 KB on gfx950; the
+// same when no device is visible, for host-only checks).
+size_t program_lds_limit() {
+    static size_t lim = 0;
+    if (lim == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+            v = 160 * 1024;
+        lim = (size_t)v;
+    }
+    return lim;
+}
+
+// Dynamic LDS a program may take: the limit less the kernel's fixed LDS
+// (and 256 bytes for its alignment).
+size_t program_dynamic_lds(int K) {
+    const size_t fixed = K == 1 ? sizeof(PgShared<1>) : sizeof(PgShared<2>);
+    return program_lds_limit() - fixed - 256;
+}
 
 size_t image_bytes(int n_ops, int grid) {
     return sizeof(ProgHeader) + (size_t)n_ops * sizeof(ProgOp) + (size_t)grid * PG_STREAM * sizeof(int32_t);
@@ -120,18 +156,21 @@ int program_num_cus() {
     return cus;
 }
 
-// tiles [t0, t0 + ntl) of an op taken by workgroup b of G: T / G each, and
-// one more for the T % G workgroups starting at the op's rotation
-__host__ __device__ inline void op_tiles(int T, int trot, int b, int G, int &t0, int &ntl) {
-    const int base = T / G, extra = T % G;
-    const int bb = (b - trot + G) % G;
+// tiles [t0, t0 + ntl) of an op taken by workgroup b of G: base = T / G
+// each, and one more for the extra = T % G workgroups starting at the op's
+// rotation (the divisions are done on the host: without an integer divider
+// each costs dozens of scalar instructions, per op and wave)
+__host__ __device__ inline void op_tiles(int base, int extra, int trot, int b, int G, int &t0, int &ntl) {
+    int bb = b - trot;
+    bb += bb < 0 ? G : 0;
     ntl = base + (bb < extra ? 1 : 0);
     t0 = bb * base + (bb < extra ? bb : extra);
 }
 
 // units [u0, u1) of stream wave sw among the U (tile, chunk) units of a workgroup
 __host__ __device__ inline void op_units(int U, int wrot, int sw, int &u0, int &u1) {
-    const int s = (sw + wrot) % PG_STREAM;
+    int s = sw + wrot;
+    s -= s >= PG_STREAM ? PG_STREAM : 0;
     u0 = (s * U) / PG_STREAM;
     u1 = ((s + 1) * U) / PG_STREAM;
 }
@@ -184,8 +223,8 @@ struct OpView {
     GLOBAL const uint16_t *scales;
     GLOBAL const uint16_t *x;
     GLOBAL uint16_t *y;
-    int out, in, wait_for, tiles, nchunks, trot, wrot, free_after;
-    uint32_t flags;
+    int out, in, wait_for, base, extra, nchunks, trot, wrot, free_after, img_off;
+    uint32_t flags, magic;
 };
 
 __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
@@ -197,11 +236,17 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     v.y = gptr(rflp(o.y));
     v.out = rfl(o.out);
     v.in = rfl(o.in);
-    v.wait_for = rfl(o.wait_for);
-    v.tiles = rfl(o.tiles);
-    v.nchunks = rfl(o.nchunks);
+    const uint32_t wf = (uint32_t)rfl(*reinterpret_cast<const int *>(&o.wait_for));
+    v.wait_for = (int)(int16_t)(wf & 0xFFFFu);
+    v.free_after = (int)(int16_t)(wf >> 16);
+    const uint32_t sp = (uint32_t)rfl((int)o.split);
+    v.base = (int)(sp & 255u);
+    v.extra = (int)(sp >> 8);
+    v.magic = (uint32_t)rfl((int)o.magic);
+    const uint32_t ni = (uint32_t)rfl((int)o.nch_img);
+    v.nchunks = (int)(ni & 255u);
+    v.img_off = (int)(ni >> 8) * 16;
     v.trot = rfl(o.trot);
-    v.free_after = rfl(o.free_after);
     v.flags = (uint32_t)rfl((int)o.flags);
     v.wrot = (int)((v.flags >> PF_WROT_SHIFT) & 15u);
     return v;
@@ -212,14 +257,15 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int img_cnt;                 // image waves' publications: 4 per op
-    __shared__ int sdone[2];                // stream waves done with an op, by op parity
-    __shared__ int isync;                   // phases of the image waves' barrier
-    __shared__ int abort_flag;              // a wait ran out: the rest runs without waiting
-    __shared__ uint32_t wmax[2][PG_PREP];
-    __shared__ float wsum[2][PG_PREP];
-    __shared__ int shs[2];
-    __shared__ uint16_t sc_lds[2][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+    __shared__ PgShared<K> sh;
+    int &img_cnt = sh.img_cnt;
+    int *sdone = sh.sdone;
+    int &isync = sh.isync;
+    int &abort_flag = sh.abort_flag;
+    auto &wmax = sh.wmax;
+    auto &wsum = sh.wsum;
+    auto &shs = sh.shs;
+    auto &sc_lds = sh.sc_lds;
 
     if (hdr->magic != PG_MAGIC || hdr->n_ops != n_ops || hdr->checksum != checksum || hdr->K != K ||
         hdr->grid != (int)gridDim.x) {
@@ -237,11 +283,11 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const int li = lane & 15, lg = lane >> 4;
     const int G = gridDim.x;
     const int b = blockIdx.x;
-    const int img_bytes = hdr->max_chunks * IMG_CHUNK;
-    const int pad = 2 * img_bytes;                           // 16 zero bytes
-    int *red0 = reinterpret_cast<int *>(lds + pad + 16);     // [2][PG_MAX_TILES][K][NC][16]
+    // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16], op table
+    const int pad = hdr->arena_bytes;
+    int *red0 = reinterpret_cast<int *>(lds + pad + 16);
     constexpr int RED_OP = PG_MAX_TILES * K * NC * TILE_ROWS;
-    ProgOp *table = reinterpret_cast<ProgOp *>(red0 + 2 * RED_OP);   // the op table, [n_ops]
+    ProgOp *table = reinterpret_cast<ProgOp *>(red0 + PG_SLOTS * RED_OP);   // the op table, [n_ops]
 
     // A wait that runs out only raises the LDS flag (the status word is
     // written once at the end): the stream waves then issue no global memory
@@ -253,11 +299,12 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 
     if (tid == 0) {
         img_cnt = 0;
-        sdone[0] = sdone[1] = 0;
+        for (int q = 0; q < PG_SLOTS; ++q)
+            sdone[q] = 0;
         isync = 0;
         abort_flag = 0;
     }
-    for (int i = tid; i < 2 * RED_OP; i += PG_THREADS)
+    for (int i = tid; i < PG_SLOTS * RED_OP; i += PG_THREADS)
         red0[i] = 0;
     if (tid < 4)
         reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
@@ -286,9 +333,9 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // ---- finish op j: y for this workgroup's rows of it
         auto finish = [&](int j) {
             const OpView op = op_view(table, j);
-            const int par = j & 1;
+            const int par = j % PG_SLOTS;
             int t0, ntl;
-            op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+            op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
             if (!lds_wait_ge(&sdone[par], PG_STREAM, &abort_flag) && lane == 0)
                 report_timeout();
             asm volatile("" ::: "memory");
@@ -399,7 +446,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         };
         auto load_scales = [&](const OpView &op) {
             int t0, ntl;
-            op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+            op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
             const int row = t0 * TILE_ROWS + tid;
             const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
 #pragma unroll
@@ -417,20 +464,20 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // op i reads the same x as op i - 1: its image (and the sums that go
         // with it) serve again; only the scales are op i's own
         auto reuse = [&](int i) {
-            const int par = i & 1;
+            const int par = i % PG_SLOTS, prev = (i + PG_SLOTS - 1) % PG_SLOTS;
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 sc_lds[par][k][tid] = a_bits[k];
             if (lane == 0)
-                wsum[par][wave] = wsum[par ^ 1][wave];
+                wsum[par][wave] = wsum[prev][wave];
             if (tid == 0)
-                shs[par] = shs[par ^ 1];
+                shs[par] = shs[prev];
             publish();
         };
 
         // ---- build op i's activation image from xw, a_bits into its buffer
         auto build = [&](int i, const OpView &op) {
-            const int par = i & 1;
+            const int par = i % PG_SLOTS;
             const int nh = (op.in >> 5) * 2;                  // half-words of the row
             const int hpad = op.nchunks * CHUNK_WORDS * 2;    // with the padded words
             const int xu = (hpad + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
@@ -461,7 +508,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             // at [chunk w/16][s][lane group (w/4)%4][limb][4 (w%4) + kk];
             // fma(x, 2^sh, 1.5 2^23) leaves 2^22 + q in the mantissa, v = q +
             // 0x808080 lies in [0, 2^24) and its bytes xor 0x80 are the limbs
-            unsigned char *img = lds + ((op.flags & PF_BUF1) ? img_bytes : 0);
+            unsigned char *img = lds + op.img_off;
             int psum = 0;
 #pragma unroll
             for (int j = 0; j < PG_MAX_XU; ++j) {
@@ -504,10 +551,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             load_x(cur);
         load_scales(cur);
         for (int i = 0; i < n_ops; ++i) {
-            // finish what the op waits for, the op whose partial sums and
-            // scales slot it takes (i - 2), and the last op that used the
-            // image buffer it is built into
-            const int upto = max(max(cur.wait_for, i - 2), cur.free_after);
+            // finish what the op waits for, the op whose slot of partial sums
+            // and scales it takes, and the last op whose image shares LDS
+            // bytes with its own
+            const int upto = max(max(cur.wait_for, i - PG_SLOTS), cur.free_after);
             while (next_fin <= upto)
                 finish(next_fin++);
             if (cur.wait_for >= 0)
@@ -544,7 +591,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             while (lop < n_ops) {
                 const OpView op = op_view(table, lop);
                 int t0, ntl;
-                op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+                op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
                 op_units(ntl * op.nchunks, op.wrot, sw, lu, lu1);
                 if (lu < lu1) {
                     lt0 = t0;
@@ -553,7 +600,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     lout = op.out;
                     lplanes = op.planes;
                     lstride = (size_t)op.out * lwords;
-                    lmagic = ((1u << 21) + lnch - 1) / lnch;
+                    lmagic = op.magic;
                     return;
                 }
                 ++lop;
@@ -587,7 +634,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         auto report = [&](int j) {   // this wave is done with op j
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (lane == 0)
-                __hip_atomic_fetch_add(&sdone[j & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&sdone[j % PG_SLOTS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             wake_workgroup();
         };
         auto cseek = [&]() {   // wait for op cop's image; skip (and report) ops without units here
@@ -597,13 +644,12 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 asm volatile("" ::: "memory");
                 const OpView op = op_view(table, cop);
                 int t0, ntl;
-                op_tiles(op.tiles, op.trot, b, G, t0, ntl);
+                op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
                 op_units(ntl * op.nchunks, op.wrot, sw, cu, cu1);
                 if (cu < cu1) {
                     cnch = op.nchunks;
-                    cimg = (op.flags & PF_BUF1) ? img_bytes : 0;
-                    const uint32_t magic = ((1u << 21) + cnch - 1) / cnch;
-                    const int tq = (int)(((uint32_t)cu * magic) >> 21);
+                    cimg = op.img_off;
+                    const int tq = (int)(((uint32_t)cu * op.magic) >> 21);
                     ctile = tq;
                     cchunk = cu - tq * cnch;
                     return;
@@ -627,7 +673,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         cseek();
 
         auto consume = [&](const v4u (&wv)[K]) {
-            const int par = cop & 1;
+            const int par = cop % PG_SLOTS;
             const unsigned char *bp = li < NC ? lds + cimg + (lg * NC + li) * 16 + cchunk * IMG_CHUNK
                                               : lds + pad;
             const int bstride = li < NC ? 4 * NC * 16 : 0;
@@ -811,10 +857,21 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     ProgHeader *h = reinterpret_cast<ProgHeader *>(img);
     ProgOp *d = reinterpret_cast<ProgOp *>(h + 1);
     int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
-    int max_chunks = 1;
-    int trot = 0, wrot = 0;
-    int last_user[2] = {-1, -1};   // the last op whose image sat in each buffer
-    int buf = 1;
+    // LDS: the image arena takes what the partial sums and the op table leave
+    const size_t fixed = 16 + (size_t)PG_SLOTS * PG_MAX_TILES * K * NC * TILE_ROWS * 4 + (size_t)n_ops * sizeof(ProgOp);
+    int max_img = 0;
+    for (int i = 0; i < n_ops; ++i)
+        max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * IMG_CHUNK);
+    const size_t budget = program_dynamic_lds(K);
+    if (fixed + (size_t)max_img > budget)
+        return RBQ_ERR_UNSUPPORTED;
+    const int arena = (int)((budget - fixed) / 16 * 16);
+    // Images go into the arena one after another, wrapping to 0 when one
+    // would pass its end.  An op is built only once every earlier op whose
+    // image shares bytes with its own is finished (free_after).
+    struct Placed { int op, lo, hi; };
+    std::vector<Placed> live;   // images placed so far, oldest first, with their byte ranges
+    int trot = 0, wrot = 0, next_off = 0, prev_off = 0;
     for (int i = 0; i < n_ops; ++i) {
         const rbq_program_op &o = ops[i];
         ProgOp &p = d[i];
@@ -824,48 +881,57 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         p.y = o.y;
         p.out = o.out_features;
         p.in = o.in_features;
-        p.wait_for = o.wait_for;
+        p.wait_for = (int16_t)o.wait_for;
         p.flags = flags[i];
-        p.tiles = (o.out_features + TILE_ROWS - 1) / TILE_ROWS;
-        p.nchunks = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+        const int tiles = (o.out_features + TILE_ROWS - 1) / TILE_ROWS;
+        const int base = tiles / G, extra = tiles % G;
+        p.split = (uint32_t)base | ((uint32_t)extra << 8);
+        const int nch = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
+        p.magic = ((1u << 21) + nch - 1) / nch;
         p.trot = trot;
         // an op that reads the same x as the one before (and no op writes it)
-        // takes that op's image; otherwise its image goes to the other buffer
+        // takes that op's image
         const bool same = i > 0 && o.x == ops[i - 1].x && o.in_features == ops[i - 1].in_features &&
                           !(flags[i] & PF_X_SHARED) && !(flags[i - 1] & PF_X_SHARED);
+        int off;
         if (same) {
             p.flags |= PF_REUSE;
             p.free_after = -1;
+            off = prev_off;
+            live.back().op = i;   // the image is in use until this op
         } else {
-            buf ^= 1;
-            p.free_after = last_user[buf];
+            const int size = nch * IMG_CHUNK;
+            off = next_off + size <= arena ? next_off : 0;
+            int fa = -1;
+            for (const Placed &q : live)
+                if (q.lo < off + size && off < q.hi)
+                    fa = std::max(fa, q.op);
+            p.free_after = (int16_t)fa;
+            live.push_back({i, off, off + size});
+            next_off = off + size;
         }
-        last_user[buf] = i;
-        if (buf)
-            p.flags |= PF_BUF1;
+        prev_off = off;
+        p.nch_img = (uint32_t)nch | ((uint32_t)(off / 16) << 8);
         p.flags |= (uint32_t)wrot << PF_WROT_SHIFT;
-        max_chunks = std::max(max_chunks, p.nchunks);
-        trot = (trot + p.tiles % G) % G;
-        wrot = (wrot + ((p.tiles + G - 1) / G) * p.nchunks) % PG_STREAM;
+        trot = (trot + extra) % G;
+        wrot = (wrot + ((tiles + G - 1) / G) * nch) % PG_STREAM;
         for (int bb = 0; bb < G; ++bb) {
             int t0, ntl;
-            op_tiles(p.tiles, p.trot, bb, G, t0, ntl);
+            op_tiles(base, extra, p.trot, bb, G, t0, ntl);
             for (int s = 0; s < PG_STREAM; ++s) {
                 int u0, u1;
-                op_units(ntl * p.nchunks, (int)((p.flags >> PF_WROT_SHIFT) & 15u), s, u0, u1);
+                op_units(ntl * nch, (int)((p.flags >> PF_WROT_SHIFT) & 15u), s, u0, u1);
                 wu[bb * PG_STREAM + s] += u1 - u0;
             }
         }
     }
-    const size_t lds = std::max(PG_MIN_LDS, (size_t)2 * max_chunks * IMG_CHUNK + 16 +
-                                                (size_t)2 * PG_MAX_TILES * K * NC * TILE_ROWS * 4 +
-                                                (size_t)n_ops * sizeof(ProgOp));
+    const size_t lds = std::max(PG_MIN_LDS, fixed + (size_t)arena);
     h->magic = PG_MAGIC;
     h->n_ops = n_ops;
     h->K = K;
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
-    h->max_chunks = max_chunks;
+    h->arena_bytes = arena;
     h->checksum = image_checksum(img, image_bytes(n_ops, G));
     return RBQ_OK;
 }
@@ -881,6 +947,9 @@ rbq_status program_check(const void *image) {
         return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
+    // never launch a layout that would not fit the compute unit's LDS
+    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K))
+        return RBQ_ERR_UNSUPPORTED;
     return RBQ_OK;
 }
 
