@@ -660,11 +660,16 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         };
 
         v4i acc[K][8];
+        uint32_t tprev[K][4];
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < K; ++k) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 acc[k][j] = (v4i){0, 0, 0, 0};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                tprev[k][v] = 0u;
+        }
 
         v4u ring[RING][K];
 #pragma unroll
@@ -701,26 +706,26 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
                         asm volatile("" : "+v"(acc[k][j]));
-                if (li < NC) {
-                    int *rp = red0 + par * RED_OP + ctile * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
-#pragma unroll
-                    for (int k = 0; k < K; ++k)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            uint32_t t = (uint32_t)acc[k][0][v];
-#pragma unroll
-                            for (int q = 1; q < 7; ++q)
-                                t = (t << 1) + (uint32_t)acc[k][q][v];
-                            t = (t << 1) - (uint32_t)acc[k][7][v];
-                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)t, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-                        }
-                }
+                // The accumulators are never cleared: T is linear in them, so
+                // the tile's share is T now less T at the previous flush, all
+                // modulo 2^32 (the int32 sums wrap; the share stays below
+                // 2^29).  That saves clearing 64 registers per flush.
+                int *rp = red0 + par * RED_OP + ctile * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
 #pragma unroll
                 for (int k = 0; k < K; ++k)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        acc[k][j] = (v4i){0, 0, 0, 0};
+                    for (int v = 0; v < 4; ++v) {
+                        uint32_t t = (uint32_t)acc[k][0][v];
+#pragma unroll
+                        for (int q = 1; q < 7; ++q)
+                            t = (t << 1) + (uint32_t)acc[k][q][v];
+                        t = (t << 1) - (uint32_t)acc[k][7][v];
+                        const uint32_t share = t - tprev[k][v];
+                        tprev[k][v] = t;
+                        if (li < NC)
+                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)share, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
             }
             if (tile_end) {
                 cchunk = 0;
@@ -925,6 +930,12 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             }
         }
     }
+    // Each MFMA adds at most 64 * 128 * 128 = 2^20 in magnitude to an int32
+    // accumulator, and the stream waves never clear theirs during a run: up
+    // to 2^11 units per wave keeps every sum below 2^31.
+    for (int q = 0; q < G * PG_STREAM; ++q)
+        if (wu[q] >= (1 << 11))
+            return RBQ_ERR_UNSUPPORTED;
     const size_t lds = std::max(PG_MIN_LDS, fixed + (size_t)arena);
     h->magic = PG_MAGIC;
     h->n_ops = n_ops;
