@@ -1,33 +1,43 @@
 """Benchmark: K=2 batch-1 GEMV on the Llama-2-7B decoder linears.
 
 One step is one decode token through the seven linears (q, k, v, o 4096x4096;
-gate, up 11008x4096; down 4096x11008) of each of 32 layers, captured once in
-a HIP graph and replayed.  By default q, k, v are stacked row-wise into one
-12288x4096 matrix and gate, up into one 22016x4096 matrix, as decode engines
-lay them out (4 rbq_gemv launches per layer, 128 per step; every row is
-encoded on its own, so the stacked encoding is exactly the separate ones);
---layout separate runs the 7 linears as 224 launches.  Each layer has its own
-copy of the encoded planes and scales (1.63 GB in total, far more than the
-L2 and Infinity Cache), so every step streams the weights from HBM.  The
-weights are seeded synthetic N(0, 0.02^2) matrices with 0.1 % outliers x20,
-encoded on the GPU by rbq_encode; activations are N(0, 1) fp16.
+gate, up 11008x4096; down 4096x11008) of each of 32 layers.  By default q, k,
+v are stacked row-wise into one 12288x4096 matrix and gate, up into one
+22016x4096 matrix, as decode engines lay them out (4 GEMVs per layer, 128 per
+step; every row is encoded on its own, so the stacked encoding is exactly the
+separate ones); --layout separate runs the 7 linears as 224 GEMVs.  Each
+layer has its own copy of the encoded planes and scales (1.63 GB in total,
+far more than the L2 and Infinity Cache), so every step streams the weights
+from HBM.  Each GEMV reads the token of its decoder-layer input (one per
+layer for the attention input, o_proj, the MLP input and down_proj; q/k/v
+and gate/up share theirs) and writes its own output.  The weights are seeded
+synthetic N(0, 0.02^2) matrices with 0.1 % outliers x20, encoded on the GPU
+by rbq_encode; activations are N(0, 1) fp16.
+
+The step runs as ONE persistent launch (rbq_program_run over the step's
+GEMVs); the same step as one rbq_gemv launch per GEMV in a HIP graph is
+reported beside it.
 
 Reported (one JSON line):
   value      whole-job GB/s = algorithmic bytes per step / wall time per step
              (bytes = K*out*in/8 planes + 2*K*out scales + 2*in x + 2*out y)
-  roofline   the GEMV kernel alone: algorithmic bytes per launch / its mean
-             device duration, from HIP events around each launch on the
-             library's stream, against MI355X's 8 TB/s HBM peak
-  cpu_baseline  the CPU oracle on the host cores on a bounded sample
-  encode     rbq_encode of the seven linears (GB/s over W read + planes and
-             scales written)
-  refit      rbq_refit of the seven linears (GB/s over W and planes read,
-             scales read and written); on the 13B g128 set both are timed
-             per distinct shape
-  encode_refit_per_shape  per distinct shape, one matrix at a time (W
-             rotated over copies larger than the caches): encoder, refit,
-             re-binarization (GB/s over W and scales read, planes written)
-             and, on the decode workload, the dual-scale encoder
+  roofline   the program kernel: algorithmic bytes per launch / its mean
+             device duration (HIP events around back-to-back launches on its
+             stream), against MI355X's 8 TB/s HBM peak; traffic from
+             FETCH_SIZE + WRITE_SIZE counters when recorded for this source
+  cpu_baseline  the CPU oracle on the host cores on a bounded sample, and on
+             one thread
+  launches   the step as per-GEMV launches; per launch group its mean launch
+             time and a streaming read of the same plane bytes (rbq_probe_read)
+  read_probe the step's plane bytes read as per-matrix launches and as one
+  decode_layer_chain  the 32 layers chained (each GEMV reads the previous
+             one's output; gate/up with the SiLU-mul epilogue), as one
+             program launch and as per-GEMV launches
+  encode / refit / encode_refit_per_shape / gemv_dual_per_shape  the other
+             entry points on the same shapes
+  other_workloads  skinny M=4 and M=16, Llama-2-13B K=4 g128 and the
+             Llama-3-8B prefill set (--no-extra skips them; --workload runs
+             one of them on its own line)
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -47,6 +57,14 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "K=2 batch-1 GEMV effective GB/s and % HBM peak on Llama-2-7B layers"
+DTYPE_INT8_LIMBS = ("i8x3: x as three int8 limbs of a 22-bit fixed-point value, sign bits as int8 0/1, "
+                    "exact int32 accumulation")
+
+
+def dtype_of(path_name):
+    if path_name in ("prefill", "split"):
+        return "f16 MFMA, f32 accumulation"
+    return "f32" if path_name == "valu" else DTYPE_INT8_LIMBS
 
 
 def gemv_bytes(out_f, in_f, K, G, M=1):
@@ -75,6 +93,8 @@ def parse():
                     choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
     ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave the skinny, 13B g128 and prefill sets out of the decode line")
     ap.add_argument("--encode-counter-pass", action="store_true",
                     help="for hardware-counter runs: encoder launches on the Llama-2-7B (K=2) and "
                          "Llama-2-13B g128 (K=4) shapes, each after a cache-flushing copy, then exit")
@@ -112,10 +132,10 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
                                "gemv_llama2_7b_decode_hbm_traffic.json")
 
 
-def measured_traffic(shape_key, path_name):
-    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a copy
-    of known size) recorded for this shape, or None when there is no record or
-    the kernel's source has changed since the counters were taken."""
+def profile_entry(shape_key, kernel_prefix):
+    """The recorded counter entry for this launch (shape key and kernel name
+    prefix), or None when there is none or the kernel's source has changed
+    since it was taken."""
     import hashlib
     try:
         with open(TRAFFIC_PROFILE) as f:
@@ -123,7 +143,7 @@ def measured_traffic(shape_key, path_name):
     except (OSError, ValueError):
         return None
     for e in doc.get("entries", []):
-        if e["shape"] != shape_key or not e["kernel"].startswith(f"gemm_{path_name}_kernel"):
+        if e["shape"] != shape_key or not e["kernel"].startswith(kernel_prefix):
             continue
         src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gemm_rbq_encode_amd", "csrc",
                            e["source"])
@@ -132,15 +152,30 @@ def measured_traffic(shape_key, path_name):
                 digest = hashlib.sha256(f.read()).hexdigest()
         except OSError:
             return None
-        return e["traffic_bytes"] if digest == e["source_sha256"] else None
+        return e if digest == e["source_sha256"] else None
     return None
 
 
+def measured_traffic(shape_key, kernel_prefix):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a copy
+    of known size) recorded for this launch, or None."""
+    e = profile_entry(shape_key, kernel_prefix)
+    return None if e is None else e.get("traffic_bytes")
+
+
+def rocprof_mean_us(shape_key, kernel_prefix="gemv_program_kernel"):
+    """Mean kernel duration (us) in the recorded rocprofv3 kernel trace of the
+    default benchmark run, or None."""
+    e = profile_entry(shape_key, kernel_prefix)
+    return None if e is None else e.get("rocprof_mean_us")
+
+
 def counter_pass(args):
-    """Launches for `rocprofv3 --pmc`: each fused decode shape of the
-    Llama-2-7B layer 8 times through rbq_gemv (rotating 8 encoded copies, so
-    no launch finds its planes in a cache), then torch copies of a 256 MiB
-    buffer, whose read bytes calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    """Launches for `rocprofv3 --pmc`: the decode step's program (as the
+    benchmark builds it) three times, then each fused decode shape 8 times
+    through rbq_gemv (rotating the layers' copies, so no launch finds its
+    planes in a cache), then torch copies of a 256 MiB buffer, whose read and
+    write bytes calibrate the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
 
     import gemm_rbq_encode_amd as rbq
@@ -149,19 +184,28 @@ def counter_pass(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = workloads.WORKLOADS["llama2_7b"]
-    K = wl.num_planes
-    for out_f, in_f in ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008)):
-        g = torch.Generator(device="cpu").manual_seed(out_f * 31 + in_f)
-        W = (torch.randn((out_f, in_f), generator=g) * 0.02).to(dev)
-        p, sc = rbq.encode(W, K, 0)
-        del W
-        copies = [(p.clone(), sc.clone()) for _ in range(8)]
-        x = torch.from_numpy(workloads.workload_activations(wl, in_f, 1).view(np.float16)).to(dev)[0]
-        for pp, ss in copies:
-            rbq.gemv(pp, ss, x)
+    K, group = wl.num_planes, wl.group_size
+    groups, layers, shapes, widths, Ws, _, _ = decode_sets(torch, rbq, workloads, wl, dev, args.layout,
+                                                           args.layers)
+    del Ws
+    xs = decode_activations(torch, workloads, wl, dev, args.layout, widths, args.layers)
+    ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes]
+          for _ in range(args.layers)]
+    ops = [{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
+           for l in range(args.layers) for i in range(len(groups))]
+    prog = rbq.Program(ops, num_planes=K)
+    nbytes = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) * args.layers
+    for _ in range(3):
+        prog.run()
+    torch.cuda.synchronize()
+    print(f"counter pass: program_{args.layout}_{args.layers}layers x3 ({len(ops)} ops, "
+          f"{nbytes} algorithmic bytes per launch)", flush=True)
+    for i, sh in enumerate(shapes):
+        for l in range(min(8, args.layers)):
+            rbq.gemv(layers[l][i][0], layers[l][i][1], xs[l][i], group, y=ys[l][i])
         torch.cuda.synchronize()
-        print(f"counter pass: {out_f}x{in_f} x8 "
-              f"({gemv_bytes(out_f, in_f, K, 1)} algorithmic bytes per launch)", flush=True)
+        print(f"counter pass: {sh.out_features}x{sh.in_features} x{min(8, args.layers)} "
+              f"({gemv_bytes(sh.out_features, sh.in_features, K, 1)} algorithmic bytes per launch)", flush=True)
     src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(4):
@@ -257,66 +301,7 @@ def graph_ms(torch, dev, fns, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, xs, K, group):
-    """The same 32 layers as a chained decoder step: q/k/v on x, o on q
-    (the attention between them is outside this library), gate/up with the
-    silu(gate) * up epilogue on rows interleaved as (gate, up) pairs, down on
-    its output h.  Each launch reads what the one before it wrote, as in
-    decoding.  One HIP graph per step; reports ms and GB/s over the same
-    algorithmic bytes (h is written once at half the gate/up rows)."""
-    n_ff = shapes[2].out_features // 2
-    perm = torch.stack([torch.arange(n_ff), torch.arange(n_ff) + n_ff], dim=1).reshape(-1).to(dev)
-    gu = [(p.index_select(1, perm).contiguous(), s.index_select(1, perm).contiguous())
-          for p, s in (layer[2] for layer in layers)]
-    x = xs[shapes[0].in_features]
-    qkv = torch.empty(shapes[0].out_features, dtype=torch.float16, device=dev)
-    o = torch.empty(shapes[1].out_features, dtype=torch.float16, device=dev)
-    h = torch.empty(n_ff, dtype=torch.float16, device=dev)
-    y = torch.empty(shapes[3].out_features, dtype=torch.float16, device=dev)
-
-    def step(st):
-        for layer, (gp, gs) in zip(layers, gu):
-            rcs = (L.rbq_gemv(layer[0][0].data_ptr(), layer[0][1].data_ptr(), shapes[0], x.data_ptr(),
-                              qkv.data_ptr(), st),
-                   L.rbq_gemv(layer[1][0].data_ptr(), layer[1][1].data_ptr(), shapes[1], qkv.data_ptr(),
-                              o.data_ptr(), st),
-                   L.rbq_gemm_ex(gp.data_ptr(), gs.data_ptr(), shapes[2], x.data_ptr(), 1, h.data_ptr(),
-                                 None, 0, rbq.RBQ_EPILOGUE_SILU_MUL, st),
-                   L.rbq_gemv(layer[3][0].data_ptr(), layer[3][1].data_ptr(), shapes[3], h.data_ptr(),
-                              y.data_ptr(), st))
-            if any(rcs):
-                raise rbq.RbqError(max(rcs), "decode layer chain")
-
-    stream = torch.cuda.current_stream(dev)
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step(side.cuda_stream)
-    side.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        step(torch.cuda.current_stream(dev).cuda_stream)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    per_layer = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) - 2 * n_ff
-    del graph, gu
-    return {"layers": len(layers), "ms_per_step": round(ms, 4),
-            "GBps": round(per_layer * len(layers) / (ms * 1e-3) / 1e9, 1),
-            "launches_per_layer": 4, "epilogue": "silu(gate)*up in the gate/up launch"}
-
-
 def bench_layer_set(args):
-    """Skinny, grouped-scale and prefill workloads: each linear of the set is
-    run back to back (one launch each) over a rotation of encoded copies;
-    reports algorithmic GB/s (decode-like sets) or dense-equivalent TFLOP/s
-    (prefill), and the per-launch device time from HIP events."""
     import torch
 
     import gemm_rbq_encode_amd as rbq
@@ -324,22 +309,38 @@ def bench_layer_set(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.WORKLOADS[args.workload]
+    print(json.dumps(measure_layer_set(args, args.workload, args.tokens, torch, rbq, workloads, dev)), flush=True)
+
+
+def measure_layer_set(args, workload, tokens, torch, rbq, workloads, dev, with_prep=True, cpu_seconds=None):
+    """Skinny, grouped-scale and prefill workloads: each linear of the set is
+    run back to back (one launch each) over a rotation of encoded copies;
+    reports algorithmic GB/s (decode-like sets) or dense-equivalent TFLOP/s
+    (prefill), the per-launch device time from HIP events, and the CPU
+    oracle on a bounded sample.  Returns the JSON line as a dict."""
+    wl = workloads.WORKLOADS[workload]
     K, group = wl.num_planes, wl.group_size
-    M = args.tokens or max(wl.tokens)
+    M = tokens or max(wl.tokens)
     stream = torch.cuda.current_stream(dev)
     # distinct shapes only (q/k/v/o and gate/up share shapes)
     uniq = []
     for i, lin in enumerate(wl.linears):
         if all((lin.out_features, lin.in_features) != (l.out_features, l.in_features) for _, l in uniq):
             uniq.append((i, lin))
-    prefill = args.workload == "llama3_8b_prefill"
+    prefill = workload == "llama3_8b_prefill"
     rot = 2 if prefill else max(2, int(2.0e9 // sum(
         K * l.out_features * l.in_features // 8 for _, l in uniq)))
     sets, prep = [], {}
     for i, lin in uniq:
         W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
         p, sc = rbq.encode(W, K, group)
+        X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
+        Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
+        copies = [(p.clone(), sc.clone()) for _ in range(rot)]
+        sets.append((lin, copies, X, Y))
+        if not with_prep:
+            del W
+            continue
         # encoder and refit time of this shape (outputs rewritten in place)
         key = f"{lin.out_features}x{lin.in_features}"
         pe, se, sr = torch.empty_like(p), torch.empty_like(sc), sc.clone()
@@ -360,10 +361,6 @@ def bench_layer_set(args):
                      "rebinarize_GBps": round((wb + pb + sb) / (rb_ms * 1e-3) / 1e9, 1)}
         del pe, se, sr, pr
         del W
-        X = torch.from_numpy(workloads.workload_activations(wl, lin.in_features, M).view(np.float16)).to(dev)
-        Y = torch.empty((M, lin.out_features), dtype=torch.float16, device=dev)
-        copies = [(p.clone(), sc.clone()) for _ in range(rot)]
-        sets.append((lin, copies, X, Y))
     torch.cuda.synchronize()
     forced = {"auto": rbq.PATH_AUTO, "valu": rbq.PATH_VALU, "decode": rbq.PATH_DECODE,
               "stream": rbq.PATH_STREAM, "flat": rbq.PATH_FLAT, "group": rbq.PATH_GROUP,
@@ -436,7 +433,7 @@ def bench_layer_set(args):
     line = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f16" if names[path] in ("prefill", "split") else ("i8" if names[path] != "valu" else "f32"),
+            "dtype": dtype_of(names[path]),
             "data": "synthetic",
             "config": {"workload": wl.name, "linears": [f"{l.out_features}x{l.in_features}" for _, l in uniq],
                        "num_planes": K, "group_size": group, "tokens": M, "rotation": rot,
@@ -448,7 +445,222 @@ def bench_layer_set(args):
             "roofline": roof, "cpu_baseline": None}
     if prep:
         line["encode_refit_per_shape"] = prep
-    print(json.dumps(line), flush=True)
+    budget = args.cpu_seconds if cpu_seconds is None else cpu_seconds
+    if budget > 0:
+        # the oracle on the first copy of each shape; prefill on 16 of the tokens
+        m_cpu = min(M, 16)
+        samples = []
+        for lin, copies, X, _ in sets:
+            G = lin.in_features // group if group else 1
+            work = 2.0 * m_cpu * lin.out_features * lin.in_features if prefill else \
+                gemv_bytes(lin.out_features, lin.in_features, K, G, m_cpu)
+            samples.append((copies[0][0].cpu().numpy().view(np.uint32), copies[0][1].cpu().numpy().view(np.uint16),
+                            X[:m_cpu].cpu().numpy().view(np.uint16), group, work))
+        line["cpu_baseline"] = oracle_baseline(samples, budget, unit="TFLOP/s" if prefill else "GB/s",
+                                               max_reps=20)
+        line["cpu_baseline"]["sample"] = (f"one copy of each shape at {m_cpu} token(s): "
+                                          + line["cpu_baseline"]["sample"])
+    for _, copies, X, Y in sets:
+        del copies[:]
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return line
+
+
+X_SLOTS = {"fused": (0, 1, 2, 3), "separate": (0, 0, 0, 1, 2, 2, 3)}
+
+
+def event_launch_us(torch, fn, stream, reps):
+    """Mean device time (us) of one launch of `fn`: `reps` launches back to
+    back between two HIP events recorded on `stream`, the stream it
+    launches on."""
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def oracle_baseline(samples, seconds, unit="GB/s", max_reps=50):
+    """The CPU oracle (fp64 dequantize-and-multiply) over `samples`, a list of
+    (planes, scales, X, group_size, work) with work in algorithmic bytes
+    (unit GB/s) or dense-equivalent flops (unit TFLOP/s), repeated for about
+    `seconds`, with all its threads and then with one thread for a third of
+    that time.  Returns the cpu_baseline object."""
+    import oracle
+
+    def run(budget):
+        t0 = time.perf_counter()
+        done, reps = 0, 0
+        while True:
+            for p, s, X, g, nb in samples:
+                oracle.gemm(p, s, X, g)
+                done += nb
+            reps += 1
+            if time.perf_counter() - t0 >= budget or reps >= max_reps:
+                return done, reps, time.perf_counter() - t0
+
+    cores = oracle.num_threads()
+    done, reps, el = run(seconds)
+    oracle.set_num_threads(1)
+    try:
+        done1, reps1, el1 = run(seconds / 3)
+    finally:
+        oracle.set_num_threads(cores)
+    div = 1e12 if unit == "TFLOP/s" else 1e9
+    return {"value": round(done / el / div, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "single_thread_value": round(done1 / el1 / div, 6),
+            "sample": f"{reps} pass(es) over {len(samples)} linear(s) in {el:.1f} s on {cores} threads, "
+                      f"{reps1} in {el1:.1f} s on 1 thread (fp64 dequantize-and-multiply)"}
+
+
+def decode_sets(torch, rbq, workloads, wl, dev, layout, n_layers):
+    """The decode step's weights: the seven Llama-2-7B linears drawn from the
+    seeded generator and encoded on the GPU, grouped by layout ("fused"
+    stacks q/k/v and gate/up row-wise; rows are encoded independently, so the
+    stacked planes and scales are exactly the separate ones placed one after
+    another), and one copy per layer.  Returns (groups, layers, shapes,
+    widths, Ws, planes, scales) with layers[l][i] = (planes, scales)."""
+    K, group = wl.num_planes, wl.group_size
+    Ws, enc_planes, enc_scales = [], [], []
+    for i, _ in enumerate(wl.linears):
+        W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
+        p, s = rbq.encode(W, K, group)
+        Ws.append(W)
+        enc_planes.append(p)
+        enc_scales.append(s)
+    if layout == "fused":
+        groups = [("qkv_proj", [0, 1, 2]), ("o_proj", [3]), ("gate_up_proj", [4, 5]), ("down_proj", [6])]
+    else:
+        groups = [(lin.name, [i]) for i, lin in enumerate(wl.linears)]
+    g_planes, g_scales, shapes, widths = [], [], [], []
+    for _, idx in groups:
+        p = torch.cat([enc_planes[i] for i in idx], dim=1).contiguous()
+        s = torch.cat([enc_scales[i] for i in idx], dim=1).contiguous()
+        g_planes.append(p)
+        g_scales.append(s)
+        shapes.append(rbq.shape(p.shape[1], p.shape[2] * 32, K, group))
+        widths.append(p.shape[2] * 32)
+    layers = [[(p.clone(), s.clone()) for p, s in zip(g_planes, g_scales)] for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    return groups, layers, shapes, widths, Ws, enc_planes, enc_scales
+
+
+def decode_activations(torch, workloads, wl, dev, layout, widths, n_layers):
+    """xs[l][i]: the fp16 token that launch group i of layer l reads (one
+    buffer per decoder-layer input, shared only by q/k/v and by gate/up as in
+    a decoder)."""
+    slots = X_SLOTS[layout]
+    width_of = {}
+    for i, sl in enumerate(slots):
+        width_of[sl] = widths[i]
+    per_slot = {sl: torch.from_numpy(workloads.layer_activations(wl, n, n_layers, sl).view(np.float16)).to(dev)
+                for sl, n in width_of.items()}
+    return [[per_slot[sl][l] for sl in slots] for l in range(n_layers)]
+
+
+def chain_buffers(torch, dev, layers, shapes, x):
+    """Interleaved (gate, up) row pairs for the SiLU-mul epilogue, and the
+    activation buffers of a chained decoder step."""
+    n_ff = shapes[2].out_features // 2
+    perm = torch.stack([torch.arange(n_ff), torch.arange(n_ff) + n_ff], dim=1).reshape(-1).to(dev)
+    gu = [(p.index_select(1, perm).contiguous(), s.index_select(1, perm).contiguous())
+          for p, s in (layer[2] for layer in layers)]
+    bufs = {"x": x,
+            "qkv": torch.empty(shapes[0].out_features, dtype=torch.float16, device=dev),
+            "o": torch.empty(shapes[1].out_features, dtype=torch.float16, device=dev),
+            "h": torch.empty(n_ff, dtype=torch.float16, device=dev),
+            "y": torch.empty(shapes[3].out_features, dtype=torch.float16, device=dev)}
+    return gu, bufs, n_ff
+
+
+def chain_program_ops(rbq, layers, gu, bufs, n_q):
+    """A chained decoder step as program ops: q/k/v on the layer input (x,
+    then the previous layer's down output), o on q (the attention between
+    them is outside this library), gate/up with the SiLU-mul epilogue on o's
+    output, down on h; each op waits for the one before it."""
+    ops = []
+    for l, layer in enumerate(layers):
+        ops.append({"planes": layer[0][0], "scales": layer[0][1], "x": bufs["x"] if l == 0 else bufs["y"],
+                    "y": bufs["qkv"], "wait_for": len(ops) - 1})
+        ops.append({"planes": layer[1][0], "scales": layer[1][1], "x": bufs["qkv"][:n_q], "y": bufs["o"],
+                    "wait_for": len(ops) - 1})
+        ops.append({"planes": gu[l][0], "scales": gu[l][1], "x": bufs["o"], "y": bufs["h"],
+                    "epilogue": rbq.RBQ_EPILOGUE_SILU_MUL, "wait_for": len(ops) - 1})
+        ops.append({"planes": layer[3][0], "scales": layer[3][1], "x": bufs["h"], "y": bufs["y"],
+                    "wait_for": len(ops) - 1})
+    return ops
+
+
+def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
+    """The 32 layers as a chained decoder step (chain_program_ops' order and
+    dependencies), once as one program launch and once as 4 launches per
+    layer in a HIP graph.  Reports ms and GB/s over the same algorithmic
+    bytes (h is written once at half the gate/up rows)."""
+    gu, bufs, n_ff = chain_buffers(torch, dev, layers, shapes, x)
+    n_q = shapes[1].in_features
+    per_layer = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) - 2 * n_ff
+    total = per_layer * len(layers)
+    stream = torch.cuda.current_stream(dev)
+
+    def launches(st):
+        for l, (layer, (gp, gs)) in enumerate(zip(layers, gu)):
+            xin = bufs["x"] if l == 0 else bufs["y"]
+            rcs = (L.rbq_gemv(layer[0][0].data_ptr(), layer[0][1].data_ptr(), shapes[0], xin.data_ptr(),
+                              bufs["qkv"].data_ptr(), st),
+                   L.rbq_gemv(layer[1][0].data_ptr(), layer[1][1].data_ptr(), shapes[1], bufs["qkv"].data_ptr(),
+                              bufs["o"].data_ptr(), st),
+                   L.rbq_gemm_ex(gp.data_ptr(), gs.data_ptr(), shapes[2], bufs["o"].data_ptr(), 1,
+                                 bufs["h"].data_ptr(), None, 0, rbq.RBQ_EPILOGUE_SILU_MUL, st),
+                   L.rbq_gemv(layer[3][0].data_ptr(), layer[3][1].data_ptr(), shapes[3], bufs["h"].data_ptr(),
+                              bufs["y"].data_ptr(), st))
+            if any(rcs):
+                raise rbq.RbqError(max(rcs), "decode layer chain")
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launches(side.cuda_stream)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        launches(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+
+    def wall_ms(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+
+    ms_launch = wall_ms(graph.replay)
+    y_launch = bufs["y"].clone()
+    del graph
+    prog = rbq.Program(chain_program_ops(rbq, layers, gu, bufs, n_q), num_planes=K)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms_prog = wall_ms(lambda: prog.run(status))
+    torch.cuda.synchronize()
+    st = int(status.item())
+    if st:
+        raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"decode chain program status {st:#x}")
+    same = bool(torch.equal(bufs["y"], y_launch))
+    del prog, gu
+    return {"layers": len(layers), "ops_per_layer": 4, "bytes_per_step": total,
+            "program": {"ms_per_step": round(ms_prog, 4), "GBps": round(total / (ms_prog * 1e-3) / 1e9, 1)},
+            "launches": {"ms_per_step": round(ms_launch, 4), "GBps": round(total / (ms_launch * 1e-3) / 1e9, 1),
+                         "graph": True},
+            "program_output_equals_launches": same,
+            "epilogue": "silu(gate)*up in the gate/up op"}
 
 
 def bench_decode(args):
@@ -467,52 +679,25 @@ def bench_decode(args):
             "group": rbq.PATH_GROUP, "split": rbq.PATH_SPLIT}[args.path]
     rbq.set_path(path)
     rbq.set_stream_split(args.split)
-
-    # ---- weights: layer 0 from the seeded generator, encoded on the GPU
     stream = torch.cuda.current_stream(dev)
-    enc_planes, enc_scales, enc_bytes, Ws = [], [], 0, []
-    for i, lin in enumerate(wl.linears):
-        W = torch.from_numpy(workloads.workload_weight(wl, i)).to(dev)
-        p, s = rbq.encode(W, K, group)
-        Ws.append(W)
-        enc_planes.append(p)
-        enc_scales.append(s)
-        enc_bytes += 4 * W.numel() + p.numel() * 4 + s.numel() * 2
-    torch.cuda.synchronize()
-    # encoder time: the seven encodes (outputs rewritten in place) captured in
-    # one HIP graph, replayed back to back
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    enc_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(enc_graph, stream=side):
-        for W, p, s in zip(Ws, enc_planes, enc_scales):
-            rbq.encode(W, K, group, planes=p, scales=s)
-    torch.cuda.synchronize()
-    enc_graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    enc_reps = 5
-    e0.record(stream)
-    for _ in range(enc_reps):
-        enc_graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    enc_ms = e0.elapsed_time(e1) / enc_reps
-    del enc_graph
-    # refit time: the seven refits (into copies of the scales) in one graph
+
+    groups, layers, shapes, widths, Ws, enc_planes, enc_scales = decode_sets(
+        torch, rbq, workloads, wl, dev, args.layout, args.layers)
+
+    # ---- encoder, refit and re-binarization per distinct shape, dual encoder
+    enc_bytes = sum(4 * W.numel() + 4 * p.numel() + 2 * s.numel() for W, p, s in zip(Ws, enc_planes, enc_scales))
+    enc_ms = graph_ms(torch, dev, [(lambda W=W, p=p, s=s: rbq.encode(W, K, group, planes=p, scales=s))
+                                   for W, p, s in zip(Ws, enc_planes, enc_scales)], 5)
     ref_scales = [s.clone() for s in enc_scales]
-    ref_bytes = sum(4 * W.numel() + p.numel() * 4 + 4 * s.numel()
-                    for W, p, s in zip(Ws, enc_planes, ref_scales))
+    ref_bytes = sum(4 * W.numel() + p.numel() * 4 + 4 * s.numel() for W, p, s in zip(Ws, enc_planes, ref_scales))
     ref_ms = graph_ms(torch, dev, [(lambda W=W, p=p, s=s: rbq.refit(W, p, s, group))
                                    for W, p, s in zip(Ws, enc_planes, ref_scales)], 5)
-    # per distinct shape: encoder and refit time of one matrix
     prep = {}
     for W, p, s in zip(Ws, enc_planes, enc_scales):
         key = f"{W.shape[0]}x{W.shape[1]}"
         if key in prep:
             continue
         pe, se, sr = torch.empty_like(p), torch.empty_like(s), s.clone()
-        # one call per copy of W (copies exceed the caches), three replays
         Wc = rotation_copies(W)
         e_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.encode(Wi, K, group, planes=pe, scales=se))
                                      for Wi in Wc], 3) / len(Wc)
@@ -521,7 +706,6 @@ def bench_decode(args):
         rb_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.rebinarize(Wi, pr, s, group)) for Wi in Wc], 3) / len(Wc)
         del Wc
         wb, pb, sb = 4 * W.numel(), 4 * p.numel(), 2 * s.numel()
-        # dual-scale encoder (residual SVID, 20 alternating steps per plane)
         shp = rbq.shape(W.shape[0], W.shape[1], K, 0)
         wsd = torch.empty(rbq.encode_dual_workspace_bytes(shp), dtype=torch.uint8, device=dev)
         pd = torch.empty_like(p)
@@ -536,78 +720,26 @@ def bench_decode(args):
                      "rebinarize_GBps": round((wb + pb + sb) / (rb_ms * 1e-3) / 1e9, 1),
                      "encode_dual_us": round(d_ms * 1e3, 1)}
         del pe, se, sr, pr, wsd, pd, gd, hd
-    del Ws, ref_scales
+    del Ws, ref_scales, enc_planes, enc_scales
 
-    # ---- launch groups.  "fused" stacks the rows of q, k, v (and of gate, up)
-    # into one matrix: rows are encoded independently, so the stacked planes
-    # and scales are exactly the separate ones placed one after another.
-    if args.layout == "fused":
-        groups = [("qkv_proj", [0, 1, 2]), ("o_proj", [3]), ("gate_up_proj", [4, 5]),
-                  ("down_proj", [6])]
-    else:
-        groups = [(lin.name, [i]) for i, lin in enumerate(wl.linears)]
-    g_planes, g_scales, g_shapes, g_in = [], [], [], []
-    for name, idx in groups:
-        p = torch.cat([enc_planes[i] for i in idx], dim=1).contiguous()
-        s = torch.cat([enc_scales[i] for i in idx], dim=1).contiguous()
-        g_planes.append(p)
-        g_scales.append(s)
-        g_shapes.append(rbq.shape(p.shape[1], p.shape[2] * 32, K, group))
-        g_in.append(p.shape[2] * 32)
-    del enc_planes, enc_scales
-
-    # ---- rotation set: one copy of planes and scales per layer
-    layers = []
-    for layer in range(args.layers):
-        layers.append([(p.clone(), s.clone()) for p, s in zip(g_planes, g_scales)])
-    torch.cuda.synchronize()
-    xs = {}
-    for n_in in g_in:
-        if n_in not in xs:
-            xa = workloads.workload_activations(wl, n_in, 1)
-            xs[n_in] = torch.from_numpy(xa.view(np.float16)[0].copy()).to(dev)
-    ys = [torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in g_shapes]
-
-    shapes = g_shapes
-    per_call = [gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in g_shapes]
+    # ---- the step: every launch group of every layer, each reading its own
+    # activations and writing its own output
+    xs = decode_activations(torch, workloads, wl, dev, args.layout, widths, args.layers)
+    ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes]
+          for _ in range(args.layers)]
+    per_call = [gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes]
     bytes_per_step = sum(per_call) * args.layers
-    calls = []
-    for layer in layers:
-        for i, (p, s) in enumerate(layer):
-            calls.append((p.data_ptr(), s.data_ptr(), shapes[i], xs[g_in[i]].data_ptr(),
-                          ys[i].data_ptr(), i))
-
-    def step(st_handle):
-        for pp, sp, sh, xp, yp, _ in calls:
-            rc = L.rbq_gemv(pp, sp, sh, xp, yp, st_handle)
-            if rc != 0:
-                raise rbq.RbqError(rc, "rbq_gemv")
-
-    names = path_names(rbq)
-    shape_paths = {f"{sh.out_features}x{sh.in_features}":
-                   names[rbq.select_path(sh, 1) if path == rbq.PATH_AUTO else path]
-                   for sh in shapes}
-    path_name = "+".join(sorted(set(shape_paths.values())))
-
-    # ---- whole-job timing: graph replays (or eager steps)
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step(side.cuda_stream)          # warm the kernels before capture
-    side.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            step(torch.cuda.current_stream(dev).cuda_stream)
-        torch.cuda.synchronize()
+    ops = [{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
+           for l in range(args.layers) for i in range(len(groups))]
+    prog = rbq.Program(ops, num_planes=K)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def run_step():
-        if graph is not None:
-            graph.replay()
-        else:
-            step(stream.cuda_stream)
+        prog.run(status)
 
+    # the kernel's own duration first (HIP events around back-to-back
+    # launches on its stream), then the whole-job timing
+    prog_us = event_launch_us(torch, run_step, stream, max(args.steps, 20))
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -618,77 +750,118 @@ def bench_decode(args):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    # (the chain's gate/up epilogue runs in the flat and VALU kernels only)
-    layer_chain = decode_layer_chain(args, torch, rbq, L, dev, layers, g_shapes, xs, K, group) \
-        if args.layout == "fused" and graph is not None and \
-        path in (rbq.PATH_AUTO, rbq.PATH_FLAT, rbq.PATH_VALU) else None
+    if int(status.item()) != 0:
+        raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
+    prog_out = [y.clone() for y in ys[-1]]
 
-    # ---- per-launch device time of each launch group: its launches over all
-    # layers in one graph, replayed between two HIP events on the launch stream
-    nlin = len(groups)
-    mean_us = [0.0] * nlin
-    for i in range(nlin):
-        fns = []
-        for layer in layers:
-            p, s = layer[i]
-            fns.append(lambda pp=p.data_ptr(), sp=s.data_ptr(), sh=shapes[i],
-                       xp=xs[g_in[i]].data_ptr(), yp=ys[i].data_ptr():
-                       L.rbq_gemv(pp, sp, sh, xp, yp, torch.cuda.current_stream(dev).cuda_stream))
-        mean_us[i] = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1) * 4)
-    # the dominant kernel: the launch group with the largest share of a step
-    dom_i = max(range(nlin), key=lambda i: mean_us[i])
-    dom = f"{groups[dom_i][0]} {shapes[dom_i].out_features}x{shapes[dom_i].in_features}"
-    achieved = per_call[dom_i] / (mean_us[dom_i] * 1e-6) / 1e9
-    dom_key = f"{shapes[dom_i].out_features}x{shapes[dom_i].in_features}"
-    tot_us = sum(mean_us)
+    # ---- the same step as one rbq_gemv launch per op, in a HIP graph
+    def launch_step(st):
+        for op in ops:
+            rc = L.rbq_gemv(op["planes"].data_ptr(), op["scales"].data_ptr(),
+                            rbq.shape(op["planes"].shape[1], op["planes"].shape[2] * 32, K, group),
+                            op["x"].data_ptr(), op["y"].data_ptr(), st)
+            if rc != 0:
+                raise rbq.RbqError(rc, "rbq_gemv")
+
+    names = path_names(rbq)
+    shape_paths = {f"{sh.out_features}x{sh.in_features}":
+                   names[rbq.select_path(sh, 1) if path == rbq.PATH_AUTO else path] for sh in shapes}
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch_step(side.cuda_stream)
+    side.synchronize()
+    # the two runs may take different kernel families for a shape, so they
+    # agree to the decode bound rather than bit for bit
+    launch_diff = max(float((a.float() - b.float()).abs().max() / b.float().abs().max().clamp_min(1e-30))
+                      for a, b in zip(prog_out, ys[-1]))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        launch_step(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_launches = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    del graph
+
+    # ---- per launch group: rbq_gemv launch time and a read of the same bytes
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    reps = max(args.kernel_reps, 1) * 4
     per_shape = {}
     for i, (name, _) in enumerate(groups):
+        fns = [(lambda op=ops[l * len(groups) + i]: rbq.gemv(op["planes"], op["scales"], op["x"], group,
+                                                            y=op["y"]))
+               for l in range(args.layers)]
+        us = graph_launch_us(torch, dev, fns, reps)
+        pbufs = [layers[l][i][0] for l in range(args.layers)]
+        pus = graph_launch_us(torch, dev, [(lambda b=b: rbq.probe_read(b, sink)) for b in pbufs], reps)
+        pbytes = pbufs[0].numel() * 4
         per_shape[name] = {"shape": f"{shapes[i].out_features}x{shapes[i].in_features}",
-                           "bytes": per_call[i], "mean_us": round(mean_us[i], 3),
-                           "GBps": round(per_call[i] / (mean_us[i] * 1e-6) / 1e9, 1)}
+                           "bytes": per_call[i], "gemv_us": round(us, 3),
+                           "gemv_GBps": round(per_call[i] / (us * 1e-6) / 1e9, 1),
+                           "read_probe_bytes": pbytes, "read_probe_us": round(pus, 3),
+                           "read_probe_GBps": round(pbytes / (pus * 1e-6) / 1e9, 1),
+                           "gemv_time_over_probe": round(us / pus, 3)}
+    # the whole step's planes read back to back as separate launches, and
+    # the same byte count read by one launch
+    step_bufs = [op["planes"] for op in ops]
+    step_probe_us = graph_launch_us(torch, dev, [(lambda b=b: rbq.probe_read(b, sink)) for b in step_bufs], 2)
+    step_probe_ms = step_probe_us * len(step_bufs) * 1e-3
+    plane_bytes = sum(b.numel() * 4 for b in step_bufs)
+    big = torch.empty(plane_bytes, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    one_us = event_launch_us(torch, lambda: rbq.probe_read(big, sink), stream, 5)
+    del big
+    read_probe = {"step_plane_bytes": plane_bytes,
+                  "per_matrix_launches_GBps": round(plane_bytes / (step_probe_ms * 1e-3) / 1e9, 1),
+                  "one_launch_GBps": round(plane_bytes / (one_us * 1e-6) / 1e9, 1),
+                  "program_time_over_one_launch_read": round(prog_us / one_us, 3)}
 
-    # ---- dual-scale layer y = sum_k g_k (B_k (h_k x)) on the same planes (the
-    # row scales serve as g; h is one input-scale vector per plane and width)
+    # ---- dual-scale layer y = sum_k g_k (B_k (h_k x)) on the same planes
     dual_shape = {}
     hvec = {}
     for i, (name, _) in enumerate(groups):
-        n_in = g_in[i]
+        n_in = widths[i]
         if n_in not in hvec:
             hvec[n_in] = torch.ones((K, n_in), dtype=torch.float16, device=dev)
-        fns = []
-        for layer in layers:
-            p, s = layer[i]
-            fns.append(lambda pp=p.data_ptr(), sp=s.data_ptr(), hp=hvec[n_in].data_ptr(), sh=shapes[i],
-                       xp=xs[n_in].data_ptr(), yp=ys[i].data_ptr():
-                       rbq.check(L.rbq_gemv_dual(pp, sp, hp, sh, xp, yp,
-                                                 torch.cuda.current_stream(dev).cuda_stream), "rbq_gemv_dual"))
-        us = graph_launch_us(torch, dev, fns, max(args.kernel_reps, 1) * 4)
+        fns = [(lambda op=ops[l * len(groups) + i], h=hvec[n_in]:
+                rbq.gemv_dual(op["planes"], op["scales"], h, op["x"], y=op["y"]))
+               for l in range(args.layers)]
+        us = graph_launch_us(torch, dev, fns, reps)
         nb = per_call[i] + 2 * K * n_in
         dual_shape[name] = {"shape": f"{shapes[i].out_features}x{n_in}", "bytes": nb,
                             "mean_us": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
 
-    # ---- CPU oracle baseline on a bounded sample (layer 0, one token)
+    layer_chain = None
+    if args.layout == "fused" and path in (rbq.PATH_AUTO, rbq.PATH_FLAT, rbq.PATH_VALU):
+        layer_chain = decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, xs[0][0], K)
+
     cpu = None
     if args.cpu_seconds > 0:
-        import oracle
-        planes_np = [p.cpu().numpy().view(np.uint32) for p in g_planes]
-        scales_np = [s.cpu().numpy().view(np.uint16) for s in g_scales]
-        xs_np = {k: v.cpu().numpy().view(np.uint16)[None, :] for k, v in xs.items()}
-        t_start = time.perf_counter()
-        done_bytes, reps = 0, 0
-        while True:
-            for i in range(nlin):
-                oracle.gemm(planes_np[i], scales_np[i], xs_np[g_in[i]], group)
-                done_bytes += per_call[i]
-            reps += 1
-            if time.perf_counter() - t_start >= args.cpu_seconds or reps >= 50:
-                break
-        el = time.perf_counter() - t_start
-        cpu = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{reps} pass(es) over the layer-0 linears at M=1 "
-                         f"(fp64 dequantize-and-multiply), {el:.1f} s"}
+        samples = [(layers[0][i][0].cpu().numpy().view(np.uint32), layers[0][i][1].cpu().numpy().view(np.uint16),
+                    xs[0][i].cpu().numpy().view(np.uint16)[None, :], group, per_call[i])
+                   for i in range(len(groups))]
+        cpu = oracle_baseline(samples, args.cpu_seconds)
+        cpu["sample"] = "layer 0 at M=1: " + cpu["sample"]
 
+    others = {}
+    if not args.no_extra:
+        for name, tokens in (("llama2_7b_skinny", 4), ("llama2_7b_skinny", 16), ("llama2_13b_g128", 1),
+                             ("llama3_8b_prefill", 2048)):
+            sub = measure_layer_set(args, name, tokens, torch, rbq, workloads, dev,
+                                    with_prep=name != "llama2_7b_skinny", cpu_seconds=min(args.cpu_seconds, 4.0))
+            others[f"{name}_m{tokens}"] = {k: sub[k] for k in ("metric", "value", "unit", "ms_per_step", "dtype",
+                                                               "config", "roofline", "cpu_baseline")
+                                           if k in sub}
+            if "encode_refit_per_shape" in sub:
+                others[f"{name}_m{tokens}"]["encode_refit_per_shape"] = sub["encode_refit_per_shape"]
+
+    prog_key = f"program_{args.layout}_{args.layers}layers"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -700,25 +873,31 @@ def bench_decode(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if path_name == "valu" else "i8",
+        "dtype": DTYPE_INT8_LIMBS,
         "data": "synthetic",
         "config": {"workload": "llama2_7b_decode_gemv", "layers": args.layers,
                    "linears": [f"{l.name} {l.out_features}x{l.in_features}" for l in wl.linears],
                    "layout": args.layout,
-                   "launches_per_layer": {name: f"{sh.out_features}x{sh.in_features}"
-                                          for (name, _), sh in zip(groups, shapes)},
+                   "ops_per_layer": {name: f"{sh.out_features}x{sh.in_features}"
+                                     for (name, _), sh in zip(groups, shapes)},
                    "num_planes": K, "group_size": group, "tokens": 1,
-                   "bytes_per_step": bytes_per_step, "graph": graph is not None,
-                   "path": path_name, "path_per_shape": shape_paths,
+                   "bytes_per_step": bytes_per_step, "launches_per_step": 1,
+                   "kernel": "rbq_program_run (one persistent launch over every op of the step)",
+                   "activations": "one token per decoder-layer input (q/k/v and gate/up share theirs)",
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dom_key, shape_paths[dom_key]),
-                     "kernel": f"rbq gemv ({shape_paths[dom_key]}) {dom}",
-                     "bytes_per_launch": per_call[dom_i], "mean_launch_us": round(mean_us[dom_i], 3),
-                     "layer_GBps_from_launch_times": round(sum(per_call) / (tot_us * 1e-6) / 1e9, 1),
-                     "per_shape": per_shape},
+        "roofline": {"bound": "hbm", "achieved": round(bytes_per_step / (prog_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(bytes_per_step / (prog_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(prog_key, "gemv_program_kernel"),
+                     "kernel": f"gemv_program_kernel<{K}> ({len(ops)} ops)",
+                     "bytes_per_launch": bytes_per_step, "mean_launch_us": round(prog_us, 2),
+                     "rocprof_mean_launch_us": rocprof_mean_us(prog_key)},
         "cpu_baseline": cpu,
+        "launches": {"ms_per_step": round(ms_launches, 4),
+                     "GBps": round(bytes_per_step / (ms_launches * 1e-3) / 1e9, 1),
+                     "launches_per_step": len(ops), "graph": True, "path_per_shape": shape_paths,
+                     "last_layer_max_rel_diff_vs_program": launch_diff, "per_shape": per_shape},
+        "read_probe": read_probe,
         "encode": {"linears": len(wl.linears), "ms": round(enc_ms, 4),
                    "GBps": round(enc_bytes / (enc_ms * 1e-3) / 1e9, 1)},
         "refit": {"linears": len(wl.linears), "ms": round(ref_ms, 4),
@@ -726,6 +905,7 @@ def bench_decode(args):
         "encode_refit_per_shape": prep,
         "gemv_dual_per_shape": dual_shape,
         "decode_layer_chain": layer_chain,
+        "other_workloads": others or None,
     }
     print(json.dumps(line), flush=True)
 

@@ -106,6 +106,7 @@ _SIGNATURES = {
                                          ctypes.c_size_t]),
     "rbq_program_run": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]),
+    "rbq_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
     "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
@@ -349,6 +350,19 @@ def gemv(planes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, group_size
     check(lib().rbq_gemv(planes.data_ptr(), scales.data_ptr(), s, x.data_ptr(), y.data_ptr(),
                          _stream(x, stream)), "rbq_gemv")
     return y
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, *, stream=None) -> None:
+    """rbq_probe_read: one launch reading the first `nbytes` bytes of the
+    device tensor `buf` (all of it by default); sink is a device int32."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    _dev(sink, torch.int32, "sink")
+    total = buf.numel() * buf.element_size()
+    n = total if nbytes is None else int(nbytes)
+    if n < 0 or n > total:
+        raise ValueError(f"nbytes must be in [0, {total}]")
+    check(lib().rbq_probe_read(buf.data_ptr(), n, sink.data_ptr(), _stream(buf, stream)), "rbq_probe_read")
 
 
 def encode_dual_workspace_bytes(s: Shape) -> int:

@@ -485,6 +485,18 @@ rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *co
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+rbq_status rbq_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (buf == nullptr || sink == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return RBQ_ERR_ALIGNMENT;
+    rbq_status st = device_present();
+    if (st != RBQ_OK || bytes == 0)
+        return st;
+    hipError_t e = rbq::launch_probe_read(buf, bytes, sink, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 int32_t rbq_last_hip_error(void) { return g_last_hip_error; }
 
 const char *rbq_status_string(rbq_status st) {

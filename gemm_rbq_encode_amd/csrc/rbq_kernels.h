@@ -100,6 +100,9 @@ int program_num_ops(const void *image);
 hipError_t launch_program(const void *image, const void *image_dev, int32_t *counters, int32_t *status,
                           hipStream_t st);
 
+// Streaming-read probe (probe.hip): one launch reading `bytes` bytes.
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
+
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);
 

@@ -438,6 +438,20 @@ rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t n
 rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *counters_dev,
                            int32_t *status_dev, void *stream);
 
+/*
+ * rbq_probe_read -- measurement aid, not a step of the method: one launch that
+ * reads `bytes` bytes at `buf` from device memory with 16-byte non-temporal
+ * loads and discards them, so that a GEMV launch can be compared with a plain
+ * read of the same size run the same way (the roofline of a kernel that reads
+ * its packed planes once).
+ *   buf   device memory, 16-byte aligned, `bytes` readable bytes (read only)
+ *   sink  device uint32: written only if the folded loads hit a fixed magic
+ *         value (practically never); keeps the loads from being dropped
+ * Errors: RBQ_ERR_INVALID_ARG (null pointer), RBQ_ERR_ALIGNMENT,
+ * RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.  bytes == 0 launches nothing.
+ */
+rbq_status rbq_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Kernel families rbq_gemm can use; RBQ_PATH_AUTO picks by shape and M. */
 typedef enum rbq_path {
     RBQ_PATH_AUTO = 0,

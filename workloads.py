@@ -136,6 +136,15 @@ def workload_activations(wl: Workload, in_features: int, tokens: int) -> np.ndar
     return gaussian_activations(full, in_features, wl.x_seed)[:tokens]
 
 
+def layer_activations(wl: Workload, in_features: int, layers: int, slot: int) -> np.ndarray:
+    """One fp16 token per layer for one input of a decoder layer (slot 0:
+    attention input, read by q, k, v; 1: o_proj input; 2: MLP input, read
+    by gate and up; 3: down_proj input), so that no two launches of a step
+    read the same activations unless a decoder's would.  x ~ N(0, 1), seed
+    100 * x_seed + 10 + slot; uint16 [layers][in]."""
+    return gaussian_activations(layers, in_features, 100 * wl.x_seed + 10 + slot)
+
+
 def random_scales(num_planes: int, out_features: int, groups: int, seed: int,
                   signed: bool = True) -> np.ndarray:
     """Arbitrary finite fp16 scales (as learned scales would be), uint16 bits."""
