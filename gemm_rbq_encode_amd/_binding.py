@@ -106,6 +106,14 @@ _SIGNATURES = {
                                          ctypes.c_size_t]),
     "rbq_program_run": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]),
+    "rbq_qat_encode": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+    "rbq_qat_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_qat_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
@@ -350,6 +358,94 @@ def gemv(planes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, group_size
     check(lib().rbq_gemv(planes.data_ptr(), scales.data_ptr(), s, x.data_ptr(), y.data_ptr(),
                          _stream(x, stream)), "rbq_gemv")
     return y
+
+
+def qat_encode(W: torch.Tensor, scales: torch.Tensor, group_size: int = 0, *,
+               planes: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
+    """rbq_qat_encode: binary cores of fp32 W [out][in] for the given fp16
+    scales [K][out][G]; returns planes int32 [K][out][in/32]."""
+    _dev(W, torch.float32, "W")
+    _dev(scales, torch.float16, "scales")
+    out_f, in_f = W.shape
+    K = scales.shape[0]
+    s = shape(out_f, in_f, K, group_size)
+    if scales.numel() * 2 != int(lib().rbq_scales_bytes(s)):
+        raise ValueError("scales do not match the shape")
+    if planes is None:
+        planes = torch.empty((K, out_f, in_f // 32), dtype=torch.int32, device=W.device)
+    _dev(planes, torch.int32, "planes")
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    check(lib().rbq_qat_encode(W.data_ptr(), s, scales.data_ptr(), planes.data_ptr(), sp, _stream(W, stream)),
+          "rbq_qat_encode")
+    return planes
+
+
+def qat_forward(W: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_size: int = 0, *,
+                planes: torch.Tensor | None = None, Y: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
+    """rbq_qat_forward: (planes, Y) with planes derived from W for the given
+    scales and Y [M][out] = X What^T (fp16)."""
+    _dev(W, torch.float32, "W")
+    _dev(scales, torch.float16, "scales")
+    _dev(X, torch.float16, "X")
+    out_f, in_f = W.shape
+    K = scales.shape[0]
+    s = shape(out_f, in_f, K, group_size)
+    if X.dim() != 2 or X.shape[1] != in_f:
+        raise ValueError(f"X must be [M][{in_f}]")
+    if scales.numel() * 2 != int(lib().rbq_scales_bytes(s)):
+        raise ValueError("scales do not match the shape")
+    M = X.shape[0]
+    if planes is None:
+        planes = torch.empty((K, out_f, in_f // 32), dtype=torch.int32, device=W.device)
+    if Y is None:
+        Y = torch.empty((M, out_f), dtype=torch.float16, device=W.device)
+    _dev(planes, torch.int32, "planes")
+    _dev(Y, torch.float16, "Y")
+    need = int(lib().rbq_gemm_workspace_bytes(s, M))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
+    wp, wn = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    check(lib().rbq_qat_forward(W.data_ptr(), scales.data_ptr(), s, X.data_ptr(), M, planes.data_ptr(),
+                                Y.data_ptr(), wp, wn, sp, _stream(W, stream)), "rbq_qat_forward")
+    return planes, Y
+
+
+def qat_backward(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, dY: torch.Tensor,
+                 group_size: int = 0, *, need_dx: bool = True, need_dw: bool = True, need_dscales: bool = True,
+                 status: torch.Tensor | None = None, stream=None):
+    """rbq_qat_backward: straight-through (dX [M][in], dW [out][in],
+    dscales [K][out][G]), fp32; an output not asked for is None."""
+    _dev(planes, torch.int32, "planes")
+    _dev(scales, torch.float16, "scales")
+    _dev(X, torch.float16, "X")
+    _dev(dY, torch.float16, "dY")
+    K, out_f, words = planes.shape
+    in_f = words * 32
+    s = shape(out_f, in_f, K, group_size)
+    M = X.shape[0]
+    if X.shape != (M, in_f) or dY.shape != (M, out_f):
+        raise ValueError("X must be [M][in] and dY [M][out]")
+    dev = planes.device
+    G = in_f // group_size if group_size else 1
+    dX = torch.empty((M, in_f), dtype=torch.float32, device=dev) if need_dx else None
+    dW = torch.empty((out_f, in_f), dtype=torch.float32, device=dev) if (need_dw or need_dscales) else None
+    ds = torch.empty((K, out_f, G), dtype=torch.float32, device=dev) if need_dscales else None
+    sp = None
+    if status is not None:
+        _dev(status, torch.int32, "status")
+        sp = status.data_ptr()
+    ptr = (lambda t: None if t is None else t.data_ptr())
+    check(lib().rbq_qat_backward(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), dY.data_ptr(), M,
+                                 ptr(dX), ptr(dW), ptr(ds), sp, _stream(planes, stream)), "rbq_qat_backward")
+    return dX, (dW if need_dw else None), ds
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, *, stream=None) -> None:

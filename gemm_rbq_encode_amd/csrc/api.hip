@@ -485,6 +485,72 @@ rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *co
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+rbq_status rbq_qat_encode(const float *W, rbq_shape s, const uint16_t *scales, uint32_t *planes,
+                          int32_t *status_dev, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (!rbq::qat_supports(s.num_planes))
+        return RBQ_ERR_UNSUPPORTED;
+    if (s.out_features == 0 || s.in_features == 0)
+        return RBQ_OK;
+    if (W == nullptr || planes == nullptr || scales == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(W, 4) || !aligned(planes, 4) || !aligned(scales, 2) ||
+        (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_qat_encode(W, s.out_features, s.in_features, s.num_planes, s.group_size, scales,
+                                          planes, status_dev, (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
+rbq_status rbq_qat_forward(const float *W, const uint16_t *scales, rbq_shape s, const uint16_t *X, int32_t M,
+                           uint32_t *planes, uint16_t *Y, void *workspace, size_t ws_bytes, int32_t *status_dev,
+                           void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (M < 0)
+        return RBQ_ERR_INVALID_ARG;
+    if ((st = rbq_qat_encode(W, s, scales, planes, status_dev, stream)) != RBQ_OK)
+        return st;
+    return gemm_impl(planes, scales, s, X, M, Y, workspace, ws_bytes, RBQ_EPILOGUE_NONE, stream);
+}
+
+rbq_status rbq_qat_backward(const uint32_t *planes, const uint16_t *scales, rbq_shape s, const uint16_t *X,
+                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales,
+                            int32_t *status_dev, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (!rbq::qat_supports(s.num_planes))
+        return RBQ_ERR_UNSUPPORTED;
+    if (M < 0 || (dscales != nullptr && dW == nullptr))
+        return RBQ_ERR_INVALID_ARG;
+    const bool want_dx = dX != nullptr && M > 0 && s.in_features > 0;
+    const bool want_dw = dW != nullptr && s.out_features > 0 && s.in_features > 0;
+    if (!want_dx && !want_dw)
+        return RBQ_OK;
+    if (M > 0 && dY == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (want_dw && M > 0 && X == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if ((want_dx || dscales != nullptr) && s.out_features > 0 && (planes == nullptr || scales == nullptr))
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(planes, 4) || !aligned(scales, 2) || !aligned(X, 2) || !aligned(dY, 2) || !aligned(dX, 4) ||
+        !aligned(dW, 4) || !aligned(dscales, 4) || (status_dev != nullptr && !aligned(status_dev, 4)))
+        return RBQ_ERR_ALIGNMENT;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_qat_backward(planes, scales, s.out_features, s.in_features, s.num_planes,
+                                            s.group_size, X, dY, M, want_dx ? dX : nullptr,
+                                            want_dw ? dW : nullptr, want_dw ? dscales : nullptr, status_dev,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 rbq_status rbq_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
     if (buf == nullptr || sink == nullptr)
         return RBQ_ERR_INVALID_ARG;

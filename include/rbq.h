@@ -438,6 +438,68 @@ rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t n
 rbq_status rbq_program_run(const void *image, const void *image_dev, int32_t *counters_dev,
                            int32_t *status_dev, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Coupled (QAT-style) forward and straight-through backward.
+ *
+ * RaBiT summary (paperlayer.ai), section 4.2 "Coupled Training" and the
+ * "RaBiT training" procedure (section G): training keeps one shared fp32
+ * weight W and learnable scales; each forward pass derives the binary cores
+ * again from W, path by path, B_1 = sign(W), R_1 = W - a_1 B_1,
+ * B_2 = sign(R_1), ...; the shared weight takes the whole gradient.  Here the
+ * scales are given (the learnable ones), sign(0) = +1, every residual step is
+ * one fp32 operation against the binary16 scale, and the backward is the
+ * straight-through estimator: sign() passes gradients unchanged.
+ * num_planes 1..4 (RBQ_ERR_UNSUPPORTED above), group_size 0 or 128.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * rbq_qat_encode -- binary cores of W for the given scales (the cascade
+ * above; planes bit-identical to it).
+ *   W       device fp32 [out][in], row-major (read only)
+ *   scales  device binary16 [K][out][G] (read only)
+ *   planes  device uint32 [K][out][in/32], written
+ *   status  device int32 or NULL: RBQ_STATUS_NONFINITE_W is OR-ed in when W
+ *           holds NaN or Inf (NaN takes -1 on every plane)
+ * Errors: RBQ_ERR_INVALID_ARG (shape, null pointer), RBQ_ERR_ALIGNMENT,
+ * RBQ_ERR_UNSUPPORTED (K > 4), RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.
+ */
+rbq_status rbq_qat_encode(const float *W, rbq_shape s, const uint16_t *scales, uint32_t *planes,
+                          int32_t *status, void *stream);
+
+/*
+ * rbq_qat_forward -- the coupled forward: planes = rbq_qat_encode(W, scales),
+ * then Y = rbq_gemm(planes, scales, X) (the same kernels, tolerance and
+ * workspace rules as rbq_gemm).  The planes are kept for the backward.
+ *   X [M][in] fp16, Y [M][out] fp16, device; workspace as for rbq_gemm.
+ * Errors: those of rbq_qat_encode and rbq_gemm.
+ */
+rbq_status rbq_qat_forward(const float *W, const uint16_t *scales, rbq_shape s, const uint16_t *X, int32_t M,
+                           uint32_t *planes, uint16_t *Y, void *workspace, size_t ws_bytes, int32_t *status,
+                           void *stream);
+
+/*
+ * rbq_qat_backward -- straight-through gradients of Y = X What^T,
+ * What = sum_k a_k B_k, given dY:
+ *   dW[r][j]       = sum_m dY[m][r] X[m][j]           fp32 [out][in]
+ *   dscales[k][r][t] = sum over columns j of group t of B_k[r][j] dW[r][j]
+ *                                                      fp32 [K][out][G]
+ *   dX[m][j]       = sum_r dY[m][r] What[r][j]        fp32 [M][in]
+ * Any of dX, dW may be NULL (not computed); dscales needs dW.  X, dY fp16
+ * [M][in], [M][out]; planes and scales as written by the forward.  dW is
+ * exact products with fp32 accumulation; dscales sums the fp32 dW in fp64;
+ * dX forms What in fp32 and multiplies its two fp16 parts (relative 2^-22,
+ * absolute 2^-25 where the lower part is subnormal) with fp32 accumulation.
+ *   status  device int32 or NULL: RBQ_STATUS_SCALE_OVERFLOW is OR-ed in when
+ *           a formed weight of What is not below 65520 in magnitude (or not
+ *           finite); dX is then not meaningful
+ * No workspace.  Errors: RBQ_ERR_INVALID_ARG (shape, M < 0, a needed pointer
+ * NULL, dscales without dW), RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (K > 4),
+ * RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.
+ */
+rbq_status rbq_qat_backward(const uint32_t *planes, const uint16_t *scales, rbq_shape s, const uint16_t *X,
+                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales,
+                            int32_t *status, void *stream);
+
 /*
  * rbq_probe_read -- measurement aid, not a step of the method: one launch that
  * reads `bytes` bytes at `buf` from device memory with 16-byte non-temporal
