@@ -39,6 +39,9 @@ Reported (one JSON line):
              Llama-3-8B prefill set (--no-extra skips them; --workload runs
              one of them on its own line)
 
+Every timing starts after about 0.3 s of untimed back-to-back runs of the
+same work (clocks settle under load) and the --warmup steps.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
 from __future__ import annotations
@@ -387,6 +390,7 @@ def measure_layer_set(args, workload, tokens, torch, rbq, workloads, dev, with_p
         for _, fn in launches:
             fn()
     torch.cuda.synchronize()
+    settle(torch, graph.replay)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -469,6 +473,17 @@ def measure_layer_set(args, workload, tokens, torch, rbq, workloads, dev, with_p
 
 
 X_SLOTS = {"fused": (0, 1, 2, 3), "separate": (0, 0, 0, 1, 2, 2, 3)}
+
+
+def settle(torch, fn, seconds=0.3):
+    """Untimed: run `fn` back to back for about `seconds`, so that the GPU's
+    clocks reach their level under this load before a timing starts (right
+    after idle gaps the first tens of launches run at other clocks)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def event_launch_us(torch, fn, stream, reps):
@@ -643,11 +658,13 @@ def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
 
+    settle(torch, graph.replay)
     ms_launch = wall_ms(graph.replay)
     y_launch = bufs["y"].clone()
     del graph
     prog = rbq.Program(chain_program_ops(rbq, layers, gu, bufs, n_q), num_planes=K)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    settle(torch, lambda: prog.run(status))
     ms_prog = wall_ms(lambda: prog.run(status))
     torch.cuda.synchronize()
     st = int(status.item())
@@ -739,6 +756,7 @@ def bench_decode(args):
 
     # the kernel's own duration first (HIP events around back-to-back
     # launches on its stream), then the whole-job timing
+    settle(torch, run_step)
     prog_us = event_launch_us(torch, run_step, stream, max(args.steps, 20))
     for _ in range(args.warmup):
         run_step()
@@ -779,6 +797,7 @@ def bench_decode(args):
     with torch.cuda.graph(graph, stream=side):
         launch_step(torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
+    settle(torch, graph.replay)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()

@@ -15,7 +15,11 @@
 // 16-wave workgroup per compute unit walks the whole list:
 //   * 12 stream waves keep a ring of 16-byte weight loads in flight that
 //     runs on from one op into the next, so HBM stays busy across op
-//     boundaries;
+//     boundaries.  A load covers 64 bytes of 16 rows, half a 128-byte line
+//     of each; the wave's next unit reads the other halves, so the loads are
+//     ordinary cached ones (with the non-temporal hint the FETCH_SIZE
+//     counter showed 1.8 times the plane bytes read from HBM, without it
+//     1.07 times);
 //   * 4 image waves build each op's activation image (x quantised into LDS,
 //     laid out as the MFMA B operand; two buffers, so op i+1's image is
 //     built while op i streams), and finish each op: the int32 partial sums
@@ -28,6 +32,7 @@
 //     the counter reaches the number of workgroups, from device-coherent
 //     loads of x.  Weight loads never wait, so the ring keeps streaming the
 //     next op's weights meanwhile.
+// A program without waits runs a kernel built without the waiting code.
 // Every wait is bounded (0.2 s of the real-time clock); a wait that runs out sets
 // RBQ_STATUS_PROGRAM_TIMEOUT in the status word and the kernel still runs to
 // its end.  The waits across workgroups need all workgroups resident: one
@@ -102,7 +107,7 @@ struct ProgHeader {
     uint32_t lds_bytes;
     uint32_t checksum;
     int32_t arena_bytes;   // LDS bytes of the image arena
-    int32_t reserved;
+    int32_t waits;         // 1 when some op waits for another (the kernel with the waits)
 };
 static_assert(sizeof(ProgHeader) == 32, "header layout");
 
@@ -252,7 +257,7 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     return v;
 }
 
-template <int K, int RING>
+template <int K, int RING, bool WAITS>
 __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 }
                 y = __builtin_ldexpf(y, -shs[par]);
             }
-            const bool shared_y = (op.flags & PF_Y_SHARED) != 0;
+            const bool shared_y = WAITS && (op.flags & PF_Y_SHARED) != 0;
             if (op.flags & PF_SILU) {
                 // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
                 const float up = __shfl_down(y, 1, RBQ_WAVE);
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 red[e] = 0;
             if (tid == 0)
                 __hip_atomic_store(&sdone[par], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (op.flags & PF_SIGNAL) {
+            if (WAITS && (op.flags & PF_SIGNAL)) {
                 // this workgroup's rows of y are stored (device-coherent) before it counts
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 img_sync();
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         auto load_x = [&](const OpView &op) {
             const int nh = (op.in >> 5) * 2;
             const int xu = (op.nchunks * CHUNK_WORDS * 2 + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
-            const bool shared_x = (op.flags & PF_X_SHARED) != 0;
+            const bool shared_x = WAITS && (op.flags & PF_X_SHARED) != 0;
 #pragma unroll
             for (int j = 0; j < PG_MAX_XU; ++j) {
                 xw[j][0] = xw[j][1] = (v4u){0u, 0u, 0u, 0u};
@@ -547,29 +552,29 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 
         int next_fin = 0;
         OpView cur = op_view(table, 0);
-        if (!(cur.flags & PF_X_SHARED))
+        if (!(WAITS && (cur.flags & PF_X_SHARED)))
             load_x(cur);
         load_scales(cur);
         for (int i = 0; i < n_ops; ++i) {
             // finish what the op waits for, the op whose slot of partial sums
             // and scales it takes, and the last op whose image shares LDS
             // bytes with its own
-            const int upto = max(max(cur.wait_for, i - PG_SLOTS), cur.free_after);
+            const int upto = max(max(WAITS ? cur.wait_for : -1, i - PG_SLOTS), cur.free_after);
             while (next_fin <= upto)
                 finish(next_fin++);
-            if (cur.wait_for >= 0)
+            if (WAITS && cur.wait_for >= 0)
                 wait_op(cur.wait_for);
             if (cur.flags & PF_REUSE) {
                 reuse(i);
             } else {
-                if (cur.flags & PF_X_SHARED)
+                if (WAITS && (cur.flags & PF_X_SHARED))
                     load_x(cur);
                 build(i, cur);
             }
             if (i + 1 < n_ops) {
                 // the next op's loads go out now, to arrive while this op streams
                 cur = op_view(table, i + 1);
-                if (!(cur.flags & (PF_X_SHARED | PF_REUSE)))
+                if (!(cur.flags & ((WAITS ? PF_X_SHARED : 0u) | PF_REUSE)))
                     load_x(cur);
                 load_scales(cur);
             }
@@ -626,7 +631,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             }
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                slot[k] = __builtin_nontemporal_load(reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride));
+                slot[k] = *reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride);
         };
 
         // ---- consume cursor: the op and unit the MFMAs work on
@@ -943,6 +948,9 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
+    h->waits = 0;
+    for (int i = 0; i < n_ops; ++i)
+        h->waits |= ops[i].wait_for >= 0 ? 1 : 0;
     h->checksum = image_checksum(img, image_bytes(n_ops, G));
     return RBQ_OK;
 }
@@ -954,7 +962,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->K != 1 && h->K != 2))
+        h->grid != program_num_cus() || (h->K != 1 && h->K != 2) || (h->waits != 0 && h->waits != 1))
         return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
@@ -970,12 +978,22 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
                           hipStream_t st) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     const ProgHeader *hd = static_cast<const ProgHeader *>(image_dev);
-    if (h->K == 1)
-        hipLaunchKernelGGL((gemv_program_kernel<1, RBQ_PROGRAM_RING>), dim3(h->grid), dim3(PG_THREADS),
-                           h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
-    else
-        hipLaunchKernelGGL((gemv_program_kernel<2, RBQ_PROGRAM_RING>), dim3(h->grid), dim3(PG_THREADS),
-                           h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
+    // programs without waits take the kernel with the waiting code compiled out
+#define RBQ_LAUNCH_PROGRAM(KK, WW)                                                                        \
+    hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW>), dim3(h->grid), dim3(PG_THREADS),   \
+                       h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status)
+    if (h->K == 1) {
+        if (h->waits)
+            RBQ_LAUNCH_PROGRAM(1, true);
+        else
+            RBQ_LAUNCH_PROGRAM(1, false);
+    } else {
+        if (h->waits)
+            RBQ_LAUNCH_PROGRAM(2, true);
+        else
+            RBQ_LAUNCH_PROGRAM(2, false);
+    }
+#undef RBQ_LAUNCH_PROGRAM
     return hipGetLastError();
 }
 
