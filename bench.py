@@ -38,6 +38,8 @@ Reported (one JSON line):
   other_workloads  skinny M=4 and M=16, Llama-2-13B K=4 g128 and the
              Llama-3-8B prefill set (--no-extra skips them; --workload runs
              one of them on its own line)
+  qat        the coupled forward (cores re-derived from W, then the layer)
+             and the straight-through backward on the Llama-2-7B shapes
 
 Every timing starts after about 0.3 s of untimed back-to-back runs of the
 same work (clocks settle under load) and the --warmup steps.
@@ -680,6 +682,60 @@ def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
             "epilogue": "silu(gate)*up in the gate/up op"}
 
 
+def bench_qat(torch, rbq, workloads, dev, shapes=((4096, 4096), (11008, 4096), (4096, 11008)), K=2,
+              tokens=(16, 2048)):
+    """The coupled forward and the straight-through backward on the
+    Llama-2-7B linear shapes: the cores for given scales (GB/s over W read
+    and planes written), the forward (cores + layer) and the backward (dW,
+    scale gradients, dX) per token count, as mean ms of graph replays and
+    dense-equivalent TFLOP/s (2*M*out*in per product: one for the forward,
+    two for the backward)."""
+    res = {}
+    for out_f, in_f in shapes:
+        W = torch.from_numpy(workloads.gaussian_weight(out_f, in_f, 4000 + out_f, outliers=True)).to(dev)
+        _, sc = rbq.encode(W, K, 0)
+        planes = torch.empty((K, out_f, in_f // 32), dtype=torch.int32, device=dev)
+        Wc = rotation_copies(W)
+        enc_ms = graph_ms(torch, dev, [(lambda Wi=Wi: rbq.qat_encode(Wi, sc, 0, planes=planes)) for Wi in Wc],
+                          3) / len(Wc)
+        del Wc
+        entry = {"encode_us": round(enc_ms * 1e3, 1),
+                 "encode_GBps": round((4 * W.numel() + 4 * planes.numel()) / (enc_ms * 1e-3) / 1e9, 1)}
+        for M in tokens:
+            X = torch.from_numpy(workloads.gaussian_activations(M, in_f, 4100).view(np.float16)).to(dev)
+            dY = torch.from_numpy(workloads.gaussian_activations(M, out_f, 4101).view(np.float16)).to(dev)
+            Y = torch.empty((M, out_f), dtype=torch.float16, device=dev)
+            need = int(rbq.lib().rbq_gemm_workspace_bytes(rbq.shape(out_f, in_f, K, 0), M))
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            dX = torch.empty((M, in_f), dtype=torch.float32, device=dev)
+            dW = torch.empty((out_f, in_f), dtype=torch.float32, device=dev)
+            ds = torch.empty((K, out_f, 1), dtype=torch.float32, device=dev)
+            L = rbq.lib()
+            s = rbq.shape(out_f, in_f, K, 0)
+
+            def fwd():
+                rbq.check(L.rbq_qat_forward(W.data_ptr(), sc.data_ptr(), s, X.data_ptr(), M, planes.data_ptr(),
+                                            Y.data_ptr(), ws.data_ptr(), need, None,
+                                            torch.cuda.current_stream(dev).cuda_stream), "rbq_qat_forward")
+
+            def bwd():
+                rbq.check(L.rbq_qat_backward(planes.data_ptr(), sc.data_ptr(), s, X.data_ptr(), dY.data_ptr(), M,
+                                             dX.data_ptr(), dW.data_ptr(), ds.data_ptr(), None,
+                                             torch.cuda.current_stream(dev).cuda_stream), "rbq_qat_backward")
+
+            f_ms = graph_ms(torch, dev, [fwd], 5)
+            b_ms = graph_ms(torch, dev, [bwd], 5)
+            flop = 2.0 * M * out_f * in_f
+            entry[f"m{M}"] = {"forward_ms": round(f_ms, 4), "forward_TFLOPs": round(flop / (f_ms * 1e-3) / 1e12, 1),
+                              "backward_ms": round(b_ms, 4),
+                              "backward_TFLOPs": round(2 * flop / (b_ms * 1e-3) / 1e12, 1)}
+            del X, dY, Y, ws, dX, dW, ds
+        res[f"{out_f}x{in_f}"] = entry
+        del W, sc, planes
+    torch.cuda.empty_cache()
+    return {"num_planes": K, "scales": "per row", "per_shape": res}
+
+
 def bench_decode(args):
     import torch
 
@@ -880,6 +936,8 @@ def bench_decode(args):
             if "encode_refit_per_shape" in sub:
                 others[f"{name}_m{tokens}"]["encode_refit_per_shape"] = sub["encode_refit_per_shape"]
 
+    qat = None if args.no_extra else bench_qat(torch, rbq, workloads, dev)
+
     prog_key = f"program_{args.layout}_{args.layers}layers"
     line = {
         "metric": METRIC,
@@ -925,6 +983,7 @@ def bench_decode(args):
         "gemv_dual_per_shape": dual_shape,
         "decode_layer_chain": layer_chain,
         "other_workloads": others or None,
+        "qat": qat,
     }
     print(json.dumps(line), flush=True)
 

@@ -460,7 +460,7 @@ size_t rbq_program_bytes(int32_t n_ops) { return rbq::program_bytes(n_ops); }
 size_t rbq_program_counters_bytes(int32_t n_ops) {
     if (n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS)
         return 0;
-    return (size_t)(n_ops + 1) * sizeof(int32_t);
+    return rbq::program_counters_bytes(n_ops);
 }
 
 // Host only: the checks and the image need no device (the image is laid out

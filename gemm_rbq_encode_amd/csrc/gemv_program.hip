@@ -119,11 +119,22 @@ struct PgShared {
     int sdone[PG_SLOTS];                      // stream waves done with an op, by op slot (i % PG_SLOTS)
     int isync;                                // phases of the image waves' barrier
     int abort_flag;                           // a wait ran out: the rest runs without waiting
+    int last_wg;                              // this workgroup is the last to finish the run
     uint32_t wmax[PG_SLOTS][PG_PREP];
     float wsum[PG_SLOTS][PG_PREP];
     int shs[PG_SLOTS];
     uint16_t sc_lds[PG_SLOTS][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
 };
+
+// Op counters: each op's count of finished workgroups is split over
+// PG_CSPLIT words (workgroup b adds to word b % PG_CSPLIT), each on its own
+// 128-byte line, so that 256 workgroups do not all contend for one address;
+// a waiter adds the words up.  The run's own count of finished workgroups
+// follows the ops' counters.
+constexpr int PG_CSPLIT = 8;
+constexpr int PG_CPAD = 32;                                // ints per 128-byte line
+__host__ __device__ inline size_t counter_index(int j, int c) { return ((size_t)j * PG_CSPLIT + c) * PG_CPAD; }
+__device__ inline int *op_counter(int *counters, int j, int c) { return counters + counter_index(j, c); }
 
 // LDS of one compute unit available to a workgroup (160 KB on gfx950; the
 // same when no device is visible, for host-only checks).
@@ -145,6 +156,8 @@ size_t program_dynamic_lds(int K) {
     const size_t fixed = K == 1 ? sizeof(PgShared<1>) : sizeof(PgShared<2>);
     return program_lds_limit() - fixed - 256;
 }
+
+size_t program_counter_ints(int n_ops) { return counter_index(n_ops, 0) + 1; }
 
 size_t image_bytes(int n_ops, int grid) {
     return sizeof(ProgHeader) + (size_t)n_ops * sizeof(ProgOp) + (size_t)grid * PG_STREAM * sizeof(int32_t);
@@ -392,7 +405,8 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 img_sync();
                 if (tid == 0)
-                    __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(op_counter(counters, j, b & (PG_CSPLIT - 1)), 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
         };
 
@@ -401,7 +415,12 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             if (tid == 0) {
                 const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + PG_WAIT_TICKS;
                 for (;;) {
-                    if (__hip_atomic_load(counters + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= G)
+                    int tot = 0;
+#pragma unroll
+                    for (int c = 0; c < PG_CSPLIT; ++c)
+                        tot += __hip_atomic_load(op_counter(counters, j, c), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    if (tot >= G)
                         break;
                     if (__hip_atomic_load(&abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ||
                         __builtin_amdgcn_s_memrealtime() > deadline) {
@@ -765,12 +784,18 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     if (tid == 0 && status != nullptr && abort_flag)
         __hip_atomic_fetch_or(status, (int)RBQ_STATUS_PROGRAM_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the last workgroup to finish clears the op counters for the next run
+    int *done_counter = op_counter(counters, n_ops, 0);
     if (tid == 0) {
-        const int done = __hip_atomic_fetch_add(counters + n_ops, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == G - 1) {
-            for (int j = 0; j <= n_ops; ++j)
-                __hip_atomic_store(counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const int done = __hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.last_wg = done == G - 1;
+    }
+    __syncthreads();
+    if (sh.last_wg) {
+        for (int e = tid; e < n_ops * PG_CSPLIT; e += PG_THREADS)
+            __hip_atomic_store(op_counter(counters, e / PG_CSPLIT, e % PG_CSPLIT), 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0)
+            __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -973,6 +998,8 @@ rbq_status program_check(const void *image) {
 }
 
 int program_num_ops(const void *image) { return static_cast<const ProgHeader *>(image)->n_ops; }
+
+size_t program_counters_bytes(int n_ops) { return program_counter_ints(n_ops) * sizeof(int32_t); }
 
 hipError_t launch_program(const void *image, const void *image_dev, int32_t *counters, int32_t *status,
                           hipStream_t st) {

@@ -97,6 +97,7 @@ size_t program_bytes(int n_ops);
 rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *image, size_t bytes);
 rbq_status program_check(const void *image);   // a valid image for the current device
 int program_num_ops(const void *image);
+size_t program_counters_bytes(int n_ops);
 hipError_t launch_program(const void *image, const void *image_dev, int32_t *counters, int32_t *status,
                           hipStream_t st);
 

@@ -395,7 +395,8 @@ typedef struct rbq_program_op {
  * n_ops is outside 1 .. RBQ_PROGRAM_MAX_OPS). */
 size_t rbq_program_bytes(int32_t n_ops);
 
-/* Bytes of the counters a program run uses: (n_ops + 1) int32. */
+/* Bytes of the counters a program run uses (int32 words: per op, one on
+ * each of 8 separate 128-byte lines, and one for the run). */
 size_t rbq_program_counters_bytes(int32_t n_ops);
 
 /*
@@ -424,7 +425,8 @@ rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t n
  * workgroup per compute unit.
  *   image        the host image written by rbq_program_build
  *   image_dev    device copy of the same bytes, 16-byte aligned (read only)
- *   counters_dev device int32 [n_ops + 1], all zero before the first run;
+ *   counters_dev device int32, rbq_program_counters_bytes(n_ops) bytes, all
+ *                zero before the first run;
  *                every run that completes leaves them zero again.  One set
  *                per program that may run concurrently with another.
  *   status_dev   device int32 or NULL: RBQ_STATUS_PROGRAM_* bits are OR-ed in
