@@ -718,10 +718,13 @@ def bench_qat(torch, rbq, workloads, dev, shapes=((4096, 4096), (11008, 4096), (
                                             Y.data_ptr(), ws.data_ptr(), need, None,
                                             torch.cuda.current_stream(dev).cuda_stream), "rbq_qat_forward")
 
+            bneed = int(L.rbq_qat_backward_workspace_bytes(s, M))
+            bws = torch.empty(max(bneed, 4), dtype=torch.uint8, device=dev)
+
             def bwd():
                 rbq.check(L.rbq_qat_backward(planes.data_ptr(), sc.data_ptr(), s, X.data_ptr(), dY.data_ptr(), M,
-                                             dX.data_ptr(), dW.data_ptr(), ds.data_ptr(), None,
-                                             torch.cuda.current_stream(dev).cuda_stream), "rbq_qat_backward")
+                                             dX.data_ptr(), dW.data_ptr(), ds.data_ptr(), bws.data_ptr(), bneed,
+                                             None, torch.cuda.current_stream(dev).cuda_stream), "rbq_qat_backward")
 
             f_ms = graph_ms(torch, dev, [fwd], 5)
             b_ms = graph_ms(torch, dev, [bwd], 5)
@@ -729,7 +732,7 @@ def bench_qat(torch, rbq, workloads, dev, shapes=((4096, 4096), (11008, 4096), (
             entry[f"m{M}"] = {"forward_ms": round(f_ms, 4), "forward_TFLOPs": round(flop / (f_ms * 1e-3) / 1e12, 1),
                               "backward_ms": round(b_ms, 4),
                               "backward_TFLOPs": round(2 * flop / (b_ms * 1e-3) / 1e12, 1)}
-            del X, dY, Y, ws, dX, dW, ds
+            del X, dY, Y, ws, dX, dW, ds, bws
         res[f"{out_f}x{in_f}"] = entry
         del W, sc, planes
     torch.cuda.empty_cache()

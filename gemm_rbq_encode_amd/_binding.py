@@ -111,9 +111,10 @@ _SIGNATURES = {
     "rbq_qat_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_qat_backward_workspace_bytes": (ctypes.c_size_t, [Shape, ctypes.c_int32]),
     "rbq_qat_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_void_p, ctypes.c_void_p]),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
@@ -420,7 +421,7 @@ def qat_forward(W: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, group_si
 
 def qat_backward(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, dY: torch.Tensor,
                  group_size: int = 0, *, need_dx: bool = True, need_dw: bool = True, need_dscales: bool = True,
-                 status: torch.Tensor | None = None, stream=None):
+                 workspace: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
     """rbq_qat_backward: straight-through (dX [M][in], dW [out][in],
     dscales [K][out][G]), fp32; an output not asked for is None."""
     _dev(planes, torch.int32, "planes")
@@ -443,8 +444,13 @@ def qat_backward(planes: torch.Tensor, scales: torch.Tensor, X: torch.Tensor, dY
         _dev(status, torch.int32, "status")
         sp = status.data_ptr()
     ptr = (lambda t: None if t is None else t.data_ptr())
+    need = int(lib().rbq_qat_backward_workspace_bytes(s, M))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(lib().rbq_qat_backward(planes.data_ptr(), scales.data_ptr(), s, X.data_ptr(), dY.data_ptr(), M,
-                                 ptr(dX), ptr(dW), ptr(ds), sp, _stream(planes, stream)), "rbq_qat_backward")
+                                 ptr(dX), ptr(dW), ptr(ds), ptr(workspace), wn, sp, _stream(planes, stream)),
+          "rbq_qat_backward")
     return dX, (dW if need_dw else None), ds
 
 

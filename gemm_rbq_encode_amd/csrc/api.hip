@@ -519,15 +519,21 @@ rbq_status rbq_qat_forward(const float *W, const uint16_t *scales, rbq_shape s, 
     return gemm_impl(planes, scales, s, X, M, Y, workspace, ws_bytes, RBQ_EPILOGUE_NONE, stream);
 }
 
+size_t rbq_qat_backward_workspace_bytes(rbq_shape s, int32_t M) {
+    if (rbq_check_shape(s) != RBQ_OK || M < 1)
+        return 0;
+    return rbq::qat_backward_workspace_bytes(M, s.out_features, s.in_features);
+}
+
 rbq_status rbq_qat_backward(const uint32_t *planes, const uint16_t *scales, rbq_shape s, const uint16_t *X,
-                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales,
-                            int32_t *status_dev, void *stream) {
+                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales, void *workspace,
+                            size_t ws_bytes, int32_t *status_dev, void *stream) {
     rbq_status st = rbq_check_shape(s);
     if (st != RBQ_OK)
         return st;
     if (!rbq::qat_supports(s.num_planes))
         return RBQ_ERR_UNSUPPORTED;
-    if (M < 0 || (dscales != nullptr && dW == nullptr))
+    if (M < 0 || (dscales != nullptr && dW == nullptr) || (ws_bytes > 0 && workspace == nullptr))
         return RBQ_ERR_INVALID_ARG;
     const bool want_dx = dX != nullptr && M > 0 && s.in_features > 0;
     const bool want_dw = dW != nullptr && s.out_features > 0 && s.in_features > 0;
@@ -540,14 +546,15 @@ rbq_status rbq_qat_backward(const uint32_t *planes, const uint16_t *scales, rbq_
     if ((want_dx || dscales != nullptr) && s.out_features > 0 && (planes == nullptr || scales == nullptr))
         return RBQ_ERR_INVALID_ARG;
     if (!aligned(planes, 4) || !aligned(scales, 2) || !aligned(X, 2) || !aligned(dY, 2) || !aligned(dX, 4) ||
-        !aligned(dW, 4) || !aligned(dscales, 4) || (status_dev != nullptr && !aligned(status_dev, 4)))
+        !aligned(dW, 4) || !aligned(dscales, 4) || !aligned(workspace, 4) ||
+        (status_dev != nullptr && !aligned(status_dev, 4)))
         return RBQ_ERR_ALIGNMENT;
     if ((st = device_present()) != RBQ_OK)
         return st;
     hipError_t e = rbq::launch_qat_backward(planes, scales, s.out_features, s.in_features, s.num_planes,
                                             s.group_size, X, dY, M, want_dx ? dX : nullptr,
-                                            want_dw ? dW : nullptr, want_dw ? dscales : nullptr, status_dev,
-                                            (hipStream_t)stream);
+                                            want_dw ? dW : nullptr, want_dw ? dscales : nullptr, workspace,
+                                            ws_bytes, status_dev, (hipStream_t)stream);
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 

@@ -30,6 +30,8 @@
 //    hi = fp16(w), lo = fp16(w - hi), so dY hi + dY lo carries w to 2^-22
 //    relative (an absolute 2^-25 where lo is subnormal) with fp32
 //    accumulation; a formed weight beyond the fp16 range is reported.
+#include <algorithm>
+
 #include "rbq.h"
 #include "rbq_device.h"
 #include "rbq_kernels.h"
@@ -235,8 +237,8 @@ template <int K>
 __global__ __launch_bounds__(QT_THREADS) void qat_dx_kernel(const uint16_t *__restrict__ dY,
                                                             const uint32_t *__restrict__ planes,
                                                             const uint16_t *__restrict__ scales, int M, int out,
-                                                            int in, int group_size, float *__restrict__ dX,
-                                                            int32_t *__restrict__ status) {
+                                                            int in, int group_size, int r_slice,
+                                                            float *__restrict__ dX, int32_t *__restrict__ status) {
     __shared__ __align__(16) _Float16 As[QT_TILE * QT_LDP];   // [token][r]
     __shared__ __align__(16) _Float16 Bh[QT_TILE * QT_LDP];   // [column][r], hi part
     __shared__ __align__(16) _Float16 Bl[QT_TILE * QT_LDP];   // lo part
@@ -267,15 +269,20 @@ __global__ __launch_bounds__(QT_THREADS) void qat_dx_kernel(const uint16_t *__re
         for (int j = 0; j < 4; ++j)
             acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int r0 = 0; r0 < out; r0 += QT_BK) {
+    // slice blockIdx.z of the contraction: rows [r_lo, r_hi) of What, its
+    // partial dX at dX + z M in (one slice: dX itself)
+    const int r_lo = blockIdx.z * r_slice;
+    const int r_hi = min(out, r_lo + r_slice);
+    dX += (size_t)blockIdx.z * M * in;
+    for (int r0 = r_lo; r0 < r_hi; r0 += QT_BK) {
         uint16_t a[16];
-        load16(dY, m_base + am, M, r0 + 16 * ah, out, out, vec_a, a);
+        load16(dY, m_base + am, M, r0 + 16 * ah, r_hi, out, vec_a, a);
         const int r = r0 + rr;
         uint32_t bits[K];
         float sc[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const bool ok = col_ok && r < out;
+            const bool ok = col_ok && r < r_hi;
             bits[k] = ok ? planes[(size_t)k * plane_stride + (size_t)r * words + wq] >> sh : 0u;
             sc[k] = ok ? h2f(scales[((size_t)k * out + r) * G + g]) : 0.0f;
         }
@@ -357,6 +364,17 @@ __global__ __launch_bounds__(QC_THREADS) void qat_dscales_kernel(const float *__
     }
 }
 
+// dX = the sum of the S partial slices, in slice order (deterministic).
+__global__ void qat_sum_slices(const float *__restrict__ parts, int S, size_t n, float *__restrict__ dX) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n)
+        return;
+    float v = parts[i];
+    for (int z = 1; z < S; ++z)
+        v += parts[(size_t)z * n + i];
+    dX[i] = v;
+}
+
 __global__ void qat_fill_zero_f32(float *p, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n)
@@ -375,6 +393,23 @@ hipError_t fill_zero(float *p, size_t n, hipStream_t st) {
 
 bool qat_supports(int K) { return K >= 1 && K <= 4; }
 
+// Contraction slices of dX: enough workgroups for about two per compute
+// unit, at most 16 slices and at least 256 rows of What per slice.
+int qat_dx_slices(int M, int out, int in) {
+    if (M <= 0 || in <= 0 || out <= 0)
+        return 1;
+    const long tiles = (long)((in + QT_TILE - 1) / QT_TILE) * ((M + QT_TILE - 1) / QT_TILE);
+    long S = (512 + tiles - 1) / tiles;
+    S = std::min(S, 16L);
+    S = std::min(S, (long)std::max(1, out / 256));
+    return (int)std::max(S, 1L);
+}
+
+size_t qat_backward_workspace_bytes(int M, int out, int in) {
+    const int S = qat_dx_slices(M, out, in);
+    return S > 1 ? (size_t)S * M * in * sizeof(float) : 0;
+}
+
 hipError_t launch_qat_encode(const float *W, int out, int in, int K, int group_size, const uint16_t *scales,
                              uint32_t *planes, int32_t *status, hipStream_t st) {
     if (out == 0 || in == 0)
@@ -391,7 +426,8 @@ hipError_t launch_qat_encode(const float *W, int out, int in, int K, int group_s
 
 hipError_t launch_qat_backward(const uint32_t *planes, const uint16_t *scales, int out, int in, int K,
                                int group_size, const uint16_t *X, const uint16_t *dY, int M, float *dX,
-                               float *dW, float *dscales, int32_t *status, hipStream_t st) {
+                               float *dW, float *dscales, void *workspace, size_t ws_bytes, int32_t *status,
+                               hipStream_t st) {
     hipError_t e = hipSuccess;
     if (dW != nullptr) {
         if (M == 0) {
@@ -419,13 +455,26 @@ hipError_t launch_qat_backward(const uint32_t *planes, const uint16_t *scales, i
     if (dX != nullptr && M > 0 && in > 0) {
         if (out == 0)
             return fill_zero(dX, (size_t)M * in, st);
-        const dim3 grid((in + QT_TILE - 1) / QT_TILE, (M + QT_TILE - 1) / QT_TILE);
+        // few output tiles (small M): split the contraction over slices whose
+        // partial sums go to the workspace, added in order by a second kernel
+        int S = qat_dx_slices(M, out, in);
+        if ((size_t)S * M * in * sizeof(float) > ws_bytes || workspace == nullptr)
+            S = 1;
+        const int r_slice = S > 1 ? ((out + S - 1) / S + QT_BK - 1) / QT_BK * QT_BK : out;
+        S = (out + r_slice - 1) / r_slice;
+        float *dst = S > 1 ? static_cast<float *>(workspace) : dX;
+        const dim3 grid((in + QT_TILE - 1) / QT_TILE, (M + QT_TILE - 1) / QT_TILE, S);
         switch (K) {
-        case 1: hipLaunchKernelGGL(qat_dx_kernel<1>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, dX, status); break;
-        case 2: hipLaunchKernelGGL(qat_dx_kernel<2>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, dX, status); break;
-        case 3: hipLaunchKernelGGL(qat_dx_kernel<3>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, dX, status); break;
-        default: hipLaunchKernelGGL(qat_dx_kernel<4>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, dX, status); break;
+        case 1: hipLaunchKernelGGL(qat_dx_kernel<1>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, r_slice, dst, status); break;
+        case 2: hipLaunchKernelGGL(qat_dx_kernel<2>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, r_slice, dst, status); break;
+        case 3: hipLaunchKernelGGL(qat_dx_kernel<3>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, r_slice, dst, status); break;
+        default: hipLaunchKernelGGL(qat_dx_kernel<4>, grid, dim3(QT_THREADS), 0, st, dY, planes, scales, M, out, in, group_size, r_slice, dst, status); break;
         }
+        if ((e = hipGetLastError()) != hipSuccess || S == 1)
+            return e;
+        const size_t n = (size_t)M * in;
+        hipLaunchKernelGGL(qat_sum_slices, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const float *>(workspace), S, n, dX);
         e = hipGetLastError();
     }
     return e;

@@ -105,9 +105,11 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
 bool qat_supports(int K);
 hipError_t launch_qat_encode(const float *W, int out, int in, int K, int group_size, const uint16_t *scales,
                              uint32_t *planes, int32_t *status, hipStream_t st);
+size_t qat_backward_workspace_bytes(int M, int out, int in);
 hipError_t launch_qat_backward(const uint32_t *planes, const uint16_t *scales, int out, int in, int K,
                                int group_size, const uint16_t *X, const uint16_t *dY, int M, float *dX,
-                               float *dW, float *dscales, int32_t *status, hipStream_t st);
+                               float *dW, float *dscales, void *workspace, size_t ws_bytes, int32_t *status,
+                               hipStream_t st);
 
 // Streaming-read probe (probe.hip): one launch reading `bytes` bytes.
 hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);

@@ -494,13 +494,20 @@ rbq_status rbq_qat_forward(const float *W, const uint16_t *scales, rbq_shape s, 
  *   status  device int32 or NULL: RBQ_STATUS_SCALE_OVERFLOW is OR-ed in when
  *           a formed weight of What is not below 65520 in magnitude (or not
  *           finite); dX is then not meaningful
- * No workspace.  Errors: RBQ_ERR_INVALID_ARG (shape, M < 0, a needed pointer
- * NULL, dscales without dW), RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (K > 4),
- * RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.
+ *   workspace  device memory of rbq_qat_backward_workspace_bytes(s, M) bytes
+ *           (0 for many tokens): with few tokens dX is computed in slices of
+ *           the contraction whose fp32 partial sums it holds, added in slice
+ *           order (deterministic); a smaller workspace (or NULL with
+ *           ws_bytes 0) gives the same result from one slice, more slowly.
+ *           Calls that share a workspace must be ordered on one stream.
+ * Errors: RBQ_ERR_INVALID_ARG (shape, M < 0, a needed pointer NULL, dscales
+ * without dW, ws_bytes > 0 with a NULL workspace), RBQ_ERR_ALIGNMENT,
+ * RBQ_ERR_UNSUPPORTED (K > 4), RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP.
  */
+size_t rbq_qat_backward_workspace_bytes(rbq_shape s, int32_t M);
 rbq_status rbq_qat_backward(const uint32_t *planes, const uint16_t *scales, rbq_shape s, const uint16_t *X,
-                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales,
-                            int32_t *status, void *stream);
+                            const uint16_t *dY, int32_t M, float *dX, float *dW, float *dscales, void *workspace,
+                            size_t ws_bytes, int32_t *status, void *stream);
 
 /*
  * rbq_probe_read -- measurement aid, not a step of the method: one launch that

@@ -201,9 +201,33 @@ def test_argument_errors():
     assert L.rbq_qat_encode(ctypes.c_void_p(p + 2), rbq.shape(32, 64, 2, 0), p, p, None, None) == \
         rbq.RBQ_ERR_ALIGNMENT
     # the scale gradient needs dW
-    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, p, 4, p, None, p, None, None) == \
+    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, p, 4, p, None, p, None, 0, None, None) == \
         rbq.RBQ_ERR_INVALID_ARG
-    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, None, 4, p, p, None, None, None) == \
+    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, None, 4, p, p, None, None, 0, None, None) == \
         rbq.RBQ_ERR_INVALID_ARG
-    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, p, -1, p, p, None, None, None) == \
+    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, p, -1, p, p, None, None, 0, None, None) == \
         rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_qat_backward(p, p, rbq.shape(32, 64, 2, 0), p, p, 4, p, p, None, None, 64, None, None) == \
+        rbq.RBQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_backward_slices_equal_one_slice(M):
+    """With few tokens dX is summed over contraction slices in a workspace;
+    without the workspace the same dX comes from one slice, within the bound,
+    and two runs with the workspace are bit-identical."""
+    out, inf, K, group = 4096, 1024, 2, 0
+    W, s, X, dY = case(out, inf, K, group, M, 70 + M)
+    planes = torch.from_numpy(qat.cascade(W, s, group).view(np.int32)).to(dev())
+    need = rbq.lib().rbq_qat_backward_workspace_bytes(rbq.shape(out, inf, K, group), M)
+    assert need > 0
+    a = rbq.qat_backward(planes, t_f16(s), t_f16(X), t_f16(dY), group, need_dw=False, need_dscales=False)[0]
+    b = rbq.qat_backward(planes, t_f16(s), t_f16(X), t_f16(dY), group, need_dw=False, need_dscales=False)[0]
+    one = rbq.qat_backward(planes, t_f16(s), t_f16(X), t_f16(dY), group, need_dw=False, need_dscales=False,
+                           workspace=torch.empty(0, dtype=torch.uint8, device=dev()))[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rdX = qat.backward(qat.cascade(W, s, group), s, X, dY, group)[0]
+    tdx = grad_tolerances(qat.cascade(W, s, group), s, X, dY, group)[0]
+    for got in (a, one):
+        assert (np.abs(got.cpu().numpy().astype(np.float64) - rdX) <= tdx).all()
