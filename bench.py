@@ -33,6 +33,8 @@ Reported (one JSON line):
   decode_layer_chain  the 32 layers chained (each GEMV reads the previous
              one's output; gate/up with the SiLU-mul epilogue), as one
              program launch and as per-GEMV launches
+  other_layout  the same step in the other layout (separate: 224 GEMVs) as
+             one program launch
   encode / refit / encode_refit_per_shape / gemv_dual_per_shape  the other
              entry points on the same shapes
   other_workloads  skinny M=4 and M=16, Llama-2-13B K=4 g128 and the
@@ -739,6 +741,42 @@ def bench_qat(torch, rbq, workloads, dev, shapes=((4096, 4096), (11008, 4096), (
     return {"num_planes": K, "scales": "per row", "per_shape": res}
 
 
+def other_layout_program(args, torch, rbq, workloads, wl, dev, layout):
+    """The same decode step in the other layout, as one program launch:
+    whole-job ms and GB/s, and the kernel's mean launch time from HIP events
+    on its stream."""
+    K = wl.num_planes
+    groups, layers, shapes, widths, Ws, p_enc, s_enc = decode_sets(torch, rbq, workloads, wl, dev, layout,
+                                                                   args.layers)
+    del Ws, p_enc, s_enc
+    xs = decode_activations(torch, workloads, wl, dev, layout, widths, args.layers)
+    ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes]
+          for _ in range(args.layers)]
+    nbytes = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) * args.layers
+    prog = rbq.Program([{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
+                        for l in range(args.layers) for i in range(len(groups))], num_planes=K)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    run = (lambda: prog.run(status))
+    settle(torch, run)
+    us = event_launch_us(torch, run, stream, max(args.steps, 20))
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    if int(status.item()) != 0:
+        raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
+    del prog, layers, xs, ys
+    torch.cuda.empty_cache()
+    return {"layout": layout, "ops": len(groups) * args.layers, "bytes_per_step": nbytes,
+            "ms_per_step": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "mean_launch_us": round(us, 2), "kernel_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def bench_decode(args):
     import torch
 
@@ -918,6 +956,8 @@ def bench_decode(args):
     layer_chain = None
     if args.layout == "fused" and path in (rbq.PATH_AUTO, rbq.PATH_FLAT, rbq.PATH_VALU):
         layer_chain = decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, xs[0][0], K)
+    other_layout = None if args.no_extra else other_layout_program(
+        args, torch, rbq, workloads, wl, dev, "separate" if args.layout == "fused" else "fused")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -985,6 +1025,7 @@ def bench_decode(args):
         "encode_refit_per_shape": prep,
         "gemv_dual_per_shape": dual_shape,
         "decode_layer_chain": layer_chain,
+        "other_layout": other_layout,
         "other_workloads": others or None,
         "qat": qat,
     }
