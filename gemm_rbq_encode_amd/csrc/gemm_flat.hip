@@ -102,7 +102,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     static_assert(!DUAL || (MT == K && !SILU), "dual scales: one activation copy per plane");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ uint32_t wmax[MT][FL_PREP];
-    __shared__ float wsum[MT][FL_PREP];
+    __shared__ double wsum[MT][FL_PREP];   // exact: integer sums below 2^53
     __shared__ int shs[MT];
     __shared__ int counters[2];       // prep waves past the maximum, past the image
 
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const float ws = wave_sum_f32_dpp((float)psum[m]);   // sum of q over the wave's entries
+            const double ws = wave_sum_f64_dpp((double)psum[m]);   // sum of q over the wave's entries (exact)
             if (lane == 0)
                 wsum[m][wave] = ws;
             if (wave == 0 && lane == 0)
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     // silu(y_2i) * y_2i+1 to column i of a Y of out / 2 columns.
     auto row_sum = [&](int m) {
         const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
-        float sx = 0.0f;
+        double sx = 0.0;
 #pragma unroll
         for (int v = 0; v < FL_PREP; ++v)
             sx += wsum[m][v];
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
             const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                              65536.0 * (double)rp[2 * TILE_ROWS];
-            y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx);
+            y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - sx);
         }
         return __builtin_ldexpf(y, -shs[m]);
     };
@@ -479,14 +479,14 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             float y = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                float sx = 0.0f;
+                double sx = 0.0;
 #pragma unroll
                 for (int v = 0; v < FL_PREP; ++v)
                     sx += wsum[k][v];
                 const int *rp = red + ((tl * K + k) * NC + NLIMB * k) * TILE_ROWS + i;
                 const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                                  65536.0 * (double)rp[2 * TILE_ROWS];
-                y += __builtin_ldexpf(h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - (double)sx), -shs[k]);
+                y += __builtin_ldexpf(h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - sx), -shs[k]);
             }
             Y[t0 * TILE_ROWS + tid] = f2h(y);
         }
