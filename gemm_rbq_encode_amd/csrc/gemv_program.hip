@@ -121,7 +121,7 @@ struct PgShared {
     int abort_flag;                           // a wait ran out: the rest runs without waiting
     int last_wg;                              // this workgroup is the last to finish the run
     uint32_t wmax[PG_SLOTS][PG_PREP];
-    float wsum[PG_SLOTS][PG_PREP];
+    double wsum[PG_SLOTS][PG_PREP];                 // sums of q (exact: integers below 2^53)
     int shs[PG_SLOTS];
     uint16_t sc_lds[PG_SLOTS][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
 };
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
             float y = 0.0f;
             if (rowok) {
-                float sx = 0.0f;
+                double sx = 0.0;
 #pragma unroll
                 for (int v = 0; v < PG_PREP; ++v)
                     sx += wsum[par][v];
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
                     const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                                      65536.0 * (double)rp[2 * TILE_ROWS];
-                    y += h2f(sc_lds[par][k][tid]) * (float)(t * (2.0 / 128.0) - (double)sx);
+                    y += h2f(sc_lds[par][k][tid]) * (float)(t * (2.0 / 128.0) - sx);
                 }
                 y = __builtin_ldexpf(y, -shs[par]);
             }
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     }
                 }
             }
-            const float ws = wave_sum_f32_dpp((float)psum);   // sum of q over the wave's columns
+            const double ws = wave_sum_f64_dpp((double)psum);   // sum of q over the wave's columns (exact)
             if (lane == 0)
                 wsum[par][wave] = ws;
             if (tid == 0)
