@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--layout", choices=["fused", "separate"], default="fused",
                     help="fused: q/k/v stacked into one 12288x4096 matrix and gate/up into one "
                          "22016x4096 matrix (4 launches per layer); separate: 7 launches per layer")
+    ap.add_argument("--planes-layout", choices=["tiles", "rows"], default="tiles",
+                    help="plane layout the decode program reads: tiles (RBQ_LAYOUT_TILES, packed once "
+                         "from the row layout by rbq_pack_tiles) or rows ([K][out][in/32])")
     ap.add_argument("--workload", default="llama2_7b",
                     choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
@@ -198,15 +201,18 @@ def counter_pass(args):
     xs = decode_activations(torch, workloads, wl, dev, args.layout, widths, args.layers)
     ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes]
           for _ in range(args.layers)]
-    ops = [{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
-           for l in range(args.layers) for i in range(len(groups))]
+    ops = [{"planes": program_planes(rbq, args, layers[l][i][0]), "scales": layers[l][i][1], "x": xs[l][i],
+            "y": ys[l][i]} for l in range(args.layers) for i in range(len(groups))]
     prog = rbq.Program(ops, num_planes=K)
     nbytes = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) * args.layers
     for _ in range(3):
         prog.run()
     torch.cuda.synchronize()
-    print(f"counter pass: program_{args.layout}_{args.layers}layers x3 ({len(ops)} ops, "
+    print(f"counter pass: {program_key(args)} x3 ({len(ops)} ops, "
           f"{nbytes} algorithmic bytes per launch)", flush=True)
+    del prog
+    for op in ops:
+        op["planes"] = None
     for i, sh in enumerate(shapes):
         for l in range(min(8, args.layers)):
             rbq.gemv(layers[l][i][0], layers[l][i][1], xs[l][i], group, y=ys[l][i])
@@ -599,20 +605,33 @@ def chain_buffers(torch, dev, layers, shapes, x):
     return gu, bufs, n_ff
 
 
-def chain_program_ops(rbq, layers, gu, bufs, n_q):
+def program_planes(rbq, args, planes):
+    """The planes a decode program reads: the tile-layout copy (packed once,
+    as when the weights are loaded) or the row-layout tensor itself."""
+    return rbq.pack_tiles(planes) if args.planes_layout == "tiles" else planes
+
+
+def program_key(args, layout=None):
+    key = f"program_{layout or args.layout}_{args.layers}layers"
+    return key + "_tiles" if args.planes_layout == "tiles" else key
+
+
+def chain_program_ops(rbq, layers, gu, bufs, n_q, tiles=None):
     """A chained decoder step as program ops: q/k/v on the layer input (x,
     then the previous layer's down output), o on q (the attention between
     them is outside this library), gate/up with the SiLU-mul epilogue on o's
     output, down on h; each op waits for the one before it."""
+    def pl(p):
+        return tiles(p) if tiles else p
     ops = []
     for l, layer in enumerate(layers):
-        ops.append({"planes": layer[0][0], "scales": layer[0][1], "x": bufs["x"] if l == 0 else bufs["y"],
+        ops.append({"planes": pl(layer[0][0]), "scales": layer[0][1], "x": bufs["x"] if l == 0 else bufs["y"],
                     "y": bufs["qkv"], "wait_for": len(ops) - 1})
-        ops.append({"planes": layer[1][0], "scales": layer[1][1], "x": bufs["qkv"][:n_q], "y": bufs["o"],
+        ops.append({"planes": pl(layer[1][0]), "scales": layer[1][1], "x": bufs["qkv"][:n_q], "y": bufs["o"],
                     "wait_for": len(ops) - 1})
-        ops.append({"planes": gu[l][0], "scales": gu[l][1], "x": bufs["o"], "y": bufs["h"],
+        ops.append({"planes": pl(gu[l][0]), "scales": gu[l][1], "x": bufs["o"], "y": bufs["h"],
                     "epilogue": rbq.RBQ_EPILOGUE_SILU_MUL, "wait_for": len(ops) - 1})
-        ops.append({"planes": layer[3][0], "scales": layer[3][1], "x": bufs["h"], "y": bufs["y"],
+        ops.append({"planes": pl(layer[3][0]), "scales": layer[3][1], "x": bufs["h"], "y": bufs["y"],
                     "wait_for": len(ops) - 1})
     return ops
 
@@ -621,7 +640,8 @@ def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
     """The 32 layers as a chained decoder step (chain_program_ops' order and
     dependencies), once as one program launch and once as 4 launches per
     layer in a HIP graph.  Reports ms and GB/s over the same algorithmic
-    bytes (h is written once at half the gate/up rows)."""
+    bytes (h is written once at half the gate/up rows).  The program reads
+    the planes in args.planes_layout, the launches the row layout."""
     gu, bufs, n_ff = chain_buffers(torch, dev, layers, shapes, x)
     n_q = shapes[1].in_features
     per_layer = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) - 2 * n_ff
@@ -666,7 +686,8 @@ def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
     ms_launch = wall_ms(graph.replay)
     y_launch = bufs["y"].clone()
     del graph
-    prog = rbq.Program(chain_program_ops(rbq, layers, gu, bufs, n_q), num_planes=K)
+    prog = rbq.Program(chain_program_ops(rbq, layers, gu, bufs, n_q,
+                                         (lambda p: program_planes(rbq, args, p))), num_planes=K)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     settle(torch, lambda: prog.run(status))
     ms_prog = wall_ms(lambda: prog.run(status))
@@ -680,7 +701,7 @@ def decode_layer_chain(args, torch, rbq, L, dev, layers, shapes, x, K):
             "program": {"ms_per_step": round(ms_prog, 4), "GBps": round(total / (ms_prog * 1e-3) / 1e9, 1)},
             "launches": {"ms_per_step": round(ms_launch, 4), "GBps": round(total / (ms_launch * 1e-3) / 1e9, 1),
                          "graph": True},
-            "program_output_equals_launches": same,
+            "program_output_equals_launches": same, "program_planes_layout": args.planes_layout,
             "epilogue": "silu(gate)*up in the gate/up op"}
 
 
@@ -753,7 +774,8 @@ def other_layout_program(args, torch, rbq, workloads, wl, dev, layout):
     ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes]
           for _ in range(args.layers)]
     nbytes = sum(gemv_bytes(sh.out_features, sh.in_features, K, 1) for sh in shapes) * args.layers
-    prog = rbq.Program([{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
+    prog = rbq.Program([{"planes": program_planes(rbq, args, layers[l][i][0]), "scales": layers[l][i][1],
+                         "x": xs[l][i], "y": ys[l][i]}
                         for l in range(args.layers) for i in range(len(groups))], num_planes=K)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -772,7 +794,8 @@ def other_layout_program(args, torch, rbq, workloads, wl, dev, layout):
         raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
     del prog, layers, xs, ys
     torch.cuda.empty_cache()
-    return {"layout": layout, "ops": len(groups) * args.layers, "bytes_per_step": nbytes,
+    return {"layout": layout, "planes_layout": args.planes_layout, "ops": len(groups) * args.layers,
+            "bytes_per_step": nbytes,
             "ms_per_step": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "mean_launch_us": round(us, 2), "kernel_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
@@ -845,8 +868,20 @@ def bench_decode(args):
     bytes_per_step = sum(per_call) * args.layers
     ops = [{"planes": layers[l][i][0], "scales": layers[l][i][1], "x": xs[l][i], "y": ys[l][i]}
            for l in range(args.layers) for i in range(len(groups))]
-    prog = rbq.Program(ops, num_planes=K)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # the program reads the tile layout by default: packed once, as when the
+    # weights are loaded (the pack's own rate is reported, outside the step)
+    pack = None
+    if args.planes_layout == "tiles":
+        pk = [(lambda p=op["planes"], t=torch.empty_like(rbq.pack_tiles(op["planes"])):
+               rbq.pack_tiles(p, tiles=t)) for op in ops[:len(groups)]]
+        pk_ms = graph_ms(torch, dev, pk, 3)
+        pk_bytes = sum(2 * op["planes"].numel() * 4 for op in ops[:len(groups)])
+        pack = {"what": "rbq_pack_tiles of one layer's planes (row layout read, tile layout written)",
+                "ms": round(pk_ms, 4), "GBps": round(pk_bytes / (pk_ms * 1e-3) / 1e9, 1)}
+        del pk
+    prog_ops = [dict(op, planes=program_planes(rbq, args, op["planes"])) for op in ops]
+    prog = rbq.Program(prog_ops, num_planes=K)
 
     def run_step():
         prog.run(status)
@@ -868,6 +903,28 @@ def bench_decode(args):
     if int(status.item()) != 0:
         raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
     prog_out = [y.clone() for y in ys[-1]]
+    rows_program = None
+    if args.planes_layout == "tiles":
+        # the same program on the row layout, for comparison
+        del prog, prog_ops
+        torch.cuda.empty_cache()
+        prog_r = rbq.Program(ops, num_planes=K)
+        run_r = (lambda: prog_r.run(status))
+        settle(torch, run_r)
+        r_us = event_launch_us(torch, run_r, stream, max(args.steps, 20))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_r()
+        torch.cuda.synchronize()
+        r_ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+        if int(status.item()) != 0:
+            raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
+        rows_program = {"planes_layout": "rows", "ms_per_step": round(r_ms, 4),
+                        "GBps": round(bytes_per_step / (r_ms * 1e-3) / 1e9, 1), "mean_launch_us": round(r_us, 2),
+                        "kernel_GBps": round(bytes_per_step / (r_us * 1e-6) / 1e9, 1),
+                        "output_equals_tiles": all(bool(torch.equal(a, b)) for a, b in zip(prog_out, ys[-1]))}
+        del prog_r
 
     # ---- the same step as one rbq_gemv launch per op, in a HIP graph
     def launch_step(st):
@@ -981,7 +1038,7 @@ def bench_decode(args):
 
     qat = None if args.no_extra else bench_qat(torch, rbq, workloads, dev)
 
-    prog_key = f"program_{args.layout}_{args.layers}layers"
+    prog_key = program_key(args)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1003,6 +1060,9 @@ def bench_decode(args):
                    "num_planes": K, "group_size": group, "tokens": 1,
                    "bytes_per_step": bytes_per_step, "launches_per_step": 1,
                    "kernel": "rbq_program_run (one persistent launch over every op of the step)",
+                   "planes_layout": ("tiles: RBQ_LAYOUT_TILES, 1 KB per 16-row x 512-column unit, packed once "
+                                     "from the row layout by rbq_pack_tiles" if args.planes_layout == "tiles"
+                                     else "rows: [K][out][in/32]"),
                    "activations": "one token per decoder-layer input (q/k/v and gate/up share theirs)",
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(bytes_per_step / (prog_us * 1e-6) / 1e9, 1),
@@ -1013,6 +1073,8 @@ def bench_decode(args):
                      "bytes_per_launch": bytes_per_step, "mean_launch_us": round(prog_us, 2),
                      "rocprof_mean_launch_us": rocprof_mean_us(prog_key)},
         "cpu_baseline": cpu,
+        "rows_layout_program": rows_program,
+        "pack_tiles": pack,
         "launches": {"ms_per_step": round(ms_launches, 4),
                      "GBps": round(bytes_per_step / (ms_launches * 1e-3) / 1e9, 1),
                      "launches_per_step": len(ops), "graph": True, "path_per_shape": shape_paths,

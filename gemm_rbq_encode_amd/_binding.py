@@ -34,6 +34,8 @@ RBQ_PROGRAM_MAX_OPS = 512
 RBQ_EPILOGUE_NONE = 0
 RBQ_EPILOGUE_SILU_MUL = 1
 RBQ_ENCODE_FORCE_SERIAL = 1
+RBQ_LAYOUT_ROWS = 0
+RBQ_LAYOUT_TILES = 1
 
 PATH_AUTO, PATH_VALU, PATH_DECODE, PATH_PREFILL, PATH_STREAM, PATH_FLAT, PATH_GROUP, PATH_SPLIT = (
     0, 1, 2, 3, 4, 5, 6, 7)
@@ -63,7 +65,7 @@ class ProgramOp(ctypes.Structure):
     """rbq_program_op."""
     _fields_ = [("planes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("out_features", ctypes.c_int32), ("in_features", ctypes.c_int32),
-                ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32)]
+                ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32), ("planes_layout", ctypes.c_uint32)]
 
 
 _lib = None
@@ -116,6 +118,8 @@ _SIGNATURES = {
                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_tiles_bytes": (ctypes.c_size_t, [Shape]),
+    "rbq_pack_tiles": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
     "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
@@ -467,6 +471,28 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None,
     check(lib().rbq_probe_read(buf.data_ptr(), n, sink.data_ptr(), _stream(buf, stream)), "rbq_probe_read")
 
 
+def tiles_bytes(s: Shape) -> int:
+    """rbq_tiles_bytes: bytes of the tile layout of shape s."""
+    return int(lib().rbq_tiles_bytes(s))
+
+
+def pack_tiles(planes: torch.Tensor, *, tiles: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """rbq_pack_tiles: the RBQ_LAYOUT_TILES copy of row-layout planes
+    (int32 [K][out][in/32]) as an int32 tensor [K][ceil(out/16)][ceil(in/512)][256]."""
+    _dev(planes, torch.int32, "planes")
+    K, out_f, words = planes.shape
+    s = shape(out_f, words * 32, K)
+    dims = (K, (out_f + 15) // 16, (words * 32 + 511) // 512, 256)
+    if tiles is None:
+        tiles = torch.empty(dims, dtype=torch.int32, device=planes.device)
+    else:
+        _dev(tiles, torch.int32, "tiles")
+        if tuple(tiles.shape) != dims:
+            raise ValueError(f"tiles must have shape {dims}")
+    check(lib().rbq_pack_tiles(planes.data_ptr(), s, tiles.data_ptr(), _stream(planes, stream)), "rbq_pack_tiles")
+    return tiles
+
+
 def encode_dual_workspace_bytes(s: Shape) -> int:
     return int(lib().rbq_encode_dual_workspace_bytes(s))
 
@@ -529,10 +555,11 @@ def gemv_dual(planes: torch.Tensor, g: torch.Tensor, h: torch.Tensor, x: torch.T
 class Program:
     """A list of one-token GEMVs run by one persistent launch (rbq_program_*).
 
-    ops: sequence of dicts with keys planes (int32 [K][out][in/32]), scales
-    (fp16 [K][out]), x (fp16 [in]), y (fp16 [out], or [out/2] with
-    epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue and wait_for
-    (index of an earlier op whose y this op reads; -1 = none).  The tensors
+    ops: sequence of dicts with keys planes (int32 [K][out][in/32], or the
+    tile layout [K][ceil(out/16)][ceil(in/512)][256] that pack_tiles
+    writes), scales (fp16 [K][out]), x (fp16 [in]), y (fp16 [out], or [out/2]
+    with epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue and
+    wait_for (index of an earlier op whose y this op reads; -1 = none).  The tensors
     are kept referenced; the image is built on the host, copied to the
     device once, and run() enqueues the launch on the current stream."""
 
@@ -548,7 +575,17 @@ class Program:
             _dev(s, torch.float16, "scales")
             _dev(x, torch.float16, "x")
             _dev(y, torch.float16, "y")
-            K, out_f, words = p.shape
+            if p.dim() == 4:   # tile layout: the shape comes from scales and x
+                layout = RBQ_LAYOUT_TILES
+                K = p.shape[0]
+                if s.dim() not in (2, 3) or s.shape[0] != K or s.numel() != K * s.shape[1]:
+                    raise ValueError(f"op {i}: scales must be [K][out] (or [K][out][1]) with tiled planes")
+                out_f, words = s.shape[1], x.numel() // 32
+                if tuple(p.shape) != (K, (out_f + 15) // 16, (words * 32 + 511) // 512, 256):
+                    raise ValueError(f"op {i}: tiled planes do not match scales and x")
+            else:
+                layout = RBQ_LAYOUT_ROWS
+                K, out_f, words = p.shape
             if K != num_planes:
                 raise ValueError(f"op {i}: {K} planes, the program has {num_planes}")
             ep = int(o.get("epilogue", RBQ_EPILOGUE_NONE))
@@ -557,7 +594,7 @@ class Program:
             if y.numel() < (out_f // 2 if ep == RBQ_EPILOGUE_SILU_MUL else out_f):
                 raise ValueError(f"op {i}: y too small")
             arr[i] = ProgramOp(p.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), out_f, words * 32, ep,
-                               int(o.get("wait_for", -1)))
+                               int(o.get("wait_for", -1)), layout)
             self._keep += [p, s, x, y]
             dev = x.device
         n = len(ops)

@@ -15,11 +15,12 @@
 // 16-wave workgroup per compute unit walks the whole list:
 //   * 12 stream waves keep a ring of 16-byte weight loads in flight that
 //     runs on from one op into the next, so HBM stays busy across op
-//     boundaries.  A load covers 64 bytes of 16 rows, half a 128-byte line
-//     of each; the wave's next unit reads the other halves, so the loads are
-//     ordinary cached ones (with the non-temporal hint the FETCH_SIZE
-//     counter showed 1.8 times the plane bytes read from HBM, without it
-//     1.07 times);
+//     boundaries.  In the row layout a load covers 64 bytes of 16 rows, half
+//     a 128-byte line of each; the wave's next unit reads the other halves,
+//     so the loads are ordinary cached ones (with the non-temporal hint the
+//     FETCH_SIZE counter showed 1.8 times the plane bytes read from HBM,
+//     without it 1.07 times).  In the tile layout (RBQ_LAYOUT_TILES) a load
+//     is one contiguous 1 KB block, 8 whole lines, which HBM serves faster;
 //   * 4 image waves build each op's activation image (x quantised into LDS,
 //     laid out as the MFMA B operand; two buffers, so op i+1's image is
 //     built while op i streams), and finish each op: the int32 partial sums
@@ -32,7 +33,10 @@
 //     the counter reaches the number of workgroups, from device-coherent
 //     loads of x.  Weight loads never wait, so the ring keeps streaming the
 //     next op's weights meanwhile.
-// A program without waits runs a kernel built without the waiting code.
+// A program without waits runs a kernel built without the waiting code, and
+// a program whose ops all read the tile layout one without the row layout's
+// addressing (the per-load choice between the two layouts cost that layout
+// its gain: 420 us per step against 408 us for the decode step).
 // Every wait is bounded (0.2 s of the real-time clock); a wait that runs out sets
 // RBQ_STATUS_PROGRAM_TIMEOUT in the status word and the kernel still runs to
 // its end.  The waits across workgroups need all workgroups resident: one
@@ -78,6 +82,7 @@ constexpr uint32_t PF_X_SHARED = 2u;   // x is written by an earlier op of the p
 constexpr uint32_t PF_SIGNAL = 4u;     // a later op waits for this one
 constexpr uint32_t PF_Y_SHARED = 8u;   // y is read (or written again) by a later op
 constexpr uint32_t PF_REUSE = 32u;     // same x as the op before: its image is used again
+constexpr uint32_t PF_TILES = 64u;     // planes in the tile layout (1 KB per 16-row, 512-column unit)
 constexpr int PF_WROT_SHIFT = 8;       // bits 8..11: rotation of the stream waves over the units
 
 // One op in device memory (64 bytes).
@@ -107,9 +112,12 @@ struct ProgHeader {
     uint32_t lds_bytes;
     uint32_t checksum;
     int32_t arena_bytes;   // LDS bytes of the image arena
-    int32_t waits;         // 1 when some op waits for another (the kernel with the waits)
+    int32_t kind;          // PK_* bits: which kernel runs the program
 };
 static_assert(sizeof(ProgHeader) == 32, "header layout");
+
+constexpr int32_t PK_WAITS = 1;        // some op waits for another: the kernel with the waits
+constexpr int32_t PK_TILES = 2;        // every op reads the tile layout
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
 // image arena what remains of the compute unit's LDS).
@@ -270,7 +278,7 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     return v;
 }
 
-template <int K, int RING, bool WAITS>
+template <int K, int RING, bool WAITS, bool TILES>
 __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
@@ -607,6 +615,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 
         // ---- load cursor: the next (op, unit) whose weights are requested
         int lop = 0, lu = 0, lu1 = 0, lt0 = 0, lnch = 1, lwords = 4, lout = 1;
+        bool ltiles = false;
         uint32_t lmagic = 0;
         const OpView op0 = op_view(table, 0);
         GLOBAL const uint32_t *lplanes = op0.planes;
@@ -623,25 +632,33 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     lwords = op.in >> 5;
                     lout = op.out;
                     lplanes = op.planes;
-                    lstride = (size_t)op.out * lwords;
+                    ltiles = TILES || (op.flags & PF_TILES) != 0;
+                    // words per plane: the tile layout pads rows and words to whole units
+                    lstride = ltiles ? (size_t)((op.out + TILE_ROWS - 1) / TILE_ROWS) * op.nchunks * 256
+                                     : (size_t)op.out * lwords;
                     lmagic = op.magic;
                     return;
                 }
                 ++lop;
             }
         };
-        // lanes (li, lg) read words 4lg .. 4lg+3 of row li of a unit's tile;
-        // past the last unit the last address is loaded again (a wave with no
-        // units at all reads the first words of op 0)
+        // lanes (li, lg) read words 4lg .. 4lg+3 of row li of a unit's tile
+        // (in the tile layout: bytes 16 lane .. 16 lane + 15 of the unit's
+        // block); past the last unit the last address is loaded again (a wave
+        // with no units at all reads the first words of op 0)
         GLOBAL const uint32_t *lastp = lplanes + min(4 * lg, (op0.in >> 5) - 4);
         size_t laststride = (size_t)op0.out * (op0.in >> 5);
         lseek();
         auto load_next = [&](v4u (&slot)[K]) {
             if (lop < n_ops) {
                 const int tq = (int)(((uint32_t)lu * lmagic) >> 21);
-                const int row = min((lt0 + tq) * TILE_ROWS + li, lout - 1);
-                const int wi = min((lu - tq * lnch) * CHUNK_WORDS + 4 * lg, lwords - 4);
-                lastp = lplanes + (size_t)row * lwords + wi;
+                if (TILES || ltiles) {
+                    lastp = lplanes + ((size_t)(lt0 + tq) * lnch + (lu - tq * lnch)) * 256 + 4 * lane;
+                } else {
+                    const int row = min((lt0 + tq) * TILE_ROWS + li, lout - 1);
+                    const int wi = min((lu - tq * lnch) * CHUNK_WORDS + 4 * lg, lwords - 4);
+                    lastp = lplanes + (size_t)row * lwords + wi;
+                }
                 laststride = lstride;
                 if (++lu == lu1) {
                     ++lop;
@@ -845,6 +862,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             return RBQ_ERR_INVALID_ARG;
         if (o.wait_for < -1 || o.wait_for >= i)
             return RBQ_ERR_INVALID_ARG;
+        if (o.planes_layout != RBQ_LAYOUT_ROWS && o.planes_layout != RBQ_LAYOUT_TILES)
+            return RBQ_ERR_INVALID_ARG;
         if (o.in_features % 128 != 0 || o.in_features > PG_MAX_CHUNKS * CHUNK_WORDS * 32 ||
             o.out_features > max_out)
             return RBQ_ERR_UNSUPPORTED;
@@ -852,7 +871,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             return RBQ_ERR_ALIGNMENT;
         xb[i] = (size_t)o.in_features * 2;
         yb[i] = (size_t)(o.epilogue == RBQ_EPILOGUE_SILU_MUL ? o.out_features / 2 : o.out_features) * 2;
-        pb[i] = (size_t)K * o.out_features * (o.in_features / 32) * 4;
+        pb[i] = o.planes_layout == RBQ_LAYOUT_TILES ? tiles_bytes(K, o.out_features, o.in_features)
+                                                    : (size_t)K * o.out_features * (o.in_features / 32) * 4;
         sb[i] = (size_t)K * o.out_features * 2;
     }
     // Ordering.  Workgroups run the ops in order, each on its own rows, so two
@@ -863,6 +883,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     for (int i = 0; i < n_ops; ++i) {
         if (ops[i].epilogue == RBQ_EPILOGUE_SILU_MUL)
             flags[i] |= PF_SILU;
+        if (ops[i].planes_layout == RBQ_LAYOUT_TILES)
+            flags[i] |= PF_TILES;
         if (ops[i].wait_for >= 0)
             flags[ops[i].wait_for] |= PF_SIGNAL;
         if (ranges_overlap(ops[i].y, yb[i], ops[i].x, xb[i]))
@@ -973,9 +995,11 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
-    h->waits = 0;
-    for (int i = 0; i < n_ops; ++i)
-        h->waits |= ops[i].wait_for >= 0 ? 1 : 0;
+    h->kind = PK_TILES;
+    for (int i = 0; i < n_ops; ++i) {
+        h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
+        h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
+    }
     h->checksum = image_checksum(img, image_bytes(n_ops, G));
     return RBQ_OK;
 }
@@ -987,7 +1011,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->K != 1 && h->K != 2) || (h->waits != 0 && h->waits != 1))
+        h->grid != program_num_cus() || (h->K != 1 && h->K != 2) || (h->kind & ~(PK_WAITS | PK_TILES)) != 0)
         return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
@@ -1005,21 +1029,24 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
                           hipStream_t st) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     const ProgHeader *hd = static_cast<const ProgHeader *>(image_dev);
-    // programs without waits take the kernel with the waiting code compiled out
-#define RBQ_LAUNCH_PROGRAM(KK, WW)                                                                        \
-    hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW>), dim3(h->grid), dim3(PG_THREADS),   \
+    // programs without waits take the kernel with the waiting code compiled
+    // out, programs of tiled ops only the one without row addressing
+#define RBQ_LAUNCH_PROGRAM(KK, WW, TT)                                                                    \
+    hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW, TT>), dim3(h->grid), dim3(PG_THREADS), \
                        h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status)
-    if (h->K == 1) {
-        if (h->waits)
-            RBQ_LAUNCH_PROGRAM(1, true);
-        else
-            RBQ_LAUNCH_PROGRAM(1, false);
-    } else {
-        if (h->waits)
-            RBQ_LAUNCH_PROGRAM(2, true);
-        else
-            RBQ_LAUNCH_PROGRAM(2, false);
+#define RBQ_LAUNCH_PROGRAM_K(KK)                                  \
+    switch (h->kind) {                                            \
+    case 0: RBQ_LAUNCH_PROGRAM(KK, false, false); break;          \
+    case PK_WAITS: RBQ_LAUNCH_PROGRAM(KK, true, false); break;    \
+    case PK_TILES: RBQ_LAUNCH_PROGRAM(KK, false, true); break;    \
+    default: RBQ_LAUNCH_PROGRAM(KK, true, true); break;           \
     }
+    if (h->K == 1) {
+        RBQ_LAUNCH_PROGRAM_K(1);
+    } else {
+        RBQ_LAUNCH_PROGRAM_K(2);
+    }
+#undef RBQ_LAUNCH_PROGRAM_K
 #undef RBQ_LAUNCH_PROGRAM
     return hipGetLastError();
 }

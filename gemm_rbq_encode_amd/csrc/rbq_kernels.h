@@ -114,6 +114,11 @@ hipError_t launch_qat_backward(const uint32_t *planes, const uint16_t *scales, i
 // Streaming-read probe (probe.hip): one launch reading `bytes` bytes.
 hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
+// Tile layout of the planes (tiles.hip): 16 rows x 512 columns of a plane per
+// contiguous 1 KB block; in % 128 == 0.
+size_t tiles_bytes(int K, int out, int in);
+hipError_t launch_pack_tiles(const uint32_t *planes, int K, int out, int in, uint32_t *tiles, hipStream_t st);
+
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);
 

@@ -377,9 +377,46 @@ rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16
 #define RBQ_STATUS_PROGRAM_MISMATCH 32u  /* image_dev does not hold the image
                                             passed on the host; nothing was run */
 
+/*
+ * Plane layouts an op of a program may read.
+ *
+ * RBQ_LAYOUT_ROWS is the layout every other call takes: uint32 [K][out][in/32],
+ * row r of plane k holds columns 32w .. 32w+31 in word w (RaBiT summary,
+ * section D "GPU implementation": 32 columns per 32-bit word).
+ *
+ * RBQ_LAYOUT_TILES holds the same bits reordered so that each unit of work
+ * of the one-token kernels -- 16 rows by 512 columns of one plane -- is one
+ * contiguous 1 KB block, read by one 64-lane load of 16 bytes per lane:
+ *   uint32 [K][T][C][4][16][4],  T = ceil(out / 16),  C = ceil(in / 512);
+ *   element [k][t][c][g][i][j] = word 16c + 4g + j of row 16t + i of plane k,
+ *   zero where that row (>= out) or word (>= in / 32) does not exist.
+ * A row-major 16-row unit is 16 runs of 64 bytes, half a 128-byte line each;
+ * the contiguous block is 8 whole lines.  rbq_pack_tiles writes this layout
+ * from the row layout once, when the weights are loaded.
+ */
+#define RBQ_LAYOUT_ROWS  0u
+#define RBQ_LAYOUT_TILES 1u
+
+/* Bytes of the tile layout of shape s (0 for an invalid shape). */
+size_t rbq_tiles_bytes(rbq_shape s);
+
+/*
+ * rbq_pack_tiles -- write the RBQ_LAYOUT_TILES copy of row-layout planes.
+ *   planes  device uint32 [K][out][in/32], 16-byte aligned (read only)
+ *   tiles   device, rbq_tiles_bytes(s) bytes, 16-byte aligned; every byte
+ *           is written, padding with zeros
+ * s.in_features % 128 == 0 (else RBQ_ERR_UNSUPPORTED); s.group_size does
+ * not change the planes and is only checked for validity.  out == 0 or
+ * in == 0 enqueues nothing.  Errors: RBQ_ERR_INVALID_ARG (null pointer, bad
+ * shape, tiles overlapping planes), RBQ_ERR_ALIGNMENT, RBQ_ERR_NO_DEVICE,
+ * RBQ_ERR_HIP.
+ */
+rbq_status rbq_pack_tiles(const uint32_t *planes, rbq_shape s, uint32_t *tiles, void *stream);
+
 /* One op of a program. */
 typedef struct rbq_program_op {
-    const uint32_t *planes;   /* device, [K][out][in/32], 16-byte aligned */
+    const uint32_t *planes;   /* device, 16-byte aligned: [K][out][in/32], or the
+                                 RBQ_LAYOUT_TILES copy (planes_layout) */
     const uint16_t *scales;   /* device, fp16 [K][out] (one scale per row), 2-byte aligned */
     const uint16_t *x;        /* device, fp16 [in], 16-byte aligned */
     uint16_t *y;              /* device, fp16 [out] ([out/2] with SILU_MUL), 2-byte aligned */
@@ -389,6 +426,8 @@ typedef struct rbq_program_op {
     int32_t wait_for;         /* -1, or an earlier op: this op reads x only after
                                  every op up to and including that one has
                                  written all of its y */
+    uint32_t planes_layout;   /* RBQ_LAYOUT_ROWS or RBQ_LAYOUT_TILES; the
+                                 results are the same bits in either */
 } rbq_program_op;
 
 /* Bytes of the program image for n_ops ops on the current device (0 when
@@ -412,8 +451,9 @@ size_t rbq_program_counters_bytes(int32_t n_ops);
  * wrote, i writes what j read, or both write it) must be ordered by a wait:
  * some op in j+1 .. i must have wait_for >= j.  An op's y may not overlap its
  * own x, or any op's planes or scales.
- * Errors: RBQ_ERR_INVALID_ARG (null pointer, bad shape or epilogue, wait_for
- * not an earlier op, an unordered overlap, image too small),
+ * Errors: RBQ_ERR_INVALID_ARG (null pointer, bad shape, epilogue or
+ * planes_layout, wait_for not an earlier op, an unordered overlap, image too
+ * small),
  * RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (num_planes > 2, in_features % 128
  * != 0 or > 16384, out_features too large, too many ops).
  */

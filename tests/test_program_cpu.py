@@ -10,8 +10,8 @@ import gemm_rbq_encode_amd as rbq
 MiB = 1 << 20
 
 
-def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1):
-    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for)
+def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1, layout=0):
+    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for, layout)
 
 
 def build(ops, K=2, nbytes=None):
@@ -102,3 +102,35 @@ def test_outputs_may_not_overlap_inputs_or_weights():
     assert build([op(W(0), W(1), A(0), W(0) + 4096)]) == rbq.RBQ_ERR_INVALID_ARG    # y inside the planes
     two = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), W(1))]                   # y on another op's scales
     assert build(two) == rbq.RBQ_ERR_INVALID_ARG
+
+
+def test_planes_layout():
+    assert build([op(W(0), W(1), A(0), A(1), layout=rbq.RBQ_LAYOUT_TILES)]) == rbq.RBQ_OK
+    mixed = [op(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2), layout=rbq.RBQ_LAYOUT_TILES)]
+    assert build(mixed) == rbq.RBQ_OK
+    assert build([op(W(0), W(1), A(0), A(1), layout=2)]) == rbq.RBQ_ERR_INVALID_ARG
+    # 250 x 640, K = 2: the row layout takes 2*250*20*4 = 40000 bytes, the
+    # tile layout 2 * 16 tiles * 2 chunks * 1 KB = 65536; a y between the two
+    # ends overlaps only the tiled planes
+    y = W(0) + 50000
+    assert build([op(W(0), W(1), A(0), y, out=250, inf=640)]) == rbq.RBQ_OK
+    assert build([op(W(0), W(1), A(0), y, out=250, inf=640, layout=rbq.RBQ_LAYOUT_TILES)]) == \
+        rbq.RBQ_ERR_INVALID_ARG
+
+
+def test_tiles_bytes_and_pack_arguments():
+    L = rbq.lib()
+    assert int(L.rbq_tiles_bytes(rbq.shape(250, 640, 2))) == 2 * 16 * 2 * 1024
+    assert int(L.rbq_tiles_bytes(rbq.shape(4096, 11008, 2))) == 2 * 256 * 22 * 1024
+    assert int(L.rbq_tiles_bytes(rbq.shape(16, 512, 1))) == 1024
+    assert int(L.rbq_tiles_bytes(rbq.shape(0, 512, 1))) == 0
+    assert int(L.rbq_tiles_bytes(rbq.shape(16, 100, 1))) == 0          # not a shape
+    s = rbq.shape(250, 640, 2)
+    assert L.rbq_pack_tiles(None, s, W(4), None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_pack_tiles(W(0), s, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_pack_tiles(W(0), rbq.shape(250, 96, 2), W(4), None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_pack_tiles(W(0) + 4, s, W(4), None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_pack_tiles(W(0), s, W(4) + 8, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_pack_tiles(W(0), s, W(0) + 39984, None) == rbq.RBQ_ERR_INVALID_ARG   # overlap
+    # (no call here passes every check: on a machine with a device it would
+    # launch on these fake addresses)
