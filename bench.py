@@ -100,7 +100,8 @@ def parse():
                     help="plane layout the decode program reads: tiles (RBQ_LAYOUT_TILES, packed once "
                          "from the row layout by rbq_pack_tiles) or rows ([K][out][in/32])")
     ap.add_argument("--workload", default="llama2_7b",
-                    choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill"],
+                    choices=["llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama2_13b_g128_program",
+                             "llama3_8b_prefill"],
                     help="the default is the headline decode GEMV; the others print their own line")
     ap.add_argument("--tokens", type=int, default=0, help="token count for llama2_7b_skinny (4 or 16)")
     ap.add_argument("--no-extra", action="store_true",
@@ -133,6 +134,14 @@ def main():
         counter_pass(args)
     elif args.workload == "llama2_7b":
         bench_decode(args)
+    elif args.workload == "llama2_13b_g128_program":
+        import torch
+
+        import gemm_rbq_encode_amd as rbq
+        import workloads
+        torch.cuda.set_device(0)
+        print(json.dumps(group_program_step(args, torch, rbq, workloads, torch.device("cuda:0"),
+                                            cpu_seconds=args.cpu_seconds)), flush=True)
     else:
         bench_layer_set(args)
 
@@ -312,6 +321,75 @@ def graph_ms(torch, dev, fns, reps):
     torch.cuda.synchronize()
     del g
     return e0.elapsed_time(e1) / reps
+
+
+def group_program_step(args, torch, rbq, workloads, dev, n_layers=40, cpu_seconds=4.0):
+    """The Llama-2-13B decode step with K = 4 and one scale per 128-column
+    group (QBB "Key results", W(4x1)A16g128), fused layout, n_layers layers,
+    each with its own copy of the weights (planes and scales in their tile
+    layouts, packed once), as ONE program launch: 4 GEMVs per layer, each
+    reading its own activations.  Reports whole-job GB/s of algorithmic
+    bytes, the kernel's mean launch time from HIP events, and the layer-0
+    outputs against rbq_gemv (the per-call g128 kernel) run on the same
+    inputs.  Returns the JSON object."""
+    wl = workloads.WORKLOADS["llama2_13b_g128"]
+    K, group = wl.num_planes, wl.group_size
+    groups, layers1, shapes, widths, Ws, p_enc, s_enc = decode_sets(torch, rbq, workloads, wl, dev, "fused", 1)
+    del Ws, p_enc, s_enc
+    base = layers1[0]
+    tiles = [[(rbq.pack_tiles(p), rbq.pack_scale_tiles(sc, sh.in_features)) for (p, sc), sh in zip(base, shapes)]
+             for _ in range(n_layers)]
+    xs = decode_activations(torch, workloads, wl, dev, "fused", widths, n_layers)
+    ys = [[torch.empty(sh.out_features, dtype=torch.float16, device=dev) for sh in shapes] for _ in range(n_layers)]
+    ops = [{"planes": tiles[l][i][0], "scales": tiles[l][i][1], "x": xs[l][i], "y": ys[l][i], "group_size": group,
+            "out_features": shapes[i].out_features} for l in range(n_layers) for i in range(len(groups))]
+    per_op = [gemv_bytes(sh.out_features, sh.in_features, K, sh.in_features // group) for sh in shapes]
+    nbytes = sum(per_op) * n_layers
+    prog = rbq.Program(ops, num_planes=K)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    run = (lambda: prog.run(status))
+    settle(torch, run)
+    us = event_launch_us(torch, run, stream, max(args.steps, 20))
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    if int(status.item()) != 0:
+        raise rbq.RbqError(rbq.RBQ_ERR_HIP, f"program status {int(status.item()):#x}")
+    # layer 0 against the per-call kernel on the row layouts (both are held
+    # to the oracle's bound in the tests; they add their fp32 sums in
+    # different orders)
+    diff = 0.0
+    for i, (p, sc) in enumerate(base):
+        ref = rbq.gemv(p, sc, xs[0][i], group)
+        diff = max(diff, float((ys[0][i].float() - ref.float()).abs().max() / ref.float().abs().max().clamp_min(1e-30)))
+    line = {"metric": f"K={K} g128 batch-1 GEMV effective GB/s on Llama-2-13B layers, decode step as one program",
+            "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "ms_per_step": round(ms, 4),
+            "dtype": DTYPE_INT8_LIMBS,
+            "config": {"workload": "llama2_13b_g128_decode_program", "layers": n_layers, "layout": "fused",
+                       "ops_per_layer": {name: f"{sh.out_features}x{sh.in_features}"
+                                         for (name, _), sh in zip(groups, shapes)},
+                       "num_planes": K, "group_size": group, "tokens": 1, "bytes_per_step": nbytes,
+                       "planes_layout": "tiles (rbq_pack_tiles), scales as scale tiles (rbq_pack_scale_tiles)"},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None, "kernel": f"gemv_program_kernel<{K}> g128 ({len(ops)} ops)",
+                         "mean_launch_us": round(us, 2)},
+            "layer0_max_rel_diff_vs_rbq_gemv": diff, "cpu_baseline": None}
+    if cpu_seconds > 0:
+        samples = [(p.cpu().numpy().view(np.uint32), sc.cpu().numpy().view(np.uint16),
+                    xs[0][i].cpu().numpy().view(np.uint16)[None, :], group, per_op[i])
+                   for i, (p, sc) in enumerate(base)]
+        line["cpu_baseline"] = oracle_baseline(samples, cpu_seconds, max_reps=20)
+        line["cpu_baseline"]["sample"] = "layer 0 at M=1: " + line["cpu_baseline"]["sample"]
+    del prog, tiles, xs, ys, base, layers1
+    torch.cuda.empty_cache()
+    return line
 
 
 def bench_layer_set(args):
@@ -1035,6 +1113,10 @@ def bench_decode(args):
                                            if k in sub}
             if "encode_refit_per_shape" in sub:
                 others[f"{name}_m{tokens}"]["encode_refit_per_shape"] = sub["encode_refit_per_shape"]
+
+    if not args.no_extra:
+        others["llama2_13b_g128_program"] = group_program_step(args, torch, rbq, workloads, dev,
+                                                               cpu_seconds=min(args.cpu_seconds, 4.0))
 
     qat = None if args.no_extra else bench_qat(torch, rbq, workloads, dev)
 

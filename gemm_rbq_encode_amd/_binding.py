@@ -65,7 +65,8 @@ class ProgramOp(ctypes.Structure):
     """rbq_program_op."""
     _fields_ = [("planes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("out_features", ctypes.c_int32), ("in_features", ctypes.c_int32),
-                ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32), ("planes_layout", ctypes.c_uint32)]
+                ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32), ("planes_layout", ctypes.c_uint32),
+                ("group_size", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,6 +121,8 @@ _SIGNATURES = {
     "rbq_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_tiles_bytes": (ctypes.c_size_t, [Shape]),
     "rbq_pack_tiles": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_scale_tiles_bytes": (ctypes.c_size_t, [Shape]),
+    "rbq_pack_scale_tiles": (ctypes.c_int, [ctypes.c_void_p, Shape, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_set_path": (ctypes.c_int, [ctypes.c_int]),
     "rbq_select_path": (ctypes.c_int, [Shape, ctypes.c_int32]),
     "rbq_set_stream_split": (ctypes.c_int32, [ctypes.c_int32]),
@@ -493,6 +496,32 @@ def pack_tiles(planes: torch.Tensor, *, tiles: torch.Tensor | None = None, strea
     return tiles
 
 
+def scale_tiles_bytes(s: Shape) -> int:
+    """rbq_scale_tiles_bytes: bytes of the scale tiles of a g128 shape (0 if none)."""
+    return int(lib().rbq_scale_tiles_bytes(s))
+
+
+def pack_scale_tiles(scales: torch.Tensor, in_features: int, *, tiles: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """rbq_pack_scale_tiles: the scale tiles of g128 scales (fp16 [K][out][in/128])
+    as an fp16 tensor [ceil(out/16)][ceil(in/512)][K*64]."""
+    _dev(scales, torch.float16, "scales")
+    if scales.dim() != 3 or scales.shape[2] * 128 != in_features:
+        raise ValueError("scales must be [K][out][in/128]")
+    K, out_f, _ = scales.shape
+    s = shape(out_f, in_features, K, 128)
+    dims = ((out_f + 15) // 16, (in_features + 511) // 512, K * 64)
+    if tiles is None:
+        tiles = torch.empty(dims, dtype=torch.float16, device=scales.device)
+    else:
+        _dev(tiles, torch.float16, "tiles")
+        if tuple(tiles.shape) != dims:
+            raise ValueError(f"tiles must have shape {dims}")
+    check(lib().rbq_pack_scale_tiles(scales.data_ptr(), s, tiles.data_ptr(), _stream(scales, stream)),
+          "rbq_pack_scale_tiles")
+    return tiles
+
+
 def encode_dual_workspace_bytes(s: Shape) -> int:
     return int(lib().rbq_encode_dual_workspace_bytes(s))
 
@@ -559,7 +588,9 @@ class Program:
     tile layout [K][ceil(out/16)][ceil(in/512)][256] that pack_tiles
     writes), scales (fp16 [K][out]), x (fp16 [in]), y (fp16 [out], or [out/2]
     with epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue and
-    wait_for (index of an earlier op whose y this op reads; -1 = none).  The tensors
+    wait_for (index of an earlier op whose y this op reads; -1 = none).
+    g128 ops (group_size=128, every op of the program) take tiled planes,
+    the scale tiles of pack_scale_tiles as scales, and out_features.  The tensors
     are kept referenced; the image is built on the host, copied to the
     device once, and run() enqueues the launch on the current stream."""
 
@@ -575,7 +606,16 @@ class Program:
             _dev(s, torch.float16, "scales")
             _dev(x, torch.float16, "x")
             _dev(y, torch.float16, "y")
-            if p.dim() == 4:   # tile layout: the shape comes from scales and x
+            gs = int(o.get("group_size", 0))
+            if gs:
+                if p.dim() != 4 or "out_features" not in o:
+                    raise ValueError(f"op {i}: g128 ops take tiled planes and out_features")
+                layout = RBQ_LAYOUT_TILES
+                K, out_f, words = p.shape[0], int(o["out_features"]), x.numel() // 32
+                if tuple(p.shape) != (K, (out_f + 15) // 16, (words * 32 + 511) // 512, 256) or \
+                        tuple(s.shape) != (p.shape[1], p.shape[2], K * 64):
+                    raise ValueError(f"op {i}: tiled planes or scale tiles do not match out_features and x")
+            elif p.dim() == 4:   # tile layout: the shape comes from scales and x
                 layout = RBQ_LAYOUT_TILES
                 K = p.shape[0]
                 if s.dim() not in (2, 3) or s.shape[0] != K or s.numel() != K * s.shape[1]:
@@ -589,12 +629,12 @@ class Program:
             if K != num_planes:
                 raise ValueError(f"op {i}: {K} planes, the program has {num_planes}")
             ep = int(o.get("epilogue", RBQ_EPILOGUE_NONE))
-            if x.numel() != words * 32 or s.numel() < K * out_f:
+            if x.numel() != words * 32 or (not gs and s.numel() < K * out_f):
                 raise ValueError(f"op {i}: x or scales do not match the planes")
             if y.numel() < (out_f // 2 if ep == RBQ_EPILOGUE_SILU_MUL else out_f):
                 raise ValueError(f"op {i}: y too small")
             arr[i] = ProgramOp(p.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), out_f, words * 32, ep,
-                               int(o.get("wait_for", -1)), layout)
+                               int(o.get("wait_for", -1)), layout, gs)
             self._keep += [p, s, x, y]
             dev = x.device
         n = len(ops)

@@ -598,6 +598,34 @@ rbq_status rbq_pack_tiles(const uint32_t *planes, rbq_shape s, uint32_t *tiles, 
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+size_t rbq_scale_tiles_bytes(rbq_shape s) {
+    if (rbq_check_shape(s) != RBQ_OK || s.group_size != 128 || s.num_planes % 2 != 0)
+        return 0;
+    return rbq::scale_tiles_bytes(s.num_planes, s.out_features, s.in_features);
+}
+
+rbq_status rbq_pack_scale_tiles(const uint16_t *scales, rbq_shape s, uint16_t *tiles, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (scales == nullptr || tiles == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (s.group_size != 128 || s.num_planes % 2 != 0)
+        return RBQ_ERR_UNSUPPORTED;
+    if (!aligned(scales, 2) || !aligned(tiles, 16))
+        return RBQ_ERR_ALIGNMENT;
+    const uintptr_t p0 = (uintptr_t)scales, p1 = p0 + rbq_scales_bytes(s);
+    const uintptr_t t0 = (uintptr_t)tiles, t1 = t0 + rbq_scale_tiles_bytes(s);
+    if (p0 < t1 && t0 < p1)
+        return RBQ_ERR_INVALID_ARG;
+    st = device_present();
+    if (st != RBQ_OK || s.out_features == 0 || s.in_features == 0)
+        return st;
+    hipError_t e = rbq::launch_pack_scale_tiles(scales, s.num_planes, s.out_features, s.in_features, tiles,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 int32_t rbq_last_hip_error(void) { return g_last_hip_error; }
 
 const char *rbq_status_string(rbq_status st) {

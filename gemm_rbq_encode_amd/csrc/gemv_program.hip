@@ -75,6 +75,7 @@ constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wai
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
 constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
 constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
+constexpr int PG_MAX_G = PG_MAX_CHUNKS * 4;                // 128-column groups of the widest input
 
 // flags of an op
 constexpr uint32_t PF_SILU = 1u;       // (gate, up) row pairs -> silu(gate) * up
@@ -118,10 +119,12 @@ static_assert(sizeof(ProgHeader) == 32, "header layout");
 
 constexpr int32_t PK_WAITS = 1;        // some op waits for another: the kernel with the waits
 constexpr int32_t PK_TILES = 2;        // every op reads the tile layout
+constexpr int32_t PK_GROUP = 4;        // g128 ops (scales per 128-column group, in the scale tile layout)
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
-// image arena what remains of the compute unit's LDS).
-template <int K>
+// image arena what remains of the compute unit's LDS).  Programs of g128 ops
+// (GROUP) also keep the sum of q over every 128-column group of each x.
+template <int K, bool GROUP>
 struct PgShared {
     int img_cnt;                              // image waves' publications: 4 per op
     int sdone[PG_SLOTS];                      // stream waves done with an op, by op slot (i % PG_SLOTS)
@@ -131,8 +134,15 @@ struct PgShared {
     uint32_t wmax[PG_SLOTS][PG_PREP];
     double wsum[PG_SLOTS][PG_PREP];                 // sums of q (exact: integers below 2^53)
     int shs[PG_SLOTS];
-    uint16_t sc_lds[PG_SLOTS][K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+    uint16_t sc_lds[PG_SLOTS][GROUP ? 1 : K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+    int gsum[PG_SLOTS][GROUP ? PG_MAX_G : 1];         // g128: sum of q over each group (|sum| < 2^30)
 };
+
+// LDS ints per op slot of partial sums: per-row ops add int32 tile sums
+// [tile][plane][limb][row]; g128 ops store fp32 [tile][stream wave][row].
+__host__ __device__ constexpr int red_op_ints(int K, bool group) {
+    return PG_MAX_TILES * (group ? PG_STREAM : K * NC) * TILE_ROWS;
+}
 
 // Op counters: each op's count of finished workgroups is split over
 // PG_CSPLIT words (workgroup b adds to word b % PG_CSPLIT), each on its own
@@ -160,8 +170,9 @@ size_t program_lds_limit() {
 
 // Dynamic LDS a program may take: the limit less the kernel's fixed LDS
 // (and 256 bytes for its alignment).
-size_t program_dynamic_lds(int K) {
-    const size_t fixed = K == 1 ? sizeof(PgShared<1>) : sizeof(PgShared<2>);
+size_t program_dynamic_lds(int K, bool group) {
+    const size_t fixed = group ? (K == 2 ? sizeof(PgShared<2, true>) : sizeof(PgShared<4, true>))
+                               : (K == 1 ? sizeof(PgShared<1, false>) : sizeof(PgShared<2, false>));
     return program_lds_limit() - fixed - 256;
 }
 
@@ -226,6 +237,17 @@ __device__ __forceinline__ bool lds_wait_ge(int *counter, int target, int *abort
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// x plus x of the lane CTRL names within the row of 16 lanes (0 past the row's edge)
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_add_i32(int x) {
+    return x + __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_add_f32(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF,
+                                                                      0xF, false));
+}
+
 template <class T>
 __device__ __forceinline__ T *rflp(T *p) {
     const uint64_t u = (uint64_t)(uintptr_t)p;
@@ -278,12 +300,12 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     return v;
 }
 
-template <int K, int RING, bool WAITS, bool TILES>
+template <int K, int RING, bool WAITS, bool TILES, bool GROUP>
 __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ PgShared<K> sh;
+    __shared__ PgShared<K, GROUP> sh;
     int &img_cnt = sh.img_cnt;
     int *sdone = sh.sdone;
     int &isync = sh.isync;
@@ -292,6 +314,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     auto &wsum = sh.wsum;
     auto &shs = sh.shs;
     auto &sc_lds = sh.sc_lds;
+    auto &gsum = sh.gsum;
 
     if (hdr->magic != PG_MAGIC || hdr->n_ops != n_ops || hdr->checksum != checksum || hdr->K != K ||
         hdr->grid != (int)gridDim.x) {
@@ -312,7 +335,8 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16], op table
     const int pad = hdr->arena_bytes;
     int *red0 = reinterpret_cast<int *>(lds + pad + 16);
-    constexpr int RED_OP = PG_MAX_TILES * K * NC * TILE_ROWS;
+    constexpr int RED_OP = red_op_ints(K, GROUP);
+    constexpr int RED_TILE = RED_OP / PG_MAX_TILES;                          // ints per tile
     ProgOp *table = reinterpret_cast<ProgOp *>(red0 + PG_SLOTS * RED_OP);   // the op table, [n_ops]
 
     // A wait that runs out only raises the LDS flag (the status word is
@@ -369,14 +393,23 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             const int row = t0 * TILE_ROWS + tid;
             const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
             float y = 0.0f;
-            if (rowok) {
+            if (GROUP && rowok) {
+                // the stream waves' per-(tile, wave) slots, added in wave order
+                const float *rf = reinterpret_cast<const float *>(red);
+                const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+                float acc = 0.0f;
+#pragma unroll
+                for (int w = 0; w < PG_STREAM; ++w)
+                    acc += rf[(tl * PG_STREAM + w) * TILE_ROWS + i];
+                y = __builtin_ldexpf(acc, -shs[par]);
+            } else if (rowok) {
                 double sx = 0.0;
 #pragma unroll
                 for (int v = 0; v < PG_PREP; ++v)
                     sx += wsum[par][v];
                 const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
+                for (int k = 0; k < (GROUP ? 1 : K); ++k) {
                     const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
                     const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                                      65536.0 * (double)rp[2 * TILE_ROWS];
@@ -404,7 +437,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     op.y[row] = h;
             }
             img_sync();   // every partial sum of the op has been read
-            for (int e = tid; e < ntl * K * NC * TILE_ROWS; e += PG_PREP_THREADS)
+            for (int e = tid; e < ntl * RED_TILE; e += PG_PREP_THREADS)
                 red[e] = 0;
             if (tid == 0)
                 __hip_atomic_store(&sdone[par], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -477,12 +510,14 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             }
         };
         auto load_scales = [&](const OpView &op) {
+            if (GROUP)   // g128 scales travel with the weights, to the stream waves
+                return;
             int t0, ntl;
             op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
             const int row = t0 * TILE_ROWS + tid;
             const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
 #pragma unroll
-            for (int k = 0; k < K; ++k)
+            for (int k = 0; k < (GROUP ? 1 : K); ++k)
                 a_bits[k] = rowok ? op.scales[(size_t)k * op.out + row] : (uint16_t)0;
         };
 
@@ -497,9 +532,14 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // with it) serve again; only the scales are op i's own
         auto reuse = [&](int i) {
             const int par = i % PG_SLOTS, prev = (i + PG_SLOTS - 1) % PG_SLOTS;
+            if (GROUP) {
+                for (int g = tid; g < PG_MAX_G; g += PG_PREP_THREADS)
+                    gsum[par][g] = gsum[prev][g];
+            } else {
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                sc_lds[par][k][tid] = a_bits[k];
+                for (int k = 0; k < K; ++k)
+                    sc_lds[par][k][tid] = a_bits[k];
+            }
             if (lane == 0)
                 wsum[par][wave] = wsum[prev][wave];
             if (tid == 0)
@@ -525,9 +565,11 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             const uint32_t mw = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
             if (lane == 0)
                 wmax[par][wave] = mw;
+            if (!GROUP) {
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                sc_lds[par][k][tid] = a_bits[k];
+                for (int k = 0; k < K; ++k)
+                    sc_lds[par][k][tid] = a_bits[k];
+            }
             img_sync();
             uint32_t mx = 0;
 #pragma unroll
@@ -545,6 +587,8 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 #pragma unroll
             for (int j = 0; j < PG_MAX_XU; ++j) {
                 const int H = tid + j * PG_PREP_THREADS;
+                if (GROUP)
+                    psum = 0;
                 if (j < xu && H < hpad) {
                     const float scale = H < nh ? __builtin_ldexpf(1.0f, sh) : 0.0f;
                     const int w = H >> 1, eh = H & 1;
@@ -568,10 +612,22 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                         *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
                     }
                 }
+                if (GROUP && j < xu) {
+                    // the 8 half-words of a 128-column group sit in 8
+                    // consecutive lanes; lane 8m + 7 adds them
+                    int g = psum;
+                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(1)>(g);
+                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(2)>(g);
+                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(4)>(g);
+                    if ((lane & 7) == 7 && H < hpad)
+                        gsum[par][H >> 3] = g;
+                }
             }
-            const double ws = wave_sum_f64_dpp((double)psum);   // sum of q over the wave's columns (exact)
-            if (lane == 0)
-                wsum[par][wave] = ws;
+            if (!GROUP) {
+                const double ws = wave_sum_f64_dpp((double)psum);   // sum of q over the wave's columns (exact)
+                if (lane == 0)
+                    wsum[par][wave] = ws;
+            }
             if (tid == 0)
                 shs[par] = sh;
             publish();
@@ -619,6 +675,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         uint32_t lmagic = 0;
         const OpView op0 = op_view(table, 0);
         GLOBAL const uint32_t *lplanes = op0.planes;
+        GLOBAL const uint16_t *lscales = op0.scales;   // g128: the op's scale tiles
         size_t lstride = 0;
         auto lseek = [&]() {   // the first op from lop on that gives this wave units
             while (lop < n_ops) {
@@ -632,6 +689,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     lwords = op.in >> 5;
                     lout = op.out;
                     lplanes = op.planes;
+                    lscales = op.scales;
                     ltiles = TILES || (op.flags & PF_TILES) != 0;
                     // words per plane: the tile layout pads rows and words to whole units
                     lstride = ltiles ? (size_t)((op.out + TILE_ROWS - 1) / TILE_ROWS) * op.nchunks * 256
@@ -648,12 +706,22 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // with no units at all reads the first words of op 0)
         GLOBAL const uint32_t *lastp = lplanes + min(4 * lg, (op0.in >> 5) - 4);
         size_t laststride = (size_t)op0.out * (op0.in >> 5);
+        // g128 (tile layouts only): lane (li, lg) loads, per pair of planes, the
+        // 16 bytes with the scales of rows 4lg .. 4lg+3 of the unit's group
+        // min(li / 3, 3) (the MFMA column li = 3 group + limb it holds)
+        constexpr int KS = GROUP ? K / 2 : 0;
+        constexpr int KR = K + KS;
+        const int sc_lane = (min(li / 3, 3) * 4 + lg) * 8;
+        GLOBAL const uint16_t *lastsp = lscales + sc_lane;
         lseek();
-        auto load_next = [&](v4u (&slot)[K]) {
+        auto load_next = [&](v4u (&slot)[KR]) {
             if (lop < n_ops) {
                 const int tq = (int)(((uint32_t)lu * lmagic) >> 21);
                 if (TILES || ltiles) {
-                    lastp = lplanes + ((size_t)(lt0 + tq) * lnch + (lu - tq * lnch)) * 256 + 4 * lane;
+                    const size_t unit = (size_t)(lt0 + tq) * lnch + (lu - tq * lnch);
+                    lastp = lplanes + unit * 256 + 4 * lane;
+                    if (GROUP)
+                        lastsp = lscales + unit * (K * 64) + sc_lane;
                 } else {
                     const int row = min((lt0 + tq) * TILE_ROWS + li, lout - 1);
                     const int wi = min((lu - tq * lnch) * CHUNK_WORDS + 4 * lg, lwords - 4);
@@ -668,6 +736,9 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 slot[k] = *reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride);
+#pragma unroll
+            for (int pp = 0; pp < KS; ++pp)
+                slot[K + pp] = *reinterpret_cast<GLOBAL const v4u *>(lastsp + pp * 128);
         };
 
         // ---- consume cursor: the op and unit the MFMAs work on
@@ -700,10 +771,11 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             }
         };
 
-        v4i acc[K][8];
-        uint32_t tprev[K][4];
+        // per-row ops: running int32 totals per plane and bit position
+        v4i acc[GROUP ? 1 : K][8];
+        uint32_t tprev[GROUP ? 1 : K][4];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
+        for (int k = 0; k < (GROUP ? 1 : K); ++k) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 acc[k][j] = (v4i){0, 0, 0, 0};
@@ -711,71 +783,148 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             for (int v = 0; v < 4; ++v)
                 tprev[k][v] = 0u;
         }
+        // g128 ops: MFMA column li = 3t + l is limb l of the chunk's group t,
+        // fed only from lane group t (the B operand is zero elsewhere), so
+        // C[i][li] is row i's sum over group t alone; the lanes apply the
+        // group's scales and keep fp32 running sums yv of rows 4lg .. 4lg+3
+        // (times 2^-(8l+1); cl restores it at the flush, where the 16 columns
+        // of each row are added).  2 S - sum q = sum_l 2^(8l+1) (T_l - [l=0] sum q / 2).
+        const bool g_live = li < 3 * 4;
+        const bool g_b = g_live && li / 3 == lg;
+        const int g_t = min(li / 3, 3);
+        const float g_zq = (g_live && li % 3 == 0) ? -0.5f : 0.0f;
+        const float g_cl = g_live ? __builtin_ldexpf(1.0f, 8 * (li % 3) + 1) : 0.0f;
+        float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-        v4u ring[RING][K];
+        v4u ring[RING][KR];
 #pragma unroll
         for (int d = 0; d < RING; ++d)
             load_next(ring[d]);
         cseek();
 
-        auto consume = [&](const v4u (&wv)[K]) {
+        auto consume = [&](const v4u (&wv)[KR]) {
             const int par = cop % PG_SLOTS;
-            const unsigned char *bp = li < NC ? lds + cimg + (lg * NC + li) * 16 + cchunk * IMG_CHUNK
+            if constexpr (GROUP) {
+                ++cu;
+                const bool tile_end = cchunk + 1 == cnch;
+                const bool op_end = cu == cu1;
+                const unsigned char *bp = g_b ? lds + cimg + (lg * NC + li - 3 * lg) * 16 + cchunk * IMG_CHUNK
                                               : lds + pad;
-            const int bstride = li < NC ? 4 * NC * 16 : 0;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const v4i bv = *reinterpret_cast<const v4i *>(bp + s * bstride);
-                const uint32_t mask = 0x01010101u << s;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const v4i av = (v4i){(int)(wv[k].x & mask), (int)(wv[k].y & mask), (int)(wv[k].z & mask),
-                                         (int)(wv[k].w & mask)};
-                    acc[k][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[k][s], 0, 0, 0);
-                }
-            }
-            // next chunk; at a tile's end or the wave's last unit of the op, add
-            // T = sum_{s<7} 2^(7-s) acc_s - acc_7 = 2^7 sum(bit * limb) into LDS
-            ++cu;
-            const bool tile_end = ++cchunk == cnch;
-            const bool op_end = cu == cu1;
-            if (tile_end || op_end) {
-                // (the empty asm keeps the recombination below inside this
-                // branch: hoisted, it cost ~80 VALU operations on every unit)
+                const int bstride = g_b ? 4 * NC * 16 : 0;
+                v4i ga[K];
 #pragma unroll
                 for (int k = 0; k < K; ++k)
+                    ga[k] = (v4i){0, 0, 0, 0};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        asm volatile("" : "+v"(acc[k][j]));
-                // The accumulators are never cleared: T is linear in them, so
-                // the tile's share is T now less T at the previous flush, all
-                // modulo 2^32 (the int32 sums wrap; the share stays below
-                // 2^29).  That saves clearing 64 registers per flush.
-                int *rp = red0 + par * RED_OP + ctile * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
+                for (int s = 0; s < 8; ++s) {
+                    const v4i bv = *reinterpret_cast<const v4i *>(bp + s * bstride);
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const v4i av = (v4i){(int)((wv[k].x >> s) & 0x01010101u), (int)((wv[k].y >> s) & 0x01010101u),
+                                             (int)((wv[k].z >> s) & 0x01010101u), (int)((wv[k].w >> s) & 0x01010101u)};
+                        ga[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, ga[k], 0, 0, 0);
+                    }
+                }
+                // The results of the last MFMAs are read next.  With only the
+                // compiler's wait states between the last MFMA and the first
+                // read, that read returned a stale first result register now
+                // and then (rows 4q of a tile wrong, differently from run to
+                // run); 16 more wait states here, tied to the result registers.
+                if constexpr (K == 2)
+                    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(ga[0]), "+v"(ga[1]));
+                else
+                    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(ga[0]), "+v"(ga[1]), "+v"(ga[2]), "+v"(ga[3]));
+                const float gq = (float)gsum[par][cchunk * 4 + g_t];
 #pragma unroll
                 for (int k = 0; k < K; ++k)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        uint32_t t = (uint32_t)acc[k][0][v];
-#pragma unroll
-                        for (int q = 1; q < 7; ++q)
-                            t = (t << 1) + (uint32_t)acc[k][q][v];
-                        t = (t << 1) - (uint32_t)acc[k][7][v];
-                        const uint32_t share = t - tprev[k][v];
-                        tprev[k][v] = t;
-                        if (li < NC)
-                            __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)share, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                        const uint32_t hw = wv[K + k / 2][(k & 1) * 2 + (v >> 1)];
+                        const float a = h2f((uint16_t)(hw >> (16 * (v & 1))));
+                        yv[v] = __builtin_fmaf(a, __builtin_fmaf(g_zq, gq, (float)ga[k][v]), yv[v]);
                     }
-            }
-            if (tile_end) {
-                cchunk = 0;
-                ++ctile;
-            }
-            if (op_end) {
-                report(cop);
-                ++cop;
-                cseek();
+                if (tile_end || op_end) {
+                    float *rf = reinterpret_cast<float *>(red0 + par * RED_OP) + (ctile * PG_STREAM + sw) * TILE_ROWS;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = yv[v] * g_cl;
+                        x = dpp_row_add_f32<RBQ_DPP_ROW_SHR(1)>(x);
+                        x = dpp_row_add_f32<RBQ_DPP_ROW_SHR(2)>(x);
+                        x = dpp_row_add_f32<RBQ_DPP_ROW_SHR(4)>(x);
+                        x = dpp_row_add_f32<RBQ_DPP_ROW_SHR(8)>(x);
+                        if (li == 15)
+                            rf[4 * lg + v] = x;
+                        yv[v] = 0.0f;
+                    }
+                }
+                // next chunk (as selects: written as two branches, the compiler
+                // merged them into one increment through a pointer to either
+                // variable, which put both on the stack)
+                ctile += tile_end ? 1 : 0;
+                cchunk = tile_end ? 0 : cchunk + 1;
+                if (op_end) {
+                    report(cop);
+                    ++cop;
+                    cseek();
+                }
+            } else {
+                const unsigned char *bp = li < NC ? lds + cimg + (lg * NC + li) * 16 + cchunk * IMG_CHUNK
+                                                  : lds + pad;
+                const int bstride = li < NC ? 4 * NC * 16 : 0;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const v4i bv = *reinterpret_cast<const v4i *>(bp + s * bstride);
+                    const uint32_t mask = 0x01010101u << s;
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const v4i av = (v4i){(int)(wv[k].x & mask), (int)(wv[k].y & mask), (int)(wv[k].z & mask),
+                                             (int)(wv[k].w & mask)};
+                        acc[k][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[k][s], 0, 0, 0);
+                    }
+                }
+                // next chunk; at a tile's end or the wave's last unit of the op, add
+                // T = sum_{s<7} 2^(7-s) acc_s - acc_7 = 2^7 sum(bit * limb) into LDS
+                ++cu;
+                const bool tile_end = ++cchunk == cnch;
+                const bool op_end = cu == cu1;
+                if (tile_end || op_end) {
+                    // (the empty asm keeps the recombination below inside this
+                    // branch: hoisted, it cost ~80 VALU operations on every unit)
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            asm volatile("" : "+v"(acc[k][j]));
+                    // The accumulators are never cleared: T is linear in them, so
+                    // the tile's share is T now less T at the previous flush, all
+                    // modulo 2^32 (the int32 sums wrap; the share stays below
+                    // 2^29).  That saves clearing 64 registers per flush.
+                    int *rp = red0 + par * RED_OP + ctile * K * NC * TILE_ROWS + li * TILE_ROWS + 4 * lg;
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            uint32_t t = (uint32_t)acc[k][0][v];
+#pragma unroll
+                            for (int q = 1; q < 7; ++q)
+                                t = (t << 1) + (uint32_t)acc[k][q][v];
+                            t = (t << 1) - (uint32_t)acc[k][7][v];
+                            const uint32_t share = t - tprev[k][v];
+                            tprev[k][v] = t;
+                            if (li < NC)
+                                __hip_atomic_fetch_add(rp + k * NC * TILE_ROWS + v, (int)share, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                }
+                if (tile_end) {
+                    cchunk = 0;
+                    ++ctile;
+                }
+                if (op_end) {
+                    report(cop);
+                    ++cop;
+                    cseek();
+                }
             }
         };
 
@@ -842,8 +991,14 @@ size_t program_bytes(int n_ops) {
 }
 
 rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *image, size_t bytes) {
-    if (ops == nullptr || image == nullptr || n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS || K < 1 || K > 2)
-        return n_ops > RBQ_PROGRAM_MAX_OPS || K > 2 ? RBQ_ERR_UNSUPPORTED : RBQ_ERR_INVALID_ARG;
+    if (ops == nullptr || image == nullptr || n_ops < 1 || n_ops > RBQ_PROGRAM_MAX_OPS || K < 1 || K > 8)
+        return n_ops > RBQ_PROGRAM_MAX_OPS ? RBQ_ERR_UNSUPPORTED : RBQ_ERR_INVALID_ARG;
+    // a program is of per-row ops (K <= 2) or of g128 ops (K = 2 or 4) alone
+    if (ops[0].group_size != 0 && ops[0].group_size != 128)
+        return RBQ_ERR_INVALID_ARG;
+    const bool group = ops[0].group_size == 128;
+    if (group ? (K != 2 && K != 4) : K > 2)
+        return RBQ_ERR_UNSUPPORTED;
     const int G = program_num_cus();
     if (bytes < image_bytes(n_ops, G))
         return RBQ_ERR_INVALID_ARG;
@@ -864,16 +1019,20 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             return RBQ_ERR_INVALID_ARG;
         if (o.planes_layout != RBQ_LAYOUT_ROWS && o.planes_layout != RBQ_LAYOUT_TILES)
             return RBQ_ERR_INVALID_ARG;
+        if (o.group_size != 0 && o.group_size != 128)
+            return RBQ_ERR_INVALID_ARG;
+        if ((o.group_size == 128) != group || (group && o.planes_layout != RBQ_LAYOUT_TILES))
+            return RBQ_ERR_UNSUPPORTED;
         if (o.in_features % 128 != 0 || o.in_features > PG_MAX_CHUNKS * CHUNK_WORDS * 32 ||
             o.out_features > max_out)
             return RBQ_ERR_UNSUPPORTED;
-        if (!al(o.planes, 16) || !al(o.x, 16) || !al(o.scales, 2) || !al(o.y, 2))
+        if (!al(o.planes, 16) || !al(o.x, 16) || !al(o.scales, group ? 16 : 2) || !al(o.y, 2))
             return RBQ_ERR_ALIGNMENT;
         xb[i] = (size_t)o.in_features * 2;
         yb[i] = (size_t)(o.epilogue == RBQ_EPILOGUE_SILU_MUL ? o.out_features / 2 : o.out_features) * 2;
         pb[i] = o.planes_layout == RBQ_LAYOUT_TILES ? tiles_bytes(K, o.out_features, o.in_features)
                                                     : (size_t)K * o.out_features * (o.in_features / 32) * 4;
-        sb[i] = (size_t)K * o.out_features * 2;
+        sb[i] = group ? scale_tiles_bytes(K, o.out_features, o.in_features) : (size_t)K * o.out_features * 2;
     }
     // Ordering.  Workgroups run the ops in order, each on its own rows, so two
     // accesses of ops j < i to one buffer are ordered across workgroups only
@@ -915,11 +1074,11 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     ProgOp *d = reinterpret_cast<ProgOp *>(h + 1);
     int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
     // LDS: the image arena takes what the partial sums and the op table leave
-    const size_t fixed = 16 + (size_t)PG_SLOTS * PG_MAX_TILES * K * NC * TILE_ROWS * 4 + (size_t)n_ops * sizeof(ProgOp);
+    const size_t fixed = 16 + (size_t)PG_SLOTS * red_op_ints(K, group) * 4 + (size_t)n_ops * sizeof(ProgOp);
     int max_img = 0;
     for (int i = 0; i < n_ops; ++i)
         max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * IMG_CHUNK);
-    const size_t budget = program_dynamic_lds(K);
+    const size_t budget = program_dynamic_lds(K, group);
     if (fixed + (size_t)max_img > budget)
         return RBQ_ERR_UNSUPPORTED;
     const int arena = (int)((budget - fixed) / 16 * 16);
@@ -995,7 +1154,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
-    h->kind = PK_TILES;
+    h->kind = PK_TILES | (group ? PK_GROUP : 0);
     for (int i = 0; i < n_ops; ++i) {
         h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
         h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
@@ -1011,12 +1170,15 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->K != 1 && h->K != 2) || (h->kind & ~(PK_WAITS | PK_TILES)) != 0)
+        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP)) != 0)
+        return RBQ_ERR_INVALID_ARG;
+    const bool group = (h->kind & PK_GROUP) != 0;
+    if (group ? (h->K != 2 && h->K != 4) || !(h->kind & PK_TILES) : (h->K != 1 && h->K != 2))
         return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
     // never launch a layout that would not fit the compute unit's LDS
-    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K))
+    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K, group))
         return RBQ_ERR_UNSUPPORTED;
     return RBQ_OK;
 }
@@ -1031,21 +1193,33 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
     const ProgHeader *hd = static_cast<const ProgHeader *>(image_dev);
     // programs without waits take the kernel with the waiting code compiled
     // out, programs of tiled ops only the one without row addressing
-#define RBQ_LAUNCH_PROGRAM(KK, WW, TT)                                                                    \
-    hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW, TT>), dim3(h->grid), dim3(PG_THREADS), \
+#define RBQ_LAUNCH_PROGRAM(KK, WW, TT, GG)                                                                  \
+    hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW, TT, GG>), dim3(h->grid), dim3(PG_THREADS), \
                        h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status)
-#define RBQ_LAUNCH_PROGRAM_K(KK)                                  \
-    switch (h->kind) {                                            \
-    case 0: RBQ_LAUNCH_PROGRAM(KK, false, false); break;          \
-    case PK_WAITS: RBQ_LAUNCH_PROGRAM(KK, true, false); break;    \
-    case PK_TILES: RBQ_LAUNCH_PROGRAM(KK, false, true); break;    \
-    default: RBQ_LAUNCH_PROGRAM(KK, true, true); break;           \
+#define RBQ_LAUNCH_PROGRAM_K(KK)                                         \
+    switch (h->kind) {                                                   \
+    case 0: RBQ_LAUNCH_PROGRAM(KK, false, false, false); break;          \
+    case PK_WAITS: RBQ_LAUNCH_PROGRAM(KK, true, false, false); break;    \
+    case PK_TILES: RBQ_LAUNCH_PROGRAM(KK, false, true, false); break;    \
+    default: RBQ_LAUNCH_PROGRAM(KK, true, true, false); break;           \
     }
-    if (h->K == 1) {
+#define RBQ_LAUNCH_GROUP_K(KK)                                           \
+    if (h->kind & PK_WAITS)                                              \
+        RBQ_LAUNCH_PROGRAM(KK, true, true, true);                        \
+    else                                                                 \
+        RBQ_LAUNCH_PROGRAM(KK, false, true, true)
+    if (h->kind & PK_GROUP) {
+        if (h->K == 2) {
+            RBQ_LAUNCH_GROUP_K(2);
+        } else {
+            RBQ_LAUNCH_GROUP_K(4);
+        }
+    } else if (h->K == 1) {
         RBQ_LAUNCH_PROGRAM_K(1);
     } else {
         RBQ_LAUNCH_PROGRAM_K(2);
     }
+#undef RBQ_LAUNCH_GROUP_K
 #undef RBQ_LAUNCH_PROGRAM_K
 #undef RBQ_LAUNCH_PROGRAM
     return hipGetLastError();

@@ -118,6 +118,10 @@ hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipS
 // contiguous 1 KB block; in % 128 == 0.
 size_t tiles_bytes(int K, int out, int in);
 hipError_t launch_pack_tiles(const uint32_t *planes, int K, int out, int in, uint32_t *tiles, hipStream_t st);
+// ... and of g128 scales (K even): K * 128 bytes per 16-row, 512-column unit.
+size_t scale_tiles_bytes(int K, int out, int in);
+hipError_t launch_pack_scale_tiles(const uint16_t *scales, int K, int out, int in, uint16_t *stiles,
+                                   hipStream_t st);
 
 // Y = 0 for in_features == 0 (an empty sum).
 hipError_t launch_fill_zero_u16(uint16_t *Y, int64_t n, hipStream_t st);

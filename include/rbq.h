@@ -413,6 +413,30 @@ size_t rbq_tiles_bytes(rbq_shape s);
  */
 rbq_status rbq_pack_tiles(const uint32_t *planes, rbq_shape s, uint32_t *tiles, void *stream);
 
+/*
+ * Scale tiles: the scales of a layer with one scale per row and 128-column
+ * group (QBB summary, "Approach" and the W(4x1)A16g128 rows of "Key
+ * results"), reordered so that a one-token kernel loads the scales of a
+ * 16-row, 512-column unit (4 groups) together with its planes, K * 128 bytes
+ * per unit:
+ *   fp16 [T][C][K/2][4][4][2][4],  T = ceil(out / 16),  C = ceil(in / 512);
+ *   element [t][c][p][g][q][kk][v] = scales[2p + kk][16t + 4q + v][4c + g],
+ *   zero where the row (>= out) or the group (>= in / 128) does not exist.
+ * Needs s.group_size == 128 and an even K; rbq_scale_tiles_bytes is 0
+ * otherwise.
+ */
+size_t rbq_scale_tiles_bytes(rbq_shape s);
+
+/*
+ * rbq_pack_scale_tiles -- write the scale tiles of g128 scales.
+ *   scales  device fp16 [K][out][in/128], 2-byte aligned (read only)
+ *   tiles   device, rbq_scale_tiles_bytes(s) bytes, 16-byte aligned; every
+ *           byte is written
+ * s.group_size must be 128 and K even (else RBQ_ERR_UNSUPPORTED).  out == 0
+ * or in == 0 enqueues nothing.  Errors as rbq_pack_tiles.
+ */
+rbq_status rbq_pack_scale_tiles(const uint16_t *scales, rbq_shape s, uint16_t *tiles, void *stream);
+
 /* One op of a program. */
 typedef struct rbq_program_op {
     const uint32_t *planes;   /* device, 16-byte aligned: [K][out][in/32], or the
@@ -428,6 +452,12 @@ typedef struct rbq_program_op {
                                  written all of its y */
     uint32_t planes_layout;   /* RBQ_LAYOUT_ROWS or RBQ_LAYOUT_TILES; the
                                  results are the same bits in either */
+    int32_t group_size;       /* 0: scales fp16 [K][out], one per row.
+                                 128: one scale per row and 128-column group;
+                                 planes in RBQ_LAYOUT_TILES and `scales` the
+                                 scale tiles of rbq_pack_scale_tiles (16-byte
+                                 aligned); K = 2 or 4.  The ops of one program
+                                 are all of one kind. */
 } rbq_program_op;
 
 /* Bytes of the program image for n_ops ops on the current device (0 when
@@ -454,8 +484,10 @@ size_t rbq_program_counters_bytes(int32_t n_ops);
  * Errors: RBQ_ERR_INVALID_ARG (null pointer, bad shape, epilogue or
  * planes_layout, wait_for not an earlier op, an unordered overlap, image too
  * small),
- * RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (num_planes > 2, in_features % 128
- * != 0 or > 16384, out_features too large, too many ops).
+ * RBQ_ERR_ALIGNMENT, RBQ_ERR_UNSUPPORTED (num_planes > 2 for per-row ops or
+ * not 2 or 4 for g128 ops, g128 ops mixed with per-row ops or on the row
+ * layout, in_features % 128 != 0 or > 16384, out_features too large, too
+ * many ops).
  */
 rbq_status rbq_program_build(const rbq_program_op *ops, int32_t n_ops, int32_t num_planes, void *image,
                              size_t image_bytes);

@@ -10,8 +10,8 @@ import gemm_rbq_encode_amd as rbq
 MiB = 1 << 20
 
 
-def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1, layout=0):
-    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for, layout)
+def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1, layout=0, group=0):
+    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for, layout, group)
 
 
 def build(ops, K=2, nbytes=None):
@@ -134,3 +134,42 @@ def test_tiles_bytes_and_pack_arguments():
     assert L.rbq_pack_tiles(W(0), s, W(0) + 39984, None) == rbq.RBQ_ERR_INVALID_ARG   # overlap
     # (no call here passes every check: on a machine with a device it would
     # launch on these fake addresses)
+
+
+def gop(planes, scales, x, y, out=256, inf=512, **kw):
+    return op(planes, scales, x, y, out, inf, layout=rbq.RBQ_LAYOUT_TILES, group=128, **kw)
+
+
+def test_group_programs():
+    """Programs of g128 ops: K = 2 or 4, tiled planes, scale tiles 16-byte
+    aligned, no per-row ops beside them."""
+    for K in (2, 4):
+        assert build([gop(W(0), W(1), A(0), A(1)), gop(W(2), W(3), A(1), A(2), wait_for=0)], K=K) == rbq.RBQ_OK
+    assert build([gop(W(0), W(1), A(0), A(1))], K=1) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([gop(W(0), W(1), A(0), A(1))], K=3) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([op(W(0), W(1), A(0), A(1), group=128)], K=4) == rbq.RBQ_ERR_UNSUPPORTED      # row layout
+    assert build([op(W(0), W(1), A(0), A(1), group=64)], K=2) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([gop(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2))], K=2) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([op(W(0), W(1), A(0), A(1)), gop(W(2), W(3), A(0), A(2))], K=2) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([gop(W(0), W(1) + 8, A(0), A(1))], K=4) == rbq.RBQ_ERR_ALIGNMENT             # scale tiles
+    # per-row programs stay at K <= 2
+    assert build([op(W(0), W(1), A(0), A(1), layout=rbq.RBQ_LAYOUT_TILES)], K=4) == rbq.RBQ_ERR_UNSUPPORTED
+    # 250 x 640, K = 4: scale tiles 16 tiles * 2 chunks * 512 bytes = 16384; a y
+    # 10000 bytes into them overlaps (the [K][out][G] scales would end at 10000)
+    assert build([gop(W(0), W(1), A(0), W(1) + 12000, out=250, inf=640)], K=4) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([gop(W(0), W(1), A(0), W(1) + 16384, out=250, inf=640)], K=4) == rbq.RBQ_OK
+
+
+def test_scale_tiles_bytes_and_pack_arguments():
+    L = rbq.lib()
+    assert int(L.rbq_scale_tiles_bytes(rbq.shape(5120, 13824, 4, 128))) == 320 * 27 * 512
+    assert int(L.rbq_scale_tiles_bytes(rbq.shape(250, 640, 2, 128))) == 16 * 2 * 256
+    assert int(L.rbq_scale_tiles_bytes(rbq.shape(250, 640, 2, 0))) == 0       # per-row scales
+    assert int(L.rbq_scale_tiles_bytes(rbq.shape(250, 640, 3, 128))) == 0     # odd K
+    s = rbq.shape(250, 640, 4, 128)
+    assert L.rbq_pack_scale_tiles(None, s, W(4), None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_pack_scale_tiles(W(0), rbq.shape(250, 640, 4, 0), W(4), None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_pack_scale_tiles(W(0), rbq.shape(250, 640, 3, 128), W(4), None) == rbq.RBQ_ERR_UNSUPPORTED
+    assert L.rbq_pack_scale_tiles(W(0) + 1, s, W(4), None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_pack_scale_tiles(W(0), s, W(4) + 8, None) == rbq.RBQ_ERR_ALIGNMENT
+    assert L.rbq_pack_scale_tiles(W(0), s, W(0) + 16, None) == rbq.RBQ_ERR_INVALID_ARG        # overlap
