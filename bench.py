@@ -149,15 +149,16 @@ def main():
 COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "gemv_llama2_7b_decode_hbm_traffic.json")
+TRAFFIC_PROFILE_13B = os.path.join(ROOT, "profiles", "gemv_llama2_13b_g128_program_hbm_traffic.json")
 
 
-def profile_entry(shape_key, kernel_prefix):
+def profile_entry(shape_key, kernel_prefix, path=None):
     """The recorded counter entry for this launch (shape key and kernel name
     prefix), or None when there is none or the kernel's source has changed
     since it was taken."""
     import hashlib
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(path or TRAFFIC_PROFILE) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -175,17 +176,17 @@ def profile_entry(shape_key, kernel_prefix):
     return None
 
 
-def measured_traffic(shape_key, kernel_prefix):
+def measured_traffic(shape_key, kernel_prefix, path=None):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a copy
     of known size) recorded for this launch, or None."""
-    e = profile_entry(shape_key, kernel_prefix)
+    e = profile_entry(shape_key, kernel_prefix, path)
     return None if e is None else e.get("traffic_bytes")
 
 
-def rocprof_mean_us(shape_key, kernel_prefix="gemv_program_kernel"):
+def rocprof_mean_us(shape_key, kernel_prefix="gemv_program_kernel", path=None):
     """Mean kernel duration (us) in the recorded rocprofv3 kernel trace of the
-    default benchmark run, or None."""
-    e = profile_entry(shape_key, kernel_prefix)
+    benchmark run, or None."""
+    e = profile_entry(shape_key, kernel_prefix, path)
     return None if e is None else e.get("rocprof_mean_us")
 
 
@@ -378,8 +379,12 @@ def group_program_step(args, torch, rbq, workloads, dev, n_layers=40, cpu_second
                        "planes_layout": "tiles (rbq_pack_tiles), scales as scale tiles (rbq_pack_scale_tiles)"},
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "kernel": f"gemv_program_kernel<{K}> g128 ({len(ops)} ops)",
-                         "mean_launch_us": round(us, 2)},
+                         "traffic": measured_traffic(f"program_fused_{n_layers}layers_g128", "gemv_program_kernel",
+                                                     TRAFFIC_PROFILE_13B),
+                         "kernel": f"gemv_program_kernel<{K}> g128 ({len(ops)} ops)",
+                         "bytes_per_launch": nbytes, "mean_launch_us": round(us, 2),
+                         "rocprof_mean_launch_us": rocprof_mean_us(f"program_fused_{n_layers}layers_g128",
+                                                                   path=TRAFFIC_PROFILE_13B)},
             "layer0_max_rel_diff_vs_rbq_gemv": diff, "cpu_baseline": None}
     if cpu_seconds > 0:
         samples = [(p.cpu().numpy().view(np.uint32), sc.cpu().numpy().view(np.uint16),
