@@ -41,6 +41,7 @@
 // RBQ_STATUS_PROGRAM_TIMEOUT in the status word and the kernel still runs to
 // its end.  The waits across workgroups need all workgroups resident: one
 // per compute unit, as launched (the LDS each takes leaves room for one).
+#include <stddef.h>
 #include <string.h>
 
 #include <algorithm>
@@ -264,8 +265,7 @@ __device__ __forceinline__ GLOBAL T *gptr(T *p) {
     return (GLOBAL T *)p;
 }
 
-// The fields of op i, read from the workgroup's LDS copy of the op table
-// (uniform across the wave: scalar registers).
+// The fields of op i (uniform across the wave: scalar registers).
 struct OpView {
     GLOBAL const uint32_t *planes;
     GLOBAL const uint16_t *scales;
@@ -275,27 +275,39 @@ struct OpView {
     uint32_t flags, magic;
 };
 
+// The device copy of the program image is only read during a run, so the op
+// descriptors come in by scalar loads through the scalar cache, off the
+// vector memory and LDS queues.  (Read field by field from an LDS copy of
+// the table, one descriptor took 400 ns while the stream waves kept LDS
+// busy, on the critical path of every op: the step ran 2-3 % slower.)
 __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
-    const ProgOp &o = table[i];
+    typedef const __attribute__((address_space(4))) uint32_t CU32;
+    CU32 *w = (CU32 *)(table + rfl(i));
+    uint32_t q[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        q[e] = w[e];
+    auto p64 = [&](int e) { return (uintptr_t)(((uint64_t)q[e + 1] << 32) | q[e]); };
+    static_assert(offsetof(ProgOp, out) == 32 && offsetof(ProgOp, wait_for) == 40 && offsetof(ProgOp, flags) == 44 &&
+                      offsetof(ProgOp, trot) == 48 && offsetof(ProgOp, split) == 52 &&
+                      offsetof(ProgOp, nch_img) == 56 && offsetof(ProgOp, magic) == 60,
+                  "op fields read by word");
     OpView v;
-    v.planes = gptr(rflp(o.planes));
-    v.scales = gptr(rflp(o.scales));
-    v.x = gptr(rflp(o.x));
-    v.y = gptr(rflp(o.y));
-    v.out = rfl(o.out);
-    v.in = rfl(o.in);
-    const uint32_t wf = (uint32_t)rfl(*reinterpret_cast<const int *>(&o.wait_for));
-    v.wait_for = (int)(int16_t)(wf & 0xFFFFu);
-    v.free_after = (int)(int16_t)(wf >> 16);
-    const uint32_t sp = (uint32_t)rfl((int)o.split);
-    v.base = (int)(sp & 255u);
-    v.extra = (int)(sp >> 8);
-    v.magic = (uint32_t)rfl((int)o.magic);
-    const uint32_t ni = (uint32_t)rfl((int)o.nch_img);
-    v.nchunks = (int)(ni & 255u);
-    v.img_off = (int)(ni >> 8) * 16;
-    v.trot = rfl(o.trot);
-    v.flags = (uint32_t)rfl((int)o.flags);
+    v.planes = gptr(reinterpret_cast<const uint32_t *>(p64(0)));
+    v.scales = gptr(reinterpret_cast<const uint16_t *>(p64(2)));
+    v.x = gptr(reinterpret_cast<const uint16_t *>(p64(4)));
+    v.y = gptr(reinterpret_cast<uint16_t *>(p64(6)));
+    v.out = (int)q[8];
+    v.in = (int)q[9];
+    v.wait_for = (int)(int16_t)(q[10] & 0xFFFFu);
+    v.free_after = (int)(int16_t)(q[10] >> 16);
+    v.flags = q[11];
+    v.trot = (int)q[12];
+    v.base = (int)(q[13] & 255u);
+    v.extra = (int)(q[13] >> 8);
+    v.nchunks = (int)(q[14] & 255u);
+    v.img_off = (int)(q[14] >> 8) * 16;
+    v.magic = q[15];
     v.wrot = (int)((v.flags >> PF_WROT_SHIFT) & 15u);
     return v;
 }
@@ -332,12 +344,11 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const int li = lane & 15, lg = lane >> 4;
     const int G = gridDim.x;
     const int b = blockIdx.x;
-    // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16], op table
+    // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16]
     const int pad = hdr->arena_bytes;
     int *red0 = reinterpret_cast<int *>(lds + pad + 16);
     constexpr int RED_OP = red_op_ints(K, GROUP);
     constexpr int RED_TILE = RED_OP / PG_MAX_TILES;                          // ints per tile
-    ProgOp *table = reinterpret_cast<ProgOp *>(red0 + PG_SLOTS * RED_OP);   // the op table, [n_ops]
 
     // A wait that runs out only raises the LDS flag (the status word is
     // written once at the end): the stream waves then issue no global memory
@@ -358,12 +369,6 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         red0[i] = 0;
     if (tid < 4)
         reinterpret_cast<uint32_t *>(lds + pad)[tid] = 0u;
-    {
-        const v4u *src = reinterpret_cast<const v4u *>(ops_g);
-        v4u *dst = reinterpret_cast<v4u *>(table);
-        for (int i = tid; i < n_ops * (int)(sizeof(ProgOp) / 16); i += PG_THREADS)
-            dst[i] = src[i];
-    }
     __syncthreads();
 
     if (wave < PG_PREP) {
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 
         // ---- finish op j: y for this workgroup's rows of it
         auto finish = [&](int j) {
-            const OpView op = op_view(table, j);
+            const OpView op = op_view(ops_g, j);
             const int par = j % PG_SLOTS;
             int t0, ntl;
             op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         };
 
         int next_fin = 0;
-        OpView cur = op_view(table, 0);
+        OpView cur = op_view(ops_g, 0);
         if (!(WAITS && (cur.flags & PF_X_SHARED)))
             load_x(cur);
         load_scales(cur);
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             }
             if (i + 1 < n_ops) {
                 // the next op's loads go out now, to arrive while this op streams
-                cur = op_view(table, i + 1);
+                cur = op_view(ops_g, i + 1);
                 if (!(cur.flags & ((WAITS ? PF_X_SHARED : 0u) | PF_REUSE)))
                     load_x(cur);
                 load_scales(cur);
@@ -673,13 +678,13 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         int lop = 0, lu = 0, lu1 = 0, lt0 = 0, lnch = 1, lwords = 4, lout = 1;
         bool ltiles = false;
         uint32_t lmagic = 0;
-        const OpView op0 = op_view(table, 0);
+        const OpView op0 = op_view(ops_g, 0);
         GLOBAL const uint32_t *lplanes = op0.planes;
         GLOBAL const uint16_t *lscales = op0.scales;   // g128: the op's scale tiles
         size_t lstride = 0;
         auto lseek = [&]() {   // the first op from lop on that gives this wave units
             while (lop < n_ops) {
-                const OpView op = op_view(table, lop);
+                const OpView op = op_view(ops_g, lop);
                 int t0, ntl;
                 op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
                 op_units(ntl * op.nchunks, op.wrot, sw, lu, lu1);
@@ -754,7 +759,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 if (!lds_wait_ge(&img_cnt, PG_PREP * (cop + 1), &abort_flag) && lane == 0)
                     report_timeout();
                 asm volatile("" ::: "memory");
-                const OpView op = op_view(table, cop);
+                const OpView op = op_view(ops_g, cop);
                 int t0, ntl;
                 op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
                 op_units(ntl * op.nchunks, op.wrot, sw, cu, cu1);
@@ -1073,8 +1078,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     ProgHeader *h = reinterpret_cast<ProgHeader *>(img);
     ProgOp *d = reinterpret_cast<ProgOp *>(h + 1);
     int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
-    // LDS: the image arena takes what the partial sums and the op table leave
-    const size_t fixed = 16 + (size_t)PG_SLOTS * red_op_ints(K, group) * 4 + (size_t)n_ops * sizeof(ProgOp);
+    // LDS: the image arena takes what the partial sums leave
+    const size_t fixed = 16 + (size_t)PG_SLOTS * red_op_ints(K, group) * 4;
     int max_img = 0;
     for (int i = 0; i < n_ops; ++i)
         max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * IMG_CHUNK);
