@@ -75,6 +75,9 @@ constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wai
                                                            // 100 MHz real-time clock (never reached)
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
 constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
+#ifndef RBQ_PROGRAM_GROUPS
+#define RBQ_PROGRAM_GROUPS 2                               // op groups of programs without waits (1, 2 or 4)
+#endif
 constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
 constexpr int PG_MAX_G = PG_MAX_CHUNKS * 4;                // 128-column groups of the widest input
 
@@ -86,6 +89,7 @@ constexpr uint32_t PF_Y_SHARED = 8u;   // y is read (or written again) by a late
 constexpr uint32_t PF_REUSE = 32u;     // same x as the op before: its image is used again
 constexpr uint32_t PF_TILES = 64u;     // planes in the tile layout (1 KB per 16-row, 512-column unit)
 constexpr int PF_WROT_SHIFT = 8;       // bits 8..11: rotation of the stream waves over the units
+constexpr int PF_GRP_SHIFT = 12;       // bits 12..13: the op group (of the workgroups) that runs the op
 
 // One op in device memory (64 bytes).
 struct ProgOp {
@@ -95,9 +99,12 @@ struct ProgOp {
     uint16_t *y;
     int32_t out, in;
     int16_t wait_for;     // earlier op this one waits for (-1: none)
-    int16_t free_after;   // the last earlier op whose image shared LDS bytes with this op's (-1: none)
+    int16_t free_after;   // the last earlier op of the group to finish before this op is built: the
+                          // one whose image shares LDS bytes with its own, or PG_SLOTS places back
+                          // (whose slot it takes) (-1: none)
     uint32_t flags;
-    int32_t trot;         // rotation of the workgroups that take one more tile
+    int32_t trot;         // rotation of the group's workgroups that take one more tile (bits 0..15) |
+                          // the op's place in its group's sequence (bits 16..)
     uint32_t split;       // tiles / G (bits 0..7) | tiles % G (bits 8..): the tile split, precomputed
     uint32_t nch_img;     // 512-column chunks (bits 0..7) | image offset in the arena / 16 (bits 8..)
     uint32_t magic;       // ceil(2^21 / chunks): unit -> (tile, chunk) by a multiply and a shift
@@ -121,6 +128,8 @@ static_assert(sizeof(ProgHeader) == 32, "header layout");
 constexpr int32_t PK_WAITS = 1;        // some op waits for another: the kernel with the waits
 constexpr int32_t PK_TILES = 2;        // every op reads the tile layout
 constexpr int32_t PK_GROUP = 4;        // g128 ops (scales per 128-column group, in the scale tile layout)
+constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups (1, 2 or 4)
+constexpr int32_t PK_P_MASK = 15 << PK_P_SHIFT;
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
 // image arena what remains of the compute unit's LDS).  Programs of g128 ops
@@ -272,6 +281,7 @@ struct OpView {
     GLOBAL const uint16_t *x;
     GLOBAL uint16_t *y;
     int out, in, wait_for, base, extra, nchunks, trot, wrot, free_after, img_off;
+    int grp, lpos;        // the op's group, and its place in the group's sequence (its slot: lpos % PG_SLOTS)
     uint32_t flags, magic;
 };
 
@@ -302,13 +312,15 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     v.wait_for = (int)(int16_t)(q[10] & 0xFFFFu);
     v.free_after = (int)(int16_t)(q[10] >> 16);
     v.flags = q[11];
-    v.trot = (int)q[12];
+    v.trot = (int)(q[12] & 0xFFFFu);
+    v.lpos = (int)(q[12] >> 16);
     v.base = (int)(q[13] & 255u);
     v.extra = (int)(q[13] >> 8);
     v.nchunks = (int)(q[14] & 255u);
     v.img_off = (int)(q[14] >> 8) * 16;
     v.magic = q[15];
     v.wrot = (int)((v.flags >> PF_WROT_SHIFT) & 15u);
+    v.grp = (int)((v.flags >> PF_GRP_SHIFT) & 3u);
     return v;
 }
 
@@ -344,6 +356,19 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const int li = lane & 15, lg = lane >> 4;
     const int G = gridDim.x;
     const int b = blockIdx.x;
+    // op groups: this workgroup is number bl of the Gl workgroups of group mygrp
+    const int P = (hdr->kind & PK_P_MASK) >> PK_P_SHIFT;
+    const int Gl = G / P;
+    const int mygrp = b / Gl, bl = b - mygrp * Gl;
+    // tiles [t0, t0 + ntl) of an op taken by this workgroup (none for another group's op)
+    auto my_tiles = [&](const OpView &op, int &t0, int &ntl) {
+        if (op.grp != mygrp) {
+            t0 = 0;
+            ntl = 0;
+        } else {
+            op_tiles(op.base, op.extra, op.trot, bl, Gl, t0, ntl);
+        }
+    };
     // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16]
     const int pad = hdr->arena_bytes;
     int *red0 = reinterpret_cast<int *>(lds + pad + 16);
@@ -388,9 +413,9 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // ---- finish op j: y for this workgroup's rows of it
         auto finish = [&](int j) {
             const OpView op = op_view(ops_g, j);
-            const int par = j % PG_SLOTS;
+            const int par = op.lpos % PG_SLOTS;
             int t0, ntl;
-            op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
+            my_tiles(op, t0, ntl);
             if (!lds_wait_ge(&sdone[par], PG_STREAM, &abort_flag) && lane == 0)
                 report_timeout();
             asm volatile("" ::: "memory");
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     for (int c = 0; c < PG_CSPLIT; ++c)
                         tot += __hip_atomic_load(op_counter(counters, j, c), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-                    if (tot >= G)
+                    if (tot >= Gl)   // every workgroup of the op's group
                         break;
                     if (__hip_atomic_load(&abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ||
                         __builtin_amdgcn_s_memrealtime() > deadline) {
@@ -518,7 +543,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             if (GROUP)   // g128 scales travel with the weights, to the stream waves
                 return;
             int t0, ntl;
-            op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
+            my_tiles(op, t0, ntl);
             const int row = t0 * TILE_ROWS + tid;
             const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
 #pragma unroll
@@ -533,10 +558,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 __hip_atomic_fetch_add(&img_cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             wake_workgroup();
         };
-        // op i reads the same x as op i - 1: its image (and the sums that go
-        // with it) serve again; only the scales are op i's own
-        auto reuse = [&](int i) {
-            const int par = i % PG_SLOTS, prev = (i + PG_SLOTS - 1) % PG_SLOTS;
+        // the op reads the same x as the group's op before it: that image (and
+        // the sums that go with it) serve again; only the scales are its own
+        auto reuse = [&](const OpView &op) {
+            const int par = op.lpos % PG_SLOTS, prev = (op.lpos + PG_SLOTS - 1) % PG_SLOTS;
             if (GROUP) {
                 for (int g = tid; g < PG_MAX_G; g += PG_PREP_THREADS)
                     gsum[par][g] = gsum[prev][g];
@@ -554,7 +579,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 
         // ---- build op i's activation image from xw, a_bits into its buffer
         auto build = [&](int i, const OpView &op) {
-            const int par = i % PG_SLOTS;
+            const int par = op.lpos % PG_SLOTS;
             const int nh = (op.in >> 5) * 2;                  // half-words of the row
             const int hpad = op.nchunks * CHUNK_WORDS * 2;    // with the padded words
             const int xu = (hpad + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
@@ -638,37 +663,50 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             publish();
         };
 
+        // this workgroup runs the ops of its group, in list order
+        auto next_mine = [&](int i) {
+            while (i < n_ops && op_view(ops_g, i).grp != mygrp)
+                ++i;
+            return i;
+        };
+        auto finish_upto = [&](int &next_fin, int upto) {
+            for (; next_fin <= upto; ++next_fin)
+                if (op_view(ops_g, next_fin).grp == mygrp)
+                    finish(next_fin);
+        };
         int next_fin = 0;
-        OpView cur = op_view(ops_g, 0);
-        if (!(WAITS && (cur.flags & PF_X_SHARED)))
-            load_x(cur);
-        load_scales(cur);
-        for (int i = 0; i < n_ops; ++i) {
+        int i = next_mine(0);
+        OpView cur = op_view(ops_g, i < n_ops ? i : 0);
+        if (i < n_ops) {
+            if (!(WAITS && (cur.flags & PF_X_SHARED)))
+                load_x(cur);
+            load_scales(cur);
+        }
+        while (i < n_ops) {
             // finish what the op waits for, the op whose slot of partial sums
             // and scales it takes, and the last op whose image shares LDS
             // bytes with its own
-            const int upto = max(max(WAITS ? cur.wait_for : -1, i - PG_SLOTS), cur.free_after);
-            while (next_fin <= upto)
-                finish(next_fin++);
+            finish_upto(next_fin, max(WAITS ? cur.wait_for : -1, cur.free_after));
             if (WAITS && cur.wait_for >= 0)
                 wait_op(cur.wait_for);
             if (cur.flags & PF_REUSE) {
-                reuse(i);
+                reuse(cur);
             } else {
                 if (WAITS && (cur.flags & PF_X_SHARED))
                     load_x(cur);
                 build(i, cur);
             }
-            if (i + 1 < n_ops) {
+            const int nx = next_mine(i + 1);
+            if (nx < n_ops) {
                 // the next op's loads go out now, to arrive while this op streams
-                cur = op_view(ops_g, i + 1);
+                cur = op_view(ops_g, nx);
                 if (!(cur.flags & ((WAITS ? PF_X_SHARED : 0u) | PF_REUSE)))
                     load_x(cur);
                 load_scales(cur);
             }
+            i = nx;
         }
-        while (next_fin < n_ops)
-            finish(next_fin++);
+        finish_upto(next_fin, n_ops - 1);
     } else {
         // ===================== stream waves =====================
         const int sw = wave - PG_PREP;
@@ -686,7 +724,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             while (lop < n_ops) {
                 const OpView op = op_view(ops_g, lop);
                 int t0, ntl;
-                op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
+                my_tiles(op, t0, ntl);
                 op_units(ntl * op.nchunks, op.wrot, sw, lu, lu1);
                 if (lu < lu1) {
                     lt0 = t0;
@@ -747,31 +785,36 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         };
 
         // ---- consume cursor: the op and unit the MFMAs work on
-        int cop = 0, cu = 0, cu1 = 0, cnch = 1, ctile = 0, cchunk = 0, cimg = 0;
-        auto report = [&](int j) {   // this wave is done with op j
+        int cop = 0, cu = 0, cu1 = 0, cnch = 1, ctile = 0, cchunk = 0, cimg = 0, cpar = 0;
+        auto report = [&](int par) {   // this wave is done with the op in slot par
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (lane == 0)
-                __hip_atomic_fetch_add(&sdone[j % PG_SLOTS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&sdone[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             wake_workgroup();
         };
-        auto cseek = [&]() {   // wait for op cop's image; skip (and report) ops without units here
+        // wait for op cop's image; skip another group's ops, and report this
+        // group's ops without units here
+        auto cseek = [&]() {
             while (cop < n_ops) {
-                if (!lds_wait_ge(&img_cnt, PG_PREP * (cop + 1), &abort_flag) && lane == 0)
-                    report_timeout();
-                asm volatile("" ::: "memory");
                 const OpView op = op_view(ops_g, cop);
-                int t0, ntl;
-                op_tiles(op.base, op.extra, op.trot, b, G, t0, ntl);
-                op_units(ntl * op.nchunks, op.wrot, sw, cu, cu1);
-                if (cu < cu1) {
-                    cnch = op.nchunks;
-                    cimg = op.img_off;
-                    const int tq = (int)(((uint32_t)cu * op.magic) >> 21);
-                    ctile = tq;
-                    cchunk = cu - tq * cnch;
-                    return;
+                if (op.grp == mygrp) {
+                    if (!lds_wait_ge(&img_cnt, PG_PREP * (op.lpos + 1), &abort_flag) && lane == 0)
+                        report_timeout();
+                    asm volatile("" ::: "memory");
+                    int t0, ntl;
+                    my_tiles(op, t0, ntl);
+                    op_units(ntl * op.nchunks, op.wrot, sw, cu, cu1);
+                    cpar = op.lpos % PG_SLOTS;
+                    if (cu < cu1) {
+                        cnch = op.nchunks;
+                        cimg = op.img_off;
+                        const int tq = (int)(((uint32_t)cu * op.magic) >> 21);
+                        ctile = tq;
+                        cchunk = cu - tq * cnch;
+                        return;
+                    }
+                    report(cpar);
                 }
-                report(cop);
                 ++cop;
             }
         };
@@ -808,7 +851,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         cseek();
 
         auto consume = [&](const v4u (&wv)[KR]) {
-            const int par = cop % PG_SLOTS;
+            const int par = cpar;
             if constexpr (GROUP) {
                 ++cu;
                 const bool tile_end = cchunk + 1 == cnch;
@@ -868,7 +911,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 ctile += tile_end ? 1 : 0;
                 cchunk = tile_end ? 0 : cchunk + 1;
                 if (op_end) {
-                    report(cop);
+                    report(cpar);
                     ++cop;
                     cseek();
                 }
@@ -926,7 +969,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     ++ctile;
                 }
                 if (op_end) {
-                    report(cop);
+                    report(cpar);
                     ++cop;
                     cseek();
                 }
@@ -1087,14 +1130,56 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     if (fixed + (size_t)max_img > budget)
         return RBQ_ERR_UNSUPPORTED;
     const int arena = (int)((budget - fixed) / 16 * 16);
-    // Images go into the arena one after another, wrapping to 0 when one
-    // would pass its end.  An op is built only once every earlier op whose
-    // image shares bytes with its own is finished (free_after).
+    // Op groups.  Without waits the ops are independent, and the workgroups
+    // are split into P groups of G / P: each op goes to one group (the one
+    // with the fewest plane bytes so far), whose workgroups take its tiles,
+    // so every workgroup runs 1/P of the ops with P times their tiles each.
+    // What a workgroup spends per op (images, finishes, flushes, cursors) is
+    // then spread over P times the units.  Programs with waits keep one group:
+    // their ops run one after another anyway.
+    int P = 1;
+    {
+        bool waits = false;
+        for (int i = 0; i < n_ops; ++i)
+            waits |= ops[i].wait_for >= 0;
+        int cand = RBQ_PROGRAM_GROUPS;
+        while (cand > 1) {
+            bool fits = !waits && n_ops >= cand && G % cand == 0;
+            for (int i = 0; fits && i < n_ops; ++i)
+                fits = ops[i].out_features <= PG_MAX_TILES * TILE_ROWS * (G / cand);
+            if (fits)
+                break;
+            cand /= 2;
+        }
+        P = cand;
+    }
+    const int Gl = G / P;
+    std::vector<int> grp(n_ops, 0);
+    {
+        std::vector<double> load(P, 0.0);
+        for (int i = 0; i < n_ops; ++i) {
+            int g = 0;
+            for (int q = 1; q < P; ++q)
+                if (load[q] < load[g])
+                    g = q;
+            grp[i] = g;
+            load[g] += (double)pb[i] + (double)sb[i];
+        }
+    }
+    // Per group: images go into the arena one after another, wrapping to 0
+    // when one would pass its end; an op is built only once every earlier op
+    // of its group whose image shares bytes with its own is finished, and the
+    // op PG_SLOTS places back in the group, whose slot it takes (free_after).
     struct Placed { int op, lo, hi; };
-    std::vector<Placed> live;   // images placed so far, oldest first, with their byte ranges
-    int trot = 0, wrot = 0, next_off = 0, prev_off = 0;
+    struct GroupPlan {
+        std::vector<Placed> live;   // images placed so far, oldest first, with their byte ranges
+        std::vector<int> seq;       // the group's ops so far
+        int trot = 0, wrot = 0, next_off = 0, prev_off = 0;
+    };
+    std::vector<GroupPlan> gp(P);
     for (int i = 0; i < n_ops; ++i) {
         const rbq_program_op &o = ops[i];
+        GroupPlan &g = gp[grp[i]];
         ProgOp &p = d[i];
         p.planes = o.planes;
         p.scales = o.scales;
@@ -1103,46 +1188,50 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         p.out = o.out_features;
         p.in = o.in_features;
         p.wait_for = (int16_t)o.wait_for;
-        p.flags = flags[i];
+        p.flags = flags[i] | ((uint32_t)grp[i] << PF_GRP_SHIFT);
         const int tiles = (o.out_features + TILE_ROWS - 1) / TILE_ROWS;
-        const int base = tiles / G, extra = tiles % G;
+        const int base = tiles / Gl, extra = tiles % Gl;
         p.split = (uint32_t)base | ((uint32_t)extra << 8);
         const int nch = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
         p.magic = ((1u << 21) + nch - 1) / nch;
-        p.trot = trot;
-        // an op that reads the same x as the one before (and no op writes it)
-        // takes that op's image
-        const bool same = i > 0 && o.x == ops[i - 1].x && o.in_features == ops[i - 1].in_features &&
-                          !(flags[i] & PF_X_SHARED) && !(flags[i - 1] & PF_X_SHARED);
+        const int lpos = (int)g.seq.size();
+        p.trot = g.trot | (lpos << 16);
+        // an op that reads the same x as the group's op before it (and no op
+        // writes it) takes that op's image
+        const int prev = g.seq.empty() ? -1 : g.seq.back();
+        const bool same = prev >= 0 && o.x == ops[prev].x && o.in_features == ops[prev].in_features &&
+                          !(flags[i] & PF_X_SHARED) && !(flags[prev] & PF_X_SHARED);
+        int fa = lpos >= PG_SLOTS ? g.seq[lpos - PG_SLOTS] : -1;
         int off;
         if (same) {
             p.flags |= PF_REUSE;
-            p.free_after = -1;
-            off = prev_off;
-            live.back().op = i;   // the image is in use until this op
+            off = g.prev_off;
+            g.live.back().op = i;   // the image is in use until this op
         } else {
             const int size = nch * IMG_CHUNK;
-            off = next_off + size <= arena ? next_off : 0;
-            int fa = -1;
-            for (const Placed &q : live)
+            off = g.next_off + size <= arena ? g.next_off : 0;
+            for (const Placed &q : g.live)
                 if (q.lo < off + size && off < q.hi)
                     fa = std::max(fa, q.op);
-            p.free_after = (int16_t)fa;
-            live.push_back({i, off, off + size});
-            next_off = off + size;
+            g.live.push_back({i, off, off + size});
+            g.next_off = off + size;
         }
-        prev_off = off;
+        p.free_after = (int16_t)fa;
+        g.prev_off = off;
+        g.seq.push_back(i);
         p.nch_img = (uint32_t)nch | ((uint32_t)(off / 16) << 8);
-        p.flags |= (uint32_t)wrot << PF_WROT_SHIFT;
-        trot = (trot + extra) % G;
-        wrot = (wrot + ((tiles + G - 1) / G) * nch) % PG_STREAM;
-        for (int bb = 0; bb < G; ++bb) {
+        p.flags |= (uint32_t)g.wrot << PF_WROT_SHIFT;
+        const int trot_op = g.trot;
+        g.trot = (g.trot + extra) % Gl;
+        g.wrot = (g.wrot + ((tiles + Gl - 1) / Gl) * nch) % PG_STREAM;
+        for (int bl = 0; bl < Gl; ++bl) {
+            const int bb = grp[i] * Gl + bl;
             int t0, ntl;
-            op_tiles(base, extra, p.trot, bb, G, t0, ntl);
-            for (int s = 0; s < PG_STREAM; ++s) {
+            op_tiles(base, extra, trot_op, bl, Gl, t0, ntl);
+            for (int sw = 0; sw < PG_STREAM; ++sw) {
                 int u0, u1;
-                op_units(ntl * nch, (int)((p.flags >> PF_WROT_SHIFT) & 15u), s, u0, u1);
-                wu[bb * PG_STREAM + s] += u1 - u0;
+                op_units(ntl * nch, (int)((p.flags >> PF_WROT_SHIFT) & 15u), sw, u0, u1);
+                wu[bb * PG_STREAM + sw] += u1 - u0;
             }
         }
     }
@@ -1159,7 +1248,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
-    h->kind = PK_TILES | (group ? PK_GROUP : 0);
+    h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT);
     for (int i = 0; i < n_ops; ++i) {
         h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
         h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
@@ -1175,7 +1264,10 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP)) != 0)
+        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK)) != 0)
+        return RBQ_ERR_INVALID_ARG;
+    const int P = (h->kind & PK_P_MASK) >> PK_P_SHIFT;
+    if ((P != 1 && P != 2 && P != 4) || h->grid % P != 0 || (P > 1 && (h->kind & PK_WAITS)))
         return RBQ_ERR_INVALID_ARG;
     const bool group = (h->kind & PK_GROUP) != 0;
     if (group ? (h->K != 2 && h->K != 4) || !(h->kind & PK_TILES) : (h->K != 1 && h->K != 2))
@@ -1202,7 +1294,7 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
     hipLaunchKernelGGL((gemv_program_kernel<KK, RBQ_PROGRAM_RING, WW, TT, GG>), dim3(h->grid), dim3(PG_THREADS), \
                        h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status)
 #define RBQ_LAUNCH_PROGRAM_K(KK)                                         \
-    switch (h->kind) {                                                   \
+    switch (h->kind & (PK_WAITS | PK_TILES)) {                           \
     case 0: RBQ_LAUNCH_PROGRAM(KK, false, false, false); break;          \
     case PK_WAITS: RBQ_LAUNCH_PROGRAM(KK, true, false, false); break;    \
     case PK_TILES: RBQ_LAUNCH_PROGRAM(KK, false, true, false); break;    \
