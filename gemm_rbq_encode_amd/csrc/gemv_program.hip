@@ -68,7 +68,8 @@ constexpr int TILE_ROWS = 16;
 constexpr int CHUNK_WORDS = 16;                            // 512 columns
 constexpr int NC = 3;                                      // MFMA columns: the 3 limbs of one token
 constexpr int IMG_CHUNK = 8 * 4 * 16 * NC + 64;            // image bytes per chunk (+64: other banks)
-constexpr int PG_MAX_TILES = PG_PREP_THREADS / TILE_ROWS;  // rows of one op per workgroup: one per image thread
+constexpr int PG_ROWS_PER_THREAD = 2;                      // rows of one op that an image thread finishes, at most
+constexpr int PG_MAX_TILES = PG_ROWS_PER_THREAD * PG_PREP_THREADS / TILE_ROWS;   // 32 tiles of one op per workgroup
 constexpr int PG_MAX_XU = 4;                               // half-words (16 columns) per image thread
 constexpr int PG_MAX_CHUNKS = PG_MAX_XU * PG_PREP_THREADS / (2 * CHUNK_WORDS);   // 32: in <= 16384
 constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wait: 0.2 s of the
@@ -76,7 +77,7 @@ constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wai
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
 constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
 #ifndef RBQ_PROGRAM_GROUPS
-#define RBQ_PROGRAM_GROUPS 2                               // op groups of programs without waits (1, 2 or 4)
+#define RBQ_PROGRAM_GROUPS 4                               // op groups of programs without waits, at most (1, 2 or 4)
 #endif
 constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
 constexpr int PG_MAX_G = PG_MAX_CHUNKS * 4;                // 128-column groups of the widest input
@@ -130,6 +131,8 @@ constexpr int32_t PK_TILES = 2;        // every op reads the tile layout
 constexpr int32_t PK_GROUP = 4;        // g128 ops (scales per 128-column group, in the scale tile layout)
 constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups (1, 2 or 4)
 constexpr int32_t PK_P_MASK = 15 << PK_P_SHIFT;
+constexpr int PK_T_SHIFT = 8;          // bits 8..15: tiles of an op per workgroup at most (the LDS slots' size)
+constexpr int32_t PK_T_MASK = 255 << PK_T_SHIFT;
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
 // image arena what remains of the compute unit's LDS).  Programs of g128 ops
@@ -144,14 +147,15 @@ struct PgShared {
     uint32_t wmax[PG_SLOTS][PG_PREP];
     double wsum[PG_SLOTS][PG_PREP];                 // sums of q (exact: integers below 2^53)
     int shs[PG_SLOTS];
-    uint16_t sc_lds[PG_SLOTS][GROUP ? 1 : K][PG_PREP_THREADS];   // scales of the row each image thread finishes
+    uint16_t sc_lds[PG_SLOTS][GROUP ? 1 : K][PG_ROWS_PER_THREAD * PG_PREP_THREADS];   // scales of the rows finished
     int gsum[PG_SLOTS][GROUP ? PG_MAX_G : 1];         // g128: sum of q over each group (|sum| < 2^30)
 };
 
-// LDS ints per op slot of partial sums: per-row ops add int32 tile sums
-// [tile][plane][limb][row]; g128 ops store fp32 [tile][stream wave][row].
-__host__ __device__ constexpr int red_op_ints(int K, bool group) {
-    return PG_MAX_TILES * (group ? PG_STREAM : K * NC) * TILE_ROWS;
+// LDS ints per tile of an op slot of partial sums: per-row ops add int32
+// tile sums [tile][plane][limb][row]; g128 ops store fp32 [tile][stream
+// wave][row].  A program's slots hold its largest op's tiles per workgroup.
+__host__ __device__ constexpr int red_tile_ints(int K, bool group) {
+    return (group ? PG_STREAM : K * NC) * TILE_ROWS;
 }
 
 // Op counters: each op's count of finished workgroups is split over
@@ -369,11 +373,11 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             op_tiles(op.base, op.extra, op.trot, bl, Gl, t0, ntl);
         }
     };
-    // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][PG_MAX_TILES][K][NC][16]
+    // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][max_tiles][K][NC][16]
     const int pad = hdr->arena_bytes;
     int *red0 = reinterpret_cast<int *>(lds + pad + 16);
-    constexpr int RED_OP = red_op_ints(K, GROUP);
-    constexpr int RED_TILE = RED_OP / PG_MAX_TILES;                          // ints per tile
+    constexpr int RED_TILE = red_tile_ints(K, GROUP);                        // ints per tile
+    const int RED_OP = ((hdr->kind & PK_T_MASK) >> PK_T_SHIFT) * RED_TILE;   // ints per op slot
 
     // A wait that runs out only raises the LDS flag (the status word is
     // written once at the end): the stream waves then issue no global memory
@@ -420,13 +424,19 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 report_timeout();
             asm volatile("" ::: "memory");
             int *red = red0 + par * RED_OP;
-            const int row = t0 * TILE_ROWS + tid;
-            const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
+            const bool shared_y = WAITS && (op.flags & PF_Y_SHARED) != 0;
+#pragma unroll
+            for (int rr = 0; rr < PG_ROWS_PER_THREAD; ++rr) {
+            const int lr = tid + rr * PG_PREP_THREADS;   // row of the workgroup's tiles
+            if (rr > 0 && ntl * TILE_ROWS <= rr * PG_PREP_THREADS)
+                break;
+            const int row = t0 * TILE_ROWS + lr;
+            const bool rowok = lr < ntl * TILE_ROWS && row < op.out;
             float y = 0.0f;
             if (GROUP && rowok) {
                 // the stream waves' per-(tile, wave) slots, added in wave order
                 const float *rf = reinterpret_cast<const float *>(red);
-                const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+                const int tl = lr / TILE_ROWS, i = lr % TILE_ROWS;
                 float acc = 0.0f;
 #pragma unroll
                 for (int w = 0; w < PG_STREAM; ++w)
@@ -437,17 +447,16 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 #pragma unroll
                 for (int v = 0; v < PG_PREP; ++v)
                     sx += wsum[par][v];
-                const int tl = tid / TILE_ROWS, i = tid % TILE_ROWS;
+                const int tl = lr / TILE_ROWS, i = lr % TILE_ROWS;
 #pragma unroll
                 for (int k = 0; k < (GROUP ? 1 : K); ++k) {
                     const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
                     const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                                      65536.0 * (double)rp[2 * TILE_ROWS];
-                    y += h2f(sc_lds[par][k][tid]) * (float)(t * (2.0 / 128.0) - sx);
+                    y += h2f(sc_lds[par][k][lr]) * (float)(t * (2.0 / 128.0) - sx);
                 }
                 y = __builtin_ldexpf(y, -shs[par]);
             }
-            const bool shared_y = WAITS && (op.flags & PF_Y_SHARED) != 0;
             if (op.flags & PF_SILU) {
                 // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
                 const float up = __shfl_down(y, 1, RBQ_WAVE);
@@ -465,6 +474,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     __hip_atomic_store(op.y + row, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else
                     op.y[row] = h;
+            }
             }
             img_sync();   // every partial sum of the op has been read
             for (int e = tid; e < ntl * RED_TILE; e += PG_PREP_THREADS)
@@ -510,7 +520,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // the thread finishes.  x that an earlier op writes is loaded only after
         // the wait, with device-coherent loads.
         v4u xw[PG_MAX_XU][2];
-        uint16_t a_bits[K];
+        uint16_t a_bits[PG_ROWS_PER_THREAD][K];
         auto load_x = [&](const OpView &op) {
             const int nh = (op.in >> 5) * 2;
             const int xu = (op.nchunks * CHUNK_WORDS * 2 + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
@@ -544,11 +554,15 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 return;
             int t0, ntl;
             my_tiles(op, t0, ntl);
-            const int row = t0 * TILE_ROWS + tid;
-            const bool rowok = tid < ntl * TILE_ROWS && row < op.out;
 #pragma unroll
-            for (int k = 0; k < (GROUP ? 1 : K); ++k)
-                a_bits[k] = rowok ? op.scales[(size_t)k * op.out + row] : (uint16_t)0;
+            for (int rr = 0; rr < PG_ROWS_PER_THREAD; ++rr) {
+                const int lr = tid + rr * PG_PREP_THREADS;
+                const int row = t0 * TILE_ROWS + lr;
+                const bool rowok = lr < ntl * TILE_ROWS && row < op.out;
+#pragma unroll
+                for (int k = 0; k < (GROUP ? 1 : K); ++k)
+                    a_bits[rr][k] = rowok ? op.scales[(size_t)k * op.out + row] : (uint16_t)0;
+            }
         };
 
         // this wave's part of op i's image and sums is written: count it
@@ -567,8 +581,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     gsum[par][g] = gsum[prev][g];
             } else {
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    sc_lds[par][k][tid] = a_bits[k];
+                for (int rr = 0; rr < PG_ROWS_PER_THREAD; ++rr)
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        sc_lds[par][k][tid + rr * PG_PREP_THREADS] = a_bits[rr][k];
             }
             if (lane == 0)
                 wsum[par][wave] = wsum[prev][wave];
@@ -597,8 +613,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 wmax[par][wave] = mw;
             if (!GROUP) {
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    sc_lds[par][k][tid] = a_bits[k];
+                for (int rr = 0; rr < PG_ROWS_PER_THREAD; ++rr)
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        sc_lds[par][k][tid + rr * PG_PREP_THREADS] = a_bits[rr][k];
             }
             img_sync();
             uint32_t mx = 0;
@@ -1121,21 +1139,26 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     ProgHeader *h = reinterpret_cast<ProgHeader *>(img);
     ProgOp *d = reinterpret_cast<ProgOp *>(h + 1);
     int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
-    // LDS: the image arena takes what the partial sums leave
-    const size_t fixed = 16 + (size_t)PG_SLOTS * red_op_ints(K, group) * 4;
     int max_img = 0;
     for (int i = 0; i < n_ops; ++i)
         max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * IMG_CHUNK);
     const size_t budget = program_dynamic_lds(K, group);
-    if (fixed + (size_t)max_img > budget)
-        return RBQ_ERR_UNSUPPORTED;
-    const int arena = (int)((budget - fixed) / 16 * 16);
+    // LDS the partial sums take when each workgroup gets up to mt tiles of an op
+    auto fixed_lds = [&](int mt) { return 16 + (size_t)PG_SLOTS * mt * red_tile_ints(K, group) * 4; };
+    auto max_tiles_of = [&](int gl) {
+        int mt = 1;
+        for (int i = 0; i < n_ops; ++i)
+            mt = std::max(mt, ((ops[i].out_features + TILE_ROWS - 1) / TILE_ROWS + gl - 1) / gl);
+        return mt;
+    };
     // Op groups.  Without waits the ops are independent, and the workgroups
     // are split into P groups of G / P: each op goes to one group (the one
     // with the fewest plane bytes so far), whose workgroups take its tiles,
     // so every workgroup runs 1/P of the ops with P times their tiles each.
     // What a workgroup spends per op (images, finishes, flushes, cursors) is
-    // then spread over P times the units.  Programs with waits keep one group:
+    // then spread over P times the units.  The most groups whose largest op
+    // fits a workgroup (PG_MAX_TILES tiles, and its partial sums in LDS next
+    // to the largest image) are taken.  Programs with waits keep one group:
     // their ops run one after another anyway.
     int P = 1;
     {
@@ -1144,15 +1167,20 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             waits |= ops[i].wait_for >= 0;
         int cand = RBQ_PROGRAM_GROUPS;
         while (cand > 1) {
-            bool fits = !waits && n_ops >= cand && G % cand == 0;
-            for (int i = 0; fits && i < n_ops; ++i)
-                fits = ops[i].out_features <= PG_MAX_TILES * TILE_ROWS * (G / cand);
+            const bool fits = !waits && n_ops >= cand && G % cand == 0 && max_tiles_of(G / cand) <= PG_MAX_TILES &&
+                              fixed_lds(max_tiles_of(G / cand)) + (size_t)max_img <= budget;
             if (fits)
                 break;
             cand /= 2;
         }
         P = cand;
     }
+    const int max_tiles = max_tiles_of(G / P);
+    // LDS: the image arena takes what the partial sums leave
+    const size_t fixed = fixed_lds(max_tiles);
+    if (max_tiles > PG_MAX_TILES || fixed + (size_t)max_img > budget)
+        return RBQ_ERR_UNSUPPORTED;
+    const int arena = (int)((budget - fixed) / 16 * 16);
     const int Gl = G / P;
     std::vector<int> grp(n_ops, 0);
     {
@@ -1248,7 +1276,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
-    h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT);
+    h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT) | (max_tiles << PK_T_SHIFT);
     for (int i = 0; i < n_ops; ++i) {
         h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
         h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
@@ -1264,7 +1292,10 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK)) != 0)
+        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK | PK_T_MASK)) != 0)
+        return RBQ_ERR_INVALID_ARG;
+    const int mt = (h->kind & PK_T_MASK) >> PK_T_SHIFT;
+    if (mt < 1 || mt > PG_MAX_TILES)
         return RBQ_ERR_INVALID_ARG;
     const int P = (h->kind & PK_P_MASK) >> PK_P_SHIFT;
     if ((P != 1 && P != 2 && P != 4) || h->grid % P != 0 || (P > 1 && (h->kind & PK_WAITS)))
