@@ -68,8 +68,8 @@ constexpr int TILE_ROWS = 16;
 constexpr int CHUNK_WORDS = 16;                            // 512 columns
 constexpr int NC = 3;                                      // MFMA columns: the 3 limbs of one token
 constexpr int IMG_CHUNK = 8 * 4 * 16 * NC + 64;            // image bytes per chunk (+64: other banks)
-constexpr int PG_ROWS_PER_THREAD = 2;                      // rows of one op that an image thread finishes, at most
-constexpr int PG_MAX_TILES = PG_ROWS_PER_THREAD * PG_PREP_THREADS / TILE_ROWS;   // 32 tiles of one op per workgroup
+constexpr int PG_ROWS_PER_THREAD = 3;                      // rows of one op that an image thread finishes, at most
+constexpr int PG_MAX_TILES = PG_ROWS_PER_THREAD * PG_PREP_THREADS / TILE_ROWS;   // 48 tiles of one op per workgroup
 constexpr int PG_MAX_XU = 4;                               // half-words (16 columns) per image thread
 constexpr int PG_MAX_CHUNKS = PG_MAX_XU * PG_PREP_THREADS / (2 * CHUNK_WORDS);   // 32: in <= 16384
 constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wait: 0.2 s of the
@@ -77,7 +77,7 @@ constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wai
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
 constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
 #ifndef RBQ_PROGRAM_GROUPS
-#define RBQ_PROGRAM_GROUPS 4                               // op groups of programs without waits, at most (1, 2 or 4)
+#define RBQ_PROGRAM_GROUPS 8                               // op groups of programs without waits, at most (1, 2, 4 or 8)
 #endif
 constexpr uint32_t PG_MAGIC = 0x52425150u;                 // "RBQP"
 constexpr int PG_MAX_G = PG_MAX_CHUNKS * 4;                // 128-column groups of the widest input
@@ -90,7 +90,7 @@ constexpr uint32_t PF_Y_SHARED = 8u;   // y is read (or written again) by a late
 constexpr uint32_t PF_REUSE = 32u;     // same x as the op before: its image is used again
 constexpr uint32_t PF_TILES = 64u;     // planes in the tile layout (1 KB per 16-row, 512-column unit)
 constexpr int PF_WROT_SHIFT = 8;       // bits 8..11: rotation of the stream waves over the units
-constexpr int PF_GRP_SHIFT = 12;       // bits 12..13: the op group (of the workgroups) that runs the op
+constexpr int PF_GRP_SHIFT = 12;       // bits 12..14: the op group (of the workgroups) that runs the op
 
 // One op in device memory (64 bytes).
 struct ProgOp {
@@ -129,7 +129,7 @@ static_assert(sizeof(ProgHeader) == 32, "header layout");
 constexpr int32_t PK_WAITS = 1;        // some op waits for another: the kernel with the waits
 constexpr int32_t PK_TILES = 2;        // every op reads the tile layout
 constexpr int32_t PK_GROUP = 4;        // g128 ops (scales per 128-column group, in the scale tile layout)
-constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups (1, 2 or 4)
+constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups (1, 2, 4 or 8)
 constexpr int32_t PK_P_MASK = 15 << PK_P_SHIFT;
 constexpr int PK_T_SHIFT = 8;          // bits 8..15: tiles of an op per workgroup at most (the LDS slots' size)
 constexpr int32_t PK_T_MASK = 255 << PK_T_SHIFT;
@@ -324,7 +324,7 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     v.img_off = (int)(q[14] >> 8) * 16;
     v.magic = q[15];
     v.wrot = (int)((v.flags >> PF_WROT_SHIFT) & 15u);
-    v.grp = (int)((v.flags >> PF_GRP_SHIFT) & 3u);
+    v.grp = (int)((v.flags >> PF_GRP_SHIFT) & 7u);
     return v;
 }
 
@@ -1298,7 +1298,7 @@ rbq_status program_check(const void *image) {
     if (mt < 1 || mt > PG_MAX_TILES)
         return RBQ_ERR_INVALID_ARG;
     const int P = (h->kind & PK_P_MASK) >> PK_P_SHIFT;
-    if ((P != 1 && P != 2 && P != 4) || h->grid % P != 0 || (P > 1 && (h->kind & PK_WAITS)))
+    if ((P != 1 && P != 2 && P != 4 && P != 8) || h->grid % P != 0 || (P > 1 && (h->kind & PK_WAITS)))
         return RBQ_ERR_INVALID_ARG;
     const bool group = (h->kind & PK_GROUP) != 0;
     if (group ? (h->K != 2 && h->K != 4) || !(h->kind & PK_TILES) : (h->K != 1 && h->K != 2))
