@@ -467,7 +467,8 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
             const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
             const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                              65536.0 * (double)rp[2 * TILE_ROWS];
-            y += h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - sx);
+            // one explicit fma per plane, as in the program kernel
+            y = __builtin_fmaf(h2f(a_bits[k]), (float)(t * (2.0 / 128.0) - sx), y);
         }
         return __builtin_ldexpf(y, -shs[m]);
     };
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                 const float y = rowok ? row_sum(m) : 0.0f;
                 const float up = __shfl_down(y, 1, RBQ_WAVE);
                 if (rowok && (tid & 1) == 0)
-                    Y[(size_t)(m0 + m) * (out / 2) + (t0 * TILE_ROWS + tid) / 2] = f2h(silu_f32(y) * up);
+                    Y[(size_t)(m0 + m) * (out / 2) + (t0 * TILE_ROWS + tid) / 2] = silu_mul_f16(y, up);
             }
         }
     }

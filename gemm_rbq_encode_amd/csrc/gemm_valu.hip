@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(
         if (silu)
             acc[1] = wave_sum_f32(acc[1]);
         if (lane == 0)
-            Y[(size_t)m * nout + r] = f2h(silu ? silu_f32(acc[0]) * acc[1] : acc[0]);
+            Y[(size_t)m * nout + r] = silu ? silu_mul_f16(acc[0], acc[1]) : f2h(acc[0]);
     }
 }
 

@@ -453,7 +453,8 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
                     const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
                                      65536.0 * (double)rp[2 * TILE_ROWS];
-                    y += h2f(sc_lds[par][k][lr]) * (float)(t * (2.0 / 128.0) - sx);
+                    // one explicit fma per plane, as in the flat kernel
+                    y = __builtin_fmaf(h2f(sc_lds[par][k][lr]), (float)(t * (2.0 / 128.0) - sx), y);
                 }
                 y = __builtin_ldexpf(y, -shs[par]);
             }
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
                 const float up = __shfl_down(y, 1, RBQ_WAVE);
                 if (rowok && (tid & 1) == 0) {
-                    const uint16_t h = f2h(silu_f32(y) * up);
+                    const uint16_t h = silu_mul_f16(y, up);
                     GLOBAL uint16_t *dst = op.y + row / 2;
                     if (shared_y)
                         __hip_atomic_store(dst, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

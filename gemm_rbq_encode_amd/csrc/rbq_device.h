@@ -55,6 +55,15 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne(double v) {
     return (uint16_t)(sign | bits);
 }
 
+// silu(gate) * up as binary16 bits, rounded once: the product of two fp32
+// values is exact in fp64.  Every kernel with the gate/up epilogue writes
+// through this, so none depends on whether the compiler fuses the product
+// and the conversion into one mixed-precision fma (one rounding) or rounds
+// to fp32 first (two).
+__device__ __forceinline__ uint16_t silu_mul_f16(float gate, float up) {
+    return f64_to_f16_rne((double)silu_f32(gate) * (double)up);
+}
+
 // Correctly rounded S / n in fp64 (n a positive integer), whatever the
 // accuracy of the compiler's division sequence: the quotient is corrected by
 // the exact remainder S - q n (an FMA) to the nearer neighbour, ties to even.

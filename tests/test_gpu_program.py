@@ -265,3 +265,44 @@ def test_mismatched_device_image_runs_nothing():
     bad[40] ^= 1
     assert L.rbq_program_run(ctypes.cast(bad, ctypes.c_void_p), pa.image_dev.data_ptr(), pa.counters.data_ptr(),
                              None, None) == rbq.RBQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_many_independent_ragged_ops(seed):
+    """Sixty independent ops of random ragged shapes (rows 1..6000, inputs
+    128..16384 columns), half on the tile layout, some sharing x with the op
+    before them (the image is reused when both fall in one op group): the
+    program splits them over op groups, each group planning its own slots
+    and images.  Every op must equal rbq_gemv's flat kernel bit for bit, on
+    two runs in a row."""
+    rng = np.random.default_rng(seed)
+    ops, outs = [], []
+    prev_x = None
+    for i in range(60):
+        o = int(rng.integers(1, 6001))
+        n = int(rng.integers(1, 129)) * 128
+        if prev_x is not None and rng.random() < 0.3 and prev_x.numel() == n:
+            x = prev_x
+        else:
+            x = torch.from_numpy(workloads.gaussian_activations(1, n, seed=seed * 1000 + i)[0].view(np.float16)).to(dev())
+        p, s = layer(o, n, 2, seed=seed * 5000 + i)
+        pt, st = to_dev(p, s)
+        epi = int(o % 2 == 0 and rng.random() < 0.2)
+        y = torch.full((o // 2 if epi else o,), float("nan"), dtype=torch.float16, device=dev())
+        planes = rbq.pack_tiles(pt) if i % 2 else pt
+        ops.append({"planes": planes, "scales": st, "x": x, "y": y, "epilogue": epi, "rows_planes": pt})
+        outs.append(y)
+        prev_x = x
+    prog = rbq.Program([{k: v for k, v in op.items() if k != "rows_planes"} for op in ops], num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    for run in range(2):
+        for y in outs:
+            y.fill_(float("nan"))
+        print(f"many ragged ops seed={seed} run {run}", flush=True)
+        prog.run(status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert not prog.counters.any()
+        for i, op in enumerate(ops):
+            ref = eager_flat(op["rows_planes"], op["scales"], op["x"], op["epilogue"])
+            assert torch.equal(outs[i].view(torch.int16), ref.view(torch.int16)), f"run {run} op {i}"

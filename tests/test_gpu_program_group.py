@@ -152,3 +152,27 @@ def test_group_program_chain_with_waits():
         assert not prog.counters.any()
         for i, (a, o) in enumerate(zip(ref, ops)):
             assert torch.equal(a.view(torch.int16), o["y"].view(torch.int16)), (rep, i)
+
+
+def test_many_independent_g128_ops():
+    """Thirty independent g128 ops (K = 4) of random ragged shapes, spread
+    over op groups, against the oracle; two runs give the same bits."""
+    rng = np.random.default_rng(17)
+    ops, host = [], []
+    for i in range(30):
+        o = int(rng.integers(1, 3000))
+        n = int(rng.integers(1, 65)) * 128
+        p, s = g128_layer(o, n, 4, seed=9000 + i)
+        x = torch.from_numpy(workloads.gaussian_activations(1, n, seed=900 + i)[0].view(np.float16)).to(dev())
+        y = torch.full((o,), float("nan"), dtype=torch.float16, device=dev())
+        ops.append(device_op(p, s, n, x, y))
+        host.append((p, s, x.cpu().numpy().view(np.uint16)))
+    print("many g128 ops", flush=True)
+    prog = run_program(ops, 4)
+    first = [o["y"].clone() for o in ops]
+    for i, ((p, s, xb), op) in enumerate(zip(host, ops)):
+        assert_close(op["y"].cpu().numpy(), oracle.gemm(p, s, xb, 128)[0], f"op {i} {p.shape[1]}x{xb.shape[0]}")
+    prog.run()
+    torch.cuda.synchronize()
+    for i, (a, o) in enumerate(zip(first, ops)):
+        assert torch.equal(a.view(torch.int16), o["y"].view(torch.int16)), f"op {i}: second run differs"
