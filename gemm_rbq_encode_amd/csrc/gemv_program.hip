@@ -76,6 +76,8 @@ constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wai
                                                            // 100 MHz real-time clock (never reached)
 constexpr size_t PG_MIN_LDS = 96 * 1024;                   // one workgroup per compute unit
 constexpr int PG_SLOTS = 4;                                // ops in flight: partial sums, scales, sums
+constexpr uint32_t PG_NO_NEXT = 0xFFFu;                    // an op's group has no later op (> RBQ_PROGRAM_MAX_OPS)
+static_assert(RBQ_PROGRAM_MAX_OPS < (int)PG_NO_NEXT, "op links take 12 bits");
 #ifndef RBQ_PROGRAM_GROUPS
 #define RBQ_PROGRAM_GROUPS 8                               // op groups of programs without waits, at most (1, 2, 4 or 8)
 #endif
@@ -106,7 +108,8 @@ struct ProgOp {
     uint32_t flags;
     int32_t trot;         // rotation of the group's workgroups that take one more tile (bits 0..15) |
                           // the op's place in its group's sequence (bits 16..)
-    uint32_t split;       // tiles / G (bits 0..7) | tiles % G (bits 8..): the tile split, precomputed
+    uint32_t split;       // tiles / G (bits 0..7) | tiles % G (bits 8..19): the tile split, precomputed |
+                          // the next op of the same group (bits 20..31; PG_NO_NEXT after its last)
     uint32_t nch_img;     // 512-column chunks (bits 0..7) | image offset in the arena / 16 (bits 8..)
     uint32_t magic;       // ceil(2^21 / chunks): unit -> (tile, chunk) by a multiply and a shift
 };
@@ -286,6 +289,7 @@ struct OpView {
     GLOBAL uint16_t *y;
     int out, in, wait_for, base, extra, nchunks, trot, wrot, free_after, img_off;
     int grp, lpos;        // the op's group, and its place in the group's sequence (its slot: lpos % PG_SLOTS)
+    int next;             // the group's next op (>= n_ops after its last)
     uint32_t flags, magic;
 };
 
@@ -319,7 +323,8 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     v.trot = (int)(q[12] & 0xFFFFu);
     v.lpos = (int)(q[12] >> 16);
     v.base = (int)(q[13] & 255u);
-    v.extra = (int)(q[13] >> 8);
+    v.extra = (int)((q[13] >> 8) & 0xFFFu);
+    v.next = (int)(q[13] >> 20);
     v.nchunks = (int)(q[14] & 255u);
     v.img_off = (int)(q[14] >> 8) * 16;
     v.magic = q[15];
@@ -688,13 +693,17 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 ++i;
             return i;
         };
+        // the group's ops are linked (each descriptor names the group's next
+        // op), so only the first one is searched for
         auto finish_upto = [&](int &next_fin, int upto) {
-            for (; next_fin <= upto; ++next_fin)
-                if (op_view(ops_g, next_fin).grp == mygrp)
-                    finish(next_fin);
+            while (next_fin <= upto) {
+                const int nf = op_view(ops_g, next_fin).next;
+                finish(next_fin);
+                next_fin = nf;
+            }
         };
-        int next_fin = 0;
         int i = next_mine(0);
+        int next_fin = i;
         OpView cur = op_view(ops_g, i < n_ops ? i : 0);
         if (i < n_ops) {
             if (!(WAITS && (cur.flags & PF_X_SHARED)))
@@ -715,7 +724,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     load_x(cur);
                 build(i, cur);
             }
-            const int nx = next_mine(i + 1);
+            const int nx = cur.next;
             if (nx < n_ops) {
                 // the next op's loads go out now, to arrive while this op streams
                 cur = op_view(ops_g, nx);
@@ -732,7 +741,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         const int total = wave_units[b * PG_STREAM + sw];
 
         // ---- load cursor: the next (op, unit) whose weights are requested
-        int lop = 0, lu = 0, lu1 = 0, lt0 = 0, lnch = 1, lwords = 4, lout = 1;
+        int lop = 0, lnext = 0, lu = 0, lu1 = 0, lt0 = 0, lnch = 1, lwords = 4, lout = 1;
         bool ltiles = false;
         uint32_t lmagic = 0;
         const OpView op0 = op_view(ops_g, 0);
@@ -757,9 +766,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     lstride = ltiles ? (size_t)((op.out + TILE_ROWS - 1) / TILE_ROWS) * op.nchunks * 256
                                      : (size_t)op.out * lwords;
                     lmagic = op.magic;
+                    lnext = op.next;
                     return;
                 }
-                ++lop;
+                lop = op.grp == mygrp ? op.next : lop + 1;
             }
         };
         // lanes (li, lg) read words 4lg .. 4lg+3 of row li of a unit's tile
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 }
                 laststride = lstride;
                 if (++lu == lu1) {
-                    ++lop;
+                    lop = lnext;
                     lseek();
                 }
             }
@@ -804,7 +814,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         };
 
         // ---- consume cursor: the op and unit the MFMAs work on
-        int cop = 0, cu = 0, cu1 = 0, cnch = 1, ctile = 0, cchunk = 0, cimg = 0, cpar = 0;
+        int cop = 0, cnext = 0, cu = 0, cu1 = 0, cnch = 1, ctile = 0, cchunk = 0, cimg = 0, cpar = 0;
         auto report = [&](int par) {   // this wave is done with the op in slot par
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (lane == 0)
@@ -830,11 +840,12 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                         const int tq = (int)(((uint32_t)cu * op.magic) >> 21);
                         ctile = tq;
                         cchunk = cu - tq * cnch;
+                        cnext = op.next;
                         return;
                     }
                     report(cpar);
                 }
-                ++cop;
+                cop = op.grp == mygrp ? op.next : cop + 1;
             }
         };
 
@@ -931,7 +942,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 cchunk = tile_end ? 0 : cchunk + 1;
                 if (op_end) {
                     report(cpar);
-                    ++cop;
+                    cop = cnext;
                     cseek();
                 }
             } else {
@@ -989,7 +1000,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 }
                 if (op_end) {
                     report(cpar);
-                    ++cop;
+                    cop = cnext;
                     cseek();
                 }
             }
@@ -1067,6 +1078,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     if (group ? (K != 2 && K != 4) : K > 2)
         return RBQ_ERR_UNSUPPORTED;
     const int G = program_num_cus();
+    if (G > 4095)   // the tile split keeps tiles % G in 12 bits
+        return RBQ_ERR_UNSUPPORTED;
     if (bytes < image_bytes(n_ops, G))
         return RBQ_ERR_INVALID_ARG;
     auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
@@ -1153,8 +1166,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         return mt;
     };
     // Op groups.  Without waits the ops are independent, and the workgroups
-    // are split into P groups of G / P: each op goes to one group (the one
-    // with the fewest plane bytes so far), whose workgroups take its tiles,
+    // are split into P groups of G / P: each op goes to one group (below:
+    // balanced by plane bytes), whose workgroups take its tiles,
     // so every workgroup runs 1/P of the ops with P times their tiles each.
     // What a workgroup spends per op (images, finishes, flushes, cursors) is
     // then spread over P times the units.  The most groups whose largest op
@@ -1185,8 +1198,18 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     const int Gl = G / P;
     std::vector<int> grp(n_ops, 0);
     {
+        // largest op first, each to the group with the fewest bytes so far;
+        // a group then runs its ops in program order.  (Taken in program
+        // order instead, the Llama-2-7B step left its heaviest group 6 % above
+        // the mean, and the step waits for that group.)
+        std::vector<int> order(n_ops);
+        for (int i = 0; i < n_ops; ++i)
+            order[i] = i;
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+            return (double)pb[a] + (double)sb[a] > (double)pb[b] + (double)sb[b];
+        });
         std::vector<double> load(P, 0.0);
-        for (int i = 0; i < n_ops; ++i) {
+        for (const int i : order) {
             int g = 0;
             for (int q = 1; q < P; ++q)
                 if (load[q] < load[g])
@@ -1220,11 +1243,13 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         p.flags = flags[i] | ((uint32_t)grp[i] << PF_GRP_SHIFT);
         const int tiles = (o.out_features + TILE_ROWS - 1) / TILE_ROWS;
         const int base = tiles / Gl, extra = tiles % Gl;
-        p.split = (uint32_t)base | ((uint32_t)extra << 8);
+        p.split = (uint32_t)base | ((uint32_t)extra << 8) | (PG_NO_NEXT << 20);
         const int nch = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
         p.magic = ((1u << 21) + nch - 1) / nch;
         const int lpos = (int)g.seq.size();
         p.trot = g.trot | (lpos << 16);
+        if (!g.seq.empty())   // link the group's previous op to this one
+            d[g.seq.back()].split = (d[g.seq.back()].split & 0xFFFFFu) | ((uint32_t)i << 20);
         // an op that reads the same x as the group's op before it (and no op
         // writes it) takes that op's image
         const int prev = g.seq.empty() ? -1 : g.seq.back();
