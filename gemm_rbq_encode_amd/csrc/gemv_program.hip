@@ -805,12 +805,28 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     lseek();
                 }
             }
+            // Every plane and scale byte is read once per run.  On the tile
+            // layout (a wave load is one whole 1 KB block) the loads are
+            // non-temporal: the Llama-2-7B step took 280 us instead of 295 us.
+            // On the row layout a 128-byte line holds the half-lines of two
+            // units, and kept in L2 the second half is a hit (non-temporal
+            // there: 398 us instead of 320 us).
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                slot[k] = *reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride);
+            for (int k = 0; k < K; ++k) {
+                GLOBAL const v4u *src = reinterpret_cast<GLOBAL const v4u *>(lastp + k * laststride);
+                if constexpr (TILES)
+                    slot[k] = __builtin_nontemporal_load(src);
+                else
+                    slot[k] = *src;
+            }
 #pragma unroll
-            for (int pp = 0; pp < KS; ++pp)
-                slot[K + pp] = *reinterpret_cast<GLOBAL const v4u *>(lastsp + pp * 128);
+            for (int pp = 0; pp < KS; ++pp) {
+                GLOBAL const v4u *src = reinterpret_cast<GLOBAL const v4u *>(lastsp + pp * 128);
+                if constexpr (TILES)
+                    slot[K + pp] = __builtin_nontemporal_load(src);
+                else
+                    slot[K + pp] = *src;
+            }
         };
 
         // ---- consume cursor: the op and unit the MFMAs work on
