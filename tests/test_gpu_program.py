@@ -306,3 +306,37 @@ def test_many_independent_ragged_ops(seed):
         for i, op in enumerate(ops):
             ref = eager_flat(op["rows_planes"], op["scales"], op["x"], op["epilogue"])
             assert torch.equal(outs[i].view(torch.int16), ref.view(torch.int16)), f"run {run} op {i}"
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_batch_tokens_as_ops_on_shared_planes(M):
+    """A batch of M tokens through one linear as M one-token ops on the same
+    planes (tile layout), one after another, as a decode step for a batch
+    runs them: every token's output meets the oracle's bar, equals rbq_gemv
+    on the flat kernel bit for bit, and the batch agrees with rbq_gemm at M
+    tokens within the same bar."""
+    shapes = [(12288, 4096), (4096, 11008)]
+    ops, checks = [], []
+    for i, (o, n) in enumerate(shapes):
+        p, s = layer(o, n, 2, seed=300 + i)
+        pt, st = to_dev(p, s)
+        tiles = rbq.pack_tiles(pt)
+        X = workloads.gaussian_activations(M, n, seed=310 + i)
+        xd = torch.from_numpy(X.view(np.float16)).to(dev())
+        Y = torch.full((M, o), float("nan"), dtype=torch.float16, device=dev())
+        for m in range(M):
+            ops.append({"planes": tiles, "scales": st, "x": xd[m], "y": Y[m]})
+        checks.append((p, s, pt, st, X, xd, Y))
+    prog = rbq.Program(ops, num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i, (p, s, pt, st, X, xd, Y) in enumerate(checks):
+        yref = oracle.gemm(p, s, X)
+        for m in range(M):
+            assert_close(Y[m].cpu().numpy(), yref[m], f"linear {i} token {m}")
+            ref = eager_flat(pt, st, xd[m])
+            assert torch.equal(Y[m].view(torch.int16), ref.view(torch.int16)), f"linear {i} token {m}"
+        yb = rbq.gemm(pt, st, xd, 0)
+        assert_close(Y.cpu().numpy(), yb.cpu().numpy(), f"linear {i} against rbq_gemm at {M} tokens")
