@@ -59,7 +59,8 @@ constexpr int FL_MAX_M = 16;                          // tokens per call (passes
 constexpr int FL_MAX_TILES = FL_THREADS / TILE_ROWS;  // one finishing thread per row
 constexpr int FL_MAX_XU = 4;                          // half-words per image thread and token
 constexpr int FL_MAX_IN = FL_MAX_XU * FL_PREP_THREADS * 16;  // 16 columns per half-word
-constexpr int FL_SPIN_LIMIT = 1 << 22;                // bound of each LDS wait (never reached)
+constexpr int FL_SPIN_LIMIT = 1 << 22;                // bound of each LDS wait (never reached;
+                                                      // a wait that runs out makes the rows NaN)
 
 // LDS bytes: activation image, 16 zero bytes, int32 partial sums.
 size_t flat_lds_bytes(int in, int K, int mt, int tiles_per_wg) {
@@ -81,13 +82,19 @@ int flat_units_per_thread(int in) {
 
 // Waits until the LDS counter reaches `target` (relaxed reads: the writers
 // release their LDS stores before counting, and LDS is coherent within the
-// compute unit).
-__device__ __forceinline__ void lds_wait_count(int *counter, int target) {
+// compute unit).  A wait that runs out sets *failed: the workgroup then
+// writes fp16 NaN for its rows instead of a value built on missing data.
+__device__ __forceinline__ void lds_wait_count(int *counter, int target, int *failed) {
+    bool done = false;
     for (int i = 0; i < FL_SPIN_LIMIT; ++i) {
-        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            done = true;
             break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (!done)
+        __hip_atomic_store(failed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" ::: "memory");
 }
 
@@ -105,6 +112,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     __shared__ double wsum[MT][FL_PREP];   // exact: integer sums below 2^53
     __shared__ int shs[MT];
     __shared__ int counters[2];       // prep waves past the maximum, past the image
+    __shared__ int wait_failed;       // an LDS wait ran out: the rows are written as NaN
 
     const int tid = threadIdx.x;
     const int lane = tid & (RBQ_WAVE - 1);
@@ -144,8 +152,10 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
     // wave passes one s_barrier).  (The same split for one token measured
     // slower.)
     auto lds_init = [&]() {
-        if (tid == 0)
+        if (tid == 0) {
             counters[0] = counters[1] = 0;
+            wait_failed = 0;
+        }
         for (int i = tid; i < ntl * K * NC * TILE_ROWS; i += FL_THREADS)
             red[i] = 0;
         if (tid < 4)
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         }
         if (lane == 0)
             __hip_atomic_fetch_add(&counters[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        lds_wait_count(&counters[0], FL_PREP);
+        lds_wait_count(&counters[0], FL_PREP, &wait_failed);
 
         // |x| < 2^E per token; q = round(x * 2^sh), sh = 22 - E, |q| <= 2^22
         int sh[MT];
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         for (int d = 0; d < RING; ++d)
             load_unit(ring[d]);
         load_scales();
-        lds_wait_count(&counters[1], FL_PREP);
+        lds_wait_count(&counters[1], FL_PREP, &wait_failed);
 
         // acc[k][s] collects bit position s of plane k
         v4i acc[K][8];
@@ -473,6 +483,9 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
         return __builtin_ldexpf(y, -shs[m]);
     };
     const bool rowok = tid < ntl * TILE_ROWS && t0 * TILE_ROWS + tid < out;
+    // fp16 NaN in place of every output of the workgroup after a wait ran out
+    const bool failed = __hip_atomic_load(&wait_failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    auto out16 = [&](uint16_t h) { return failed ? (uint16_t)0x7E00u : h; };
     if constexpr (DUAL) {
         // plane k against copy k, each copy with its own power of two
         if (rowok) {
@@ -489,14 +502,14 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                                  65536.0 * (double)rp[2 * TILE_ROWS];
                 y += __builtin_ldexpf(h2f(a_bits[k]) * (float)(t * (2.0 / 128.0) - sx), -shs[k]);
             }
-            Y[t0 * TILE_ROWS + tid] = f2h(y);
+            Y[t0 * TILE_ROWS + tid] = out16(f2h(y));
         }
     } else if constexpr (!SILU) {
         if (rowok) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 if (m < mt)
-                    Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = f2h(row_sum(m));
+                    Y[(size_t)(m0 + m) * out + t0 * TILE_ROWS + tid] = out16(f2h(row_sum(m)));
         }
     } else {
 #pragma unroll
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(FL_THREADS, 1) void gemm_flat_kernel(
                 const float y = rowok ? row_sum(m) : 0.0f;
                 const float up = __shfl_down(y, 1, RBQ_WAVE);
                 if (rowok && (tid & 1) == 0)
-                    Y[(size_t)(m0 + m) * (out / 2) + (t0 * TILE_ROWS + tid) / 2] = silu_mul_f16(y, up);
+                    Y[(size_t)(m0 + m) * (out / 2) + (t0 * TILE_ROWS + tid) / 2] = out16(silu_mul_f16(y, up));
             }
         }
     }

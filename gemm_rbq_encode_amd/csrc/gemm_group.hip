@@ -55,7 +55,8 @@ constexpr int IMG_CHUNK = 8 * 4 * IMG_ENTRY_ROW + 64;  // padded: next chunk on 
 constexpr int GR_MAX_XU = 4;                           // half-words per image thread
 constexpr int GR_MAX_IN = GR_MAX_XU * GR_PREP_THREADS * 16;
 constexpr int GR_MAX_TILES = GR_THREADS / TILE_ROWS;   // one finishing thread per row
-constexpr int GR_SPIN_LIMIT = 1 << 22;                 // bound of each LDS wait (never reached)
+constexpr int GR_SPIN_LIMIT = 1 << 22;                 // bound of each LDS wait (never reached;
+                                                       // a wait that runs out makes the rows NaN)
 constexpr int GR_RING = 2;
 
 // LDS bytes: image, 16 zero bytes, per-group sums of q, the tiles' scales,
@@ -66,12 +67,19 @@ size_t group_lds_bytes(int in, int K, int tiles_per_wg) {
            (size_t)tiles_per_wg * GR_STREAM * TILE_ROWS * 4;
 }
 
-__device__ __forceinline__ void lds_wait_count(int *counter, int target) {
+// Waits until the LDS counter reaches `target`; a wait that runs out sets
+// *failed, and the workgroup then writes fp16 NaN for its rows.
+__device__ __forceinline__ void lds_wait_count(int *counter, int target, int *failed) {
+    bool done = false;
     for (int i = 0; i < GR_SPIN_LIMIT; ++i) {
-        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            done = true;
             break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (!done)
+        __hip_atomic_store(failed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     asm volatile("" ::: "memory");
 }
 
@@ -94,6 +102,7 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
     __shared__ uint32_t wmax[GR_PREP];
     __shared__ int shs;
     __shared__ int counters[3];       // image waves past the maximum, the image, the scales
+    __shared__ int wait_failed;       // an LDS wait ran out: the rows are written as NaN
 
     const int tid = threadIdx.x;
     const int lane = tid & (RBQ_WAVE - 1);
@@ -113,8 +122,10 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
     uint16_t *scl = reinterpret_cast<uint16_t *>(lds + pad + 16 + G * 4);        // [ntl][K][G][16]
     float *red = reinterpret_cast<float *>(scl + (size_t)ntl * K * G * TILE_ROWS);   // [ntl][12][16]
 
-    if (tid == 0)
+    if (tid == 0) {
         counters[0] = counters[1] = counters[2] = 0;
+        wait_failed = 0;
+    }
     for (int i = tid; i < ntl * GR_STREAM * TILE_ROWS; i += GR_THREADS)
         red[i] = 0.0f;
     if (tid < 4)
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
             wmax[wave] = mxw;
             __hip_atomic_fetch_add(&counters[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        lds_wait_count(&counters[0], GR_PREP);
+        lds_wait_count(&counters[0], GR_PREP, &wait_failed);
         uint32_t mx = 0;
 #pragma unroll
         for (int v = 0; v < GR_PREP; ++v)
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
 #pragma unroll
         for (int d = 0; d < GR_RING; ++d)
             load_unit(wring[d]);
-        lds_wait_count(&counters[1], GR_PREP);
+        lds_wait_count(&counters[1], GR_PREP, &wait_failed);
 
         // B: lane (li, lg) supplies MFMA column li from lane group lg, nonzero
         // only where column li's group li / 3 is this lane group's group
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
                 }
             }
             if (!have_scales) {   // uniform; only before the first unit's scales
-                lds_wait_count(&counters[2], GR_PREP);
+                lds_wait_count(&counters[2], GR_PREP, &wait_failed);
                 have_scales = true;
             }
             const float gq = (float)gsum[pchunk * GROUPS_PER_CHUNK + gt];
@@ -375,7 +386,8 @@ __global__ __launch_bounds__(GR_THREADS, 1) void gemm_group_kernel(
 #pragma unroll
         for (int v = 0; v < GR_STREAM; ++v)
             y += red[(tl * GR_STREAM + v) * TILE_ROWS + i];
-        Y[t0 * TILE_ROWS + tid] = f2h(__builtin_ldexpf(y, -shs));
+        const bool failed = __hip_atomic_load(&wait_failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+        Y[t0 * TILE_ROWS + tid] = failed ? (uint16_t)0x7E00u : f2h(__builtin_ldexpf(y, -shs));
     }
 }
 

@@ -215,7 +215,10 @@ rbq_status rbq_rebinarize(const float *W, rbq_shape s, uint32_t *planes, const u
  *                   (may be NULL when that is 0); contents on return are
  *                   unspecified
  * Errors: RBQ_ERR_INVALID_ARG, RBQ_ERR_ALIGNMENT, RBQ_ERR_NO_DEVICE,
- * RBQ_ERR_HIP.
+ * RBQ_ERR_HIP.  The one- and few-token kernels coordinate their waves
+ * through bounded waits on LDS counters (the bound is never reached in a
+ * correct launch); should one run out, the workgroup writes fp16 NaN for
+ * all of its outputs instead of a value built on missing data.
  */
 rbq_status rbq_gemm(const uint32_t *planes, const uint16_t *scales, rbq_shape s,
                     const uint16_t *X, int32_t M, uint16_t *Y,
