@@ -66,7 +66,7 @@ class ProgramOp(ctypes.Structure):
     _fields_ = [("planes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("out_features", ctypes.c_int32), ("in_features", ctypes.c_int32),
                 ("epilogue", ctypes.c_uint32), ("wait_for", ctypes.c_int32), ("planes_layout", ctypes.c_uint32),
-                ("group_size", ctypes.c_int32)]
+                ("group_size", ctypes.c_int32), ("tokens", ctypes.c_int32)]
 
 
 _lib = None
@@ -587,8 +587,10 @@ class Program:
     ops: sequence of dicts with keys planes (int32 [K][out][in/32], or the
     tile layout [K][ceil(out/16)][ceil(in/512)][256] that pack_tiles
     writes), scales (fp16 [K][out]), x (fp16 [in]), y (fp16 [out], or [out/2]
-    with epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue and
-    wait_for (index of an earlier op whose y this op reads; -1 = none).
+    with epilogue=RBQ_EPILOGUE_SILU_MUL), and optionally epilogue,
+    wait_for (index of an earlier op whose y this op reads; -1 = none) and
+    tokens (2: x is [2][in] and y [2][out], each token quantised on its own;
+    every op of the program then has two tokens).
     g128 ops (group_size=128, every op of the program) take tiled planes,
     the scale tiles of pack_scale_tiles as scales, and out_features.  The tensors
     are kept referenced; the image is built on the host, copied to the
@@ -602,6 +604,8 @@ class Program:
         dev = None
         for i, o in enumerate(ops):
             p, s, x, y = o["planes"], o["scales"], o["x"], o["y"]
+            tok = int(o.get("tokens", 1))
+            nt = max(tok, 1)
             _dev(p, torch.int32, "planes")
             _dev(s, torch.float16, "scales")
             _dev(x, torch.float16, "x")
@@ -611,7 +615,7 @@ class Program:
                 if p.dim() != 4 or "out_features" not in o:
                     raise ValueError(f"op {i}: g128 ops take tiled planes and out_features")
                 layout = RBQ_LAYOUT_TILES
-                K, out_f, words = p.shape[0], int(o["out_features"]), x.numel() // 32
+                K, out_f, words = p.shape[0], int(o["out_features"]), x.numel() // (32 * nt)
                 if tuple(p.shape) != (K, (out_f + 15) // 16, (words * 32 + 511) // 512, 256) or \
                         tuple(s.shape) != (p.shape[1], p.shape[2], K * 64):
                     raise ValueError(f"op {i}: tiled planes or scale tiles do not match out_features and x")
@@ -620,7 +624,7 @@ class Program:
                 K = p.shape[0]
                 if s.dim() not in (2, 3) or s.shape[0] != K or s.numel() != K * s.shape[1]:
                     raise ValueError(f"op {i}: scales must be [K][out] (or [K][out][1]) with tiled planes")
-                out_f, words = s.shape[1], x.numel() // 32
+                out_f, words = s.shape[1], x.numel() // (32 * nt)
                 if tuple(p.shape) != (K, (out_f + 15) // 16, (words * 32 + 511) // 512, 256):
                     raise ValueError(f"op {i}: tiled planes do not match scales and x")
             else:
@@ -629,12 +633,12 @@ class Program:
             if K != num_planes:
                 raise ValueError(f"op {i}: {K} planes, the program has {num_planes}")
             ep = int(o.get("epilogue", RBQ_EPILOGUE_NONE))
-            if x.numel() != words * 32 or (not gs and s.numel() < K * out_f):
+            if x.numel() != nt * words * 32 or (not gs and s.numel() < K * out_f):
                 raise ValueError(f"op {i}: x or scales do not match the planes")
-            if y.numel() < (out_f // 2 if ep == RBQ_EPILOGUE_SILU_MUL else out_f):
+            if y.numel() < nt * (out_f // 2 if ep == RBQ_EPILOGUE_SILU_MUL else out_f):
                 raise ValueError(f"op {i}: y too small")
             arr[i] = ProgramOp(p.data_ptr(), s.data_ptr(), x.data_ptr(), y.data_ptr(), out_f, words * 32, ep,
-                               int(o.get("wait_for", -1)), layout, gs)
+                               int(o.get("wait_for", -1)), layout, gs, tok)
             self._keep += [p, s, x, y]
             dev = x.device
         n = len(ops)

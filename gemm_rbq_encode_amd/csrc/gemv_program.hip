@@ -66,8 +66,11 @@ constexpr int PG_PREP_THREADS = PG_PREP * RBQ_WAVE;
 constexpr int PG_STREAM = PG_WAVES - PG_PREP;              // stream waves
 constexpr int TILE_ROWS = 16;
 constexpr int CHUNK_WORDS = 16;                            // 512 columns
-constexpr int NC = 3;                                      // MFMA columns: the 3 limbs of one token
-constexpr int IMG_CHUNK = 8 * 4 * 16 * NC + 64;            // image bytes per chunk (+64: other banks)
+constexpr int NLIMB = 3;                                   // MFMA columns per token: its 3 limbs
+// image bytes per chunk for ops of mt tokens (3 mt MFMA columns; +64: other banks)
+__host__ __device__ constexpr int img_chunk_bytes(int mt) { return 8 * 4 * 16 * NLIMB * mt + 64; }
+constexpr int PG_MAX_XU2 = 3;                              // half-words per image thread and token, two-token ops
+constexpr int PG_MAX_IN2 = PG_MAX_XU2 * PG_PREP_THREADS * 16;   // 12288: widest input of two-token ops
 constexpr int PG_ROWS_PER_THREAD = 3;                      // rows of one op that an image thread finishes, at most
 constexpr int PG_MAX_TILES = PG_ROWS_PER_THREAD * PG_PREP_THREADS / TILE_ROWS;   // 48 tiles of one op per workgroup
 constexpr int PG_MAX_XU = 4;                               // half-words (16 columns) per image thread
@@ -136,20 +139,21 @@ constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups 
 constexpr int32_t PK_P_MASK = 15 << PK_P_SHIFT;
 constexpr int PK_T_SHIFT = 8;          // bits 8..15: tiles of an op per workgroup at most (the LDS slots' size)
 constexpr int32_t PK_T_MASK = 255 << PK_T_SHIFT;
+constexpr int32_t PK_PAIRS = 1 << 16;  // every op carries two tokens (x [2][in], y [2][out])
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
 // image arena what remains of the compute unit's LDS).  Programs of g128 ops
 // (GROUP) also keep the sum of q over every 128-column group of each x.
-template <int K, bool GROUP>
+template <int K, bool GROUP, int MT = 1>
 struct PgShared {
     int img_cnt;                              // image waves' publications: 4 per op
     int sdone[PG_SLOTS];                      // stream waves done with an op, by op slot (i % PG_SLOTS)
     int isync;                                // phases of the image waves' barrier
     int abort_flag;                           // a wait ran out: the rest runs without waiting
     int last_wg;                              // this workgroup is the last to finish the run
-    uint32_t wmax[PG_SLOTS][PG_PREP];
-    double wsum[PG_SLOTS][PG_PREP];                 // sums of q (exact: integers below 2^53)
-    int shs[PG_SLOTS];
+    uint32_t wmax[PG_SLOTS][MT][PG_PREP];
+    double wsum[PG_SLOTS][MT][PG_PREP];             // sums of q per token (exact: integers below 2^53)
+    int shs[PG_SLOTS][MT];
     uint16_t sc_lds[PG_SLOTS][GROUP ? 1 : K][PG_ROWS_PER_THREAD * PG_PREP_THREADS];   // scales of the rows finished
     int gsum[PG_SLOTS][GROUP ? PG_MAX_G : 1];         // g128: sum of q over each group (|sum| < 2^30)
 };
@@ -157,8 +161,8 @@ struct PgShared {
 // LDS ints per tile of an op slot of partial sums: per-row ops add int32
 // tile sums [tile][plane][limb][row]; g128 ops store fp32 [tile][stream
 // wave][row].  A program's slots hold its largest op's tiles per workgroup.
-__host__ __device__ constexpr int red_tile_ints(int K, bool group) {
-    return (group ? PG_STREAM : K * NC) * TILE_ROWS;
+__host__ __device__ constexpr int red_tile_ints(int K, bool group, int mt = 1) {
+    return (group ? PG_STREAM : K * NLIMB * mt) * TILE_ROWS;
 }
 
 // Op counters: each op's count of finished workgroups is split over
@@ -187,9 +191,10 @@ size_t program_lds_limit() {
 
 // Dynamic LDS a program may take: the limit less the kernel's fixed LDS
 // (and 256 bytes for its alignment).
-size_t program_dynamic_lds(int K, bool group) {
+size_t program_dynamic_lds(int K, bool group, int mt = 1) {
     const size_t fixed = group ? (K == 2 ? sizeof(PgShared<2, true>) : sizeof(PgShared<4, true>))
-                               : (K == 1 ? sizeof(PgShared<1, false>) : sizeof(PgShared<2, false>));
+                               : mt == 2 ? sizeof(PgShared<2, false, 2>)
+                                         : (K == 1 ? sizeof(PgShared<1, false>) : sizeof(PgShared<2, false>));
     return program_lds_limit() - fixed - 256;
 }
 
@@ -333,12 +338,18 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     return v;
 }
 
-template <int K, int RING, bool WAITS, bool TILES, bool GROUP>
+// MT: tokens per op (1, or 2 for programs of two-token per-row ops on the
+// tile layout without waits); the MFMA columns 3m .. 3m + 2 hold token m's limbs.
+template <int K, int RING, bool WAITS, bool TILES, bool GROUP, int MT = 1>
 __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
+    static_assert(MT == 1 || (MT == 2 && !GROUP && !WAITS && TILES), "two-token ops: per-row, tiled, no waits");
+    constexpr int NC = NLIMB * MT;                  // MFMA columns in use
+    constexpr int IMG_CHUNK = img_chunk_bytes(MT);
+    constexpr int XU = MT == 1 ? PG_MAX_XU : PG_MAX_XU2;
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ PgShared<K, GROUP> sh;
+    __shared__ PgShared<K, GROUP, MT> sh;
     int &img_cnt = sh.img_cnt;
     int *sdone = sh.sdone;
     int &isync = sh.isync;
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     // LDS: image arena, 16 zero bytes, partial sums [PG_SLOTS][max_tiles][K][NC][16]
     const int pad = hdr->arena_bytes;
     int *red0 = reinterpret_cast<int *>(lds + pad + 16);
-    constexpr int RED_TILE = red_tile_ints(K, GROUP);                        // ints per tile
+    constexpr int RED_TILE = red_tile_ints(K, GROUP, MT);                    // ints per tile
     const int RED_OP = ((hdr->kind & PK_T_MASK) >> PK_T_SHIFT) * RED_TILE;   // ints per op slot
 
     // A wait that runs out only raises the LDS flag (the status word is
@@ -437,7 +448,10 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                 break;
             const int row = t0 * TILE_ROWS + lr;
             const bool rowok = lr < ntl * TILE_ROWS && row < op.out;
-            float y = 0.0f;
+            float yv[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                yv[m] = 0.0f;
             if (GROUP && rowok) {
                 // the stream waves' per-(tile, wave) slots, added in wave order
                 const float *rf = reinterpret_cast<const float *>(red);
@@ -446,40 +460,52 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
 #pragma unroll
                 for (int w = 0; w < PG_STREAM; ++w)
                     acc += rf[(tl * PG_STREAM + w) * TILE_ROWS + i];
-                y = __builtin_ldexpf(acc, -shs[par]);
+                yv[0] = __builtin_ldexpf(acc, -shs[par][0]);
             } else if (rowok) {
-                double sx = 0.0;
-#pragma unroll
-                for (int v = 0; v < PG_PREP; ++v)
-                    sx += wsum[par][v];
                 const int tl = lr / TILE_ROWS, i = lr % TILE_ROWS;
 #pragma unroll
-                for (int k = 0; k < (GROUP ? 1 : K); ++k) {
-                    const int *rp = red + (tl * K + k) * NC * TILE_ROWS + i;
-                    const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
-                                     65536.0 * (double)rp[2 * TILE_ROWS];
-                    // one explicit fma per plane, as in the flat kernel
-                    y = __builtin_fmaf(h2f(sc_lds[par][k][lr]), (float)(t * (2.0 / 128.0) - sx), y);
+                for (int m = 0; m < MT; ++m) {
+                    double sx = 0.0;
+#pragma unroll
+                    for (int v = 0; v < PG_PREP; ++v)
+                        sx += wsum[par][m][v];
+                    float y = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < (GROUP ? 1 : K); ++k) {
+                        const int *rp = red + ((tl * K + k) * NC + NLIMB * m) * TILE_ROWS + i;
+                        const double t = (double)rp[0] + 256.0 * (double)rp[TILE_ROWS] +
+                                         65536.0 * (double)rp[2 * TILE_ROWS];
+                        // one explicit fma per plane, as in the flat kernel
+                        y = __builtin_fmaf(h2f(sc_lds[par][k][lr]), (float)(t * (2.0 / 128.0) - sx), y);
+                    }
+                    yv[m] = __builtin_ldexpf(y, -shs[par][m]);
                 }
-                y = __builtin_ldexpf(y, -shs[par]);
             }
-            if (op.flags & PF_SILU) {
-                // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
-                const float up = __shfl_down(y, 1, RBQ_WAVE);
-                if (rowok && (tid & 1) == 0) {
-                    const uint16_t h = silu_mul_f16(y, up);
-                    GLOBAL uint16_t *dst = op.y + row / 2;
+            // token m's outputs follow token m - 1's (y is [MT][out], or [MT][out / 2])
+            const bool silu = (op.flags & PF_SILU) != 0;
+            const int ycount = silu ? op.out / 2 : op.out;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float y = yv[m];
+                if (silu) {
+                    // (gate, up) rows 2i, 2i + 1 sit on neighbouring threads (tiles start at even rows)
+                    const float up = __shfl_down(y, 1, RBQ_WAVE);
+                    if (rowok && (tid & 1) == 0) {
+                        const uint16_t h = silu_mul_f16(y, up);
+                        GLOBAL uint16_t *dst = op.y + (size_t)m * ycount + row / 2;
+                        if (shared_y)
+                            __hip_atomic_store(dst, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *dst = h;
+                    }
+                } else if (rowok) {
+                    const uint16_t h = f2h(y);
+                    GLOBAL uint16_t *dst = op.y + (size_t)m * ycount + row;
                     if (shared_y)
                         __hip_atomic_store(dst, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     else
                         *dst = h;
                 }
-            } else if (rowok) {
-                const uint16_t h = f2h(y);
-                if (shared_y)
-                    __hip_atomic_store(op.y + row, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else
-                    op.y[row] = h;
             }
             }
             img_sync();   // every partial sum of the op has been read
@@ -525,32 +551,35 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
         // loads the last one, quantised with scale 0) and the scales of the row
         // the thread finishes.  x that an earlier op writes is loaded only after
         // the wait, with device-coherent loads.
-        v4u xw[PG_MAX_XU][2];
+        v4u xw[MT][XU][2];
         uint16_t a_bits[PG_ROWS_PER_THREAD][K];
         auto load_x = [&](const OpView &op) {
             const int nh = (op.in >> 5) * 2;
             const int xu = (op.nchunks * CHUNK_WORDS * 2 + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
             const bool shared_x = WAITS && (op.flags & PF_X_SHARED) != 0;
 #pragma unroll
-            for (int j = 0; j < PG_MAX_XU; ++j) {
-                xw[j][0] = xw[j][1] = (v4u){0u, 0u, 0u, 0u};
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < XU; ++j) {
+                v4u (&xwj)[2] = xw[m][j];
+                xwj[0] = xwj[1] = (v4u){0u, 0u, 0u, 0u};
                 if (j < xu) {
                     const int Hh = min(tid + j * PG_PREP_THREADS, nh - 1);
-                    GLOBAL const uint16_t *src = op.x + 16 * Hh;
+                    GLOBAL const uint16_t *src = op.x + (size_t)m * op.in + 16 * Hh;
                     if (shared_x) {
                         GLOBAL const uint64_t *p = reinterpret_cast<GLOBAL const uint64_t *>(src);
                         uint64_t q[4];
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
                             q[c] = __hip_atomic_load(p + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        xw[j][0] = (v4u){(uint32_t)q[0], (uint32_t)(q[0] >> 32), (uint32_t)q[1],
-                                         (uint32_t)(q[1] >> 32)};
-                        xw[j][1] = (v4u){(uint32_t)q[2], (uint32_t)(q[2] >> 32), (uint32_t)q[3],
-                                         (uint32_t)(q[3] >> 32)};
+                        xwj[0] = (v4u){(uint32_t)q[0], (uint32_t)(q[0] >> 32), (uint32_t)q[1],
+                                       (uint32_t)(q[1] >> 32)};
+                        xwj[1] = (v4u){(uint32_t)q[2], (uint32_t)(q[2] >> 32), (uint32_t)q[3],
+                                       (uint32_t)(q[3] >> 32)};
                     } else {
                         GLOBAL const v4u *xp = reinterpret_cast<GLOBAL const v4u *>(src);
-                        xw[j][0] = xp[0];
-                        xw[j][1] = xp[1];
+                        xwj[0] = xp[0];
+                        xwj[1] = xp[1];
                     }
                 }
             }
@@ -592,10 +621,13 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                     for (int k = 0; k < K; ++k)
                         sc_lds[par][k][tid + rr * PG_PREP_THREADS] = a_bits[rr][k];
             }
-            if (lane == 0)
-                wsum[par][wave] = wsum[prev][wave];
-            if (tid == 0)
-                shs[par] = shs[prev];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (lane == 0)
+                    wsum[par][m][wave] = wsum[prev][m][wave];
+                if (tid == 0)
+                    shs[par][m] = shs[prev][m];
+            }
             publish();
         };
 
@@ -605,18 +637,22 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
             const int nh = (op.in >> 5) * 2;                  // half-words of the row
             const int hpad = op.nchunks * CHUNK_WORDS * 2;    // with the padded words
             const int xu = (hpad + PG_PREP_THREADS - 1) / PG_PREP_THREADS;
-            // maximum of |x| (fp16 bits without the sign order like magnitudes)
-            v2u16 mx2 = (v2u16){0, 0};
+            // maximum of |x| per token (fp16 bits without the sign order like magnitudes)
 #pragma unroll
-            for (int j = 0; j < PG_MAX_XU; ++j)
+            for (int m = 0; m < MT; ++m) {
+                v2u16 mx2 = (v2u16){0, 0};
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int j = 0; j < XU; ++j)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, xw[j][h][c] & 0x7FFF7FFFu));
-            const uint32_t mw = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
-            if (lane == 0)
-                wmax[par][wave] = mw;
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            mx2 = __builtin_elementwise_max(mx2,
+                                                            __builtin_bit_cast(v2u16, xw[m][j][h][c] & 0x7FFF7FFFu));
+                const uint32_t mw = wave_max_u32_dpp(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+                if (lane == 0)
+                    wmax[par][m][wave] = mw;
+            }
             if (!GROUP) {
 #pragma unroll
                 for (int rr = 0; rr < PG_ROWS_PER_THREAD; ++rr)
@@ -625,65 +661,69 @@ __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
                         sc_lds[par][k][tid + rr * PG_PREP_THREADS] = a_bits[rr][k];
             }
             img_sync();
-            uint32_t mx = 0;
-#pragma unroll
-            for (int v = 0; v < PG_PREP; ++v)
-                mx = max(mx, wmax[par][v]);
-            // |x| < 2^E; q = round(x 2^sh), sh = 22 - E, |q| <= 2^22
-            const int e = (int)(mx >> 10);
-            const int sh = 22 - ((e == 0 ? 1 : e) - 14);
             // image entry (word w, bit s): the columns 32w + 8kk + s, kk = 0..3,
-            // at [chunk w/16][s][lane group (w/4)%4][limb][4 (w%4) + kk];
-            // fma(x, 2^sh, 1.5 2^23) leaves 2^22 + q in the mantissa, v = q +
-            // 0x808080 lies in [0, 2^24) and its bytes xor 0x80 are the limbs
+            // at [chunk w/16][s][lane group (w/4)%4][limb column][4 (w%4) + kk];
+            // token m's limbs are columns 3m .. 3m + 2.  fma(x, 2^sh, 1.5 2^23)
+            // leaves 2^22 + q in the mantissa, v = q + 0x808080 lies in
+            // [0, 2^24) and its bytes xor 0x80 are the limbs
             unsigned char *img = lds + op.img_off;
-            int psum = 0;
 #pragma unroll
-            for (int j = 0; j < PG_MAX_XU; ++j) {
-                const int H = tid + j * PG_PREP_THREADS;
-                if (GROUP)
-                    psum = 0;
-                if (j < xu && H < hpad) {
-                    const float scale = H < nh ? __builtin_ldexpf(1.0f, sh) : 0.0f;
-                    const int w = H >> 1, eh = H & 1;
-                    unsigned char *dst = img + (w / CHUNK_WORDS) * IMG_CHUNK + ((w >> 2) & 3) * (NC * 16) +
-                                         (w & 3) * 4 + 2 * eh;
+            for (int m = 0; m < MT; ++m) {
+                uint32_t mx = 0;
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const uint32_t u0 = xw[j][0][s >> 1], u1 = xw[j][1][s >> 1];
-                        const uint16_t h0 = (s & 1) ? (uint16_t)(u0 >> 16) : (uint16_t)u0;
-                        const uint16_t h1 = (s & 1) ? (uint16_t)(u1 >> 16) : (uint16_t)u1;
-                        const uint32_t v0 =
-                            __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) - 0x4ABF7F80u;
-                        const uint32_t v1 =
-                            __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) - 0x4ABF7F80u;
-                        psum += (int)(v0 + v1) - 2 * 0x808080;
-                        const uint32_t l01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u) ^ 0x80808080u;
-                        const uint32_t l2 = __builtin_amdgcn_perm(v1, v0, 0x0C0C0602u) ^ 0x8080u;
-                        unsigned char *d = dst + s * (4 * NC * 16);
-                        *reinterpret_cast<uint16_t *>(d) = (uint16_t)l01;
-                        *reinterpret_cast<uint16_t *>(d + 16) = (uint16_t)(l01 >> 16);
-                        *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
+                for (int v = 0; v < PG_PREP; ++v)
+                    mx = max(mx, wmax[par][m][v]);
+                // |x| < 2^E; q = round(x 2^sh), sh = 22 - E, |q| <= 2^22
+                const int e = (int)(mx >> 10);
+                const int sh = 22 - ((e == 0 ? 1 : e) - 14);
+                int psum = 0;
+#pragma unroll
+                for (int j = 0; j < XU; ++j) {
+                    const int H = tid + j * PG_PREP_THREADS;
+                    if (GROUP)
+                        psum = 0;
+                    if (j < xu && H < hpad) {
+                        const float scale = H < nh ? __builtin_ldexpf(1.0f, sh) : 0.0f;
+                        const int w = H >> 1, eh = H & 1;
+                        unsigned char *dst = img + (w / CHUNK_WORDS) * IMG_CHUNK + ((w >> 2) & 3) * (NC * 16) +
+                                             NLIMB * m * 16 + (w & 3) * 4 + 2 * eh;
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) {
+                            const uint32_t u0 = xw[m][j][0][s >> 1], u1 = xw[m][j][1][s >> 1];
+                            const uint16_t h0 = (s & 1) ? (uint16_t)(u0 >> 16) : (uint16_t)u0;
+                            const uint16_t h1 = (s & 1) ? (uint16_t)(u1 >> 16) : (uint16_t)u1;
+                            const uint32_t v0 =
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h0), scale, 12582912.0f)) - 0x4ABF7F80u;
+                            const uint32_t v1 =
+                                __builtin_bit_cast(uint32_t, __builtin_fmaf(h2f(h1), scale, 12582912.0f)) - 0x4ABF7F80u;
+                            psum += (int)(v0 + v1) - 2 * 0x808080;
+                            const uint32_t l01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u) ^ 0x80808080u;
+                            const uint32_t l2 = __builtin_amdgcn_perm(v1, v0, 0x0C0C0602u) ^ 0x8080u;
+                            unsigned char *d = dst + s * (4 * NC * 16);
+                            *reinterpret_cast<uint16_t *>(d) = (uint16_t)l01;
+                            *reinterpret_cast<uint16_t *>(d + 16) = (uint16_t)(l01 >> 16);
+                            *reinterpret_cast<uint16_t *>(d + 32) = (uint16_t)l2;
+                        }
+                    }
+                    if (GROUP && j < xu) {
+                        // the 8 half-words of a 128-column group sit in 8
+                        // consecutive lanes; lane 8m + 7 adds them
+                        int g = psum;
+                        g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(1)>(g);
+                        g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(2)>(g);
+                        g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(4)>(g);
+                        if ((lane & 7) == 7 && H < hpad)
+                            gsum[par][H >> 3] = g;
                     }
                 }
-                if (GROUP && j < xu) {
-                    // the 8 half-words of a 128-column group sit in 8
-                    // consecutive lanes; lane 8m + 7 adds them
-                    int g = psum;
-                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(1)>(g);
-                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(2)>(g);
-                    g = dpp_row_add_i32<RBQ_DPP_ROW_SHR(4)>(g);
-                    if ((lane & 7) == 7 && H < hpad)
-                        gsum[par][H >> 3] = g;
+                if (!GROUP) {
+                    const double ws = wave_sum_f64_dpp((double)psum);   // sum of q over the wave's columns (exact)
+                    if (lane == 0)
+                        wsum[par][m][wave] = ws;
                 }
+                if (tid == 0)
+                    shs[par][m] = sh;
             }
-            if (!GROUP) {
-                const double ws = wave_sum_f64_dpp((double)psum);   // sum of q over the wave's columns (exact)
-                if (lane == 0)
-                    wsum[par][wave] = ws;
-            }
-            if (tid == 0)
-                shs[par] = sh;
             publish();
         };
 
@@ -1093,6 +1133,16 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     const bool group = ops[0].group_size == 128;
     if (group ? (K != 2 && K != 4) : K > 2)
         return RBQ_ERR_UNSUPPORTED;
+    // tokens per op: 0 and 1 both mean one; two-token ops are per-row K = 2
+    // ops on the tile layout in programs without waits, every op of the
+    // program with two tokens
+    if (ops[0].tokens < 0)
+        return RBQ_ERR_INVALID_ARG;
+    const int tok = ops[0].tokens <= 1 ? 1 : ops[0].tokens;
+    if (tok > 2)
+        return RBQ_ERR_UNSUPPORTED;
+    if (tok == 2 && (group || K != 2))
+        return RBQ_ERR_UNSUPPORTED;
     const int G = program_num_cus();
     if (G > 4095)   // the tile split keeps tiles % G in 12 bits
         return RBQ_ERR_UNSUPPORTED;
@@ -1105,6 +1155,10 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         const rbq_program_op &o = ops[i];
         if (o.planes == nullptr || o.scales == nullptr || o.x == nullptr || o.y == nullptr)
             return RBQ_ERR_INVALID_ARG;
+        if (o.tokens < 0 || (o.tokens <= 1 ? 1 : o.tokens) != tok)
+            return RBQ_ERR_INVALID_ARG;
+        if (tok == 2 && (o.planes_layout != RBQ_LAYOUT_TILES || o.wait_for >= 0 || o.in_features > PG_MAX_IN2))
+            return RBQ_ERR_UNSUPPORTED;
         if (o.out_features < 1 || o.in_features < 1 || o.in_features % 32 != 0)
             return RBQ_ERR_INVALID_ARG;
         if (o.epilogue != RBQ_EPILOGUE_NONE && o.epilogue != RBQ_EPILOGUE_SILU_MUL)
@@ -1124,8 +1178,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             return RBQ_ERR_UNSUPPORTED;
         if (!al(o.planes, 16) || !al(o.x, 16) || !al(o.scales, group ? 16 : 2) || !al(o.y, 2))
             return RBQ_ERR_ALIGNMENT;
-        xb[i] = (size_t)o.in_features * 2;
-        yb[i] = (size_t)(o.epilogue == RBQ_EPILOGUE_SILU_MUL ? o.out_features / 2 : o.out_features) * 2;
+        xb[i] = (size_t)tok * o.in_features * 2;
+        yb[i] = (size_t)tok * (o.epilogue == RBQ_EPILOGUE_SILU_MUL ? o.out_features / 2 : o.out_features) * 2;
         pb[i] = o.planes_layout == RBQ_LAYOUT_TILES ? tiles_bytes(K, o.out_features, o.in_features)
                                                     : (size_t)K * o.out_features * (o.in_features / 32) * 4;
         sb[i] = group ? scale_tiles_bytes(K, o.out_features, o.in_features) : (size_t)K * o.out_features * 2;
@@ -1171,10 +1225,10 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     int32_t *wu = reinterpret_cast<int32_t *>(d + n_ops);
     int max_img = 0;
     for (int i = 0; i < n_ops; ++i)
-        max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * IMG_CHUNK);
-    const size_t budget = program_dynamic_lds(K, group);
+        max_img = std::max(max_img, ((ops[i].in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS) * img_chunk_bytes(tok));
+    const size_t budget = program_dynamic_lds(K, group, tok);
     // LDS the partial sums take when each workgroup gets up to mt tiles of an op
-    auto fixed_lds = [&](int mt) { return 16 + (size_t)PG_SLOTS * mt * red_tile_ints(K, group) * 4; };
+    auto fixed_lds = [&](int mt) { return 16 + (size_t)PG_SLOTS * mt * red_tile_ints(K, group, tok) * 4; };
     auto max_tiles_of = [&](int gl) {
         int mt = 1;
         for (int i = 0; i < n_ops; ++i)
@@ -1278,7 +1332,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             off = g.prev_off;
             g.live.back().op = i;   // the image is in use until this op
         } else {
-            const int size = nch * IMG_CHUNK;
+            const int size = nch * img_chunk_bytes(tok);
             off = g.next_off + size <= arena ? g.next_off : 0;
             for (const Placed &q : g.live)
                 if (q.lo < off + size && off < q.hi)
@@ -1318,7 +1372,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->grid = G;
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
-    h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT) | (max_tiles << PK_T_SHIFT);
+    h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT) | (max_tiles << PK_T_SHIFT) |
+              (tok == 2 ? PK_PAIRS : 0);
     for (int i = 0; i < n_ops; ++i) {
         h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
         h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
@@ -1334,7 +1389,8 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
 rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
-        h->grid != program_num_cus() || (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK | PK_T_MASK)) != 0)
+        h->grid != program_num_cus() ||
+        (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK | PK_T_MASK | PK_PAIRS)) != 0)
         return RBQ_ERR_INVALID_ARG;
     const int mt = (h->kind & PK_T_MASK) >> PK_T_SHIFT;
     if (mt < 1 || mt > PG_MAX_TILES)
@@ -1345,10 +1401,13 @@ rbq_status program_check(const void *image) {
     const bool group = (h->kind & PK_GROUP) != 0;
     if (group ? (h->K != 2 && h->K != 4) || !(h->kind & PK_TILES) : (h->K != 1 && h->K != 2))
         return RBQ_ERR_INVALID_ARG;
+    const bool pairs = (h->kind & PK_PAIRS) != 0;
+    if (pairs && (group || h->K != 2 || !(h->kind & PK_TILES) || (h->kind & PK_WAITS)))
+        return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
     // never launch a layout that would not fit the compute unit's LDS
-    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K, group))
+    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K, group, pairs ? 2 : 1))
         return RBQ_ERR_UNSUPPORTED;
     return RBQ_OK;
 }
@@ -1378,7 +1437,10 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
         RBQ_LAUNCH_PROGRAM(KK, true, true, true);                        \
     else                                                                 \
         RBQ_LAUNCH_PROGRAM(KK, false, true, true)
-    if (h->kind & PK_GROUP) {
+    if (h->kind & PK_PAIRS) {
+        hipLaunchKernelGGL((gemv_program_kernel<2, RBQ_PROGRAM_RING, false, true, false, 2>), dim3(h->grid),
+                           dim3(PG_THREADS), h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
+    } else if (h->kind & PK_GROUP) {
         if (h->K == 2) {
             RBQ_LAUNCH_GROUP_K(2);
         } else {

@@ -340,3 +340,81 @@ def test_batch_tokens_as_ops_on_shared_planes(M):
             assert torch.equal(Y[m].view(torch.int16), ref.view(torch.int16)), f"linear {i} token {m}"
         yb = rbq.gemm(pt, st, xd, 0)
         assert_close(Y.cpu().numpy(), yb.cpu().numpy(), f"linear {i} against rbq_gemm at {M} tokens")
+
+
+def two_token_program(shapes, seed):
+    """Ops of two tokens (x [2][in], y [2][out] or [2][out / 2]) on tiled planes."""
+    host, ops, outs = [], [], []
+    for i, (o, n, epi) in enumerate(shapes):
+        p, s = layer(o, n, 2, seed=seed + i)
+        if epi:
+            p, s = interleave_gate_up(p, s)
+        pt, st = to_dev(p, s)
+        X = workloads.gaussian_activations(2, n, seed=seed + 50 + i)
+        xd = torch.from_numpy(X.view(np.float16)).to(dev())
+        y = torch.full((2, o // 2 if epi else o), float("nan"), dtype=torch.float16, device=dev())
+        ops.append({"planes": rbq.pack_tiles(pt), "scales": st, "x": xd, "y": y, "epilogue": epi, "tokens": 2})
+        host.append((p, s, pt, st, X, xd, epi))
+        outs.append(y)
+    return host, ops, outs
+
+
+def one_token_program(pt, st, x, epi):
+    """the same op on one token, as a one-op program on the tile layout"""
+    y = torch.full((pt.shape[1] // 2 if epi else pt.shape[1],), float("nan"), dtype=torch.float16, device=dev())
+    rbq.Program([{"planes": rbq.pack_tiles(pt), "scales": st, "x": x, "y": y, "epilogue": epi}], num_planes=2).run()
+    torch.cuda.synchronize()
+    return y
+
+
+def check_two_token_outputs(host, outs, shapes, against_flat=False):
+    for i, ((p, s, pt, st, X, xd, epi), y) in enumerate(zip(host, outs)):
+        yr = oracle.gemm(p, s, X)
+        if epi:
+            yr = oracle.silu_mul(yr)
+        for m in range(2):
+            what = f"op {i} {shapes[i]} token {m}"
+            assert_close(y[m].cpu().numpy(), yr[m], what)
+            ref = eager_flat(pt, st, xd[m], epilogue=epi) if against_flat else one_token_program(pt, st, xd[m], epi)
+            assert torch.equal(y[m].view(torch.int16), ref.view(torch.int16)), f"{what}: not the one-token result"
+
+
+def test_two_token_ops_llama2_7b_shapes():
+    """The fused Llama-2-7B decode shapes with two tokens per op (gate/up with
+    the SiLU-mul epilogue): each token's output equals rbq_gemv's on that
+    token bit for bit, and the run leaves the counters clear for the next."""
+    shapes = [(12288, 4096, 0), (4096, 4096, 0), (22016, 4096, 1), (4096, 11008, 0)] * 2
+    host, ops, outs = two_token_program(shapes, seed=500)
+    prog = rbq.Program(ops, num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert not prog.counters.any()
+    check_two_token_outputs(host, outs, shapes, against_flat=True)
+    first = [y.clone() for y in outs]
+    for y in outs:
+        y.fill_(float("nan"))
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for a, b in zip(first, outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_two_token_ops_ragged():
+    """Rows not a multiple of 16, inputs not a multiple of 512 (padded tile
+    units), the widest two-token input (12288 columns), few tiles, and
+    consecutive ops on the same x (the image is built once)."""
+    shapes = [(1, 128, 0), (17, 384, 0), (300, 12288, 0), (4100, 640, 0), (34, 512, 1), (4098, 2048, 1),
+              (23, 1152, 0), (999, 1152, 0)]
+    host, ops, outs = two_token_program(shapes, seed=700)
+    # op 7 reads op 6's x
+    ops[7]["x"] = ops[6]["x"]
+    host[7] = host[7][:4] + host[6][4:6] + host[7][6:]
+    prog = rbq.Program(ops, num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_two_token_outputs(host, outs, shapes)

@@ -10,8 +10,8 @@ import gemm_rbq_encode_amd as rbq
 MiB = 1 << 20
 
 
-def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1, layout=0, group=0):
-    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for, layout, group)
+def op(planes, scales, x, y, out=256, inf=512, epilogue=0, wait_for=-1, layout=0, group=0, tokens=0):
+    return rbq.ProgramOp(planes, scales, x, y, out, inf, epilogue, wait_for, layout, group, tokens)
 
 
 def build(ops, K=2, nbytes=None):
@@ -173,3 +173,38 @@ def test_scale_tiles_bytes_and_pack_arguments():
     assert L.rbq_pack_scale_tiles(W(0) + 1, s, W(4), None) == rbq.RBQ_ERR_ALIGNMENT
     assert L.rbq_pack_scale_tiles(W(0), s, W(4) + 8, None) == rbq.RBQ_ERR_ALIGNMENT
     assert L.rbq_pack_scale_tiles(W(0), s, W(0) + 16, None) == rbq.RBQ_ERR_INVALID_ARG        # overlap
+
+
+def pop(planes, scales, x, y, out=256, inf=512, **kw):
+    """a two-token op on the tile layout"""
+    kw.setdefault("tokens", 2)
+    return op(planes, scales, x, y, out, inf, layout=rbq.RBQ_LAYOUT_TILES, **kw)
+
+
+def test_two_token_programs():
+    """Two-token ops: K = 2, per-row scales, tile layout, no waits, in <=
+    12288, every op of the program with two tokens; x and y hold two rows,
+    which the overlap checks count."""
+    many = [pop(W(2 * i), W(2 * i + 1), A(0), A(1 + i), out=4096 + 16 * i, inf=4096) for i in range(64)]
+    assert build(many) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(1), out=4096, inf=11008)]) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(1), out=4096, inf=12288)]) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(1), out=4096, inf=12416)]) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([pop(W(0), W(1), A(0), A(1), epilogue=rbq.RBQ_EPILOGUE_SILU_MUL)]) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(1))], K=1) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([op(W(0), W(1), A(0), A(1), tokens=2)]) == rbq.RBQ_ERR_UNSUPPORTED            # row layout
+    assert build([pop(W(0), W(1), A(0), A(1)), pop(W(2), W(3), A(1), A(2), wait_for=0)]) == \
+        rbq.RBQ_ERR_UNSUPPORTED                                                                   # a wait
+    assert build([pop(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2), layout=rbq.RBQ_LAYOUT_TILES)]) == \
+        rbq.RBQ_ERR_INVALID_ARG                                                                   # mixed counts
+    assert build([pop(W(0), W(1), A(0), A(1), tokens=3)]) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([pop(W(0), W(1), A(0), A(1), tokens=-1)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([op(W(0), W(1), A(0), A(1), layout=rbq.RBQ_LAYOUT_TILES, tokens=1),
+                  op(W(2), W(3), A(0), A(2), layout=rbq.RBQ_LAYOUT_TILES, tokens=0)]) == rbq.RBQ_OK
+    assert build([gop(W(0), W(1), A(0), A(1), tokens=2)], K=4) == rbq.RBQ_ERR_UNSUPPORTED
+    # x of 2 x 512 fp16 = 2048 bytes: a y 1024 bytes in overlaps only the second token's row
+    assert build([op(W(0), W(1), A(0), A(0) + 1024, layout=rbq.RBQ_LAYOUT_TILES)]) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(0) + 1024)]) == rbq.RBQ_ERR_INVALID_ARG
+    # y of 2 x 256 fp16 = 1024 bytes: a second op's y 600 bytes on overlaps it
+    assert build([pop(W(0), W(1), A(0), A(1)), pop(W(2), W(3), A(0), A(1) + 600)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([pop(W(0), W(1), A(0), A(1)), pop(W(2), W(3), A(0), A(1) + 1024)]) == rbq.RBQ_OK
