@@ -408,18 +408,21 @@ def group_program_step(args, torch, rbq, workloads, dev, n_layers=40, cpu_second
 def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
     """The Llama-2-7B decode step for a batch of M tokens (K = 2, fused
     layout, args.layers layers with their own weights, planes in the tile
-    layout) as ONE program launch.  Two forms of the same arithmetic (each
+    layout) as program launches, in three forms of the same arithmetic (each
     token quantised on its own, as in rbq_gemm):
-      * two-token ops (M even): one op per (linear, pair of tokens), the
-        pair's limbs in 6 of the 16 MFMA columns, so a unit of planes feeds
-        two tokens for the same MFMAs -- the reported value;
-      * one-token ops: one op per (linear, token) on shared planes.
+      * four- and two-token ops (M a multiple of 4): q/k/v, o and gate/up
+        (4096 inputs) as ops of four tokens, whose limbs fill 12 of the 16
+        MFMA columns, so a unit of planes feeds four tokens for the same
+        MFMAs; down (11008 inputs, too wide for a four-token image) as ops of
+        two tokens in a second launch -- the reported value;
+      * two-token ops (M even), one launch;
+      * one-token ops on shared planes, one launch.
     The ops of a linear run one after another, so its planes come from HBM
-    once and from the caches otherwise.  Reports whole-job GB/s of
+    once and from the caches otherwise.  A form whose launches would exceed
+    RBQ_PROGRAM_MAX_OPS ops is left out.  Reports whole-job GB/s of
     algorithmic bytes (planes and scales once, M tokens of x and y), the
-    launch time from HIP events, and layer 0 against rbq_gemm at M tokens.
-    Returns the JSON object, or None when no form fits the program limit
-    (RBQ_PROGRAM_MAX_OPS)."""
+    step's launch time from HIP events, and layer 0 against rbq_gemm at M
+    tokens.  Returns the JSON object, or None when no form fits."""
     wl = workloads.WORKLOADS["llama2_7b_skinny"]
     K, group = wl.num_planes, wl.group_size
     n_layers = args.layers
@@ -433,17 +436,32 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
     per_lin = [gemv_bytes(sh.out_features, sh.in_features, K, 1, M) for sh in shapes]
     nbytes = sum(per_lin) * n_layers
     stream = torch.cuda.current_stream(dev)
+    narrow = [i for i, sh in enumerate(shapes) if sh.in_features <= 4096]
+    wide = [i for i in range(len(shapes)) if i not in narrow]
+    candidates = []
+    if M % 4 == 0:
+        candidates.append(("4_and_2_token_ops", [(narrow, 4), (wide, 2)]))
+    if M % 2 == 0:
+        candidates.append(("2_token_ops", [(list(range(len(shapes))), 2)]))
+    candidates.append(("1_token_ops", [(list(range(len(shapes))), 1)]))
     forms = {}
-    for tok in ((2, 1) if M % 2 == 0 else (1,)):
-        if n_layers * len(shapes) * (M // tok) > rbq.RBQ_PROGRAM_MAX_OPS:
+    for name, parts in candidates:
+        if any(n_layers * len(lins) * (M // tok) > rbq.RBQ_PROGRAM_MAX_OPS for lins, tok in parts if lins):
             continue
         ys = [[torch.empty((M, sh.out_features), dtype=torch.float16, device=dev) for sh in shapes]
               for _ in range(n_layers)]
-        ops = [{"planes": tiles[l][i], "scales": layers[l][i][1], "x": xs[l][i][m:m + tok], "y": ys[l][i][m:m + tok],
-                "tokens": tok} for l in range(n_layers) for i in range(len(shapes)) for m in range(0, M, tok)]
-        prog = rbq.Program(ops, num_planes=K)
+        progs = []
+        for lins, tok in parts:
+            if lins:
+                progs.append(rbq.Program([{"planes": tiles[l][i], "scales": layers[l][i][1], "x": xs[l][i][m:m + tok],
+                                           "y": ys[l][i][m:m + tok], "tokens": tok}
+                                          for l in range(n_layers) for i in lins for m in range(0, M, tok)],
+                                         num_planes=K))
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-        run = (lambda prog=prog, status=status: prog.run(status))
+
+        def run(progs=progs, status=status):
+            for pr in progs:
+                pr.run(status)
         settle(torch, run)
         us = event_launch_us(torch, run, stream, max(args.steps, 20))
         for _ in range(args.warmup):
@@ -461,29 +479,31 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
             ref = rbq.gemm(p, sc, xs[0][i], group)
             diff = max(diff, float((ys[0][i].float() - ref.float()).abs().max() /
                                    ref.float().abs().max().clamp_min(1e-30)))
-        forms[tok] = {"ops": len(ops), "ms_per_step": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                      "mean_launch_us": round(us, 2), "layer0_max_rel_diff_vs_rbq_gemm": diff}
-        del prog, ops, ys
+        forms[name] = {"launches": len(progs), "ops": [pr.n_ops for pr in progs],
+                       "tokens_per_op": {shapes[i].in_features: tok for lins, tok in parts for i in lins},
+                       "ms_per_step": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "mean_step_launch_us": round(us, 2), "layer0_max_rel_diff_vs_rbq_gemm": diff}
+        del progs, ys
     if not forms:
         return None
-    tok = max(forms)
-    f = forms[tok]
-    line = {"metric": f"K={K} batch-{M} GEMM effective GB/s on Llama-2-7B layers, decode step as one program",
+    name = next(n for n, _ in candidates if n in forms)
+    f = forms[name]
+    line = {"metric": f"K={K} batch-{M} GEMM effective GB/s on Llama-2-7B layers, decode step as program launches",
             "value": round(nbytes / (f["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": f["ms_per_step"], "dtype": DTYPE_INT8_LIMBS,
             "config": {"workload": f"llama2_7b_skinny_m{M}_decode_program", "layers": n_layers, "layout": "fused",
-                       "ops_per_layer": {name: f"{sh.out_features}x{sh.in_features}"
-                                         for (name, _), sh in zip(groups, shapes)},
-                       "num_planes": K, "group_size": group, "tokens": M, "tokens_per_op": tok, "ops": f["ops"],
-                       "bytes_per_step": nbytes, "planes_layout": "tiles (rbq_pack_tiles)",
-                       "ops_of_a_linear": f"{M // tok} ops of {tok} token(s) on the same planes, one after another"},
-            "roofline": {"bound": "hbm", "achieved": round(nbytes / (f["mean_launch_us"] * 1e-6) / 1e9, 1),
+                       "ops_per_layer": {name_: f"{sh.out_features}x{sh.in_features}"
+                                         for (name_, _), sh in zip(groups, shapes)},
+                       "num_planes": K, "group_size": group, "tokens": M, "form": name,
+                       "launches_per_step": f["launches"], "ops": f["ops"], "bytes_per_step": nbytes,
+                       "planes_layout": "tiles (rbq_pack_tiles)"},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (f["mean_step_launch_us"] * 1e-6) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(nbytes / (f["mean_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "kernel": f"gemv_program_kernel<{K}> ({f['ops']} ops of {tok} token(s))",
-                         "bytes_per_launch": nbytes, "mean_launch_us": f["mean_launch_us"]},
+                         "frac": round(nbytes / (f["mean_step_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None, "kernel": f"gemv_program_kernel<{K}> ({name})",
+                         "bytes_per_launch": nbytes, "mean_launch_us": f["mean_step_launch_us"]},
             "layer0_max_rel_diff_vs_rbq_gemm": f["layer0_max_rel_diff_vs_rbq_gemm"],
-            "forms": {f"{t}_token_ops": v for t, v in forms.items()}, "cpu_baseline": None}
+            "forms": forms, "cpu_baseline": None}
     if cpu_seconds > 0:
         samples = [(p.cpu().numpy().view(np.uint32), sc.cpu().numpy().view(np.uint16),
                     xs[0][i].cpu().numpy().view(np.uint16), group, per_lin[i])
@@ -1220,9 +1240,10 @@ def bench_decode(args):
     if not args.no_extra:
         others["llama2_13b_g128_program"] = group_program_step(args, torch, rbq, workloads, dev,
                                                                cpu_seconds=min(args.cpu_seconds, 4.0))
-        m4 = skinny_program_step(args, torch, rbq, workloads, dev, 4, cpu_seconds=min(args.cpu_seconds, 4.0))
-        if m4 is not None:
-            others["llama2_7b_skinny_m4_program"] = m4
+        for mb in (4, 16):
+            sk = skinny_program_step(args, torch, rbq, workloads, dev, mb, cpu_seconds=min(args.cpu_seconds, 4.0))
+            if sk is not None:
+                others[f"llama2_7b_skinny_m{mb}_program"] = sk
 
     qat = None if args.no_extra else bench_qat(torch, rbq, workloads, dev)
 

@@ -69,11 +69,14 @@ constexpr int CHUNK_WORDS = 16;                            // 512 columns
 constexpr int NLIMB = 3;                                   // MFMA columns per token: its 3 limbs
 // image bytes per chunk for ops of mt tokens (3 mt MFMA columns; +64: other banks)
 __host__ __device__ constexpr int img_chunk_bytes(int mt) { return 8 * 4 * 16 * NLIMB * mt + 64; }
-constexpr int PG_MAX_XU2 = 3;                              // half-words per image thread and token, two-token ops
-constexpr int PG_MAX_IN2 = PG_MAX_XU2 * PG_PREP_THREADS * 16;   // 12288: widest input of two-token ops
 constexpr int PG_ROWS_PER_THREAD = 3;                      // rows of one op that an image thread finishes, at most
 constexpr int PG_MAX_TILES = PG_ROWS_PER_THREAD * PG_PREP_THREADS / TILE_ROWS;   // 48 tiles of one op per workgroup
 constexpr int PG_MAX_XU = 4;                               // half-words (16 columns) per image thread
+// half-words (16 columns) per image thread and token for ops of mt tokens;
+// the widest input of such ops is that times 256 threads times 16 columns:
+// 16384 (one token), 12288 (two), 4096 (four)
+__host__ __device__ constexpr int max_xu(int mt) { return mt == 1 ? PG_MAX_XU : mt == 2 ? 3 : 1; }
+__host__ __device__ constexpr int max_in_of(int mt) { return max_xu(mt) * PG_PREP_THREADS * 16; }
 constexpr int PG_MAX_CHUNKS = PG_MAX_XU * PG_PREP_THREADS / (2 * CHUNK_WORDS);   // 32: in <= 16384
 constexpr uint64_t PG_WAIT_TICKS = 20000000;               // bound of every wait: 0.2 s of the
                                                            // 100 MHz real-time clock (never reached)
@@ -139,7 +142,8 @@ constexpr int PK_P_SHIFT = 4;          // bits 4..7: P, the number of op groups 
 constexpr int32_t PK_P_MASK = 15 << PK_P_SHIFT;
 constexpr int PK_T_SHIFT = 8;          // bits 8..15: tiles of an op per workgroup at most (the LDS slots' size)
 constexpr int32_t PK_T_MASK = 255 << PK_T_SHIFT;
-constexpr int32_t PK_PAIRS = 1 << 16;  // every op carries two tokens (x [2][in], y [2][out])
+constexpr int PK_MT_SHIFT = 16;        // bits 16..17: log2 of the tokens every op carries (1, 2 or 4)
+constexpr int32_t PK_MT_MASK = 3 << PK_MT_SHIFT;
 
 // The kernel's fixed LDS (its size is known to the host, which gives the
 // image arena what remains of the compute unit's LDS).  Programs of g128 ops
@@ -193,6 +197,7 @@ size_t program_lds_limit() {
 // (and 256 bytes for its alignment).
 size_t program_dynamic_lds(int K, bool group, int mt = 1) {
     const size_t fixed = group ? (K == 2 ? sizeof(PgShared<2, true>) : sizeof(PgShared<4, true>))
+                               : mt == 4 ? sizeof(PgShared<2, false, 4>)
                                : mt == 2 ? sizeof(PgShared<2, false, 2>)
                                          : (K == 1 ? sizeof(PgShared<1, false>) : sizeof(PgShared<2, false>));
     return program_lds_limit() - fixed - 256;
@@ -338,16 +343,18 @@ __device__ __forceinline__ OpView op_view(const ProgOp *table, int i) {
     return v;
 }
 
-// MT: tokens per op (1, or 2 for programs of two-token per-row ops on the
-// tile layout without waits); the MFMA columns 3m .. 3m + 2 hold token m's limbs.
+// MT: tokens per op (1, or 2 or 4 for programs of several-token per-row ops
+// on the tile layout without waits); the MFMA columns 3m .. 3m + 2 hold
+// token m's limbs (12 of the 16 columns with four tokens).
 template <int K, int RING, bool WAITS, bool TILES, bool GROUP, int MT = 1>
 __global__ __launch_bounds__(PG_THREADS, 1) void gemv_program_kernel(
     const ProgHeader *__restrict__ hdr, int n_ops, uint32_t checksum, int *__restrict__ counters,
     int32_t *__restrict__ status) {
-    static_assert(MT == 1 || (MT == 2 && !GROUP && !WAITS && TILES), "two-token ops: per-row, tiled, no waits");
+    static_assert(MT == 1 || ((MT == 2 || MT == 4) && !GROUP && !WAITS && TILES),
+                  "several-token ops: per-row, tiled, no waits");
     constexpr int NC = NLIMB * MT;                  // MFMA columns in use
     constexpr int IMG_CHUNK = img_chunk_bytes(MT);
-    constexpr int XU = MT == 1 ? PG_MAX_XU : PG_MAX_XU2;
+    constexpr int XU = max_xu(MT);
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ PgShared<K, GROUP, MT> sh;
     int &img_cnt = sh.img_cnt;
@@ -1133,15 +1140,15 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     const bool group = ops[0].group_size == 128;
     if (group ? (K != 2 && K != 4) : K > 2)
         return RBQ_ERR_UNSUPPORTED;
-    // tokens per op: 0 and 1 both mean one; two-token ops are per-row K = 2
-    // ops on the tile layout in programs without waits, every op of the
-    // program with two tokens
+    // tokens per op: 0 and 1 both mean one; ops of 2 or 4 tokens are per-row
+    // K = 2 ops on the tile layout in programs without waits, every op of
+    // the program with the same count
     if (ops[0].tokens < 0)
         return RBQ_ERR_INVALID_ARG;
     const int tok = ops[0].tokens <= 1 ? 1 : ops[0].tokens;
-    if (tok > 2)
+    if (tok != 1 && tok != 2 && tok != 4)
         return RBQ_ERR_UNSUPPORTED;
-    if (tok == 2 && (group || K != 2))
+    if (tok > 1 && (group || K != 2))
         return RBQ_ERR_UNSUPPORTED;
     const int G = program_num_cus();
     if (G > 4095)   // the tile split keeps tiles % G in 12 bits
@@ -1157,7 +1164,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
             return RBQ_ERR_INVALID_ARG;
         if (o.tokens < 0 || (o.tokens <= 1 ? 1 : o.tokens) != tok)
             return RBQ_ERR_INVALID_ARG;
-        if (tok == 2 && (o.planes_layout != RBQ_LAYOUT_TILES || o.wait_for >= 0 || o.in_features > PG_MAX_IN2))
+        if (tok > 1 && (o.planes_layout != RBQ_LAYOUT_TILES || o.wait_for >= 0 || o.in_features > max_in_of(tok)))
             return RBQ_ERR_UNSUPPORTED;
         if (o.out_features < 1 || o.in_features < 1 || o.in_features % 32 != 0)
             return RBQ_ERR_INVALID_ARG;
@@ -1249,13 +1256,21 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         bool waits = false;
         for (int i = 0; i < n_ops; ++i)
             waits |= ops[i].wait_for >= 0;
+        // (ops of several tokens: the most groups that leave room for two of
+        // the largest images, so that the next op's image is built while an
+        // op streams; failing that, the most that fit one)
+        auto fits = [&](int cand, int images) {
+            return !waits && n_ops >= cand && G % cand == 0 && max_tiles_of(G / cand) <= PG_MAX_TILES &&
+                   fixed_lds(max_tiles_of(G / cand)) + (size_t)images * max_img <= budget;
+        };
         int cand = RBQ_PROGRAM_GROUPS;
-        while (cand > 1) {
-            const bool fits = !waits && n_ops >= cand && G % cand == 0 && max_tiles_of(G / cand) <= PG_MAX_TILES &&
-                              fixed_lds(max_tiles_of(G / cand)) + (size_t)max_img <= budget;
-            if (fits)
-                break;
-            cand /= 2;
+        if (tok > 1)
+            while (cand > 1 && !fits(cand, 2))
+                cand /= 2;
+        if (tok == 1 || !fits(cand, 2)) {
+            cand = RBQ_PROGRAM_GROUPS;
+            while (cand > 1 && !fits(cand, 1))
+                cand /= 2;
         }
         P = cand;
     }
@@ -1373,7 +1388,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
     h->lds_bytes = (uint32_t)lds;
     h->arena_bytes = arena;
     h->kind = PK_TILES | (group ? PK_GROUP : 0) | (P << PK_P_SHIFT) | (max_tiles << PK_T_SHIFT) |
-              (tok == 2 ? PK_PAIRS : 0);
+              ((tok == 4 ? 2 : tok == 2 ? 1 : 0) << PK_MT_SHIFT);
     for (int i = 0; i < n_ops; ++i) {
         h->kind |= ops[i].wait_for >= 0 ? PK_WAITS : 0;
         h->kind &= ops[i].planes_layout == RBQ_LAYOUT_TILES ? ~0 : ~PK_TILES;
@@ -1390,7 +1405,7 @@ rbq_status program_check(const void *image) {
     const ProgHeader *h = static_cast<const ProgHeader *>(image);
     if (h == nullptr || h->magic != PG_MAGIC || h->n_ops < 1 || h->n_ops > RBQ_PROGRAM_MAX_OPS ||
         h->grid != program_num_cus() ||
-        (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK | PK_T_MASK | PK_PAIRS)) != 0)
+        (h->kind & ~(PK_WAITS | PK_TILES | PK_GROUP | PK_P_MASK | PK_T_MASK | PK_MT_MASK)) != 0)
         return RBQ_ERR_INVALID_ARG;
     const int mt = (h->kind & PK_T_MASK) >> PK_T_SHIFT;
     if (mt < 1 || mt > PG_MAX_TILES)
@@ -1401,13 +1416,13 @@ rbq_status program_check(const void *image) {
     const bool group = (h->kind & PK_GROUP) != 0;
     if (group ? (h->K != 2 && h->K != 4) || !(h->kind & PK_TILES) : (h->K != 1 && h->K != 2))
         return RBQ_ERR_INVALID_ARG;
-    const bool pairs = (h->kind & PK_PAIRS) != 0;
-    if (pairs && (group || h->K != 2 || !(h->kind & PK_TILES) || (h->kind & PK_WAITS)))
+    const int lmt = (h->kind & PK_MT_MASK) >> PK_MT_SHIFT;   // log2 of the tokens per op
+    if (lmt > 2 || (lmt > 0 && (group || h->K != 2 || !(h->kind & PK_TILES) || (h->kind & PK_WAITS))))
         return RBQ_ERR_INVALID_ARG;
     if (image_checksum(static_cast<const unsigned char *>(image), image_bytes(h->n_ops, h->grid)) != h->checksum)
         return RBQ_ERR_INVALID_ARG;
     // never launch a layout that would not fit the compute unit's LDS
-    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K, group, pairs ? 2 : 1))
+    if ((size_t)h->lds_bytes > program_dynamic_lds(h->K, group, 1 << lmt))
         return RBQ_ERR_UNSUPPORTED;
     return RBQ_OK;
 }
@@ -1437,8 +1452,12 @@ hipError_t launch_program(const void *image, const void *image_dev, int32_t *cou
         RBQ_LAUNCH_PROGRAM(KK, true, true, true);                        \
     else                                                                 \
         RBQ_LAUNCH_PROGRAM(KK, false, true, true)
-    if (h->kind & PK_PAIRS) {
+    const int lmt = (h->kind & PK_MT_MASK) >> PK_MT_SHIFT;
+    if (lmt == 1) {
         hipLaunchKernelGGL((gemv_program_kernel<2, RBQ_PROGRAM_RING, false, true, false, 2>), dim3(h->grid),
+                           dim3(PG_THREADS), h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
+    } else if (lmt == 2) {
+        hipLaunchKernelGGL((gemv_program_kernel<2, RBQ_PROGRAM_RING, false, true, false, 4>), dim3(h->grid),
                            dim3(PG_THREADS), h->lds_bytes, st, hd, h->n_ops, h->checksum, counters, status);
     } else if (h->kind & PK_GROUP) {
         if (h->K == 2) {

@@ -461,14 +461,14 @@ typedef struct rbq_program_op {
                                  scale tiles of rbq_pack_scale_tiles (16-byte
                                  aligned); K = 2 or 4.  The ops of one program
                                  are all of one kind. */
-    int32_t tokens;           /* tokens the op carries: 0 or 1 (x fp16 [in], y as
-                                 above), or 2 (x fp16 [2][in], y [2][out] or
-                                 [2][out/2]; each token is quantised on its own,
+    int32_t tokens;           /* tokens T the op carries: 0 or 1 (x fp16 [in], y
+                                 as above), 2 or 4 (x fp16 [T][in], y [T][out] or
+                                 [T][out/2]; each token is quantised on its own,
                                  so token m's y equals that of a one-token op on
-                                 row m of x).  Two-token ops take K = 2, per-row
-                                 scales, RBQ_LAYOUT_TILES, in <= 12288 and no
-                                 waits; every op of a program has the same
-                                 token count. */
+                                 row m of x).  Ops of several tokens take K = 2,
+                                 per-row scales, RBQ_LAYOUT_TILES, no waits and
+                                 in <= 12288 (T = 2) or in <= 4096 (T = 4);
+                                 every op of a program has the same count. */
 } rbq_program_op;
 
 /* Bytes of the program image for n_ops ops on the current device (0 when

@@ -342,18 +342,18 @@ def test_batch_tokens_as_ops_on_shared_planes(M):
         assert_close(Y.cpu().numpy(), yb.cpu().numpy(), f"linear {i} against rbq_gemm at {M} tokens")
 
 
-def two_token_program(shapes, seed):
-    """Ops of two tokens (x [2][in], y [2][out] or [2][out / 2]) on tiled planes."""
+def two_token_program(shapes, seed, T=2):
+    """Ops of T tokens (x [T][in], y [T][out] or [T][out / 2]) on tiled planes."""
     host, ops, outs = [], [], []
     for i, (o, n, epi) in enumerate(shapes):
         p, s = layer(o, n, 2, seed=seed + i)
         if epi:
             p, s = interleave_gate_up(p, s)
         pt, st = to_dev(p, s)
-        X = workloads.gaussian_activations(2, n, seed=seed + 50 + i)
+        X = workloads.gaussian_activations(T, n, seed=seed + 50 + i)
         xd = torch.from_numpy(X.view(np.float16)).to(dev())
-        y = torch.full((2, o // 2 if epi else o), float("nan"), dtype=torch.float16, device=dev())
-        ops.append({"planes": rbq.pack_tiles(pt), "scales": st, "x": xd, "y": y, "epilogue": epi, "tokens": 2})
+        y = torch.full((T, o // 2 if epi else o), float("nan"), dtype=torch.float16, device=dev())
+        ops.append({"planes": rbq.pack_tiles(pt), "scales": st, "x": xd, "y": y, "epilogue": epi, "tokens": T})
         host.append((p, s, pt, st, X, xd, epi))
         outs.append(y)
     return host, ops, outs
@@ -372,7 +372,7 @@ def check_two_token_outputs(host, outs, shapes, against_flat=False):
         yr = oracle.gemm(p, s, X)
         if epi:
             yr = oracle.silu_mul(yr)
-        for m in range(2):
+        for m in range(X.shape[0]):
             what = f"op {i} {shapes[i]} token {m}"
             assert_close(y[m].cpu().numpy(), yr[m], what)
             ref = eager_flat(pt, st, xd[m], epilogue=epi) if against_flat else one_token_program(pt, st, xd[m], epi)
@@ -410,6 +410,45 @@ def test_two_token_ops_ragged():
               (23, 1152, 0), (999, 1152, 0)]
     host, ops, outs = two_token_program(shapes, seed=700)
     # op 7 reads op 6's x
+    ops[7]["x"] = ops[6]["x"]
+    host[7] = host[7][:4] + host[6][4:6] + host[7][6:]
+    prog = rbq.Program(ops, num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_two_token_outputs(host, outs, shapes)
+
+
+def test_four_token_ops_llama2_7b_shapes():
+    """The fused Llama-2-7B decode shapes of 4096 inputs with four tokens per
+    op (12 of the 16 MFMA columns), gate/up with the SiLU-mul epilogue: each
+    token's output equals rbq_gemv's bit for bit; a second run repeats it."""
+    shapes = [(12288, 4096, 0), (4096, 4096, 0), (22016, 4096, 1)] * 2
+    host, ops, outs = two_token_program(shapes, seed=900, T=4)
+    prog = rbq.Program(ops, num_planes=2)
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert not prog.counters.any()
+    check_two_token_outputs(host, outs, shapes, against_flat=True)
+    first = [y.clone() for y in outs]
+    for y in outs:
+        y.fill_(float("nan"))
+    prog.run(status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for a, b in zip(first, outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_four_token_ops_ragged():
+    """Four-token ops on ragged shapes up to the widest input they take (4096
+    columns), an odd number of gate/up pairs, and two ops on one x."""
+    shapes = [(1, 128, 0), (17, 384, 0), (300, 4096, 0), (4100, 640, 0), (34, 512, 1), (4098, 2048, 1),
+              (23, 1152, 0), (999, 1152, 0)]
+    host, ops, outs = two_token_program(shapes, seed=1100, T=4)
     ops[7]["x"] = ops[6]["x"]
     host[7] = host[7][:4] + host[6][4:6] + host[7][6:]
     prog = rbq.Program(ops, num_planes=2)

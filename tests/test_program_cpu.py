@@ -198,6 +198,16 @@ def test_two_token_programs():
     assert build([pop(W(0), W(1), A(0), A(1)), op(W(2), W(3), A(0), A(2), layout=rbq.RBQ_LAYOUT_TILES)]) == \
         rbq.RBQ_ERR_INVALID_ARG                                                                   # mixed counts
     assert build([pop(W(0), W(1), A(0), A(1), tokens=3)]) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([pop(W(0), W(1), A(0), A(1), tokens=8)]) == rbq.RBQ_ERR_UNSUPPORTED
+    # four-token ops: inputs of at most 4096 columns
+    four = [pop(W(2 * i), W(2 * i + 1), A(0), A(1 + i), out=22016 if i % 2 else 4096, inf=4096, tokens=4)
+            for i in range(96)]
+    assert build(four) == rbq.RBQ_OK
+    assert build([pop(W(0), W(1), A(0), A(1), inf=4224, tokens=4)]) == rbq.RBQ_ERR_UNSUPPORTED
+    assert build([pop(W(0), W(1), A(0), A(1), tokens=4), pop(W(2), W(3), A(0), A(2))]) == rbq.RBQ_ERR_INVALID_ARG
+    # x of 4 x 512 fp16 = 4096 bytes
+    assert build([pop(W(0), W(1), A(0), A(0) + 3072, tokens=4)]) == rbq.RBQ_ERR_INVALID_ARG
+    assert build([pop(W(0), W(1), A(0), A(0) + 4096, tokens=4)]) == rbq.RBQ_OK
     assert build([pop(W(0), W(1), A(0), A(1), tokens=-1)]) == rbq.RBQ_ERR_INVALID_ARG
     assert build([op(W(0), W(1), A(0), A(1), layout=rbq.RBQ_LAYOUT_TILES, tokens=1),
                   op(W(2), W(3), A(0), A(2), layout=rbq.RBQ_LAYOUT_TILES, tokens=0)]) == rbq.RBQ_OK
