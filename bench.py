@@ -149,7 +149,7 @@ def main():
         import workloads
         torch.cuda.set_device(0)
         print(json.dumps(skinny_program_step(args, torch, rbq, workloads, torch.device("cuda:0"), args.tokens or 4,
-                                             cpu_seconds=args.cpu_seconds)), flush=True)
+                                             cpu_seconds=args.cpu_seconds, layout=args.layout)), flush=True)
     else:
         bench_layer_set(args)
 
@@ -405,7 +405,7 @@ def group_program_step(args, torch, rbq, workloads, dev, n_layers=40, cpu_second
     return line
 
 
-def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
+def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0, layout="fused"):
     """The Llama-2-7B decode step for a batch of M tokens (K = 2, fused
     layout, args.layers layers with their own weights, planes in the tile
     layout) as program launches, in three forms of the same arithmetic (each
@@ -414,7 +414,8 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
         (4096 inputs) as ops of four tokens, whose limbs fill 12 of the 16
         MFMA columns, so a unit of planes feeds four tokens for the same
         MFMAs; down (11008 inputs, too wide for a four-token image) as ops of
-        two tokens in a second launch -- the reported value;
+        two tokens; one launch per linear (the reported value), or one
+        launch for the four-token ops and one for the two-token ones;
       * two-token ops (M even), one launch;
       * one-token ops on shared planes, one launch.
     The ops of a linear run one after another, so its planes come from HBM
@@ -426,13 +427,14 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
     wl = workloads.WORKLOADS["llama2_7b_skinny"]
     K, group = wl.num_planes, wl.group_size
     n_layers = args.layers
-    groups, layers, shapes, widths, Ws, _, _ = decode_sets(torch, rbq, workloads, wl, dev, "fused", n_layers)
+    groups, layers, shapes, widths, Ws, _, _ = decode_sets(torch, rbq, workloads, wl, dev, layout, n_layers)
     del Ws
     tiles = [[rbq.pack_tiles(p) for p, _ in layer] for layer in layers]
-    slots = X_SLOTS["fused"]
+    slots = X_SLOTS[layout]
     per_slot = {sl: torch.from_numpy(workloads.layer_activations(wl, widths[i], n_layers * M, sl).view(
         np.float16)).to(dev).reshape(n_layers, M, widths[i]) for i, sl in enumerate(slots)}
     xs = [[per_slot[sl][l] for sl in slots] for l in range(n_layers)]
+    # algorithmic bytes per linear: planes and scales once, M tokens of its x and y
     per_lin = [gemv_bytes(sh.out_features, sh.in_features, K, 1, M) for sh in shapes]
     nbytes = sum(per_lin) * n_layers
     stream = torch.cuda.current_stream(dev)
@@ -440,6 +442,11 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
     wide = [i for i in range(len(shapes)) if i not in narrow]
     candidates = []
     if M % 4 == 0:
+        # one launch per linear: each program's op groups and LDS layout fit
+        # its own shape (mixed in one launch, the 22016-row gate/up ops leave
+        # room for one op group only, which the 4096-row ops run poorly)
+        candidates.append(("4_and_2_token_ops_per_linear", [([i], 4 if i in narrow else 2)
+                                                            for i in range(len(shapes))]))
         candidates.append(("4_and_2_token_ops", [(narrow, 4), (wide, 2)]))
     if M % 2 == 0:
         candidates.append(("2_token_ops", [(list(range(len(shapes))), 2)]))
@@ -491,7 +498,7 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0):
     line = {"metric": f"K={K} batch-{M} GEMM effective GB/s on Llama-2-7B layers, decode step as program launches",
             "value": round(nbytes / (f["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": f["ms_per_step"], "dtype": DTYPE_INT8_LIMBS,
-            "config": {"workload": f"llama2_7b_skinny_m{M}_decode_program", "layers": n_layers, "layout": "fused",
+            "config": {"workload": f"llama2_7b_skinny_m{M}_decode_program", "layers": n_layers, "layout": layout,
                        "ops_per_layer": {name_: f"{sh.out_features}x{sh.in_features}"
                                          for (name_, _), sh in zip(groups, shapes)},
                        "num_planes": K, "group_size": group, "tokens": M, "form": name,
