@@ -211,6 +211,9 @@ def counter_pass(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "llama2_7b_skinny_program":
+        skinny_counter_pass(args, torch, rbq, workloads, dev, args.tokens or 4)
+        return
     wl = workloads.WORKLOADS["llama2_7b"]
     K, group = wl.num_planes, wl.group_size
     groups, layers, shapes, widths, Ws, _, _ = decode_sets(torch, rbq, workloads, wl, dev, args.layout,
@@ -243,6 +246,44 @@ def counter_pass(args):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"counter pass: copy of {COPY_PROBE_BYTES} bytes x4", flush=True)
+
+
+def skinny_counter_pass(args, torch, rbq, workloads, dev, M):
+    """Launches for `rocprofv3 --pmc` (with --workload llama2_7b_skinny_program):
+    the batch-M decode step as the benchmark's per-linear programs (four-token
+    ops for the 4096-column inputs, two-token ops for down), each run three
+    times in step order, then torch copies of a 256 MiB buffer for the
+    calibration."""
+    wl = workloads.WORKLOADS["llama2_7b_skinny"]
+    K = wl.num_planes
+    groups, layers, shapes, widths, Ws, _, _ = decode_sets(torch, rbq, workloads, wl, dev, "fused", args.layers)
+    del Ws
+    tiles = [[rbq.pack_tiles(p) for p, _ in layer] for layer in layers]
+    slots = X_SLOTS["fused"]
+    xs = {sl: torch.from_numpy(workloads.layer_activations(wl, widths[i], args.layers * M, sl).view(
+        np.float16)).to(dev).reshape(args.layers, M, widths[i]) for i, sl in enumerate(slots)}
+    progs = []
+    for i, sh in enumerate(shapes):
+        tok = 4 if sh.in_features <= 4096 else 2
+        ys = [torch.empty((M, sh.out_features), dtype=torch.float16, device=dev) for _ in range(args.layers)]
+        progs.append((sh, tok, rbq.Program([{"planes": tiles[l][i], "scales": layers[l][i][1],
+                                              "x": xs[slots[i]][l][m:m + tok], "y": ys[l][m:m + tok], "tokens": tok}
+                                             for l in range(args.layers) for m in range(0, M, tok)], num_planes=K),
+                      ys))
+    for _ in range(3):
+        for sh, tok, pr, _ in progs:
+            pr.run()
+    torch.cuda.synchronize()
+    for sh, tok, pr, _ in progs:
+        nb = gemv_bytes(sh.out_features, sh.in_features, K, 1, M) * args.layers
+        print(f"skinny counter pass: {sh.out_features}x{sh.in_features}, {args.layers} layers, {M} tokens in ops "
+              f"of {tok}: {pr.n_ops} ops x3 ({nb} algorithmic bytes per launch)", flush=True)
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"skinny counter pass: copy of {COPY_PROBE_BYTES} bytes x4", flush=True)
 
 
 def encode_counter_pass(args):

@@ -23,5 +23,6 @@ def test_several_gpus_are_refused():
 def test_help_lists_the_workloads():
     r = run("--help")
     assert r.returncode == 0
-    for name in ("llama2_7b", "llama2_7b_skinny", "llama2_13b_g128", "llama3_8b_prefill", "--layout", "--no-extra"):
+    for name in ("llama2_7b", "llama2_7b_skinny", "llama2_7b_skinny_program", "llama2_13b_g128", "llama2_13b_g128_program",
+                 "llama3_8b_prefill", "--layout", "--no-extra", "--counter-pass"):
         assert name in r.stdout
