@@ -103,6 +103,8 @@ _SIGNATURES = {
                                        ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_gemv_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, Shape,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "rbq_gemm_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, Shape, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "rbq_program_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
     "rbq_program_counters_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
     "rbq_program_build": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -579,6 +581,31 @@ def gemv_dual(planes: torch.Tensor, g: torch.Tensor, h: torch.Tensor, x: torch.T
     check(lib().rbq_gemv_dual(planes.data_ptr(), g.data_ptr(), h.data_ptr(), s, x.data_ptr(),
                               y.data_ptr(), _stream(x, stream)), "rbq_gemv_dual")
     return y
+
+
+def gemm_dual(planes: torch.Tensor, g: torch.Tensor, h: torch.Tensor, X: torch.Tensor, *,
+              Y: torch.Tensor | None = None, stream=None):
+    """rbq_gemm_dual: Y[M][out] = X Ŵᵀ with Ŵ = sum_k diag(g_k) B_k diag(h_k), fp16 in and out."""
+    _dev(planes, torch.int32, "planes")
+    _dev(g, torch.float16, "g")
+    _dev(h, torch.float16, "h")
+    _dev(X, torch.float16, "X")
+    K, out_f, words = planes.shape
+    in_f = words * 32
+    if X.dim() != 2 or X.shape[1] != in_f:
+        raise ValueError(f"X must be [M][{in_f}]")
+    M = X.shape[0]
+    s = shape(out_f, in_f, K, 0)
+    if g.numel() * 2 < int(lib().rbq_dual_g_bytes(s)) or h.numel() * 2 < int(lib().rbq_dual_h_bytes(s)):
+        raise ValueError("g/h buffers are too small for the shape")
+    if Y is None:
+        Y = torch.empty((M, out_f), dtype=torch.float16, device=X.device)
+    _dev(Y, torch.float16, "Y")
+    if Y.numel() < M * out_f:
+        raise ValueError("Y too small")
+    check(lib().rbq_gemm_dual(planes.data_ptr(), g.data_ptr(), h.data_ptr(), s, X.data_ptr(), M, Y.data_ptr(),
+                              _stream(X, stream)), "rbq_gemm_dual")
+    return Y
 
 
 class Program:

@@ -455,6 +455,41 @@ rbq_status rbq_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16
     return e == hipSuccess ? RBQ_OK : hip_fail(e);
 }
 
+rbq_status rbq_gemm_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,
+                         const uint16_t *X, int32_t M, uint16_t *Y, void *stream) {
+    rbq_status st = rbq_check_shape(s);
+    if (st != RBQ_OK)
+        return st;
+    if (s.group_size != 0 || M < 0)
+        return RBQ_ERR_INVALID_ARG;
+    if (M == 0 || s.out_features == 0)
+        return RBQ_OK;
+    // one token: the matrix-core kernels of rbq_gemv_dual where they take the
+    // shape (and no plain-kernel run is forced)
+    if (M == 1 && (rbq_path)g_forced_path.load() != RBQ_PATH_VALU && rbq::dual_supports(s.in_features, s.num_planes))
+        return rbq_gemv_dual(planes, g, h, s, X, Y, stream);
+    if (Y == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(Y, 2))
+        return RBQ_ERR_ALIGNMENT;
+    hipStream_t hs = (hipStream_t)stream;
+    if (s.in_features == 0) {  // empty sums: Y = 0
+        if ((st = device_present()) != RBQ_OK)
+            return st;
+        hipError_t e = rbq::launch_fill_zero_u16(Y, (int64_t)M * s.out_features, hs);
+        return e == hipSuccess ? RBQ_OK : hip_fail(e);
+    }
+    if (planes == nullptr || g == nullptr || h == nullptr || X == nullptr)
+        return RBQ_ERR_INVALID_ARG;
+    if (!aligned(planes, 16) || !aligned(g, 2) || !aligned(h, 16) || !aligned(X, 16))
+        return RBQ_ERR_ALIGNMENT;
+    if ((st = device_present()) != RBQ_OK)
+        return st;
+    hipError_t e = rbq::launch_gemm_valu_dual(planes, g, h, s.out_features, s.in_features, s.num_planes, X, M, Y,
+                                              hs);
+    return e == hipSuccess ? RBQ_OK : hip_fail(e);
+}
+
 size_t rbq_program_bytes(int32_t n_ops) { return rbq::program_bytes(n_ops); }
 
 size_t rbq_program_counters_bytes(int32_t n_ops) {

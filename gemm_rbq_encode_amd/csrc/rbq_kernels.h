@@ -36,6 +36,8 @@ hipError_t launch_gemm_decode(const uint32_t *planes, const uint16_t *scales, in
 // Dual-scale GEMV on the decode kernel: y = sum_k g_k (.) (B_k (h_k (.) x)),
 // g [K][out], h [K][in] binary16, one token (K <= 4, in % 128 == 0).
 bool dual_supports(int in, int K);
+hipError_t launch_gemm_valu_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
+                                 int K, const uint16_t *X, int M, uint16_t *Y, hipStream_t st);
 hipError_t launch_gemv_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, int out, int in,
                             int K, const uint16_t *x, uint16_t *y, hipStream_t st);
 

@@ -340,6 +340,25 @@ rbq_status rbq_encode_dual(const float *W, rbq_shape s, uint32_t *planes, uint16
                            void *workspace, size_t workspace_bytes, int32_t *status_dev, void *stream);
 
 /*
+ * rbq_gemm_dual -- Y[m] = sum_k g_k (.) (B_k (h_k (.) X[m])) for M tokens
+ * (RaBiT section 4.1: scaling vectors on both sides of each binary core).
+ * One token takes rbq_gemv_dual's matrix-core kernels where they serve the
+ * shape (K <= 4, in % 128 == 0) and RBQ_PATH_VALU is not forced; otherwise
+ * a plain fp32 kernel runs (each product h_k[j] X[m][j] exact in fp32, fp32
+ * sums, one binary16 rounding of each output), not tuned for speed.
+ *   planes  device uint32 [K][out][in/32], 16-byte aligned
+ *   g       device binary16 [K][out], 2-byte aligned
+ *   h       device binary16 [K][in], 16-byte aligned
+ *   X       device fp16 [M][in], 16-byte aligned;  Y device fp16 [M][out], written
+ *   M       tokens, >= 0 (0 enqueues nothing)
+ * group_size must be 0 (RBQ_ERR_INVALID_ARG).  Errors: RBQ_ERR_INVALID_ARG,
+ * RBQ_ERR_ALIGNMENT, RBQ_ERR_NO_DEVICE, RBQ_ERR_HIP (and rbq_gemv_dual's for
+ * one token).
+ */
+rbq_status rbq_gemm_dual(const uint32_t *planes, const uint16_t *g, const uint16_t *h, rbq_shape s,
+                         const uint16_t *X, int32_t M, uint16_t *Y, void *stream);
+
+/*
  * rbq_gemv_dual -- y = sum_k g_k (.) (B_k (h_k (.) x)) for one token, on the
  * int8 matrix cores: the K products h_k (.) x (exact in fp32) take the place
  * of tokens, each quantised to three 8-bit limbs with its own power of two.

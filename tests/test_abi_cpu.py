@@ -197,3 +197,18 @@ def test_dual_valid_call_without_device_reports_no_device():
     ws = L.rbq_encode_dual_workspace_bytes(s)
     assert L.rbq_encode_dual(ok, s, ok, ok, ok, ok, ws, None, None) == rbq.RBQ_ERR_NO_DEVICE
     assert L.rbq_gemv_dual(ok, ok, ok, s, ok, ok, None) == rbq.RBQ_ERR_NO_DEVICE
+
+
+def test_gemm_dual_argument_errors():
+    L = rbq.lib()
+    s = rbq.shape(64, 128, 2, 0)
+    ok = 0x10000
+    assert L.rbq_gemm_dual(ok, ok, ok, s, ok, -1, ok, None) == rbq.RBQ_ERR_INVALID_ARG         # M < 0
+    assert L.rbq_gemm_dual(ok, ok, ok, rbq.shape(64, 128, 2, 128), ok, 4, ok, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm_dual(ok, ok, ok, rbq.shape(64, 100, 2), ok, 4, ok, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm_dual(None, ok, ok, s, ok, 4, ok, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm_dual(ok, ok, ok, s, ok, 4, None, None) == rbq.RBQ_ERR_INVALID_ARG
+    assert L.rbq_gemm_dual(ok, ok, ok + 8, s, ok, 4, ok, None) == rbq.RBQ_ERR_ALIGNMENT          # h
+    assert L.rbq_gemm_dual(ok, ok, ok, s, ok + 8, 4, ok, None) == rbq.RBQ_ERR_ALIGNMENT          # X
+    assert L.rbq_gemm_dual(ok, ok, ok, s, ok, 4, ok + 1, None) == rbq.RBQ_ERR_ALIGNMENT          # Y
+    assert L.rbq_gemm_dual(ok, ok, ok, s, ok, 0, ok, None) == rbq.RBQ_OK                         # nothing to do

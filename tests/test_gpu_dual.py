@@ -229,3 +229,71 @@ def test_gemv_dual_zero_input_columns_and_empty():
     torch.cuda.synchronize()
     assert st == rbq.RBQ_OK and not y.any()
     assert L.rbq_gemv_dual(None, None, None, rbq.shape(0, 128, 2), None, None, None) == rbq.RBQ_OK
+
+
+def random_dual_layer(K, out, inf, seed):
+    """Random planes; g ~ 1/sqrt(K in) and h ~ 1 (both signs) in binary16."""
+    rng = np.random.default_rng(seed)
+    p = workloads.random_planes(K, out, inf, seed=seed)
+    g = (rng.uniform(0.5, 1.5, (K, out)) / np.sqrt(K * inf) * rng.choice([-1.0, 1.0], (K, out))).astype(np.float16)
+    h = (rng.uniform(0.25, 2.0, (K, inf)) * rng.choice([-1.0, 1.0], (K, inf))).astype(np.float16)
+    return p, g.view(np.uint16), h.view(np.uint16)
+
+
+def assert_close_dual(y, yref, what):
+    y = np.asarray(y, dtype=np.float64)
+    assert np.isfinite(y).all(), what
+    rms = np.sqrt(np.mean(yref ** 2))
+    rel = np.linalg.norm(y - yref) / max(np.linalg.norm(yref), 1e-300)
+    mx = np.abs(y - yref).max()
+    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
+    assert mx <= MAX_ABS_RMS * rms, f"{what}: max-abs {mx:.3e} vs rms {rms:.3e}"
+
+
+@pytest.mark.parametrize("K,out,inf,M", [(2, 256, 512, 2), (2, 300, 640, 5), (1, 64, 96, 3), (3, 17, 384, 16),
+                                         (4, 130, 1152, 4), (2, 4096, 4096, 4), (2, 11008, 4096, 2),
+                                         (2, 4096, 11008, 16), (2, 512, 1024, 1), (2, 64, 96, 1)])
+def test_gemm_dual_matches_oracle(K, out, inf, M):
+    """rbq_gemm_dual for M tokens (one token on the matrix-core kernels where
+    they take the shape, else and for several tokens the plain kernel)
+    against Y = X What^T in fp64; ragged rows, inputs not a multiple of 128,
+    K from 1 to 4, and mixed-magnitude tokens."""
+    p, g, h = random_dual_layer(K, out, inf, seed=out * 7 + inf + K + M)
+    X = workloads.gaussian_activations(M, inf, seed=M * 13 + inf)
+    Xv = X.view(np.float16).copy()
+    if M >= 3:
+        Xv[1] *= np.float16(1e-3)            # a small token beside ordinary ones
+        Xv[2, ::7] = np.float16(300.0)       # a token with large entries
+    pt = torch.from_numpy(np.ascontiguousarray(p).view(np.int32)).to(dev())
+    gt = torch.from_numpy(g.view(np.float16)).to(dev())
+    ht = torch.from_numpy(h.view(np.float16)).to(dev())
+    Xt = torch.from_numpy(Xv).to(dev())
+    Y = rbq.gemm_dual(pt, gt, ht, Xt)
+    torch.cuda.synchronize()
+    yref = dual.gemm_dual(p, g, h, Xv.view(np.uint16))
+    for m in range(M):
+        assert_close_dual(Y[m].cpu().numpy(), yref[m], f"token {m}")
+    if M == 1:
+        # the plain kernel forced for the same call agrees with the same bar
+        old = rbq.set_path(rbq.PATH_VALU)
+        try:
+            Yv = rbq.gemm_dual(pt, gt, ht, Xt)
+        finally:
+            rbq.set_path(old)
+        torch.cuda.synchronize()
+        assert_close_dual(Yv[0].cpu().numpy(), yref[0], "plain kernel, one token")
+
+
+def test_gemm_dual_on_encoded_layer():
+    """The dual-scale encoder's output through rbq_gemm_dual for 8 tokens,
+    against the oracle's layer output on the same planes and scales."""
+    W = workloads.gaussian_weight(512, 1024, 31)
+    p, g, h, st = gpu_encode_dual(W, 2)
+    assert st == 0
+    X = workloads.gaussian_activations(8, 1024, seed=32)
+    Y = rbq.gemm_dual(torch.from_numpy(p.view(np.int32)).to(dev()), torch.from_numpy(g.view(np.float16)).to(dev()),
+                      torch.from_numpy(h.view(np.float16)).to(dev()), torch.from_numpy(X.view(np.float16)).to(dev()))
+    torch.cuda.synchronize()
+    yref = dual.gemm_dual(p, g, h, X)
+    for m in range(8):
+        assert_close_dual(Y[m].cpu().numpy(), yref[m], f"token {m}")
