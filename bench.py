@@ -563,6 +563,36 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0, la
     return line
 
 
+def prefill_more_planes(args, torch, rbq, workloads, dev, M=2048, shapes=((14336, 4096), (4096, 14336))):
+    """The prefill contraction at K = 3 and K = 4 (per-row scales, and K = 4
+    with 128-column groups as in QBB), which run the kernel that unpacks
+    What into LDS: random planes and scales (the time does not depend on the
+    values), M fp16 tokens; per-launch device time from HIP events around
+    graph replays, dense-equivalent TFLOP/s (2 M out in / t)."""
+    res = {}
+    X = torch.from_numpy(workloads.gaussian_activations(M, max(i for _, i in shapes), seed=77).view(np.float16)).to(dev)
+    for K, group in ((3, 0), (4, 0), (4, 128)):
+        per = {}
+        for out_f, in_f in shapes:
+            p = torch.from_numpy(workloads.random_planes(K, out_f, in_f, seed=out_f + in_f + K).view(np.int32)).to(dev)
+            G = in_f // group if group else 1
+            sc = torch.from_numpy((np.random.default_rng(K).uniform(0.001, 0.01, (K, out_f, G))).astype(
+                np.float16)).to(dev).reshape(K, -1)
+            Xs = X[:, :in_f].contiguous()
+            Y = torch.empty((M, out_f), dtype=torch.float16, device=dev)
+            fn = (lambda p=p, sc=sc, Xs=Xs, Y=Y: rbq.gemm(p, sc, Xs, group, Y=Y))
+            fn()
+            torch.cuda.synchronize()
+            us = graph_launch_us(torch, dev, [fn], max(args.kernel_reps, 3))
+            per[f"{out_f}x{in_f}"] = {"mean_us": round(us, 2),
+                                      "TFLOPs_dense_eq": round(2.0 * M * out_f * in_f / (us * 1e-6) / 1e12, 1)}
+            del p, sc, Xs, Y
+        res[f"K{K}" + ("_g128" if group else "")] = per
+    del X
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_layer_set(args):
     import torch
 
@@ -1284,6 +1314,8 @@ def bench_decode(args):
                                            if k in sub}
             if "encode_refit_per_shape" in sub:
                 others[f"{name}_m{tokens}"]["encode_refit_per_shape"] = sub["encode_refit_per_shape"]
+        others["llama3_8b_prefill_m2048"]["more_planes_unpack_kernel"] = prefill_more_planes(
+            args, torch, rbq, workloads, dev)
 
     if not args.no_extra:
         others["llama2_13b_g128_program"] = group_program_step(args, torch, rbq, workloads, dev,

@@ -106,6 +106,9 @@ int main(void)
     CHECK(rbq_pack_tiles(NULL, s, ok, NULL) == RBQ_ERR_INVALID_ARG, "pack null");
     CHECK(rbq_qat_encode(NULL, s, ok, ok, NULL, NULL) == RBQ_ERR_INVALID_ARG, "qat encode null");
     CHECK(rbq_probe_read(NULL, 16, ok, NULL) == RBQ_ERR_INVALID_ARG, "probe null");
+    CHECK(rbq_gemm_dual(ok, ok, ok, s, ok, -1, ok, NULL) == RBQ_ERR_INVALID_ARG, "gemm_dual M");
+    CHECK(rbq_gemm_dual(ok, ok, (const uint16_t *)((char *)ok + 8), s, ok, 4, ok, NULL) == RBQ_ERR_ALIGNMENT,
+          "gemm_dual h alignment");
 
     /* the program builder: valid lists of many ops, chains, tiles, g128 */
     enum { N = 224 };
@@ -131,6 +134,21 @@ int main(void)
     ops[0] = op(0, 0, 1, 250, 16512, -1, RBQ_LAYOUT_ROWS, 0);
     CHECK(build(ops, 1, 2, 0) == RBQ_ERR_UNSUPPORTED, "in beyond 16384");
     CHECK(rbq_program_build(NULL, 1, 2, NULL, 0) == RBQ_ERR_INVALID_ARG, "null ops");
+    /* ops of two and four tokens */
+    for (int i = 0; i < 128; ++i) {
+        ops[i] = op(i, 0, 1 + i, i % 2 ? 22016 : 4096, 4096, -1, RBQ_LAYOUT_TILES, 0);
+        ops[i].tokens = 4;
+    }
+    CHECK(build(ops, 128, 2, 0) == RBQ_OK, "four-token ops");
+    ops[3].tokens = 2;
+    CHECK(build(ops, 128, 2, 0) == RBQ_ERR_INVALID_ARG, "mixed token counts");
+    for (int i = 0; i < 64; ++i) {
+        ops[i] = op(i, 0, 1 + i, 4096, 11008, -1, RBQ_LAYOUT_TILES, 0);
+        ops[i].tokens = 2;
+    }
+    CHECK(build(ops, 64, 2, 0) == RBQ_OK, "two-token ops");
+    ops[0].in_features = 16384;
+    CHECK(build(ops, 64, 2, 0) == RBQ_ERR_UNSUPPORTED, "two-token ops beyond 12288 columns");
 
     for (int st = 0; st < 8; ++st)
         CHECK(rbq_status_string((rbq_status)st) != NULL, "status string");
