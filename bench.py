@@ -37,9 +37,12 @@ Reported (one JSON line):
              one program launch
   encode / refit / encode_refit_per_shape / gemv_dual_per_shape  the other
              entry points on the same shapes
-  other_workloads  skinny M=4 and M=16, Llama-2-13B K=4 g128 and the
-             Llama-3-8B prefill set (--no-extra skips them; --workload runs
-             one of them on its own line)
+  other_workloads  skinny M=4 and M=16 per call, the batch-4 and batch-16
+             decode steps as program launches (several-token ops),
+             Llama-2-13B K=4 g128 per call and its decode step as one
+             program, and the Llama-3-8B prefill set with K = 3 and 4 beside
+             it (--no-extra skips them; --workload runs one of them on its
+             own line)
   qat        the coupled forward (cores re-derived from W, then the layer)
              and the straight-through backward on the Llama-2-7B shapes
 
