@@ -161,6 +161,7 @@ COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "gemv_llama2_7b_decode_hbm_traffic.json")
 TRAFFIC_PROFILE_13B = os.path.join(ROOT, "profiles", "gemv_llama2_13b_g128_program_hbm_traffic.json")
+TRAFFIC_PROFILE_BATCH = os.path.join(ROOT, "profiles", "gemv_llama2_7b_batch_program_hbm_traffic.json")
 
 
 def profile_entry(shape_key, kernel_prefix, path=None):
@@ -551,7 +552,9 @@ def skinny_program_step(args, torch, rbq, workloads, dev, M, cpu_seconds=4.0, la
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (f["mean_step_launch_us"] * 1e-6) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(nbytes / (f["mean_step_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "kernel": f"gemv_program_kernel<{K}> ({name})",
+                         "traffic": (measured_traffic(f"batch{M}_per_linear", "gemv_program_kernel", TRAFFIC_PROFILE_BATCH)
+                                     if name == "4_and_2_token_ops_per_linear" and layout == "fused" else None),
+                         "kernel": f"gemv_program_kernel<{K}> ({name})",
                          "bytes_per_launch": nbytes, "mean_launch_us": f["mean_step_launch_us"]},
             "layer0_max_rel_diff_vs_rbq_gemm": f["layer0_max_rel_diff_vs_rbq_gemm"],
             "forms": forms, "cpu_baseline": None}
