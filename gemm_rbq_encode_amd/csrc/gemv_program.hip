@@ -1312,6 +1312,7 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         std::vector<Placed> live;   // images placed so far, oldest first, with their byte ranges
         std::vector<int> seq;       // the group's ops so far
         int trot = 0, wrot = 0, next_off = 0, prev_off = 0;
+        int last_trot = 0;          // the tile rotation of the group's op before
     };
     std::vector<GroupPlan> gp(P);
     for (int i = 0; i < n_ops; ++i) {
@@ -1332,7 +1333,13 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         const int nch = (o.in_features / 32 + CHUNK_WORDS - 1) / CHUNK_WORDS;
         p.magic = ((1u << 21) + nch - 1) / nch;
         const int lpos = (int)g.seq.size();
-        p.trot = g.trot | (lpos << 16);
+        // an op on the planes of the group's op before (another batch of
+        // tokens) takes that op's tiles: each workgroup re-reads the planes it
+        // has just read, from its L2
+        const bool same_planes = !g.seq.empty() && ops[g.seq.back()].planes == o.planes &&
+                                 ops[g.seq.back()].out_features == o.out_features;
+        const int trot_op = same_planes ? g.last_trot : g.trot;
+        p.trot = trot_op | (lpos << 16);
         if (!g.seq.empty())   // link the group's previous op to this one
             d[g.seq.back()].split = (d[g.seq.back()].split & 0xFFFFFu) | ((uint32_t)i << 20);
         // an op that reads the same x as the group's op before it (and no op
@@ -1360,8 +1367,10 @@ rbq_status program_build(const rbq_program_op *ops, int n_ops, int K, void *imag
         g.seq.push_back(i);
         p.nch_img = (uint32_t)nch | ((uint32_t)(off / 16) << 8);
         p.flags |= (uint32_t)g.wrot << PF_WROT_SHIFT;
-        const int trot_op = g.trot;
-        g.trot = (g.trot + extra) % Gl;
+        if (!same_planes) {
+            g.last_trot = g.trot;
+            g.trot = (g.trot + extra) % Gl;
+        }
         g.wrot = (g.wrot + ((tiles + Gl - 1) / Gl) * nch) % PG_STREAM;
         for (int bl = 0; bl < Gl; ++bl) {
             const int bb = grp[i] * Gl + bl;
